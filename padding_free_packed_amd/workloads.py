@@ -1,0 +1,183 @@
+"""Seeded synthetic workloads shared by the oracle side and the HIP side.
+
+This module only draws inputs. It holds none of the attention, packing or
+gradient arithmetic: both implementations receive the same arrays from here and
+compute on their own.
+
+Every workload follows one recipe:
+
+* ``rng = numpy.random.default_rng(seed)``;
+* draw the sequence lengths first, then (if the workload has one) the padded
+  grid ``[B, S, D]``, then Q, K, V and dO, each ``rng.standard_normal(shape,
+  dtype=float32)`` with shape ``[N, H, d]``;
+* "uniform int in [a, b]" is ``rng.integers(a, b + 1)``; "round" is
+  ``numpy.rint`` (half to even), clipped after rounding;
+* bf16 values are the round-to-nearest-even images of those fp32 draws,
+  produced on the bit patterns below; arrays of bf16 are ``uint16`` bit arrays;
+* padding cells of a grid hold NaN, so a pack that reads padding is caught.
+
+The length distributions and shapes are those of the workloads described on the
+GiGL packed-attention page (graph-transformer sequences of at most 256 tokens,
+about 90 real, hidden 512 in 8 heads) and the packed-encoders page (queries of
+about 30 tokens, documents of hundreds to thousands, contrastive batches that
+mix both, hidden 768 in 12 heads and 1024 in 16 heads).
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+import numpy as np
+
+FP32 = "fp32"
+BF16 = "bf16"
+
+BF16_NAN = np.uint16(0x7FC0)
+
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round fp32 values to bf16 (nearest, ties to even) and return the uint16 bits."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    nan = (u & 0x7FFFFFFF) > 0x7F800000
+    rounded = (u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16)
+    out = rounded.astype(np.uint16)
+    out[nan] = BF16_NAN
+    return out
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    """Exact widening of bf16 bit patterns to fp32."""
+    return (np.ascontiguousarray(b, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def to_f64(x: np.ndarray, dtype: str) -> np.ndarray:
+    """Exact widening of a workload array (fp32 values or bf16 bits) to float64."""
+    if dtype == BF16:
+        return bf16_bits_to_f32(x).astype(np.float64)
+    return np.asarray(x, dtype=np.float32).astype(np.float64)
+
+
+@dataclass
+class Workload:
+    name: str
+    dtype: str
+    lengths: np.ndarray            # int32 [B]
+    max_seq_len: int               # S, the grid width and the bound on every length
+    num_heads: int
+    head_dim: int
+    scale: float                   # softmax scale as the fp32 value both sides receive
+    q: np.ndarray | None = None    # [N, H, d] fp32 values or bf16 bits
+    k: np.ndarray | None = None
+    v: np.ndarray | None = None
+    dout: np.ndarray | None = None
+    grid: np.ndarray | None = None  # [B, S, D] with NaN padding, D = H * d
+    extra: dict = field(default_factory=dict)
+
+    @property
+    def num_seqs(self) -> int:
+        return int(self.lengths.shape[0])
+
+    @property
+    def total_tokens(self) -> int:
+        return int(self.lengths.astype(np.int64).sum())
+
+    @property
+    def row_elems(self) -> int:
+        return self.num_heads * self.head_dim
+
+
+def _cast(x: np.ndarray, dtype: str) -> np.ndarray:
+    return f32_to_bf16_bits(x) if dtype == BF16 else x
+
+
+def _draw_grid(rng, lengths, S, D, dtype):
+    g = rng.standard_normal((lengths.shape[0], S, D), dtype=np.float32)
+    g = _cast(g, dtype)
+    pad = np.arange(S)[None, :] >= lengths[:, None]
+    g[pad] = BF16_NAN if dtype == BF16 else np.float32("nan")
+    return g
+
+
+def _draw_tensors(rng, N, H, d, dtype, names):
+    out = {}
+    for nm in names:
+        out[nm] = _cast(rng.standard_normal((N, H, d), dtype=np.float32), dtype)
+    return out
+
+
+def _finish(name, dtype, rng, lengths, S, H, d, grid, names):
+    lengths = np.asarray(lengths, dtype=np.int32)
+    N = int(lengths.astype(np.int64).sum())
+    g = _draw_grid(rng, lengths, S, H * d, dtype) if grid else None
+    t = _draw_tensors(rng, N, H, d, dtype, names)
+    scale = float(np.float32(1.0 / np.sqrt(d)))
+    return Workload(name, dtype, lengths, S, H, d, scale, t.get("q"), t.get("k"),
+                    t.get("v"), t.get("dout"), g)
+
+
+# The five standing workloads. Numbers in the names are those of the list of
+# configurations this library is measured on.
+
+def tiny(with_grad: bool = True) -> Workload:
+    """8 sequences, lengths uniform in [1, 64], S = 64, 2 heads x 8, fp32, grid [8, 64, 16]."""
+    rng = np.random.default_rng(0)
+    lengths = rng.integers(1, 65, size=8)
+    names = ("q", "k", "v", "dout") if with_grad else ("q", "k", "v")
+    return _finish("tiny", FP32, rng, lengths, 64, 2, 8, True, names)
+
+
+def graph_transformer(grid: bool = True, with_grad: bool = True) -> Workload:
+    """4096 sequences, lengths round(N(90, 40)) clipped to [1, 256], S = 256, 8 x 64, fp32."""
+    rng = np.random.default_rng(1)
+    lengths = np.clip(np.rint(rng.normal(90.0, 40.0, size=4096)), 1, 256).astype(np.int64)
+    names = ("q", "k", "v", "dout") if with_grad else ("q", "k", "v")
+    return _finish("graph_transformer", FP32, rng, lengths, 256, 8, 64, grid, names)
+
+
+def short_query(grid: bool = True) -> Workload:
+    """32768 sequences, lengths uniform in [8, 48], S = 48, 12 x 64, bf16."""
+    rng = np.random.default_rng(2)
+    lengths = rng.integers(8, 49, size=32768)
+    return _finish("short_query", BF16, rng, lengths, 48, 12, 64, grid, ("q", "k", "v"))
+
+
+def long_document() -> Workload:
+    """1024 sequences, lengths round(lognormal(ln 512, 0.8)) clipped to [64, 8192], S = 8192, 12 x 64, bf16."""
+    rng = np.random.default_rng(3)
+    lengths = np.clip(np.rint(rng.lognormal(np.log(512.0), 0.8, size=1024)), 64, 8192).astype(np.int64)
+    return _finish("long_document", BF16, rng, lengths, 8192, 12, 64, False, ("q", "k", "v"))
+
+
+def mixed_training() -> Workload:
+    """2048 queries U[16, 48] + 256 documents round(lognormal(ln 1024, 0.7)) clipped to [128, 8192],
+    shuffled together, S = 8192, 16 x 64, bf16, with dO for the backward."""
+    rng = np.random.default_rng(4)
+    queries = rng.integers(16, 49, size=2048)
+    docs = np.clip(np.rint(rng.lognormal(np.log(1024.0), 0.7, size=256)), 128, 8192).astype(np.int64)
+    lengths = rng.permutation(np.concatenate([queries, docs]))
+    return _finish("mixed_training", BF16, rng, lengths, 8192, 16, 64, False, ("q", "k", "v", "dout"))
+
+
+STANDING = {
+    "tiny": tiny,
+    "graph_transformer": graph_transformer,
+    "short_query": short_query,
+    "long_document": long_document,
+    "mixed_training": mixed_training,
+}
+
+
+def custom(seed: int, lengths, max_seq_len: int, num_heads: int, head_dim: int, dtype: str,
+           grid: bool = False, with_grad: bool = False, scale: float | None = None) -> Workload:
+    """A workload with given lengths (drawn by the caller or fixed) and seeded N(0, 1) tensors."""
+    rng = np.random.default_rng(seed)
+    names = ("q", "k", "v", "dout") if with_grad else ("q", "k", "v")
+    w = _finish(f"custom{seed}", dtype, rng, np.asarray(lengths), max_seq_len, num_heads,
+                head_dim, grid, names)
+    if scale is not None:
+        w.scale = float(np.float32(scale))
+    return w
+
+
+def random_lengths(seed: int, num_seqs: int, lo: int, hi: int) -> np.ndarray:
+    """Lengths uniform in [lo, hi], seeded; used for the ragged parity cases."""
+    return np.random.default_rng(seed).integers(lo, hi + 1, size=num_seqs).astype(np.int32)
