@@ -1,0 +1,220 @@
+/*
+ * pe.h - packed, padding-free attention for AMD MI355X (gfx950).
+ *
+ * A C ABI over hand-written HIP kernels. Many variable-length sequences share
+ * one buffer with no padding; each sequence attends only to itself, and the
+ * sequence boundaries come from int32 offsets (cu_seqlens). The operations are
+ * those of the GiGL page "Source code for gigl.nn.packed_attention": packing a
+ * padded grid (module docstring, data flow diagram and "Example"), attention
+ * within each sequence (`_varlen_attention`), the first-token query variant
+ * (`packed_attention` with `query_is_first_token`), the gradients
+ * (`_varlen_attention_backward`) and the scatter back to the padded grid.
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * - Pointers without the `h_` prefix are DEVICE memory owned by the caller. The
+ *   library never allocates or frees memory; scratch space comes from the
+ *   caller's `workspace`, sized by the matching *_workspace_size call.
+ * - Every device pointer must be 16-byte aligned. Outputs must not alias inputs.
+ * - Token tensors are row-major [N, H, d]: token, then head, then head_dim,
+ *   contiguous (the layout of a [tokens, heads, head_dim] tensor).
+ * - cu_seqlens is int32 [B+1], cu[0] = 0, cu[b+1] = cu[b] + L_b, cu[B] = N.
+ * - `stream` is a hipStream_t passed as void* (NULL = the default stream). All
+ *   work is enqueued on it. Only pe_pack waits on the host (once, to read the
+ *   token count); every other call is asynchronous and launches no more work
+ *   than its host arguments fix, so it may be captured in a HIP graph.
+ * - Host arguments are validated before anything is launched; a call that
+ *   returns an error has enqueued nothing (except PE_ERR_CAPACITY and
+ *   PE_ERR_LENGTHS from pe_pack, described there). PE_ERR_HIP means a HIP
+ *   runtime call or launch failed.
+ * - The attention calls do not validate device contents: cu_seqlens must be
+ *   non-decreasing from 0 to N with every length in [1, max_seq_len], as
+ *   pe_pack produces it. Anything else is undefined behaviour.
+ * - dtype PE_FP32 computes in fp32 throughout (the GiGL page runs its kernel in
+ *   fp32 because inference needs it). PE_BF16 reads and writes bf16 and
+ *   accumulates in fp32; the probabilities are rounded to bf16 before they
+ *   multiply V. Log-sum-exp values are always fp32.
+ * - Supported head_dim: 8, 16, 32, 64, 128 (the GiGL page requires a multiple
+ *   of 8 for its aligned kernels).
+ */
+#ifndef PE_H
+#define PE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  PE_OK = 0,
+  PE_ERR_NULL = 1,        /* a required pointer is NULL */
+  PE_ERR_ARG = 2,         /* a size, count, alignment or the scale is invalid */
+  PE_ERR_UNSUPPORTED = 3, /* head_dim or dtype outside what the kernels support */
+  PE_ERR_LENGTHS = 4,     /* pe_pack found a length outside [1, max_seq_len] */
+  PE_ERR_CAPACITY = 5,    /* pe_pack: the token count exceeds `capacity` */
+  PE_ERR_WORKSPACE = 6,   /* workspace NULL or smaller than required */
+  PE_ERR_HIP = 7          /* a HIP runtime call or kernel launch failed */
+} pe_status;
+
+typedef enum { PE_FP32 = 0, PE_BF16 = 1 } pe_dtype;
+
+/* Human-readable name of a status code. Never NULL. */
+const char* pe_status_string(int status);
+
+/* Tile height (packed query or key rows per work item) of the attention kernels. */
+int32_t pe_attn_tile_rows(void);
+
+/* ------------------------------------------------------------------------ pack
+ * pe_pack: lengths -> cu_seqlens, flat_index and the packed rows of a grid.
+ *
+ * Source: GiGL module docstring, data flow diagram and "Example":
+ * `pack_sequences(lengths, max_seq_len)` returns `flat_index` and the offsets;
+ * `grid.flatten()[flat_index]` gathers the real tokens into a [num_tokens, dim]
+ * buffer; packing needs one host read, of the total token count.
+ *
+ *   cu[0] = 0, cu[b+1] = cu[b] + L_b,  N = cu[B]
+ *   flat_index[cu[b] + t] = b * max_seq_len + t            for t < L_b
+ *   packed[r, :] = grid[flat_index[r], :]                   (rows of row_elems)
+ *
+ * `grid` is [num_seqs * max_seq_len, row_elems], i.e. a padded
+ * [num_seqs, max_seq_len, row_elems] tensor; rows past a sequence's length are
+ * never read. The copy moves bits (element size from `dtype`: 4 or 2 bytes).
+ *
+ * Arguments
+ *   lengths      device int32 [num_seqs]; every length must lie in [1, max_seq_len]
+ *   grid         device, or NULL to compute only the layout (cu_seqlens, flat_index)
+ *   cu_seqlens   device int32 [num_seqs + 1], written
+ *   flat_index   device int64 [capacity], or NULL; rows [0, N) written
+ *   packed       device [capacity, row_elems], or NULL (must be NULL if grid is NULL)
+ *   h_total_tokens  HOST int64, receives N (also on PE_ERR_CAPACITY)
+ * Behaviour
+ *   One device-to-host read of N and of a length-error flag; this is the only
+ *   host wait in the library. If any length is outside [1, max_seq_len] it
+ *   returns PE_ERR_LENGTHS after the read (cu_seqlens holds the running sum of
+ *   the given values; nothing else written). If N exceeds INT32_MAX it returns
+ *   PE_ERR_ARG. If N > capacity it returns PE_ERR_CAPACITY with
+ *   *h_total_tokens = N: cu_seqlens is valid, flat_index and packed untouched;
+ *   the caller may allocate N rows and call again.
+ */
+size_t pe_pack_workspace_size(int32_t num_seqs, int32_t max_seq_len, int64_t row_elems, pe_dtype dtype);
+pe_status pe_pack(const int32_t* lengths, int32_t num_seqs, int32_t max_seq_len,
+                  const void* grid, int64_t row_elems, pe_dtype dtype,
+                  int32_t* cu_seqlens, int64_t* flat_index, void* packed, int64_t capacity,
+                  int64_t* h_total_tokens, void* workspace, size_t workspace_bytes, void* stream);
+
+/* -------------------------------------------------------------------- unpack
+ * pe_unpack: packed rows -> padded grid, the inverse of the gather.
+ *
+ * Source: GiGL data flow diagram (the padded interface around the packed
+ * buffer) and `_padded_packed_attention`, which scatters packed rows back into a
+ * [num_sequences, max_seq_len] grid and fills the rest from `zeros_like`.
+ *
+ *   grid[b, t, :] = packed[cu[b] + t, :]   for t < L_b
+ *   grid[b, t, :] = +0.0                   for L_b <= t < max_seq_len
+ *
+ * Arguments
+ *   packed       device [total_tokens, row_elems]
+ *   cu_seqlens   device int32 [num_seqs + 1]
+ *   grid         device [num_seqs * max_seq_len, row_elems], every element written
+ * A bit copy; no workspace; asynchronous.
+ */
+pe_status pe_unpack(const void* packed, const int32_t* cu_seqlens, int32_t num_seqs,
+                    int32_t max_seq_len, int64_t total_tokens, int64_t row_elems, pe_dtype dtype,
+                    void* grid, void* stream);
+
+/* ----------------------------------------------------------------- work list
+ * pe_worklist: cu_seqlens -> the attention kernels' work items.
+ *
+ * The packed rows are cut into tiles of `tile_rows` consecutive rows, so a
+ * launch mixes ~30-token queries and multi-thousand-token documents (the
+ * packed-encoders README, "Why packing?", on contrastive batches that mix
+ * both) without padding any sequence to a tile. Item t covers rows
+ * [t*R, min((t+1)*R, N)); its keys are those of every sequence the tile
+ * touches. items[t] is the sequence holding row t*R (cu[b] <= t*R < cu[b+1]);
+ * items[T] = num_seqs closes the list, T = ceil(N / R).
+ *
+ *   items   device int32 [ceil(total_tokens / tile_rows) + 1], written
+ * Asynchronous. The attention calls run this themselves in their workspace;
+ * it is exported so it can be checked and reused.
+ */
+pe_status pe_worklist(const int32_t* cu_seqlens, int32_t num_seqs, int64_t total_tokens,
+                      int32_t tile_rows, int32_t* items, void* stream);
+
+/* ------------------------------------------------------------------- forward
+ * pe_varlen_attn_fwd: non-causal attention within each packed sequence.
+ *
+ * Source: GiGL `_varlen_attention` ("query sequence i attends to key sequence
+ * i"; offsets read on the device, length bounds as host ints, no host sync) and
+ * `_varlen_attention_op` (output plus log-sum-exp, the latter computed only when
+ * a gradient will be needed). For sequence b, head h, query row i in it:
+ *
+ *   s_j   = softmax_scale * <q[i,h,:], k[j,h,:]>   for j in [cu[b], cu[b+1])
+ *   out[i,h,:] = sum_j exp(s_j - m) v[j,h,:] / sum_j exp(s_j - m),  m = max_j s_j
+ *   lse[h, i]  = m + ln(sum_j exp(s_j - m))        (natural log, fp32)
+ *
+ * Arguments
+ *   q, k, v      device [total_tokens, num_heads, head_dim] of `dtype`
+ *   out          device [total_tokens, num_heads, head_dim] of `dtype`
+ *   lse          device fp32 [num_heads, total_tokens], or NULL to skip it
+ *   max_seq_len  upper bound on every length (host int, as the GiGL call takes)
+ *   softmax_scale  finite and > 0; the GiGL call uses the SDPA default 1/sqrt(d)
+ *   workspace    device, at least pe_attn_workspace_size(..., for_backward=0)
+ */
+size_t pe_attn_workspace_size(int32_t num_seqs, int64_t total_tokens, int32_t num_heads,
+                              int32_t head_dim, pe_dtype dtype, int for_backward);
+pe_status pe_varlen_attn_fwd(const void* q, const void* k, const void* v, const int32_t* cu_seqlens,
+                             int32_t num_seqs, int64_t total_tokens, int32_t max_seq_len,
+                             int32_t num_heads, int32_t head_dim, pe_dtype dtype, float softmax_scale,
+                             void* out, float* lse, void* workspace, size_t workspace_bytes, void* stream);
+
+/* --------------------------------------------------------- first-token query
+ * pe_varlen_attn_fwd_first_token: one query per sequence, its first token.
+ *
+ * Source: GiGL `packed_attention` with `query_is_first_token` (the caller
+ * passes `query[cu_seqlens[:-1]]`; each sequence's single query attends over
+ * all its keys; "all the anchor readout of the last layer needs"). The result
+ * equals rows cu[:-1] of pe_varlen_attn_fwd.
+ *
+ *   q_first      device [num_seqs, num_heads, head_dim]
+ *   k, v         device [total_tokens, num_heads, head_dim]
+ *   out_first    device [num_seqs, num_heads, head_dim]
+ *   lse_first    device fp32 [num_heads, num_seqs], or NULL
+ * No workspace; asynchronous.
+ */
+pe_status pe_varlen_attn_fwd_first_token(const void* q_first, const void* k, const void* v,
+                                         const int32_t* cu_seqlens, int32_t num_seqs,
+                                         int64_t total_tokens, int32_t max_seq_len, int32_t num_heads,
+                                         int32_t head_dim, pe_dtype dtype, float softmax_scale,
+                                         void* out_first, float* lse_first, void* stream);
+
+/* ------------------------------------------------------------------ backward
+ * pe_varlen_attn_bwd: gradients of pe_varlen_attn_fwd in q, k and v.
+ *
+ * Source: GiGL `_varlen_attention_backward` (gradients in query, key and value
+ * from grad_output, the inputs, the output and the log-sum-exp; the gradient of
+ * the log-sum-exp is dropped). Recomputes the probabilities from `lse`:
+ *
+ *   P_ij = exp(s_ij - lse_i)   D_i = <dout_i, out_i>   dS_ij = P_ij (<dout_i, v_j> - D_i)
+ *   dv_j = sum_i P_ij dout_i   dq_i = scale sum_j dS_ij k_j   dk_j = scale sum_i dS_ij q_i
+ *
+ * Arguments
+ *   dout, q, k, v, out   device [total_tokens, num_heads, head_dim] of `dtype`
+ *   lse                  device fp32 [num_heads, total_tokens] from the forward
+ *   dq, dk, dv           device [total_tokens, num_heads, head_dim] of `dtype`, written
+ *   workspace            at least pe_attn_workspace_size(..., for_backward=1)
+ * Deterministic: no floating-point atomics; the same inputs give the same bits.
+ */
+pe_status pe_varlen_attn_bwd(const void* dout, const void* q, const void* k, const void* v,
+                             const void* out, const float* lse, const int32_t* cu_seqlens,
+                             int32_t num_seqs, int64_t total_tokens, int32_t max_seq_len,
+                             int32_t num_heads, int32_t head_dim, pe_dtype dtype, float softmax_scale,
+                             void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
+                             void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PE_H */

@@ -1,0 +1,226 @@
+// C ABI of the packed-attention library: argument validation, workspace
+// layout, and the launch sequence of every call. See include/pe.h.
+#include <hip/hip_runtime.h>
+
+#include <climits>
+#include <cmath>
+#include <cstdint>
+
+#include "kernels.h"
+#include "pe.h"
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool supported_head_dim(int32_t d) { return d == 8 || d == 16 || d == 32 || d == 64 || d == 128; }
+
+bool valid_dtype(int dt) { return dt == PE_FP32 || dt == PE_BF16; }
+
+int64_t elem_bytes(pe_dtype dt) { return dt == PE_BF16 ? 2 : 4; }
+
+hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
+
+pe_status hip_status(hipError_t e) { return e == hipSuccess ? PE_OK : PE_ERR_HIP; }
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+size_t items_bytes(int64_t total_tokens) {
+  return round_up(static_cast<size_t>(ceil_div(total_tokens, pe::kAttnTileRows) + 1) * sizeof(int32_t));
+}
+
+// Checks shared by the attention calls.
+pe_status check_attn_args(int32_t num_seqs, int64_t total_tokens, int32_t max_seq_len, int32_t num_heads,
+                          int32_t head_dim, int dtype, float scale) {
+  if (num_seqs < 1 || max_seq_len < 1 || num_heads < 1) return PE_ERR_ARG;
+  if (total_tokens < num_seqs || total_tokens > INT32_MAX) return PE_ERR_ARG;
+  if (total_tokens > static_cast<int64_t>(num_seqs) * max_seq_len) return PE_ERR_ARG;
+  if (!valid_dtype(dtype) || !supported_head_dim(head_dim)) return PE_ERR_UNSUPPORTED;
+  if (!(std::isfinite(scale) && scale > 0.f)) return PE_ERR_ARG;
+  if (ceil_div(total_tokens, pe::kAttnTileRows) * num_heads > INT32_MAX) return PE_ERR_ARG;
+  if (static_cast<int64_t>(num_heads) * head_dim > (1 << 16)) return PE_ERR_UNSUPPORTED;
+  return PE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* pe_status_string(int status) {
+  switch (status) {
+    case PE_OK: return "PE_OK";
+    case PE_ERR_NULL: return "PE_ERR_NULL: a required pointer is NULL";
+    case PE_ERR_ARG: return "PE_ERR_ARG: invalid size, count, alignment or scale";
+    case PE_ERR_UNSUPPORTED: return "PE_ERR_UNSUPPORTED: head_dim or dtype not supported";
+    case PE_ERR_LENGTHS: return "PE_ERR_LENGTHS: a sequence length lies outside [1, max_seq_len]";
+    case PE_ERR_CAPACITY: return "PE_ERR_CAPACITY: token count exceeds the output capacity";
+    case PE_ERR_WORKSPACE: return "PE_ERR_WORKSPACE: workspace missing or too small";
+    case PE_ERR_HIP: return "PE_ERR_HIP: a HIP runtime call or kernel launch failed";
+    default: return "unknown pe_status";
+  }
+}
+
+int32_t pe_attn_tile_rows(void) { return pe::kAttnTileRows; }
+
+// ------------------------------------------------------------------------ pack
+
+size_t pe_pack_workspace_size(int32_t num_seqs, int32_t max_seq_len, int64_t row_elems, pe_dtype dtype) {
+  if (num_seqs < 1 || max_seq_len < 1) return 0;
+  const int64_t rowbytes = (row_elems > 0 ? row_elems : 1) * elem_bytes(dtype);
+  const int64_t R = pe::pack_tile_rows(rowbytes);
+  const int64_t max_rows = static_cast<int64_t>(num_seqs) * max_seq_len;
+  return kAlign + round_up(static_cast<size_t>(ceil_div(max_rows, R) + 1) * sizeof(int32_t));
+}
+
+pe_status pe_pack(const int32_t* lengths, int32_t num_seqs, int32_t max_seq_len, const void* grid,
+                  int64_t row_elems, pe_dtype dtype, int32_t* cu_seqlens, int64_t* flat_index,
+                  void* packed, int64_t capacity, int64_t* h_total_tokens, void* workspace,
+                  size_t workspace_bytes, void* stream) {
+  if (!lengths || !cu_seqlens || !h_total_tokens) return PE_ERR_NULL;
+  if (grid && !packed) return PE_ERR_NULL;
+  if (!grid && packed) return PE_ERR_ARG;
+  if (num_seqs < 1 || max_seq_len < 1 || capacity < 0) return PE_ERR_ARG;
+  if (!valid_dtype(dtype)) return PE_ERR_UNSUPPORTED;
+  if (grid && row_elems < 1) return PE_ERR_ARG;
+  for (const void* p : {static_cast<const void*>(lengths), static_cast<const void*>(cu_seqlens),
+                        static_cast<const void*>(flat_index), grid, static_cast<const void*>(packed),
+                        static_cast<const void*>(workspace)})
+    if (p && !aligned16(p)) return PE_ERR_ARG;
+  if (!workspace || workspace_bytes < pe_pack_workspace_size(num_seqs, max_seq_len, row_elems, dtype))
+    return PE_ERR_WORKSPACE;
+
+  hipStream_t st = as_stream(stream);
+  int64_t* result = static_cast<int64_t*>(workspace);
+  int32_t* items = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + kAlign);
+  hipError_t e = pe::launch_scan(lengths, num_seqs, max_seq_len, cu_seqlens, result, st);
+  if (e != hipSuccess) return PE_ERR_HIP;
+  // The one host read of the library: the token count and the length-error flag.
+  int64_t host[2] = {0, 0};
+  e = hipMemcpyAsync(host, result, sizeof(host), hipMemcpyDeviceToHost, st);
+  if (e == hipSuccess) e = hipStreamSynchronize(st);
+  if (e != hipSuccess) return PE_ERR_HIP;
+  *h_total_tokens = host[0];
+  if (host[1] != 0) return PE_ERR_LENGTHS;
+  const int64_t N = host[0];
+  if (N > INT32_MAX) return PE_ERR_ARG;
+  if (!flat_index && !packed) return PE_OK;
+  if (N > capacity) return PE_ERR_CAPACITY;
+  const int64_t rowbytes = (packed ? row_elems : 1) * elem_bytes(dtype);
+  const int32_t R = pe::pack_tile_rows(packed ? rowbytes : 64);
+  e = pe::launch_worklist(cu_seqlens, num_seqs, N, R, items, st);
+  if (e != hipSuccess) return PE_ERR_HIP;
+  e = pe::launch_pack_rows(grid, packed, flat_index, cu_seqlens, items, num_seqs, max_seq_len, rowbytes, N,
+                           R, st);
+  return hip_status(e);
+}
+
+// -------------------------------------------------------------------- unpack
+
+pe_status pe_unpack(const void* packed, const int32_t* cu_seqlens, int32_t num_seqs, int32_t max_seq_len,
+                    int64_t total_tokens, int64_t row_elems, pe_dtype dtype, void* grid, void* stream) {
+  if (!packed || !cu_seqlens || !grid) return PE_ERR_NULL;
+  if (num_seqs < 1 || max_seq_len < 1 || row_elems < 1) return PE_ERR_ARG;
+  if (total_tokens < num_seqs || total_tokens > INT32_MAX ||
+      total_tokens > static_cast<int64_t>(num_seqs) * max_seq_len)
+    return PE_ERR_ARG;
+  if (!valid_dtype(dtype)) return PE_ERR_UNSUPPORTED;
+  if (!aligned16(packed) || !aligned16(cu_seqlens) || !aligned16(grid)) return PE_ERR_ARG;
+  return hip_status(pe::launch_unpack_rows(packed, grid, cu_seqlens, num_seqs, max_seq_len,
+                                           row_elems * elem_bytes(dtype), as_stream(stream)));
+}
+
+// ----------------------------------------------------------------- work list
+
+pe_status pe_worklist(const int32_t* cu_seqlens, int32_t num_seqs, int64_t total_tokens, int32_t tile_rows,
+                      int32_t* items, void* stream) {
+  if (!cu_seqlens || !items) return PE_ERR_NULL;
+  if (num_seqs < 1 || tile_rows < 1 || total_tokens < num_seqs || total_tokens > INT32_MAX) return PE_ERR_ARG;
+  return hip_status(pe::launch_worklist(cu_seqlens, num_seqs, total_tokens, tile_rows, items,
+                                        as_stream(stream)));
+}
+
+// ------------------------------------------------------------------- forward
+
+size_t pe_attn_workspace_size(int32_t num_seqs, int64_t total_tokens, int32_t num_heads, int32_t head_dim,
+                              pe_dtype dtype, int for_backward) {
+  (void)num_seqs;
+  (void)head_dim;
+  (void)dtype;
+  if (total_tokens < 0 || num_heads < 1) return 0;
+  size_t s = items_bytes(total_tokens);
+  if (for_backward) s += round_up(static_cast<size_t>(total_tokens) * num_heads * sizeof(float));
+  return s;
+}
+
+pe_status pe_varlen_attn_fwd(const void* q, const void* k, const void* v, const int32_t* cu_seqlens,
+                             int32_t num_seqs, int64_t total_tokens, int32_t max_seq_len, int32_t num_heads,
+                             int32_t head_dim, pe_dtype dtype, float softmax_scale, void* out, float* lse,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+  if (!q || !k || !v || !cu_seqlens || !out) return PE_ERR_NULL;
+  const pe_status s =
+      check_attn_args(num_seqs, total_tokens, max_seq_len, num_heads, head_dim, dtype, softmax_scale);
+  if (s != PE_OK) return s;
+  for (const void* p : {q, k, v, static_cast<const void*>(cu_seqlens), static_cast<const void*>(out),
+                        static_cast<const void*>(lse), static_cast<const void*>(workspace)})
+    if (p && !aligned16(p)) return PE_ERR_ARG;
+  if (!workspace || workspace_bytes < pe_attn_workspace_size(num_seqs, total_tokens, num_heads, head_dim, dtype, 0))
+    return PE_ERR_WORKSPACE;
+  hipStream_t st = as_stream(stream);
+  int32_t* items = static_cast<int32_t*>(workspace);
+  hipError_t e = pe::launch_worklist(cu_seqlens, num_seqs, total_tokens, pe::kAttnTileRows, items, st);
+  if (e != hipSuccess) return PE_ERR_HIP;
+  e = pe::launch_attn_fwd(dtype == PE_BF16, head_dim, q, k, v, cu_seqlens, items, num_seqs,
+                          static_cast<int32_t>(total_tokens), num_heads, softmax_scale, out, lse, st);
+  return hip_status(e);
+}
+
+pe_status pe_varlen_attn_fwd_first_token(const void* q_first, const void* k, const void* v,
+                                         const int32_t* cu_seqlens, int32_t num_seqs, int64_t total_tokens,
+                                         int32_t max_seq_len, int32_t num_heads, int32_t head_dim,
+                                         pe_dtype dtype, float softmax_scale, void* out_first, float* lse_first,
+                                         void* stream) {
+  if (!q_first || !k || !v || !cu_seqlens || !out_first) return PE_ERR_NULL;
+  const pe_status s =
+      check_attn_args(num_seqs, total_tokens, max_seq_len, num_heads, head_dim, dtype, softmax_scale);
+  if (s != PE_OK) return s;
+  for (const void* p : {q_first, k, v, static_cast<const void*>(cu_seqlens), static_cast<const void*>(out_first),
+                        static_cast<const void*>(lse_first)})
+    if (p && !aligned16(p)) return PE_ERR_ARG;
+  return hip_status(pe::launch_attn_fwd_first(dtype == PE_BF16, head_dim, q_first, k, v, cu_seqlens, num_seqs,
+                                              static_cast<int32_t>(total_tokens), num_heads, softmax_scale,
+                                              out_first, lse_first, as_stream(stream)));
+}
+
+// ------------------------------------------------------------------ backward
+
+pe_status pe_varlen_attn_bwd(const void* dout, const void* q, const void* k, const void* v, const void* out,
+                             const float* lse, const int32_t* cu_seqlens, int32_t num_seqs, int64_t total_tokens,
+                             int32_t max_seq_len, int32_t num_heads, int32_t head_dim, pe_dtype dtype,
+                             float softmax_scale, void* dq, void* dk, void* dv, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  if (!dout || !q || !k || !v || !out || !lse || !cu_seqlens || !dq || !dk || !dv) return PE_ERR_NULL;
+  const pe_status s =
+      check_attn_args(num_seqs, total_tokens, max_seq_len, num_heads, head_dim, dtype, softmax_scale);
+  if (s != PE_OK) return s;
+  for (const void* p : {dout, q, k, v, out, static_cast<const void*>(lse), static_cast<const void*>(cu_seqlens),
+                        static_cast<const void*>(dq), static_cast<const void*>(dk), static_cast<const void*>(dv),
+                        static_cast<const void*>(workspace)})
+    if (p && !aligned16(p)) return PE_ERR_ARG;
+  if (!workspace || workspace_bytes < pe_attn_workspace_size(num_seqs, total_tokens, num_heads, head_dim, dtype, 1))
+    return PE_ERR_WORKSPACE;
+  hipStream_t st = as_stream(stream);
+  int32_t* items = static_cast<int32_t*>(workspace);
+  float* delta = reinterpret_cast<float*>(static_cast<char*>(workspace) + items_bytes(total_tokens));
+  hipError_t e = pe::launch_worklist(cu_seqlens, num_seqs, total_tokens, pe::kAttnTileRows, items, st);
+  if (e != hipSuccess) return PE_ERR_HIP;
+  e = pe::launch_attn_bwd(dtype == PE_BF16, head_dim, dout, q, k, v, out, lse, cu_seqlens, items, num_seqs,
+                          static_cast<int32_t>(total_tokens), num_heads, softmax_scale, dq, dk, dv, delta, st);
+  if (e == hipErrorNotSupported) return PE_ERR_UNSUPPORTED;
+  return hip_status(e);
+}
+
+}  // extern "C"

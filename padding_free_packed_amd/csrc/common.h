@@ -1,0 +1,59 @@
+// Shared device helpers for the gfx950 kernels: vector types, bf16 bit
+// conversions, wave reductions and the XCD-aware block mapping.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pe {
+
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef uint16_t u16x8 __attribute__((ext_vector_type(8)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+// Finite stand-in for minus infinity as the running maximum, so that
+// exp2(m_old - m_new) never evaluates inf - inf.
+constexpr float kNegBig = -1.0e30f;
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// Round to nearest, ties to even (the hardware conversion on gfx950).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  __bf16 h = static_cast<__bf16>(f);
+  return __builtin_bit_cast(uint16_t, h);
+}
+
+__device__ __forceinline__ float wave_max32(float x) {
+  // maximum over the 32 lanes of each half wave
+#pragma unroll
+  for (int o = 1; o < 32; o <<= 1) x = fmaxf(x, __shfl_xor(x, o));
+  return x;
+}
+
+__device__ __forceinline__ int wave_min_i(int x) {
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) x = min(x, __shfl_xor(x, o));
+  return x;
+}
+
+__device__ __forceinline__ int wave_max_i(int x) {
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) x = max(x, __shfl_xor(x, o));
+  return x;
+}
+
+// Workgroups of one launch are handed to the 8 XCDs in round-robin order of
+// their block index. This remaps block indices so that XCD x receives one
+// contiguous range of logical work items; neighbouring items (the tiles of one
+// sequence and head) then share that XCD's L2.
+__device__ __forceinline__ int xcd_remap(int bid, int nblocks) {
+  const int x = bid & 7, i = bid >> 3;
+  const int per = nblocks >> 3, rem = nblocks & 7;
+  return x * per + min(x, rem) + i;
+}
+
+}  // namespace pe

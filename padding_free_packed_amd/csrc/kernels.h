@@ -1,0 +1,37 @@
+// Internal launch functions of the HIP kernels (not part of the C ABI).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pe {
+
+// packed query (or key) rows per attention work item
+constexpr int kAttnTileRows = 128;
+
+hipError_t launch_scan(const int32_t* lengths, int32_t B, int32_t S, int32_t* cu, int64_t* result,
+                       hipStream_t stream);
+hipError_t launch_worklist(const int32_t* cu, int32_t B, int64_t N, int32_t R, int32_t* items,
+                           hipStream_t stream);
+int32_t pack_tile_rows(int64_t rowbytes);
+hipError_t launch_pack_rows(const void* grid, void* packed, int64_t* flat_index, const int32_t* cu,
+                            const int32_t* items, int32_t B, int32_t S, int64_t rowbytes, int64_t N,
+                            int32_t R, hipStream_t stream);
+hipError_t launch_unpack_rows(const void* packed, void* grid, const int32_t* cu, int32_t B, int32_t S,
+                              int64_t rowbytes, hipStream_t stream);
+
+// Forward over tiles of kAttnTileRows packed query rows; items from launch_worklist.
+hipError_t launch_attn_fwd(bool bf16, int D, const void* q, const void* k, const void* v,
+                           const int32_t* cu, const int32_t* items, int32_t B, int32_t N, int32_t H,
+                           float scale, void* out, float* lse, hipStream_t stream);
+
+hipError_t launch_attn_fwd_first(bool bf16, int D, const void* q_first, const void* k, const void* v,
+                                 const int32_t* cu, int32_t B, int32_t N, int32_t H, float scale,
+                                 void* out_first, float* lse_first, hipStream_t stream);
+
+// Backward: D = rowsum(dO * O) per (head, row), then dK/dV over key tiles, then dQ over query tiles.
+hipError_t launch_attn_bwd(bool bf16, int D, const void* dout, const void* q, const void* k,
+                           const void* v, const void* out, const float* lse, const int32_t* cu,
+                           const int32_t* items, int32_t B, int32_t N, int32_t H, float scale,
+                           void* dq, void* dk, void* dv, float* delta, hipStream_t stream);
+
+}  // namespace pe

@@ -1,0 +1,236 @@
+// Packing kernels: lengths -> offsets (one workgroup scan), the tile work list,
+// the row gather from the padded grid into the packed buffer (with flat_index),
+// and the scatter back to the padded grid with zero fill.
+//
+// The gather of sequence b is one contiguous byte range in both buffers
+// (grid rows b*S .. b*S+L_b-1 go to packed rows cu[b] .. cu[b+1]-1), so both
+// copies are streams of contiguous segments. Work is split by bytes of the
+// OUTPUT, evenly, so that one 8192-token document and many 30-token queries
+// cost the same per byte.
+#include "common.h"
+#include "kernels.h"
+
+namespace pe {
+
+// ---------------------------------------------------------------- scan
+// One workgroup of 1024 threads; each pass scans 8192 lengths (8 per thread)
+// and carries the running total in int64. Writes cu[0..B], result[0] = total
+// token count (int64), result[1] = 1 if any length lies outside [1, S].
+constexpr int kScanThreads = 1024;
+constexpr int kScanPer = 8;
+
+__global__ __launch_bounds__(kScanThreads) void scan_lengths_kernel(
+    const int32_t* __restrict__ lengths, int32_t B, int32_t S, int32_t* __restrict__ cu,
+    int64_t* __restrict__ result) {
+  __shared__ int64_t wsum[kScanThreads / 64];
+  __shared__ int bad_any;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  if (tid == 0) { cu[0] = 0; bad_any = 0; }
+  int bad = 0;
+  int64_t carry = 0;
+  for (int64_t base = 0; base < B; base += kScanThreads * kScanPer) {
+    int64_t v[kScanPer];
+    int64_t local = 0;
+#pragma unroll
+    for (int j = 0; j < kScanPer; ++j) {
+      const int64_t idx = base + static_cast<int64_t>(tid) * kScanPer + j;
+      int64_t L = 0;
+      if (idx < B) {
+        L = lengths[idx];
+        bad |= (L < 1) | (L > S);
+      }
+      local += L;
+      v[j] = local;  // inclusive within the thread
+    }
+    // inclusive scan of `local` across the wave
+    int64_t incl = local;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int64_t up = __shfl_up(incl, o);
+      if (lane >= o) incl += up;
+    }
+    if (lane == 63) wsum[wv] = incl;
+    __syncthreads();
+    int64_t wprefix = 0, total = 0;
+#pragma unroll
+    for (int w = 0; w < kScanThreads / 64; ++w) {
+      const int64_t s = wsum[w];
+      if (w < wv) wprefix += s;
+      total += s;
+    }
+    const int64_t excl = carry + wprefix + incl - local;
+#pragma unroll
+    for (int j = 0; j < kScanPer; ++j) {
+      const int64_t idx = base + static_cast<int64_t>(tid) * kScanPer + j;
+      if (idx < B) cu[idx + 1] = static_cast<int32_t>(excl + v[j]);
+    }
+    carry += total;
+    __syncthreads();  // wsum is rewritten by the next pass
+  }
+  if (bad) atomicOr(&bad_any, 1);
+  __syncthreads();
+  if (tid == 0) {
+    result[0] = carry;
+    result[1] = bad_any;
+  }
+}
+
+// ---------------------------------------------------------------- work list
+// items[t] = b with cu[b] <= t*R < cu[b+1]; items[T] = B. One thread per
+// sequence writes the entries of the tiles that start inside it.
+__global__ void worklist_kernel(const int32_t* __restrict__ cu, int32_t B, int64_t N, int32_t R,
+                                int32_t* __restrict__ items) {
+  const int64_t T = (N + R - 1) / R;
+  const int64_t b = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (b == 0) items[T] = B;
+  if (b >= B) return;
+  const int64_t c0 = cu[b], c1 = cu[b + 1];
+  int64_t t = (c0 + R - 1) / R;
+  const int64_t tend = min((c1 + R - 1) / R, T);
+  for (; t < tend; ++t) items[t] = static_cast<int32_t>(b);
+}
+
+// ---------------------------------------------------------------- segment copy
+template <typename U>
+__device__ __forceinline__ void copy_units(const U* __restrict__ src, U* __restrict__ dst, int64_t n) {
+  int64_t i = threadIdx.x;
+  constexpr int BS = 256;
+  for (; i + 3 * BS < n; i += 4 * BS) {
+    const U a = src[i], b = src[i + BS], c = src[i + 2 * BS], d = src[i + 3 * BS];
+    dst[i] = a;
+    dst[i + BS] = b;
+    dst[i + 2 * BS] = c;
+    dst[i + 3 * BS] = d;
+  }
+  for (; i < n; i += BS) dst[i] = src[i];
+}
+
+template <typename U>
+__device__ __forceinline__ void zero_units(U* __restrict__ dst, int64_t n) {
+  U z;
+  __builtin_memset(&z, 0, sizeof(U));
+  for (int64_t i = threadIdx.x; i < n; i += 256) dst[i] = z;
+}
+
+// Block w packs rows [w*R, min((w+1)*R, N)) of the packed buffer. items[w] is
+// the sequence of its first row (work list with tile height R).
+template <typename U>
+__global__ __launch_bounds__(256) void pack_rows_kernel(
+    const char* __restrict__ grid, char* __restrict__ packed, int64_t* __restrict__ flat_index,
+    const int32_t* __restrict__ cu, const int32_t* __restrict__ items, int32_t B, int32_t S,
+    int64_t rowbytes, int64_t N, int32_t R) {
+  const int64_t r0 = static_cast<int64_t>(blockIdx.x) * R;
+  const int64_t r1 = min(r0 + R, N);
+  int b = items[blockIdx.x];
+  while (b < B) {
+    const int64_t c0 = cu[b], c1 = cu[b + 1];
+    const int64_t s0 = max(c0, r0), s1 = min(c1, r1);
+    if (s0 < s1) {
+      if (flat_index) {
+        const int64_t base = static_cast<int64_t>(b) * S - c0;
+        for (int64_t r = s0 + threadIdx.x; r < s1; r += 256) flat_index[r] = base + r;
+      }
+      if (packed) {
+        const char* src = grid + (static_cast<int64_t>(b) * S + (s0 - c0)) * rowbytes;
+        char* dst = packed + s0 * rowbytes;
+        copy_units(reinterpret_cast<const U*>(src), reinterpret_cast<U*>(dst),
+                   (s1 - s0) * rowbytes / static_cast<int64_t>(sizeof(U)));
+      }
+    }
+    if (c1 >= r1) break;
+    ++b;
+  }
+}
+
+// Block w writes grid rows [w*R, min((w+1)*R, B*S)).
+template <typename U>
+__global__ __launch_bounds__(256) void unpack_rows_kernel(
+    const char* __restrict__ packed, char* __restrict__ grid, const int32_t* __restrict__ cu,
+    int32_t B, int32_t S, int64_t rowbytes, int64_t R) {
+  const int64_t g0 = static_cast<int64_t>(blockIdx.x) * R;
+  const int64_t g1 = min(g0 + R, static_cast<int64_t>(B) * S);
+  for (int64_t b = g0 / S; b < B && b * S < g1; ++b) {
+    const int64_t base = b * S;
+    const int64_t c0 = cu[b];
+    const int64_t L = cu[b + 1] - c0;
+    const int64_t t0 = max(g0 - base, int64_t(0)), t1 = min(g1 - base, static_cast<int64_t>(S));
+    const int64_t tc = min(t1, L);
+    constexpr int64_t us = sizeof(U);
+    if (t0 < tc)
+      copy_units(reinterpret_cast<const U*>(packed + (c0 + t0) * rowbytes),
+                 reinterpret_cast<U*>(grid + (base + t0) * rowbytes), (tc - t0) * rowbytes / us);
+    const int64_t tz = max(t0, L);
+    if (tz < t1) zero_units(reinterpret_cast<U*>(grid + (base + tz) * rowbytes), (t1 - tz) * rowbytes / us);
+  }
+}
+
+// ---------------------------------------------------------------- launchers
+
+hipError_t launch_scan(const int32_t* lengths, int32_t B, int32_t S, int32_t* cu, int64_t* result,
+                       hipStream_t stream) {
+  hipLaunchKernelGGL(scan_lengths_kernel, dim3(1), dim3(kScanThreads), 0, stream, lengths, B, S, cu,
+                     result);
+  return hipGetLastError();
+}
+
+hipError_t launch_worklist(const int32_t* cu, int32_t B, int64_t N, int32_t R, int32_t* items,
+                           hipStream_t stream) {
+  const int threads = 256;
+  const int blocks = static_cast<int>((static_cast<int64_t>(B) + threads - 1) / threads);
+  hipLaunchKernelGGL(worklist_kernel, dim3(blocks), dim3(threads), 0, stream, cu, B, N, R, items);
+  return hipGetLastError();
+}
+
+// Rows per copy block: about 32 KiB of output per block.
+int32_t pack_tile_rows(int64_t rowbytes) {
+  const int64_t r = (32 * 1024) / (rowbytes > 0 ? rowbytes : 1);
+  return static_cast<int32_t>(r < 1 ? 1 : (r > (1 << 20) ? (1 << 20) : r));
+}
+
+static int unit_bytes(int64_t rowbytes, const void* a, const void* b) {
+  const uintptr_t m = reinterpret_cast<uintptr_t>(a) | reinterpret_cast<uintptr_t>(b);
+  for (int u = 16; u > 1; u >>= 1)
+    if (rowbytes % u == 0 && (m % u) == 0) return u;
+  return 1;
+}
+
+hipError_t launch_pack_rows(const void* grid, void* packed, int64_t* flat_index, const int32_t* cu,
+                            const int32_t* items, int32_t B, int32_t S, int64_t rowbytes, int64_t N,
+                            int32_t R, hipStream_t stream) {
+  const int64_t blocks = (N + R - 1) / R;
+  if (blocks == 0) return hipSuccess;
+  const char* g = static_cast<const char*>(grid);
+  char* p = static_cast<char*>(packed);
+  const int u = packed ? unit_bytes(rowbytes, grid, packed) : 16;
+  const dim3 gd(static_cast<unsigned>(blocks)), bd(256);
+  switch (u) {
+    case 16: hipLaunchKernelGGL(pack_rows_kernel<uint4>, gd, bd, 0, stream, g, p, flat_index, cu, items, B, S, rowbytes, N, R); break;
+    case 8: hipLaunchKernelGGL(pack_rows_kernel<uint2>, gd, bd, 0, stream, g, p, flat_index, cu, items, B, S, rowbytes, N, R); break;
+    case 4: hipLaunchKernelGGL(pack_rows_kernel<uint32_t>, gd, bd, 0, stream, g, p, flat_index, cu, items, B, S, rowbytes, N, R); break;
+    case 2: hipLaunchKernelGGL(pack_rows_kernel<uint16_t>, gd, bd, 0, stream, g, p, flat_index, cu, items, B, S, rowbytes, N, R); break;
+    default: hipLaunchKernelGGL(pack_rows_kernel<uint8_t>, gd, bd, 0, stream, g, p, flat_index, cu, items, B, S, rowbytes, N, R); break;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_unpack_rows(const void* packed, void* grid, const int32_t* cu, int32_t B, int32_t S,
+                              int64_t rowbytes, hipStream_t stream) {
+  const int64_t R = pack_tile_rows(rowbytes);
+  const int64_t rows = static_cast<int64_t>(B) * S;
+  const int64_t blocks = (rows + R - 1) / R;
+  if (blocks == 0) return hipSuccess;
+  const char* p = static_cast<const char*>(packed);
+  char* g = static_cast<char*>(grid);
+  const int u = unit_bytes(rowbytes, packed, grid);
+  const dim3 gd(static_cast<unsigned>(blocks)), bd(256);
+  switch (u) {
+    case 16: hipLaunchKernelGGL(unpack_rows_kernel<uint4>, gd, bd, 0, stream, p, g, cu, B, S, rowbytes, R); break;
+    case 8: hipLaunchKernelGGL(unpack_rows_kernel<uint2>, gd, bd, 0, stream, p, g, cu, B, S, rowbytes, R); break;
+    case 4: hipLaunchKernelGGL(unpack_rows_kernel<uint32_t>, gd, bd, 0, stream, p, g, cu, B, S, rowbytes, R); break;
+    case 2: hipLaunchKernelGGL(unpack_rows_kernel<uint16_t>, gd, bd, 0, stream, p, g, cu, B, S, rowbytes, R); break;
+    default: hipLaunchKernelGGL(unpack_rows_kernel<uint8_t>, gd, bd, 0, stream, p, g, cu, B, S, rowbytes, R); break;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace pe

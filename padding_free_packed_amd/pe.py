@@ -1,0 +1,190 @@
+"""Python binding of ``libpe.so`` (include/pe.h): argument marshalling only.
+
+Each ``pe_*`` function takes torch tensors (device memory) and host ints, passes
+their pointers and the current HIP stream to the C function of the same name,
+and raises :class:`PeError` on any status other than ``PE_OK``. Every step of
+the computation runs in the library's HIP kernels; nothing here computes.
+
+Loading fails loudly if the library has not been built
+(``python -m padding_free_packed_amd.build``).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libpe.so")
+
+PE_OK, PE_ERR_NULL, PE_ERR_ARG, PE_ERR_UNSUPPORTED, PE_ERR_LENGTHS, PE_ERR_CAPACITY, \
+    PE_ERR_WORKSPACE, PE_ERR_HIP = range(8)
+PE_FP32, PE_BF16 = 0, 1
+
+EXPORTS = (
+    "pe_status_string", "pe_attn_tile_rows", "pe_pack_workspace_size", "pe_pack", "pe_unpack",
+    "pe_worklist", "pe_attn_workspace_size", "pe_varlen_attn_fwd", "pe_varlen_attn_fwd_first_token",
+    "pe_varlen_attn_bwd",
+)
+
+
+class PeError(RuntimeError):
+    def __init__(self, fn: str, status: int, total_tokens: int | None = None):
+        self.status = status
+        self.total_tokens = total_tokens
+        super().__init__(f"{fn}: {_lib.pe_status_string(status).decode()}")
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with `python -m padding_free_packed_amd.build`"
+                          " (or __graft_entry__.build()); there is no fallback path")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I32, I64, SZ, F = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_float
+    sig = {
+        "pe_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+        "pe_attn_tile_rows": (I32, []),
+        "pe_pack_workspace_size": (SZ, [I32, I32, I64, ctypes.c_int]),
+        "pe_pack": (ctypes.c_int, [P, I32, I32, P, I64, ctypes.c_int, P, P, P, I64, P, P, SZ, P]),
+        "pe_unpack": (ctypes.c_int, [P, P, I32, I32, I64, I64, ctypes.c_int, P, P]),
+        "pe_worklist": (ctypes.c_int, [P, I32, I64, I32, P, P]),
+        "pe_attn_workspace_size": (SZ, [I32, I64, I32, I32, ctypes.c_int, ctypes.c_int]),
+        "pe_varlen_attn_fwd": (ctypes.c_int, [P, P, P, P, I32, I64, I32, I32, I32, ctypes.c_int, F, P, P, P,
+                                               SZ, P]),
+        "pe_varlen_attn_fwd_first_token": (ctypes.c_int, [P, P, P, P, I32, I64, I32, I32, I32, ctypes.c_int,
+                                                           F, P, P, P]),
+        "pe_varlen_attn_bwd": (ctypes.c_int, [P, P, P, P, P, P, P, I32, I64, I32, I32, I32, ctypes.c_int, F,
+                                               P, P, P, P, SZ, P]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+_lib = _load()
+
+
+def library():
+    return _lib
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return PE_FP32
+    if t.dtype == torch.bfloat16:
+        return PE_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _check(fn, status, total=None):
+    if status != PE_OK:
+        raise PeError(fn, status, total)
+
+
+# ------------------------------------------------------------------ sizes
+
+def pe_attn_tile_rows() -> int:
+    return int(_lib.pe_attn_tile_rows())
+
+
+def pe_pack_workspace_size(num_seqs: int, max_seq_len: int, row_elems: int, dtype: int) -> int:
+    return int(_lib.pe_pack_workspace_size(num_seqs, max_seq_len, row_elems, dtype))
+
+
+def pe_attn_workspace_size(num_seqs: int, total_tokens: int, num_heads: int, head_dim: int, dtype: int,
+                           for_backward: bool) -> int:
+    return int(_lib.pe_attn_workspace_size(num_seqs, total_tokens, num_heads, head_dim, dtype,
+                                           int(for_backward)))
+
+
+# ------------------------------------------------------------------ calls
+
+def pe_pack(lengths, max_seq_len, grid, cu_seqlens, flat_index, packed, capacity, workspace,
+            dtype: int | None = None) -> int:
+    """Returns the token count N. Raises PeError (``.total_tokens`` set) on failure."""
+    if dtype is None:
+        dtype = _dtype_code(grid) if grid is not None else PE_FP32
+    row_elems = 0 if grid is None else grid.numel() // (lengths.numel() * max_seq_len)
+    n = ctypes.c_int64(0)
+    st = _lib.pe_pack(_ptr(lengths), lengths.numel(), max_seq_len, _ptr(grid), row_elems, dtype,
+                      _ptr(cu_seqlens), _ptr(flat_index), _ptr(packed), capacity, ctypes.byref(n),
+                      _ptr(workspace), 0 if workspace is None else workspace.numel(), _stream())
+    _check("pe_pack", st, n.value)
+    return n.value
+
+
+def pe_unpack(packed, cu_seqlens, num_seqs, max_seq_len, total_tokens, grid):
+    row_elems = packed.numel() // max(total_tokens, 1)
+    st = _lib.pe_unpack(_ptr(packed), _ptr(cu_seqlens), num_seqs, max_seq_len, total_tokens, row_elems,
+                        _dtype_code(packed), _ptr(grid), _stream())
+    _check("pe_unpack", st)
+
+
+def pe_worklist(cu_seqlens, num_seqs, total_tokens, tile_rows, items):
+    _check("pe_worklist", _lib.pe_worklist(_ptr(cu_seqlens), num_seqs, total_tokens, tile_rows,
+                                           _ptr(items), _stream()))
+
+
+def pe_varlen_attn_fwd(q, k, v, cu_seqlens, num_seqs, total_tokens, max_seq_len, softmax_scale, out,
+                       lse, workspace):
+    N, H, d = q.shape
+    st = _lib.pe_varlen_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens), num_seqs, total_tokens,
+                                 max_seq_len, H, d, _dtype_code(q), softmax_scale, _ptr(out), _ptr(lse),
+                                 _ptr(workspace), workspace.numel(), _stream())
+    _check("pe_varlen_attn_fwd", st)
+
+
+def pe_varlen_attn_fwd_first_token(q_first, k, v, cu_seqlens, num_seqs, total_tokens, max_seq_len,
+                                   softmax_scale, out_first, lse_first):
+    B, H, d = q_first.shape
+    st = _lib.pe_varlen_attn_fwd_first_token(_ptr(q_first), _ptr(k), _ptr(v), _ptr(cu_seqlens), num_seqs,
+                                             total_tokens, max_seq_len, H, d, _dtype_code(q_first),
+                                             softmax_scale, _ptr(out_first), _ptr(lse_first), _stream())
+    _check("pe_varlen_attn_fwd_first_token", st)
+
+
+def pe_varlen_attn_bwd(dout, q, k, v, out, lse, cu_seqlens, num_seqs, total_tokens, max_seq_len,
+                       softmax_scale, dq, dk, dv, workspace):
+    N, H, d = q.shape
+    st = _lib.pe_varlen_attn_bwd(_ptr(dout), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse),
+                                 _ptr(cu_seqlens), num_seqs, total_tokens, max_seq_len, H, d,
+                                 _dtype_code(q), softmax_scale, _ptr(dq), _ptr(dk), _ptr(dv),
+                                 _ptr(workspace), workspace.numel(), _stream())
+    _check("pe_varlen_attn_bwd", st)
+
+
+# ------------------------------------------------------------------ allocating helpers
+
+def workspace(nbytes: int, device) -> torch.Tensor:
+    return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+
+
+def pack(lengths, max_seq_len, grid=None, capacity=None):
+    """Layout (and packed rows) from device lengths; allocates outputs.
+
+    With ``capacity`` unknown, a first call computes the layout only; its token
+    count sizes the outputs of the second call.
+    """
+    dev = lengths.device
+    B = lengths.numel()
+    row_elems = 0 if grid is None else grid.numel() // (B * max_seq_len)
+    dt = _dtype_code(grid) if grid is not None else PE_FP32
+    ws = workspace(pe_pack_workspace_size(B, max_seq_len, max(row_elems, 1), dt), dev)
+    cu = torch.empty(B + 1, dtype=torch.int32, device=dev)
+    if capacity is None:
+        capacity = pe_pack(lengths, max_seq_len, None, cu, None, None, 0, ws, dt)
+    flat = torch.empty(capacity, dtype=torch.int64, device=dev)
+    packed = None if grid is None else torch.empty(capacity, row_elems, dtype=grid.dtype, device=dev)
+    n = pe_pack(lengths, max_seq_len, grid, cu, flat, packed, capacity, ws, dt)
+    return cu, flat[:n], (None if packed is None else packed[:n]), n

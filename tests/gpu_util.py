@@ -1,0 +1,99 @@
+"""Shared pieces of the GPU tests: moving workload arrays to the device and
+back, and the tolerance checks against the fp64 oracle.
+
+Tolerances (written here once, used by every parity test):
+* fp32: max |gpu - ref| <= 1e-5, and |gpu - ref| / |ref| <= 1e-4 wherever
+  |ref| >= 0.1 (below that the absolute bound governs);
+* bf16 in / fp32 accumulate: max |gpu - ref| <= 2e-2, and the cosine between
+  the GPU and oracle vectors of every token row (all heads and head dims of
+  that row) >= 0.999; rows whose norms are both < 1e-30 pass;
+* log-sum-exp (always fp32): |delta| <= 1e-5 * max(1, |lse|) for fp32 inputs,
+  |delta| <= 1e-3 for bf16 inputs;
+* integer and byte outputs: bit-exact.
+"""
+import sys
+
+import numpy as np
+import torch
+
+from padding_free_packed_amd import workloads as W
+
+DEV = "cuda:0"
+
+
+def say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def to_dev(x: np.ndarray, dtype: str) -> torch.Tensor:
+    if dtype == W.BF16:
+        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).to(DEV)
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(DEV)
+
+
+def from_dev(t: torch.Tensor) -> np.ndarray:
+    t = t.detach().cpu()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16)
+    return t.numpy()
+
+
+def to_f64(t: torch.Tensor) -> np.ndarray:
+    a = from_dev(t)
+    return W.bf16_bits_to_f32(a).astype(np.float64) if a.dtype == np.uint16 else a.astype(np.float64)
+
+
+def check_out(gpu: np.ndarray, ref: np.ndarray, dtype: str, what: str = "out"):
+    """gpu, ref: float64 arrays whose first axis is the token (or query) row."""
+    assert gpu.shape == ref.shape, (what, gpu.shape, ref.shape)
+    assert np.isfinite(gpu).all(), f"{what}: non-finite values"
+    err = np.abs(gpu - ref)
+    if dtype == W.FP32:
+        assert err.max() <= 1e-5, f"{what}: max abs err {err.max():.3e} > 1e-5"
+        big = np.abs(ref) >= 0.1
+        if big.any():
+            rel = (err[big] / np.abs(ref[big])).max()
+            assert rel <= 1e-4, f"{what}: max rel err {rel:.3e} > 1e-4"
+    else:
+        assert err.max() <= 2e-2, f"{what}: max abs err {err.max():.3e} > 2e-2"
+        g = gpu.reshape(gpu.shape[0], -1)
+        r = ref.reshape(ref.shape[0], -1)
+        ng, nr = np.linalg.norm(g, axis=1), np.linalg.norm(r, axis=1)
+        both_zero = (ng < 1e-30) & (nr < 1e-30)
+        cos = np.where(both_zero, 1.0, (g * r).sum(1) / np.maximum(ng * nr, 1e-300))
+        assert cos.min() >= 0.999, f"{what}: min per-token cosine {cos.min():.6f} < 0.999"
+    return float(err.max())
+
+
+def check_lse(gpu: np.ndarray, ref: np.ndarray, dtype: str, what: str = "lse"):
+    assert gpu.shape == ref.shape
+    assert np.isfinite(gpu).all(), f"{what}: non-finite values"
+    d = np.abs(gpu - ref)
+    if dtype == W.FP32:
+        bound = 1e-5 * np.maximum(1.0, np.abs(ref))
+    else:
+        bound = np.full_like(ref, 1e-3)
+    assert (d <= bound).all(), f"{what}: max |delta| {d.max():.3e}"
+    return float(d.max())
+
+
+def sample_rows(cu: np.ndarray, tile: int, n_random: int, seed: int):
+    """Rows to check at full size: first/last rows, tile edges, sequence edges,
+    every row of the longest sequence's first and last tile, and random rows."""
+    cu = np.asarray(cu, dtype=np.int64)
+    N = int(cu[-1])
+    rng = np.random.default_rng(seed)
+    rows = {0, 1, N - 1, N - 2}
+    for t in (1, 2, N // tile // 2, N // tile - 1):
+        for r in (t * tile - 1, t * tile, t * tile + 1):
+            if 0 <= r < N:
+                rows.add(r)
+    L = cu[1:] - cu[:-1]
+    b = int(np.argmax(L))
+    for r in list(range(int(cu[b]), min(int(cu[b]) + 40, int(cu[b + 1])))) + \
+            list(range(max(int(cu[b + 1]) - 40, int(cu[b])), int(cu[b + 1]))):
+        rows.add(r)
+    for bb in rng.integers(0, len(L), size=16):
+        rows.update({int(cu[bb]), int(cu[bb + 1]) - 1})
+    rows.update(int(x) for x in rng.integers(0, N, size=n_random))
+    return sorted(rows)

@@ -1,0 +1,147 @@
+"""The C ABI on the CPU: the library loads, exports every symbol include/pe.h
+declares, sizes workspaces, and rejects bad host arguments before launching
+anything (so no GPU is needed). Device pointers here are fake addresses that
+the library never dereferences on these paths."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from padding_free_packed_amd import pe
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+lib = pe.library()
+
+P = 1 << 20          # a 16-byte aligned fake device address
+MIS = P + 4           # misaligned
+NUL = None
+
+
+def _header_functions():
+    with open(os.path.join(ROOT, "include", "pe.h")) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pe_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_symbols_exported():
+    names = _header_functions()
+    assert len(names) == 10
+    for n in names:
+        assert hasattr(lib, n), n
+    assert sorted(pe.EXPORTS) == names
+
+
+def test_status_strings():
+    for s in range(8):
+        assert lib.pe_status_string(s).decode().startswith("PE_")
+    assert b"unknown" in lib.pe_status_string(99)
+
+
+def test_tile_rows():
+    assert pe.pe_attn_tile_rows() == 128
+
+
+def test_workspace_sizes():
+    # work list: ceil(N/128)+1 int32, rounded to 256 bytes; backward adds an fp32 [H, N] array
+    assert pe.pe_attn_workspace_size(4, 1000, 8, 64, pe.PE_FP32, False) == 256
+    assert pe.pe_attn_workspace_size(4, 1000, 8, 64, pe.PE_FP32, True) == 256 + 32000
+    big = pe.pe_attn_workspace_size(4096, 368449, 8, 64, pe.PE_FP32, False)
+    assert big >= (368449 // 128 + 2) * 4 and big % 256 == 0
+    assert pe.pe_pack_workspace_size(8, 64, 16, pe.PE_FP32) >= 256 + 8
+    assert pe.pe_pack_workspace_size(0, 64, 16, pe.PE_FP32) == 0
+
+
+def _fwd(**kw):
+    a = dict(q=P, k=P, v=P, cu=P, B=4, N=100, S=64, H=2, d=64, dt=pe.PE_FP32, scale=0.125, out=P, lse=NUL,
+             ws=P, wsb=1 << 20)
+    a.update(kw)
+    return lib.pe_varlen_attn_fwd(a["q"], a["k"], a["v"], a["cu"], a["B"], a["N"], a["S"], a["H"], a["d"],
+                                  a["dt"], a["scale"], a["out"], a["lse"], a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=NUL), pe.PE_ERR_NULL),
+    (dict(cu=NUL), pe.PE_ERR_NULL),
+    (dict(out=NUL), pe.PE_ERR_NULL),
+    (dict(B=0), pe.PE_ERR_ARG),
+    (dict(S=0), pe.PE_ERR_ARG),
+    (dict(H=0), pe.PE_ERR_ARG),
+    (dict(N=3), pe.PE_ERR_ARG),                 # fewer tokens than sequences: an empty sequence
+    (dict(N=4 * 64 + 1), pe.PE_ERR_ARG),        # more tokens than B * max_seq_len
+    (dict(N=2**31, B=2**20, S=2**12), pe.PE_ERR_ARG),   # token count beyond int32
+    (dict(d=12), pe.PE_ERR_UNSUPPORTED),        # not a supported multiple of 8
+    (dict(d=256), pe.PE_ERR_UNSUPPORTED),
+    (dict(dt=5), pe.PE_ERR_UNSUPPORTED),
+    (dict(scale=0.0), pe.PE_ERR_ARG),
+    (dict(scale=float("nan")), pe.PE_ERR_ARG),
+    (dict(q=MIS), pe.PE_ERR_ARG),
+    (dict(ws=NUL), pe.PE_ERR_WORKSPACE),
+    (dict(wsb=8), pe.PE_ERR_WORKSPACE),
+])
+def test_fwd_rejects(kw, code):
+    assert _fwd(**kw) == code
+
+
+def test_first_token_rejects():
+    f = lib.pe_varlen_attn_fwd_first_token
+    assert f(NUL, P, P, P, 4, 100, 64, 2, 64, 0, 0.125, P, NUL, None) == pe.PE_ERR_NULL
+    assert f(P, P, P, P, 4, 100, 64, 2, 24, 0, 0.125, P, NUL, None) == pe.PE_ERR_UNSUPPORTED
+    assert f(P, P, P, P, 4, 100, 64, 2, 64, 0, -1.0, P, NUL, None) == pe.PE_ERR_ARG
+    assert f(P, P, P, P, 4, 100, 64, 2, 64, 0, 0.125, P, MIS, None) == pe.PE_ERR_ARG
+
+
+def test_bwd_rejects():
+    f = lib.pe_varlen_attn_bwd
+    ok = [P, P, P, P, P, P, P, 4, 100, 64, 2, 64, 0, 0.125, P, P, P, P, 1 << 20, None]
+    for i in (0, 1, 2, 3, 4, 5, 6, 14, 15, 16):
+        a = list(ok)
+        a[i] = NUL
+        assert f(*a) == pe.PE_ERR_NULL, i
+    a = list(ok)
+    a[18] = 100
+    assert f(*a) == pe.PE_ERR_WORKSPACE
+    a = list(ok)
+    a[11] = 40
+    assert f(*a) == pe.PE_ERR_UNSUPPORTED
+
+
+def test_pack_rejects():
+    f = lib.pe_pack
+    n = ctypes.c_int64(0)
+    ok = [P, 4, 64, P, 16, 0, P, P, P, 100, ctypes.byref(n), P, 1 << 20, None]
+    a = list(ok); a[0] = NUL
+    assert f(*a) == pe.PE_ERR_NULL
+    a = list(ok); a[10] = NUL
+    assert f(*a) == pe.PE_ERR_NULL
+    a = list(ok); a[8] = NUL                     # grid without a packed output
+    assert f(*a) == pe.PE_ERR_NULL
+    a = list(ok); a[3] = NUL                     # packed output without a grid
+    assert f(*a) == pe.PE_ERR_ARG
+    a = list(ok); a[1] = 0
+    assert f(*a) == pe.PE_ERR_ARG
+    a = list(ok); a[2] = 0
+    assert f(*a) == pe.PE_ERR_ARG
+    a = list(ok); a[9] = -1
+    assert f(*a) == pe.PE_ERR_ARG
+    a = list(ok); a[5] = 7
+    assert f(*a) == pe.PE_ERR_UNSUPPORTED
+    a = list(ok); a[4] = 0
+    assert f(*a) == pe.PE_ERR_ARG
+    a = list(ok); a[12] = 10
+    assert f(*a) == pe.PE_ERR_WORKSPACE
+    a = list(ok); a[6] = MIS
+    assert f(*a) == pe.PE_ERR_ARG
+
+
+def test_unpack_and_worklist_reject():
+    u = lib.pe_unpack
+    assert u(NUL, P, 4, 64, 100, 16, 0, P, None) == pe.PE_ERR_NULL
+    assert u(P, P, 4, 64, 3, 16, 0, P, None) == pe.PE_ERR_ARG
+    assert u(P, P, 4, 64, 100, 0, 0, P, None) == pe.PE_ERR_ARG
+    assert u(P, P, 4, 64, 100, 16, 9, P, None) == pe.PE_ERR_UNSUPPORTED
+    w = lib.pe_worklist
+    assert w(NUL, 4, 100, 128, P, None) == pe.PE_ERR_NULL
+    assert w(P, 4, 100, 0, P, None) == pe.PE_ERR_ARG
+    assert w(P, 0, 100, 128, P, None) == pe.PE_ERR_ARG
