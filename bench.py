@@ -1,0 +1,294 @@
+#!/usr/bin/env python3
+"""Benchmark of the packed-attention path on one MI355X.
+
+One step is one pass of the whole path over one batch of synthetic input that
+is already resident in HBM:
+
+    pe_pack (lengths -> cu_seqlens, flat_index, packed rows of the padded grid;
+             its one host read included)
+    pe_varlen_attn_fwd (work list + forward with log-sum-exp)
+    pe_varlen_attn_fwd_first_token
+    pe_varlen_attn_bwd (when the workload carries dO)
+    pe_unpack (attention output back to the padded grid)
+
+The default workload is the graph-transformer shape: 4096 sequences of at most
+256 tokens, lengths round(N(90, 40)) clipped to [1, 256], 8 heads x 64, fp32,
+padded grid [4096, 256, 512]. `value` is real tokens per second of the whole
+step. Every kernel launch inside the timed region is bracketed by HIP events
+(pe_timing_enable), which gives each kernel's average duration; the roofline
+entry is for the kernel with the largest time per step, priced at its
+algorithmic work (algo_work below). The CPU baseline times the fp64 oracle on a
+bounded sample of the same batch.
+
+Prints ONE JSON line.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "packed varlen attn fwd real tokens/s + TFLOP/s, % of MI355X MFMA/HBM roofline"
+PEAK = {"bf16": 2500.0, "fp32": 157.3}   # dense MFMA TFLOP/s
+HBM_PEAK = 8000.0                        # GB/s
+
+KERNEL_SOURCES = {
+    "attn_fwd": ["attn_fwd.hip", "attn_common.h"],
+    "attn_fwd_first": ["attn_fwd.hip"],
+    "bwd_delta": ["attn_bwd.hip", "attn_common.h"],
+    "bwd_dkdv": ["attn_bwd.hip", "attn_common.h"],
+    "bwd_dq": ["attn_bwd.hip", "attn_common.h"],
+    "pack_rows": ["pack.hip"],
+    "unpack_rows": ["pack.hip"],
+    "scan": ["pack.hip"],
+    "worklist": ["pack.hip"],
+}
+
+
+def source_hash(kernel: str) -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES.get(kernel, []):
+        with open(os.path.join(ROOT, "padding_free_packed_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def algo_work(kernel, w, N, L2, e, with_lse):
+    """Algorithmic work of one launch: ('flop', count) or ('byte', count)."""
+    B, S, H, d = w.num_seqs, w.max_seq_len, w.num_heads, w.head_dim
+    D = H * d
+    T = (N + 127) // 128
+    return {
+        # forward: 4 sum(L^2) H d flops (QK^T and PV)
+        "attn_fwd": ("flop", 4.0 * L2 * H * d),
+        # backward split by kernel: dK/dV performs S, dP, dV and dK (8 sum L^2 H d),
+        # dQ performs dQ (2 sum L^2 H d); its recomputation of S and dP is not counted
+        "bwd_dkdv": ("flop", 8.0 * L2 * H * d),
+        "bwd_dq": ("flop", 2.0 * L2 * H * d),
+        # first token: read K and V once, the B queries, write B outputs (+ LSE)
+        "attn_fwd_first": ("byte", 2.0 * N * D * e + 2.0 * B * D * e + (4.0 * B * H if with_lse else 0.0)),
+        "bwd_delta": ("byte", 2.0 * N * D * e + 4.0 * N * H),
+        # pack: read and write the real rows, write flat_index
+        "pack_rows": ("byte", 2.0 * N * D * e + 8.0 * N),
+        # unpack: read the real rows, write the whole grid
+        "unpack_rows": ("byte", 1.0 * N * D * e + 1.0 * B * S * D * e),
+        "scan": ("byte", 4.0 * B + 4.0 * (B + 1)),
+        "worklist": ("byte", 4.0 * (B + 1) + 4.0 * (T + 1)),
+    }.get(kernel)
+
+
+def rate(kind, amount, ms, dtype):
+    if kind == "flop":
+        a = amount / (ms * 1e-3) / 1e12
+        return {"bound": "mfma", "achieved": a, "peak": PEAK[dtype], "unit": "TFLOP/s", "frac": a / PEAK[dtype]}
+    a = amount / (ms * 1e-3) / 1e9
+    return {"bound": "hbm", "achieved": a, "peak": HBM_PEAK, "unit": "GB/s", "frac": a / HBM_PEAK}
+
+
+def load_traffic(kernel, workload):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if taken on this source."""
+    p = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.json")
+    if not os.path.exists(p):
+        return None
+    with open(p) as f:
+        t = json.load(f)
+    if t.get("source_hash") != source_hash(kernel):
+        return None
+    return t.get("bytes_per_launch")
+
+
+def cpu_baseline(w, budget_s):
+    """The fp64 oracle on the first m sequences of the batch (a valid packed batch itself),
+    with m sized for about `budget_s` seconds, BLAS limited to one thread."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    import oracle
+    from padding_free_packed_amd import workloads as W
+
+    cu_all = np.concatenate([[0], np.cumsum(w.lengths.astype(np.int64))])
+
+    def run(m):
+        n = int(cu_all[m])
+        L = w.lengths[:m]
+        grid = w.grid[:m] if w.grid is not None else None
+        q, k, v = (W.to_f64(x[:n], w.dtype) for x in (w.q, w.k, w.v))
+        do = W.to_f64(w.dout[:n], w.dtype) if w.dout is not None else None
+        t0 = time.perf_counter()
+        cu, flat, N = oracle.layout(L, w.max_seq_len)
+        if grid is not None:
+            oracle.pack(grid, flat)
+        o, _ = oracle.attention(q, k, v, cu, w.scale)
+        oracle.attention_first_token(q[cu[:-1]], k, v, cu, w.scale)
+        if do is not None:
+            oracle.attention_backward(do, q, k, v, cu, w.scale)
+        if grid is not None:
+            oracle.unpack(o.reshape(N, -1), cu, w.max_seq_len)
+        return time.perf_counter() - t0, n
+
+    with threadpool_limits(limits=1):
+        m = min(64, w.num_seqs)
+        t, n = run(m)
+        m = int(min(w.num_seqs, max(m, m * budget_s / max(t, 1e-3))))
+        t, n = run(m)
+    return {"value": n / t, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"first {m} of {w.num_seqs} sequences ({n} tokens): layout, pack, forward, first-token,"
+                      f"{' backward,' if w.dout is not None else ''}{' unpack' if w.grid is not None else ''} in float64,"
+                      f" {t:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="graph_transformer",
+                    choices=["graph_transformer", "short_query", "long_document", "mixed_training", "tiny"])
+    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE={world}): this build "
+              "measures the single-GPU path; sharding across GPUs is described in DESIGN.md, not run.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from padding_free_packed_amd import pe
+    from padding_free_packed_amd import workloads as W
+
+    gen = {
+        "graph_transformer": lambda: W.graph_transformer(grid=True, with_grad=True),
+        "short_query": lambda: W.short_query(grid=True),
+        "long_document": W.long_document,
+        "mixed_training": W.mixed_training,
+        "tiny": lambda: W.tiny(with_grad=True),
+    }[args.workload]
+    w = gen()
+    dev = "cuda:0"
+    B, S, H, d = w.num_seqs, w.max_seq_len, w.num_heads, w.head_dim
+    D = H * d
+    N = w.total_tokens
+    L2 = float((w.lengths.astype(np.float64) ** 2).sum())
+    bf = w.dtype == W.BF16
+    e = 2 if bf else 4
+    code = pe.PE_BF16 if bf else pe.PE_FP32
+
+    def up(x):
+        if x is None:
+            return None
+        if bf:
+            return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+
+    lengths = torch.from_numpy(w.lengths.astype(np.int32)).to(dev)
+    q, k, v, dout = up(w.q), up(w.k), up(w.v), up(w.dout)
+    # workloads without a padded grid of their own pack the layout only (cu_seqlens, flat_index)
+    grid = up(w.grid)
+    cu_h = np.concatenate([[0], np.cumsum(w.lengths.astype(np.int64))])
+    q_first = q[torch.from_numpy(cu_h[:-1]).to(dev)].contiguous()
+
+    cu = torch.empty(B + 1, dtype=torch.int32, device=dev)
+    flat = torch.empty(N, dtype=torch.int64, device=dev)
+    packed = torch.empty(N, D, dtype=q.dtype, device=dev) if grid is not None else None
+    out = torch.empty_like(q)
+    lse = torch.empty(H, N, device=dev)
+    out_first = torch.empty_like(q_first)
+    lse_first = torch.empty(H, B, device=dev)
+    grid_out = torch.empty_like(grid) if grid is not None else None
+    with_bwd = dout is not None
+    dq, dk, dv = ((torch.empty_like(q) for _ in range(3)) if with_bwd else (None, None, None))
+    ws_pack = pe.workspace(pe.pe_pack_workspace_size(B, S, D, code), dev)
+    ws = pe.workspace(pe.pe_attn_workspace_size(B, N, H, d, code, with_bwd), dev)
+    scale = w.scale
+
+    def step():
+        n = pe.pe_pack(lengths, S, grid, cu, flat, packed, N, ws_pack, code)
+        assert n == N
+        pe.pe_varlen_attn_fwd(q, k, v, cu, B, N, S, scale, out, lse, ws)
+        pe.pe_varlen_attn_fwd_first_token(q_first, k, v, cu, B, N, S, scale, out_first, lse_first)
+        if with_bwd:
+            pe.pe_varlen_attn_bwd(dout, q, k, v, out, lse, cu, B, N, S, scale, dq, dk, dv, ws)
+        if grid is not None:
+            pe.pe_unpack(out.view(N, D), cu, B, S, N, grid_out)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    pe.pe_timing_enable(True)
+    pe.pe_timing_read()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t0.record()
+    for _ in range(args.steps):
+        step()
+    t1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    recs = pe.pe_timing_read()
+    pe.pe_timing_enable(False)
+    ms_total = t0.elapsed_time(t1)
+    ms_step = ms_total / args.steps
+
+    per = {}
+    for name, ms in recs:
+        per.setdefault(name, []).append(ms)
+    breakdown = {}
+    for name, lst in per.items():
+        launches_per_step = len(lst) / args.steps
+        avg = float(np.mean(lst))
+        ent = {"avg_ms": avg, "launches_per_step": launches_per_step, "ms_per_step": avg * launches_per_step}
+        aw = algo_work(name, w, N, L2, e, True)
+        if aw is not None and avg > 0:
+            ent.update(rate(aw[0], aw[1], avg, "bf16" if bf else "fp32"))
+        breakdown[name] = ent
+    dom = max(breakdown, key=lambda k_: breakdown[k_]["ms_per_step"])
+    kind, amount = algo_work(dom, w, N, L2, e, True)
+    roof = rate(kind, amount, breakdown[dom]["avg_ms"], "bf16" if bf else "fp32")
+    roof["traffic"] = load_traffic(dom, args.workload)
+    roof["kernel"] = dom
+    roof["algorithmic_per_launch"] = amount
+
+    fwd_ms = breakdown["attn_fwd"]["avg_ms"]
+    result = {
+        "metric": METRIC,
+        "value": N / (ms_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if bf else "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": args.workload, "num_seqs": B, "max_seq_len": S, "total_tokens": N, "num_heads": H,
+            "head_dim": d, "grid": [B, S, D] if grid is not None else None,
+            "step": ("pack" if grid is not None else "pack(layout only)") + "+fwd(lse)+first_token"
+                    + ("+bwd" if with_bwd else "") + ("+unpack" if grid is not None else ""),
+        },
+        "fwd": {"ms": fwd_ms, "tokens_per_s": N / (fwd_ms * 1e-3),
+                "tflops": 4.0 * L2 * H * d / (fwd_ms * 1e-3) / 1e12},
+        "roofline": roof,
+        "breakdown": breakdown,
+        "wall_s_timed_region": wall,
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)
+    print(json.dumps(result))
+
+
+if __name__ == "__main__":
+    main()

@@ -213,6 +213,21 @@ pe_status pe_varlen_attn_bwd(const void* dout, const void* q, const void* k, con
                              void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
                              void* stream);
 
+/* ------------------------------------------------------------- kernel timing
+ * Measurement support, not part of the computation. While enabled, every
+ * kernel the library launches is bracketed by two HIP events recorded on the
+ * launch's stream (the events come from a pool the library creates on first
+ * use; no device memory is allocated). pe_timing_read waits for the recorded
+ * events and writes, in launch order, the kernel name (NUL-terminated, at most
+ * 31 characters, into `names` + 32*i; `names` may be NULL) and its duration in
+ * milliseconds (`ms`, may be NULL; -1 if unavailable) of up to `max_records`
+ * kernels launched since the previous read, forgets all records, and returns
+ * how many it wrote. At most 4096 kernels are recorded between reads. Disabled
+ * by default; disabling drops unread records. Not thread-safe.
+ */
+pe_status pe_timing_enable(int on);
+int pe_timing_read(char* names, float* ms, int max_records);
+
 #ifdef __cplusplus
 }
 #endif

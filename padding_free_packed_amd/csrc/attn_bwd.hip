@@ -1,13 +1,283 @@
-// Backward of packed attention (being written; returns hipErrorNotSupported).
-#include "common.h"
-#include "kernels.h"
+// Backward of non-causal attention over packed sequences, recomputing the
+// probabilities from the forward's log-sum-exp. Three launches, no atomics,
+// so the result is bitwise reproducible:
+//
+//   delta:  D[h, i] = <dO[i, h, :], O[i, h, :]>                       (HBM-bound)
+//   dK/dV:  per head and tile of 128 packed KEY rows (4 waves x 32 keys), over
+//           the query rows of every sequence the tile touches, 64 at a time:
+//             S  = Q K^T, dP = dO V^T                (mma_rows_regs, K and V in registers)
+//             P  = exp(scale*S - lse), dS = P (dP - D)
+//             dV^T += dO^T P, dK^T += Q^T dS          (mma_tr_regs, Q and dO from LDS)
+//   dQ:     per head and tile of 128 packed QUERY rows, over their keys:
+//             S^T = K Q^T, dP^T = V dO^T, dS^T = P^T (dP^T - D)
+//             dQ^T += K^T dS^T
+//   and dK, dQ are scaled by the softmax scale at the store.
+//
+// The dQ pass recomputes S and dP once more than an atomic-accumulation scheme
+// would (14 instead of 10 matrix products of the size of S per head), the price
+// of determinism.
+#include <climits>
+
+#include "attn_common.h"
 
 namespace pe {
 
-hipError_t launch_attn_bwd(bool, int, const void*, const void*, const void*, const void*, const void*,
-                           const float*, const int32_t*, const int32_t*, int32_t, int32_t, int32_t, float,
-                           void*, void*, void*, float*, hipStream_t) {
-  return hipErrorNotSupported;
+namespace {
+
+template <bool BF, int D>
+__global__ __launch_bounds__(256) void bwd_delta_kernel(const void* __restrict__ dout, const void* __restrict__ out,
+                                                        int32_t N, int32_t H, float* __restrict__ delta) {
+  using G = Geo<BF, D>;
+  const int64_t ch = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;  // 16-byte chunk
+  const int64_t total = static_cast<int64_t>(N) * H * G::CH;
+  float s = 0.f;
+  if (ch < total) {
+    const uint4 a = *reinterpret_cast<const uint4*>(static_cast<const char*>(dout) + ch * 16);
+    const uint4 b = *reinterpret_cast<const uint4*>(static_cast<const char*>(out) + ch * 16);
+    if constexpr (BF) {
+      const u16x8 x = __builtin_bit_cast(u16x8, a), y = __builtin_bit_cast(u16x8, b);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) s = fmaf(bf16_to_f32(x[e]), bf16_to_f32(y[e]), s);
+    } else {
+      const float4 x = __builtin_bit_cast(float4, a), y = __builtin_bit_cast(float4, b);
+      s = fmaf(x.x, y.x, fmaf(x.y, y.y, fmaf(x.z, y.z, x.w * y.w)));
+    }
+  }
+#pragma unroll
+  for (int o = 1; o < G::CH; o <<= 1) s += __shfl_xor(s, o);
+  if (ch < total && (ch % G::CH) == 0) {
+    const int64_t hr = ch / G::CH;
+    const int64_t i = hr / H, hh = hr - i * H;
+    delta[hh * N + i] = s;
+  }
+}
+
+template <bool BF, int D>
+__global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(
+    const void* __restrict__ dop, const void* __restrict__ qp, const void* __restrict__ kp,
+    const void* __restrict__ vp, const float* __restrict__ lse, const float* __restrict__ delta,
+    const int32_t* __restrict__ cu, const int32_t* __restrict__ items, int32_t B, int32_t N, int32_t H,
+    int32_t T, float c, float scale, void* __restrict__ dkp, void* __restrict__ dvp) {
+  using G = Geo<BF, D>;
+  using E = typename G::E;
+  __shared__ __align__(16) E qt[2][G::TSZ];
+  __shared__ __align__(16) E dt[2][G::TSZ];
+  __shared__ __align__(16) float ls[2][kBlk];
+  __shared__ __align__(16) float dl[2][kBlk];
+  __shared__ int32_t cul[kAttnTileRows + 2];
+
+  const int lin = xcd_remap(blockIdx.x, gridDim.x);
+  const int h = lin / T, t = lin - h * T;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, ql = lane & 31, g = lane >> 5;
+
+  const TileSpan sp = tile_span(cu, items, t, B, N, cul);
+  const int krow = sp.r0 + wv * 32 + ql;
+  const bool kvalid = krow < sp.rend;
+  int jk0 = 0, jk1 = 0;  // query rows of this key's sequence
+  if (kvalid) own_range(cul, sp.ncu, krow, jk0, jk1);
+  const int wq0 = wave_min_i(kvalid ? jk0 : INT_MAX);
+  const int wq1 = wave_max_i(kvalid ? jk1 : INT_MIN);
+  const int mq0 = wave_max_i(kvalid ? jk0 : INT_MIN);
+  const int mq1 = wave_min_i(kvalid ? jk1 : INT_MAX);
+
+  typename RegT<BF>::T kreg[G::QS], vreg[G::QS];
+  const int64_t roff = (static_cast<int64_t>(krow) * H + h) * D;
+  load_row_regs<BF, D>(kp, roff + g * G::HALF, kvalid, kreg);
+  load_row_regs<BF, D>(vp, roff + g * G::HALF, kvalid, vreg);
+
+  floatx16 dk[G::DB], dv[G::DB];
+#pragma unroll
+  for (int db = 0; db < G::DB; ++db) {
+    dk[db] = floatx16{};
+    dv[db] = floatx16{};
+  }
+
+  uint4 qr[G::PER], dr[G::PER];
+  float lsr = 0.f, dlr = 0.f;
+  const float* lse_h = lse + static_cast<int64_t>(h) * N;
+  const float* del_h = delta + static_cast<int64_t>(h) * N;
+  auto gload = [&](int qb) {
+    tile_gload<BF, D>(qp, qb, sp.hi, H, h, qr);
+    tile_gload<BF, D>(dop, qb, sp.hi, H, h, dr);
+    if (tid < kBlk) {
+      const int row = qb + tid;
+      lsr = row < sp.hi ? lse_h[row] * kLog2e : 0.f;
+      dlr = row < sp.hi ? del_h[row] : 0.f;
+    }
+  };
+
+  int buf = 0;
+  if (sp.lo < sp.hi) gload(sp.lo);
+  for (int qb = sp.lo; qb < sp.hi; qb += kBlk) {
+    tile_store<BF, D>(qt[buf], qr);
+    tile_store<BF, D>(dt[buf], dr);
+    if (tid < kBlk) {
+      ls[buf][tid] = lsr;
+      dl[buf][tid] = dlr;
+    }
+    __syncthreads();
+    if (qb + kBlk < sp.hi) gload(qb + kBlk);
+    if (qb < wq1 && qb + kBlk > wq0) {
+      const bool need_mask = !(qb >= mq0 && qb + kBlk <= mq1);
+#pragma unroll
+      for (int qq = 0; qq < 2; ++qq) {
+        floatx16 s = floatx16{}, dp = floatx16{};
+        mma_rows_regs<BF, D>(qt[buf], 32 * qq, kreg, s, ql, g);   // S[q][key]
+        mma_rows_regs<BF, D>(dt[buf], 32 * qq, vreg, dp, ql, g);  // dP[q][key]
+        const int base = qb + 32 * qq + 4 * g;
+        if (need_mask) mask_block(s, jk0 - base, jk1 - base);
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4) {
+          const float4 l4 = *reinterpret_cast<const float4*>(&ls[buf][32 * qq + 8 * i4 + 4 * g]);
+          const float4 d4 = *reinterpret_cast<const float4*>(&dl[buf][32 * qq + 8 * i4 + 4 * g]);
+          const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+          const float dvv[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int i = 4 * i4 + j;
+            const float p = __builtin_amdgcn_exp2f(fmaf(s[i], c, -lv[j]));
+            s[i] = p;
+            dp[i] = p * (dp[i] - dvv[j]);
+          }
+        }
+        mma_tr_regs<BF, D>(dt[buf], 32 * qq, s, dv, lane);   // dV^T += dO^T P
+        mma_tr_regs<BF, D>(qt[buf], 32 * qq, dp, dk, lane);  // dK^T += Q^T dS
+      }
+    }
+    buf ^= 1;
+  }
+  if (kvalid) {
+    store_acc_row<BF, D>(dkp, roff, dk, scale, g);
+    store_acc_row<BF, D>(dvp, roff, dv, 1.f, g);
+  }
+}
+
+template <bool BF, int D>
+__global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
+    const void* __restrict__ dop, const void* __restrict__ qp, const void* __restrict__ kp,
+    const void* __restrict__ vp, const float* __restrict__ lse, const float* __restrict__ delta,
+    const int32_t* __restrict__ cu, const int32_t* __restrict__ items, int32_t B, int32_t N, int32_t H,
+    int32_t T, float c, float scale, void* __restrict__ dqp) {
+  using G = Geo<BF, D>;
+  using E = typename G::E;
+  __shared__ __align__(16) E kt[2][G::TSZ];
+  __shared__ __align__(16) E vt[2][G::TSZ];
+  __shared__ int32_t cul[kAttnTileRows + 2];
+
+  const int lin = xcd_remap(blockIdx.x, gridDim.x);
+  const int h = lin / T, t = lin - h * T;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, ql = lane & 31, g = lane >> 5;
+
+  const TileSpan sp = tile_span(cu, items, t, B, N, cul);
+  const int qrow = sp.r0 + wv * 32 + ql;
+  const bool qvalid = qrow < sp.rend;
+  int qk0 = 0, qk1 = 0;
+  if (qvalid) own_range(cul, sp.ncu, qrow, qk0, qk1);
+  const int wk0 = wave_min_i(qvalid ? qk0 : INT_MAX);
+  const int wk1 = wave_max_i(qvalid ? qk1 : INT_MIN);
+  const int mk0 = wave_max_i(qvalid ? qk0 : INT_MIN);
+  const int mk1 = wave_min_i(qvalid ? qk1 : INT_MAX);
+
+  typename RegT<BF>::T qreg[G::QS], dreg[G::QS];
+  const int64_t roff = (static_cast<int64_t>(qrow) * H + h) * D;
+  load_row_regs<BF, D>(qp, roff + g * G::HALF, qvalid, qreg);
+  load_row_regs<BF, D>(dop, roff + g * G::HALF, qvalid, dreg);
+  const float lse2 = qvalid ? lse[static_cast<int64_t>(h) * N + qrow] * kLog2e : 0.f;
+  const float dlq = qvalid ? delta[static_cast<int64_t>(h) * N + qrow] : 0.f;
+
+  floatx16 dq[G::DB];
+#pragma unroll
+  for (int db = 0; db < G::DB; ++db) dq[db] = floatx16{};
+
+  uint4 kr[G::PER], vr[G::PER];
+  int buf = 0;
+  if (sp.lo < sp.hi) {
+    tile_gload<BF, D>(kp, sp.lo, sp.hi, H, h, kr);
+    tile_gload<BF, D>(vp, sp.lo, sp.hi, H, h, vr);
+  }
+  for (int kb = sp.lo; kb < sp.hi; kb += kBlk) {
+    tile_store<BF, D>(kt[buf], kr);
+    tile_store<BF, D>(vt[buf], vr);
+    __syncthreads();
+    if (kb + kBlk < sp.hi) {
+      tile_gload<BF, D>(kp, kb + kBlk, sp.hi, H, h, kr);
+      tile_gload<BF, D>(vp, kb + kBlk, sp.hi, H, h, vr);
+    }
+    if (kb < wk1 && kb + kBlk > wk0) {
+      const bool need_mask = !(kb >= mk0 && kb + kBlk <= mk1);
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        floatx16 s = floatx16{}, dp = floatx16{};
+        mma_rows_regs<BF, D>(kt[buf], 32 * kk, qreg, s, ql, g);   // S^T[key][q]
+        mma_rows_regs<BF, D>(vt[buf], 32 * kk, dreg, dp, ql, g);  // dP^T[key][q]
+        if (need_mask) {
+          const int base = kb + 32 * kk + 4 * g;
+          mask_block(s, qk0 - base, qk1 - base);
+        }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const float p = __builtin_amdgcn_exp2f(fmaf(s[i], c, -lse2));
+          dp[i] = p * (dp[i] - dlq);
+        }
+        mma_tr_regs<BF, D>(kt[buf], 32 * kk, dp, dq, lane);  // dQ^T += K^T dS^T
+      }
+    }
+    buf ^= 1;
+  }
+  if (qvalid) store_acc_row<BF, D>(dqp, roff, dq, scale, g);
+}
+
+template <bool BF, int D>
+hipError_t bwd_dispatch(const void* dout, const void* q, const void* k, const void* v, const void* out,
+                        const float* lse, const int32_t* cu, const int32_t* items, int32_t B, int32_t N,
+                        int32_t H, float scale, void* dq, void* dk, void* dv, float* delta,
+                        hipStream_t stream) {
+  using G = Geo<BF, D>;
+  if (N == 0) return hipSuccess;
+  const int64_t chunks = static_cast<int64_t>(N) * H * G::CH;
+  hipEvent_t ev_bwd_delta = timing_start(stream);
+  hipLaunchKernelGGL((bwd_delta_kernel<BF, D>), dim3(static_cast<unsigned>((chunks + 255) / 256)), dim3(256), 0,
+                   stream, dout, out, N, H, delta);
+  timing_stop("bwd_delta", ev_bwd_delta, stream);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int T = (N + kAttnTileRows - 1) / kAttnTileRows;
+  const unsigned blocks = static_cast<unsigned>(static_cast<int64_t>(T) * H);
+  const float c = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
+  hipEvent_t ev_bwd_dkdv = timing_start(stream);
+  hipLaunchKernelGGL((bwd_dkdv_kernel<BF, D>), dim3(blocks), dim3(kThreads), 0, stream, dout, q, k, v, lse, delta,
+                   cu, items, B, N, H, T, c, scale, dk, dv);
+  timing_stop("bwd_dkdv", ev_bwd_dkdv, stream);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipEvent_t ev_bwd_dq = timing_start(stream);
+  hipLaunchKernelGGL((bwd_dq_kernel<BF, D>), dim3(blocks), dim3(kThreads), 0, stream, dout, q, k, v, lse, delta,
+                   cu, items, B, N, H, T, c, scale, dq);
+  timing_stop("bwd_dq", ev_bwd_dq, stream);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_attn_bwd(bool bf16, int D, const void* dout, const void* q, const void* k, const void* v,
+                           const void* out, const float* lse, const int32_t* cu, const int32_t* items, int32_t B,
+                           int32_t N, int32_t H, float scale, void* dq, void* dk, void* dv, float* delta,
+                           hipStream_t stream) {
+#define PE_BWD_CASE(DD)                                                                                    \
+  case DD:                                                                                                \
+    return bf16 ? bwd_dispatch<true, DD>(dout, q, k, v, out, lse, cu, items, B, N, H, scale, dq, dk, dv,  \
+                                         delta, stream)                                                   \
+                : bwd_dispatch<false, DD>(dout, q, k, v, out, lse, cu, items, B, N, H, scale, dq, dk, dv, \
+                                          delta, stream);
+  switch (D) {
+    PE_BWD_CASE(8)
+    PE_BWD_CASE(16)
+    PE_BWD_CASE(32)
+    PE_BWD_CASE(64)
+    PE_BWD_CASE(128)
+    default: return hipErrorInvalidValue;
+  }
+#undef PE_BWD_CASE
 }
 
 }  // namespace pe

@@ -1,0 +1,278 @@
+// Building blocks shared by the attention kernels: tile geometry, staging of
+// 64-row tiles through LDS, and the two MFMA products every kernel is made of.
+//
+// All products work on 32x32 output blocks of v_mfma_f32_32x32x16_bf16 (bf16)
+// or v_mfma_f32_32x32x2_f32 (fp32). In the 32x32 accumulator layout lane l,
+// register i holds row 8*(i/4) + 4*(l/32) + (i%4), column l%32. Kernels place
+// the index they keep per lane (a query in the forward and dQ kernels, a key in
+// the dK/dV kernel) on the columns, so each lane owns one row of attention
+// scores and the score block can be fed back as the B operand of the next
+// product without leaving registers.
+//
+//   mma_rows_regs:  acc[32 x 32] += X[32 rows of an LDS tile] . Y^T,
+//                   Y = the lane's own row held in registers; reduction over head_dim.
+//   mma_tr_regs:    acc[d x 32]  += X[32 rows of an LDS tile]^T . P,
+//                   P = a 32x32 accumulator block; reduction over the 32 rows.
+//
+// The reduction index of an MFMA may be permuted freely as long as A and B use
+// the same order. mma_tr_regs uses the order in which the accumulator layout
+// holds rows (lane half g owns rows 4g..4g+3 and 8+4g..8+4g+3 of every 16), and
+// reads X^T in that order with ds_read_b64_tr_b16: within each group of 16
+// lanes, lane i receives element i%4 of the 8-byte chunks addressed by lanes
+// i/4 + 4j, j = 0..3, i.e. four consecutive rows of one column when lane s
+// addresses row s/4 and columns 4*(s%4)..4*(s%4)+3.
+#pragma once
+#include <type_traits>
+
+#include "common.h"
+#include "kernels.h"
+
+namespace pe {
+
+constexpr int kBlk = 64;       // rows per LDS stage
+constexpr int kThreads = 256;  // 4 waves per block
+
+typedef uint16_t u16x4 __attribute__((ext_vector_type(4)));
+typedef short shortx4 __attribute__((ext_vector_type(4)));
+
+template <bool BF, int D>
+struct Geo {
+  using E = typename std::conditional<BF, uint16_t, float>::type;
+  static constexpr int ES = BF ? 2 : 4;
+  static constexpr int ROWB = D * ES;              // bytes of one head row
+  static constexpr int CH = ROWB / 16;             // 16-byte chunks per head row
+  static constexpr int EPC = 16 / ES;              // elements per chunk
+  static constexpr int ST = BF ? D + 8 : D + 4;    // LDS row stride in elements
+  static constexpr int TSZ = kBlk * ST;            // elements of one staged tile
+  static constexpr int HALF = D / 2;               // head-dim elements per lane half
+  static constexpr int QS = BF ? (HALF + 7) / 8 : HALF;  // MFMA steps over head_dim
+  static constexpr int DB = (D + 31) / 32;         // 32-row blocks over head_dim
+  static constexpr int TOTCH = kBlk * CH;
+  static constexpr int PER = (TOTCH + kThreads - 1) / kThreads;
+};
+
+template <bool BF>
+struct RegT;
+template <>
+struct RegT<true> { using T = bf16x8; };
+template <>
+struct RegT<false> { using T = float; };
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u16x8 x) { return __builtin_bit_cast(bf16x8, x); }
+
+__device__ __forceinline__ u16x4 ds_read_tr16(const uint16_t* p) {
+  const shortx4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) shortx4*)(p));
+  return __builtin_bit_cast(u16x4, r);
+}
+
+// max / sum of a value with the same lane of the other half wave
+__device__ __forceinline__ float xhalf_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xhalf_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// The lane's own head row (elements g*HALF .. g*HALF+HALF-1) as MFMA operands.
+template <bool BF, int D>
+__device__ __forceinline__ void load_row_regs(const void* base, int64_t off, bool valid,
+                                              typename RegT<BF>::T (&r)[Geo<BF, D>::QS]) {
+  using G = Geo<BF, D>;
+  if constexpr (BF) {
+    const uint16_t* src = static_cast<const uint16_t*>(base) + off;
+#pragma unroll
+    for (int s = 0; s < G::QS; ++s) {
+      u16x8 x = {0, 0, 0, 0, 0, 0, 0, 0};
+      if (valid) {
+        if constexpr (G::HALF >= 8) {
+          x = *reinterpret_cast<const u16x8*>(src + 8 * s);
+        } else {
+#pragma unroll
+          for (int j = 0; j < G::HALF; ++j) x[j] = src[j];
+        }
+      }
+      r[s] = as_bf16x8(x);
+    }
+  } else {
+    const float* src = static_cast<const float*>(base) + off;
+#pragma unroll
+    for (int s = 0; s < G::QS; ++s) r[s] = valid ? src[s] : 0.f;
+  }
+}
+
+// Global -> registers for one 64-row tile of head h; rows >= row_lim are zero.
+template <bool BF, int D>
+__device__ __forceinline__ void tile_gload(const void* base, int row0, int row_lim, int H, int h,
+                                           uint4 (&r)[Geo<BF, D>::PER]) {
+  using G = Geo<BF, D>;
+  const char* b = static_cast<const char*>(base);
+#pragma unroll
+  for (int p = 0; p < G::PER; ++p) {
+    const int ch = threadIdx.x + p * kThreads;
+    const int row = ch / G::CH, col = ch - row * G::CH;
+    const int gr = row0 + row;
+    if ((G::TOTCH % kThreads == 0 || ch < G::TOTCH) && gr < row_lim) {
+      r[p] = *reinterpret_cast<const uint4*>(b + (static_cast<int64_t>(gr) * H + h) * G::ROWB + col * 16);
+    } else {
+      r[p] = make_uint4(0, 0, 0, 0);
+    }
+  }
+}
+
+// Registers -> LDS tile [kBlk][ST], row-major.
+template <bool BF, int D>
+__device__ __forceinline__ void tile_store(typename Geo<BF, D>::E* tile, const uint4 (&r)[Geo<BF, D>::PER]) {
+  using G = Geo<BF, D>;
+#pragma unroll
+  for (int p = 0; p < G::PER; ++p) {
+    const int ch = threadIdx.x + p * kThreads;
+    if (G::TOTCH % kThreads == 0 || ch < G::TOTCH) {
+      const int row = ch / G::CH, col = ch - row * G::CH;
+      *reinterpret_cast<uint4*>(tile + row * G::ST + col * G::EPC) = r[p];
+    }
+  }
+}
+
+// acc += X . Y^T over head_dim; X = rows row0..row0+31 of an LDS tile (row l%32
+// for lane l), Y = the lane's row in registers.
+template <bool BF, int D>
+__device__ __forceinline__ void mma_rows_regs(const typename Geo<BF, D>::E* tile, int row0,
+                                              const typename RegT<BF>::T (&y)[Geo<BF, D>::QS],
+                                              floatx16& acc, int ql, int g) {
+  using G = Geo<BF, D>;
+  const typename G::E* xr = tile + (row0 + ql) * G::ST + g * G::HALF;
+#pragma unroll
+  for (int st = 0; st < G::QS; ++st) {
+    if constexpr (BF) {
+      u16x8 a;
+      if constexpr (G::HALF >= 8) {
+        a = *reinterpret_cast<const u16x8*>(xr + 8 * st);
+      } else {
+        a = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+        for (int j = 0; j < G::HALF; ++j) a[j] = xr[j];
+      }
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), y[st], acc, 0, 0, 0);
+    } else {
+      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(xr[st], y[st], acc, 0, 0, 0);
+    }
+  }
+}
+
+// acc[db] += X^T . P; X = rows row0..row0+31 of an LDS tile (reduction index),
+// P = 32x32 accumulator block whose rows are those 32 tile rows.
+template <bool BF, int D>
+__device__ __forceinline__ void mma_tr_regs(const typename Geo<BF, D>::E* tile, int row0, const floatx16& p,
+                                            floatx16 (&acc)[Geo<BF, D>::DB], int lane) {
+  using G = Geo<BF, D>;
+  const int ql = lane & 31, g = lane >> 5;
+  if constexpr (BF) {
+    const int sub = lane & 15, grp = (lane >> 4) & 1;
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      bf16x8 pb;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) pb[j] = static_cast<__bf16>(p[8 * s + j]);
+      const int rowa = row0 + 16 * s + 4 * g + (sub >> 2);
+#pragma unroll
+      for (int db = 0; db < G::DB; ++db) {
+        int col = db * 32 + 16 * grp + 4 * (sub & 3);
+        if constexpr (D % 32 != 0) col = min(col, D - 4);   // stay inside the row; zeroed below
+        const u16x4 lo = ds_read_tr16(tile + rowa * G::ST + col);
+        const u16x4 hi = ds_read_tr16(tile + (rowa + 8) * G::ST + col);
+        u16x8 a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        if constexpr (D % 32 != 0) {
+          if (db * 32 + ql >= D) a = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
+        }
+        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), pb, acc[db], 0, 0, 0);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int st = 0; st < 16; ++st) {
+      const int row = row0 + 8 * (st >> 2) + 4 * g + (st & 3);
+#pragma unroll
+      for (int db = 0; db < G::DB; ++db) {
+        const int d = db * 32 + ql;
+        const float a = (D % 32 == 0 || d < D) ? tile[row * G::ST + d] : 0.f;
+        acc[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, p[st], acc[db], 0, 0, 0);
+      }
+    }
+  }
+}
+
+// Store a [d x 32] accumulator (lane = row of the output, registers = head dim)
+// to out[row][h][:], multiplied by `mul`.
+template <bool BF, int D>
+__device__ __forceinline__ void store_acc_row(void* outp, int64_t off, const floatx16 (&acc)[Geo<BF, D>::DB],
+                                              float mul, int g) {
+  using G = Geo<BF, D>;
+#pragma unroll
+  for (int db = 0; db < G::DB; ++db)
+#pragma unroll
+    for (int i4 = 0; i4 < 4; ++i4) {
+      const int d0 = db * 32 + 8 * i4 + 4 * g;
+      if (d0 < D) {
+        if constexpr (BF) {
+          uint16_t* O = static_cast<uint16_t*>(outp) + off + d0;
+          const uint32_t lo = f32_to_bf16(acc[db][4 * i4 + 0] * mul) | (uint32_t(f32_to_bf16(acc[db][4 * i4 + 1] * mul)) << 16);
+          const uint32_t hi = f32_to_bf16(acc[db][4 * i4 + 2] * mul) | (uint32_t(f32_to_bf16(acc[db][4 * i4 + 3] * mul)) << 16);
+          *reinterpret_cast<uint2*>(O) = make_uint2(lo, hi);
+        } else {
+          float* O = static_cast<float*>(outp) + off + d0;
+          *reinterpret_cast<float4*>(O) = make_float4(acc[db][4 * i4 + 0] * mul, acc[db][4 * i4 + 1] * mul,
+                                                      acc[db][4 * i4 + 2] * mul, acc[db][4 * i4 + 3] * mul);
+        }
+      }
+    }
+}
+
+// The sequences one tile of kAttnTileRows packed rows touches: their offsets
+// are staged in `cul` (at most kAttnTileRows + 2 entries) and the range of
+// rows they span [lo, hi) is returned.
+struct TileSpan {
+  int r0, rend, ncu, lo, hi;
+};
+
+__device__ __forceinline__ TileSpan tile_span(const int32_t* __restrict__ cu, const int32_t* __restrict__ items,
+                                              int t, int B, int N, int32_t* cul) {
+  TileSpan s;
+  s.r0 = t * kAttnTileRows;
+  s.rend = min(s.r0 + kAttnTileRows, N);
+  const int blo = items[t], nxt = items[t + 1];
+  const int bhi = nxt >= B ? B - 1 : (cu[nxt] == s.rend ? nxt - 1 : nxt);
+  // at most kAttnTileRows + 1 sequences touch a tile when every length is >= 1;
+  // the clamp keeps LDS writes in bounds even for malformed offsets
+  s.ncu = min(bhi - blo + 2, kAttnTileRows + 2);
+  for (int i = threadIdx.x; i < s.ncu; i += kThreads) cul[i] = cu[blo + i];
+  __syncthreads();
+  s.lo = cul[0];
+  s.hi = cul[s.ncu - 1];
+  return s;
+}
+
+// [first, last) rows of the sequence holding `row` (binary search in cul).
+__device__ __forceinline__ void own_range(const int32_t* cul, int ncu, int row, int& lo_out, int& hi_out) {
+  int lo = 0, hi = ncu - 2;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (cul[mid] <= row) lo = mid; else hi = mid - 1;
+  }
+  lo_out = cul[lo];
+  hi_out = cul[lo + 1];
+}
+
+// Set entries of a 32x32 score block outside [lo, hi) (row index relative to
+// the block's first row, per register) to -inf.
+__device__ __forceinline__ void mask_block(floatx16& s, int lo, int hi) {
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int r = 8 * (i >> 2) + (i & 3);
+    if (r < lo || r >= hi) s[i] = -INFINITY;
+  }
+}
+
+}  // namespace pe

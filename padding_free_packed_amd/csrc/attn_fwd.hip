@@ -8,230 +8,96 @@
 // launch without padding any sequence to a tile.
 //
 // Each of the 4 waves owns 32 query rows. Per 64-key block staged in LDS:
-//   S^T (32 keys x 32 queries) = K Q^T          MFMA, A = K rows from LDS, B = Q in registers
+//   S^T (32 keys x 32 queries) = K Q^T     (mma_rows_regs: K from LDS, Q in registers)
 //   online softmax in base 2 (scale*log2(e) folded into one FMA)
-//   O^T (d x 32 queries) += V^T P^T             MFMA, B = P straight from the S^T accumulators
+//   O^T (d x 32 queries) += V^T P^T        (mma_tr_regs: V from LDS, P straight from S^T)
 // Computing S transposed leaves every lane with one query and 16 of its keys,
-// the layout the PV product needs as its B operand, so P never goes through
-// LDS. The order of the reduction index of an MFMA is free as long as A and B
-// agree, which lets V^T be read in the order the S^T accumulators hold keys.
+// the layout the PV product needs as its B operand, so P never goes through LDS.
 #include <climits>
 #include <type_traits>
 
-#include "common.h"
-#include "kernels.h"
+#include "attn_common.h"
 
 namespace pe {
 
 namespace {
 
-constexpr int BM = kAttnTileRows;  // query rows per block
-constexpr int BN = 64;             // keys per LDS stage
-constexpr int NT = 256;            // 4 waves
-
 template <bool BF, int D>
-struct Shape {
-  static constexpr int ES = BF ? 2 : 4;
-  static constexpr int ROWB = D * ES;           // bytes of one head row
-  static constexpr int CH = ROWB / 16;          // 16-byte chunks per head row
-  static constexpr int EPC = 16 / ES;           // elements per chunk
-  static constexpr int KST = BF ? D + 8 : D + 4;    // K tile: [BN][KST]
-  static constexpr int VST = BF ? BN + 8 : D + 8;   // bf16: V^T tile [D][VST]; fp32: V tile [BN][VST]
-  static constexpr int KSZ = BN * KST;
-  static constexpr int VSZ = BF ? D * VST : BN * VST;
-  static constexpr int HALF = D / 2;            // head-dim elements per lane half
-  static constexpr int QS = BF ? (HALF + 7) / 8 : HALF;  // MFMA steps of S
-  static constexpr int DB = (D + 31) / 32;      // 32-row blocks of O^T
-  static constexpr int TOTCH = BN * CH;
-  static constexpr int PER = (TOTCH + NT - 1) / NT;
-};
-
-// Position of key r (0..63) inside the bf16 V^T tile: within every 16 keys
-// the middle two quads swap, matching the key order of the S^T accumulators.
-__device__ __forceinline__ int vt_pos(int r) {
-  return (r & ~15) | (((r >> 2) & 1) << 3) | (((r >> 3) & 1) << 2) | (r & 3);
-}
-
-template <bool BF>
-struct QReg;
-template <>
-struct QReg<true> { using T = bf16x8; };
-template <>
-struct QReg<false> { using T = float; };
-
-__device__ __forceinline__ bf16x8 u16x8_as_bf16(u16x8 x) { return __builtin_bit_cast(bf16x8, x); }
-
-template <bool BF, int D>
-__device__ __forceinline__ void load_q(const void* qp, int64_t off, bool valid,
-                                       typename QReg<BF>::T (&q)[Shape<BF, D>::QS]) {
-  using Sh = Shape<BF, D>;
-  if constexpr (BF) {
-    const uint16_t* src = static_cast<const uint16_t*>(qp) + off;
-#pragma unroll
-    for (int s = 0; s < Sh::QS; ++s) {
-      u16x8 x = {0, 0, 0, 0, 0, 0, 0, 0};
-      if (valid) {
-        if constexpr (Sh::HALF >= 8) {
-          x = *reinterpret_cast<const u16x8*>(src + 8 * s);
-        } else {
-#pragma unroll
-          for (int j = 0; j < Sh::HALF; ++j) x[j] = src[j];
-        }
-      }
-      q[s] = u16x8_as_bf16(x);
-    }
-  } else {
-    const float* src = static_cast<const float*>(qp) + off;
-#pragma unroll
-    for (int s = 0; s < Sh::QS; ++s) q[s] = valid ? src[s] : 0.f;
-  }
-}
-
-template <bool BF, int D>
-__global__ __launch_bounds__(NT, 2) void attn_fwd_kernel(
+__global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
     const void* __restrict__ qp, const void* __restrict__ kp, const void* __restrict__ vp,
     const int32_t* __restrict__ cu, const int32_t* __restrict__ items, int32_t B, int32_t N,
     int32_t H, int32_t T, float c, void* __restrict__ op, float* __restrict__ lse) {
-  using Sh = Shape<BF, D>;
-  using E = typename std::conditional<BF, uint16_t, float>::type;
-  __shared__ __align__(16) E kl[2][Sh::KSZ];
-  __shared__ __align__(16) E vl[2][Sh::VSZ];
-  __shared__ int32_t cul[BM + 2];
+  using G = Geo<BF, D>;
+  using E = typename G::E;
+  __shared__ __align__(16) E kt[2][G::TSZ];
+  __shared__ __align__(16) E vt[2][G::TSZ];
+  __shared__ int32_t cul[kAttnTileRows + 2];
 
   const int lin = xcd_remap(blockIdx.x, gridDim.x);
   const int h = lin / T, t = lin - h * T;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, ql = lane & 31, g = lane >> 5;
 
-  // ---- the sequences this tile touches and the key range they span
-  const int r0 = t * BM, rend = min(r0 + BM, N);
-  const int blo = items[t], nxt = items[t + 1];
-  const int bhi = nxt >= B ? B - 1 : (cu[nxt] == rend ? nxt - 1 : nxt);
-  // at most BM + 1 sequences touch BM rows when every length is >= 1; the
-  // clamp keeps LDS writes in bounds even for malformed offsets
-  const int ncu = min(bhi - blo + 2, BM + 2);
-  for (int i = tid; i < ncu; i += NT) cul[i] = cu[blo + i];
-  __syncthreads();
-  const int kb0 = cul[0], kb1 = cul[ncu - 1];
+  // the sequences this tile touches; their keys are [sp.lo, sp.hi)
+  const TileSpan sp = tile_span(cu, items, t, B, N, cul);
 
-  // ---- this lane's query row and its own key range [qk0, qk1)
-  const int qrow = r0 + wv * 32 + ql;
-  const bool qvalid = qrow < rend;
+  // this lane's query row and its own key range [qk0, qk1)
+  const int qrow = sp.r0 + wv * 32 + ql;
+  const bool qvalid = qrow < sp.rend;
   int qk0 = 0, qk1 = 0;
-  if (qvalid) {
-    int lo = 0, hi = ncu - 2;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (cul[mid] <= qrow) lo = mid; else hi = mid - 1;
-    }
-    qk0 = cul[lo];
-    qk1 = cul[lo + 1];
-  }
+  if (qvalid) own_range(cul, sp.ncu, qrow, qk0, qk1);
   const int wk0 = wave_min_i(qvalid ? qk0 : INT_MAX);  // keys any row of the wave needs
   const int wk1 = wave_max_i(qvalid ? qk1 : INT_MIN);
   const int mk0 = wave_max_i(qvalid ? qk0 : INT_MIN);  // keys every row of the wave needs
   const int mk1 = wave_min_i(qvalid ? qk1 : INT_MAX);
 
-  typename QReg<BF>::T qr[Sh::QS];
-  load_q<BF, D>(qp, (static_cast<int64_t>(qrow) * H + h) * D + g * Sh::HALF, qvalid, qr);
+  typename RegT<BF>::T qr[G::QS];
+  load_row_regs<BF, D>(qp, (static_cast<int64_t>(qrow) * H + h) * D + g * G::HALF, qvalid, qr);
 
-  // ---- K/V staging: global -> registers (prefetch) -> LDS
-  uint4 kr[Sh::PER], vr[Sh::PER];
-  const char* kbase = static_cast<const char*>(kp);
-  const char* vbase = static_cast<const char*>(vp);
-  auto gload = [&](int kb) {
+  uint4 kr[G::PER], vr[G::PER];
+  floatx16 o[G::DB];
 #pragma unroll
-    for (int p = 0; p < Sh::PER; ++p) {
-      const int ch = tid + p * NT;
-      const int row = ch / Sh::CH, col = ch - row * Sh::CH;
-      const int key = kb + row;
-      if ((Sh::TOTCH % NT == 0 || ch < Sh::TOTCH) && key < kb1) {
-        const int64_t off = (static_cast<int64_t>(key) * H + h) * Sh::ROWB + col * 16;
-        kr[p] = *reinterpret_cast<const uint4*>(kbase + off);
-        vr[p] = *reinterpret_cast<const uint4*>(vbase + off);
-      } else {
-        kr[p] = make_uint4(0, 0, 0, 0);
-        vr[p] = make_uint4(0, 0, 0, 0);
-      }
-    }
-  };
-  auto swrite = [&](int buf) {
-#pragma unroll
-    for (int p = 0; p < Sh::PER; ++p) {
-      const int ch = tid + p * NT;
-      if (Sh::TOTCH % NT == 0 || ch < Sh::TOTCH) {
-        const int row = ch / Sh::CH, col = ch - row * Sh::CH;
-        *reinterpret_cast<uint4*>(&kl[buf][row * Sh::KST + col * Sh::EPC]) = kr[p];
-        if constexpr (BF) {
-          const u16x8 x = __builtin_bit_cast(u16x8, vr[p]);
-          const int kpos = vt_pos(row);
-#pragma unroll
-          for (int i = 0; i < 8; ++i) vl[buf][(col * 8 + i) * Sh::VST + kpos] = x[i];
-        } else {
-          *reinterpret_cast<uint4*>(&vl[buf][row * Sh::VST + col * 4]) = vr[p];
-        }
-      }
-    }
-  };
-
-  floatx16 o[Sh::DB];
-#pragma unroll
-  for (int db = 0; db < Sh::DB; ++db) o[db] = floatx16{};
+  for (int db = 0; db < G::DB; ++db) o[db] = floatx16{};
   float m = kNegBig, l = 0.f;
 
   int buf = 0;
-  if (kb0 < kb1) gload(kb0);
-  for (int kb = kb0; kb < kb1; kb += BN) {
-    swrite(buf);
+  if (sp.lo < sp.hi) {
+    tile_gload<BF, D>(kp, sp.lo, sp.hi, H, h, kr);
+    tile_gload<BF, D>(vp, sp.lo, sp.hi, H, h, vr);
+  }
+  for (int kb = sp.lo; kb < sp.hi; kb += kBlk) {
+    tile_store<BF, D>(kt[buf], kr);
+    tile_store<BF, D>(vt[buf], vr);
     __syncthreads();
-    if (kb + BN < kb1) gload(kb + BN);
-    if (kb < wk1 && kb + BN > wk0) {
-      const E* K = kl[buf];
-      const E* V = vl[buf];
+    if (kb + kBlk < sp.hi) {
+      tile_gload<BF, D>(kp, kb + kBlk, sp.hi, H, h, kr);
+      tile_gload<BF, D>(vp, kb + kBlk, sp.hi, H, h, vr);
+    }
+    if (kb < wk1 && kb + kBlk > wk0) {
       floatx16 s[2];
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
         s[kk] = floatx16{};
-        const E* krow = K + (kk * 32 + ql) * Sh::KST + g * Sh::HALF;
-#pragma unroll
-        for (int st = 0; st < Sh::QS; ++st) {
-          if constexpr (BF) {
-            u16x8 a;
-            if constexpr (Sh::HALF >= 8) {
-              a = *reinterpret_cast<const u16x8*>(krow + 8 * st);
-            } else {
-              a = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
-#pragma unroll
-              for (int j = 0; j < Sh::HALF; ++j) a[j] = krow[j];
-            }
-            s[kk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(u16x8_as_bf16(a), qr[st], s[kk], 0, 0, 0);
-          } else {
-            s[kk] = __builtin_amdgcn_mfma_f32_32x32x2f32(krow[st], qr[st], s[kk], 0, 0, 0);
-          }
-        }
+        mma_rows_regs<BF, D>(kt[buf], 32 * kk, qr, s[kk], ql, g);
       }
-      // keys outside the lane's own sequence
-      if (!(kb >= mk0 && kb + BN <= mk1)) {
-        const int lo = qk0 - kb - 4 * g, hi = qk1 - kb - 4 * g;
+      if (!(kb >= mk0 && kb + kBlk <= mk1)) {
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int kidx = 32 * kk + 8 * (i >> 2) + (i & 3);
-            if (kidx < lo || kidx >= hi) s[kk][i] = -INFINITY;
-          }
+        for (int kk = 0; kk < 2; ++kk) {
+          const int base = kb + 32 * kk + 4 * g;
+          mask_block(s[kk], qk0 - base, qk1 - base);
+        }
       }
       float mx = -INFINITY;
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
         for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kk][i]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      mx = xhalf_max(mx);
       const float mnew = fmaxf(m, mx * c);
       if (__any(mnew > m)) {
         const float alpha = __builtin_amdgcn_exp2f(m - mnew);
         l *= alpha;
 #pragma unroll
-        for (int db = 0; db < Sh::DB; ++db)
+        for (int db = 0; db < G::DB; ++db)
 #pragma unroll
           for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
         m = mnew;
@@ -244,64 +110,16 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_kernel(
           s[kk][i] = p;
           l += p;
         }
-      // O^T += V^T P^T
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        if constexpr (BF) {
-#pragma unroll
-          for (int st = 0; st < 2; ++st) {
-            bf16x8 pb;
-#pragma unroll
-            for (int j = 0; j < 8; ++j) pb[j] = static_cast<__bf16>(s[kk][8 * st + j]);
-#pragma unroll
-            for (int db = 0; db < Sh::DB; ++db) {
-              const int d = db * 32 + ql;
-              u16x8 a = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
-              if (D % 32 == 0 || d < D)
-                a = *reinterpret_cast<const u16x8*>(V + d * Sh::VST + 32 * kk + 16 * st + 8 * g);
-              o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(u16x8_as_bf16(a), pb, o[db], 0, 0, 0);
-            }
-          }
-        } else {
-#pragma unroll
-          for (int st = 0; st < 16; ++st) {
-            const int krow = 32 * kk + 8 * (st >> 2) + 4 * g + (st & 3);
-#pragma unroll
-            for (int db = 0; db < Sh::DB; ++db) {
-              const int d = db * 32 + ql;
-              const float a = (D % 32 == 0 || d < D) ? V[krow * Sh::VST + d] : 0.f;
-              o[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, s[kk][st], o[db], 0, 0, 0);
-            }
-          }
-        }
-      }
+      for (int kk = 0; kk < 2; ++kk) mma_tr_regs<BF, D>(vt[buf], 32 * kk, s[kk], o, lane);
     }
     buf ^= 1;
   }
 
-  // ---- normalise and store
-  const float lt = l + __shfl_xor(l, 32);
+  const float lt = xhalf_sum(l);
   const float inv = lt > 0.f ? 1.f / lt : 0.f;
   if (qvalid) {
-    const int64_t obase = (static_cast<int64_t>(qrow) * H + h) * D;
-#pragma unroll
-    for (int db = 0; db < Sh::DB; ++db)
-#pragma unroll
-      for (int i4 = 0; i4 < 4; ++i4) {
-        const int d0 = db * 32 + 8 * i4 + 4 * g;
-        if (d0 < D) {
-          if constexpr (BF) {
-            uint16_t* O = static_cast<uint16_t*>(op) + obase + d0;
-            const uint32_t lo = f32_to_bf16(o[db][4 * i4 + 0] * inv) | (uint32_t(f32_to_bf16(o[db][4 * i4 + 1] * inv)) << 16);
-            const uint32_t hi = f32_to_bf16(o[db][4 * i4 + 2] * inv) | (uint32_t(f32_to_bf16(o[db][4 * i4 + 3] * inv)) << 16);
-            *reinterpret_cast<uint2*>(O) = make_uint2(lo, hi);
-          } else {
-            float* O = static_cast<float*>(op) + obase + d0;
-            *reinterpret_cast<float4*>(O) = make_float4(o[db][4 * i4 + 0] * inv, o[db][4 * i4 + 1] * inv,
-                                                        o[db][4 * i4 + 2] * inv, o[db][4 * i4 + 3] * inv);
-          }
-        }
-      }
+    store_acc_row<BF, D>(op, (static_cast<int64_t>(qrow) * H + h) * D, o, inv, g);
     if (lse != nullptr && g == 0) lse[static_cast<int64_t>(h) * N + qrow] = (m + log2f(lt)) * kLn2;
   }
 }
@@ -413,12 +231,14 @@ template <bool BF, int D>
 hipError_t fwd_dispatch(const void* q, const void* k, const void* v, const int32_t* cu,
                         const int32_t* items, int32_t B, int32_t N, int32_t H, float scale, void* out,
                         float* lse, hipStream_t stream) {
-  const int T = (N + BM - 1) / BM;
+  const int T = (N + kAttnTileRows - 1) / kAttnTileRows;
   const int64_t blocks = static_cast<int64_t>(T) * H;
   if (blocks == 0) return hipSuccess;
   const float c = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
-  hipLaunchKernelGGL((attn_fwd_kernel<BF, D>), dim3(static_cast<unsigned>(blocks)), dim3(NT), 0, stream,
-                     q, k, v, cu, items, B, N, H, T, c, out, lse);
+  hipEvent_t ev_attn_fwd = timing_start(stream);
+  hipLaunchKernelGGL((attn_fwd_kernel<BF, D>), dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0, stream,
+                   q, k, v, cu, items, B, N, H, T, c, out, lse);
+  timing_stop("attn_fwd", ev_attn_fwd, stream);
   return hipGetLastError();
 }
 
@@ -429,8 +249,10 @@ hipError_t first_dispatch(const void* q, const void* k, const void* v, const int
   const int HPB = (H * GS <= 256) ? H : 256 / GS;
   const int HG = (H + HPB - 1) / HPB;
   const float c = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
+  hipEvent_t ev_attn_fwd_first = timing_start(stream);
   hipLaunchKernelGGL((attn_fwd_first_kernel<BF, D>), dim3(B, HG), dim3(256), 0, stream, q, k, v, cu, B,
-                     N, H, HPB, c, out, lse);
+                   N, H, HPB, c, out, lse);
+  timing_stop("attn_fwd_first", ev_attn_fwd_first, stream);
   return hipGetLastError();
 }
 

@@ -5,6 +5,10 @@
 
 namespace pe {
 
+// Per-kernel timing hooks (no-ops unless pe_timing_enable(1) was called).
+hipEvent_t timing_start(hipStream_t stream);
+void timing_stop(const char* name, hipEvent_t start, hipStream_t stream);
+
 // packed query (or key) rows per attention work item
 constexpr int kAttnTileRows = 128;
 

@@ -168,8 +168,9 @@ __global__ __launch_bounds__(256) void unpack_rows_kernel(
 
 hipError_t launch_scan(const int32_t* lengths, int32_t B, int32_t S, int32_t* cu, int64_t* result,
                        hipStream_t stream) {
-  hipLaunchKernelGGL(scan_lengths_kernel, dim3(1), dim3(kScanThreads), 0, stream, lengths, B, S, cu,
-                     result);
+  hipEvent_t ev = timing_start(stream);
+  hipLaunchKernelGGL(scan_lengths_kernel, dim3(1), dim3(kScanThreads), 0, stream, lengths, B, S, cu, result);
+  timing_stop("scan", ev, stream);
   return hipGetLastError();
 }
 
@@ -177,7 +178,9 @@ hipError_t launch_worklist(const int32_t* cu, int32_t B, int64_t N, int32_t R, i
                            hipStream_t stream) {
   const int threads = 256;
   const int blocks = static_cast<int>((static_cast<int64_t>(B) + threads - 1) / threads);
+  hipEvent_t ev = timing_start(stream);
   hipLaunchKernelGGL(worklist_kernel, dim3(blocks), dim3(threads), 0, stream, cu, B, N, R, items);
+  timing_stop("worklist", ev, stream);
   return hipGetLastError();
 }
 
@@ -194,6 +197,16 @@ static int unit_bytes(int64_t rowbytes, const void* a, const void* b) {
   return 1;
 }
 
+template <typename U>
+static void pack_rows_typed(const char* g, char* p, int64_t* flat_index, const int32_t* cu, const int32_t* items,
+                            int32_t B, int32_t S, int64_t rowbytes, int64_t N, int32_t R, unsigned blocks,
+                            hipStream_t stream) {
+  hipEvent_t ev = timing_start(stream);
+  hipLaunchKernelGGL(pack_rows_kernel<U>, dim3(blocks), dim3(256), 0, stream, g, p, flat_index, cu, items, B, S,
+                     rowbytes, N, R);
+  timing_stop("pack_rows", ev, stream);
+}
+
 hipError_t launch_pack_rows(const void* grid, void* packed, int64_t* flat_index, const int32_t* cu,
                             const int32_t* items, int32_t B, int32_t S, int64_t rowbytes, int64_t N,
                             int32_t R, hipStream_t stream) {
@@ -202,15 +215,23 @@ hipError_t launch_pack_rows(const void* grid, void* packed, int64_t* flat_index,
   const char* g = static_cast<const char*>(grid);
   char* p = static_cast<char*>(packed);
   const int u = packed ? unit_bytes(rowbytes, grid, packed) : 16;
-  const dim3 gd(static_cast<unsigned>(blocks)), bd(256);
+  const unsigned nb = static_cast<unsigned>(blocks);
   switch (u) {
-    case 16: hipLaunchKernelGGL(pack_rows_kernel<uint4>, gd, bd, 0, stream, g, p, flat_index, cu, items, B, S, rowbytes, N, R); break;
-    case 8: hipLaunchKernelGGL(pack_rows_kernel<uint2>, gd, bd, 0, stream, g, p, flat_index, cu, items, B, S, rowbytes, N, R); break;
-    case 4: hipLaunchKernelGGL(pack_rows_kernel<uint32_t>, gd, bd, 0, stream, g, p, flat_index, cu, items, B, S, rowbytes, N, R); break;
-    case 2: hipLaunchKernelGGL(pack_rows_kernel<uint16_t>, gd, bd, 0, stream, g, p, flat_index, cu, items, B, S, rowbytes, N, R); break;
-    default: hipLaunchKernelGGL(pack_rows_kernel<uint8_t>, gd, bd, 0, stream, g, p, flat_index, cu, items, B, S, rowbytes, N, R); break;
+    case 16: pack_rows_typed<uint4>(g, p, flat_index, cu, items, B, S, rowbytes, N, R, nb, stream); break;
+    case 8: pack_rows_typed<uint2>(g, p, flat_index, cu, items, B, S, rowbytes, N, R, nb, stream); break;
+    case 4: pack_rows_typed<uint32_t>(g, p, flat_index, cu, items, B, S, rowbytes, N, R, nb, stream); break;
+    case 2: pack_rows_typed<uint16_t>(g, p, flat_index, cu, items, B, S, rowbytes, N, R, nb, stream); break;
+    default: pack_rows_typed<uint8_t>(g, p, flat_index, cu, items, B, S, rowbytes, N, R, nb, stream); break;
   }
   return hipGetLastError();
+}
+
+template <typename U>
+static void unpack_rows_typed(const char* p, char* g, const int32_t* cu, int32_t B, int32_t S, int64_t rowbytes,
+                              int64_t R, unsigned blocks, hipStream_t stream) {
+  hipEvent_t ev = timing_start(stream);
+  hipLaunchKernelGGL(unpack_rows_kernel<U>, dim3(blocks), dim3(256), 0, stream, p, g, cu, B, S, rowbytes, R);
+  timing_stop("unpack_rows", ev, stream);
 }
 
 hipError_t launch_unpack_rows(const void* packed, void* grid, const int32_t* cu, int32_t B, int32_t S,
@@ -222,13 +243,13 @@ hipError_t launch_unpack_rows(const void* packed, void* grid, const int32_t* cu,
   const char* p = static_cast<const char*>(packed);
   char* g = static_cast<char*>(grid);
   const int u = unit_bytes(rowbytes, packed, grid);
-  const dim3 gd(static_cast<unsigned>(blocks)), bd(256);
+  const unsigned nb = static_cast<unsigned>(blocks);
   switch (u) {
-    case 16: hipLaunchKernelGGL(unpack_rows_kernel<uint4>, gd, bd, 0, stream, p, g, cu, B, S, rowbytes, R); break;
-    case 8: hipLaunchKernelGGL(unpack_rows_kernel<uint2>, gd, bd, 0, stream, p, g, cu, B, S, rowbytes, R); break;
-    case 4: hipLaunchKernelGGL(unpack_rows_kernel<uint32_t>, gd, bd, 0, stream, p, g, cu, B, S, rowbytes, R); break;
-    case 2: hipLaunchKernelGGL(unpack_rows_kernel<uint16_t>, gd, bd, 0, stream, p, g, cu, B, S, rowbytes, R); break;
-    default: hipLaunchKernelGGL(unpack_rows_kernel<uint8_t>, gd, bd, 0, stream, p, g, cu, B, S, rowbytes, R); break;
+    case 16: unpack_rows_typed<uint4>(p, g, cu, B, S, rowbytes, R, nb, stream); break;
+    case 8: unpack_rows_typed<uint2>(p, g, cu, B, S, rowbytes, R, nb, stream); break;
+    case 4: unpack_rows_typed<uint32_t>(p, g, cu, B, S, rowbytes, R, nb, stream); break;
+    case 2: unpack_rows_typed<uint16_t>(p, g, cu, B, S, rowbytes, R, nb, stream); break;
+    default: unpack_rows_typed<uint8_t>(p, g, cu, B, S, rowbytes, R, nb, stream); break;
   }
   return hipGetLastError();
 }

@@ -25,7 +25,7 @@ PE_FP32, PE_BF16 = 0, 1
 EXPORTS = (
     "pe_status_string", "pe_attn_tile_rows", "pe_pack_workspace_size", "pe_pack", "pe_unpack",
     "pe_worklist", "pe_attn_workspace_size", "pe_varlen_attn_fwd", "pe_varlen_attn_fwd_first_token",
-    "pe_varlen_attn_bwd",
+    "pe_varlen_attn_bwd", "pe_timing_enable", "pe_timing_read",
 )
 
 
@@ -56,6 +56,8 @@ def _load():
                                                            F, P, P, P]),
         "pe_varlen_attn_bwd": (ctypes.c_int, [P, P, P, P, P, P, P, I32, I64, I32, I32, I32, ctypes.c_int, F,
                                                P, P, P, P, SZ, P]),
+        "pe_timing_enable": (ctypes.c_int, [ctypes.c_int]),
+        "pe_timing_read": (ctypes.c_int, [P, P, ctypes.c_int]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -162,6 +164,21 @@ def pe_varlen_attn_bwd(dout, q, k, v, out, lse, cu_seqlens, num_seqs, total_toke
                                  _dtype_code(q), softmax_scale, _ptr(dq), _ptr(dk), _ptr(dv),
                                  _ptr(workspace), workspace.numel(), _stream())
     _check("pe_varlen_attn_bwd", st)
+
+
+# ------------------------------------------------------------------ kernel timing
+
+def pe_timing_enable(on: bool) -> None:
+    _check("pe_timing_enable", _lib.pe_timing_enable(int(bool(on))))
+
+
+def pe_timing_read(max_records: int = 4096):
+    """[(kernel name, milliseconds)] of the kernels launched since the last read."""
+    names = ctypes.create_string_buffer(32 * max_records)
+    ms = (ctypes.c_float * max_records)()
+    n = _lib.pe_timing_read(ctypes.cast(names, ctypes.c_void_p), ctypes.cast(ms, ctypes.c_void_p), max_records)
+    raw = names.raw
+    return [(raw[32 * i:32 * i + 32].split(b"\0", 1)[0].decode(), float(ms[i])) for i in range(n)]
 
 
 # ------------------------------------------------------------------ allocating helpers

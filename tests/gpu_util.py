@@ -6,7 +6,9 @@ Tolerances (written here once, used by every parity test):
   |ref| >= 0.1 (below that the absolute bound governs);
 * bf16 in / fp32 accumulate: max |gpu - ref| <= 2e-2, and the cosine between
   the GPU and oracle vectors of every token row (all heads and head dims of
-  that row) >= 0.999; rows whose norms are both < 1e-30 pass;
+  that row) >= 0.999 for rows whose oracle norm exceeds 2e-2 (a row below the
+  per-element bound is rounding noise around zero, e.g. the exactly-zero dQ and
+  dK of a length-1 sequence, and is held by the element-wise bound alone);
 * log-sum-exp (always fp32): |delta| <= 1e-5 * max(1, |lse|) for fp32 inputs,
   |delta| <= 1e-3 for bf16 inputs;
 * integer and byte outputs: bit-exact.
@@ -58,11 +60,23 @@ def check_out(gpu: np.ndarray, ref: np.ndarray, dtype: str, what: str = "out"):
         assert err.max() <= 2e-2, f"{what}: max abs err {err.max():.3e} > 2e-2"
         g = gpu.reshape(gpu.shape[0], -1)
         r = ref.reshape(ref.shape[0], -1)
-        ng, nr = np.linalg.norm(g, axis=1), np.linalg.norm(r, axis=1)
-        both_zero = (ng < 1e-30) & (nr < 1e-30)
-        cos = np.where(both_zero, 1.0, (g * r).sum(1) / np.maximum(ng * nr, 1e-300))
-        assert cos.min() >= 0.999, f"{what}: min per-token cosine {cos.min():.6f} < 0.999"
+        c, i, nrm, e = min_cosine(g, r, where=True)
+        assert c >= 0.999, f"{what}: min per-token cosine {c:.6f} < 0.999 at row {i} (ref norm {nrm:.4g}, max err {e:.3g})"
     return float(err.max())
+
+
+def min_cosine(g: np.ndarray, r: np.ndarray, where: bool = False):
+    """Smallest per-row cosine over rows whose reference norm exceeds 2e-2
+    (with where=True also the row index, its reference norm and max abs error)."""
+    ng, nr = np.linalg.norm(g, axis=1), np.linalg.norm(r, axis=1)
+    keep = nr > 2e-2
+    if not keep.any():
+        return (1.0, -1, 0.0, 0.0) if where else 1.0
+    cos = np.where(keep, (g * r).sum(1) / np.maximum(ng * nr, 1e-300), 2.0)
+    i = int(np.argmin(cos))
+    if where:
+        return float(cos[i]), i, float(nr[i]), float(np.abs(g[i] - r[i]).max())
+    return float(cos[i])
 
 
 def check_lse(gpu: np.ndarray, ref: np.ndarray, dtype: str, what: str = "lse"):

@@ -27,7 +27,7 @@ def _header_functions():
 
 def test_header_symbols_exported():
     names = _header_functions()
-    assert len(names) == 10
+    assert len(names) == 12
     for n in names:
         assert hasattr(lib, n), n
     assert sorted(pe.EXPORTS) == names
