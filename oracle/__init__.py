@@ -26,7 +26,9 @@ gigl.nn.packed_attention" and the packed-encoders README):
 * ``attention_backward``: gradients of the same definition in Q, K and V, with no
   gradient flowing into the log-sum-exp (GiGL ``_varlen_attention_backward``
   drops the log-sum-exp's gradient). The pages give no formulas; these are the
-  derivatives of softmax attention, written out from its definition.
+  derivatives of softmax attention, written out from its definition. As GiGL's
+  backward op does, it can take the forward's output and log-sum-exp as inputs
+  (its D term is formed from the output it is given).
 * ``padded_attention``: an independent second route, the padded grid with an
   additive ``finfo.min / 2`` key bias and a dense softmax over all positions,
   as ``_padded_packed_attention`` does.
@@ -223,14 +225,19 @@ def attention_first_token(q_first, k, v, cu_seqlens, scale: float, seqs=None):
     return o, lse
 
 
-def attention_backward(dout, q, k, v, cu_seqlens, scale: float, seqs=None):
+def attention_backward(dout, q, k, v, cu_seqlens, scale: float, seqs=None, out=None, lse=None):
     """Gradients of ``<dout, attention(q, k, v)>`` in q, k and v.
 
     Per sequence and head, with P = softmax(scale * Q K^T) (rows) and O = P V:
     dV = P^T dO; dP = dO V^T; D_i = sum_c dO_ic O_ic; dS = P * (dP - D);
-    dQ = scale * dS K; dK = scale * dS^T Q. O and the log-sum-exp come from
-    this module's own forward (P_ij = exp(s_ij - lse_i)). No gradient enters
-    through the log-sum-exp, as in GiGL's ``_varlen_attention_backward``.
+    dQ = scale * dS K; dK = scale * dS^T Q. No gradient enters through the
+    log-sum-exp, as in GiGL's ``_varlen_attention_backward``.
+
+    GiGL's backward op receives the forward's ``output`` and ``logsumexp`` as
+    inputs; ``out`` [N, H, d] and ``lse`` [H, N] play those roles here: when
+    given, D is formed from ``out`` and P = exp(s - lse) from ``lse``. When
+    omitted they are this module's own float64 forward, and the result is the
+    exact gradient.
 
     ``seqs`` optionally limits the computation to some sequences (rows of other
     sequences are left zero). Returns dq, dk, dv float64 [N, H, d].
@@ -247,10 +254,13 @@ def attention_backward(dout, q, k, v, cu_seqlens, scale: float, seqs=None):
         for h in range(H):
             qs, ks, vs, dos = q[c0:c1, h, :], k[c0:c1, h, :], v[c0:c1, h, :], dout[c0:c1, h, :]
             s = scale * (qs @ ks.T)
-            m = s.max(axis=1, keepdims=True)
-            lse = m + np.log(np.exp(s - m).sum(axis=1, keepdims=True))
-            p = np.exp(s - lse)
-            o = p @ vs
+            if lse is None:
+                m = s.max(axis=1, keepdims=True)
+                lse_b = m + np.log(np.exp(s - m).sum(axis=1, keepdims=True))
+            else:
+                lse_b = np.asarray(lse, dtype=np.float64)[h, c0:c1][:, None]
+            p = np.exp(s - lse_b)
+            o = p @ vs if out is None else np.asarray(out, dtype=np.float64)[c0:c1, h, :]
             dv[c0:c1, h, :] = p.T @ dos
             dp = dos @ vs.T
             D = (dos * o).sum(axis=1, keepdims=True)

@@ -174,7 +174,7 @@ pe_status pe_varlen_attn_fwd(const void* q, const void* k, const void* v, const 
   hipError_t e = pe::launch_worklist(cu_seqlens, num_seqs, total_tokens, pe::kAttnTileRows, items, st);
   if (e != hipSuccess) return PE_ERR_HIP;
   e = pe::launch_attn_fwd(dtype == PE_BF16, head_dim, q, k, v, cu_seqlens, items, num_seqs,
-                          static_cast<int32_t>(total_tokens), num_heads, softmax_scale, out, lse, st);
+                          static_cast<int32_t>(total_tokens), num_heads, max_seq_len, softmax_scale, out, lse, st);
   return hip_status(e);
 }
 

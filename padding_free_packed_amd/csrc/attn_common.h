@@ -275,4 +275,125 @@ __device__ __forceinline__ void mask_block(floatx16& s, int lo, int hi) {
   }
 }
 
+// ---------------------------------------------------------------- bf16 tiles staged by LDS DMA
+// bf16 tiles of kBlk rows x D elements are copied global -> LDS by
+// global_load_lds_dwordx4 (no registers, no VALU) into a ring of stages. Rows
+// are not padded; instead the 16-byte chunk c of row r sits at position
+// c ^ swz(r) of the row. With 64 LDS banks of 4 bytes this puts the 16 rows of
+// one ds_read_b128 phase (same logical chunk) on 16 distinct bank groups, and
+// the 4 rows x 4 chunks of one ds_read_b64_tr_b16 phase likewise.
+__device__ __forceinline__ int swz(int r) { return (((r >> 1) & 1) << 2) | ((r >> 2) & 3); }
+
+// byte offset of logical 16-byte chunk c of row r in a tile with CH chunks per row
+template <int CH>
+__device__ __forceinline__ int chunk_off(int r, int c) {
+  return (r * CH + (c ^ (swz(r) & (CH - 1)))) * 16;
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return static_cast<uint32_t>(reinterpret_cast<size_t>((__attribute__((address_space(3))) const char*)(p)));
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// s_waitcnt vmcnt(0) issued through the builtin, so the compiler's own wait
+// tracking knows every earlier VMEM load has completed (gfx9 encoding: expcnt
+// and lgkmcnt left at their no-wait maxima).
+__device__ __forceinline__ void vmem_fence_for_compiler() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// Barrier without the memory fence of __syncthreads(): the waits that matter
+// (LDS-DMA completion) are issued explicitly before it.
+__device__ __forceinline__ void raw_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+// DMA instructions each thread issues per bf16 tile of head dim D
+template <int D>
+constexpr int dma_per_tile() { return kBlk * (D / 8) / kThreads; }
+
+// Issue the LDS-DMA copy of rows row0..row0+kBlk-1 of head h of a [N, H, D]
+// bf16 tensor into an LDS tile. Rows >= row_lim repeat row row_lim-1 (valid
+// memory; kernels mask those keys). A wave's instruction fills 64 consecutive
+// 16-byte LDS slots (M0 = wave base, lane l -> slot l); the global address of
+// each lane is chosen so that the slot receives its swizzled chunk.
+// The copy is asynchronous: it is complete for this thread once vmcnt drops
+// below the number of later VMEM instructions.
+template <int D>
+__device__ __forceinline__ void dma_tile_bf16(const uint16_t* lds_tile, const void* gbase, int row0, int row_lim,
+                                              int H, int h) {
+  constexpr int CH = D / 8;
+  constexpr int NLD = dma_per_tile<D>();
+  static_assert(NLD >= 1, "one DMA instruction per thread at least");
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+  const char* gb = static_cast<const char*>(gbase);
+  const uint32_t tile = lds_addr(lds_tile);
+#pragma unroll
+  for (int j = 0; j < NLD; ++j) {
+    const int slot = j * kThreads + w * 64 + l;
+    const int r = slot / CH, pc = slot - r * CH;
+    const int c = pc ^ (swz(r) & (CH - 1));
+    const int gr = min(row0 + r, row_lim - 1);
+    const char* src = gb + (static_cast<int64_t>(gr) * H + h) * (D * 2) + c * 16;
+    const uint32_t dst = __builtin_amdgcn_readfirstlane(tile + (j * kThreads + w * 64) * 16);
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(dst), "v"(src)
+                 : "memory", "m0");
+  }
+}
+
+// One LDS-DMA instruction: 16 bytes per lane from sbase + voff (sbase wave-
+// uniform, voff per lane) to LDS bytes [lds, lds + 1024) of the wave, lane l
+// writing lds + 16*l.
+__device__ __forceinline__ void dma16(uint32_t lds, const void* sbase, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(__builtin_amdgcn_readfirstlane(lds)),
+               "v"(voff), "s"(sbase)
+               : "memory", "m0");
+}
+
+// A operand (8 bf16 along head_dim) of mma over a swizzled tile: row r,
+// logical chunk c.
+template <int CH>
+__device__ __forceinline__ bf16x8 swz_read_b128(const uint16_t* tile, int r, int c) {
+  return as_bf16x8(*reinterpret_cast<const u16x8*>(reinterpret_cast<const char*>(tile) + chunk_off<CH>(r, c)));
+}
+
+// acc[db] += X^T . P over a swizzled bf16 tile (the mma_tr_regs product).
+template <int D>
+__device__ __forceinline__ void mma_tr_swz(const uint16_t* tile, int row0, const bf16x8 (&pb)[2],
+                                           floatx16 (&acc)[D / 32], int lane) {
+  constexpr int CH = D / 8;
+  const int g = lane >> 5, sub = lane & 15, grp = (lane >> 4) & 1;
+  const char* t = reinterpret_cast<const char*>(tile);
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    const int rowa = row0 + 16 * s + 4 * g + (sub >> 2);
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+      const int c = 4 * db + 2 * grp + ((sub >> 1) & 1);
+      const int within = 8 * (sub & 1);
+      const u16x4 lo = ds_read_tr16(reinterpret_cast<const uint16_t*>(t + chunk_off<CH>(rowa, c) + within));
+      const u16x4 hi = ds_read_tr16(reinterpret_cast<const uint16_t*>(t + chunk_off<CH>(rowa + 8, c) + within));
+      const u16x8 a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), pb[s], acc[db], 0, 0, 0);
+    }
+  }
+}
+
+// Round the 16 probabilities of a 32x32 accumulator block to bf16 (two MFMA
+// B operands) and add their fp32 sum to l. The log-sum-exp needs the sum of the
+// unrounded values: bf16 rounding would move it by up to 2^-9 relative.
+__device__ __forceinline__ void probs_to_bf16(const floatx16& p, bf16x8 (&pb)[2], float& l) {
+  float acc0 = 0.f, acc1 = 0.f;
+#pragma unroll
+  for (int s = 0; s < 2; ++s)
+#pragma unroll
+    for (int j = 0; j < 8; j += 2) {
+      pb[s][j] = static_cast<__bf16>(p[8 * s + j]);
+      pb[s][j + 1] = static_cast<__bf16>(p[8 * s + j + 1]);
+      acc0 += p[8 * s + j];
+      acc1 += p[8 * s + j + 1];
+    }
+  l += acc0 + acc1;
+}
+
 }  // namespace pe

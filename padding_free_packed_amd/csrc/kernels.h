@@ -26,7 +26,13 @@ hipError_t launch_unpack_rows(const void* packed, void* grid, const int32_t* cu,
 // Forward over tiles of kAttnTileRows packed query rows; items from launch_worklist.
 hipError_t launch_attn_fwd(bool bf16, int D, const void* q, const void* k, const void* v,
                            const int32_t* cu, const int32_t* items, int32_t B, int32_t N, int32_t H,
-                           float scale, void* out, float* lse, hipStream_t stream);
+                           int32_t max_seq_len, float scale, void* out, float* lse, hipStream_t stream);
+
+// bf16 forward with LDS-DMA staging (head dims 32, 64, 128).
+bool attn_fwd_bf16_supported(int D, int max_seq_len);
+hipError_t launch_attn_fwd_bf16(int D, const void* q, const void* k, const void* v, const int32_t* cu,
+                                const int32_t* items, int32_t B, int32_t N, int32_t H, float scale, void* out,
+                                float* lse, hipStream_t stream);
 
 hipError_t launch_attn_fwd_first(bool bf16, int D, const void* q_first, const void* k, const void* v,
                                  const int32_t* cu, int32_t B, int32_t N, int32_t H, float scale,

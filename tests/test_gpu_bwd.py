@@ -48,14 +48,23 @@ def gpu_fwd_bwd(w: W.Workload):
 
 
 def check_bwd(w: W.Workload, label: str, seqs=None):
+    """The backward op takes the forward's output as an input (its D term is
+    <dO, out>). For bf16 the reference is therefore evaluated at the output the
+    forward contract delivers: the oracle's own output rounded to bf16 (nearest
+    even). fp32 compares against the exact gradient."""
     say(f"[bwd] {label}: B={w.num_seqs} N={w.total_tokens} H={w.num_heads} d={w.head_dim} {w.dtype}")
     cu_ref, dq, dk, dv = gpu_fwd_bwd(w)
     q, k, v, do = (W.to_f64(x, w.dtype) for x in (w.q, w.k, w.v, w.dout))
-    ref = oracle.attention_backward(do, q, k, v, cu_ref, w.scale, seqs)
     if seqs is None:
         rows = np.arange(int(cu_ref[-1]))
     else:
         rows = np.concatenate([np.arange(cu_ref[b], cu_ref[b + 1]) for b in seqs])
+    out_given = None
+    if w.dtype == W.BF16:
+        o_rows, _ = oracle.attention_rows(q, k, v, cu_ref, w.scale, rows)
+        out_given = np.zeros_like(q)
+        out_given[rows] = W.bf16_bits_to_f32(W.f32_to_bf16_bits(o_rows.astype(np.float32))).astype(np.float64)
+    ref = oracle.attention_backward(do, q, k, v, cu_ref, w.scale, seqs, out=out_given)
     for name, gtens, r in zip(("dq", "dk", "dv"), (dq, dk, dv), ref):
         check_grad(to_f64(gtens)[rows], r[rows], w.dtype, f"{label} {name}")
 

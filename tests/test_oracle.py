@@ -245,6 +245,32 @@ def _torch_padded_sdpa_autograd(q, k, v, cu, S, scale):
     return out.transpose(1, 2)[mask]
 
 
+def test_backward_given_output_and_lse():
+    # With the exact forward passed in, the result is unchanged; an output
+    # perturbation delta at row i moves only the D term: dQ_i changes by
+    # -scale * <dO_i, delta> * sum_j P_ij K_j and dK_j by -scale * P_ij <dO_i, delta> Q_i.
+    lengths = [4, 7]
+    q, k, v, do, cu, sc = _rand_case(12, lengths)
+    o, lse = oracle.attention(q, k, v, cu, sc)
+    base = oracle.attention_backward(do, q, k, v, cu, sc)
+    same = oracle.attention_backward(do, q, k, v, cu, sc, out=o, lse=lse)
+    for a, b in zip(base, same):
+        np.testing.assert_allclose(a, b, rtol=1e-12, atol=1e-13)
+    i, h = 6, 1
+    delta = np.zeros_like(o)
+    delta[i, h] = np.random.default_rng(4).standard_normal(8) * 1e-3
+    pert = oracle.attention_backward(do, q, k, v, cu, sc, out=o + delta, lse=lse)
+    c0, c1 = 4, 11
+    p = np.exp(sc * q[i, h] @ k[c0:c1, h].T - lse[h, i])
+    dD = float(do[i, h] @ delta[i, h])
+    np.testing.assert_allclose(pert[0][i, h] - base[0][i, h], -sc * dD * (p @ k[c0:c1, h]), rtol=1e-9, atol=1e-15)
+    np.testing.assert_allclose(pert[1][c0:c1, h] - base[1][c0:c1, h], -sc * dD * np.outer(p, q[i, h]),
+                               rtol=1e-9, atol=1e-15)
+    np.testing.assert_array_equal(pert[2], base[2])          # dV does not involve D
+    others = [r for r in range(11) if r != i]
+    np.testing.assert_allclose(pert[0][others], base[0][others], rtol=1e-12, atol=1e-15)
+
+
 def test_backward_finite_differences():
     lengths = [1, 5, 13, 3]
     q, k, v, do, cu, sc = _rand_case(6, lengths)
