@@ -29,8 +29,9 @@ pe_status hip_status(hipError_t e) { return e == hipSuccess ? PE_OK : PE_ERR_HIP
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+// work list of the finest tiling any kernel uses (kAttnWaveRows rows per item)
 size_t items_bytes(int64_t total_tokens) {
-  return round_up(static_cast<size_t>(ceil_div(total_tokens, pe::kAttnTileRows) + 1) * sizeof(int32_t));
+  return round_up(static_cast<size_t>(ceil_div(total_tokens, pe::kAttnWaveRows) + 1) * sizeof(int32_t));
 }
 
 // Checks shared by the attention calls.
@@ -152,7 +153,7 @@ size_t pe_attn_workspace_size(int32_t num_seqs, int64_t total_tokens, int32_t nu
   (void)dtype;
   if (total_tokens < 0 || num_heads < 1) return 0;
   size_t s = items_bytes(total_tokens);
-  if (for_backward) s += round_up(static_cast<size_t>(total_tokens) * num_heads * sizeof(float));
+  if (for_backward) s += items_bytes(total_tokens) + round_up(static_cast<size_t>(total_tokens) * num_heads * sizeof(float));
   return s;
 }
 
@@ -171,6 +172,13 @@ pe_status pe_varlen_attn_fwd(const void* q, const void* k, const void* v, const 
     return PE_ERR_WORKSPACE;
   hipStream_t st = as_stream(stream);
   int32_t* items = static_cast<int32_t*>(workspace);
+  if (dtype == PE_FP32 && pe::attn_fwd_f32_wave_supported(head_dim)) {
+    hipError_t e = pe::launch_worklist(cu_seqlens, num_seqs, total_tokens, pe::kAttnWaveRows, items, st);
+    if (e != hipSuccess) return PE_ERR_HIP;
+    return hip_status(pe::launch_attn_fwd_f32_wave(head_dim, q, k, v, cu_seqlens, items, num_seqs,
+                                                   static_cast<int32_t>(total_tokens), num_heads, softmax_scale, out,
+                                                   lse, st));
+  }
   hipError_t e = pe::launch_worklist(cu_seqlens, num_seqs, total_tokens, pe::kAttnTileRows, items, st);
   if (e != hipSuccess) return PE_ERR_HIP;
   e = pe::launch_attn_fwd(dtype == PE_BF16, head_dim, q, k, v, cu_seqlens, items, num_seqs,
@@ -214,11 +222,17 @@ pe_status pe_varlen_attn_bwd(const void* dout, const void* q, const void* k, con
     return PE_ERR_WORKSPACE;
   hipStream_t st = as_stream(stream);
   int32_t* items = static_cast<int32_t*>(workspace);
-  float* delta = reinterpret_cast<float*>(static_cast<char*>(workspace) + items_bytes(total_tokens));
+  int32_t* items32 = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + items_bytes(total_tokens));
+  float* delta = reinterpret_cast<float*>(static_cast<char*>(workspace) + 2 * items_bytes(total_tokens));
   hipError_t e = pe::launch_worklist(cu_seqlens, num_seqs, total_tokens, pe::kAttnTileRows, items, st);
   if (e != hipSuccess) return PE_ERR_HIP;
-  e = pe::launch_attn_bwd(dtype == PE_BF16, head_dim, dout, q, k, v, out, lse, cu_seqlens, items, num_seqs,
-                          static_cast<int32_t>(total_tokens), num_heads, softmax_scale, dq, dk, dv, delta, st);
+  if (dtype == PE_FP32) {
+    e = pe::launch_worklist(cu_seqlens, num_seqs, total_tokens, pe::kAttnWaveRows, items32, st);
+    if (e != hipSuccess) return PE_ERR_HIP;
+  }
+  e = pe::launch_attn_bwd(dtype == PE_BF16, head_dim, dout, q, k, v, out, lse, cu_seqlens, items,
+                          dtype == PE_FP32 ? items32 : nullptr, num_seqs, static_cast<int32_t>(total_tokens),
+                          num_heads, softmax_scale, dq, dk, dv, delta, st);
   if (e == hipErrorNotSupported) return PE_ERR_UNSUPPORTED;
   return hip_status(e);
 }

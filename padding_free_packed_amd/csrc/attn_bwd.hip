@@ -229,8 +229,8 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
 
 template <bool BF, int D>
 hipError_t bwd_dispatch(const void* dout, const void* q, const void* k, const void* v, const void* out,
-                        const float* lse, const int32_t* cu, const int32_t* items, int32_t B, int32_t N,
-                        int32_t H, float scale, void* dq, void* dk, void* dv, float* delta,
+                        const float* lse, const int32_t* cu, const int32_t* items, const int32_t* items32, int32_t B,
+                        int32_t N, int32_t H, float scale, void* dq, void* dk, void* dv, float* delta,
                         hipStream_t stream) {
   using G = Geo<BF, D>;
   if (N == 0) return hipSuccess;
@@ -250,6 +250,8 @@ hipError_t bwd_dispatch(const void* dout, const void* q, const void* k, const vo
   timing_stop("bwd_dkdv", ev_bwd_dkdv, stream);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
+  if (!BF && items32 != nullptr && (D == 32 || D == 64))
+    return launch_bwd_dq_f32_wave(D, dout, q, k, v, lse, delta, cu, items32, B, N, H, scale, dq, stream);
   hipEvent_t ev_bwd_dq = timing_start(stream);
   hipLaunchKernelGGL((bwd_dq_kernel<BF, D>), dim3(blocks), dim3(kThreads), 0, stream, dout, q, k, v, lse, delta,
                    cu, items, B, N, H, T, c, scale, dq);
@@ -260,14 +262,14 @@ hipError_t bwd_dispatch(const void* dout, const void* q, const void* k, const vo
 }  // namespace
 
 hipError_t launch_attn_bwd(bool bf16, int D, const void* dout, const void* q, const void* k, const void* v,
-                           const void* out, const float* lse, const int32_t* cu, const int32_t* items, int32_t B,
-                           int32_t N, int32_t H, float scale, void* dq, void* dk, void* dv, float* delta,
-                           hipStream_t stream) {
+                           const void* out, const float* lse, const int32_t* cu, const int32_t* items,
+                           const int32_t* items32, int32_t B, int32_t N, int32_t H, float scale, void* dq, void* dk,
+                           void* dv, float* delta, hipStream_t stream) {
 #define PE_BWD_CASE(DD)                                                                                    \
   case DD:                                                                                                \
-    return bf16 ? bwd_dispatch<true, DD>(dout, q, k, v, out, lse, cu, items, B, N, H, scale, dq, dk, dv,  \
+    return bf16 ? bwd_dispatch<true, DD>(dout, q, k, v, out, lse, cu, items, items32, B, N, H, scale, dq, dk, dv,  \
                                          delta, stream)                                                   \
-                : bwd_dispatch<false, DD>(dout, q, k, v, out, lse, cu, items, B, N, H, scale, dq, dk, dv, \
+                : bwd_dispatch<false, DD>(dout, q, k, v, out, lse, cu, items, items32, B, N, H, scale, dq, dk, dv, \
                                           delta, stream);
   switch (D) {
     PE_BWD_CASE(8)

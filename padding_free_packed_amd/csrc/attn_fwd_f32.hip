@@ -1,0 +1,330 @@
+// fp32 forward, one independent wave per (head, 32 packed query rows).
+//
+// On fp32 the MFMA operands of both products are one element per lane per
+// step, so no operand ever needs a transposed copy and the waves need not share
+// an LDS tile. Each wave therefore walks only the key span of its own 32 rows,
+// in 32-key steps starting exactly at the first key it needs, with K and V
+// operands loaded straight from global memory (L2-resident: neighbouring waves
+// read the same sequences) one step ahead of their use. There are no LDS tiles
+// and no barriers, so a wave whose rows cover short sequences never waits for
+// one covering long ones.
+//
+//   S^T (32 keys x 32 queries) += K Q^T   v_mfma_f32_32x32x2f32, 32 steps of 2 over d=64
+//   O^T (d x 32 queries)       += V^T P^T 16 steps per 32-row d block
+#include <climits>
+
+#include "attn_common.h"
+
+namespace pe {
+
+namespace {
+
+constexpr int kRows = 32;  // query rows per wave
+
+template <int D>
+struct F32Ops {
+  static constexpr int HALF = D / 2;  // head-dim elements per lane half (MFMA steps of S)
+  static constexpr int DB = D / 32;   // 32-row blocks of O^T
+  float k[HALF];                      // K[key][g*HALF + st], key = kb + lane%32
+  float v[16][DB];                    // V[kb + 8(st/4) + 4g + st%4][db*32 + lane%32]
+};
+
+template <int D>
+__device__ __forceinline__ void load_ops(F32Ops<D>& ops, const float* __restrict__ kp, const float* __restrict__ vp,
+                                         int kb, int klast, int H, int h, int ql, int g) {
+  using O = F32Ops<D>;
+  {
+    const int key = min(kb + ql, klast);
+    const float4* src = reinterpret_cast<const float4*>(kp + (static_cast<int64_t>(key) * H + h) * D + g * O::HALF);
+#pragma unroll
+    for (int j = 0; j < O::HALF / 4; ++j) {
+      const float4 x = src[j];
+      ops.k[4 * j + 0] = x.x;
+      ops.k[4 * j + 1] = x.y;
+      ops.k[4 * j + 2] = x.z;
+      ops.k[4 * j + 3] = x.w;
+    }
+  }
+#pragma unroll
+  for (int st = 0; st < 16; ++st) {
+    const int key = min(kb + 8 * (st >> 2) + 4 * g + (st & 3), klast);
+    const float* row = vp + (static_cast<int64_t>(key) * H + h) * D;
+#pragma unroll
+    for (int db = 0; db < O::DB; ++db) ops.v[st][db] = row[db * 32 + ql];
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(64, 2) void attn_fwd_f32_kernel(
+    const float* __restrict__ qp, const float* __restrict__ kp, const float* __restrict__ vp,
+    const int32_t* __restrict__ cu, const int32_t* __restrict__ items, int32_t B, int32_t N, int32_t H, int32_t T,
+    float c, float* __restrict__ op, float* __restrict__ lse) {
+  using O = F32Ops<D>;
+  __shared__ int32_t cul[kRows + 2];
+  const int lin = xcd_remap(blockIdx.x, gridDim.x);
+  const int h = lin / T, t = lin - h * T;
+  const int lane = threadIdx.x, ql = lane & 31, g = lane >> 5;
+
+  // sequences of rows r0 .. rend-1
+  const int r0 = t * kRows, rend = min(r0 + kRows, N);
+  const int blo = items[t], nxt = items[t + 1];
+  const int bhi = nxt >= B ? B - 1 : (cu[nxt] == rend ? nxt - 1 : nxt);
+  const int ncu = min(bhi - blo + 2, kRows + 2);
+  if (lane < ncu) cul[lane] = cu[blo + lane];
+  __syncthreads();
+
+  const int qrow = r0 + ql;
+  const bool qvalid = qrow < rend;
+  int qk0 = 0, qk1 = 0;
+  if (qvalid) own_range(cul, ncu, qrow, qk0, qk1);
+  const int wk0 = wave_min_i(qvalid ? qk0 : INT_MAX);
+  const int wk1 = wave_max_i(qvalid ? qk1 : INT_MIN);
+  const int mk0 = wave_max_i(qvalid ? qk0 : INT_MIN);
+  const int mk1 = wave_min_i(qvalid ? qk1 : INT_MAX);
+
+  float qf[O::HALF];
+  {
+    const float4* src =
+        reinterpret_cast<const float4*>(qp + (static_cast<int64_t>(qvalid ? qrow : r0) * H + h) * D + g * O::HALF);
+#pragma unroll
+    for (int j = 0; j < O::HALF / 4; ++j) {
+      const float4 x = src[j];
+      qf[4 * j + 0] = qvalid ? x.x : 0.f;
+      qf[4 * j + 1] = qvalid ? x.y : 0.f;
+      qf[4 * j + 2] = qvalid ? x.z : 0.f;
+      qf[4 * j + 3] = qvalid ? x.w : 0.f;
+    }
+  }
+
+  floatx16 o[O::DB];
+#pragma unroll
+  for (int db = 0; db < O::DB; ++db) o[db] = floatx16{};
+  float m = kNegBig, l = 0.f;
+
+  auto block = [&](const O& ops, int kb) __attribute__((always_inline)) {
+    floatx16 s = floatx16{};
+#pragma unroll
+    for (int st = 0; st < O::HALF; ++st) s = __builtin_amdgcn_mfma_f32_32x32x2f32(ops.k[st], qf[st], s, 0, 0, 0);
+    if (!(kb >= mk0 && kb + 32 <= mk1)) {
+      const int base = kb + 4 * g;
+      mask_block(s, qk0 - base, qk1 - base);
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[i]);
+    mx = xhalf_max(mx);
+    const float mnew = fmaxf(m, mx * c);
+    if (__any(mnew > m)) {
+      const float alpha = __builtin_amdgcn_exp2f(m - mnew);
+      l *= alpha;
+#pragma unroll
+      for (int db = 0; db < O::DB; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
+      m = mnew;
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float p = __builtin_amdgcn_exp2f(fmaf(s[i], c, -m));
+      s[i] = p;
+      l += p;
+    }
+#pragma unroll
+    for (int st = 0; st < 16; ++st)
+#pragma unroll
+      for (int db = 0; db < O::DB; ++db) o[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(ops.v[st][db], s[st], o[db], 0, 0, 0);
+  };
+
+  // keys [wk0, wk1) in steps of 32; operands of the next step load while this one computes
+  if (wk0 < wk1) {
+    const int klast = wk1 - 1;
+    O a, b;
+    load_ops<D>(a, kp, vp, wk0, klast, H, h, ql, g);
+    for (int kb = wk0; kb < wk1; kb += 64) {
+      if (kb + 32 < wk1) load_ops<D>(b, kp, vp, kb + 32, klast, H, h, ql, g);
+      block(a, kb);
+      if (kb + 32 >= wk1) break;
+      if (kb + 64 < wk1) load_ops<D>(a, kp, vp, kb + 64, klast, H, h, ql, g);
+      block(b, kb + 32);
+    }
+  }
+
+  const float lt = xhalf_sum(l);
+  const float inv = lt > 0.f ? 1.f / lt : 0.f;
+  if (qvalid) {
+    store_acc_row<false, D>(op, (static_cast<int64_t>(qrow) * H + h) * D, o, inv, g);
+    if (lse != nullptr && g == 0) lse[static_cast<int64_t>(h) * N + qrow] = (m + log2f(lt)) * kLn2;
+  }
+}
+
+template <int D>
+hipError_t dispatch(const void* q, const void* k, const void* v, const int32_t* cu, const int32_t* items,
+                    int32_t B, int32_t N, int32_t H, float scale, void* out, float* lse, hipStream_t stream) {
+  const int T = (N + kRows - 1) / kRows;
+  const int64_t blocks = static_cast<int64_t>(T) * H;
+  if (blocks == 0) return hipSuccess;
+  const float c = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
+  hipEvent_t ev = timing_start(stream);
+  hipLaunchKernelGGL((attn_fwd_f32_kernel<D>), dim3(static_cast<unsigned>(blocks)), dim3(64), 0, stream,
+                     static_cast<const float*>(q), static_cast<const float*>(k), static_cast<const float*>(v), cu,
+                     items, B, N, H, T, c, static_cast<float*>(out), lse);
+  timing_stop("attn_fwd", ev, stream);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool attn_fwd_f32_wave_supported(int D) { return D == 32 || D == 64; }
+
+hipError_t launch_attn_fwd_f32_wave(int D, const void* q, const void* k, const void* v, const int32_t* cu,
+                                    const int32_t* items32, int32_t B, int32_t N, int32_t H, float scale, void* out,
+                                    float* lse, hipStream_t stream) {
+  switch (D) {
+    case 32: return dispatch<32>(q, k, v, cu, items32, B, N, H, scale, out, lse, stream);
+    case 64: return dispatch<64>(q, k, v, cu, items32, B, N, H, scale, out, lse, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace pe
+
+// ---------------------------------------------------------------- fp32 dQ, one wave per 32 query rows
+// Same walk as the forward: per 32-key step
+//   S^T = K Q^T, dP^T = V dO^T          (K and V row chunks as A operands)
+//   dS^T = P^T (dP^T - D), P^T = exp(scale S^T - lse)
+//   dQ^T += K^T dS^T                    (K scalars K[key(st)][d] as A operands)
+namespace pe {
+namespace {
+
+template <int D>
+__device__ __forceinline__ void load_rows(float (&r)[D / 2], const float* __restrict__ base, int key, int H, int h,
+                                          int g) {
+  const float4* src = reinterpret_cast<const float4*>(base + (static_cast<int64_t>(key) * H + h) * D + g * (D / 2));
+#pragma unroll
+  for (int j = 0; j < D / 8; ++j) {
+    const float4 x = src[j];
+    r[4 * j + 0] = x.x;
+    r[4 * j + 1] = x.y;
+    r[4 * j + 2] = x.z;
+    r[4 * j + 3] = x.w;
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void load_tr(float (&t)[16][D / 32], const float* __restrict__ base, int kb, int klast,
+                                        int H, int h, int ql, int g) {
+#pragma unroll
+  for (int st = 0; st < 16; ++st) {
+    const int key = min(kb + 8 * (st >> 2) + 4 * g + (st & 3), klast);
+    const float* row = base + (static_cast<int64_t>(key) * H + h) * D;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) t[st][db] = row[db * 32 + ql];
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(64, 2) void bwd_dq_f32_kernel(
+    const float* __restrict__ dop, const float* __restrict__ qp, const float* __restrict__ kp,
+    const float* __restrict__ vp, const float* __restrict__ lse, const float* __restrict__ delta,
+    const int32_t* __restrict__ cu, const int32_t* __restrict__ items, int32_t B, int32_t N, int32_t H, int32_t T,
+    float c, float scale, float* __restrict__ dqp) {
+  constexpr int HALF = D / 2, DB = D / 32;
+  __shared__ int32_t cul[kRows + 2];
+  const int lin = xcd_remap(blockIdx.x, gridDim.x);
+  const int h = lin / T, t = lin - h * T;
+  const int lane = threadIdx.x, ql = lane & 31, g = lane >> 5;
+
+  const int r0 = t * kRows, rend = min(r0 + kRows, N);
+  const int blo = items[t], nxt = items[t + 1];
+  const int bhi = nxt >= B ? B - 1 : (cu[nxt] == rend ? nxt - 1 : nxt);
+  const int ncu = min(bhi - blo + 2, kRows + 2);
+  if (lane < ncu) cul[lane] = cu[blo + lane];
+  __syncthreads();
+
+  const int qrow = r0 + ql;
+  const bool qvalid = qrow < rend;
+  int qk0 = 0, qk1 = 0;
+  if (qvalid) own_range(cul, ncu, qrow, qk0, qk1);
+  const int wk0 = wave_min_i(qvalid ? qk0 : INT_MAX);
+  const int wk1 = wave_max_i(qvalid ? qk1 : INT_MIN);
+  const int mk0 = wave_max_i(qvalid ? qk0 : INT_MIN);
+  const int mk1 = wave_min_i(qvalid ? qk1 : INT_MAX);
+
+  float qf[HALF], df[HALF];
+  const int qsafe = qvalid ? qrow : r0;
+  load_rows<D>(qf, qp, qsafe, H, h, g);
+  load_rows<D>(df, dop, qsafe, H, h, g);
+  if (!qvalid) {
+#pragma unroll
+    for (int i = 0; i < HALF; ++i) qf[i] = df[i] = 0.f;
+  }
+  const float lse2 = qvalid ? lse[static_cast<int64_t>(h) * N + qrow] * kLog2e : 0.f;
+  const float dlq = qvalid ? delta[static_cast<int64_t>(h) * N + qrow] : 0.f;
+
+  floatx16 dq[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) dq[db] = floatx16{};
+
+  if (wk0 < wk1) {
+    const int klast = wk1 - 1;
+    float kr[HALF], vr[HALF], kt[16][DB];
+    load_rows<D>(kr, kp, min(wk0 + ql, klast), H, h, g);
+    load_rows<D>(vr, vp, min(wk0 + ql, klast), H, h, g);
+    load_tr<D>(kt, kp, wk0, klast, H, h, ql, g);
+    for (int kb = wk0; kb < wk1; kb += 32) {
+      const bool more = kb + 32 < wk1;
+      floatx16 s = floatx16{}, dp = floatx16{};
+#pragma unroll
+      for (int st = 0; st < HALF; ++st) {
+        s = __builtin_amdgcn_mfma_f32_32x32x2f32(kr[st], qf[st], s, 0, 0, 0);
+        dp = __builtin_amdgcn_mfma_f32_32x32x2f32(vr[st], df[st], dp, 0, 0, 0);
+      }
+      if (more) {
+        load_rows<D>(kr, kp, min(kb + 32 + ql, klast), H, h, g);
+        load_rows<D>(vr, vp, min(kb + 32 + ql, klast), H, h, g);
+      }
+      if (!(kb >= mk0 && kb + 32 <= mk1)) {
+        const int base = kb + 4 * g;
+        mask_block(s, qk0 - base, qk1 - base);
+      }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float p = __builtin_amdgcn_exp2f(fmaf(s[i], c, -lse2));
+        dp[i] = p * (dp[i] - dlq);
+      }
+#pragma unroll
+      for (int st = 0; st < 16; ++st)
+#pragma unroll
+        for (int db = 0; db < DB; ++db) dq[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(kt[st][db], dp[st], dq[db], 0, 0, 0);
+      if (more) load_tr<D>(kt, kp, kb + 32, klast, H, h, ql, g);
+    }
+  }
+  if (qvalid) store_acc_row<false, D>(dqp, (static_cast<int64_t>(qrow) * H + h) * D, dq, scale, g);
+}
+
+}  // namespace
+
+hipError_t launch_bwd_dq_f32_wave(int D, const void* dout, const void* q, const void* k, const void* v,
+                                  const float* lse, const float* delta, const int32_t* cu, const int32_t* items32,
+                                  int32_t B, int32_t N, int32_t H, float scale, void* dq, hipStream_t stream) {
+  const int T = (N + kRows - 1) / kRows;
+  const int64_t blocks = static_cast<int64_t>(T) * H;
+  if (blocks == 0) return hipSuccess;
+  const float c = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
+  const dim3 gd(static_cast<unsigned>(blocks)), bd(64);
+  hipEvent_t ev = timing_start(stream);
+  if (D == 32)
+    hipLaunchKernelGGL((bwd_dq_f32_kernel<32>), gd, bd, 0, stream, static_cast<const float*>(dout),
+                       static_cast<const float*>(q), static_cast<const float*>(k), static_cast<const float*>(v), lse,
+                       delta, cu, items32, B, N, H, T, c, scale, static_cast<float*>(dq));
+  else if (D == 64)
+    hipLaunchKernelGGL((bwd_dq_f32_kernel<64>), gd, bd, 0, stream, static_cast<const float*>(dout),
+                       static_cast<const float*>(q), static_cast<const float*>(k), static_cast<const float*>(v), lse,
+                       delta, cu, items32, B, N, H, T, c, scale, static_cast<float*>(dq));
+  else
+    return hipErrorInvalidValue;
+  timing_stop("bwd_dq", ev, stream);
+  return hipGetLastError();
+}
+
+}  // namespace pe

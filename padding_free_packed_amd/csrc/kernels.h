@@ -11,6 +11,8 @@ void timing_stop(const char* name, hipEvent_t start, hipStream_t stream);
 
 // packed query (or key) rows per attention work item
 constexpr int kAttnTileRows = 128;
+// packed rows per work item of the one-wave fp32 kernels
+constexpr int kAttnWaveRows = 32;
 
 hipError_t launch_scan(const int32_t* lengths, int32_t B, int32_t S, int32_t* cu, int64_t* result,
                        hipStream_t stream);
@@ -34,14 +36,27 @@ hipError_t launch_attn_fwd_bf16(int D, const void* q, const void* k, const void*
                                 const int32_t* items, int32_t B, int32_t N, int32_t H, float scale, void* out,
                                 float* lse, hipStream_t stream);
 
+// fp32 forward, one independent wave per 32 query rows (head dims 32, 64);
+// items32 is the work list with tile height kAttnWaveRows.
+bool attn_fwd_f32_wave_supported(int D);
+hipError_t launch_attn_fwd_f32_wave(int D, const void* q, const void* k, const void* v, const int32_t* cu,
+                                    const int32_t* items32, int32_t B, int32_t N, int32_t H, float scale, void* out,
+                                    float* lse, hipStream_t stream);
+
+// fp32 dQ, one independent wave per 32 query rows (head dims 32, 64)
+hipError_t launch_bwd_dq_f32_wave(int D, const void* dout, const void* q, const void* k, const void* v,
+                                  const float* lse, const float* delta, const int32_t* cu, const int32_t* items32,
+                                  int32_t B, int32_t N, int32_t H, float scale, void* dq, hipStream_t stream);
+
 hipError_t launch_attn_fwd_first(bool bf16, int D, const void* q_first, const void* k, const void* v,
                                  const int32_t* cu, int32_t B, int32_t N, int32_t H, float scale,
                                  void* out_first, float* lse_first, hipStream_t stream);
 
 // Backward: D = rowsum(dO * O) per (head, row), then dK/dV over key tiles, then dQ over query tiles.
+// items: work list with tile height kAttnTileRows; items32: with kAttnWaveRows (or NULL)
 hipError_t launch_attn_bwd(bool bf16, int D, const void* dout, const void* q, const void* k,
                            const void* v, const void* out, const float* lse, const int32_t* cu,
-                           const int32_t* items, int32_t B, int32_t N, int32_t H, float scale,
-                           void* dq, void* dk, void* dv, float* delta, hipStream_t stream);
+                           const int32_t* items, const int32_t* items32, int32_t B, int32_t N, int32_t H,
+                           float scale, void* dq, void* dk, void* dv, float* delta, hipStream_t stream);
 
 }  // namespace pe
