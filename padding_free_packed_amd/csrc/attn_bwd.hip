@@ -241,6 +241,11 @@ hipError_t bwd_dispatch(const void* dout, const void* q, const void* k, const vo
   timing_stop("bwd_delta", ev_bwd_delta, stream);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  if (!BF && items32 != nullptr && (D == 32 || D == 64)) {
+    e = launch_bwd_dkdv_f32_wave(D, dout, q, k, v, lse, delta, cu, items32, B, N, H, scale, dk, dv, stream);
+    if (e != hipSuccess) return e;
+    return launch_bwd_dq_f32_wave(D, dout, q, k, v, lse, delta, cu, items32, B, N, H, scale, dq, stream);
+  }
   const int T = (N + kAttnTileRows - 1) / kAttnTileRows;
   const unsigned blocks = static_cast<unsigned>(static_cast<int64_t>(T) * H);
   const float c = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
@@ -250,8 +255,6 @@ hipError_t bwd_dispatch(const void* dout, const void* q, const void* k, const vo
   timing_stop("bwd_dkdv", ev_bwd_dkdv, stream);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (!BF && items32 != nullptr && (D == 32 || D == 64))
-    return launch_bwd_dq_f32_wave(D, dout, q, k, v, lse, delta, cu, items32, B, N, H, scale, dq, stream);
   hipEvent_t ev_bwd_dq = timing_start(stream);
   hipLaunchKernelGGL((bwd_dq_kernel<BF, D>), dim3(blocks), dim3(kThreads), 0, stream, dout, q, k, v, lse, delta,
                    cu, items, B, N, H, T, c, scale, dq);

@@ -196,10 +196,12 @@ hipError_t launch_attn_fwd_f32_wave(int D, const void* q, const void* k, const v
 namespace pe {
 namespace {
 
+// Row loads relative to a wave-uniform base (row `r`, head h) with 32-bit
+// element offsets, so one scalar base and one offset register serve many loads.
 template <int D>
-__device__ __forceinline__ void load_rows(float (&r)[D / 2], const float* __restrict__ base, int key, int H, int h,
+__device__ __forceinline__ void load_rows(float (&r)[D / 2], const float* __restrict__ base, uint32_t rel, uint32_t HD,
                                           int g) {
-  const float4* src = reinterpret_cast<const float4*>(base + (static_cast<int64_t>(key) * H + h) * D + g * (D / 2));
+  const float4* src = reinterpret_cast<const float4*>(base + (rel * HD + static_cast<uint32_t>(g * (D / 2))));
 #pragma unroll
   for (int j = 0; j < D / 8; ++j) {
     const float4 x = src[j];
@@ -210,15 +212,16 @@ __device__ __forceinline__ void load_rows(float (&r)[D / 2], const float* __rest
   }
 }
 
+// t[st][db] = X[row 8(st/4) + 4g + st%4 (clamped to `last`)][db*32 + lane%32], rows relative to `base`.
 template <int D>
-__device__ __forceinline__ void load_tr(float (&t)[16][D / 32], const float* __restrict__ base, int kb, int klast,
-                                        int H, int h, int ql, int g) {
+__device__ __forceinline__ void load_tr(float (&t)[16][D / 32], const float* __restrict__ base, int last, uint32_t HD,
+                                        int ql, int g) {
 #pragma unroll
   for (int st = 0; st < 16; ++st) {
-    const int key = min(kb + 8 * (st >> 2) + 4 * g + (st & 3), klast);
-    const float* row = base + (static_cast<int64_t>(key) * H + h) * D;
+    const uint32_t rel = static_cast<uint32_t>(min(8 * (st >> 2) + 4 * g + (st & 3), last));
+    const float* row = base + (rel * HD + static_cast<uint32_t>(ql));
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db) t[st][db] = row[db * 32 + ql];
+    for (int db = 0; db < D / 32; ++db) t[st][db] = row[db * 32];
   }
 }
 
@@ -252,8 +255,11 @@ __global__ __launch_bounds__(64, 2) void bwd_dq_f32_kernel(
 
   float qf[HALF], df[HALF];
   const int qsafe = qvalid ? qrow : r0;
-  load_rows<D>(qf, qp, qsafe, H, h, g);
-  load_rows<D>(df, dop, qsafe, H, h, g);
+  const uint32_t HD = static_cast<uint32_t>(H) * D;
+  const int64_t hoff = static_cast<int64_t>(h) * D;
+  auto at = [&](const float* p, int row) { return p + (static_cast<int64_t>(row) * HD + hoff); };
+  load_rows<D>(qf, at(qp, r0), qsafe - r0, HD, g);
+  load_rows<D>(df, at(dop, r0), qsafe - r0, HD, g);
   if (!qvalid) {
 #pragma unroll
     for (int i = 0; i < HALF; ++i) qf[i] = df[i] = 0.f;
@@ -268,9 +274,9 @@ __global__ __launch_bounds__(64, 2) void bwd_dq_f32_kernel(
   if (wk0 < wk1) {
     const int klast = wk1 - 1;
     float kr[HALF], vr[HALF], kt[16][DB];
-    load_rows<D>(kr, kp, min(wk0 + ql, klast), H, h, g);
-    load_rows<D>(vr, vp, min(wk0 + ql, klast), H, h, g);
-    load_tr<D>(kt, kp, wk0, klast, H, h, ql, g);
+    load_rows<D>(kr, at(kp, wk0), min(ql, klast - wk0), HD, g);
+    load_rows<D>(vr, at(vp, wk0), min(ql, klast - wk0), HD, g);
+    load_tr<D>(kt, at(kp, wk0), klast - wk0, HD, ql, g);
     for (int kb = wk0; kb < wk1; kb += 32) {
       const bool more = kb + 32 < wk1;
       floatx16 s = floatx16{}, dp = floatx16{};
@@ -280,8 +286,8 @@ __global__ __launch_bounds__(64, 2) void bwd_dq_f32_kernel(
         dp = __builtin_amdgcn_mfma_f32_32x32x2f32(vr[st], df[st], dp, 0, 0, 0);
       }
       if (more) {
-        load_rows<D>(kr, kp, min(kb + 32 + ql, klast), H, h, g);
-        load_rows<D>(vr, vp, min(kb + 32 + ql, klast), H, h, g);
+        load_rows<D>(kr, at(kp, kb + 32), min(ql, klast - kb - 32), HD, g);
+        load_rows<D>(vr, at(vp, kb + 32), min(ql, klast - kb - 32), HD, g);
       }
       if (!(kb >= mk0 && kb + 32 <= mk1)) {
         const int base = kb + 4 * g;
@@ -296,7 +302,7 @@ __global__ __launch_bounds__(64, 2) void bwd_dq_f32_kernel(
       for (int st = 0; st < 16; ++st)
 #pragma unroll
         for (int db = 0; db < DB; ++db) dq[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(kt[st][db], dp[st], dq[db], 0, 0, 0);
-      if (more) load_tr<D>(kt, kp, kb + 32, klast, H, h, ql, g);
+      if (more) load_tr<D>(kt, at(kp, kb + 32), klast - kb - 32, HD, ql, g);
     }
   }
   if (qvalid) store_acc_row<false, D>(dqp, (static_cast<int64_t>(qrow) * H + h) * D, dq, scale, g);
@@ -324,6 +330,142 @@ hipError_t launch_bwd_dq_f32_wave(int D, const void* dout, const void* q, const 
   else
     return hipErrorInvalidValue;
   timing_stop("bwd_dq", ev, stream);
+  return hipGetLastError();
+}
+
+}  // namespace pe
+
+// ---------------------------------------------------------------- fp32 dK/dV, one wave per 32 key rows
+// The mirror of the dQ walk, over the query span of the wave's 32 keys:
+//   S = Q K^T, dP = dO V^T                  (Q and dO row chunks as A operands,
+//                                            K and V rows held for the whole walk)
+//   P = exp2(c S - lse2), dS = P (dP - D)   (row statistics per query = per register)
+//   dV^T += dO^T P, dK^T += Q^T dS          (dO and Q scalars as A operands)
+// The per-query statistics arrive one per lane (query = lane%32) and are
+// turned into the per-register layout through a 32-float LDS slot.
+namespace pe {
+namespace {
+
+template <int D>
+__global__ __launch_bounds__(64, D > 32 ? 1 : 2) void bwd_dkdv_f32_kernel(
+    const float* __restrict__ dop, const float* __restrict__ qp, const float* __restrict__ kp,
+    const float* __restrict__ vp, const float* __restrict__ lse, const float* __restrict__ delta,
+    const int32_t* __restrict__ cu, const int32_t* __restrict__ items, int32_t B, int32_t N, int32_t H, int32_t T,
+    float c, float scale, float* __restrict__ dkp, float* __restrict__ dvp) {
+  constexpr int HALF = D / 2, DB = D / 32;
+  __shared__ int32_t cul[kRows + 2];
+  __shared__ __align__(16) float stat[2][kRows];
+  const int lin = xcd_remap(blockIdx.x, gridDim.x);
+  const int h = lin / T, t = lin - h * T;
+  const int lane = threadIdx.x, ql = lane & 31, g = lane >> 5;
+
+  const int r0 = t * kRows, rend = min(r0 + kRows, N);
+  const int blo = items[t], nxt = items[t + 1];
+  const int bhi = nxt >= B ? B - 1 : (cu[nxt] == rend ? nxt - 1 : nxt);
+  const int ncu = min(bhi - blo + 2, kRows + 2);
+  if (lane < ncu) cul[lane] = cu[blo + lane];
+  __syncthreads();
+
+  const int krow = r0 + ql;
+  const bool kvalid = krow < rend;
+  int kq0 = 0, kq1 = 0;
+  if (kvalid) own_range(cul, ncu, krow, kq0, kq1);
+  const int wq0 = wave_min_i(kvalid ? kq0 : INT_MAX);
+  const int wq1 = wave_max_i(kvalid ? kq1 : INT_MIN);
+  const int mq0 = wave_max_i(kvalid ? kq0 : INT_MIN);
+  const int mq1 = wave_min_i(kvalid ? kq1 : INT_MAX);
+
+  float kr[HALF], vr[HALF];
+  const int ksafe = kvalid ? krow : r0;
+  const uint32_t HD = static_cast<uint32_t>(H) * D;
+  const int64_t hoff = static_cast<int64_t>(h) * D;
+  auto at = [&](const float* p, int row) { return p + (static_cast<int64_t>(row) * HD + hoff); };
+  load_rows<D>(kr, at(kp, r0), ksafe - r0, HD, g);
+  load_rows<D>(vr, at(vp, r0), ksafe - r0, HD, g);
+
+  floatx16 dk[DB], dv[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) dk[db] = dv[db] = floatx16{};
+
+  const float* lse_h = lse + static_cast<int64_t>(h) * N;
+  const float* del_h = delta + static_cast<int64_t>(h) * N;
+  const int qlast = wq1 - 1;
+  for (int qb = wq0; qb < wq1; qb += 32) {
+    const int qrow = min(qb + ql, qlast);
+    float qr[HALF], dr[HALF];
+    load_rows<D>(qr, at(qp, qb), qrow - qb, HD, g);
+    load_rows<D>(dr, at(dop, qb), qrow - qb, HD, g);
+    if (g == 0) {
+      stat[0][ql] = lse_h[qrow] * kLog2e;
+      stat[1][ql] = del_h[qrow];
+    }
+    floatx16 s = floatx16{}, dp = floatx16{};
+#pragma unroll
+    for (int st = 0; st < HALF; ++st) {
+      s = __builtin_amdgcn_mfma_f32_32x32x2f32(qr[st], kr[st], s, 0, 0, 0);
+      dp = __builtin_amdgcn_mfma_f32_32x32x2f32(dr[st], vr[st], dp, 0, 0, 0);
+    }
+    float qt[16][DB], dt[16][DB];
+    load_tr<D>(qt, at(qp, qb), qlast - qb, HD, ql, g);
+    load_tr<D>(dt, at(dop, qb), qlast - qb, HD, ql, g);
+    // rows of this block are queries qb + 8(i/4) + 4g + i%4; keep those inside the key's own sequence
+    if (!(qb >= mq0 && qb + 32 <= mq1)) {
+      const int base = qb + 4 * g;
+      mask_block(s, kq0 - base, kq1 - base);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float4 l4 = *reinterpret_cast<const float4*>(&stat[0][8 * j + 4 * g]);
+      const float4 d4 = *reinterpret_cast<const float4*>(&stat[1][8 * j + 4 * g]);
+      const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dl[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int i = 4 * j + e;
+        const float p = __builtin_amdgcn_exp2f(fmaf(s[i], c, -lv[e]));
+        s[i] = p;
+        dp[i] = p * (dp[i] - dl[e]);
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int st = 0; st < 16; ++st)
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        dv[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(dt[st][db], s[st], dv[db], 0, 0, 0);
+        dk[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(qt[st][db], dp[st], dk[db], 0, 0, 0);
+      }
+  }
+  if (kvalid) {
+    const int64_t off = (static_cast<int64_t>(krow) * H + h) * D;
+    store_acc_row<false, D>(dkp, off, dk, scale, g);
+    store_acc_row<false, D>(dvp, off, dv, 1.0f, g);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_bwd_dkdv_f32_wave(int D, const void* dout, const void* q, const void* k, const void* v,
+                                    const float* lse, const float* delta, const int32_t* cu, const int32_t* items32,
+                                    int32_t B, int32_t N, int32_t H, float scale, void* dk, void* dv,
+                                    hipStream_t stream) {
+  const int T = (N + kRows - 1) / kRows;
+  const int64_t blocks = static_cast<int64_t>(T) * H;
+  if (blocks == 0) return hipSuccess;
+  const float c = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
+  const dim3 gd(static_cast<unsigned>(blocks)), bd(64);
+  hipEvent_t ev = timing_start(stream);
+  if (D == 32)
+    hipLaunchKernelGGL((bwd_dkdv_f32_kernel<32>), gd, bd, 0, stream, static_cast<const float*>(dout),
+                       static_cast<const float*>(q), static_cast<const float*>(k), static_cast<const float*>(v), lse,
+                       delta, cu, items32, B, N, H, T, c, scale, static_cast<float*>(dk), static_cast<float*>(dv));
+  else if (D == 64)
+    hipLaunchKernelGGL((bwd_dkdv_f32_kernel<64>), gd, bd, 0, stream, static_cast<const float*>(dout),
+                       static_cast<const float*>(q), static_cast<const float*>(k), static_cast<const float*>(v), lse,
+                       delta, cu, items32, B, N, H, T, c, scale, static_cast<float*>(dk), static_cast<float*>(dv));
+  else
+    return hipErrorInvalidValue;
+  timing_stop("bwd_dkdv", ev, stream);
   return hipGetLastError();
 }
 

@@ -43,7 +43,11 @@ hipError_t launch_attn_fwd_f32_wave(int D, const void* q, const void* k, const v
                                     const int32_t* items32, int32_t B, int32_t N, int32_t H, float scale, void* out,
                                     float* lse, hipStream_t stream);
 
-// fp32 dQ, one independent wave per 32 query rows (head dims 32, 64)
+// fp32 dK/dV and dQ, one independent wave per 32 key (query) rows (head dims 32, 64)
+hipError_t launch_bwd_dkdv_f32_wave(int D, const void* dout, const void* q, const void* k, const void* v,
+                                    const float* lse, const float* delta, const int32_t* cu, const int32_t* items32,
+                                    int32_t B, int32_t N, int32_t H, float scale, void* dk, void* dv,
+                                    hipStream_t stream);
 hipError_t launch_bwd_dq_f32_wave(int D, const void* dout, const void* q, const void* k, const void* v,
                                   const float* lse, const float* delta, const int32_t* cu, const int32_t* items32,
                                   int32_t B, int32_t N, int32_t H, float scale, void* dq, hipStream_t stream);
