@@ -237,6 +237,7 @@ struct TileSpan {
   int r0, rend, ncu, lo, hi;
 };
 
+template <int NT = kThreads>
 __device__ __forceinline__ TileSpan tile_span(const int32_t* __restrict__ cu, const int32_t* __restrict__ items,
                                               int t, int B, int N, int32_t* cul) {
   TileSpan s;
@@ -247,7 +248,7 @@ __device__ __forceinline__ TileSpan tile_span(const int32_t* __restrict__ cu, co
   // at most kAttnTileRows + 1 sequences touch a tile when every length is >= 1;
   // the clamp keeps LDS writes in bounds even for malformed offsets
   s.ncu = min(bhi - blo + 2, kAttnTileRows + 2);
-  for (int i = threadIdx.x; i < s.ncu; i += kThreads) cul[i] = cu[blo + i];
+  for (int i = threadIdx.x; i < s.ncu; i += NT) cul[i] = cu[blo + i];
   __syncthreads();
   s.lo = cul[0];
   s.hi = cul[s.ncu - 1];
@@ -383,16 +384,16 @@ __device__ __forceinline__ void mma_tr_swz(const uint16_t* tile, int row0, const
 // B operands) and add their fp32 sum to l. The log-sum-exp needs the sum of the
 // unrounded values: bf16 rounding would move it by up to 2^-9 relative.
 __device__ __forceinline__ void probs_to_bf16(const floatx16& p, bf16x8 (&pb)[2], float& l) {
-  float acc0 = 0.f, acc1 = 0.f;
 #pragma unroll
   for (int s = 0; s < 2; ++s)
 #pragma unroll
-    for (int j = 0; j < 8; j += 2) {
-      pb[s][j] = static_cast<__bf16>(p[8 * s + j]);
-      pb[s][j + 1] = static_cast<__bf16>(p[8 * s + j + 1]);
-      acc0 += p[8 * s + j];
-      acc1 += p[8 * s + j + 1];
-    }
+    for (int j = 0; j < 8; ++j) pb[s][j] = static_cast<__bf16>(p[8 * s + j]);
+  float acc0 = p[0], acc1 = p[1];  // two chains
+#pragma unroll
+  for (int i = 2; i < 16; i += 2) {
+    acc0 += p[i];
+    acc1 += p[i + 1];
+  }
   l += acc0 + acc1;
 }
 

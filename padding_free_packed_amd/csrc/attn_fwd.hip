@@ -261,8 +261,11 @@ hipError_t first_dispatch(const void* q, const void* k, const void* v, const int
 hipError_t launch_attn_fwd(bool bf16, int D, const void* q, const void* k, const void* v,
                            const int32_t* cu, const int32_t* items, int32_t B, int32_t N, int32_t H,
                            int32_t max_seq_len, float scale, void* out, float* lse, hipStream_t stream) {
-  if (bf16 && attn_fwd_bf16_supported(D, max_seq_len))
+  if (bf16 && attn_fwd_bf16_supported(D, max_seq_len)) {
+    if (attn_fwd_bf16_w64_supported(D))
+      return launch_attn_fwd_bf16_w64(D, q, k, v, cu, items, B, N, H, scale, out, lse, stream);
     return launch_attn_fwd_bf16(D, q, k, v, cu, items, B, N, H, scale, out, lse, stream);
+  }
 #define PE_FWD_CASE(DD)                                                                      \
   case DD:                                                                                  \
     return bf16 ? fwd_dispatch<true, DD>(q, k, v, cu, items, B, N, H, scale, out, lse, stream) \

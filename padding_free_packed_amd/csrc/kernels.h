@@ -32,6 +32,11 @@ hipError_t launch_attn_fwd(bool bf16, int D, const void* q, const void* k, const
 
 // bf16 forward with LDS-DMA staging (head dims 32, 64, 128).
 bool attn_fwd_bf16_supported(int D, int max_seq_len);
+// the same items with two 64-row waves per block (head dims 32, 64)
+bool attn_fwd_bf16_w64_supported(int D);
+hipError_t launch_attn_fwd_bf16_w64(int D, const void* q, const void* k, const void* v, const int32_t* cu,
+                                    const int32_t* items, int32_t B, int32_t N, int32_t H, float scale, void* out,
+                                    float* lse, hipStream_t stream);
 hipError_t launch_attn_fwd_bf16(int D, const void* q, const void* k, const void* v, const int32_t* cu,
                                 const int32_t* items, int32_t B, int32_t N, int32_t H, float scale, void* out,
                                 float* lse, hipStream_t stream);

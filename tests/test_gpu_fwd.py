@@ -100,6 +100,21 @@ def test_closed_forms_on_gpu():
     np.testing.assert_allclose(o[38:338], 0.25, atol=1e-6)
 
 
+@pytest.mark.parametrize("d", [32, 64, 128])
+def test_running_max_paths(d):
+    # logits that drift along the keys: for some queries the running max creeps up
+    # block after block (small steps that add up), for others it is set by the first
+    # keys, and a late block of much larger keys forces a jump in every row
+    L = np.array([2000, 700, 45], dtype=np.int32)
+    w = W.custom(47 + d, L, 2048, 2, d, W.BF16)
+    k = W.bf16_bits_to_f32(w.k)
+    ramp = np.linspace(0.0, 3.0, 2000, dtype=np.float32)[:, None, None]
+    k[0:2000] = k[0] * ramp + 0.1 * k[0:2000]
+    k[1500:1530] *= 4.0
+    w.k = W.f32_to_bf16_bits(k)
+    check_full(w, f"running max paths d={d}")
+
+
 def test_isolation_bitwise():
     L = np.array([50, 130, 7, 260, 90, 1, 128], dtype=np.int32)
     w = W.custom(44, L, 260, 2, 64, W.BF16)
