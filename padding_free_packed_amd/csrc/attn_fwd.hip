@@ -125,26 +125,34 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
 }
 
 // ---------------------------------------------------------------- first-token query
-// One block per (sequence, group of heads). Threads are laid out as
-// [key slot][head][16-byte chunk of the head row]: every K and V row of the
-// sequence (all heads of the group) is read once, fully coalesced, and each
-// key slot keeps its own running max, sum and output; slots merge at the end.
+// One block of kFirstThreads per (sequence, group of heads). Threads are laid out
+// as [key slot][head][16-byte chunk of the head row]: the K and V rows of all
+// heads of a key are contiguous, so every row of the sequence is read once,
+// fully coalesced. Each key slot walks the keys slot, slot + KS, ... in batches
+// of kFirstBatch rows whose loads are all issued before any is used (several
+// HBM round trips in flight per thread), keeps its own running max, sum and
+// output, and the slots merge through LDS at the end.
+constexpr int kFirstThreads = 512;
+constexpr int kFirstBatch = 4;
+
 template <bool BF, int D>
-__global__ __launch_bounds__(256) void attn_fwd_first_kernel(
+__global__ __launch_bounds__(kFirstThreads) void attn_fwd_first_kernel(
     const void* __restrict__ qf, const void* __restrict__ kp, const void* __restrict__ vp,
     const int32_t* __restrict__ cu, int32_t B, int32_t N, int32_t H, int32_t HPB, float c,
     void* __restrict__ outp, float* __restrict__ lse) {
   constexpr int ES = BF ? 2 : 4;
   constexpr int EPC = 16 / ES;       // elements per 16-byte chunk
   constexpr int GS = D / EPC;        // chunks (threads) per head row
-  __shared__ float sm[256], sl[256];
-  __shared__ float so[256 * EPC];
+  constexpr int U = kFirstBatch;
+  using Chunk = typename std::conditional<BF, u16x8, float4>::type;
+  __shared__ float sm[kFirstThreads], sl[kFirstThreads];
+  __shared__ float so[kFirstThreads * EPC];
 
   const int b = blockIdx.x;
   const int hg = blockIdx.y;
   const int tid = threadIdx.x;
   const int CPR = HPB * GS;
-  const int KS = 256 / CPR;
+  const int KS = kFirstThreads / CPR;
   const int slot = tid / CPR, cidx = tid - slot * CPR;
   const int hl = cidx / GS, sub = cidx - hl * GS;
   const int h = hg * HPB + hl;
@@ -155,42 +163,57 @@ __global__ __launch_bounds__(256) void attn_fwd_first_kernel(
   float m = kNegBig, l = 0.f;
 #pragma unroll
   for (int e = 0; e < EPC; ++e) ov[e] = 0.f;
-  if (active) {
-    const int64_t off = (static_cast<int64_t>(b) * H + h) * D + sub * EPC;
+  auto widen = [](const Chunk& x, float (&y)[EPC]) __attribute__((always_inline)) {
     if constexpr (BF) {
-      const u16x8 x = *reinterpret_cast<const u16x8*>(static_cast<const uint16_t*>(qf) + off);
 #pragma unroll
-      for (int e = 0; e < EPC; ++e) qv[e] = bf16_to_f32(x[e]);
+      for (int e = 0; e < EPC; ++e) y[e] = bf16_to_f32(x[e]);
     } else {
-      const float4 x = *reinterpret_cast<const float4*>(static_cast<const float*>(qf) + off);
-      qv[0] = x.x; qv[1] = x.y; qv[2] = x.z; qv[3] = x.w;
+      y[0] = x.x; y[1] = x.y; y[2] = x.z; y[3] = x.w;
     }
-    for (int j = c0 + slot; j < c1; j += KS) {
-      const int64_t koff = (static_cast<int64_t>(j) * H + h) * D + sub * EPC;
-      float kv[EPC], vv[EPC];
-      if constexpr (BF) {
-        const u16x8 xk = *reinterpret_cast<const u16x8*>(static_cast<const uint16_t*>(kp) + koff);
-        const u16x8 xv = *reinterpret_cast<const u16x8*>(static_cast<const uint16_t*>(vp) + koff);
+  };
+  if (active) {
+    const int64_t hoff = static_cast<int64_t>(h) * D + sub * EPC;
+    widen(*reinterpret_cast<const Chunk*>(static_cast<const char*>(qf) + (static_cast<int64_t>(b) * H * D + hoff) * ES),
+          qv);
+    const char* kb = static_cast<const char*>(kp) + hoff * ES;
+    const char* vb = static_cast<const char*>(vp) + hoff * ES;
+    const int64_t rs = static_cast<int64_t>(H) * D * ES;  // bytes per packed row
+    for (int j0 = c0 + slot; j0 < c1; j0 += U * KS) {
+      Chunk xk[U], xv[U];
 #pragma unroll
-        for (int e = 0; e < EPC; ++e) { kv[e] = bf16_to_f32(xk[e]); vv[e] = bf16_to_f32(xv[e]); }
-      } else {
-        const float4 xk = *reinterpret_cast<const float4*>(static_cast<const float*>(kp) + koff);
-        const float4 xv = *reinterpret_cast<const float4*>(static_cast<const float*>(vp) + koff);
-        kv[0] = xk.x; kv[1] = xk.y; kv[2] = xk.z; kv[3] = xk.w;
-        vv[0] = xv.x; vv[1] = xv.y; vv[2] = xv.z; vv[3] = xv.w;
+      for (int u = 0; u < U; ++u) {  // rows past the sequence re-read its last row; their weight is 0
+        const int j = min(j0 + u * KS, c1 - 1);
+        xk[u] = *reinterpret_cast<const Chunk*>(kb + j * rs);
+        xv[u] = *reinterpret_cast<const Chunk*>(vb + j * rs);
       }
-      float s = 0.f;
+      float x[U];
+      float bmax = -INFINITY;
 #pragma unroll
-      for (int e = 0; e < EPC; ++e) s = fmaf(qv[e], kv[e], s);
+      for (int u = 0; u < U; ++u) {
+        float kv[EPC];
+        widen(xk[u], kv);
+        float s = 0.f;
 #pragma unroll
-      for (int o = 1; o < GS; o <<= 1) s += __shfl_xor(s, o);
-      const float x = s * c;
-      const float mnew = fmaxf(m, x);
+        for (int e = 0; e < EPC; ++e) s = fmaf(qv[e], kv[e], s);
+#pragma unroll
+        for (int o = 1; o < GS; o <<= 1) s += __shfl_xor(s, o);
+        x[u] = j0 + u * KS < c1 ? s * c : -INFINITY;
+        bmax = fmaxf(bmax, x[u]);
+      }
+      const float mnew = fmaxf(m, bmax);
       const float alpha = __builtin_amdgcn_exp2f(m - mnew);
-      const float p = __builtin_amdgcn_exp2f(x - mnew);
-      l = fmaf(l, alpha, p);
+      l *= alpha;
 #pragma unroll
-      for (int e = 0; e < EPC; ++e) ov[e] = fmaf(ov[e], alpha, p * vv[e]);
+      for (int e = 0; e < EPC; ++e) ov[e] *= alpha;
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const float p = __builtin_amdgcn_exp2f(x[u] - mnew);
+        float vv[EPC];
+        widen(xv[u], vv);
+        l += p;
+#pragma unroll
+        for (int e = 0; e < EPC; ++e) ov[e] = fmaf(p, vv[e], ov[e]);
+      }
       m = mnew;
     }
   }
@@ -246,11 +269,11 @@ template <bool BF, int D>
 hipError_t first_dispatch(const void* q, const void* k, const void* v, const int32_t* cu, int32_t B,
                           int32_t N, int32_t H, float scale, void* out, float* lse, hipStream_t stream) {
   constexpr int GS = D / (BF ? 8 : 4);
-  const int HPB = (H * GS <= 256) ? H : 256 / GS;
+  const int HPB = (H * GS <= kFirstThreads) ? H : kFirstThreads / GS;
   const int HG = (H + HPB - 1) / HPB;
   const float c = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
   hipEvent_t ev_attn_fwd_first = timing_start(stream);
-  hipLaunchKernelGGL((attn_fwd_first_kernel<BF, D>), dim3(B, HG), dim3(256), 0, stream, q, k, v, cu, B,
+  hipLaunchKernelGGL((attn_fwd_first_kernel<BF, D>), dim3(B, HG), dim3(kFirstThreads), 0, stream, q, k, v, cu, B,
                    N, H, HPB, c, out, lse);
   timing_stop("attn_fwd_first", ev_attn_fwd_first, stream);
   return hipGetLastError();
