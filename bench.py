@@ -23,7 +23,6 @@ bounded sample of the same batch.
 Prints ONE JSON line.
 """
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -35,26 +34,6 @@ sys.path.insert(0, ROOT)
 METRIC = "packed varlen attn fwd real tokens/s + TFLOP/s, % of MI355X MFMA/HBM roofline"
 PEAK = {"bf16": 2500.0, "fp32": 157.3}   # dense MFMA TFLOP/s
 HBM_PEAK = 8000.0                        # GB/s
-
-KERNEL_SOURCES = {
-    "attn_fwd": ["attn_fwd.hip", "attn_common.h"],
-    "attn_fwd_first": ["attn_fwd.hip"],
-    "bwd_delta": ["attn_bwd.hip", "attn_common.h"],
-    "bwd_dkdv": ["attn_bwd.hip", "attn_common.h"],
-    "bwd_dq": ["attn_bwd.hip", "attn_common.h"],
-    "pack_rows": ["pack.hip"],
-    "unpack_rows": ["pack.hip"],
-    "scan": ["pack.hip"],
-    "worklist": ["pack.hip"],
-}
-
-
-def source_hash(kernel: str) -> str:
-    h = hashlib.sha256()
-    for f in KERNEL_SOURCES.get(kernel, []):
-        with open(os.path.join(ROOT, "padding_free_packed_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
-    return h.hexdigest()[:16]
 
 
 def algo_work(kernel, w, N, L2, e, with_lse):
@@ -90,6 +69,8 @@ def rate(kind, amount, ms, dtype):
 
 
 def load_traffic(kernel, workload):
+    from padding_free_packed_amd.profiling import source_hash
+
     """HBM bytes per launch from committed rocprofv3 counter runs, if taken on this source."""
     p = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.json")
     if not os.path.exists(p):
@@ -150,6 +131,9 @@ def main():
                     choices=["graph_transformer", "short_query", "long_document", "mixed_training", "tiny"])
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="after the timed region, copy a buffer of this many MiB three times (a plain copy kernel "
+                         "of known size, for scaling HBM counters)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -285,6 +269,15 @@ def main():
         "breakdown": breakdown,
         "wall_s_timed_region": wall,
     }
+    if args.copy_probe_mib > 0:
+        nbytes = args.copy_probe_mib << 20
+        src = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        result["copy_probe_bytes"] = nbytes
+        del src, dst
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)
     print(json.dumps(result))

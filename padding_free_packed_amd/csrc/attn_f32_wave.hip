@@ -1,3 +1,6 @@
+// fp32 attention kernels with one independent wave per 32 packed rows: the forward,
+// and the dQ and dK/dV passes of the backward.
+//
 // fp32 forward, one independent wave per (head, 32 packed query rows).
 //
 // On fp32 the MFMA operands of both products are one element per lane per
