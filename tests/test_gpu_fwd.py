@@ -100,6 +100,25 @@ def test_closed_forms_on_gpu():
     np.testing.assert_allclose(o[38:338], 0.25, atol=1e-6)
 
 
+SHORT_EDGE = [64, 1, 63, 33, 32, 31, 1, 1, 64, 64, 2, 17, 48, 49, 5, 64, 1]
+
+
+@pytest.mark.parametrize("d", [8, 32, 64, 128])
+@pytest.mark.parametrize("S", [64, 48, 16])
+def test_short_length_bounds(d, S):
+    # length bounds <= 64 take the windowed short-sequence path for bf16 d 32/64:
+    # lengths at the bound, of one token, and straddling 32-key blocks and 64-row tiles
+    rng = np.random.default_rng(48 + S + d)
+    L = np.concatenate([np.minimum(SHORT_EDGE, S), rng.integers(1, S + 1, size=300)])
+    L = rng.permutation(L).astype(np.int32)
+    check_full(W.custom(49 + d, L, S, 3, d, W.BF16), f"short bound S={S} d={d}")
+
+
+def test_short_bound_far_above_lengths():
+    # a bound much larger than every length: the window holds many foreign rows
+    check_full(W.custom(50, W.random_lengths(51, 400, 1, 9), 64, 2, 64, W.BF16), "bound 64, lengths <= 9")
+
+
 @pytest.mark.parametrize("d", [32, 64, 128])
 def test_running_max_paths(d):
     # logits that drift along the keys: for some queries the running max creeps up
