@@ -60,8 +60,12 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(
     int32_t T, float c, float scale, void* __restrict__ dkp, void* __restrict__ dvp) {
   using G = Geo<BF, D>;
   using E = typename G::E;
-  __shared__ __align__(16) E qt[2][G::TSZ];
-  __shared__ __align__(16) E dt[2][G::TSZ];
+  // bf16 tiles with whole 16-byte chunks per lane half use the XOR-swizzled layout
+  // (conflict-free for both the row reads and the transposing reads)
+  constexpr bool SWZ = BF && D % 32 == 0;
+  constexpr int TS = SWZ ? kBlk * D : G::TSZ;
+  __shared__ __align__(16) E qt[2][TS];
+  __shared__ __align__(16) E dt[2][TS];
   __shared__ __align__(16) float ls[2][kBlk];
   __shared__ __align__(16) float dl[2][kBlk];
   __shared__ int32_t cul[kAttnTileRows + 2];
@@ -109,8 +113,13 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(
   int buf = 0;
   if (sp.lo < sp.hi) gload(sp.lo);
   for (int qb = sp.lo; qb < sp.hi; qb += kBlk) {
-    tile_store<BF, D>(qt[buf], qr);
-    tile_store<BF, D>(dt[buf], dr);
+    if constexpr (SWZ) {
+      tile_store_swz<D>(qt[buf], qr);
+      tile_store_swz<D>(dt[buf], dr);
+    } else {
+      tile_store<BF, D>(qt[buf], qr);
+      tile_store<BF, D>(dt[buf], dr);
+    }
     if (tid < kBlk) {
       ls[buf][tid] = lsr;
       dl[buf][tid] = dlr;
@@ -122,8 +131,13 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(
 #pragma unroll
       for (int qq = 0; qq < 2; ++qq) {
         floatx16 s = floatx16{}, dp = floatx16{};
-        mma_rows_regs<BF, D>(qt[buf], 32 * qq, kreg, s, ql, g);   // S[q][key]
-        mma_rows_regs<BF, D>(dt[buf], 32 * qq, vreg, dp, ql, g);  // dP[q][key]
+        if constexpr (SWZ) {
+          mma_rows_swz<D>(qt[buf], 32 * qq, kreg, s, ql, g);   // S[q][key]
+          mma_rows_swz<D>(dt[buf], 32 * qq, vreg, dp, ql, g);  // dP[q][key]
+        } else {
+          mma_rows_regs<BF, D>(qt[buf], 32 * qq, kreg, s, ql, g);
+          mma_rows_regs<BF, D>(dt[buf], 32 * qq, vreg, dp, ql, g);
+        }
         const int base = qb + 32 * qq + 4 * g;
         if (need_mask) mask_block(s, jk0 - base, jk1 - base);
 #pragma unroll
@@ -140,8 +154,16 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(
             dp[i] = p * (dp[i] - dvv[j]);
           }
         }
-        mma_tr_regs<BF, D>(dt[buf], 32 * qq, s, dv, lane);   // dV^T += dO^T P
-        mma_tr_regs<BF, D>(qt[buf], 32 * qq, dp, dk, lane);  // dK^T += Q^T dS
+        if constexpr (SWZ) {
+          bf16x8 pb[2], sb[2];
+          acc_to_bf16(s, pb);
+          acc_to_bf16(dp, sb);
+          mma_tr_swz<D>(dt[buf], 32 * qq, pb, dv, lane);  // dV^T += dO^T P
+          mma_tr_swz<D>(qt[buf], 32 * qq, sb, dk, lane);  // dK^T += Q^T dS
+        } else {
+          mma_tr_regs<BF, D>(dt[buf], 32 * qq, s, dv, lane);
+          mma_tr_regs<BF, D>(qt[buf], 32 * qq, dp, dk, lane);
+        }
       }
     }
     buf ^= 1;
@@ -160,8 +182,10 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
     int32_t T, float c, float scale, void* __restrict__ dqp) {
   using G = Geo<BF, D>;
   using E = typename G::E;
-  __shared__ __align__(16) E kt[2][G::TSZ];
-  __shared__ __align__(16) E vt[2][G::TSZ];
+  constexpr bool SWZ = BF && D % 32 == 0;
+  constexpr int TS = SWZ ? kBlk * D : G::TSZ;
+  __shared__ __align__(16) E kt[2][TS];
+  __shared__ __align__(16) E vt[2][TS];
   __shared__ int32_t cul[kAttnTileRows + 2];
 
   const int lin = xcd_remap(blockIdx.x, gridDim.x);
@@ -196,8 +220,13 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
     tile_gload<BF, D>(vp, sp.lo, sp.hi, H, h, vr);
   }
   for (int kb = sp.lo; kb < sp.hi; kb += kBlk) {
-    tile_store<BF, D>(kt[buf], kr);
-    tile_store<BF, D>(vt[buf], vr);
+    if constexpr (SWZ) {
+      tile_store_swz<D>(kt[buf], kr);
+      tile_store_swz<D>(vt[buf], vr);
+    } else {
+      tile_store<BF, D>(kt[buf], kr);
+      tile_store<BF, D>(vt[buf], vr);
+    }
     __syncthreads();
     if (kb + kBlk < sp.hi) {
       tile_gload<BF, D>(kp, kb + kBlk, sp.hi, H, h, kr);
@@ -208,8 +237,13 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
         floatx16 s = floatx16{}, dp = floatx16{};
-        mma_rows_regs<BF, D>(kt[buf], 32 * kk, qreg, s, ql, g);   // S^T[key][q]
-        mma_rows_regs<BF, D>(vt[buf], 32 * kk, dreg, dp, ql, g);  // dP^T[key][q]
+        if constexpr (SWZ) {
+          mma_rows_swz<D>(kt[buf], 32 * kk, qreg, s, ql, g);   // S^T[key][q]
+          mma_rows_swz<D>(vt[buf], 32 * kk, dreg, dp, ql, g);  // dP^T[key][q]
+        } else {
+          mma_rows_regs<BF, D>(kt[buf], 32 * kk, qreg, s, ql, g);
+          mma_rows_regs<BF, D>(vt[buf], 32 * kk, dreg, dp, ql, g);
+        }
         if (need_mask) {
           const int base = kb + 32 * kk + 4 * g;
           mask_block(s, qk0 - base, qk1 - base);
@@ -219,7 +253,13 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
           const float p = __builtin_amdgcn_exp2f(fmaf(s[i], c, -lse2));
           dp[i] = p * (dp[i] - dlq);
         }
-        mma_tr_regs<BF, D>(kt[buf], 32 * kk, dp, dq, lane);  // dQ^T += K^T dS^T
+        if constexpr (SWZ) {
+          bf16x8 sb[2];
+          acc_to_bf16(dp, sb);
+          mma_tr_swz<D>(kt[buf], 32 * kk, sb, dq, lane);  // dQ^T += K^T dS^T
+        } else {
+          mma_tr_regs<BF, D>(kt[buf], 32 * kk, dp, dq, lane);
+        }
       }
     }
     buf ^= 1;

@@ -358,6 +358,41 @@ __device__ __forceinline__ bf16x8 swz_read_b128(const uint16_t* tile, int r, int
   return as_bf16x8(*reinterpret_cast<const u16x8*>(reinterpret_cast<const char*>(tile) + chunk_off<CH>(r, c)));
 }
 
+// Registers (as loaded by tile_gload) -> unpadded bf16 tile of kBlk rows with
+// XOR-swizzled 16-byte chunks.
+template <int D>
+__device__ __forceinline__ void tile_store_swz(uint16_t* tile, const uint4 (&r)[Geo<true, D>::PER]) {
+  using G = Geo<true, D>;
+  constexpr int CH = D / 8;
+#pragma unroll
+  for (int p = 0; p < G::PER; ++p) {
+    const int ch = threadIdx.x + p * kThreads;
+    if (G::TOTCH % kThreads == 0 || ch < G::TOTCH) {
+      const int row = ch / CH, col = ch - row * CH;
+      *reinterpret_cast<uint4*>(reinterpret_cast<char*>(tile) + chunk_off<CH>(row, col)) = r[p];
+    }
+  }
+}
+
+// The mma_rows_regs product over a swizzled bf16 tile.
+template <int D>
+__device__ __forceinline__ void mma_rows_swz(const uint16_t* tile, int row0, const bf16x8 (&y)[D / 16],
+                                             floatx16& acc, int ql, int g) {
+  constexpr int CH = D / 8;
+#pragma unroll
+  for (int st = 0; st < D / 16; ++st)
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(swz_read_b128<CH>(tile, row0 + ql, g * (CH / 2) + st), y[st], acc,
+                                                  0, 0, 0);
+}
+
+// The 16 values of a 32x32 accumulator block as two bf16 MFMA B operands.
+__device__ __forceinline__ void acc_to_bf16(const floatx16& p, bf16x8 (&pb)[2]) {
+#pragma unroll
+  for (int s = 0; s < 2; ++s)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) pb[s][j] = static_cast<__bf16>(p[8 * s + j]);
+}
+
 // acc[db] += X^T . P over a swizzled bf16 tile (the mma_tr_regs product).
 template <int D>
 __device__ __forceinline__ void mma_tr_swz(const uint16_t* tile, int row0, const bf16x8 (&pb)[2],

@@ -29,8 +29,12 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
     int32_t H, int32_t T, float c, void* __restrict__ op, float* __restrict__ lse) {
   using G = Geo<BF, D>;
   using E = typename G::E;
-  __shared__ __align__(16) E kt[2][G::TSZ];
-  __shared__ __align__(16) E vt[2][G::TSZ];
+  // bf16 tiles with whole 16-byte chunks per lane half use the XOR-swizzled layout
+  // (conflict-free for both the row reads and the transposing reads)
+  constexpr bool SWZ = BF && D % 32 == 0;
+  constexpr int TS = SWZ ? kBlk * D : G::TSZ;
+  __shared__ __align__(16) E kt[2][TS];
+  __shared__ __align__(16) E vt[2][TS];
   __shared__ int32_t cul[kAttnTileRows + 2];
 
   const int lin = xcd_remap(blockIdx.x, gridDim.x);
@@ -65,8 +69,13 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
     tile_gload<BF, D>(vp, sp.lo, sp.hi, H, h, vr);
   }
   for (int kb = sp.lo; kb < sp.hi; kb += kBlk) {
-    tile_store<BF, D>(kt[buf], kr);
-    tile_store<BF, D>(vt[buf], vr);
+    if constexpr (SWZ) {
+      tile_store_swz<D>(kt[buf], kr);
+      tile_store_swz<D>(vt[buf], vr);
+    } else {
+      tile_store<BF, D>(kt[buf], kr);
+      tile_store<BF, D>(vt[buf], vr);
+    }
     __syncthreads();
     if (kb + kBlk < sp.hi) {
       tile_gload<BF, D>(kp, kb + kBlk, sp.hi, H, h, kr);
@@ -77,7 +86,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
         s[kk] = floatx16{};
-        mma_rows_regs<BF, D>(kt[buf], 32 * kk, qr, s[kk], ql, g);
+        if constexpr (SWZ) mma_rows_swz<D>(kt[buf], 32 * kk, qr, s[kk], ql, g);
+        else mma_rows_regs<BF, D>(kt[buf], 32 * kk, qr, s[kk], ql, g);
       }
       if (!(kb >= mk0 && kb + kBlk <= mk1)) {
 #pragma unroll
@@ -111,7 +121,15 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
           l += p;
         }
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk) mma_tr_regs<BF, D>(vt[buf], 32 * kk, s[kk], o, lane);
+      for (int kk = 0; kk < 2; ++kk) {
+        if constexpr (SWZ) {
+          bf16x8 pb[2];
+          acc_to_bf16(s[kk], pb);
+          mma_tr_swz<D>(vt[buf], 32 * kk, pb, o, lane);
+        } else {
+          mma_tr_regs<BF, D>(vt[buf], 32 * kk, s[kk], o, lane);
+        }
+      }
     }
     buf ^= 1;
   }
