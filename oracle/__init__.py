@@ -34,6 +34,12 @@ gigl.nn.packed_attention" and the packed-encoders README):
   as ``_padded_packed_attention`` does.
 * ``worklist``: for a tile height R, the sequence holding the first row of every
   R-row tile of the packed buffer (the library's work list; brute force).
+* local attention: every attention function takes an optional ``window`` w;
+  query i then sees only the keys j of its own sequence with |i - j| <= w. This
+  is the sliding-window ("local") non-causal attention that the packed-encoders
+  README lists next to global attention for its short-sequence kernel and that
+  its FlashAttention backend prunes; the README names a "local-64" variant
+  without fixing how 64 maps to a radius, so w is a parameter here.
 
 Every input array is float64 (attention) or raw bits (pack/unpack); callers widen
 fp32 values and bf16 bit patterns exactly before calling.
@@ -130,7 +136,21 @@ def _segments(cu_seqlens):
     return [(cu[b], cu[b + 1]) for b in range(len(cu) - 1)]
 
 
-def attention(q, k, v, cu_seqlens, scale: float):
+def _band(rows, cols, window):
+    """Allowed (query, key) pairs for packed row indices ``rows`` x ``cols`` of one
+    sequence: all of them (global attention) or |i - j| <= window (local)."""
+    if window is None:
+        return None
+    i = np.asarray(rows, dtype=np.int64)[:, None]
+    j = np.asarray(cols, dtype=np.int64)[None, :]
+    return np.abs(i - j) <= int(window)
+
+
+def _restrict(s, allowed):
+    return s if allowed is None else np.where(allowed, s, -np.inf)
+
+
+def attention(q, k, v, cu_seqlens, scale: float, window=None):
     """Non-causal attention confined to each sequence, plus its log-sum-exp.
 
     For sequence b (rows c0..c1-1) and head h, for every query row i:
@@ -140,6 +160,9 @@ def attention(q, k, v, cu_seqlens, scale: float):
     logits). This is softmax(scale * Q K^T) V per sequence, the result of the
     varlen kernel and of the padded SDPA path on the GiGL page.
 
+    With ``window`` w (local attention) the keys are further limited to
+    |i - j| <= w.
+
     q, k, v: float64 [N, H, d]. Returns o float64 [N, H, d], lse float64 [H, N].
     """
     _check_f64(q, k, v)
@@ -147,8 +170,9 @@ def attention(q, k, v, cu_seqlens, scale: float):
     o = np.zeros((N, H, d))
     lse = np.zeros((H, N))
     for c0, c1 in _segments(cu_seqlens):
+        allowed = _band(range(c0, c1), range(c0, c1), window)
         for h in range(H):
-            s = scale * (q[c0:c1, h, :] @ k[c0:c1, h, :].T)
+            s = _restrict(scale * (q[c0:c1, h, :] @ k[c0:c1, h, :].T), allowed)
             m = s.max(axis=1, keepdims=True)
             w = np.exp(s - m)
             l = w.sum(axis=1, keepdims=True)
@@ -170,7 +194,7 @@ def sequence_of_rows(cu_seqlens, rows):
     return out
 
 
-def attention_rows(q, k, v, cu_seqlens, scale: float, rows):
+def attention_rows(q, k, v, cu_seqlens, scale: float, rows, window=None):
     """``attention`` evaluated only at the given packed query rows (all heads).
 
     Used to check very large batches at sampled outputs: each sampled row needs
@@ -186,8 +210,10 @@ def attention_rows(q, k, v, cu_seqlens, scale: float, rows):
     lse = np.zeros((H, len(rows)))
     for n, (r, b) in enumerate(zip(rows, seqs)):
         c0, c1 = cu[b], cu[b + 1]
+        allowed = _band([r], range(c0, c1), window)
+        allowed = None if allowed is None else allowed[0]
         for h in range(H):
-            s = scale * (k[c0:c1, h, :] @ q[r, h, :])
+            s = _restrict(scale * (k[c0:c1, h, :] @ q[r, h, :]), allowed)
             m = s.max()
             w = np.exp(s - m)
             l = w.sum()
@@ -196,7 +222,7 @@ def attention_rows(q, k, v, cu_seqlens, scale: float, rows):
     return o, lse
 
 
-def attention_first_token(q_first, k, v, cu_seqlens, scale: float, seqs=None):
+def attention_first_token(q_first, k, v, cu_seqlens, scale: float, seqs=None, window=None):
     """One query per sequence (its first token) attending over that sequence's keys.
 
     GiGL ``packed_attention`` with ``query_is_first_token``: ``query`` holds one
@@ -215,8 +241,10 @@ def attention_first_token(q_first, k, v, cu_seqlens, scale: float, seqs=None):
     lse = np.zeros((H, len(seqs)))
     for n, b in enumerate(seqs):
         c0, c1 = segs[b]
+        allowed = _band([c0], range(c0, c1), window)
+        allowed = None if allowed is None else allowed[0]
         for h in range(H):
-            s = scale * (k[c0:c1, h, :] @ q_first[b, h, :])
+            s = _restrict(scale * (k[c0:c1, h, :] @ q_first[b, h, :]), allowed)
             m = s.max()
             w = np.exp(s - m)
             l = w.sum()
@@ -225,7 +253,7 @@ def attention_first_token(q_first, k, v, cu_seqlens, scale: float, seqs=None):
     return o, lse
 
 
-def attention_backward(dout, q, k, v, cu_seqlens, scale: float, seqs=None, out=None, lse=None):
+def attention_backward(dout, q, k, v, cu_seqlens, scale: float, seqs=None, out=None, lse=None, window=None):
     """Gradients of ``<dout, attention(q, k, v)>`` in q, k and v.
 
     Per sequence and head, with P = softmax(scale * Q K^T) (rows) and O = P V:
@@ -240,7 +268,8 @@ def attention_backward(dout, q, k, v, cu_seqlens, scale: float, seqs=None, out=N
     exact gradient.
 
     ``seqs`` optionally limits the computation to some sequences (rows of other
-    sequences are left zero). Returns dq, dk, dv float64 [N, H, d].
+    sequences are left zero). With ``window`` the pairs outside |i - j| <= w
+    have P = 0. Returns dq, dk, dv float64 [N, H, d].
     """
     _check_f64(dout, q, k, v)
     N, H, d = q.shape
@@ -251,9 +280,10 @@ def attention_backward(dout, q, k, v, cu_seqlens, scale: float, seqs=None, out=N
     seqs = range(len(segs)) if seqs is None else seqs
     for b in seqs:
         c0, c1 = segs[b]
+        allowed = _band(range(c0, c1), range(c0, c1), window)
         for h in range(H):
             qs, ks, vs, dos = q[c0:c1, h, :], k[c0:c1, h, :], v[c0:c1, h, :], dout[c0:c1, h, :]
-            s = scale * (qs @ ks.T)
+            s = _restrict(scale * (qs @ ks.T), allowed)
             if lse is None:
                 m = s.max(axis=1, keepdims=True)
                 lse_b = m + np.log(np.exp(s - m).sum(axis=1, keepdims=True))
@@ -273,7 +303,7 @@ def attention_backward(dout, q, k, v, cu_seqlens, scale: float, seqs=None, out=N
 # ---------------------------------------------------------------- second route: padded grid
 
 def padded_attention(q, k, v, cu_seqlens, max_seq_len: int, scale: float,
-                     query_is_first_token: bool = False):
+                     query_is_first_token: bool = False, window=None):
     """Attention by padding, following GiGL's ``_padded_packed_attention``.
 
     Tokens are placed on a ``[B, S]`` grid; padded key positions get the additive
@@ -306,7 +336,11 @@ def padded_attention(q, k, v, cu_seqlens, max_seq_len: int, scale: float,
         g[seq_of_token, pos_of_token] = x
         grids.append(g.transpose(0, 2, 1, 3))  # [B, H, S, d]
     qg, kg, vg = grids
-    bias = np.where(mask, 0.0, np.finfo(np.float64).min / 2.0)[:, None, None, :]
+    keep = np.broadcast_to(mask[:, None, None, :], (B, 1, S, S))
+    if window is not None:  # grid positions stand for packed rows at the same offsets
+        pos = np.arange(S)
+        keep = keep & (np.abs(pos[:, None] - pos[None, :]) <= int(window))[None, None]
+    bias = np.where(keep, 0.0, np.finfo(np.float64).min / 2.0)
     s = scale * np.einsum("bhid,bhjd->bhij", qg, kg) + bias
     m = s.max(axis=-1, keepdims=True)
     w = np.exp(s - m)
