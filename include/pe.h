@@ -213,6 +213,34 @@ pe_status pe_varlen_attn_bwd(const void* dout, const void* q, const void* k, con
                              void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
                              void* stream);
 
+/* ---------------------------------------------------------- local attention
+ * pe_varlen_attn_fwd_local / pe_varlen_attn_bwd_local: pe_varlen_attn_fwd and
+ * pe_varlen_attn_bwd with each query row i seeing only the keys j of its own
+ * sequence with |i - j| <= window (sliding-window, non-causal).
+ *
+ * Source: the packed-encoders README, backend table: its short-sequence kernel
+ * serves "global or local" attention (a "local-64" variant) and its
+ * FlashAttention backend prunes by sliding window. The README does not say how
+ * 64 maps to a radius; `window` is the radius itself (a window of 64 keys
+ * centred on the query is window = 32). Key tiles outside every row's band are
+ * skipped, so the cost falls with the window.
+ *
+ * Arguments as for the global calls, plus
+ *   window   >= 0 (PE_ERR_ARG otherwise); window >= max_seq_len - 1 is global
+ *            attention. The backward must be given the window of its forward.
+ */
+pe_status pe_varlen_attn_fwd_local(const void* q, const void* k, const void* v, const int32_t* cu_seqlens,
+                                   int32_t num_seqs, int64_t total_tokens, int32_t max_seq_len,
+                                   int32_t num_heads, int32_t head_dim, pe_dtype dtype, float softmax_scale,
+                                   int32_t window, void* out, float* lse, void* workspace,
+                                   size_t workspace_bytes, void* stream);
+pe_status pe_varlen_attn_bwd_local(const void* dout, const void* q, const void* k, const void* v,
+                                   const void* out, const float* lse, const int32_t* cu_seqlens,
+                                   int32_t num_seqs, int64_t total_tokens, int32_t max_seq_len,
+                                   int32_t num_heads, int32_t head_dim, pe_dtype dtype, float softmax_scale,
+                                   int32_t window, void* dq, void* dk, void* dv, void* workspace,
+                                   size_t workspace_bytes, void* stream);
+
 /* ------------------------------------------------------------- kernel timing
  * Measurement support, not part of the computation. While enabled, every
  * kernel the library launches is bracketed by two HIP events recorded on the

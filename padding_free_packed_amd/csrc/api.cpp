@@ -157,10 +157,15 @@ size_t pe_attn_workspace_size(int32_t num_seqs, int64_t total_tokens, int32_t nu
   return s;
 }
 
-pe_status pe_varlen_attn_fwd(const void* q, const void* k, const void* v, const int32_t* cu_seqlens,
-                             int32_t num_seqs, int64_t total_tokens, int32_t max_seq_len, int32_t num_heads,
-                             int32_t head_dim, pe_dtype dtype, float softmax_scale, void* out, float* lse,
-                             void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// The forward for every entry point: win is the local-attention radius, or -1.
+pe_status fwd_impl(const void* q, const void* k, const void* v, const int32_t* cu_seqlens, int32_t num_seqs,
+                   int64_t total_tokens, int32_t max_seq_len, int32_t num_heads, int32_t head_dim, pe_dtype dtype,
+                   float softmax_scale, int32_t win, void* out, float* lse, void* workspace, size_t workspace_bytes,
+                   void* stream) {
   if (!q || !k || !v || !cu_seqlens || !out) return PE_ERR_NULL;
   const pe_status s =
       check_attn_args(num_seqs, total_tokens, max_seq_len, num_heads, head_dim, dtype, softmax_scale);
@@ -176,14 +181,40 @@ pe_status pe_varlen_attn_fwd(const void* q, const void* k, const void* v, const 
     hipError_t e = pe::launch_worklist(cu_seqlens, num_seqs, total_tokens, pe::kAttnWaveRows, items, st);
     if (e != hipSuccess) return PE_ERR_HIP;
     return hip_status(pe::launch_attn_fwd_f32_wave(head_dim, q, k, v, cu_seqlens, items, num_seqs,
-                                                   static_cast<int32_t>(total_tokens), num_heads, softmax_scale, out,
-                                                   lse, st));
+                                                   static_cast<int32_t>(total_tokens), num_heads, win, softmax_scale,
+                                                   out, lse, st));
   }
   hipError_t e = pe::launch_worklist(cu_seqlens, num_seqs, total_tokens, pe::kAttnTileRows, items, st);
   if (e != hipSuccess) return PE_ERR_HIP;
   e = pe::launch_attn_fwd(dtype == PE_BF16, head_dim, q, k, v, cu_seqlens, items, num_seqs,
-                          static_cast<int32_t>(total_tokens), num_heads, max_seq_len, softmax_scale, out, lse, st);
+                          static_cast<int32_t>(total_tokens), num_heads, max_seq_len, win, softmax_scale, out, lse,
+                          st);
   return hip_status(e);
+}
+
+
+// A window at least max_seq_len - 1 keeps every key of every sequence: global attention.
+int32_t effective_window(int32_t window, int32_t max_seq_len) { return window >= max_seq_len - 1 ? -1 : window; }
+
+}  // namespace
+
+extern "C" {
+
+pe_status pe_varlen_attn_fwd(const void* q, const void* k, const void* v, const int32_t* cu_seqlens,
+                             int32_t num_seqs, int64_t total_tokens, int32_t max_seq_len, int32_t num_heads,
+                             int32_t head_dim, pe_dtype dtype, float softmax_scale, void* out, float* lse,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+  return fwd_impl(q, k, v, cu_seqlens, num_seqs, total_tokens, max_seq_len, num_heads, head_dim, dtype,
+                  softmax_scale, -1, out, lse, workspace, workspace_bytes, stream);
+}
+
+pe_status pe_varlen_attn_fwd_local(const void* q, const void* k, const void* v, const int32_t* cu_seqlens,
+                                   int32_t num_seqs, int64_t total_tokens, int32_t max_seq_len, int32_t num_heads,
+                                   int32_t head_dim, pe_dtype dtype, float softmax_scale, int32_t window, void* out,
+                                   float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+  if (window < 0) return PE_ERR_ARG;
+  return fwd_impl(q, k, v, cu_seqlens, num_seqs, total_tokens, max_seq_len, num_heads, head_dim, dtype,
+                  softmax_scale, effective_window(window, max_seq_len), out, lse, workspace, workspace_bytes, stream);
 }
 
 pe_status pe_varlen_attn_fwd_first_token(const void* q_first, const void* k, const void* v,
@@ -205,11 +236,15 @@ pe_status pe_varlen_attn_fwd_first_token(const void* q_first, const void* k, con
 
 // ------------------------------------------------------------------ backward
 
-pe_status pe_varlen_attn_bwd(const void* dout, const void* q, const void* k, const void* v, const void* out,
-                             const float* lse, const int32_t* cu_seqlens, int32_t num_seqs, int64_t total_tokens,
-                             int32_t max_seq_len, int32_t num_heads, int32_t head_dim, pe_dtype dtype,
-                             float softmax_scale, void* dq, void* dk, void* dv, void* workspace,
-                             size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// The backward for every entry point: win is the local-attention radius, or -1.
+pe_status bwd_impl(const void* dout, const void* q, const void* k, const void* v, const void* out, const float* lse,
+                   const int32_t* cu_seqlens, int32_t num_seqs, int64_t total_tokens, int32_t max_seq_len,
+                   int32_t num_heads, int32_t head_dim, pe_dtype dtype, float softmax_scale, int32_t win, void* dq,
+                   void* dk, void* dv, void* workspace, size_t workspace_bytes, void* stream) {
   if (!dout || !q || !k || !v || !out || !lse || !cu_seqlens || !dq || !dk || !dv) return PE_ERR_NULL;
   const pe_status s =
       check_attn_args(num_seqs, total_tokens, max_seq_len, num_heads, head_dim, dtype, softmax_scale);
@@ -232,9 +267,33 @@ pe_status pe_varlen_attn_bwd(const void* dout, const void* q, const void* k, con
   }
   e = pe::launch_attn_bwd(dtype == PE_BF16, head_dim, dout, q, k, v, out, lse, cu_seqlens, items,
                           dtype == PE_FP32 ? items32 : nullptr, num_seqs, static_cast<int32_t>(total_tokens),
-                          num_heads, softmax_scale, dq, dk, dv, delta, st);
+                          num_heads, win, softmax_scale, dq, dk, dv, delta, st);
   if (e == hipErrorNotSupported) return PE_ERR_UNSUPPORTED;
   return hip_status(e);
+}
+
+}  // namespace
+
+extern "C" {
+
+pe_status pe_varlen_attn_bwd(const void* dout, const void* q, const void* k, const void* v, const void* out,
+                             const float* lse, const int32_t* cu_seqlens, int32_t num_seqs, int64_t total_tokens,
+                             int32_t max_seq_len, int32_t num_heads, int32_t head_dim, pe_dtype dtype,
+                             float softmax_scale, void* dq, void* dk, void* dv, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  return bwd_impl(dout, q, k, v, out, lse, cu_seqlens, num_seqs, total_tokens, max_seq_len, num_heads, head_dim,
+                  dtype, softmax_scale, -1, dq, dk, dv, workspace, workspace_bytes, stream);
+}
+
+pe_status pe_varlen_attn_bwd_local(const void* dout, const void* q, const void* k, const void* v, const void* out,
+                                   const float* lse, const int32_t* cu_seqlens, int32_t num_seqs,
+                                   int64_t total_tokens, int32_t max_seq_len, int32_t num_heads, int32_t head_dim,
+                                   pe_dtype dtype, float softmax_scale, int32_t window, void* dq, void* dk, void* dv,
+                                   void* workspace, size_t workspace_bytes, void* stream) {
+  if (window < 0) return PE_ERR_ARG;
+  return bwd_impl(dout, q, k, v, out, lse, cu_seqlens, num_seqs, total_tokens, max_seq_len, num_heads, head_dim,
+                  dtype, softmax_scale, effective_window(window, max_seq_len), dq, dk, dv, workspace,
+                  workspace_bytes, stream);
 }
 
 }  // extern "C"

@@ -57,7 +57,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(
     const void* __restrict__ dop, const void* __restrict__ qp, const void* __restrict__ kp,
     const void* __restrict__ vp, const float* __restrict__ lse, const float* __restrict__ delta,
     const int32_t* __restrict__ cu, const int32_t* __restrict__ items, int32_t B, int32_t N, int32_t H,
-    int32_t T, float c, float scale, void* __restrict__ dkp, void* __restrict__ dvp) {
+    int32_t T, int32_t win, float c, float scale, void* __restrict__ dkp, void* __restrict__ dvp) {
   using G = Geo<BF, D>;
   using E = typename G::E;
   // bf16 tiles with whole 16-byte chunks per lane half use the XOR-swizzled layout
@@ -78,7 +78,10 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(
   const int krow = sp.r0 + wv * 32 + ql;
   const bool kvalid = krow < sp.rend;
   int jk0 = 0, jk1 = 0;  // query rows of this key's sequence
-  if (kvalid) own_range(cul, sp.ncu, krow, jk0, jk1);
+  if (kvalid) {
+    own_range(cul, sp.ncu, krow, jk0, jk1);
+    band_limit(krow, win, jk0, jk1);
+  }
   const int wq0 = wave_min_i(kvalid ? jk0 : INT_MAX);
   const int wq1 = wave_max_i(kvalid ? jk1 : INT_MIN);
   const int mq0 = wave_max_i(kvalid ? jk0 : INT_MIN);
@@ -96,23 +99,26 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(
     dv[db] = floatx16{};
   }
 
+  // query rows of the tile's sequences, and within win of its keys for local attention
+  const int qlo = win >= 0 ? max(sp.lo, sp.r0 - win) : sp.lo;
+  const int qhi = win >= 0 ? min(sp.hi, sp.rend + win) : sp.hi;
   uint4 qr[G::PER], dr[G::PER];
   float lsr = 0.f, dlr = 0.f;
   const float* lse_h = lse + static_cast<int64_t>(h) * N;
   const float* del_h = delta + static_cast<int64_t>(h) * N;
   auto gload = [&](int qb) {
-    tile_gload<BF, D>(qp, qb, sp.hi, H, h, qr);
-    tile_gload<BF, D>(dop, qb, sp.hi, H, h, dr);
+    tile_gload<BF, D>(qp, qb, qhi, H, h, qr);
+    tile_gload<BF, D>(dop, qb, qhi, H, h, dr);
     if (tid < kBlk) {
       const int row = qb + tid;
-      lsr = row < sp.hi ? lse_h[row] * kLog2e : 0.f;
-      dlr = row < sp.hi ? del_h[row] : 0.f;
+      lsr = row < qhi ? lse_h[row] * kLog2e : 0.f;
+      dlr = row < qhi ? del_h[row] : 0.f;
     }
   };
 
   int buf = 0;
-  if (sp.lo < sp.hi) gload(sp.lo);
-  for (int qb = sp.lo; qb < sp.hi; qb += kBlk) {
+  if (qlo < qhi) gload(qlo);
+  for (int qb = qlo; qb < qhi; qb += kBlk) {
     if constexpr (SWZ) {
       tile_store_swz<D>(qt[buf], qr);
       tile_store_swz<D>(dt[buf], dr);
@@ -125,7 +131,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(
       dl[buf][tid] = dlr;
     }
     __syncthreads();
-    if (qb + kBlk < sp.hi) gload(qb + kBlk);
+    if (qb + kBlk < qhi) gload(qb + kBlk);
     if (qb < wq1 && qb + kBlk > wq0) {
       const bool need_mask = !(qb >= mq0 && qb + kBlk <= mq1);
 #pragma unroll
@@ -179,7 +185,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
     const void* __restrict__ dop, const void* __restrict__ qp, const void* __restrict__ kp,
     const void* __restrict__ vp, const float* __restrict__ lse, const float* __restrict__ delta,
     const int32_t* __restrict__ cu, const int32_t* __restrict__ items, int32_t B, int32_t N, int32_t H,
-    int32_t T, float c, float scale, void* __restrict__ dqp) {
+    int32_t T, int32_t win, float c, float scale, void* __restrict__ dqp) {
   using G = Geo<BF, D>;
   using E = typename G::E;
   constexpr bool SWZ = BF && D % 32 == 0;
@@ -196,7 +202,10 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
   const int qrow = sp.r0 + wv * 32 + ql;
   const bool qvalid = qrow < sp.rend;
   int qk0 = 0, qk1 = 0;
-  if (qvalid) own_range(cul, sp.ncu, qrow, qk0, qk1);
+  if (qvalid) {
+    own_range(cul, sp.ncu, qrow, qk0, qk1);
+    band_limit(qrow, win, qk0, qk1);
+  }
   const int wk0 = wave_min_i(qvalid ? qk0 : INT_MAX);
   const int wk1 = wave_max_i(qvalid ? qk1 : INT_MIN);
   const int mk0 = wave_max_i(qvalid ? qk0 : INT_MIN);
@@ -214,12 +223,14 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
   for (int db = 0; db < G::DB; ++db) dq[db] = floatx16{};
 
   uint4 kr[G::PER], vr[G::PER];
+  const int klo = win >= 0 ? max(sp.lo, sp.r0 - win) : sp.lo;
+  const int khi = win >= 0 ? min(sp.hi, sp.rend + win) : sp.hi;
   int buf = 0;
-  if (sp.lo < sp.hi) {
-    tile_gload<BF, D>(kp, sp.lo, sp.hi, H, h, kr);
-    tile_gload<BF, D>(vp, sp.lo, sp.hi, H, h, vr);
+  if (klo < khi) {
+    tile_gload<BF, D>(kp, klo, khi, H, h, kr);
+    tile_gload<BF, D>(vp, klo, khi, H, h, vr);
   }
-  for (int kb = sp.lo; kb < sp.hi; kb += kBlk) {
+  for (int kb = klo; kb < khi; kb += kBlk) {
     if constexpr (SWZ) {
       tile_store_swz<D>(kt[buf], kr);
       tile_store_swz<D>(vt[buf], vr);
@@ -228,9 +239,9 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
       tile_store<BF, D>(vt[buf], vr);
     }
     __syncthreads();
-    if (kb + kBlk < sp.hi) {
-      tile_gload<BF, D>(kp, kb + kBlk, sp.hi, H, h, kr);
-      tile_gload<BF, D>(vp, kb + kBlk, sp.hi, H, h, vr);
+    if (kb + kBlk < khi) {
+      tile_gload<BF, D>(kp, kb + kBlk, khi, H, h, kr);
+      tile_gload<BF, D>(vp, kb + kBlk, khi, H, h, vr);
     }
     if (kb < wk1 && kb + kBlk > wk0) {
       const bool need_mask = !(kb >= mk0 && kb + kBlk <= mk1);
@@ -270,7 +281,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
 template <bool BF, int D>
 hipError_t bwd_dispatch(const void* dout, const void* q, const void* k, const void* v, const void* out,
                         const float* lse, const int32_t* cu, const int32_t* items, const int32_t* items32, int32_t B,
-                        int32_t N, int32_t H, float scale, void* dq, void* dk, void* dv, float* delta,
+                        int32_t N, int32_t H, int32_t win, float scale, void* dq, void* dk, void* dv, float* delta,
                         hipStream_t stream) {
   using G = Geo<BF, D>;
   if (N == 0) return hipSuccess;
@@ -282,22 +293,22 @@ hipError_t bwd_dispatch(const void* dout, const void* q, const void* k, const vo
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (!BF && items32 != nullptr && (D == 32 || D == 64)) {
-    e = launch_bwd_dkdv_f32_wave(D, dout, q, k, v, lse, delta, cu, items32, B, N, H, scale, dk, dv, stream);
+    e = launch_bwd_dkdv_f32_wave(D, dout, q, k, v, lse, delta, cu, items32, B, N, H, win, scale, dk, dv, stream);
     if (e != hipSuccess) return e;
-    return launch_bwd_dq_f32_wave(D, dout, q, k, v, lse, delta, cu, items32, B, N, H, scale, dq, stream);
+    return launch_bwd_dq_f32_wave(D, dout, q, k, v, lse, delta, cu, items32, B, N, H, win, scale, dq, stream);
   }
   const int T = (N + kAttnTileRows - 1) / kAttnTileRows;
   const unsigned blocks = static_cast<unsigned>(static_cast<int64_t>(T) * H);
   const float c = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
   hipEvent_t ev_bwd_dkdv = timing_start(stream);
   hipLaunchKernelGGL((bwd_dkdv_kernel<BF, D>), dim3(blocks), dim3(kThreads), 0, stream, dout, q, k, v, lse, delta,
-                   cu, items, B, N, H, T, c, scale, dk, dv);
+                   cu, items, B, N, H, T, win, c, scale, dk, dv);
   timing_stop("bwd_dkdv", ev_bwd_dkdv, stream);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipEvent_t ev_bwd_dq = timing_start(stream);
   hipLaunchKernelGGL((bwd_dq_kernel<BF, D>), dim3(blocks), dim3(kThreads), 0, stream, dout, q, k, v, lse, delta,
-                   cu, items, B, N, H, T, c, scale, dq);
+                   cu, items, B, N, H, T, win, c, scale, dq);
   timing_stop("bwd_dq", ev_bwd_dq, stream);
   return hipGetLastError();
 }
@@ -306,13 +317,13 @@ hipError_t bwd_dispatch(const void* dout, const void* q, const void* k, const vo
 
 hipError_t launch_attn_bwd(bool bf16, int D, const void* dout, const void* q, const void* k, const void* v,
                            const void* out, const float* lse, const int32_t* cu, const int32_t* items,
-                           const int32_t* items32, int32_t B, int32_t N, int32_t H, float scale, void* dq, void* dk,
-                           void* dv, float* delta, hipStream_t stream) {
+                           const int32_t* items32, int32_t B, int32_t N, int32_t H, int32_t win, float scale,
+                           void* dq, void* dk, void* dv, float* delta, hipStream_t stream) {
 #define PE_BWD_CASE(DD)                                                                                    \
   case DD:                                                                                                \
-    return bf16 ? bwd_dispatch<true, DD>(dout, q, k, v, out, lse, cu, items, items32, B, N, H, scale, dq, dk, dv,  \
+    return bf16 ? bwd_dispatch<true, DD>(dout, q, k, v, out, lse, cu, items, items32, B, N, H, win, scale, dq, dk, dv, \
                                          delta, stream)                                                   \
-                : bwd_dispatch<false, DD>(dout, q, k, v, out, lse, cu, items, items32, B, N, H, scale, dq, dk, dv, \
+                : bwd_dispatch<false, DD>(dout, q, k, v, out, lse, cu, items, items32, B, N, H, win, scale, dq, dk, dv, \
                                           delta, stream);
   switch (D) {
     PE_BWD_CASE(8)

@@ -266,6 +266,15 @@ __device__ __forceinline__ void own_range(const int32_t* cul, int ncu, int row, 
   hi_out = cul[lo + 1];
 }
 
+// Local (sliding-window) attention: narrow a row's own key range [lo, hi) to
+// the keys within distance win of the row (win < 0: global attention).
+__device__ __forceinline__ void band_limit(int row, int win, int& lo, int& hi) {
+  if (win >= 0) {
+    lo = max(lo, row - win);
+    hi = min(hi, row + win + 1);
+  }
+}
+
 // Set entries of a 32x32 score block outside [lo, hi) (row index relative to
 // the block's first row, per register) to -inf.
 __device__ __forceinline__ void mask_block(floatx16& s, int lo, int hi) {

@@ -61,7 +61,7 @@ template <int D>
 __global__ __launch_bounds__(64, 2) void attn_fwd_f32_kernel(
     const float* __restrict__ qp, const float* __restrict__ kp, const float* __restrict__ vp,
     const int32_t* __restrict__ cu, const int32_t* __restrict__ items, int32_t B, int32_t N, int32_t H, int32_t T,
-    float c, float* __restrict__ op, float* __restrict__ lse) {
+    int32_t win, float c, float* __restrict__ op, float* __restrict__ lse) {
   using O = F32Ops<D>;
   __shared__ int32_t cul[kRows + 2];
   const int lin = xcd_remap(blockIdx.x, gridDim.x);
@@ -79,7 +79,10 @@ __global__ __launch_bounds__(64, 2) void attn_fwd_f32_kernel(
   const int qrow = r0 + ql;
   const bool qvalid = qrow < rend;
   int qk0 = 0, qk1 = 0;
-  if (qvalid) own_range(cul, ncu, qrow, qk0, qk1);
+  if (qvalid) {
+    own_range(cul, ncu, qrow, qk0, qk1);
+    band_limit(qrow, win, qk0, qk1);
+  }
   const int wk0 = wave_min_i(qvalid ? qk0 : INT_MAX);
   const int wk1 = wave_max_i(qvalid ? qk1 : INT_MIN);
   const int mk0 = wave_max_i(qvalid ? qk0 : INT_MIN);
@@ -162,7 +165,8 @@ __global__ __launch_bounds__(64, 2) void attn_fwd_f32_kernel(
 
 template <int D>
 hipError_t dispatch(const void* q, const void* k, const void* v, const int32_t* cu, const int32_t* items,
-                    int32_t B, int32_t N, int32_t H, float scale, void* out, float* lse, hipStream_t stream) {
+                    int32_t B, int32_t N, int32_t H, int32_t win, float scale, void* out, float* lse,
+                    hipStream_t stream) {
   const int T = (N + kRows - 1) / kRows;
   const int64_t blocks = static_cast<int64_t>(T) * H;
   if (blocks == 0) return hipSuccess;
@@ -170,7 +174,7 @@ hipError_t dispatch(const void* q, const void* k, const void* v, const int32_t* 
   hipEvent_t ev = timing_start(stream);
   hipLaunchKernelGGL((attn_fwd_f32_kernel<D>), dim3(static_cast<unsigned>(blocks)), dim3(64), 0, stream,
                      static_cast<const float*>(q), static_cast<const float*>(k), static_cast<const float*>(v), cu,
-                     items, B, N, H, T, c, static_cast<float*>(out), lse);
+                     items, B, N, H, T, win, c, static_cast<float*>(out), lse);
   timing_stop("attn_fwd", ev, stream);
   return hipGetLastError();
 }
@@ -180,11 +184,11 @@ hipError_t dispatch(const void* q, const void* k, const void* v, const int32_t* 
 bool attn_fwd_f32_wave_supported(int D) { return D == 32 || D == 64; }
 
 hipError_t launch_attn_fwd_f32_wave(int D, const void* q, const void* k, const void* v, const int32_t* cu,
-                                    const int32_t* items32, int32_t B, int32_t N, int32_t H, float scale, void* out,
-                                    float* lse, hipStream_t stream) {
+                                    const int32_t* items32, int32_t B, int32_t N, int32_t H, int32_t win, float scale,
+                                    void* out, float* lse, hipStream_t stream) {
   switch (D) {
-    case 32: return dispatch<32>(q, k, v, cu, items32, B, N, H, scale, out, lse, stream);
-    case 64: return dispatch<64>(q, k, v, cu, items32, B, N, H, scale, out, lse, stream);
+    case 32: return dispatch<32>(q, k, v, cu, items32, B, N, H, win, scale, out, lse, stream);
+    case 64: return dispatch<64>(q, k, v, cu, items32, B, N, H, win, scale, out, lse, stream);
     default: return hipErrorInvalidValue;
   }
 }
@@ -233,7 +237,7 @@ __global__ __launch_bounds__(64, 2) void bwd_dq_f32_kernel(
     const float* __restrict__ dop, const float* __restrict__ qp, const float* __restrict__ kp,
     const float* __restrict__ vp, const float* __restrict__ lse, const float* __restrict__ delta,
     const int32_t* __restrict__ cu, const int32_t* __restrict__ items, int32_t B, int32_t N, int32_t H, int32_t T,
-    float c, float scale, float* __restrict__ dqp) {
+    int32_t win, float c, float scale, float* __restrict__ dqp) {
   constexpr int HALF = D / 2, DB = D / 32;
   __shared__ int32_t cul[kRows + 2];
   const int lin = xcd_remap(blockIdx.x, gridDim.x);
@@ -250,7 +254,10 @@ __global__ __launch_bounds__(64, 2) void bwd_dq_f32_kernel(
   const int qrow = r0 + ql;
   const bool qvalid = qrow < rend;
   int qk0 = 0, qk1 = 0;
-  if (qvalid) own_range(cul, ncu, qrow, qk0, qk1);
+  if (qvalid) {
+    own_range(cul, ncu, qrow, qk0, qk1);
+    band_limit(qrow, win, qk0, qk1);
+  }
   const int wk0 = wave_min_i(qvalid ? qk0 : INT_MAX);
   const int wk1 = wave_max_i(qvalid ? qk1 : INT_MIN);
   const int mk0 = wave_max_i(qvalid ? qk0 : INT_MIN);
@@ -315,7 +322,8 @@ __global__ __launch_bounds__(64, 2) void bwd_dq_f32_kernel(
 
 hipError_t launch_bwd_dq_f32_wave(int D, const void* dout, const void* q, const void* k, const void* v,
                                   const float* lse, const float* delta, const int32_t* cu, const int32_t* items32,
-                                  int32_t B, int32_t N, int32_t H, float scale, void* dq, hipStream_t stream) {
+                                  int32_t B, int32_t N, int32_t H, int32_t win, float scale, void* dq,
+                                  hipStream_t stream) {
   const int T = (N + kRows - 1) / kRows;
   const int64_t blocks = static_cast<int64_t>(T) * H;
   if (blocks == 0) return hipSuccess;
@@ -325,11 +333,11 @@ hipError_t launch_bwd_dq_f32_wave(int D, const void* dout, const void* q, const 
   if (D == 32)
     hipLaunchKernelGGL((bwd_dq_f32_kernel<32>), gd, bd, 0, stream, static_cast<const float*>(dout),
                        static_cast<const float*>(q), static_cast<const float*>(k), static_cast<const float*>(v), lse,
-                       delta, cu, items32, B, N, H, T, c, scale, static_cast<float*>(dq));
+                       delta, cu, items32, B, N, H, T, win, c, scale, static_cast<float*>(dq));
   else if (D == 64)
     hipLaunchKernelGGL((bwd_dq_f32_kernel<64>), gd, bd, 0, stream, static_cast<const float*>(dout),
                        static_cast<const float*>(q), static_cast<const float*>(k), static_cast<const float*>(v), lse,
-                       delta, cu, items32, B, N, H, T, c, scale, static_cast<float*>(dq));
+                       delta, cu, items32, B, N, H, T, win, c, scale, static_cast<float*>(dq));
   else
     return hipErrorInvalidValue;
   timing_stop("bwd_dq", ev, stream);
@@ -354,7 +362,7 @@ __global__ __launch_bounds__(64, D > 32 ? 1 : 2) void bwd_dkdv_f32_kernel(
     const float* __restrict__ dop, const float* __restrict__ qp, const float* __restrict__ kp,
     const float* __restrict__ vp, const float* __restrict__ lse, const float* __restrict__ delta,
     const int32_t* __restrict__ cu, const int32_t* __restrict__ items, int32_t B, int32_t N, int32_t H, int32_t T,
-    float c, float scale, float* __restrict__ dkp, float* __restrict__ dvp) {
+    int32_t win, float c, float scale, float* __restrict__ dkp, float* __restrict__ dvp) {
   constexpr int HALF = D / 2, DB = D / 32;
   __shared__ int32_t cul[kRows + 2];
   __shared__ __align__(16) float stat[2][kRows];
@@ -372,7 +380,10 @@ __global__ __launch_bounds__(64, D > 32 ? 1 : 2) void bwd_dkdv_f32_kernel(
   const int krow = r0 + ql;
   const bool kvalid = krow < rend;
   int kq0 = 0, kq1 = 0;
-  if (kvalid) own_range(cul, ncu, krow, kq0, kq1);
+  if (kvalid) {  // the queries that attend to this key
+    own_range(cul, ncu, krow, kq0, kq1);
+    band_limit(krow, win, kq0, kq1);
+  }
   const int wq0 = wave_min_i(kvalid ? kq0 : INT_MAX);
   const int wq1 = wave_max_i(kvalid ? kq1 : INT_MIN);
   const int mq0 = wave_max_i(kvalid ? kq0 : INT_MIN);
@@ -450,7 +461,7 @@ __global__ __launch_bounds__(64, D > 32 ? 1 : 2) void bwd_dkdv_f32_kernel(
 
 hipError_t launch_bwd_dkdv_f32_wave(int D, const void* dout, const void* q, const void* k, const void* v,
                                     const float* lse, const float* delta, const int32_t* cu, const int32_t* items32,
-                                    int32_t B, int32_t N, int32_t H, float scale, void* dk, void* dv,
+                                    int32_t B, int32_t N, int32_t H, int32_t win, float scale, void* dk, void* dv,
                                     hipStream_t stream) {
   const int T = (N + kRows - 1) / kRows;
   const int64_t blocks = static_cast<int64_t>(T) * H;
@@ -461,11 +472,11 @@ hipError_t launch_bwd_dkdv_f32_wave(int D, const void* dout, const void* q, cons
   if (D == 32)
     hipLaunchKernelGGL((bwd_dkdv_f32_kernel<32>), gd, bd, 0, stream, static_cast<const float*>(dout),
                        static_cast<const float*>(q), static_cast<const float*>(k), static_cast<const float*>(v), lse,
-                       delta, cu, items32, B, N, H, T, c, scale, static_cast<float*>(dk), static_cast<float*>(dv));
+                       delta, cu, items32, B, N, H, T, win, c, scale, static_cast<float*>(dk), static_cast<float*>(dv));
   else if (D == 64)
     hipLaunchKernelGGL((bwd_dkdv_f32_kernel<64>), gd, bd, 0, stream, static_cast<const float*>(dout),
                        static_cast<const float*>(q), static_cast<const float*>(k), static_cast<const float*>(v), lse,
-                       delta, cu, items32, B, N, H, T, c, scale, static_cast<float*>(dk), static_cast<float*>(dv));
+                       delta, cu, items32, B, N, H, T, win, c, scale, static_cast<float*>(dk), static_cast<float*>(dv));
   else
     return hipErrorInvalidValue;
   timing_stop("bwd_dkdv", ev, stream);

@@ -26,7 +26,7 @@ template <bool BF, int D>
 __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
     const void* __restrict__ qp, const void* __restrict__ kp, const void* __restrict__ vp,
     const int32_t* __restrict__ cu, const int32_t* __restrict__ items, int32_t B, int32_t N,
-    int32_t H, int32_t T, float c, void* __restrict__ op, float* __restrict__ lse) {
+    int32_t H, int32_t T, int32_t win, float c, void* __restrict__ op, float* __restrict__ lse) {
   using G = Geo<BF, D>;
   using E = typename G::E;
   // bf16 tiles with whole 16-byte chunks per lane half use the XOR-swizzled layout
@@ -48,7 +48,10 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
   const int qrow = sp.r0 + wv * 32 + ql;
   const bool qvalid = qrow < sp.rend;
   int qk0 = 0, qk1 = 0;
-  if (qvalid) own_range(cul, sp.ncu, qrow, qk0, qk1);
+  if (qvalid) {
+    own_range(cul, sp.ncu, qrow, qk0, qk1);
+    band_limit(qrow, win, qk0, qk1);
+  }
   const int wk0 = wave_min_i(qvalid ? qk0 : INT_MAX);  // keys any row of the wave needs
   const int wk1 = wave_max_i(qvalid ? qk1 : INT_MIN);
   const int mk0 = wave_max_i(qvalid ? qk0 : INT_MIN);  // keys every row of the wave needs
@@ -63,12 +66,15 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
   for (int db = 0; db < G::DB; ++db) o[db] = floatx16{};
   float m = kNegBig, l = 0.f;
 
+  // keys of the tile: those of its sequences, and within win of its rows for local attention
+  const int klo = win >= 0 ? max(sp.lo, sp.r0 - win) : sp.lo;
+  const int khi = win >= 0 ? min(sp.hi, sp.rend + win) : sp.hi;
   int buf = 0;
-  if (sp.lo < sp.hi) {
-    tile_gload<BF, D>(kp, sp.lo, sp.hi, H, h, kr);
-    tile_gload<BF, D>(vp, sp.lo, sp.hi, H, h, vr);
+  if (klo < khi) {
+    tile_gload<BF, D>(kp, klo, khi, H, h, kr);
+    tile_gload<BF, D>(vp, klo, khi, H, h, vr);
   }
-  for (int kb = sp.lo; kb < sp.hi; kb += kBlk) {
+  for (int kb = klo; kb < khi; kb += kBlk) {
     if constexpr (SWZ) {
       tile_store_swz<D>(kt[buf], kr);
       tile_store_swz<D>(vt[buf], vr);
@@ -77,9 +83,9 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
       tile_store<BF, D>(vt[buf], vr);
     }
     __syncthreads();
-    if (kb + kBlk < sp.hi) {
-      tile_gload<BF, D>(kp, kb + kBlk, sp.hi, H, h, kr);
-      tile_gload<BF, D>(vp, kb + kBlk, sp.hi, H, h, vr);
+    if (kb + kBlk < khi) {
+      tile_gload<BF, D>(kp, kb + kBlk, khi, H, h, kr);
+      tile_gload<BF, D>(vp, kb + kBlk, khi, H, h, vr);
     }
     if (kb < wk1 && kb + kBlk > wk0) {
       floatx16 s[2];
@@ -270,7 +276,7 @@ __global__ __launch_bounds__(kFirstThreads) void attn_fwd_first_kernel(
 
 template <bool BF, int D>
 hipError_t fwd_dispatch(const void* q, const void* k, const void* v, const int32_t* cu,
-                        const int32_t* items, int32_t B, int32_t N, int32_t H, float scale, void* out,
+                        const int32_t* items, int32_t B, int32_t N, int32_t H, int32_t win, float scale, void* out,
                         float* lse, hipStream_t stream) {
   const int T = (N + kAttnTileRows - 1) / kAttnTileRows;
   const int64_t blocks = static_cast<int64_t>(T) * H;
@@ -278,7 +284,7 @@ hipError_t fwd_dispatch(const void* q, const void* k, const void* v, const int32
   const float c = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
   hipEvent_t ev_attn_fwd = timing_start(stream);
   hipLaunchKernelGGL((attn_fwd_kernel<BF, D>), dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0, stream,
-                   q, k, v, cu, items, B, N, H, T, c, out, lse);
+                   q, k, v, cu, items, B, N, H, T, win, c, out, lse);
   timing_stop("attn_fwd", ev_attn_fwd, stream);
   return hipGetLastError();
 }
@@ -301,16 +307,17 @@ hipError_t first_dispatch(const void* q, const void* k, const void* v, const int
 
 hipError_t launch_attn_fwd(bool bf16, int D, const void* q, const void* k, const void* v,
                            const int32_t* cu, const int32_t* items, int32_t B, int32_t N, int32_t H,
-                           int32_t max_seq_len, float scale, void* out, float* lse, hipStream_t stream) {
+                           int32_t max_seq_len, int32_t win, float scale, void* out, float* lse,
+                           hipStream_t stream) {
   if (bf16 && attn_fwd_bf16_supported(D, max_seq_len)) {
     if (attn_fwd_bf16_w64_supported(D))
-      return launch_attn_fwd_bf16_w64(D, q, k, v, cu, items, B, N, H, scale, out, lse, stream);
-    return launch_attn_fwd_bf16(D, q, k, v, cu, items, B, N, H, scale, out, lse, stream);
+      return launch_attn_fwd_bf16_w64(D, q, k, v, cu, items, B, N, H, win, scale, out, lse, stream);
+    return launch_attn_fwd_bf16(D, q, k, v, cu, items, B, N, H, win, scale, out, lse, stream);
   }
 #define PE_FWD_CASE(DD)                                                                      \
   case DD:                                                                                  \
-    return bf16 ? fwd_dispatch<true, DD>(q, k, v, cu, items, B, N, H, scale, out, lse, stream) \
-                : fwd_dispatch<false, DD>(q, k, v, cu, items, B, N, H, scale, out, lse, stream);
+    return bf16 ? fwd_dispatch<true, DD>(q, k, v, cu, items, B, N, H, win, scale, out, lse, stream) \
+                : fwd_dispatch<false, DD>(q, k, v, cu, items, B, N, H, win, scale, out, lse, stream);
   switch (D) {
     PE_FWD_CASE(8)
     PE_FWD_CASE(16)

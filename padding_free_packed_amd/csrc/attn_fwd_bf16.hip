@@ -32,7 +32,7 @@ template <int D>
 __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
     const void* __restrict__ qp, const void* __restrict__ kp, const void* __restrict__ vp,
     const int32_t* __restrict__ cu, const int32_t* __restrict__ items, int32_t B, int32_t N, int32_t H,
-    int32_t T, float c, void* __restrict__ op, float* __restrict__ lse) {
+    int32_t T, int32_t win, float c, void* __restrict__ op, float* __restrict__ lse) {
   constexpr int CH = D / 8;           // 16-byte chunks per row
   constexpr int TB = kBlk * D * 2;    // bytes per tile
   constexpr int QS = D / 16;          // MFMA steps over head_dim
@@ -49,13 +49,17 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
   const int qrow = sp.r0 + wv * 32 + ql;
   const bool qvalid = qrow < sp.rend;
   int qk0 = 0, qk1 = 0;
-  if (qvalid) own_range(cul, sp.ncu, qrow, qk0, qk1);
+  if (qvalid) {
+    own_range(cul, sp.ncu, qrow, qk0, qk1);
+    band_limit(qrow, win, qk0, qk1);
+  }
   const int wk0 = wave_min_i(qvalid ? qk0 : INT_MAX);
   const int wk1 = wave_max_i(qvalid ? qk1 : INT_MIN);
   const int mk0 = wave_max_i(qvalid ? qk0 : INT_MIN);
   const int mk1 = wave_min_i(qvalid ? qk1 : INT_MAX);
-  const int klo = __builtin_amdgcn_readfirstlane(sp.lo);
-  const int khi = __builtin_amdgcn_readfirstlane(sp.hi);
+  // keys of the tile: those of its sequences, and within win of its rows for local attention
+  const int klo = __builtin_amdgcn_readfirstlane(win >= 0 ? max(sp.lo, sp.r0 - win) : sp.lo);
+  const int khi = __builtin_amdgcn_readfirstlane(win >= 0 ? min(sp.hi, sp.rend + win) : sp.hi);
 
   bf16x8 qr[QS];
   load_row_regs<true, D>(qp, (static_cast<int64_t>(qrow) * H + h) * D + g * (D / 2), qvalid, qr);
@@ -229,14 +233,15 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
 
 template <int D>
 hipError_t dispatch(const void* q, const void* k, const void* v, const int32_t* cu, const int32_t* items,
-                    int32_t B, int32_t N, int32_t H, float scale, void* out, float* lse, hipStream_t stream) {
+                    int32_t B, int32_t N, int32_t H, int32_t win, float scale, void* out, float* lse,
+                    hipStream_t stream) {
   const int T = (N + kAttnTileRows - 1) / kAttnTileRows;
   const int64_t blocks = static_cast<int64_t>(T) * H;
   if (blocks == 0) return hipSuccess;
   const float c = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
   hipEvent_t ev = timing_start(stream);
   hipLaunchKernelGGL((attn_fwd_bf16_kernel<D>), dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0, stream, q,
-                     k, v, cu, items, B, N, H, T, c, out, lse);
+                     k, v, cu, items, B, N, H, T, win, c, out, lse);
   timing_stop("attn_fwd", ev, stream);
   return hipGetLastError();
 }
@@ -251,12 +256,12 @@ bool attn_fwd_bf16_supported(int D, int max_seq_len) {
 }
 
 hipError_t launch_attn_fwd_bf16(int D, const void* q, const void* k, const void* v, const int32_t* cu,
-                                const int32_t* items, int32_t B, int32_t N, int32_t H, float scale, void* out,
-                                float* lse, hipStream_t stream) {
+                                const int32_t* items, int32_t B, int32_t N, int32_t H, int32_t win, float scale,
+                                void* out, float* lse, hipStream_t stream) {
   switch (D) {
-    case 32: return dispatch<32>(q, k, v, cu, items, B, N, H, scale, out, lse, stream);
-    case 64: return dispatch<64>(q, k, v, cu, items, B, N, H, scale, out, lse, stream);
-    case 128: return dispatch<128>(q, k, v, cu, items, B, N, H, scale, out, lse, stream);
+    case 32: return dispatch<32>(q, k, v, cu, items, B, N, H, win, scale, out, lse, stream);
+    case 64: return dispatch<64>(q, k, v, cu, items, B, N, H, win, scale, out, lse, stream);
+    case 128: return dispatch<128>(q, k, v, cu, items, B, N, H, win, scale, out, lse, stream);
     default: return hipErrorInvalidValue;
   }
 }

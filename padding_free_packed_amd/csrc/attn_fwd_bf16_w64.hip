@@ -43,7 +43,7 @@ template <int D>
 __global__ __launch_bounds__(kW64Threads) __attribute__((amdgpu_waves_per_eu(2))) void attn_fwd_bf16_w64_kernel(
     const void* __restrict__ qp, const void* __restrict__ kp, const void* __restrict__ vp,
     const int32_t* __restrict__ cu, const int32_t* __restrict__ items, int32_t B, int32_t N, int32_t H,
-    int32_t T, float c, void* __restrict__ op, float* __restrict__ lse) {
+    int32_t T, int32_t win, float c, void* __restrict__ op, float* __restrict__ lse) {
   constexpr int CH = D / 8;                    // 16-byte chunks per row
   constexpr int TB = kW64Keys * D * 2;         // bytes per tile
   constexpr int QS = D / 16;                   // MFMA steps over head_dim
@@ -65,15 +65,19 @@ __global__ __launch_bounds__(kW64Threads) __attribute__((amdgpu_waves_per_eu(2))
     qrow[qb] = sp.r0 + wv * 64 + 32 * qb + ql;
     qvalid[qb] = qrow[qb] < sp.rend;
     qk0[qb] = qk1[qb] = 0;
-    if (qvalid[qb]) own_range(cul, sp.ncu, qrow[qb], qk0[qb], qk1[qb]);
+    if (qvalid[qb]) {
+      own_range(cul, sp.ncu, qrow[qb], qk0[qb], qk1[qb]);
+      band_limit(qrow[qb], win, qk0[qb], qk1[qb]);
+    }
     // wave-uniform bounds (scalar registers, so the per-block tests are scalar branches)
     bk0[qb] = __builtin_amdgcn_readfirstlane(wave_min_i(qvalid[qb] ? qk0[qb] : INT_MAX));  // keys it needs
     bk1[qb] = __builtin_amdgcn_readfirstlane(wave_max_i(qvalid[qb] ? qk1[qb] : INT_MIN));
     mk0[qb] = __builtin_amdgcn_readfirstlane(wave_max_i(qvalid[qb] ? qk0[qb] : INT_MIN));  // every lane needs
     mk1[qb] = __builtin_amdgcn_readfirstlane(wave_min_i(qvalid[qb] ? qk1[qb] : INT_MAX));
   }
-  const int klo = __builtin_amdgcn_readfirstlane(sp.lo);
-  const int khi = __builtin_amdgcn_readfirstlane(sp.hi);
+  // keys of the tile: those of its sequences, and within win of its rows for local attention
+  const int klo = __builtin_amdgcn_readfirstlane(win >= 0 ? max(sp.lo, sp.r0 - win) : sp.lo);
+  const int khi = __builtin_amdgcn_readfirstlane(win >= 0 ? min(sp.hi, sp.rend + win) : sp.hi);
 
   bf16x8 qr[2][QS];
 #pragma unroll
@@ -246,14 +250,15 @@ __global__ __launch_bounds__(kW64Threads) __attribute__((amdgpu_waves_per_eu(2))
 
 template <int D>
 hipError_t dispatch_w64(const void* q, const void* k, const void* v, const int32_t* cu, const int32_t* items,
-                        int32_t B, int32_t N, int32_t H, float scale, void* out, float* lse, hipStream_t stream) {
+                        int32_t B, int32_t N, int32_t H, int32_t win, float scale, void* out, float* lse,
+                        hipStream_t stream) {
   const int T = (N + kAttnTileRows - 1) / kAttnTileRows;
   const int64_t blocks = static_cast<int64_t>(T) * H;
   if (blocks == 0) return hipSuccess;
   const float c = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
   hipEvent_t ev = timing_start(stream);
   hipLaunchKernelGGL((attn_fwd_bf16_w64_kernel<D>), dim3(static_cast<unsigned>(blocks)), dim3(kW64Threads), 0,
-                     stream, q, k, v, cu, items, B, N, H, T, c, out, lse);
+                     stream, q, k, v, cu, items, B, N, H, T, win, c, out, lse);
   timing_stop("attn_fwd", ev, stream);
   return hipGetLastError();
 }
@@ -263,11 +268,11 @@ hipError_t dispatch_w64(const void* q, const void* k, const void* v, const int32
 bool attn_fwd_bf16_w64_supported(int D) { return D == 32 || D == 64; }
 
 hipError_t launch_attn_fwd_bf16_w64(int D, const void* q, const void* k, const void* v, const int32_t* cu,
-                                    const int32_t* items, int32_t B, int32_t N, int32_t H, float scale, void* out,
-                                    float* lse, hipStream_t stream) {
+                                    const int32_t* items, int32_t B, int32_t N, int32_t H, int32_t win, float scale,
+                                    void* out, float* lse, hipStream_t stream) {
   switch (D) {
-    case 32: return dispatch_w64<32>(q, k, v, cu, items, B, N, H, scale, out, lse, stream);
-    case 64: return dispatch_w64<64>(q, k, v, cu, items, B, N, H, scale, out, lse, stream);
+    case 32: return dispatch_w64<32>(q, k, v, cu, items, B, N, H, win, scale, out, lse, stream);
+    case 64: return dispatch_w64<64>(q, k, v, cu, items, B, N, H, win, scale, out, lse, stream);
     default: return hipErrorInvalidValue;
   }
 }

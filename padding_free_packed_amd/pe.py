@@ -25,7 +25,8 @@ PE_FP32, PE_BF16 = 0, 1
 EXPORTS = (
     "pe_status_string", "pe_attn_tile_rows", "pe_pack_workspace_size", "pe_pack", "pe_unpack",
     "pe_worklist", "pe_attn_workspace_size", "pe_varlen_attn_fwd", "pe_varlen_attn_fwd_first_token",
-    "pe_varlen_attn_bwd", "pe_timing_enable", "pe_timing_read",
+    "pe_varlen_attn_bwd", "pe_varlen_attn_fwd_local", "pe_varlen_attn_bwd_local", "pe_timing_enable",
+    "pe_timing_read",
 )
 
 
@@ -56,6 +57,10 @@ def _load():
                                                            F, P, P, P]),
         "pe_varlen_attn_bwd": (ctypes.c_int, [P, P, P, P, P, P, P, I32, I64, I32, I32, I32, ctypes.c_int, F,
                                                P, P, P, P, SZ, P]),
+        "pe_varlen_attn_fwd_local": (ctypes.c_int, [P, P, P, P, I32, I64, I32, I32, I32, ctypes.c_int, F, I32,
+                                                     P, P, P, SZ, P]),
+        "pe_varlen_attn_bwd_local": (ctypes.c_int, [P, P, P, P, P, P, P, I32, I64, I32, I32, I32, ctypes.c_int,
+                                                     F, I32, P, P, P, P, SZ, P]),
         "pe_timing_enable": (ctypes.c_int, [ctypes.c_int]),
         "pe_timing_read": (ctypes.c_int, [P, P, ctypes.c_int]),
     }
@@ -164,6 +169,25 @@ def pe_varlen_attn_bwd(dout, q, k, v, out, lse, cu_seqlens, num_seqs, total_toke
                                  _dtype_code(q), softmax_scale, _ptr(dq), _ptr(dk), _ptr(dv),
                                  _ptr(workspace), workspace.numel(), _stream())
     _check("pe_varlen_attn_bwd", st)
+
+
+def pe_varlen_attn_fwd_local(q, k, v, cu_seqlens, num_seqs, total_tokens, max_seq_len, softmax_scale, window,
+                             out, lse, workspace):
+    N, H, d = q.shape
+    st = _lib.pe_varlen_attn_fwd_local(_ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens), num_seqs, total_tokens,
+                                       max_seq_len, H, d, _dtype_code(q), softmax_scale, window, _ptr(out),
+                                       _ptr(lse), _ptr(workspace), workspace.numel(), _stream())
+    _check("pe_varlen_attn_fwd_local", st)
+
+
+def pe_varlen_attn_bwd_local(dout, q, k, v, out, lse, cu_seqlens, num_seqs, total_tokens, max_seq_len,
+                             softmax_scale, window, dq, dk, dv, workspace):
+    N, H, d = q.shape
+    st = _lib.pe_varlen_attn_bwd_local(_ptr(dout), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse),
+                                       _ptr(cu_seqlens), num_seqs, total_tokens, max_seq_len, H, d,
+                                       _dtype_code(q), softmax_scale, window, _ptr(dq), _ptr(dk), _ptr(dv),
+                                       _ptr(workspace), workspace.numel(), _stream())
+    _check("pe_varlen_attn_bwd_local", st)
 
 
 # ------------------------------------------------------------------ kernel timing

@@ -27,7 +27,7 @@ def _header_functions():
 
 def test_header_symbols_exported():
     names = _header_functions()
-    assert len(names) == 12
+    assert len(names) == 14
     for n in names:
         assert hasattr(lib, n), n
     assert sorted(pe.EXPORTS) == names
@@ -90,6 +90,27 @@ def test_first_token_rejects():
     assert f(P, P, P, P, 4, 100, 64, 2, 24, 0, 0.125, P, NUL, None) == pe.PE_ERR_UNSUPPORTED
     assert f(P, P, P, P, 4, 100, 64, 2, 64, 0, -1.0, P, NUL, None) == pe.PE_ERR_ARG
     assert f(P, P, P, P, 4, 100, 64, 2, 64, 0, 0.125, P, MIS, None) == pe.PE_ERR_ARG
+
+
+def test_local_rejects():
+    f = lib.pe_varlen_attn_fwd_local
+    ok = [P, P, P, P, 4, 100, 64, 2, 64, 0, 0.125, 32, P, NUL, P, 1 << 20, None]
+    a = list(ok); a[11] = -1                     # a negative radius
+    assert f(*a) == pe.PE_ERR_ARG
+    a = list(ok); a[0] = NUL
+    assert f(*a) == pe.PE_ERR_NULL
+    a = list(ok); a[8] = 12
+    assert f(*a) == pe.PE_ERR_UNSUPPORTED
+    a = list(ok); a[15] = 8
+    assert f(*a) == pe.PE_ERR_WORKSPACE
+    b = lib.pe_varlen_attn_bwd_local
+    okb = [P, P, P, P, P, P, P, 4, 100, 64, 2, 64, 0, 0.125, 32, P, P, P, P, 1 << 20, None]
+    a = list(okb); a[14] = -5
+    assert b(*a) == pe.PE_ERR_ARG
+    a = list(okb); a[5] = NUL
+    assert b(*a) == pe.PE_ERR_NULL
+    a = list(okb); a[19] = 8
+    assert b(*a) == pe.PE_ERR_WORKSPACE
 
 
 def test_bwd_rejects():
