@@ -36,36 +36,58 @@ PEAK = {"bf16": 2500.0, "fp32": 157.3}   # dense MFMA TFLOP/s
 HBM_PEAK = 8000.0                        # GB/s
 
 
+def band_pairs(lengths, window):
+    """Query-key pairs a sequence keeps: L^2 (global), or those with |i - j| <= window."""
+    import numpy as np
+    L = np.asarray(lengths, dtype=np.float64)
+    if window is None:
+        return float((L * L).sum())
+    m = np.minimum(float(window), L - 1)
+    return float((L + 2.0 * (m * L - m * (m + 1) / 2.0)).sum())
+
+
 def algo_work(kernel, w, N, L2, e, with_lse):
-    """Algorithmic work of one launch: ('flop', count) or ('byte', count)."""
+    """Algorithmic work of one launch: {'flop': count, 'byte': count} (attention kernels
+    carry both). L2 is the number of attended (query, key) pairs: sum L^2, or the
+    band's for local attention."""
     B, S, H, d = w.num_seqs, w.max_seq_len, w.num_heads, w.head_dim
     D = H * d
     T = (N + 127) // 128
+    lse_b = 4.0 * N * H if with_lse else 0.0
     return {
-        # forward: 4 sum(L^2) H d flops (QK^T and PV)
-        "attn_fwd": ("flop", 4.0 * L2 * H * d),
-        # backward split by kernel: dK/dV performs S, dP, dV and dK (8 sum L^2 H d),
-        # dQ performs dQ (2 sum L^2 H d); its recomputation of S and dP is not counted
-        "bwd_dkdv": ("flop", 8.0 * L2 * H * d),
-        "bwd_dq": ("flop", 2.0 * L2 * H * d),
+        # forward: 4 L2 H d flops (QK^T and PV); read Q, K, V, write O (+ LSE)
+        "attn_fwd": {"flop": 4.0 * L2 * H * d, "byte": 4.0 * N * D * e + lse_b},
+        # backward split by kernel: dK/dV performs S, dP, dV and dK (8 L2 H d) and moves
+        # Q, K, V, dO, LSE, D in and dK, dV out; dQ is credited with dQ alone (2 L2 H d),
+        # its recomputation of S and dP is not counted
+        "bwd_dkdv": {"flop": 8.0 * L2 * H * d, "byte": 6.0 * N * D * e + 8.0 * N * H},
+        "bwd_dq": {"flop": 2.0 * L2 * H * d, "byte": 5.0 * N * D * e + 8.0 * N * H},
         # first token: read K and V once, the B queries, write B outputs (+ LSE)
-        "attn_fwd_first": ("byte", 2.0 * N * D * e + 2.0 * B * D * e + (4.0 * B * H if with_lse else 0.0)),
-        "bwd_delta": ("byte", 2.0 * N * D * e + 4.0 * N * H),
+        "attn_fwd_first": {"byte": 2.0 * N * D * e + 2.0 * B * D * e + (4.0 * B * H if with_lse else 0.0)},
+        "bwd_delta": {"byte": 2.0 * N * D * e + 4.0 * N * H},
         # pack: read and write the real rows, write flat_index
-        "pack_rows": ("byte", 2.0 * N * D * e + 8.0 * N),
+        "pack_rows": {"byte": 2.0 * N * D * e + 8.0 * N},
         # unpack: read the real rows, write the whole grid
-        "unpack_rows": ("byte", 1.0 * N * D * e + 1.0 * B * S * D * e),
-        "scan": ("byte", 4.0 * B + 4.0 * (B + 1)),
-        "worklist": ("byte", 4.0 * (B + 1) + 4.0 * (T + 1)),
+        "unpack_rows": {"byte": 1.0 * N * D * e + 1.0 * B * S * D * e},
+        "scan": {"byte": 4.0 * B + 4.0 * (B + 1)},
+        "worklist": {"byte": 4.0 * (B + 1) + 4.0 * (T + 1)},
     }.get(kernel)
 
 
-def rate(kind, amount, ms, dtype):
-    if kind == "flop":
-        a = amount / (ms * 1e-3) / 1e12
-        return {"bound": "mfma", "achieved": a, "peak": PEAK[dtype], "unit": "TFLOP/s", "frac": a / PEAK[dtype]}
-    a = amount / (ms * 1e-3) / 1e9
-    return {"bound": "hbm", "achieved": a, "peak": HBM_PEAK, "unit": "GB/s", "frac": a / HBM_PEAK}
+def rate(work, ms, dtype):
+    """Roofline entry of one launch: bound by arithmetic intensity (flops per algorithmic
+    byte) against the ridge point peak / 8 TB/s; HBM-bound work is priced in bytes."""
+    peak = PEAK[dtype]
+    ridge = peak * 1e12 / (HBM_PEAK * 1e9)
+    if "flop" in work and work["flop"] >= ridge * work["byte"]:
+        a = work["flop"] / (ms * 1e-3) / 1e12
+        return {"bound": "mfma", "achieved": a, "peak": peak, "unit": "TFLOP/s", "frac": a / peak,
+                "intensity": work["flop"] / work["byte"]}
+    a = work["byte"] / (ms * 1e-3) / 1e9
+    r = {"bound": "hbm", "achieved": a, "peak": HBM_PEAK, "unit": "GB/s", "frac": a / HBM_PEAK}
+    if "flop" in work:
+        r["intensity"] = work["flop"] / work["byte"]
+    return r
 
 
 def load_traffic(kernel, workload):
@@ -82,7 +104,7 @@ def load_traffic(kernel, workload):
     return t.get("bytes_per_launch")
 
 
-def cpu_baseline(w, budget_s):
+def cpu_baseline(w, budget_s, window=None):
     """The fp64 oracle on the first m sequences of the batch (a valid packed batch itself),
     with m sized for about `budget_s` seconds, BLAS limited to one thread."""
     import numpy as np
@@ -103,10 +125,10 @@ def cpu_baseline(w, budget_s):
         cu, flat, N = oracle.layout(L, w.max_seq_len)
         if grid is not None:
             oracle.pack(grid, flat)
-        o, _ = oracle.attention(q, k, v, cu, w.scale)
+        o, _ = oracle.attention(q, k, v, cu, w.scale, window=window)
         oracle.attention_first_token(q[cu[:-1]], k, v, cu, w.scale)
         if do is not None:
-            oracle.attention_backward(do, q, k, v, cu, w.scale)
+            oracle.attention_backward(do, q, k, v, cu, w.scale, window=window)
         if grid is not None:
             oracle.unpack(o.reshape(N, -1), cu, w.max_seq_len)
         return time.perf_counter() - t0, n
@@ -129,6 +151,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="graph_transformer",
                     choices=["graph_transformer", "short_query", "long_document", "mixed_training", "tiny"])
+    ap.add_argument("--window", type=int, default=None,
+                    help="local attention: each query sees the keys within this distance in its sequence "
+                         "(pe_varlen_attn_fwd_local / _bwd_local); default global attention")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -160,7 +185,7 @@ def main():
     B, S, H, d = w.num_seqs, w.max_seq_len, w.num_heads, w.head_dim
     D = H * d
     N = w.total_tokens
-    L2 = float((w.lengths.astype(np.float64) ** 2).sum())
+    L2 = band_pairs(w.lengths, args.window)
     bf = w.dtype == W.BF16
     e = 2 if bf else 4
     code = pe.PE_BF16 if bf else pe.PE_FP32
@@ -196,10 +221,15 @@ def main():
     def step():
         n = pe.pe_pack(lengths, S, grid, cu, flat, packed, N, ws_pack, code)
         assert n == N
-        pe.pe_varlen_attn_fwd(q, k, v, cu, B, N, S, scale, out, lse, ws)
+        if args.window is None:
+            pe.pe_varlen_attn_fwd(q, k, v, cu, B, N, S, scale, out, lse, ws)
+        else:
+            pe.pe_varlen_attn_fwd_local(q, k, v, cu, B, N, S, scale, args.window, out, lse, ws)
         pe.pe_varlen_attn_fwd_first_token(q_first, k, v, cu, B, N, S, scale, out_first, lse_first)
-        if with_bwd:
+        if with_bwd and args.window is None:
             pe.pe_varlen_attn_bwd(dout, q, k, v, out, lse, cu, B, N, S, scale, dq, dk, dv, ws)
+        elif with_bwd:
+            pe.pe_varlen_attn_bwd_local(dout, q, k, v, out, lse, cu, B, N, S, scale, args.window, dq, dk, dv, ws)
         if grid is not None:
             pe.pe_unpack(out.view(N, D), cu, B, S, N, grid_out)
 
@@ -234,14 +264,14 @@ def main():
         ent = {"avg_ms": avg, "launches_per_step": launches_per_step, "ms_per_step": avg * launches_per_step}
         aw = algo_work(name, w, N, L2, e, True)
         if aw is not None and avg > 0:
-            ent.update(rate(aw[0], aw[1], avg, "bf16" if bf else "fp32"))
+            ent.update(rate(aw, avg, "bf16" if bf else "fp32"))
         breakdown[name] = ent
     dom = max(breakdown, key=lambda k_: breakdown[k_]["ms_per_step"])
-    kind, amount = algo_work(dom, w, N, L2, e, True)
-    roof = rate(kind, amount, breakdown[dom]["avg_ms"], "bf16" if bf else "fp32")
-    roof["traffic"] = load_traffic(dom, args.workload)
+    work = algo_work(dom, w, N, L2, e, True)
+    roof = rate(work, breakdown[dom]["avg_ms"], "bf16" if bf else "fp32")
+    roof["traffic"] = load_traffic(dom, args.workload if args.window is None else f"{args.workload}_w{args.window}")
     roof["kernel"] = dom
-    roof["algorithmic_per_launch"] = amount
+    roof["algorithmic_per_launch"] = work["flop"] if roof["bound"] == "mfma" else work["byte"]
 
     fwd_ms = breakdown["attn_fwd"]["avg_ms"]
     result = {
@@ -259,7 +289,7 @@ def main():
         "data": "synthetic",
         "config": {
             "workload": args.workload, "num_seqs": B, "max_seq_len": S, "total_tokens": N, "num_heads": H,
-            "head_dim": d, "grid": [B, S, D] if grid is not None else None,
+            "head_dim": d, "grid": [B, S, D] if grid is not None else None, "window": args.window,
             "step": ("pack" if grid is not None else "pack(layout only)") + "+fwd(lse)+first_token"
                     + ("+bwd" if with_bwd else "") + ("+unpack" if grid is not None else ""),
         },
@@ -279,7 +309,7 @@ def main():
         result["copy_probe_bytes"] = nbytes
         del src, dst
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)
+        result["cpu_baseline"] = cpu_baseline(w, args.cpu_budget, args.window)
     print(json.dumps(result))
 
 

@@ -22,7 +22,10 @@ gigl.nn.packed_attention" and the packed-encoders README):
   sequence i"). The result has a plain definition, so this is that definition
   written out per sequence and per head, with a matmul as a step.
 * ``attention_first_token``: one query per sequence, the sequence's first token
-  (GiGL ``packed_attention``, ``query_is_first_token``).
+  (GiGL ``packed_attention``, ``query_is_first_token``), and its backward
+  ``attention_first_token_backward``: GiGL runs the readout through the same
+  autograd-registered varlen op, with one query per sequence
+  (``cu_seqlens_q = arange(B + 1)``), so it trains through it.
 * ``attention_backward``: gradients of the same definition in Q, K and V, with no
   gradient flowing into the log-sum-exp (GiGL ``_varlen_attention_backward``
   drops the log-sum-exp's gradient). The pages give no formulas; these are the
@@ -251,6 +254,45 @@ def attention_first_token(q_first, k, v, cu_seqlens, scale: float, seqs=None, wi
             o[n, h, :] = (w @ v[c0:c1, h, :]) / l
             lse[h, n] = m + np.log(l)
     return o, lse
+
+
+def attention_first_token_backward(dout_first, q_first, k, v, cu_seqlens, scale: float, out_first=None,
+                                   lse_first=None):
+    """Gradients of ``<dout_first, attention_first_token(q_first, k, v)>`` in q_first, k and v.
+
+    The first-token readout is the full attention evaluated at rows cu[:-1] only,
+    so its backward is the full backward with every other row's output gradient
+    zero. Per sequence b and head h, with s_j = scale <q_b, k_j> over the keys j
+    of sequence b, P_j = exp(s_j - lse_b), D_b = <dO_b, O_b>:
+    dv_j = P_j dO_b; dS_j = P_j (<dO_b, v_j> - D_b); dq_b = scale sum_j dS_j k_j;
+    dk_j = scale dS_j q_b. No gradient enters through the log-sum-exp.
+
+    ``out_first`` [B, H, d] and ``lse_first`` [H, B] play the role of the forward's
+    output and log-sum-exp (this module's own float64 forward when omitted).
+    Returns dq_first float64 [B, H, d], dk and dv float64 [N, H, d].
+    """
+    _check_f64(dout_first, q_first, k, v)
+    B, H, d = q_first.shape
+    N = k.shape[0]
+    dq = np.zeros((B, H, d))
+    dk = np.zeros((N, H, d))
+    dv = np.zeros((N, H, d))
+    if out_first is None or lse_first is None:
+        o_own, l_own = attention_first_token(q_first, k, v, cu_seqlens, scale)
+        out_first = o_own if out_first is None else out_first
+        lse_first = l_own if lse_first is None else lse_first
+    out_first = np.asarray(out_first, dtype=np.float64)
+    lse_first = np.asarray(lse_first, dtype=np.float64)
+    for b, (c0, c1) in enumerate(_segments(cu_seqlens)):
+        for h in range(H):
+            qb, dob = q_first[b, h, :], dout_first[b, h, :]
+            s = scale * (k[c0:c1, h, :] @ qb)
+            p = np.exp(s - lse_first[h, b])
+            dv[c0:c1, h, :] = np.outer(p, dob)
+            ds = p * (v[c0:c1, h, :] @ dob - float(dob @ out_first[b, h, :]))
+            dq[b, h, :] = scale * (ds @ k[c0:c1, h, :])
+            dk[c0:c1, h, :] = scale * np.outer(ds, qb)
+    return dq, dk, dv
 
 
 def attention_backward(dout, q, k, v, cu_seqlens, scale: float, seqs=None, out=None, lse=None, window=None):
