@@ -6,9 +6,11 @@ is already resident in HBM:
 
     pe_pack (lengths -> cu_seqlens, flat_index, packed rows of the padded grid;
              its one host read included)
-    pe_varlen_attn_fwd (work list + forward with log-sum-exp)
+    pe_varlen_attn_fwd (work list + forward with log-sum-exp; _local with --window)
     pe_varlen_attn_fwd_first_token
-    pe_varlen_attn_bwd (when the workload carries dO)
+    pe_varlen_attn_bwd (when the workload carries dO; _local with --window)
+    pe_varlen_attn_bwd_first_token (when the workload carries dO: the readout's
+             gradient is dO at the first rows)
     pe_unpack (attention output back to the padded grid)
 
 The default workload is the graph-transformer shape: 4096 sequences of at most
@@ -46,7 +48,7 @@ def band_pairs(lengths, window):
     return float((L + 2.0 * (m * L - m * (m + 1) / 2.0)).sum())
 
 
-def algo_work(kernel, w, N, L2, e, with_lse):
+def algo_work(kernel, w, N, L2, e, with_lse, with_grid=True):
     """Algorithmic work of one launch: {'flop': count, 'byte': count} (attention kernels
     carry both). L2 is the number of attended (query, key) pairs: sum L^2, or the
     band's for local attention."""
@@ -64,9 +66,11 @@ def algo_work(kernel, w, N, L2, e, with_lse):
         "bwd_dq": {"flop": 2.0 * L2 * H * d, "byte": 5.0 * N * D * e + 8.0 * N * H},
         # first token: read K and V once, the B queries, write B outputs (+ LSE)
         "attn_fwd_first": {"byte": 2.0 * N * D * e + 2.0 * B * D * e + (4.0 * B * H if with_lse else 0.0)},
+        # first-token backward: read K, V and the B rows of q, dO, O (+ LSE), write dK, dV and dq_first
+        "attn_bwd_first": {"byte": 4.0 * N * D * e + 4.0 * B * D * e + 4.0 * B * H},
         "bwd_delta": {"byte": 2.0 * N * D * e + 4.0 * N * H},
-        # pack: read and write the real rows, write flat_index
-        "pack_rows": {"byte": 2.0 * N * D * e + 8.0 * N},
+        # pack: read and write the real rows, write flat_index (only flat_index without a grid)
+        "pack_rows": {"byte": (2.0 * N * D * e if with_grid else 0.0) + 8.0 * N},
         # unpack: read the real rows, write the whole grid
         "unpack_rows": {"byte": 1.0 * N * D * e + 1.0 * B * S * D * e},
         "scan": {"byte": 4.0 * B + 4.0 * (B + 1)},
@@ -129,6 +133,7 @@ def cpu_baseline(w, budget_s, window=None):
         oracle.attention_first_token(q[cu[:-1]], k, v, cu, w.scale)
         if do is not None:
             oracle.attention_backward(do, q, k, v, cu, w.scale, window=window)
+            oracle.attention_first_token_backward(do[cu[:-1]], q[cu[:-1]], k, v, cu, w.scale)
         if grid is not None:
             oracle.unpack(o.reshape(N, -1), cu, w.max_seq_len)
         return time.perf_counter() - t0, n
@@ -140,7 +145,7 @@ def cpu_baseline(w, budget_s, window=None):
         t, n = run(m)
     return {"value": n / t, "unit": "tokens/s", "cores": 1, "kind": "oracle",
             "sample": f"first {m} of {w.num_seqs} sequences ({n} tokens): layout, pack, forward, first-token,"
-                      f"{' backward,' if w.dout is not None else ''}{' unpack' if w.grid is not None else ''} in float64,"
+                      f"{' backward, first-token backward,' if w.dout is not None else ''}{' unpack' if w.grid is not None else ''} in float64,"
                       f" {t:.1f} s"}
 
 
@@ -214,6 +219,11 @@ def main():
     grid_out = torch.empty_like(grid) if grid is not None else None
     with_bwd = dout is not None
     dq, dk, dv = ((torch.empty_like(q) for _ in range(3)) if with_bwd else (None, None, None))
+    # the first-token readout is trained through as well: its gradient is dO at the first rows
+    first_rows = torch.from_numpy(cu_h[:-1]).to(dev)
+    dout_first = dout[first_rows].contiguous() if with_bwd else None
+    dq_first = torch.empty_like(q_first) if with_bwd else None
+    dk_first, dv_first = ((torch.empty_like(k), torch.empty_like(v)) if with_bwd else (None, None))
     ws_pack = pe.workspace(pe.pe_pack_workspace_size(B, S, D, code), dev)
     ws = pe.workspace(pe.pe_attn_workspace_size(B, N, H, d, code, with_bwd), dev)
     scale = w.scale
@@ -230,6 +240,9 @@ def main():
             pe.pe_varlen_attn_bwd(dout, q, k, v, out, lse, cu, B, N, S, scale, dq, dk, dv, ws)
         elif with_bwd:
             pe.pe_varlen_attn_bwd_local(dout, q, k, v, out, lse, cu, B, N, S, scale, args.window, dq, dk, dv, ws)
+        if with_bwd:
+            pe.pe_varlen_attn_bwd_first_token(dout_first, q_first, k, v, out_first, lse_first, cu, B, N, S, scale,
+                                              dq_first, dk_first, dv_first)
         if grid is not None:
             pe.pe_unpack(out.view(N, D), cu, B, S, N, grid_out)
 
@@ -262,12 +275,12 @@ def main():
         launches_per_step = len(lst) / args.steps
         avg = float(np.mean(lst))
         ent = {"avg_ms": avg, "launches_per_step": launches_per_step, "ms_per_step": avg * launches_per_step}
-        aw = algo_work(name, w, N, L2, e, True)
+        aw = algo_work(name, w, N, L2, e, True, grid is not None)
         if aw is not None and avg > 0:
             ent.update(rate(aw, avg, "bf16" if bf else "fp32"))
         breakdown[name] = ent
     dom = max(breakdown, key=lambda k_: breakdown[k_]["ms_per_step"])
-    work = algo_work(dom, w, N, L2, e, True)
+    work = algo_work(dom, w, N, L2, e, True, grid is not None)
     roof = rate(work, breakdown[dom]["avg_ms"], "bf16" if bf else "fp32")
     roof["traffic"] = load_traffic(dom, args.workload if args.window is None else f"{args.workload}_w{args.window}")
     roof["kernel"] = dom
@@ -291,7 +304,7 @@ def main():
             "workload": args.workload, "num_seqs": B, "max_seq_len": S, "total_tokens": N, "num_heads": H,
             "head_dim": d, "grid": [B, S, D] if grid is not None else None, "window": args.window,
             "step": ("pack" if grid is not None else "pack(layout only)") + "+fwd(lse)+first_token"
-                    + ("+bwd" if with_bwd else "") + ("+unpack" if grid is not None else ""),
+                    + ("+bwd+first_token_bwd" if with_bwd else "") + ("+unpack" if grid is not None else ""),
         },
         "fwd": {"ms": fwd_ms, "tokens_per_s": N / (fwd_ms * 1e-3),
                 "tflops": 4.0 * L2 * H * d / (fwd_ms * 1e-3) / 1e12},

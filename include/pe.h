@@ -189,6 +189,43 @@ pe_status pe_varlen_attn_fwd_first_token(const void* q_first, const void* k, con
                                          int32_t head_dim, pe_dtype dtype, float softmax_scale,
                                          void* out_first, float* lse_first, void* stream);
 
+/* pe_varlen_attn_fwd_first_row: pe_varlen_attn_fwd_first_token with the query
+ * gather fused: the query of sequence b is row cu_seqlens[b] of the packed
+ * q [total_tokens, num_heads, head_dim], which GiGL's caller otherwise gathers
+ * itself (`query[cu_seqlens[:-1]]`) before the call. Same outputs and errors.
+ */
+pe_status pe_varlen_attn_fwd_first_row(const void* q, const void* k, const void* v, const int32_t* cu_seqlens,
+                                       int32_t num_seqs, int64_t total_tokens, int32_t max_seq_len,
+                                       int32_t num_heads, int32_t head_dim, pe_dtype dtype, float softmax_scale,
+                                       void* out_first, float* lse_first, void* stream);
+
+/* pe_varlen_attn_bwd_first_token: gradients of the first-token readout.
+ *
+ * Source: GiGL `packed_attention` runs the readout through its autograd-
+ * registered varlen op with one query per sequence (cu_seqlens_q =
+ * arange(num_seqs + 1)), so training flows through it; the backward of that op
+ * (`_varlen_attention_backward`) takes the output and log-sum-exp and drops the
+ * log-sum-exp's gradient. With one query per sequence, for key row j of
+ * sequence b:
+ *
+ *   P_j = exp(s_j - lse_b)   D_b = <dout_b, out_b>   dS_j = P_j (<dout_b, v_j> - D_b)
+ *   dv_j = P_j dout_b        dk_j = scale dS_j q_b   dq_b = scale sum_j dS_j k_j
+ *
+ * Arguments
+ *   dout_first, q_first, out_first, dq_first   device [num_seqs, num_heads, head_dim] of `dtype`
+ *   lse_first                                   device fp32 [num_heads, num_seqs] (required)
+ *   k, v, dk, dv                                device [total_tokens, num_heads, head_dim] of `dtype`;
+ *                                               every row of dk and dv is written
+ * For pe_varlen_attn_fwd_first_row the gradient of the packed q is dq_first
+ * placed at rows cu_seqlens[:-1] and zero elsewhere. No workspace;
+ * asynchronous; deterministic (every output element has one writer).
+ */
+pe_status pe_varlen_attn_bwd_first_token(const void* dout_first, const void* q_first, const void* k, const void* v,
+                                         const void* out_first, const float* lse_first, const int32_t* cu_seqlens,
+                                         int32_t num_seqs, int64_t total_tokens, int32_t max_seq_len,
+                                         int32_t num_heads, int32_t head_dim, pe_dtype dtype, float softmax_scale,
+                                         void* dq_first, void* dk, void* dv, void* stream);
+
 /* ------------------------------------------------------------------ backward
  * pe_varlen_attn_bwd: gradients of pe_varlen_attn_fwd in q, k and v.
  *

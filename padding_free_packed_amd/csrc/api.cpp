@@ -217,21 +217,63 @@ pe_status pe_varlen_attn_fwd_local(const void* q, const void* k, const void* v, 
                   softmax_scale, effective_window(window, max_seq_len), out, lse, workspace, workspace_bytes, stream);
 }
 
+}  // extern "C"
+
+namespace {
+
+pe_status first_impl(const void* q, int32_t gather, const void* k, const void* v, const int32_t* cu_seqlens,
+                     int32_t num_seqs, int64_t total_tokens, int32_t max_seq_len, int32_t num_heads, int32_t head_dim,
+                     pe_dtype dtype, float softmax_scale, void* out_first, float* lse_first, void* stream) {
+  if (!q || !k || !v || !cu_seqlens || !out_first) return PE_ERR_NULL;
+  const pe_status s =
+      check_attn_args(num_seqs, total_tokens, max_seq_len, num_heads, head_dim, dtype, softmax_scale);
+  if (s != PE_OK) return s;
+  for (const void* p : {q, k, v, static_cast<const void*>(cu_seqlens), static_cast<const void*>(out_first),
+                        static_cast<const void*>(lse_first)})
+    if (p && !aligned16(p)) return PE_ERR_ARG;
+  return hip_status(pe::launch_attn_fwd_first(dtype == PE_BF16, head_dim, q, k, v, cu_seqlens, num_seqs,
+                                              static_cast<int32_t>(total_tokens), num_heads, gather, softmax_scale,
+                                              out_first, lse_first, as_stream(stream)));
+}
+
+}  // namespace
+
+extern "C" {
+
 pe_status pe_varlen_attn_fwd_first_token(const void* q_first, const void* k, const void* v,
                                          const int32_t* cu_seqlens, int32_t num_seqs, int64_t total_tokens,
                                          int32_t max_seq_len, int32_t num_heads, int32_t head_dim,
                                          pe_dtype dtype, float softmax_scale, void* out_first, float* lse_first,
                                          void* stream) {
-  if (!q_first || !k || !v || !cu_seqlens || !out_first) return PE_ERR_NULL;
+  return first_impl(q_first, 0, k, v, cu_seqlens, num_seqs, total_tokens, max_seq_len, num_heads, head_dim, dtype,
+                    softmax_scale, out_first, lse_first, stream);
+}
+
+pe_status pe_varlen_attn_fwd_first_row(const void* q, const void* k, const void* v, const int32_t* cu_seqlens,
+                                       int32_t num_seqs, int64_t total_tokens, int32_t max_seq_len,
+                                       int32_t num_heads, int32_t head_dim, pe_dtype dtype, float softmax_scale,
+                                       void* out_first, float* lse_first, void* stream) {
+  return first_impl(q, 1, k, v, cu_seqlens, num_seqs, total_tokens, max_seq_len, num_heads, head_dim, dtype,
+                    softmax_scale, out_first, lse_first, stream);
+}
+
+pe_status pe_varlen_attn_bwd_first_token(const void* dout_first, const void* q_first, const void* k, const void* v,
+                                         const void* out_first, const float* lse_first, const int32_t* cu_seqlens,
+                                         int32_t num_seqs, int64_t total_tokens, int32_t max_seq_len,
+                                         int32_t num_heads, int32_t head_dim, pe_dtype dtype, float softmax_scale,
+                                         void* dq_first, void* dk, void* dv, void* stream) {
+  if (!dout_first || !q_first || !k || !v || !out_first || !lse_first || !cu_seqlens || !dq_first || !dk || !dv)
+    return PE_ERR_NULL;
   const pe_status s =
       check_attn_args(num_seqs, total_tokens, max_seq_len, num_heads, head_dim, dtype, softmax_scale);
   if (s != PE_OK) return s;
-  for (const void* p : {q_first, k, v, static_cast<const void*>(cu_seqlens), static_cast<const void*>(out_first),
-                        static_cast<const void*>(lse_first)})
-    if (p && !aligned16(p)) return PE_ERR_ARG;
-  return hip_status(pe::launch_attn_fwd_first(dtype == PE_BF16, head_dim, q_first, k, v, cu_seqlens, num_seqs,
-                                              static_cast<int32_t>(total_tokens), num_heads, softmax_scale,
-                                              out_first, lse_first, as_stream(stream)));
+  for (const void* p : {dout_first, q_first, k, v, out_first, static_cast<const void*>(lse_first),
+                        static_cast<const void*>(cu_seqlens), static_cast<const void*>(dq_first),
+                        static_cast<const void*>(dk), static_cast<const void*>(dv)})
+    if (!aligned16(p)) return PE_ERR_ARG;
+  return hip_status(pe::launch_attn_bwd_first(dtype == PE_BF16, head_dim, dout_first, q_first, k, v, out_first,
+                                              lse_first, cu_seqlens, num_seqs, static_cast<int32_t>(total_tokens),
+                                              num_heads, softmax_scale, dq_first, dk, dv, as_stream(stream)));
 }
 
 // ------------------------------------------------------------------ backward

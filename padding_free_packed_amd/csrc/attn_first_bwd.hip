@@ -1,0 +1,188 @@
+// Backward of the first-token readout: one query per sequence (its first row),
+// so every key row j of sequence b receives gradient from that single query:
+//
+//   P_j  = exp(scale <q_b, k_j> - lse_b)        D_b = <dO_b, O_b>
+//   dS_j = P_j (<dO_b, v_j> - D_b)
+//   dk_j = scale dS_j q_b     dv_j = P_j dO_b     dq_b = scale sum_j dS_j k_j
+//
+// One pass over K and V, HBM-bound like the forward: one block per (sequence,
+// group of heads), threads laid out as [key slot][head][16-byte chunk of the
+// head row] so each K/V row of the sequence (all heads of the group) is read
+// once and each dK/dV row written once, fully coalesced. Each slot walks the
+// keys slot, slot + KS, ... in batches of four rows whose loads are issued
+// before any is used; dq partials of the slots merge through LDS at the end.
+// No atomics: every output element has exactly one writer.
+#include <type_traits>
+
+#include "attn_common.h"
+
+namespace pe {
+
+namespace {
+
+constexpr int kFbThreads = 512;
+constexpr int kFbBatch = 4;
+
+template <bool BF, int D>
+__global__ __launch_bounds__(kFbThreads) void attn_bwd_first_kernel(
+    const void* __restrict__ dof, const void* __restrict__ qf, const void* __restrict__ kp,
+    const void* __restrict__ vp, const void* __restrict__ of, const float* __restrict__ lse,
+    const int32_t* __restrict__ cu, int32_t B, int32_t N, int32_t H, int32_t HPB, float c, float scale,
+    void* __restrict__ dqp, void* __restrict__ dkp, void* __restrict__ dvp) {
+  constexpr int ES = BF ? 2 : 4;
+  constexpr int EPC = 16 / ES;  // elements per 16-byte chunk
+  constexpr int GS = D / EPC;   // chunks (threads) per head row
+  constexpr int U = kFbBatch;
+  using Chunk = typename std::conditional<BF, u16x8, float4>::type;
+  __shared__ float sq[kFbThreads * EPC];
+
+  const int b = blockIdx.x;
+  const int hg = blockIdx.y;
+  const int tid = threadIdx.x;
+  const int CPR = HPB * GS;
+  const int KS = kFbThreads / CPR;
+  const int slot = tid / CPR, cidx = tid - slot * CPR;
+  const int hl = cidx / GS, sub = cidx - hl * GS;
+  const int h = hg * HPB + hl;
+  const bool active = slot < KS && h < H;
+
+  auto widen = [](const Chunk& x, float (&y)[EPC]) __attribute__((always_inline)) {
+    if constexpr (BF) {
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) y[e] = bf16_to_f32(x[e]);
+    } else {
+      y[0] = x.x; y[1] = x.y; y[2] = x.z; y[3] = x.w;
+    }
+  };
+  auto narrow = [](const float (&y)[EPC]) __attribute__((always_inline)) {
+    Chunk x;
+    if constexpr (BF) {
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) x[e] = f32_to_bf16(y[e]);
+    } else {
+      x = make_float4(y[0], y[1], y[2], y[3]);
+    }
+    return x;
+  };
+
+  float dq[EPC];
+#pragma unroll
+  for (int e = 0; e < EPC; ++e) dq[e] = 0.f;
+  if (active) {
+    const int c0 = cu[b], c1 = cu[b + 1];
+    const int64_t hoff = static_cast<int64_t>(h) * D + sub * EPC;
+    const int64_t boff = (static_cast<int64_t>(b) * H * D + hoff) * ES;
+    float qv[EPC], dov[EPC], ov[EPC];
+    widen(*reinterpret_cast<const Chunk*>(static_cast<const char*>(qf) + boff), qv);
+    widen(*reinterpret_cast<const Chunk*>(static_cast<const char*>(dof) + boff), dov);
+    widen(*reinterpret_cast<const Chunk*>(static_cast<const char*>(of) + boff), ov);
+    float dd = 0.f;
+#pragma unroll
+    for (int e = 0; e < EPC; ++e) dd = fmaf(dov[e], ov[e], dd);
+#pragma unroll
+    for (int o = 1; o < GS; o <<= 1) dd += __shfl_xor(dd, o);
+    const float lse2 = lse[static_cast<int64_t>(h) * B + b] * kLog2e;
+    const char* kb = static_cast<const char*>(kp) + hoff * ES;
+    const char* vb = static_cast<const char*>(vp) + hoff * ES;
+    char* dkb = static_cast<char*>(dkp) + hoff * ES;
+    char* dvb = static_cast<char*>(dvp) + hoff * ES;
+    const int64_t rs = static_cast<int64_t>(H) * D * ES;  // bytes per packed row
+    for (int j0 = c0 + slot; j0 < c1; j0 += U * KS) {
+      Chunk xk[U], xv[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {  // rows past the sequence re-read its last row and are not stored
+        const int j = min(j0 + u * KS, c1 - 1);
+        xk[u] = *reinterpret_cast<const Chunk*>(kb + j * rs);
+        xv[u] = *reinterpret_cast<const Chunk*>(vb + j * rs);
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int j = j0 + u * KS;
+        float kv[EPC], vv[EPC];
+        widen(xk[u], kv);
+        widen(xv[u], vv);
+        float s = 0.f, dp = 0.f;
+#pragma unroll
+        for (int e = 0; e < EPC; ++e) {
+          s = fmaf(qv[e], kv[e], s);
+          dp = fmaf(dov[e], vv[e], dp);
+        }
+#pragma unroll
+        for (int o = 1; o < GS; o <<= 1) {
+          s += __shfl_xor(s, o);
+          dp += __shfl_xor(dp, o);
+        }
+        if (j < c1) {
+          const float p = __builtin_amdgcn_exp2f(fmaf(s, c, -lse2));
+          const float ds = p * (dp - dd);
+          float dk[EPC], dv[EPC];
+#pragma unroll
+          for (int e = 0; e < EPC; ++e) {
+            dk[e] = scale * ds * qv[e];
+            dv[e] = p * dov[e];
+            dq[e] = fmaf(ds, kv[e], dq[e]);
+          }
+          *reinterpret_cast<Chunk*>(dkb + j * rs) = narrow(dk);
+          *reinterpret_cast<Chunk*>(dvb + j * rs) = narrow(dv);
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < EPC; ++e) sq[tid * EPC + e] = dq[e];
+  __syncthreads();
+  if (slot == 0 && h < H) {
+    float acc[EPC];
+#pragma unroll
+    for (int e = 0; e < EPC; ++e) acc[e] = 0.f;
+    for (int s2 = 0; s2 < KS; ++s2) {
+      const int t2 = s2 * CPR + cidx;
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) acc[e] += sq[t2 * EPC + e];
+    }
+#pragma unroll
+    for (int e = 0; e < EPC; ++e) acc[e] *= scale;
+    const int64_t off = (static_cast<int64_t>(b) * H + h) * D + sub * EPC;
+    *reinterpret_cast<Chunk*>(static_cast<char*>(dqp) + off * ES) = narrow(acc);
+  }
+}
+
+template <bool BF, int D>
+hipError_t bwd_first_dispatch(const void* dof, const void* qf, const void* k, const void* v, const void* of,
+                              const float* lse, const int32_t* cu, int32_t B, int32_t N, int32_t H, float scale,
+                              void* dq, void* dk, void* dv, hipStream_t stream) {
+  constexpr int GS = D / (BF ? 8 : 4);
+  const int HPB = (H * GS <= kFbThreads) ? H : kFbThreads / GS;
+  const int HG = (H + HPB - 1) / HPB;
+  const float c = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
+  hipEvent_t ev = timing_start(stream);
+  hipLaunchKernelGGL((attn_bwd_first_kernel<BF, D>), dim3(B, HG), dim3(kFbThreads), 0, stream, dof, qf, k, v, of,
+                     lse, cu, B, N, H, HPB, c, scale, dq, dk, dv);
+  timing_stop("attn_bwd_first", ev, stream);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_attn_bwd_first(bool bf16, int D, const void* dout_first, const void* q_first, const void* k,
+                                 const void* v, const void* out_first, const float* lse_first, const int32_t* cu,
+                                 int32_t B, int32_t N, int32_t H, float scale, void* dq_first, void* dk, void* dv,
+                                 hipStream_t stream) {
+#define PE_BF_CASE(DD)                                                                                         \
+  case DD:                                                                                                    \
+    return bf16 ? bwd_first_dispatch<true, DD>(dout_first, q_first, k, v, out_first, lse_first, cu, B, N, H,  \
+                                               scale, dq_first, dk, dv, stream)                               \
+                : bwd_first_dispatch<false, DD>(dout_first, q_first, k, v, out_first, lse_first, cu, B, N, H, \
+                                                scale, dq_first, dk, dv, stream);
+  switch (D) {
+    PE_BF_CASE(8)
+    PE_BF_CASE(16)
+    PE_BF_CASE(32)
+    PE_BF_CASE(64)
+    PE_BF_CASE(128)
+    default: return hipErrorInvalidValue;
+  }
+#undef PE_BF_CASE
+}
+
+}  // namespace pe

@@ -162,7 +162,7 @@ constexpr int kFirstBatch = 4;
 template <bool BF, int D>
 __global__ __launch_bounds__(kFirstThreads) void attn_fwd_first_kernel(
     const void* __restrict__ qf, const void* __restrict__ kp, const void* __restrict__ vp,
-    const int32_t* __restrict__ cu, int32_t B, int32_t N, int32_t H, int32_t HPB, float c,
+    const int32_t* __restrict__ cu, int32_t B, int32_t N, int32_t H, int32_t HPB, int32_t gather, float c,
     void* __restrict__ outp, float* __restrict__ lse) {
   constexpr int ES = BF ? 2 : 4;
   constexpr int EPC = 16 / ES;       // elements per 16-byte chunk
@@ -197,8 +197,9 @@ __global__ __launch_bounds__(kFirstThreads) void attn_fwd_first_kernel(
   };
   if (active) {
     const int64_t hoff = static_cast<int64_t>(h) * D + sub * EPC;
-    widen(*reinterpret_cast<const Chunk*>(static_cast<const char*>(qf) + (static_cast<int64_t>(b) * H * D + hoff) * ES),
-          qv);
+    // the query is row b of q_first [B, H, D], or (gather) row cu[b] of the packed Q [N, H, D]
+    const int64_t qrow = gather ? c0 : b;
+    widen(*reinterpret_cast<const Chunk*>(static_cast<const char*>(qf) + (qrow * H * D + hoff) * ES), qv);
     const char* kb = static_cast<const char*>(kp) + hoff * ES;
     const char* vb = static_cast<const char*>(vp) + hoff * ES;
     const int64_t rs = static_cast<int64_t>(H) * D * ES;  // bytes per packed row
@@ -291,14 +292,15 @@ hipError_t fwd_dispatch(const void* q, const void* k, const void* v, const int32
 
 template <bool BF, int D>
 hipError_t first_dispatch(const void* q, const void* k, const void* v, const int32_t* cu, int32_t B,
-                          int32_t N, int32_t H, float scale, void* out, float* lse, hipStream_t stream) {
+                          int32_t N, int32_t H, int32_t gather, float scale, void* out, float* lse,
+                          hipStream_t stream) {
   constexpr int GS = D / (BF ? 8 : 4);
   const int HPB = (H * GS <= kFirstThreads) ? H : kFirstThreads / GS;
   const int HG = (H + HPB - 1) / HPB;
   const float c = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
   hipEvent_t ev_attn_fwd_first = timing_start(stream);
   hipLaunchKernelGGL((attn_fwd_first_kernel<BF, D>), dim3(B, HG), dim3(kFirstThreads), 0, stream, q, k, v, cu, B,
-                   N, H, HPB, c, out, lse);
+                   N, H, HPB, gather, c, out, lse);
   timing_stop("attn_fwd_first", ev_attn_fwd_first, stream);
   return hipGetLastError();
 }
@@ -330,12 +332,14 @@ hipError_t launch_attn_fwd(bool bf16, int D, const void* q, const void* k, const
 }
 
 hipError_t launch_attn_fwd_first(bool bf16, int D, const void* q_first, const void* k, const void* v,
-                                 const int32_t* cu, int32_t B, int32_t N, int32_t H, float scale,
+                                 const int32_t* cu, int32_t B, int32_t N, int32_t H, int32_t gather, float scale,
                                  void* out_first, float* lse_first, hipStream_t stream) {
 #define PE_FIRST_CASE(DD)                                                                          \
   case DD:                                                                                        \
-    return bf16 ? first_dispatch<true, DD>(q_first, k, v, cu, B, N, H, scale, out_first, lse_first, stream) \
-                : first_dispatch<false, DD>(q_first, k, v, cu, B, N, H, scale, out_first, lse_first, stream);
+    return bf16 ? first_dispatch<true, DD>(q_first, k, v, cu, B, N, H, gather, scale, out_first, lse_first,  \
+                                           stream)                                                          \
+                : first_dispatch<false, DD>(q_first, k, v, cu, B, N, H, gather, scale, out_first, lse_first, \
+                                            stream);
   switch (D) {
     PE_FIRST_CASE(8)
     PE_FIRST_CASE(16)

@@ -25,8 +25,8 @@ PE_FP32, PE_BF16 = 0, 1
 EXPORTS = (
     "pe_status_string", "pe_attn_tile_rows", "pe_pack_workspace_size", "pe_pack", "pe_unpack",
     "pe_worklist", "pe_attn_workspace_size", "pe_varlen_attn_fwd", "pe_varlen_attn_fwd_first_token",
-    "pe_varlen_attn_bwd", "pe_varlen_attn_fwd_local", "pe_varlen_attn_bwd_local", "pe_timing_enable",
-    "pe_timing_read",
+    "pe_varlen_attn_bwd", "pe_varlen_attn_fwd_local", "pe_varlen_attn_bwd_local", "pe_varlen_attn_fwd_first_row",
+    "pe_varlen_attn_bwd_first_token", "pe_timing_enable", "pe_timing_read",
 )
 
 
@@ -61,6 +61,10 @@ def _load():
                                                      P, P, P, SZ, P]),
         "pe_varlen_attn_bwd_local": (ctypes.c_int, [P, P, P, P, P, P, P, I32, I64, I32, I32, I32, ctypes.c_int,
                                                      F, I32, P, P, P, P, SZ, P]),
+        "pe_varlen_attn_fwd_first_row": (ctypes.c_int, [P, P, P, P, I32, I64, I32, I32, I32, ctypes.c_int, F,
+                                                         P, P, P]),
+        "pe_varlen_attn_bwd_first_token": (ctypes.c_int, [P, P, P, P, P, P, P, I32, I64, I32, I32, I32,
+                                                           ctypes.c_int, F, P, P, P, P]),
         "pe_timing_enable": (ctypes.c_int, [ctypes.c_int]),
         "pe_timing_read": (ctypes.c_int, [P, P, ctypes.c_int]),
     }
@@ -159,6 +163,25 @@ def pe_varlen_attn_fwd_first_token(q_first, k, v, cu_seqlens, num_seqs, total_to
                                              total_tokens, max_seq_len, H, d, _dtype_code(q_first),
                                              softmax_scale, _ptr(out_first), _ptr(lse_first), _stream())
     _check("pe_varlen_attn_fwd_first_token", st)
+
+
+def pe_varlen_attn_fwd_first_row(q, k, v, cu_seqlens, num_seqs, total_tokens, max_seq_len, softmax_scale,
+                                 out_first, lse_first):
+    N, H, d = q.shape
+    st = _lib.pe_varlen_attn_fwd_first_row(_ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens), num_seqs, total_tokens,
+                                           max_seq_len, H, d, _dtype_code(q), softmax_scale, _ptr(out_first),
+                                           _ptr(lse_first), _stream())
+    _check("pe_varlen_attn_fwd_first_row", st)
+
+
+def pe_varlen_attn_bwd_first_token(dout_first, q_first, k, v, out_first, lse_first, cu_seqlens, num_seqs,
+                                   total_tokens, max_seq_len, softmax_scale, dq_first, dk, dv):
+    B, H, d = q_first.shape
+    st = _lib.pe_varlen_attn_bwd_first_token(_ptr(dout_first), _ptr(q_first), _ptr(k), _ptr(v), _ptr(out_first),
+                                             _ptr(lse_first), _ptr(cu_seqlens), num_seqs, total_tokens,
+                                             max_seq_len, H, d, _dtype_code(q_first), softmax_scale,
+                                             _ptr(dq_first), _ptr(dk), _ptr(dv), _stream())
+    _check("pe_varlen_attn_bwd_first_token", st)
 
 
 def pe_varlen_attn_bwd(dout, q, k, v, out, lse, cu_seqlens, num_seqs, total_tokens, max_seq_len,

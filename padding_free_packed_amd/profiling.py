@@ -24,6 +24,7 @@ KERNEL_SOURCES = {
     "attn_fwd": ["attn_fwd.hip", "attn_fwd_bf16.hip", "attn_fwd_bf16_w64.hip", "attn_f32_wave.hip", "attn_common.h",
                  "common.h"],
     "attn_fwd_first": ["attn_fwd.hip", "common.h"],
+    "attn_bwd_first": ["attn_first_bwd.hip", "attn_common.h", "common.h"],
     "bwd_delta": ["attn_bwd.hip", "attn_common.h", "common.h"],
     "bwd_dkdv": ["attn_bwd.hip", "attn_f32_wave.hip", "attn_common.h", "common.h"],
     "bwd_dq": ["attn_bwd.hip", "attn_f32_wave.hip", "attn_common.h", "common.h"],
@@ -37,6 +38,7 @@ KERNEL_SOURCES = {
 KERNEL_PATTERNS = {
     "attn_fwd": r"attn_fwd(_bf16|_bf16_w64|_f32)?_kernel<",
     "attn_fwd_first": r"attn_fwd_first_kernel<",
+    "attn_bwd_first": r"attn_bwd_first_kernel<",
     "bwd_delta": r"bwd_delta_kernel<",
     "bwd_dkdv": r"bwd_dkdv(_f32)?_kernel<",
     "bwd_dq": r"bwd_dq(_f32)?_kernel<",

@@ -27,7 +27,7 @@ def _header_functions():
 
 def test_header_symbols_exported():
     names = _header_functions()
-    assert len(names) == 14
+    assert len(names) == 16
     for n in names:
         assert hasattr(lib, n), n
     assert sorted(pe.EXPORTS) == names
@@ -90,6 +90,22 @@ def test_first_token_rejects():
     assert f(P, P, P, P, 4, 100, 64, 2, 24, 0, 0.125, P, NUL, None) == pe.PE_ERR_UNSUPPORTED
     assert f(P, P, P, P, 4, 100, 64, 2, 64, 0, -1.0, P, NUL, None) == pe.PE_ERR_ARG
     assert f(P, P, P, P, 4, 100, 64, 2, 64, 0, 0.125, P, MIS, None) == pe.PE_ERR_ARG
+
+
+def test_first_row_and_first_token_backward_reject():
+    f = lib.pe_varlen_attn_fwd_first_row
+    assert f(NUL, P, P, P, 4, 100, 64, 2, 64, 0, 0.125, P, NUL, None) == pe.PE_ERR_NULL
+    assert f(P, P, P, P, 4, 3, 64, 2, 64, 0, 0.125, P, NUL, None) == pe.PE_ERR_ARG
+    assert f(P, P, P, P, 4, 100, 64, 2, 64, 0, 0.125, MIS, NUL, None) == pe.PE_ERR_ARG
+    b = lib.pe_varlen_attn_bwd_first_token
+    ok = [P, P, P, P, P, P, P, 4, 100, 64, 2, 64, 0, 0.125, P, P, P, None]
+    for i in (0, 1, 2, 3, 4, 5, 6, 14, 15, 16):  # lse_first is required too
+        a = list(ok); a[i] = NUL
+        assert b(*a) == pe.PE_ERR_NULL, i
+    a = list(ok); a[11] = 40
+    assert b(*a) == pe.PE_ERR_UNSUPPORTED
+    a = list(ok); a[16] = MIS
+    assert b(*a) == pe.PE_ERR_ARG
 
 
 def test_local_rejects():
