@@ -37,6 +37,11 @@ gigl.nn.packed_attention" and the packed-encoders README):
   as ``_padded_packed_attention`` does.
 * ``worklist``: for a tile height R, the sequence holding the first row of every
   R-row tile of the packed buffer (the library's work list; brute force).
+* packing metadata (``position_ids``, ``document_ids``, ``flatten_packed_metadata``,
+  ``flatten_document_mask``, ``gather_rows``, ``scatter_rows``): the metadata of
+  the packed-encoders README's direct packed entry (position ids) and of NeMo's
+  packing (indexed document masks, ``flatten_packed_sequence_metadata``), written
+  out from their documented meaning with plain loops.
 * local attention: every attention function takes an optional ``window`` w;
   query i then sees only the keys j of its own sequence with |i - j| <= w. This
   is the sliding-window ("local") non-causal attention that the packed-encoders
@@ -411,3 +416,126 @@ def worklist(cu_seqlens, tile_rows: int):
     T = (N + tile_rows - 1) // tile_rows
     out = sequence_of_rows(cu, [t * tile_rows for t in range(T)])
     return np.array(out + [B], dtype=np.int32)
+
+
+# ---------------------------------------------------------------- packing metadata
+
+def position_ids(cu_seqlens):
+    """Position of every packed token inside its own sequence, int64 [N].
+
+    The packed-encoders README builds them for its direct packed entry as the
+    concatenation of arange(L_b) over the sequences.
+    """
+    cu = [int(x) for x in cu_seqlens]
+    return np.concatenate([np.arange(cu[b + 1] - cu[b], dtype=np.int64) for b in range(len(cu) - 1)])
+
+
+def document_ids(cu_seqlens):
+    """1-based index of the sequence (document) holding every packed token, int32 [N].
+
+    NeMo's indexed packing mask marks document i (1-based) with the integer i and
+    padding with 0; for a packed stream without padding this is that mask.
+    """
+    cu = [int(x) for x in cu_seqlens]
+    return np.concatenate([np.full(cu[b + 1] - cu[b], b + 1, dtype=np.int32) for b in range(len(cu) - 1)])
+
+
+class MetadataError(ValueError):
+    """Inconsistent packed metadata (NeMo raises ValueError for these)."""
+
+
+def _valid_prefix(row, width_limit=None):
+    """Length of the prefix of non-negative entries of a -1-padded row; checks that
+    only -1 follows it and that the prefix is strictly increasing."""
+    row = [int(x) for x in row]
+    n = 0
+    while n < len(row) and row[n] >= 0:
+        n += 1
+    if any(x != -1 for x in row[n:]):
+        raise MetadataError("padding other than -1, or -1 before a valid entry")
+    if any(row[i + 1] <= row[i] for i in range(n - 1)):
+        raise MetadataError("entries not strictly increasing")
+    if width_limit is not None and n > 0 and row[n - 1] >= width_limit:
+        raise MetadataError("token index outside the row")
+    return n
+
+
+def flatten_packed_metadata(token_index, cu_local, width: int):
+    """NeMo ``flatten_packed_sequence_metadata`` for the batch-major form.
+
+    token_index int [rows, width']: row-local indices of the real tokens of each
+    row, -1 padded. cu_local int [rows, max_docs + 1]: row-local cumulative
+    document lengths, -1 padded (a row without documents is all -1 or 0 then -1).
+    Returns the flat token indices int64 [tokens] into the padded [rows, width]
+    grid (row-major, rows in order) and the global cumulative lengths int32
+    [documents + 1] of the same stream. Raises MetadataError when a row's
+    boundaries are not 0 then strictly increasing, when its last boundary differs
+    from its number of tokens, or when indices are out of order or outside the row.
+    """
+    token_index = np.asarray(token_index)
+    cu_local = np.asarray(cu_local)
+    rows = token_index.shape[0]
+    if cu_local.shape[0] != rows:
+        raise MetadataError("token_index and cu_seqlens disagree on the number of rows")
+    flat, cu = [], [0]
+    base = 0
+    for r in range(rows):
+        n = _valid_prefix(token_index[r], width)
+        m = _valid_prefix(cu_local[r])
+        if m == 0:
+            docs_end = 0
+        else:
+            if int(cu_local[r, 0]) != 0:
+                raise MetadataError("a row's cumulative lengths do not start at 0")
+            docs_end = int(cu_local[r, m - 1])
+        if docs_end != n:
+            raise MetadataError("a row's cumulative lengths do not add up to its tokens")
+        flat.extend(r * width + int(token_index[r, j]) for j in range(n))
+        cu.extend(base + int(cu_local[r, i]) for i in range(1, m))
+        base += n
+    return np.asarray(flat, dtype=np.int64), np.asarray(cu, dtype=np.int32)
+
+
+def flatten_document_mask(mask):
+    """Flatten a NeMo indexed packing mask int [rows, width] (document i of a row,
+    1-based, marked i; padding 0, at the end of the row) to flat token indices
+    int64 [tokens] and global cumulative lengths int32 [documents + 1]. A document
+    is a maximal run of equal ids. Raises MetadataError unless every row is
+    1, then ids equal to or one above their predecessor, then only zeros.
+    """
+    mask = np.asarray(mask)
+    rows, width = mask.shape
+    flat, cu = [], [0]
+    for r in range(rows):
+        row = [int(x) for x in mask[r]]
+        n = 0
+        while n < width and row[n] > 0:
+            n += 1
+        if any(x != 0 for x in row[n:]):
+            raise MetadataError("padding other than 0, or 0 before a document")
+        for t in range(n):
+            prev = 0 if t == 0 else row[t - 1]
+            if row[t] != prev and row[t] != prev + 1:
+                raise MetadataError("document ids must start at 1 and grow by one")
+        start = len(flat)
+        flat.extend(r * width + t for t in range(n))
+        for t in range(1, n + 1):  # a document ends where the id changes or the row's tokens end
+            if t == n or row[t] != row[t - 1]:
+                cu.append(start + t)
+    return np.asarray(flat, dtype=np.int64), np.asarray(cu, dtype=np.int32)
+
+
+def gather_rows(src, flat_index):
+    """dst[r] = src[flat_index[r]] for rows of any width (bit copy)."""
+    src = np.asarray(src)
+    return src.reshape(src.shape[0], -1)[np.asarray(flat_index, dtype=np.int64)].reshape(
+        (len(flat_index),) + src.shape[1:])
+
+
+def scatter_rows(src, flat_index, dst_rows: int):
+    """dst[flat_index[r]] = src[r]; every other row of dst is +0.0 (zero bits)."""
+    src = np.asarray(src)
+    bits = _as_bits(src)
+    dst = np.zeros((dst_rows,) + src.shape[1:], dtype=bits.dtype)
+    dst[np.asarray(flat_index, dtype=np.int64)] = bits
+    return dst.view(src.dtype)
