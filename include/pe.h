@@ -55,7 +55,8 @@ typedef enum {
   PE_ERR_LENGTHS = 4,     /* pe_pack found a length outside [1, max_seq_len] */
   PE_ERR_CAPACITY = 5,    /* pe_pack: the token count exceeds `capacity` */
   PE_ERR_WORKSPACE = 6,   /* workspace NULL or smaller than required */
-  PE_ERR_HIP = 7          /* a HIP runtime call or kernel launch failed */
+  PE_ERR_HIP = 7,         /* a HIP runtime call or kernel launch failed */
+  PE_ERR_METADATA = 8     /* pe_flatten_*: packed metadata that is not consistent */
 } pe_status;
 
 typedef enum { PE_FP32 = 0, PE_BF16 = 1 } pe_dtype;
@@ -277,6 +278,72 @@ pe_status pe_varlen_attn_bwd_local(const void* dout, const void* q, const void* 
                                    int32_t num_heads, int32_t head_dim, pe_dtype dtype, float softmax_scale,
                                    int32_t window, void* dq, void* dk, void* dv, void* workspace,
                                    size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------- packing metadata
+ * pe_position_ids / pe_document_ids: per packed token, its position inside its
+ * own sequence (int64, position_ids[r] = r - cu[b]) and the 1-based index of its
+ * sequence (int32, document_ids[r] = b + 1).
+ *
+ * Sources: the packed-encoders README's direct packed entry takes position ids
+ * built as the concatenation of arange(L_b); NeMo's indexed packing mask marks
+ * document i (1-based) with i (padding 0), which for a stream without padding is
+ * document_ids. Either output may be NULL. Asynchronous; no workspace.
+ */
+pe_status pe_position_ids(const int32_t* cu_seqlens, int32_t num_seqs, int64_t total_tokens,
+                          int64_t* position_ids, int32_t* document_ids, void* stream);
+
+/* pe_flatten_packed_metadata / pe_flatten_document_mask: NeMo's batch-major
+ * packed metadata to one token stream.
+ *
+ * Source: NeMo `flatten_packed_sequence_metadata` (token indices [batch,
+ * sequence] row-local with -1 padding, cumulative lengths [batch, max_documents
+ * + 1] row-local with -1 padding, flattened to flat token indices into the padded
+ * [batch, sequence] grid; inconsistent layouts, boundaries or token counts are
+ * errors) and NeMo's indexed packing mask ([batch, sequence]; document i of a
+ * row marked i, padding 0).
+ *
+ *   token_index    device int32 [rows, width]: a strictly increasing prefix of
+ *                  indices in [0, width), then only -1
+ *   cu_local       device int32 [rows, max_docs + 1]: 0, then strictly increasing
+ *                  ends, then only -1; the last end equals the row's token count
+ *                  (a row without documents is all -1 or 0 then -1)
+ *   document_mask  device int32 [rows, width]: 1, then ids equal to or one above
+ *                  their predecessor, then only 0
+ * Outputs (rows in order, each row's tokens in order):
+ *   flat_index     device int64 [capacity] or NULL: r * width + the token's index
+ *   cu_seqlens     device int32 [doc_capacity + 1]: 0 and the end of every document
+ *                  in the stream (usable as the attention calls' cu_seqlens)
+ *   *h_total_tokens, *h_num_docs   host: the stream's token and document counts
+ * One host read (counts and the validity flag), as pe_pack. PE_ERR_METADATA if
+ * any row breaks the rules (outputs untouched); PE_ERR_CAPACITY if the counts
+ * exceed capacity / doc_capacity (counts still reported, outputs untouched).
+ * workspace: pe_flatten_workspace_size(rows) bytes.
+ */
+size_t pe_flatten_workspace_size(int32_t rows);
+pe_status pe_flatten_packed_metadata(const int32_t* token_index, const int32_t* cu_local, int32_t rows, int32_t width,
+                                     int32_t max_docs, int64_t* flat_index, int32_t* cu_seqlens, int64_t capacity,
+                                     int64_t doc_capacity, int64_t* h_total_tokens, int64_t* h_num_docs,
+                                     void* workspace, size_t workspace_bytes, void* stream);
+pe_status pe_flatten_document_mask(const int32_t* document_mask, int32_t rows, int32_t width, int64_t* flat_index,
+                                   int32_t* cu_seqlens, int64_t capacity, int64_t doc_capacity,
+                                   int64_t* h_total_tokens, int64_t* h_num_docs, void* workspace,
+                                   size_t workspace_bytes, void* stream);
+
+/* pe_gather_rows / pe_scatter_rows: the row copies of pack and unpack for any
+ * flat index (e.g. one from pe_flatten_*): dst[r] = src[flat_index[r]] for
+ * r < n, and dst[flat_index[r]] = src[r] with every other row of dst zero
+ * (+0.0). Source: GiGL's `grid.flatten()[flat_index]` gather and its scatter
+ * back into zeros (the data flow of the packed path).
+ *   src, dst         device, rows of row_elems elements of `dtype`
+ *   src_rows         rows of src (gather) / dst_rows rows of dst (scatter);
+ *                    index entries outside them give a zero row (gather) or are
+ *                    skipped (scatter)
+ * Bit copies; asynchronous; no workspace.
+ */
+pe_status pe_gather_rows(const void* src, int64_t src_rows, const int64_t* flat_index, int64_t n, int64_t row_elems,
+                         pe_dtype dtype, void* dst, void* stream);
+pe_status pe_scatter_rows(const void* src, const int64_t* flat_index, int64_t n, int64_t row_elems, pe_dtype dtype,
+                          void* dst, int64_t dst_rows, void* stream);
 
 /* ------------------------------------------------------------- kernel timing
  * Measurement support, not part of the computation. While enabled, every

@@ -60,6 +60,7 @@ const char* pe_status_string(int status) {
     case PE_ERR_LENGTHS: return "PE_ERR_LENGTHS: a sequence length lies outside [1, max_seq_len]";
     case PE_ERR_CAPACITY: return "PE_ERR_CAPACITY: token count exceeds the output capacity";
     case PE_ERR_WORKSPACE: return "PE_ERR_WORKSPACE: workspace missing or too small";
+    case PE_ERR_METADATA: return "PE_ERR_METADATA: inconsistent packed metadata (indices, boundaries or counts)";
     case PE_ERR_HIP: return "PE_ERR_HIP: a HIP runtime call or kernel launch failed";
     default: return "unknown pe_status";
   }
@@ -336,6 +337,88 @@ pe_status pe_varlen_attn_bwd_local(const void* dout, const void* q, const void* 
   return bwd_impl(dout, q, k, v, out, lse, cu_seqlens, num_seqs, total_tokens, max_seq_len, num_heads, head_dim,
                   dtype, softmax_scale, effective_window(window, max_seq_len), dq, dk, dv, workspace,
                   workspace_bytes, stream);
+}
+
+pe_status pe_position_ids(const int32_t* cu_seqlens, int32_t num_seqs, int64_t total_tokens,
+                          int64_t* position_ids, int32_t* document_ids, void* stream) {
+  if (!cu_seqlens) return PE_ERR_NULL;
+  if (num_seqs < 1 || total_tokens < 0 || total_tokens > INT32_MAX) return PE_ERR_ARG;
+  for (const void* p : {static_cast<const void*>(cu_seqlens), static_cast<const void*>(position_ids),
+                        static_cast<const void*>(document_ids)})
+    if (p && !aligned16(p)) return PE_ERR_ARG;
+  if (!position_ids && !document_ids) return PE_OK;
+  return hip_status(pe::launch_ids(cu_seqlens, num_seqs, total_tokens, position_ids, document_ids, as_stream(stream)));
+}
+
+size_t pe_flatten_workspace_size(int32_t rows) { return rows < 1 ? 0 : pe::flatten_workspace_bytes(rows); }
+
+}  // extern "C"
+
+namespace {
+
+pe_status flatten_impl(int form, const int32_t* a, const int32_t* cl, int32_t rows, int32_t width, int32_t ld,
+                       int64_t* flat_index, int32_t* cu_seqlens, int64_t capacity, int64_t doc_capacity,
+                       int64_t* h_total_tokens, int64_t* h_num_docs, void* workspace, size_t workspace_bytes,
+                       void* stream) {
+  if (!a || (form == 0 && !cl) || !cu_seqlens || !h_total_tokens || !h_num_docs) return PE_ERR_NULL;
+  if (rows < 1 || width < 1 || ld < 1 || capacity < 0 || doc_capacity < 0) return PE_ERR_ARG;
+  if (static_cast<int64_t>(rows) * width > INT32_MAX) return PE_ERR_ARG;
+  for (const void* p : {static_cast<const void*>(a), static_cast<const void*>(cl),
+                        static_cast<const void*>(flat_index), static_cast<const void*>(cu_seqlens),
+                        static_cast<const void*>(workspace)})
+    if (p && !aligned16(p)) return PE_ERR_ARG;
+  if (!workspace || workspace_bytes < pe_flatten_workspace_size(rows)) return PE_ERR_WORKSPACE;
+  hipStream_t st = as_stream(stream);
+  hipError_t e = pe::launch_flatten_counts(form, a, cl, rows, width, ld, workspace, st);
+  if (e != hipSuccess) return PE_ERR_HIP;
+  int64_t host[3] = {0, 0, 0};  // tokens, documents, error flag: the one host read
+  e = hipMemcpyAsync(host, workspace, sizeof(host), hipMemcpyDeviceToHost, st);
+  if (e == hipSuccess) e = hipStreamSynchronize(st);
+  if (e != hipSuccess) return PE_ERR_HIP;
+  *h_total_tokens = host[0];
+  *h_num_docs = host[1];
+  if (host[2] != 0) return PE_ERR_METADATA;
+  if (host[0] > capacity || host[1] > doc_capacity) return PE_ERR_CAPACITY;
+  return hip_status(pe::launch_flatten_write(form, a, cl, rows, width, ld, workspace, flat_index, cu_seqlens, st));
+}
+
+}  // namespace
+
+extern "C" {
+
+pe_status pe_flatten_packed_metadata(const int32_t* token_index, const int32_t* cu_local, int32_t rows, int32_t width,
+                                     int32_t max_docs, int64_t* flat_index, int32_t* cu_seqlens, int64_t capacity,
+                                     int64_t doc_capacity, int64_t* h_total_tokens, int64_t* h_num_docs,
+                                     void* workspace, size_t workspace_bytes, void* stream) {
+  if (max_docs < 0) return PE_ERR_ARG;
+  return flatten_impl(0, token_index, cu_local, rows, width, max_docs + 1, flat_index, cu_seqlens, capacity,
+                      doc_capacity, h_total_tokens, h_num_docs, workspace, workspace_bytes, stream);
+}
+
+pe_status pe_flatten_document_mask(const int32_t* document_mask, int32_t rows, int32_t width, int64_t* flat_index,
+                                   int32_t* cu_seqlens, int64_t capacity, int64_t doc_capacity,
+                                   int64_t* h_total_tokens, int64_t* h_num_docs, void* workspace,
+                                   size_t workspace_bytes, void* stream) {
+  return flatten_impl(1, document_mask, nullptr, rows, width, 1, flat_index, cu_seqlens, capacity, doc_capacity,
+                      h_total_tokens, h_num_docs, workspace, workspace_bytes, stream);
+}
+
+pe_status pe_gather_rows(const void* src, int64_t src_rows, const int64_t* flat_index, int64_t n, int64_t row_elems,
+                         pe_dtype dtype, void* dst, void* stream) {
+  if (!src || !flat_index || !dst) return PE_ERR_NULL;
+  if (src_rows < 0 || n < 0 || row_elems < 1) return PE_ERR_ARG;
+  if (!valid_dtype(dtype)) return PE_ERR_UNSUPPORTED;
+  return hip_status(pe::launch_gather_rows(src, src_rows, flat_index, n, row_elems * elem_bytes(dtype), dst,
+                                           as_stream(stream)));
+}
+
+pe_status pe_scatter_rows(const void* src, const int64_t* flat_index, int64_t n, int64_t row_elems, pe_dtype dtype,
+                          void* dst, int64_t dst_rows, void* stream) {
+  if (!src || !flat_index || !dst) return PE_ERR_NULL;
+  if (dst_rows < 0 || n < 0 || row_elems < 1) return PE_ERR_ARG;
+  if (!valid_dtype(dtype)) return PE_ERR_UNSUPPORTED;
+  return hip_status(pe::launch_scatter_rows(src, flat_index, n, row_elems * elem_bytes(dtype), dst, dst_rows,
+                                            as_stream(stream)));
 }
 
 }  // extern "C"

@@ -77,4 +77,18 @@ hipError_t launch_attn_bwd(bool bf16, int D, const void* dout, const void* q, co
                            const int32_t* items, const int32_t* items32, int32_t B, int32_t N, int32_t H,
                            int32_t win, float scale, void* dq, void* dk, void* dv, float* delta, hipStream_t stream);
 
+// packing metadata (meta.hip)
+hipError_t launch_ids(const int32_t* cu, int32_t B, int64_t N, int64_t* pos, int32_t* doc, hipStream_t stream);
+size_t flatten_workspace_bytes(int32_t rows);
+// form 0: token_index + cu_local (ld = max_docs + 1); form 1: document mask. Writes the
+// totals and the error flag to the first 24 bytes of ws (int64 x 3).
+hipError_t launch_flatten_counts(int form, const int32_t* a, const int32_t* cl, int32_t rows, int32_t width,
+                                 int32_t ld, void* ws, hipStream_t stream);
+hipError_t launch_flatten_write(int form, const int32_t* a, const int32_t* cl, int32_t rows, int32_t width,
+                                int32_t ld, const void* ws, int64_t* flat, int32_t* cu_out, hipStream_t stream);
+hipError_t launch_gather_rows(const void* src, int64_t src_rows, const int64_t* flat, int64_t n, int64_t rowbytes,
+                              void* dst, hipStream_t stream);
+hipError_t launch_scatter_rows(const void* src, const int64_t* flat, int64_t n, int64_t rowbytes, void* dst,
+                               int64_t dst_rows, hipStream_t stream);
+
 }  // namespace pe

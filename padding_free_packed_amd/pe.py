@@ -19,14 +19,15 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libpe.so")
 
 PE_OK, PE_ERR_NULL, PE_ERR_ARG, PE_ERR_UNSUPPORTED, PE_ERR_LENGTHS, PE_ERR_CAPACITY, \
-    PE_ERR_WORKSPACE, PE_ERR_HIP = range(8)
+    PE_ERR_WORKSPACE, PE_ERR_HIP, PE_ERR_METADATA = range(9)
 PE_FP32, PE_BF16 = 0, 1
 
 EXPORTS = (
     "pe_status_string", "pe_attn_tile_rows", "pe_pack_workspace_size", "pe_pack", "pe_unpack",
     "pe_worklist", "pe_attn_workspace_size", "pe_varlen_attn_fwd", "pe_varlen_attn_fwd_first_token",
     "pe_varlen_attn_bwd", "pe_varlen_attn_fwd_local", "pe_varlen_attn_bwd_local", "pe_varlen_attn_fwd_first_row",
-    "pe_varlen_attn_bwd_first_token", "pe_timing_enable", "pe_timing_read",
+    "pe_varlen_attn_bwd_first_token", "pe_position_ids", "pe_flatten_workspace_size", "pe_flatten_packed_metadata",
+    "pe_flatten_document_mask", "pe_gather_rows", "pe_scatter_rows", "pe_timing_enable", "pe_timing_read",
 )
 
 
@@ -65,6 +66,12 @@ def _load():
                                                          P, P, P]),
         "pe_varlen_attn_bwd_first_token": (ctypes.c_int, [P, P, P, P, P, P, P, I32, I64, I32, I32, I32,
                                                            ctypes.c_int, F, P, P, P, P]),
+        "pe_position_ids": (ctypes.c_int, [P, I32, I64, P, P, P]),
+        "pe_flatten_workspace_size": (SZ, [I32]),
+        "pe_flatten_packed_metadata": (ctypes.c_int, [P, P, I32, I32, I32, P, P, I64, I64, P, P, P, SZ, P]),
+        "pe_flatten_document_mask": (ctypes.c_int, [P, I32, I32, P, P, I64, I64, P, P, P, SZ, P]),
+        "pe_gather_rows": (ctypes.c_int, [P, I64, P, I64, I64, ctypes.c_int, P, P]),
+        "pe_scatter_rows": (ctypes.c_int, [P, P, I64, I64, ctypes.c_int, P, I64, P]),
         "pe_timing_enable": (ctypes.c_int, [ctypes.c_int]),
         "pe_timing_read": (ctypes.c_int, [P, P, ctypes.c_int]),
     }
@@ -211,6 +218,61 @@ def pe_varlen_attn_bwd_local(dout, q, k, v, out, lse, cu_seqlens, num_seqs, tota
                                        _dtype_code(q), softmax_scale, window, _ptr(dq), _ptr(dk), _ptr(dv),
                                        _ptr(workspace), workspace.numel(), _stream())
     _check("pe_varlen_attn_bwd_local", st)
+
+
+# ------------------------------------------------------------------ packing metadata
+
+def pe_position_ids(cu_seqlens, num_seqs, total_tokens, position_ids, document_ids):
+    _check("pe_position_ids", _lib.pe_position_ids(_ptr(cu_seqlens), num_seqs, total_tokens, _ptr(position_ids),
+                                                   _ptr(document_ids), _stream()))
+
+
+def pe_flatten_workspace_size(rows: int) -> int:
+    return int(_lib.pe_flatten_workspace_size(rows))
+
+
+def _flatten_result(fn, status, tok, docs):
+    if status != PE_OK:
+        raise PeError(fn, status, tok.value)
+    return tok.value, docs.value
+
+
+def pe_flatten_packed_metadata(token_index, cu_local, flat_index, cu_seqlens, workspace):
+    """token_index int32 [rows, width], cu_local int32 [rows, max_docs + 1] (device);
+    fills flat_index (int64, its length is the capacity) and cu_seqlens (int32); returns
+    (tokens, documents). PeError carries the status (capacity: token count in total_tokens)."""
+    rows, width = token_index.shape
+    tok, docs = ctypes.c_int64(0), ctypes.c_int64(0)
+    st = _lib.pe_flatten_packed_metadata(_ptr(token_index), _ptr(cu_local), rows, width, cu_local.shape[1] - 1,
+                                         _ptr(flat_index), _ptr(cu_seqlens),
+                                         0 if flat_index is None else flat_index.numel(), cu_seqlens.numel() - 1,
+                                         ctypes.byref(tok), ctypes.byref(docs), _ptr(workspace), workspace.numel(),
+                                         _stream())
+    return _flatten_result("pe_flatten_packed_metadata", st, tok, docs)
+
+
+def pe_flatten_document_mask(document_mask, flat_index, cu_seqlens, workspace):
+    rows, width = document_mask.shape
+    tok, docs = ctypes.c_int64(0), ctypes.c_int64(0)
+    st = _lib.pe_flatten_document_mask(_ptr(document_mask), rows, width, _ptr(flat_index), _ptr(cu_seqlens),
+                                       0 if flat_index is None else flat_index.numel(), cu_seqlens.numel() - 1,
+                                       ctypes.byref(tok), ctypes.byref(docs), _ptr(workspace), workspace.numel(),
+                                       _stream())
+    return _flatten_result("pe_flatten_document_mask", st, tok, docs)
+
+
+def pe_gather_rows(src, flat_index, dst):
+    """dst[r] = src[flat_index[r]]; src [rows, ...], dst [n, ...] of the same dtype."""
+    row_elems = src[0].numel() if src.shape[0] > 0 else int(torch.tensor(src.shape[1:]).prod())
+    _check("pe_gather_rows", _lib.pe_gather_rows(_ptr(src), src.shape[0], _ptr(flat_index), flat_index.numel(),
+                                                 row_elems, _dtype_code(src), _ptr(dst), _stream()))
+
+
+def pe_scatter_rows(src, flat_index, dst):
+    """dst[flat_index[r]] = src[r], every other row of dst zero."""
+    row_elems = dst[0].numel() if dst.shape[0] > 0 else int(torch.tensor(dst.shape[1:]).prod())
+    _check("pe_scatter_rows", _lib.pe_scatter_rows(_ptr(src), _ptr(flat_index), flat_index.numel(), row_elems,
+                                                   _dtype_code(src), _ptr(dst), dst.shape[0], _stream()))
 
 
 # ------------------------------------------------------------------ kernel timing

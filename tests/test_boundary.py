@@ -27,14 +27,14 @@ def _header_functions():
 
 def test_header_symbols_exported():
     names = _header_functions()
-    assert len(names) == 16
+    assert len(names) == 22
     for n in names:
         assert hasattr(lib, n), n
     assert sorted(pe.EXPORTS) == names
 
 
 def test_status_strings():
-    for s in range(8):
+    for s in range(9):
         assert lib.pe_status_string(s).decode().startswith("PE_")
     assert b"unknown" in lib.pe_status_string(99)
 
@@ -106,6 +106,34 @@ def test_first_row_and_first_token_backward_reject():
     assert b(*a) == pe.PE_ERR_UNSUPPORTED
     a = list(ok); a[16] = MIS
     assert b(*a) == pe.PE_ERR_ARG
+
+
+def test_metadata_calls_reject():
+    assert lib.pe_position_ids(NUL, 4, 100, P, P, None) == pe.PE_ERR_NULL
+    assert lib.pe_position_ids(P, 0, 100, P, P, None) == pe.PE_ERR_ARG
+    assert lib.pe_position_ids(P, 4, 100, MIS, NUL, None) == pe.PE_ERR_ARG
+    assert lib.pe_position_ids(P, 4, 100, NUL, NUL, None) == pe.PE_OK    # nothing asked, nothing launched
+    assert pe.pe_flatten_workspace_size(0) == 0 and pe.pe_flatten_workspace_size(10) >= 256 + 80 + 160
+    n, m = ctypes.c_int64(0), ctypes.c_int64(0)
+    f = lib.pe_flatten_packed_metadata
+    ok = [P, P, 4, 16, 3, P, P, 64, 8, ctypes.byref(n), ctypes.byref(m), P, 1 << 20, None]
+    for i in (0, 1, 6, 9, 10):
+        a = list(ok); a[i] = NUL
+        assert f(*a) == pe.PE_ERR_NULL, i
+    a = list(ok); a[2] = 0
+    assert f(*a) == pe.PE_ERR_ARG
+    a = list(ok); a[4] = -1
+    assert f(*a) == pe.PE_ERR_ARG
+    a = list(ok); a[12] = 16
+    assert f(*a) == pe.PE_ERR_WORKSPACE
+    g = lib.pe_flatten_document_mask
+    assert g(NUL, 4, 16, P, P, 64, 8, ctypes.byref(n), ctypes.byref(m), P, 1 << 20, None) == pe.PE_ERR_NULL
+    assert g(P, 4, 0, P, P, 64, 8, ctypes.byref(n), ctypes.byref(m), P, 1 << 20, None) == pe.PE_ERR_ARG
+    assert lib.pe_gather_rows(NUL, 4, P, 4, 16, 0, P, None) == pe.PE_ERR_NULL
+    assert lib.pe_gather_rows(P, 4, P, 4, 0, 0, P, None) == pe.PE_ERR_ARG
+    assert lib.pe_gather_rows(P, 4, P, 4, 16, 7, P, None) == pe.PE_ERR_UNSUPPORTED
+    assert lib.pe_scatter_rows(P, NUL, 4, 16, 0, P, 4, None) == pe.PE_ERR_NULL
+    assert lib.pe_scatter_rows(P, P, 4, 16, 0, P, -1, None) == pe.PE_ERR_ARG
 
 
 def test_local_rejects():
