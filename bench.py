@@ -74,6 +74,12 @@ def algo_work(kernel, w, N, L2, e, with_lse, with_grid=True):
         # unpack: read the real rows, write the whole grid
         "unpack_rows": {"byte": 1.0 * N * D * e + 1.0 * B * S * D * e},
         "scan": {"byte": 4.0 * B + 4.0 * (B + 1)},
+        # NeMo rows: the mask is read by both passes; flat index and cu written once
+        "flatten_count": {"byte": 4.0 * w.extra.get("grid_rows", 0) + 8.0 * w.extra.get("rows", 0)},
+        "flatten_write": {"byte": 4.0 * w.extra.get("grid_rows", 0) + 8.0 * N + 4.0 * (B + 1)},
+        # gather: read and write the real rows (+ the flat index); scatter: read the real rows, write the grid
+        "gather_rows": {"byte": 2.0 * N * D * e + 8.0 * N},
+        "scatter_rows": {"byte": 1.0 * N * D * e + 1.0 * w.extra.get("grid_rows", 0) * D * e + 8.0 * N},
         "worklist": {"byte": 4.0 * (B + 1) + 4.0 * (T + 1)},
     }.get(kernel)
 
@@ -108,7 +114,7 @@ def load_traffic(kernel, workload):
     return t.get("bytes_per_launch")
 
 
-def cpu_baseline(w, budget_s, window=None):
+def cpu_baseline(w, budget_s, window=None, nemo_mask=None):
     """The fp64 oracle on the first m sequences of the batch (a valid packed batch itself),
     with m sized for about `budget_s` seconds, BLAS limited to one thread."""
     import numpy as np
@@ -126,11 +132,18 @@ def cpu_baseline(w, budget_s, window=None):
         q, k, v = (W.to_f64(x[:n], w.dtype) for x in (w.q, w.k, w.v))
         do = W.to_f64(w.dout[:n], w.dtype) if w.dout is not None else None
         t0 = time.perf_counter()
+        if nemo_mask is not None:  # the rows holding these documents: flatten, gather q, k, v
+            rows = int(np.count_nonzero(nemo_mask.max(axis=1) > 0)) if m == w.num_seqs else \
+                min(nemo_mask.shape[0], 1 + int(np.searchsorted(np.cumsum((nemo_mask > 0).sum(1)), n)))
+            fl, _ = oracle.flatten_document_mask(nemo_mask[:rows])
+            for x in (w.q, w.k, w.v):
+                oracle.gather_rows(np.zeros((rows * nemo_mask.shape[1],) + x.shape[1:], dtype=x.dtype), fl)
         cu, flat, N = oracle.layout(L, w.max_seq_len)
         if grid is not None:
             oracle.pack(grid, flat)
         o, _ = oracle.attention(q, k, v, cu, w.scale, window=window)
-        oracle.attention_first_token(q[cu[:-1]], k, v, cu, w.scale)
+        if nemo_mask is None:
+            oracle.attention_first_token(q[cu[:-1]], k, v, cu, w.scale)
         if do is not None:
             oracle.attention_backward(do, q, k, v, cu, w.scale, window=window)
             oracle.attention_first_token_backward(do[cu[:-1]], q[cu[:-1]], k, v, cu, w.scale)
@@ -144,9 +157,11 @@ def cpu_baseline(w, budget_s, window=None):
         m = int(min(w.num_seqs, max(m, m * budget_s / max(t, 1e-3))))
         t, n = run(m)
     return {"value": n / t, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"first {m} of {w.num_seqs} sequences ({n} tokens): layout, pack, forward, first-token,"
-                      f"{' backward, first-token backward,' if w.dout is not None else ''}{' unpack' if w.grid is not None else ''} in float64,"
-                      f" {t:.1f} s"}
+            "sample": f"first {m} of {w.num_seqs} sequences ({n} tokens): "
+                      + ("flatten of their rows, gather, layout, forward," if nemo_mask is not None else
+                         "layout, pack, forward, first-token,")
+                      + (" backward, first-token backward," if w.dout is not None else "")
+                      + (" unpack" if w.grid is not None else "") + f" in float64, {t:.1f} s"}
 
 
 def main():
@@ -155,7 +170,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="graph_transformer",
-                    choices=["graph_transformer", "short_query", "long_document", "mixed_training", "tiny"])
+                    choices=["graph_transformer", "short_query", "long_document", "mixed_training", "tiny",
+                             "nemo_packed"])
     ap.add_argument("--window", type=int, default=None,
                     help="local attention: each query sees the keys within this distance in its sequence "
                          "(pe_varlen_attn_fwd_local / _bwd_local); default global attention")
@@ -184,8 +200,16 @@ def main():
         "long_document": W.long_document,
         "mixed_training": W.mixed_training,
         "tiny": lambda: W.tiny(with_grad=True),
+        # the mixed-training documents packed NeMo-style into rows of 8192 tokens (forward only)
+        "nemo_packed": W.mixed_training,
     }[args.workload]
     w = gen()
+    nemo = args.workload == "nemo_packed"
+    if nemo:
+        nemo_mask, nemo_grids = W.nemo_rows(w, w.max_seq_len)
+        w.dout = None
+        w.extra["rows"] = nemo_mask.shape[0]
+        w.extra["grid_rows"] = nemo_mask.size
     dev = "cuda:0"
     B, S, H, d = w.num_seqs, w.max_seq_len, w.num_heads, w.head_dim
     D = H * d
@@ -228,7 +252,24 @@ def main():
     ws = pe.workspace(pe.pe_attn_workspace_size(B, N, H, d, code, with_bwd), dev)
     scale = w.scale
 
+    if nemo:
+        # flatten the indexed document mask, gather Q, K, V from the padded row grids, attend,
+        # scatter the output back to the row grid
+        mask_d = torch.from_numpy(nemo_mask).to(dev)
+        ws_flat = pe.workspace(pe.pe_flatten_workspace_size(nemo_mask.shape[0]), dev)
+        grids_d = [up(nemo_grids[nm]) for nm in ("q", "k", "v")]
+        del nemo_grids
+        grid_rows_out = torch.empty_like(grids_d[0])
+
     def step():
+        if nemo:
+            n, docs = pe.pe_flatten_document_mask(mask_d, flat, cu, ws_flat)
+            assert (n, docs) == (N, B)
+            for src, dst in zip(grids_d, (q, k, v)):
+                pe.pe_gather_rows(src, flat, dst)
+            pe.pe_varlen_attn_fwd(q, k, v, cu, B, N, S, scale, out, lse, ws)
+            pe.pe_scatter_rows(out, flat, grid_rows_out)
+            return
         n = pe.pe_pack(lengths, S, grid, cu, flat, packed, N, ws_pack, code)
         assert n == N
         if args.window is None:
@@ -303,8 +344,10 @@ def main():
         "config": {
             "workload": args.workload, "num_seqs": B, "max_seq_len": S, "total_tokens": N, "num_heads": H,
             "head_dim": d, "grid": [B, S, D] if grid is not None else None, "window": args.window,
-            "step": ("pack" if grid is not None else "pack(layout only)") + "+fwd(lse)+first_token"
-                    + ("+bwd+first_token_bwd" if with_bwd else "") + ("+unpack" if grid is not None else ""),
+            "step": ("flatten(mask)+gather(q,k,v)+fwd(lse)+scatter" if nemo else
+                     ("pack" if grid is not None else "pack(layout only)") + "+fwd(lse)+first_token"
+                     + ("+bwd+first_token_bwd" if with_bwd else "") + ("+unpack" if grid is not None else "")),
+            "rows": [int(w.extra["rows"]), int(S)] if nemo else None,
         },
         "fwd": {"ms": fwd_ms, "tokens_per_s": N / (fwd_ms * 1e-3),
                 "tflops": 4.0 * L2 * H * d / (fwd_ms * 1e-3) / 1e12},
@@ -322,7 +365,7 @@ def main():
         result["copy_probe_bytes"] = nbytes
         del src, dst
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(w, args.cpu_budget, args.window)
+        result["cpu_baseline"] = cpu_baseline(w, args.cpu_budget, args.window, nemo_mask if nemo else None)
     print(json.dumps(result))
 
 

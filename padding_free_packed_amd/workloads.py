@@ -157,6 +157,39 @@ def mixed_training() -> Workload:
     return _finish("mixed_training", BF16, rng, lengths, 8192, 16, 64, False, ("q", "k", "v", "dout"))
 
 
+def nemo_rows(base: Workload, width: int):
+    """The documents of `base`, in their order, packed NeMo-style into rows of `width`
+    tokens (a document goes to the current row while it fits, else opens a new row).
+    Returns the indexed document mask int32 [rows, width] (document i of a row marked i,
+    padding 0) and, for each of q, k, v, a padded row grid [rows * width, H, d] holding the
+    packed tensors of `base` at the document positions (padding NaN, as the other grids)."""
+    rows_of, starts, row, fill = [], [], 0, 0
+    for L in base.lengths.astype(np.int64):
+        if fill + L > width:
+            row, fill = row + 1, 0
+        rows_of.append(row)
+        starts.append(fill)
+        fill += int(L)
+    R = row + 1
+    mask = np.zeros((R, width), dtype=np.int32)
+    dest = np.empty(base.total_tokens, dtype=np.int64)
+    pos, per_row = 0, {}
+    for b, L in enumerate(base.lengths.astype(np.int64)):
+        r, s0 = rows_of[b], starts[b]
+        per_row[r] = per_row.get(r, 0) + 1
+        mask[r, s0:s0 + L] = per_row[r]
+        dest[pos:pos + L] = r * width + s0 + np.arange(L)
+        pos += L
+    nan = BF16_NAN if base.dtype == BF16 else np.float32("nan")
+    grids = {}
+    for nm in ("q", "k", "v"):
+        x = getattr(base, nm)
+        g = np.full((R * width,) + x.shape[1:], nan, dtype=x.dtype)
+        g[dest] = x
+        grids[nm] = g
+    return mask, grids
+
+
 STANDING = {
     "tiny": tiny,
     "graph_transformer": graph_transformer,
