@@ -279,6 +279,32 @@ pe_status pe_varlen_attn_bwd_local(const void* dout, const void* q, const void* 
                                    int32_t window, void* dq, void* dk, void* dv, void* workspace,
                                    size_t workspace_bytes, void* stream);
 
+/* ---------------------------------------------------------------- fused QKV
+ * pe_varlen_attn_fwd_qkv / pe_varlen_attn_bwd_qkv: the attention calls on a
+ * fused projection buffer qkv [total_tokens, 3, num_heads, head_dim] (Q, K and V
+ * of a token side by side in one row, the layout of a fused QKV projection),
+ * read in place through a row stride of 3 * num_heads * head_dim elements; the
+ * backward writes dqkv in the same fused layout.
+ *
+ * Source: the packed-encoders README (its kernels consume the Hugging Face
+ * weight layout as is, nothing re-packed; ModernBERT projects Q, K and V with
+ * one fused matrix).
+ *
+ *   window   -1 for global attention, or the local radius as in
+ *            pe_varlen_attn_fwd_local (window >= 0)
+ *   out, dout   device [total_tokens, num_heads, head_dim] (dense); lse fp32 [H, N]
+ * Everything else as pe_varlen_attn_fwd / pe_varlen_attn_bwd (same workspace).
+ */
+pe_status pe_varlen_attn_fwd_qkv(const void* qkv, const int32_t* cu_seqlens, int32_t num_seqs, int64_t total_tokens,
+                                 int32_t max_seq_len, int32_t num_heads, int32_t head_dim, pe_dtype dtype,
+                                 float softmax_scale, int32_t window, void* out, float* lse, void* workspace,
+                                 size_t workspace_bytes, void* stream);
+pe_status pe_varlen_attn_bwd_qkv(const void* dout, const void* qkv, const void* out, const float* lse,
+                                 const int32_t* cu_seqlens, int32_t num_seqs, int64_t total_tokens,
+                                 int32_t max_seq_len, int32_t num_heads, int32_t head_dim, pe_dtype dtype,
+                                 float softmax_scale, int32_t window, void* dqkv, void* workspace,
+                                 size_t workspace_bytes, void* stream);
+
 /* ---------------------------------------------------------- packing metadata
  * pe_position_ids / pe_document_ids: per packed token, its position inside its
  * own sequence (int64, position_ids[r] = r - cu[b]) and the 1-based index of its

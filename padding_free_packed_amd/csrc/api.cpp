@@ -165,8 +165,8 @@ namespace {
 // The forward for every entry point: win is the local-attention radius, or -1.
 pe_status fwd_impl(const void* q, const void* k, const void* v, const int32_t* cu_seqlens, int32_t num_seqs,
                    int64_t total_tokens, int32_t max_seq_len, int32_t num_heads, int32_t head_dim, pe_dtype dtype,
-                   float softmax_scale, int32_t win, void* out, float* lse, void* workspace, size_t workspace_bytes,
-                   void* stream) {
+                   float softmax_scale, int32_t win, int64_t ld, void* out, float* lse, void* workspace,
+                   size_t workspace_bytes, void* stream) {
   if (!q || !k || !v || !cu_seqlens || !out) return PE_ERR_NULL;
   const pe_status s =
       check_attn_args(num_seqs, total_tokens, max_seq_len, num_heads, head_dim, dtype, softmax_scale);
@@ -182,17 +182,20 @@ pe_status fwd_impl(const void* q, const void* k, const void* v, const int32_t* c
     hipError_t e = pe::launch_worklist(cu_seqlens, num_seqs, total_tokens, pe::kAttnWaveRows, items, st);
     if (e != hipSuccess) return PE_ERR_HIP;
     return hip_status(pe::launch_attn_fwd_f32_wave(head_dim, q, k, v, cu_seqlens, items, num_seqs,
-                                                   static_cast<int32_t>(total_tokens), num_heads, win, softmax_scale,
-                                                   out, lse, st));
+                                                   static_cast<int32_t>(total_tokens), num_heads, win, ld,
+                                                   softmax_scale, out, lse, st));
   }
   hipError_t e = pe::launch_worklist(cu_seqlens, num_seqs, total_tokens, pe::kAttnTileRows, items, st);
   if (e != hipSuccess) return PE_ERR_HIP;
   e = pe::launch_attn_fwd(dtype == PE_BF16, head_dim, q, k, v, cu_seqlens, items, num_seqs,
-                          static_cast<int32_t>(total_tokens), num_heads, max_seq_len, win, softmax_scale, out, lse,
-                          st);
+                          static_cast<int32_t>(total_tokens), num_heads, max_seq_len, win, ld, softmax_scale, out,
+                          lse, st);
   return hip_status(e);
 }
 
+
+// Elements between rows of separate [N, H, d] tensors.
+int64_t dense_ld(int32_t num_heads, int32_t head_dim) { return static_cast<int64_t>(num_heads) * head_dim; }
 
 // A window at least max_seq_len - 1 keeps every key of every sequence: global attention.
 int32_t effective_window(int32_t window, int32_t max_seq_len) { return window >= max_seq_len - 1 ? -1 : window; }
@@ -206,7 +209,7 @@ pe_status pe_varlen_attn_fwd(const void* q, const void* k, const void* v, const 
                              int32_t head_dim, pe_dtype dtype, float softmax_scale, void* out, float* lse,
                              void* workspace, size_t workspace_bytes, void* stream) {
   return fwd_impl(q, k, v, cu_seqlens, num_seqs, total_tokens, max_seq_len, num_heads, head_dim, dtype,
-                  softmax_scale, -1, out, lse, workspace, workspace_bytes, stream);
+                  softmax_scale, -1, dense_ld(num_heads, head_dim), out, lse, workspace, workspace_bytes, stream);
 }
 
 pe_status pe_varlen_attn_fwd_local(const void* q, const void* k, const void* v, const int32_t* cu_seqlens,
@@ -215,7 +218,8 @@ pe_status pe_varlen_attn_fwd_local(const void* q, const void* k, const void* v, 
                                    float* lse, void* workspace, size_t workspace_bytes, void* stream) {
   if (window < 0) return PE_ERR_ARG;
   return fwd_impl(q, k, v, cu_seqlens, num_seqs, total_tokens, max_seq_len, num_heads, head_dim, dtype,
-                  softmax_scale, effective_window(window, max_seq_len), out, lse, workspace, workspace_bytes, stream);
+                  softmax_scale, effective_window(window, max_seq_len), dense_ld(num_heads, head_dim), out, lse,
+                  workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"
@@ -233,8 +237,9 @@ pe_status first_impl(const void* q, int32_t gather, const void* k, const void* v
                         static_cast<const void*>(lse_first)})
     if (p && !aligned16(p)) return PE_ERR_ARG;
   return hip_status(pe::launch_attn_fwd_first(dtype == PE_BF16, head_dim, q, k, v, cu_seqlens, num_seqs,
-                                              static_cast<int32_t>(total_tokens), num_heads, gather, softmax_scale,
-                                              out_first, lse_first, as_stream(stream)));
+                                              static_cast<int32_t>(total_tokens), num_heads, gather,
+                                              static_cast<int64_t>(num_heads) * head_dim, softmax_scale, out_first,
+                                              lse_first, as_stream(stream)));
 }
 
 }  // namespace
@@ -274,7 +279,8 @@ pe_status pe_varlen_attn_bwd_first_token(const void* dout_first, const void* q_f
     if (!aligned16(p)) return PE_ERR_ARG;
   return hip_status(pe::launch_attn_bwd_first(dtype == PE_BF16, head_dim, dout_first, q_first, k, v, out_first,
                                               lse_first, cu_seqlens, num_seqs, static_cast<int32_t>(total_tokens),
-                                              num_heads, softmax_scale, dq_first, dk, dv, as_stream(stream)));
+                                              num_heads, static_cast<int64_t>(num_heads) * head_dim, softmax_scale,
+                                              dq_first, dk, dv, as_stream(stream)));
 }
 
 // ------------------------------------------------------------------ backward
@@ -286,8 +292,8 @@ namespace {
 // The backward for every entry point: win is the local-attention radius, or -1.
 pe_status bwd_impl(const void* dout, const void* q, const void* k, const void* v, const void* out, const float* lse,
                    const int32_t* cu_seqlens, int32_t num_seqs, int64_t total_tokens, int32_t max_seq_len,
-                   int32_t num_heads, int32_t head_dim, pe_dtype dtype, float softmax_scale, int32_t win, void* dq,
-                   void* dk, void* dv, void* workspace, size_t workspace_bytes, void* stream) {
+                   int32_t num_heads, int32_t head_dim, pe_dtype dtype, float softmax_scale, int32_t win, int64_t ld,
+                   void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes, void* stream) {
   if (!dout || !q || !k || !v || !out || !lse || !cu_seqlens || !dq || !dk || !dv) return PE_ERR_NULL;
   const pe_status s =
       check_attn_args(num_seqs, total_tokens, max_seq_len, num_heads, head_dim, dtype, softmax_scale);
@@ -310,7 +316,7 @@ pe_status bwd_impl(const void* dout, const void* q, const void* k, const void* v
   }
   e = pe::launch_attn_bwd(dtype == PE_BF16, head_dim, dout, q, k, v, out, lse, cu_seqlens, items,
                           dtype == PE_FP32 ? items32 : nullptr, num_seqs, static_cast<int32_t>(total_tokens),
-                          num_heads, win, softmax_scale, dq, dk, dv, delta, st);
+                          num_heads, win, ld, softmax_scale, dq, dk, dv, delta, st);
   if (e == hipErrorNotSupported) return PE_ERR_UNSUPPORTED;
   return hip_status(e);
 }
@@ -325,7 +331,8 @@ pe_status pe_varlen_attn_bwd(const void* dout, const void* q, const void* k, con
                              float softmax_scale, void* dq, void* dk, void* dv, void* workspace,
                              size_t workspace_bytes, void* stream) {
   return bwd_impl(dout, q, k, v, out, lse, cu_seqlens, num_seqs, total_tokens, max_seq_len, num_heads, head_dim,
-                  dtype, softmax_scale, -1, dq, dk, dv, workspace, workspace_bytes, stream);
+                  dtype, softmax_scale, -1, dense_ld(num_heads, head_dim), dq, dk, dv, workspace, workspace_bytes,
+                  stream);
 }
 
 pe_status pe_varlen_attn_bwd_local(const void* dout, const void* q, const void* k, const void* v, const void* out,
@@ -335,8 +342,39 @@ pe_status pe_varlen_attn_bwd_local(const void* dout, const void* q, const void* 
                                    void* workspace, size_t workspace_bytes, void* stream) {
   if (window < 0) return PE_ERR_ARG;
   return bwd_impl(dout, q, k, v, out, lse, cu_seqlens, num_seqs, total_tokens, max_seq_len, num_heads, head_dim,
-                  dtype, softmax_scale, effective_window(window, max_seq_len), dq, dk, dv, workspace,
-                  workspace_bytes, stream);
+                  dtype, softmax_scale, effective_window(window, max_seq_len), dense_ld(num_heads, head_dim), dq, dk,
+                  dv, workspace, workspace_bytes, stream);
+}
+
+pe_status pe_varlen_attn_fwd_qkv(const void* qkv, const int32_t* cu_seqlens, int32_t num_seqs, int64_t total_tokens,
+                                 int32_t max_seq_len, int32_t num_heads, int32_t head_dim, pe_dtype dtype,
+                                 float softmax_scale, int32_t window, void* out, float* lse, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+  if (!qkv) return PE_ERR_NULL;
+  if (window < -1) return PE_ERR_ARG;
+  const int64_t hd = dense_ld(num_heads, head_dim);
+  const char* base = static_cast<const char*>(qkv);
+  const size_t step = static_cast<size_t>(hd) * elem_bytes(dtype);
+  return fwd_impl(base, base + step, base + 2 * step, cu_seqlens, num_seqs, total_tokens, max_seq_len, num_heads,
+                  head_dim, dtype, softmax_scale, window < 0 ? -1 : effective_window(window, max_seq_len), 3 * hd,
+                  out, lse, workspace, workspace_bytes, stream);
+}
+
+pe_status pe_varlen_attn_bwd_qkv(const void* dout, const void* qkv, const void* out, const float* lse,
+                                 const int32_t* cu_seqlens, int32_t num_seqs, int64_t total_tokens,
+                                 int32_t max_seq_len, int32_t num_heads, int32_t head_dim, pe_dtype dtype,
+                                 float softmax_scale, int32_t window, void* dqkv, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+  if (!qkv || !dqkv) return PE_ERR_NULL;
+  if (window < -1) return PE_ERR_ARG;
+  const int64_t hd = dense_ld(num_heads, head_dim);
+  const char* base = static_cast<const char*>(qkv);
+  char* dbase = static_cast<char*>(dqkv);
+  const size_t step = static_cast<size_t>(hd) * elem_bytes(dtype);
+  return bwd_impl(dout, base, base + step, base + 2 * step, out, lse, cu_seqlens, num_seqs, total_tokens,
+                  max_seq_len, num_heads, head_dim, dtype, softmax_scale,
+                  window < 0 ? -1 : effective_window(window, max_seq_len), 3 * hd, dbase, dbase + step,
+                  dbase + 2 * step, workspace, workspace_bytes, stream);
 }
 
 pe_status pe_position_ids(const int32_t* cu_seqlens, int32_t num_seqs, int64_t total_tokens,

@@ -57,7 +57,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(
     const void* __restrict__ dop, const void* __restrict__ qp, const void* __restrict__ kp,
     const void* __restrict__ vp, const float* __restrict__ lse, const float* __restrict__ delta,
     const int32_t* __restrict__ cu, const int32_t* __restrict__ items, int32_t B, int32_t N, int32_t H,
-    int32_t T, int32_t win, float c, float scale, void* __restrict__ dkp, void* __restrict__ dvp) {
+    int32_t T, int32_t win, int64_t ld, float c, float scale, void* __restrict__ dkp, void* __restrict__ dvp) {
   using G = Geo<BF, D>;
   using E = typename G::E;
   // bf16 tiles with whole 16-byte chunks per lane half use the XOR-swizzled layout
@@ -88,7 +88,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(
   const int mq1 = wave_min_i(kvalid ? jk1 : INT_MAX);
 
   typename RegT<BF>::T kreg[G::QS], vreg[G::QS];
-  const int64_t roff = (static_cast<int64_t>(krow) * H + h) * D;
+  const int64_t roff = static_cast<int64_t>(krow) * ld + h * D;  // rows of K, V, dK, dV are ld apart
   load_row_regs<BF, D>(kp, roff + g * G::HALF, kvalid, kreg);
   load_row_regs<BF, D>(vp, roff + g * G::HALF, kvalid, vreg);
 
@@ -107,8 +107,8 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(
   const float* lse_h = lse + static_cast<int64_t>(h) * N;
   const float* del_h = delta + static_cast<int64_t>(h) * N;
   auto gload = [&](int qb) {
-    tile_gload<BF, D>(qp, qb, qhi, H, h, qr);
-    tile_gload<BF, D>(dop, qb, qhi, H, h, dr);
+    tile_gload<BF, D>(qp, qb, qhi, ld, h, qr);
+    tile_gload<BF, D>(dop, qb, qhi, static_cast<int64_t>(H) * D, h, dr);
     if (tid < kBlk) {
       const int row = qb + tid;
       lsr = row < qhi ? lse_h[row] * kLog2e : 0.f;
@@ -185,7 +185,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
     const void* __restrict__ dop, const void* __restrict__ qp, const void* __restrict__ kp,
     const void* __restrict__ vp, const float* __restrict__ lse, const float* __restrict__ delta,
     const int32_t* __restrict__ cu, const int32_t* __restrict__ items, int32_t B, int32_t N, int32_t H,
-    int32_t T, int32_t win, float c, float scale, void* __restrict__ dqp) {
+    int32_t T, int32_t win, int64_t ld, float c, float scale, void* __restrict__ dqp) {
   using G = Geo<BF, D>;
   using E = typename G::E;
   constexpr bool SWZ = BF && D % 32 == 0;
@@ -212,9 +212,9 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
   const int mk1 = wave_min_i(qvalid ? qk1 : INT_MAX);
 
   typename RegT<BF>::T qreg[G::QS], dreg[G::QS];
-  const int64_t roff = (static_cast<int64_t>(qrow) * H + h) * D;
+  const int64_t roff = static_cast<int64_t>(qrow) * ld + h * D;  // rows of Q and dQ are ld apart
   load_row_regs<BF, D>(qp, roff + g * G::HALF, qvalid, qreg);
-  load_row_regs<BF, D>(dop, roff + g * G::HALF, qvalid, dreg);
+  load_row_regs<BF, D>(dop, (static_cast<int64_t>(qrow) * H + h) * D + g * G::HALF, qvalid, dreg);
   const float lse2 = qvalid ? lse[static_cast<int64_t>(h) * N + qrow] * kLog2e : 0.f;
   const float dlq = qvalid ? delta[static_cast<int64_t>(h) * N + qrow] : 0.f;
 
@@ -227,8 +227,8 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
   const int khi = win >= 0 ? min(sp.hi, sp.rend + win) : sp.hi;
   int buf = 0;
   if (klo < khi) {
-    tile_gload<BF, D>(kp, klo, khi, H, h, kr);
-    tile_gload<BF, D>(vp, klo, khi, H, h, vr);
+    tile_gload<BF, D>(kp, klo, khi, ld, h, kr);
+    tile_gload<BF, D>(vp, klo, khi, ld, h, vr);
   }
   for (int kb = klo; kb < khi; kb += kBlk) {
     if constexpr (SWZ) {
@@ -240,8 +240,8 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
     }
     __syncthreads();
     if (kb + kBlk < khi) {
-      tile_gload<BF, D>(kp, kb + kBlk, khi, H, h, kr);
-      tile_gload<BF, D>(vp, kb + kBlk, khi, H, h, vr);
+      tile_gload<BF, D>(kp, kb + kBlk, khi, ld, h, kr);
+      tile_gload<BF, D>(vp, kb + kBlk, khi, ld, h, vr);
     }
     if (kb < wk1 && kb + kBlk > wk0) {
       const bool need_mask = !(kb >= mk0 && kb + kBlk <= mk1);
@@ -281,8 +281,8 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
 template <bool BF, int D>
 hipError_t bwd_dispatch(const void* dout, const void* q, const void* k, const void* v, const void* out,
                         const float* lse, const int32_t* cu, const int32_t* items, const int32_t* items32, int32_t B,
-                        int32_t N, int32_t H, int32_t win, float scale, void* dq, void* dk, void* dv, float* delta,
-                        hipStream_t stream) {
+                        int32_t N, int32_t H, int32_t win, int64_t ld, float scale, void* dq, void* dk, void* dv,
+                        float* delta, hipStream_t stream) {
   using G = Geo<BF, D>;
   if (N == 0) return hipSuccess;
   const int64_t chunks = static_cast<int64_t>(N) * H * G::CH;
@@ -293,22 +293,23 @@ hipError_t bwd_dispatch(const void* dout, const void* q, const void* k, const vo
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (!BF && items32 != nullptr && (D == 32 || D == 64)) {
-    e = launch_bwd_dkdv_f32_wave(D, dout, q, k, v, lse, delta, cu, items32, B, N, H, win, scale, dk, dv, stream);
+    e = launch_bwd_dkdv_f32_wave(D, dout, q, k, v, lse, delta, cu, items32, B, N, H, win, ld, scale, dk, dv,
+                                 stream);
     if (e != hipSuccess) return e;
-    return launch_bwd_dq_f32_wave(D, dout, q, k, v, lse, delta, cu, items32, B, N, H, win, scale, dq, stream);
+    return launch_bwd_dq_f32_wave(D, dout, q, k, v, lse, delta, cu, items32, B, N, H, win, ld, scale, dq, stream);
   }
   const int T = (N + kAttnTileRows - 1) / kAttnTileRows;
   const unsigned blocks = static_cast<unsigned>(static_cast<int64_t>(T) * H);
   const float c = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
   hipEvent_t ev_bwd_dkdv = timing_start(stream);
   hipLaunchKernelGGL((bwd_dkdv_kernel<BF, D>), dim3(blocks), dim3(kThreads), 0, stream, dout, q, k, v, lse, delta,
-                   cu, items, B, N, H, T, win, c, scale, dk, dv);
+                   cu, items, B, N, H, T, win, ld, c, scale, dk, dv);
   timing_stop("bwd_dkdv", ev_bwd_dkdv, stream);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipEvent_t ev_bwd_dq = timing_start(stream);
   hipLaunchKernelGGL((bwd_dq_kernel<BF, D>), dim3(blocks), dim3(kThreads), 0, stream, dout, q, k, v, lse, delta,
-                   cu, items, B, N, H, T, win, c, scale, dq);
+                   cu, items, B, N, H, T, win, ld, c, scale, dq);
   timing_stop("bwd_dq", ev_bwd_dq, stream);
   return hipGetLastError();
 }
@@ -317,14 +318,14 @@ hipError_t bwd_dispatch(const void* dout, const void* q, const void* k, const vo
 
 hipError_t launch_attn_bwd(bool bf16, int D, const void* dout, const void* q, const void* k, const void* v,
                            const void* out, const float* lse, const int32_t* cu, const int32_t* items,
-                           const int32_t* items32, int32_t B, int32_t N, int32_t H, int32_t win, float scale,
-                           void* dq, void* dk, void* dv, float* delta, hipStream_t stream) {
+                           const int32_t* items32, int32_t B, int32_t N, int32_t H, int32_t win, int64_t ld,
+                           float scale, void* dq, void* dk, void* dv, float* delta, hipStream_t stream) {
 #define PE_BWD_CASE(DD)                                                                                    \
   case DD:                                                                                                \
-    return bf16 ? bwd_dispatch<true, DD>(dout, q, k, v, out, lse, cu, items, items32, B, N, H, win, scale, dq, dk, dv, \
-                                         delta, stream)                                                   \
-                : bwd_dispatch<false, DD>(dout, q, k, v, out, lse, cu, items, items32, B, N, H, win, scale, dq, dk, dv, \
-                                          delta, stream);
+    return bf16 ? bwd_dispatch<true, DD>(dout, q, k, v, out, lse, cu, items, items32, B, N, H, win, ld, scale, dq,  \
+                                         dk, dv, delta, stream)                                           \
+                : bwd_dispatch<false, DD>(dout, q, k, v, out, lse, cu, items, items32, B, N, H, win, ld, scale, dq, \
+                                          dk, dv, delta, stream);
   switch (D) {
     PE_BWD_CASE(8)
     PE_BWD_CASE(16)

@@ -103,9 +103,10 @@ __device__ __forceinline__ void load_row_regs(const void* base, int64_t off, boo
   }
 }
 
-// Global -> registers for one 64-row tile of head h; rows >= row_lim are zero.
+// Global -> registers for one 64-row tile of head h of a tensor whose rows are
+// `ld` elements apart; rows >= row_lim are zero.
 template <bool BF, int D>
-__device__ __forceinline__ void tile_gload(const void* base, int row0, int row_lim, int H, int h,
+__device__ __forceinline__ void tile_gload(const void* base, int row0, int row_lim, int64_t ld, int h,
                                            uint4 (&r)[Geo<BF, D>::PER]) {
   using G = Geo<BF, D>;
   const char* b = static_cast<const char*>(base);
@@ -115,7 +116,8 @@ __device__ __forceinline__ void tile_gload(const void* base, int row0, int row_l
     const int row = ch / G::CH, col = ch - row * G::CH;
     const int gr = row0 + row;
     if ((G::TOTCH % kThreads == 0 || ch < G::TOTCH) && gr < row_lim) {
-      r[p] = *reinterpret_cast<const uint4*>(b + (static_cast<int64_t>(gr) * H + h) * G::ROWB + col * 16);
+      r[p] = *reinterpret_cast<const uint4*>(b + (static_cast<int64_t>(gr) * ld + static_cast<int64_t>(h) * D) * G::ES +
+                                             col * 16);
     } else {
       r[p] = make_uint4(0, 0, 0, 0);
     }

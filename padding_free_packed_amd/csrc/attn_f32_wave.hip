@@ -34,11 +34,11 @@ struct F32Ops {
 
 template <int D>
 __device__ __forceinline__ void load_ops(F32Ops<D>& ops, const float* __restrict__ kp, const float* __restrict__ vp,
-                                         int kb, int klast, int H, int h, int ql, int g) {
+                                         int kb, int klast, int64_t ld, int h, int ql, int g) {
   using O = F32Ops<D>;
   {
     const int key = min(kb + ql, klast);
-    const float4* src = reinterpret_cast<const float4*>(kp + (static_cast<int64_t>(key) * H + h) * D + g * O::HALF);
+    const float4* src = reinterpret_cast<const float4*>(kp + static_cast<int64_t>(key) * ld + h * D + g * O::HALF);
 #pragma unroll
     for (int j = 0; j < O::HALF / 4; ++j) {
       const float4 x = src[j];
@@ -51,7 +51,7 @@ __device__ __forceinline__ void load_ops(F32Ops<D>& ops, const float* __restrict
 #pragma unroll
   for (int st = 0; st < 16; ++st) {
     const int key = min(kb + 8 * (st >> 2) + 4 * g + (st & 3), klast);
-    const float* row = vp + (static_cast<int64_t>(key) * H + h) * D;
+    const float* row = vp + static_cast<int64_t>(key) * ld + h * D;
 #pragma unroll
     for (int db = 0; db < O::DB; ++db) ops.v[st][db] = row[db * 32 + ql];
   }
@@ -61,7 +61,7 @@ template <int D>
 __global__ __launch_bounds__(64, 2) void attn_fwd_f32_kernel(
     const float* __restrict__ qp, const float* __restrict__ kp, const float* __restrict__ vp,
     const int32_t* __restrict__ cu, const int32_t* __restrict__ items, int32_t B, int32_t N, int32_t H, int32_t T,
-    int32_t win, float c, float* __restrict__ op, float* __restrict__ lse) {
+    int32_t win, int64_t ld, float c, float* __restrict__ op, float* __restrict__ lse) {
   using O = F32Ops<D>;
   __shared__ int32_t cul[kRows + 2];
   const int lin = xcd_remap(blockIdx.x, gridDim.x);
@@ -91,7 +91,7 @@ __global__ __launch_bounds__(64, 2) void attn_fwd_f32_kernel(
   float qf[O::HALF];
   {
     const float4* src =
-        reinterpret_cast<const float4*>(qp + (static_cast<int64_t>(qvalid ? qrow : r0) * H + h) * D + g * O::HALF);
+        reinterpret_cast<const float4*>(qp + static_cast<int64_t>(qvalid ? qrow : r0) * ld + h * D + g * O::HALF);
 #pragma unroll
     for (int j = 0; j < O::HALF / 4; ++j) {
       const float4 x = src[j];
@@ -145,12 +145,12 @@ __global__ __launch_bounds__(64, 2) void attn_fwd_f32_kernel(
   if (wk0 < wk1) {
     const int klast = wk1 - 1;
     O a, b;
-    load_ops<D>(a, kp, vp, wk0, klast, H, h, ql, g);
+    load_ops<D>(a, kp, vp, wk0, klast, ld, h, ql, g);
     for (int kb = wk0; kb < wk1; kb += 64) {
-      if (kb + 32 < wk1) load_ops<D>(b, kp, vp, kb + 32, klast, H, h, ql, g);
+      if (kb + 32 < wk1) load_ops<D>(b, kp, vp, kb + 32, klast, ld, h, ql, g);
       block(a, kb);
       if (kb + 32 >= wk1) break;
-      if (kb + 64 < wk1) load_ops<D>(a, kp, vp, kb + 64, klast, H, h, ql, g);
+      if (kb + 64 < wk1) load_ops<D>(a, kp, vp, kb + 64, klast, ld, h, ql, g);
       block(b, kb + 32);
     }
   }
@@ -165,7 +165,7 @@ __global__ __launch_bounds__(64, 2) void attn_fwd_f32_kernel(
 
 template <int D>
 hipError_t dispatch(const void* q, const void* k, const void* v, const int32_t* cu, const int32_t* items,
-                    int32_t B, int32_t N, int32_t H, int32_t win, float scale, void* out, float* lse,
+                    int32_t B, int32_t N, int32_t H, int32_t win, int64_t ld, float scale, void* out, float* lse,
                     hipStream_t stream) {
   const int T = (N + kRows - 1) / kRows;
   const int64_t blocks = static_cast<int64_t>(T) * H;
@@ -174,7 +174,7 @@ hipError_t dispatch(const void* q, const void* k, const void* v, const int32_t* 
   hipEvent_t ev = timing_start(stream);
   hipLaunchKernelGGL((attn_fwd_f32_kernel<D>), dim3(static_cast<unsigned>(blocks)), dim3(64), 0, stream,
                      static_cast<const float*>(q), static_cast<const float*>(k), static_cast<const float*>(v), cu,
-                     items, B, N, H, T, win, c, static_cast<float*>(out), lse);
+                     items, B, N, H, T, win, ld, c, static_cast<float*>(out), lse);
   timing_stop("attn_fwd", ev, stream);
   return hipGetLastError();
 }
@@ -184,11 +184,11 @@ hipError_t dispatch(const void* q, const void* k, const void* v, const int32_t* 
 bool attn_fwd_f32_wave_supported(int D) { return D == 32 || D == 64; }
 
 hipError_t launch_attn_fwd_f32_wave(int D, const void* q, const void* k, const void* v, const int32_t* cu,
-                                    const int32_t* items32, int32_t B, int32_t N, int32_t H, int32_t win, float scale,
-                                    void* out, float* lse, hipStream_t stream) {
+                                    const int32_t* items32, int32_t B, int32_t N, int32_t H, int32_t win, int64_t ld,
+                                    float scale, void* out, float* lse, hipStream_t stream) {
   switch (D) {
-    case 32: return dispatch<32>(q, k, v, cu, items32, B, N, H, win, scale, out, lse, stream);
-    case 64: return dispatch<64>(q, k, v, cu, items32, B, N, H, win, scale, out, lse, stream);
+    case 32: return dispatch<32>(q, k, v, cu, items32, B, N, H, win, ld, scale, out, lse, stream);
+    case 64: return dispatch<64>(q, k, v, cu, items32, B, N, H, win, ld, scale, out, lse, stream);
     default: return hipErrorInvalidValue;
   }
 }
@@ -237,7 +237,7 @@ __global__ __launch_bounds__(64, 2) void bwd_dq_f32_kernel(
     const float* __restrict__ dop, const float* __restrict__ qp, const float* __restrict__ kp,
     const float* __restrict__ vp, const float* __restrict__ lse, const float* __restrict__ delta,
     const int32_t* __restrict__ cu, const int32_t* __restrict__ items, int32_t B, int32_t N, int32_t H, int32_t T,
-    int32_t win, float c, float scale, float* __restrict__ dqp) {
+    int32_t win, int64_t ld, float c, float scale, float* __restrict__ dqp) {
   constexpr int HALF = D / 2, DB = D / 32;
   __shared__ int32_t cul[kRows + 2];
   const int lin = xcd_remap(blockIdx.x, gridDim.x);
@@ -265,11 +265,12 @@ __global__ __launch_bounds__(64, 2) void bwd_dq_f32_kernel(
 
   float qf[HALF], df[HALF];
   const int qsafe = qvalid ? qrow : r0;
-  const uint32_t HD = static_cast<uint32_t>(H) * D;
+  const uint32_t HD = static_cast<uint32_t>(H) * D;  // rows of dO
+  const uint32_t LD = static_cast<uint32_t>(ld);     // rows of Q, K, V and dQ
   const int64_t hoff = static_cast<int64_t>(h) * D;
-  auto at = [&](const float* p, int row) { return p + (static_cast<int64_t>(row) * HD + hoff); };
-  load_rows<D>(qf, at(qp, r0), qsafe - r0, HD, g);
-  load_rows<D>(df, at(dop, r0), qsafe - r0, HD, g);
+  auto at = [&](const float* p, int row, uint32_t stride) { return p + (static_cast<int64_t>(row) * stride + hoff); };
+  load_rows<D>(qf, at(qp, r0, LD), qsafe - r0, LD, g);
+  load_rows<D>(df, at(dop, r0, HD), qsafe - r0, HD, g);
   if (!qvalid) {
 #pragma unroll
     for (int i = 0; i < HALF; ++i) qf[i] = df[i] = 0.f;
@@ -284,9 +285,9 @@ __global__ __launch_bounds__(64, 2) void bwd_dq_f32_kernel(
   if (wk0 < wk1) {
     const int klast = wk1 - 1;
     float kr[HALF], vr[HALF], kt[16][DB];
-    load_rows<D>(kr, at(kp, wk0), min(ql, klast - wk0), HD, g);
-    load_rows<D>(vr, at(vp, wk0), min(ql, klast - wk0), HD, g);
-    load_tr<D>(kt, at(kp, wk0), klast - wk0, HD, ql, g);
+    load_rows<D>(kr, at(kp, wk0, LD), min(ql, klast - wk0), LD, g);
+    load_rows<D>(vr, at(vp, wk0, LD), min(ql, klast - wk0), LD, g);
+    load_tr<D>(kt, at(kp, wk0, LD), klast - wk0, LD, ql, g);
     for (int kb = wk0; kb < wk1; kb += 32) {
       const bool more = kb + 32 < wk1;
       floatx16 s = floatx16{}, dp = floatx16{};
@@ -296,8 +297,8 @@ __global__ __launch_bounds__(64, 2) void bwd_dq_f32_kernel(
         dp = __builtin_amdgcn_mfma_f32_32x32x2f32(vr[st], df[st], dp, 0, 0, 0);
       }
       if (more) {
-        load_rows<D>(kr, at(kp, kb + 32), min(ql, klast - kb - 32), HD, g);
-        load_rows<D>(vr, at(vp, kb + 32), min(ql, klast - kb - 32), HD, g);
+        load_rows<D>(kr, at(kp, kb + 32, LD), min(ql, klast - kb - 32), LD, g);
+        load_rows<D>(vr, at(vp, kb + 32, LD), min(ql, klast - kb - 32), LD, g);
       }
       if (!(kb >= mk0 && kb + 32 <= mk1)) {
         const int base = kb + 4 * g;
@@ -312,17 +313,17 @@ __global__ __launch_bounds__(64, 2) void bwd_dq_f32_kernel(
       for (int st = 0; st < 16; ++st)
 #pragma unroll
         for (int db = 0; db < DB; ++db) dq[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(kt[st][db], dp[st], dq[db], 0, 0, 0);
-      if (more) load_tr<D>(kt, at(kp, kb + 32), klast - kb - 32, HD, ql, g);
+      if (more) load_tr<D>(kt, at(kp, kb + 32, LD), klast - kb - 32, LD, ql, g);
     }
   }
-  if (qvalid) store_acc_row<false, D>(dqp, (static_cast<int64_t>(qrow) * H + h) * D, dq, scale, g);
+  if (qvalid) store_acc_row<false, D>(dqp, static_cast<int64_t>(qrow) * ld + hoff, dq, scale, g);
 }
 
 }  // namespace
 
 hipError_t launch_bwd_dq_f32_wave(int D, const void* dout, const void* q, const void* k, const void* v,
                                   const float* lse, const float* delta, const int32_t* cu, const int32_t* items32,
-                                  int32_t B, int32_t N, int32_t H, int32_t win, float scale, void* dq,
+                                  int32_t B, int32_t N, int32_t H, int32_t win, int64_t ld, float scale, void* dq,
                                   hipStream_t stream) {
   const int T = (N + kRows - 1) / kRows;
   const int64_t blocks = static_cast<int64_t>(T) * H;
@@ -333,11 +334,11 @@ hipError_t launch_bwd_dq_f32_wave(int D, const void* dout, const void* q, const 
   if (D == 32)
     hipLaunchKernelGGL((bwd_dq_f32_kernel<32>), gd, bd, 0, stream, static_cast<const float*>(dout),
                        static_cast<const float*>(q), static_cast<const float*>(k), static_cast<const float*>(v), lse,
-                       delta, cu, items32, B, N, H, T, win, c, scale, static_cast<float*>(dq));
+                       delta, cu, items32, B, N, H, T, win, ld, c, scale, static_cast<float*>(dq));
   else if (D == 64)
     hipLaunchKernelGGL((bwd_dq_f32_kernel<64>), gd, bd, 0, stream, static_cast<const float*>(dout),
                        static_cast<const float*>(q), static_cast<const float*>(k), static_cast<const float*>(v), lse,
-                       delta, cu, items32, B, N, H, T, win, c, scale, static_cast<float*>(dq));
+                       delta, cu, items32, B, N, H, T, win, ld, c, scale, static_cast<float*>(dq));
   else
     return hipErrorInvalidValue;
   timing_stop("bwd_dq", ev, stream);
@@ -362,7 +363,7 @@ __global__ __launch_bounds__(64, D > 32 ? 1 : 2) void bwd_dkdv_f32_kernel(
     const float* __restrict__ dop, const float* __restrict__ qp, const float* __restrict__ kp,
     const float* __restrict__ vp, const float* __restrict__ lse, const float* __restrict__ delta,
     const int32_t* __restrict__ cu, const int32_t* __restrict__ items, int32_t B, int32_t N, int32_t H, int32_t T,
-    int32_t win, float c, float scale, float* __restrict__ dkp, float* __restrict__ dvp) {
+    int32_t win, int64_t ld, float c, float scale, float* __restrict__ dkp, float* __restrict__ dvp) {
   constexpr int HALF = D / 2, DB = D / 32;
   __shared__ int32_t cul[kRows + 2];
   __shared__ __align__(16) float stat[2][kRows];
@@ -391,11 +392,12 @@ __global__ __launch_bounds__(64, D > 32 ? 1 : 2) void bwd_dkdv_f32_kernel(
 
   float kr[HALF], vr[HALF];
   const int ksafe = kvalid ? krow : r0;
-  const uint32_t HD = static_cast<uint32_t>(H) * D;
+  const uint32_t HD = static_cast<uint32_t>(H) * D;  // rows of dO
+  const uint32_t LD = static_cast<uint32_t>(ld);     // rows of Q, K, V, dK and dV
   const int64_t hoff = static_cast<int64_t>(h) * D;
-  auto at = [&](const float* p, int row) { return p + (static_cast<int64_t>(row) * HD + hoff); };
-  load_rows<D>(kr, at(kp, r0), ksafe - r0, HD, g);
-  load_rows<D>(vr, at(vp, r0), ksafe - r0, HD, g);
+  auto at = [&](const float* p, int row, uint32_t stride) { return p + (static_cast<int64_t>(row) * stride + hoff); };
+  load_rows<D>(kr, at(kp, r0, LD), ksafe - r0, LD, g);
+  load_rows<D>(vr, at(vp, r0, LD), ksafe - r0, LD, g);
 
   floatx16 dk[DB], dv[DB];
 #pragma unroll
@@ -407,8 +409,8 @@ __global__ __launch_bounds__(64, D > 32 ? 1 : 2) void bwd_dkdv_f32_kernel(
   for (int qb = wq0; qb < wq1; qb += 32) {
     const int qrow = min(qb + ql, qlast);
     float qr[HALF], dr[HALF];
-    load_rows<D>(qr, at(qp, qb), qrow - qb, HD, g);
-    load_rows<D>(dr, at(dop, qb), qrow - qb, HD, g);
+    load_rows<D>(qr, at(qp, qb, LD), qrow - qb, LD, g);
+    load_rows<D>(dr, at(dop, qb, HD), qrow - qb, HD, g);
     if (g == 0) {
       stat[0][ql] = lse_h[qrow] * kLog2e;
       stat[1][ql] = del_h[qrow];
@@ -420,8 +422,8 @@ __global__ __launch_bounds__(64, D > 32 ? 1 : 2) void bwd_dkdv_f32_kernel(
       dp = __builtin_amdgcn_mfma_f32_32x32x2f32(dr[st], vr[st], dp, 0, 0, 0);
     }
     float qt[16][DB], dt[16][DB];
-    load_tr<D>(qt, at(qp, qb), qlast - qb, HD, ql, g);
-    load_tr<D>(dt, at(dop, qb), qlast - qb, HD, ql, g);
+    load_tr<D>(qt, at(qp, qb, LD), qlast - qb, LD, ql, g);
+    load_tr<D>(dt, at(dop, qb, HD), qlast - qb, HD, ql, g);
     // rows of this block are queries qb + 8(i/4) + 4g + i%4; keep those inside the key's own sequence
     if (!(qb >= mq0 && qb + 32 <= mq1)) {
       const int base = qb + 4 * g;
@@ -451,7 +453,7 @@ __global__ __launch_bounds__(64, D > 32 ? 1 : 2) void bwd_dkdv_f32_kernel(
       }
   }
   if (kvalid) {
-    const int64_t off = (static_cast<int64_t>(krow) * H + h) * D;
+    const int64_t off = static_cast<int64_t>(krow) * ld + hoff;
     store_acc_row<false, D>(dkp, off, dk, scale, g);
     store_acc_row<false, D>(dvp, off, dv, 1.0f, g);
   }
@@ -461,8 +463,8 @@ __global__ __launch_bounds__(64, D > 32 ? 1 : 2) void bwd_dkdv_f32_kernel(
 
 hipError_t launch_bwd_dkdv_f32_wave(int D, const void* dout, const void* q, const void* k, const void* v,
                                     const float* lse, const float* delta, const int32_t* cu, const int32_t* items32,
-                                    int32_t B, int32_t N, int32_t H, int32_t win, float scale, void* dk, void* dv,
-                                    hipStream_t stream) {
+                                    int32_t B, int32_t N, int32_t H, int32_t win, int64_t ld, float scale, void* dk,
+                                    void* dv, hipStream_t stream) {
   const int T = (N + kRows - 1) / kRows;
   const int64_t blocks = static_cast<int64_t>(T) * H;
   if (blocks == 0) return hipSuccess;
@@ -472,11 +474,13 @@ hipError_t launch_bwd_dkdv_f32_wave(int D, const void* dout, const void* q, cons
   if (D == 32)
     hipLaunchKernelGGL((bwd_dkdv_f32_kernel<32>), gd, bd, 0, stream, static_cast<const float*>(dout),
                        static_cast<const float*>(q), static_cast<const float*>(k), static_cast<const float*>(v), lse,
-                       delta, cu, items32, B, N, H, T, win, c, scale, static_cast<float*>(dk), static_cast<float*>(dv));
+                       delta, cu, items32, B, N, H, T, win, ld, c, scale, static_cast<float*>(dk),
+                       static_cast<float*>(dv));
   else if (D == 64)
     hipLaunchKernelGGL((bwd_dkdv_f32_kernel<64>), gd, bd, 0, stream, static_cast<const float*>(dout),
                        static_cast<const float*>(q), static_cast<const float*>(k), static_cast<const float*>(v), lse,
-                       delta, cu, items32, B, N, H, T, win, c, scale, static_cast<float*>(dk), static_cast<float*>(dv));
+                       delta, cu, items32, B, N, H, T, win, ld, c, scale, static_cast<float*>(dk),
+                       static_cast<float*>(dv));
   else
     return hipErrorInvalidValue;
   timing_stop("bwd_dkdv", ev, stream);

@@ -27,7 +27,7 @@ template <bool BF, int D>
 __global__ __launch_bounds__(kFbThreads) void attn_bwd_first_kernel(
     const void* __restrict__ dof, const void* __restrict__ qf, const void* __restrict__ kp,
     const void* __restrict__ vp, const void* __restrict__ of, const float* __restrict__ lse,
-    const int32_t* __restrict__ cu, int32_t B, int32_t N, int32_t H, int32_t HPB, float c, float scale,
+    const int32_t* __restrict__ cu, int32_t B, int32_t N, int32_t H, int32_t HPB, int64_t ld, float c, float scale,
     void* __restrict__ dqp, void* __restrict__ dkp, void* __restrict__ dvp) {
   constexpr int ES = BF ? 2 : 4;
   constexpr int EPC = 16 / ES;  // elements per 16-byte chunk
@@ -86,7 +86,7 @@ __global__ __launch_bounds__(kFbThreads) void attn_bwd_first_kernel(
     const char* vb = static_cast<const char*>(vp) + hoff * ES;
     char* dkb = static_cast<char*>(dkp) + hoff * ES;
     char* dvb = static_cast<char*>(dvp) + hoff * ES;
-    const int64_t rs = static_cast<int64_t>(H) * D * ES;  // bytes per packed row
+    const int64_t rs = ld * ES;  // bytes between rows of K, V, dK, dV
     for (int j0 = c0 + slot; j0 < c1; j0 += U * KS) {
       Chunk xk[U], xv[U];
 #pragma unroll
@@ -149,15 +149,15 @@ __global__ __launch_bounds__(kFbThreads) void attn_bwd_first_kernel(
 
 template <bool BF, int D>
 hipError_t bwd_first_dispatch(const void* dof, const void* qf, const void* k, const void* v, const void* of,
-                              const float* lse, const int32_t* cu, int32_t B, int32_t N, int32_t H, float scale,
-                              void* dq, void* dk, void* dv, hipStream_t stream) {
+                              const float* lse, const int32_t* cu, int32_t B, int32_t N, int32_t H, int64_t ld,
+                              float scale, void* dq, void* dk, void* dv, hipStream_t stream) {
   constexpr int GS = D / (BF ? 8 : 4);
   const int HPB = (H * GS <= kFbThreads) ? H : kFbThreads / GS;
   const int HG = (H + HPB - 1) / HPB;
   const float c = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
   hipEvent_t ev = timing_start(stream);
   hipLaunchKernelGGL((attn_bwd_first_kernel<BF, D>), dim3(B, HG), dim3(kFbThreads), 0, stream, dof, qf, k, v, of,
-                     lse, cu, B, N, H, HPB, c, scale, dq, dk, dv);
+                     lse, cu, B, N, H, HPB, ld, c, scale, dq, dk, dv);
   timing_stop("attn_bwd_first", ev, stream);
   return hipGetLastError();
 }
@@ -166,13 +166,13 @@ hipError_t bwd_first_dispatch(const void* dof, const void* qf, const void* k, co
 
 hipError_t launch_attn_bwd_first(bool bf16, int D, const void* dout_first, const void* q_first, const void* k,
                                  const void* v, const void* out_first, const float* lse_first, const int32_t* cu,
-                                 int32_t B, int32_t N, int32_t H, float scale, void* dq_first, void* dk, void* dv,
-                                 hipStream_t stream) {
+                                 int32_t B, int32_t N, int32_t H, int64_t ld, float scale, void* dq_first, void* dk,
+                                 void* dv, hipStream_t stream) {
 #define PE_BF_CASE(DD)                                                                                         \
   case DD:                                                                                                    \
-    return bf16 ? bwd_first_dispatch<true, DD>(dout_first, q_first, k, v, out_first, lse_first, cu, B, N, H,  \
-                                               scale, dq_first, dk, dv, stream)                               \
-                : bwd_first_dispatch<false, DD>(dout_first, q_first, k, v, out_first, lse_first, cu, B, N, H, \
+    return bf16 ? bwd_first_dispatch<true, DD>(dout_first, q_first, k, v, out_first, lse_first, cu, B, N, H, ld,  \
+                                               scale, dq_first, dk, dv, stream)                                   \
+                : bwd_first_dispatch<false, DD>(dout_first, q_first, k, v, out_first, lse_first, cu, B, N, H, ld, \
                                                 scale, dq_first, dk, dv, stream);
   switch (D) {
     PE_BF_CASE(8)

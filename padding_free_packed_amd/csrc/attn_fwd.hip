@@ -26,7 +26,7 @@ template <bool BF, int D>
 __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
     const void* __restrict__ qp, const void* __restrict__ kp, const void* __restrict__ vp,
     const int32_t* __restrict__ cu, const int32_t* __restrict__ items, int32_t B, int32_t N,
-    int32_t H, int32_t T, int32_t win, float c, void* __restrict__ op, float* __restrict__ lse) {
+    int32_t H, int32_t T, int32_t win, int64_t ld, float c, void* __restrict__ op, float* __restrict__ lse) {
   using G = Geo<BF, D>;
   using E = typename G::E;
   // bf16 tiles with whole 16-byte chunks per lane half use the XOR-swizzled layout
@@ -58,7 +58,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
   const int mk1 = wave_min_i(qvalid ? qk1 : INT_MAX);
 
   typename RegT<BF>::T qr[G::QS];
-  load_row_regs<BF, D>(qp, (static_cast<int64_t>(qrow) * H + h) * D + g * G::HALF, qvalid, qr);
+  load_row_regs<BF, D>(qp, static_cast<int64_t>(qrow) * ld + h * D + g * G::HALF, qvalid, qr);
 
   uint4 kr[G::PER], vr[G::PER];
   floatx16 o[G::DB];
@@ -71,8 +71,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
   const int khi = win >= 0 ? min(sp.hi, sp.rend + win) : sp.hi;
   int buf = 0;
   if (klo < khi) {
-    tile_gload<BF, D>(kp, klo, khi, H, h, kr);
-    tile_gload<BF, D>(vp, klo, khi, H, h, vr);
+    tile_gload<BF, D>(kp, klo, khi, ld, h, kr);
+    tile_gload<BF, D>(vp, klo, khi, ld, h, vr);
   }
   for (int kb = klo; kb < khi; kb += kBlk) {
     if constexpr (SWZ) {
@@ -84,8 +84,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
     }
     __syncthreads();
     if (kb + kBlk < khi) {
-      tile_gload<BF, D>(kp, kb + kBlk, khi, H, h, kr);
-      tile_gload<BF, D>(vp, kb + kBlk, khi, H, h, vr);
+      tile_gload<BF, D>(kp, kb + kBlk, khi, ld, h, kr);
+      tile_gload<BF, D>(vp, kb + kBlk, khi, ld, h, vr);
     }
     if (kb < wk1 && kb + kBlk > wk0) {
       floatx16 s[2];
@@ -162,8 +162,8 @@ constexpr int kFirstBatch = 4;
 template <bool BF, int D>
 __global__ __launch_bounds__(kFirstThreads) void attn_fwd_first_kernel(
     const void* __restrict__ qf, const void* __restrict__ kp, const void* __restrict__ vp,
-    const int32_t* __restrict__ cu, int32_t B, int32_t N, int32_t H, int32_t HPB, int32_t gather, float c,
-    void* __restrict__ outp, float* __restrict__ lse) {
+    const int32_t* __restrict__ cu, int32_t B, int32_t N, int32_t H, int32_t HPB, int32_t gather, int64_t ld,
+    float c, void* __restrict__ outp, float* __restrict__ lse) {
   constexpr int ES = BF ? 2 : 4;
   constexpr int EPC = 16 / ES;       // elements per 16-byte chunk
   constexpr int GS = D / EPC;        // chunks (threads) per head row
@@ -197,12 +197,12 @@ __global__ __launch_bounds__(kFirstThreads) void attn_fwd_first_kernel(
   };
   if (active) {
     const int64_t hoff = static_cast<int64_t>(h) * D + sub * EPC;
-    // the query is row b of q_first [B, H, D], or (gather) row cu[b] of the packed Q [N, H, D]
-    const int64_t qrow = gather ? c0 : b;
-    widen(*reinterpret_cast<const Chunk*>(static_cast<const char*>(qf) + (qrow * H * D + hoff) * ES), qv);
+    // the query is row b of q_first [B, H, D], or (gather) row cu[b] of the packed Q (rows ld apart)
+    const int64_t qoff = gather ? static_cast<int64_t>(c0) * ld : static_cast<int64_t>(b) * H * D;
+    widen(*reinterpret_cast<const Chunk*>(static_cast<const char*>(qf) + (qoff + hoff) * ES), qv);
     const char* kb = static_cast<const char*>(kp) + hoff * ES;
     const char* vb = static_cast<const char*>(vp) + hoff * ES;
-    const int64_t rs = static_cast<int64_t>(H) * D * ES;  // bytes per packed row
+    const int64_t rs = ld * ES;  // bytes between packed K/V rows
     for (int j0 = c0 + slot; j0 < c1; j0 += U * KS) {
       Chunk xk[U], xv[U];
 #pragma unroll
@@ -277,22 +277,22 @@ __global__ __launch_bounds__(kFirstThreads) void attn_fwd_first_kernel(
 
 template <bool BF, int D>
 hipError_t fwd_dispatch(const void* q, const void* k, const void* v, const int32_t* cu,
-                        const int32_t* items, int32_t B, int32_t N, int32_t H, int32_t win, float scale, void* out,
-                        float* lse, hipStream_t stream) {
+                        const int32_t* items, int32_t B, int32_t N, int32_t H, int32_t win, int64_t ld,
+                        float scale, void* out, float* lse, hipStream_t stream) {
   const int T = (N + kAttnTileRows - 1) / kAttnTileRows;
   const int64_t blocks = static_cast<int64_t>(T) * H;
   if (blocks == 0) return hipSuccess;
   const float c = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
   hipEvent_t ev_attn_fwd = timing_start(stream);
   hipLaunchKernelGGL((attn_fwd_kernel<BF, D>), dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0, stream,
-                   q, k, v, cu, items, B, N, H, T, win, c, out, lse);
+                   q, k, v, cu, items, B, N, H, T, win, ld, c, out, lse);
   timing_stop("attn_fwd", ev_attn_fwd, stream);
   return hipGetLastError();
 }
 
 template <bool BF, int D>
 hipError_t first_dispatch(const void* q, const void* k, const void* v, const int32_t* cu, int32_t B,
-                          int32_t N, int32_t H, int32_t gather, float scale, void* out, float* lse,
+                          int32_t N, int32_t H, int32_t gather, int64_t ld, float scale, void* out, float* lse,
                           hipStream_t stream) {
   constexpr int GS = D / (BF ? 8 : 4);
   const int HPB = (H * GS <= kFirstThreads) ? H : kFirstThreads / GS;
@@ -300,7 +300,7 @@ hipError_t first_dispatch(const void* q, const void* k, const void* v, const int
   const float c = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
   hipEvent_t ev_attn_fwd_first = timing_start(stream);
   hipLaunchKernelGGL((attn_fwd_first_kernel<BF, D>), dim3(B, HG), dim3(kFirstThreads), 0, stream, q, k, v, cu, B,
-                   N, H, HPB, gather, c, out, lse);
+                   N, H, HPB, gather, ld, c, out, lse);
   timing_stop("attn_fwd_first", ev_attn_fwd_first, stream);
   return hipGetLastError();
 }
@@ -309,17 +309,17 @@ hipError_t first_dispatch(const void* q, const void* k, const void* v, const int
 
 hipError_t launch_attn_fwd(bool bf16, int D, const void* q, const void* k, const void* v,
                            const int32_t* cu, const int32_t* items, int32_t B, int32_t N, int32_t H,
-                           int32_t max_seq_len, int32_t win, float scale, void* out, float* lse,
+                           int32_t max_seq_len, int32_t win, int64_t ld, float scale, void* out, float* lse,
                            hipStream_t stream) {
   if (bf16 && attn_fwd_bf16_supported(D, max_seq_len)) {
     if (attn_fwd_bf16_w64_supported(D))
-      return launch_attn_fwd_bf16_w64(D, q, k, v, cu, items, B, N, H, win, scale, out, lse, stream);
-    return launch_attn_fwd_bf16(D, q, k, v, cu, items, B, N, H, win, scale, out, lse, stream);
+      return launch_attn_fwd_bf16_w64(D, q, k, v, cu, items, B, N, H, win, ld, scale, out, lse, stream);
+    return launch_attn_fwd_bf16(D, q, k, v, cu, items, B, N, H, win, ld, scale, out, lse, stream);
   }
 #define PE_FWD_CASE(DD)                                                                      \
   case DD:                                                                                  \
-    return bf16 ? fwd_dispatch<true, DD>(q, k, v, cu, items, B, N, H, win, scale, out, lse, stream) \
-                : fwd_dispatch<false, DD>(q, k, v, cu, items, B, N, H, win, scale, out, lse, stream);
+    return bf16 ? fwd_dispatch<true, DD>(q, k, v, cu, items, B, N, H, win, ld, scale, out, lse, stream) \
+                : fwd_dispatch<false, DD>(q, k, v, cu, items, B, N, H, win, ld, scale, out, lse, stream);
   switch (D) {
     PE_FWD_CASE(8)
     PE_FWD_CASE(16)
@@ -332,13 +332,13 @@ hipError_t launch_attn_fwd(bool bf16, int D, const void* q, const void* k, const
 }
 
 hipError_t launch_attn_fwd_first(bool bf16, int D, const void* q_first, const void* k, const void* v,
-                                 const int32_t* cu, int32_t B, int32_t N, int32_t H, int32_t gather, float scale,
-                                 void* out_first, float* lse_first, hipStream_t stream) {
+                                 const int32_t* cu, int32_t B, int32_t N, int32_t H, int32_t gather, int64_t ld,
+                                 float scale, void* out_first, float* lse_first, hipStream_t stream) {
 #define PE_FIRST_CASE(DD)                                                                          \
   case DD:                                                                                        \
-    return bf16 ? first_dispatch<true, DD>(q_first, k, v, cu, B, N, H, gather, scale, out_first, lse_first,  \
-                                           stream)                                                          \
-                : first_dispatch<false, DD>(q_first, k, v, cu, B, N, H, gather, scale, out_first, lse_first, \
+    return bf16 ? first_dispatch<true, DD>(q_first, k, v, cu, B, N, H, gather, ld, scale, out_first, lse_first, \
+                                           stream)                                                              \
+                : first_dispatch<false, DD>(q_first, k, v, cu, B, N, H, gather, ld, scale, out_first, lse_first, \
                                             stream);
   switch (D) {
     PE_FIRST_CASE(8)

@@ -32,7 +32,7 @@ template <int D>
 __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
     const void* __restrict__ qp, const void* __restrict__ kp, const void* __restrict__ vp,
     const int32_t* __restrict__ cu, const int32_t* __restrict__ items, int32_t B, int32_t N, int32_t H,
-    int32_t T, int32_t win, float c, void* __restrict__ op, float* __restrict__ lse) {
+    int32_t T, int32_t win, int64_t ld, float c, void* __restrict__ op, float* __restrict__ lse) {
   constexpr int CH = D / 8;           // 16-byte chunks per row
   constexpr int TB = kBlk * D * 2;    // bytes per tile
   constexpr int QS = D / 16;          // MFMA steps over head_dim
@@ -62,13 +62,13 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
   const int khi = __builtin_amdgcn_readfirstlane(win >= 0 ? min(sp.hi, sp.rend + win) : sp.hi);
 
   bf16x8 qr[QS];
-  load_row_regs<true, D>(qp, (static_cast<int64_t>(qrow) * H + h) * D + g * (D / 2), qvalid, qr);
+  load_row_regs<true, D>(qp, static_cast<int64_t>(qrow) * ld + h * D + g * (D / 2), qvalid, qr);
   // Retire the Q loads with a wait the compiler sees: otherwise it places a
   // vmcnt wait for them inside the loop, which would also drain the DMA ring.
   vmem_fence_for_compiler();
 
   // ---- DMA: per-lane source offsets relative to the block's first row
-  const int rowstride = H * D * 2;
+  const int64_t rowstride = ld * 2;  // bytes between packed K/V rows
   uint32_t doff[NL];
 #pragma unroll
   for (int j = 0; j < NL; ++j) {
@@ -233,7 +233,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
 
 template <int D>
 hipError_t dispatch(const void* q, const void* k, const void* v, const int32_t* cu, const int32_t* items,
-                    int32_t B, int32_t N, int32_t H, int32_t win, float scale, void* out, float* lse,
+                    int32_t B, int32_t N, int32_t H, int32_t win, int64_t ld, float scale, void* out, float* lse,
                     hipStream_t stream) {
   const int T = (N + kAttnTileRows - 1) / kAttnTileRows;
   const int64_t blocks = static_cast<int64_t>(T) * H;
@@ -241,7 +241,7 @@ hipError_t dispatch(const void* q, const void* k, const void* v, const int32_t* 
   const float c = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
   hipEvent_t ev = timing_start(stream);
   hipLaunchKernelGGL((attn_fwd_bf16_kernel<D>), dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0, stream, q,
-                     k, v, cu, items, B, N, H, T, win, c, out, lse);
+                     k, v, cu, items, B, N, H, T, win, ld, c, out, lse);
   timing_stop("attn_fwd", ev, stream);
   return hipGetLastError();
 }
@@ -256,12 +256,12 @@ bool attn_fwd_bf16_supported(int D, int max_seq_len) {
 }
 
 hipError_t launch_attn_fwd_bf16(int D, const void* q, const void* k, const void* v, const int32_t* cu,
-                                const int32_t* items, int32_t B, int32_t N, int32_t H, int32_t win, float scale,
-                                void* out, float* lse, hipStream_t stream) {
+                                const int32_t* items, int32_t B, int32_t N, int32_t H, int32_t win, int64_t ld,
+                                float scale, void* out, float* lse, hipStream_t stream) {
   switch (D) {
-    case 32: return dispatch<32>(q, k, v, cu, items, B, N, H, win, scale, out, lse, stream);
-    case 64: return dispatch<64>(q, k, v, cu, items, B, N, H, win, scale, out, lse, stream);
-    case 128: return dispatch<128>(q, k, v, cu, items, B, N, H, win, scale, out, lse, stream);
+    case 32: return dispatch<32>(q, k, v, cu, items, B, N, H, win, ld, scale, out, lse, stream);
+    case 64: return dispatch<64>(q, k, v, cu, items, B, N, H, win, ld, scale, out, lse, stream);
+    case 128: return dispatch<128>(q, k, v, cu, items, B, N, H, win, ld, scale, out, lse, stream);
     default: return hipErrorInvalidValue;
   }
 }

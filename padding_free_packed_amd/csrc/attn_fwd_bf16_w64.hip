@@ -43,7 +43,7 @@ template <int D>
 __global__ __launch_bounds__(kW64Threads) __attribute__((amdgpu_waves_per_eu(2))) void attn_fwd_bf16_w64_kernel(
     const void* __restrict__ qp, const void* __restrict__ kp, const void* __restrict__ vp,
     const int32_t* __restrict__ cu, const int32_t* __restrict__ items, int32_t B, int32_t N, int32_t H,
-    int32_t T, int32_t win, float c, void* __restrict__ op, float* __restrict__ lse) {
+    int32_t T, int32_t win, int64_t ld, float c, void* __restrict__ op, float* __restrict__ lse) {
   constexpr int CH = D / 8;                    // 16-byte chunks per row
   constexpr int TB = kW64Keys * D * 2;         // bytes per tile
   constexpr int QS = D / 16;                   // MFMA steps over head_dim
@@ -82,12 +82,12 @@ __global__ __launch_bounds__(kW64Threads) __attribute__((amdgpu_waves_per_eu(2))
   bf16x8 qr[2][QS];
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb)
-    load_row_regs<true, D>(qp, (static_cast<int64_t>(qrow[qb]) * H + h) * D + g * (D / 2), qvalid[qb], qr[qb]);
+    load_row_regs<true, D>(qp, static_cast<int64_t>(qrow[qb]) * ld + h * D + g * (D / 2), qvalid[qb], qr[qb]);
   // retire the Q loads with a wait the compiler sees, so none lands inside the DMA loop
   vmem_fence_for_compiler();
 
   // ---- DMA: per-lane source offsets relative to the tile's first row
-  const int rowstride = H * D * 2;
+  const int64_t rowstride = ld * 2;  // bytes between packed K/V rows
   uint32_t doff[NL];
 #pragma unroll
   for (int j = 0; j < NL; ++j) {
@@ -250,15 +250,15 @@ __global__ __launch_bounds__(kW64Threads) __attribute__((amdgpu_waves_per_eu(2))
 
 template <int D>
 hipError_t dispatch_w64(const void* q, const void* k, const void* v, const int32_t* cu, const int32_t* items,
-                        int32_t B, int32_t N, int32_t H, int32_t win, float scale, void* out, float* lse,
-                        hipStream_t stream) {
+                        int32_t B, int32_t N, int32_t H, int32_t win, int64_t ld, float scale, void* out,
+                        float* lse, hipStream_t stream) {
   const int T = (N + kAttnTileRows - 1) / kAttnTileRows;
   const int64_t blocks = static_cast<int64_t>(T) * H;
   if (blocks == 0) return hipSuccess;
   const float c = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
   hipEvent_t ev = timing_start(stream);
   hipLaunchKernelGGL((attn_fwd_bf16_w64_kernel<D>), dim3(static_cast<unsigned>(blocks)), dim3(kW64Threads), 0,
-                     stream, q, k, v, cu, items, B, N, H, T, win, c, out, lse);
+                     stream, q, k, v, cu, items, B, N, H, T, win, ld, c, out, lse);
   timing_stop("attn_fwd", ev, stream);
   return hipGetLastError();
 }
@@ -268,11 +268,11 @@ hipError_t dispatch_w64(const void* q, const void* k, const void* v, const int32
 bool attn_fwd_bf16_w64_supported(int D) { return D == 32 || D == 64; }
 
 hipError_t launch_attn_fwd_bf16_w64(int D, const void* q, const void* k, const void* v, const int32_t* cu,
-                                    const int32_t* items, int32_t B, int32_t N, int32_t H, int32_t win, float scale,
-                                    void* out, float* lse, hipStream_t stream) {
+                                    const int32_t* items, int32_t B, int32_t N, int32_t H, int32_t win, int64_t ld,
+                                    float scale, void* out, float* lse, hipStream_t stream) {
   switch (D) {
-    case 32: return dispatch_w64<32>(q, k, v, cu, items, B, N, H, win, scale, out, lse, stream);
-    case 64: return dispatch_w64<64>(q, k, v, cu, items, B, N, H, win, scale, out, lse, stream);
+    case 32: return dispatch_w64<32>(q, k, v, cu, items, B, N, H, win, ld, scale, out, lse, stream);
+    case 64: return dispatch_w64<64>(q, k, v, cu, items, B, N, H, win, ld, scale, out, lse, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -28,54 +28,58 @@ hipError_t launch_unpack_rows(const void* packed, void* grid, const int32_t* cu,
 // Forward over tiles of kAttnTileRows packed query rows; items from launch_worklist.
 hipError_t launch_attn_fwd(bool bf16, int D, const void* q, const void* k, const void* v,
                            const int32_t* cu, const int32_t* items, int32_t B, int32_t N, int32_t H,
-                           int32_t max_seq_len, int32_t win, float scale, void* out, float* lse, hipStream_t stream);
+                           int32_t max_seq_len, int32_t win, int64_t ld, float scale, void* out, float* lse,
+                           hipStream_t stream);
 
 // bf16 forward with LDS-DMA staging (head dims 32, 64, 128).
 bool attn_fwd_bf16_supported(int D, int max_seq_len);
 // the same items with two 64-row waves per block (head dims 32, 64)
 bool attn_fwd_bf16_w64_supported(int D);
 hipError_t launch_attn_fwd_bf16_w64(int D, const void* q, const void* k, const void* v, const int32_t* cu,
-                                    const int32_t* items, int32_t B, int32_t N, int32_t H, int32_t win, float scale,
-                                    void* out, float* lse, hipStream_t stream);
+                                    const int32_t* items, int32_t B, int32_t N, int32_t H, int32_t win, int64_t ld,
+                                    float scale, void* out, float* lse, hipStream_t stream);
 hipError_t launch_attn_fwd_bf16(int D, const void* q, const void* k, const void* v, const int32_t* cu,
-                                const int32_t* items, int32_t B, int32_t N, int32_t H, int32_t win, float scale,
-                                void* out, float* lse, hipStream_t stream);
+                                const int32_t* items, int32_t B, int32_t N, int32_t H, int32_t win, int64_t ld,
+                                float scale, void* out, float* lse, hipStream_t stream);
 
 // fp32 forward, one independent wave per 32 query rows (head dims 32, 64);
 // items32 is the work list with tile height kAttnWaveRows.
 bool attn_fwd_f32_wave_supported(int D);
 hipError_t launch_attn_fwd_f32_wave(int D, const void* q, const void* k, const void* v, const int32_t* cu,
-                                    const int32_t* items32, int32_t B, int32_t N, int32_t H, int32_t win, float scale,
-                                    void* out, float* lse, hipStream_t stream);
+                                    const int32_t* items32, int32_t B, int32_t N, int32_t H, int32_t win, int64_t ld,
+                                    float scale, void* out, float* lse, hipStream_t stream);
 
 // fp32 dK/dV and dQ, one independent wave per 32 key (query) rows (head dims 32, 64)
 hipError_t launch_bwd_dkdv_f32_wave(int D, const void* dout, const void* q, const void* k, const void* v,
                                     const float* lse, const float* delta, const int32_t* cu, const int32_t* items32,
-                                    int32_t B, int32_t N, int32_t H, int32_t win, float scale, void* dk, void* dv,
-                                    hipStream_t stream);
+                                    int32_t B, int32_t N, int32_t H, int32_t win, int64_t ld, float scale, void* dk,
+                                    void* dv, hipStream_t stream);
 hipError_t launch_bwd_dq_f32_wave(int D, const void* dout, const void* q, const void* k, const void* v,
                                   const float* lse, const float* delta, const int32_t* cu, const int32_t* items32,
-                                  int32_t B, int32_t N, int32_t H, int32_t win, float scale, void* dq,
+                                  int32_t B, int32_t N, int32_t H, int32_t win, int64_t ld, float scale, void* dq,
                                   hipStream_t stream);
 
 // gather = 0: q_first is [B, H, D]; gather = 1: the query of sequence b is row cu[b] of a packed [N, H, D]
 hipError_t launch_attn_fwd_first(bool bf16, int D, const void* q_first, const void* k, const void* v,
-                                 const int32_t* cu, int32_t B, int32_t N, int32_t H, int32_t gather, float scale,
-                                 void* out_first, float* lse_first, hipStream_t stream);
+                                 const int32_t* cu, int32_t B, int32_t N, int32_t H, int32_t gather, int64_t ld,
+                                 float scale, void* out_first, float* lse_first, hipStream_t stream);
 // backward of the first-token readout: dq_first [B, H, D], dk and dv [N, H, D] (every row written)
 hipError_t launch_attn_bwd_first(bool bf16, int D, const void* dout_first, const void* q_first, const void* k,
                                  const void* v, const void* out_first, const float* lse_first, const int32_t* cu,
-                                 int32_t B, int32_t N, int32_t H, float scale, void* dq_first, void* dk, void* dv,
-                                 hipStream_t stream);
+                                 int32_t B, int32_t N, int32_t H, int64_t ld, float scale, void* dq_first, void* dk,
+                                 void* dv, hipStream_t stream);
 
 // Backward: D = rowsum(dO * O) per (head, row), then dK/dV over key tiles, then dQ over query tiles.
 // items: work list with tile height kAttnTileRows; items32: with kAttnWaveRows (or NULL).
 // win: local attention radius (keys with |i - j| <= win), or -1 for global attention;
-// every attention launcher takes it.
+// ld: elements between consecutive rows of Q, K, V (and of dQ, dK, dV): num_heads * D for
+// separate [N, H, D] tensors, 3 * num_heads * D for a fused [N, 3, H, D] buffer. O, dO,
+// LSE and D keep their own dense layouts. Every attention launcher takes both.
 hipError_t launch_attn_bwd(bool bf16, int D, const void* dout, const void* q, const void* k,
                            const void* v, const void* out, const float* lse, const int32_t* cu,
                            const int32_t* items, const int32_t* items32, int32_t B, int32_t N, int32_t H,
-                           int32_t win, float scale, void* dq, void* dk, void* dv, float* delta, hipStream_t stream);
+                           int32_t win, int64_t ld, float scale, void* dq, void* dk, void* dv, float* delta,
+                           hipStream_t stream);
 
 // packing metadata (meta.hip)
 hipError_t launch_ids(const int32_t* cu, int32_t B, int64_t N, int64_t* pos, int32_t* doc, hipStream_t stream);

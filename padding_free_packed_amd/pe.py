@@ -27,7 +27,8 @@ EXPORTS = (
     "pe_worklist", "pe_attn_workspace_size", "pe_varlen_attn_fwd", "pe_varlen_attn_fwd_first_token",
     "pe_varlen_attn_bwd", "pe_varlen_attn_fwd_local", "pe_varlen_attn_bwd_local", "pe_varlen_attn_fwd_first_row",
     "pe_varlen_attn_bwd_first_token", "pe_position_ids", "pe_flatten_workspace_size", "pe_flatten_packed_metadata",
-    "pe_flatten_document_mask", "pe_gather_rows", "pe_scatter_rows", "pe_timing_enable", "pe_timing_read",
+    "pe_flatten_document_mask", "pe_gather_rows", "pe_scatter_rows", "pe_varlen_attn_fwd_qkv",
+    "pe_varlen_attn_bwd_qkv", "pe_timing_enable", "pe_timing_read",
 )
 
 
@@ -72,6 +73,10 @@ def _load():
         "pe_flatten_document_mask": (ctypes.c_int, [P, I32, I32, P, P, I64, I64, P, P, P, SZ, P]),
         "pe_gather_rows": (ctypes.c_int, [P, I64, P, I64, I64, ctypes.c_int, P, P]),
         "pe_scatter_rows": (ctypes.c_int, [P, P, I64, I64, ctypes.c_int, P, I64, P]),
+        "pe_varlen_attn_fwd_qkv": (ctypes.c_int, [P, P, I32, I64, I32, I32, I32, ctypes.c_int, F, I32, P, P, P,
+                                                   SZ, P]),
+        "pe_varlen_attn_bwd_qkv": (ctypes.c_int, [P, P, P, P, P, I32, I64, I32, I32, I32, ctypes.c_int, F, I32, P,
+                                                   P, SZ, P]),
         "pe_timing_enable": (ctypes.c_int, [ctypes.c_int]),
         "pe_timing_read": (ctypes.c_int, [P, P, ctypes.c_int]),
     }
@@ -218,6 +223,27 @@ def pe_varlen_attn_bwd_local(dout, q, k, v, out, lse, cu_seqlens, num_seqs, tota
                                        _dtype_code(q), softmax_scale, window, _ptr(dq), _ptr(dk), _ptr(dv),
                                        _ptr(workspace), workspace.numel(), _stream())
     _check("pe_varlen_attn_bwd_local", st)
+
+
+def pe_varlen_attn_fwd_qkv(qkv, cu_seqlens, num_seqs, total_tokens, max_seq_len, softmax_scale, window, out, lse,
+                           workspace):
+    """qkv [N, 3, H, d] (fused projection rows); window -1 for global attention."""
+    N, three, H, d = qkv.shape
+    assert three == 3 and qkv.is_contiguous()
+    st = _lib.pe_varlen_attn_fwd_qkv(_ptr(qkv), _ptr(cu_seqlens), num_seqs, total_tokens, max_seq_len, H, d,
+                                     _dtype_code(qkv), softmax_scale, window, _ptr(out), _ptr(lse), _ptr(workspace),
+                                     workspace.numel(), _stream())
+    _check("pe_varlen_attn_fwd_qkv", st)
+
+
+def pe_varlen_attn_bwd_qkv(dout, qkv, out, lse, cu_seqlens, num_seqs, total_tokens, max_seq_len, softmax_scale,
+                           window, dqkv, workspace):
+    N, three, H, d = qkv.shape
+    assert three == 3 and qkv.is_contiguous() and dqkv.is_contiguous()
+    st = _lib.pe_varlen_attn_bwd_qkv(_ptr(dout), _ptr(qkv), _ptr(out), _ptr(lse), _ptr(cu_seqlens), num_seqs,
+                                     total_tokens, max_seq_len, H, d, _dtype_code(qkv), softmax_scale, window,
+                                     _ptr(dqkv), _ptr(workspace), workspace.numel(), _stream())
+    _check("pe_varlen_attn_bwd_qkv", st)
 
 
 # ------------------------------------------------------------------ packing metadata

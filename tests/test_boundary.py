@@ -27,7 +27,7 @@ def _header_functions():
 
 def test_header_symbols_exported():
     names = _header_functions()
-    assert len(names) == 22
+    assert len(names) == 24
     for n in names:
         assert hasattr(lib, n), n
     assert sorted(pe.EXPORTS) == names
@@ -134,6 +134,26 @@ def test_metadata_calls_reject():
     assert lib.pe_gather_rows(P, 4, P, 4, 16, 7, P, None) == pe.PE_ERR_UNSUPPORTED
     assert lib.pe_scatter_rows(P, NUL, 4, 16, 0, P, 4, None) == pe.PE_ERR_NULL
     assert lib.pe_scatter_rows(P, P, 4, 16, 0, P, -1, None) == pe.PE_ERR_ARG
+
+
+def test_qkv_rejects():
+    f = lib.pe_varlen_attn_fwd_qkv
+    ok = [P, P, 4, 100, 64, 2, 64, 0, 0.125, -1, P, NUL, P, 1 << 20, None]
+    a = list(ok); a[0] = NUL
+    assert f(*a) == pe.PE_ERR_NULL
+    a = list(ok); a[9] = -2
+    assert f(*a) == pe.PE_ERR_ARG
+    a = list(ok); a[6] = 20
+    assert f(*a) == pe.PE_ERR_UNSUPPORTED
+    a = list(ok); a[13] = 8
+    assert f(*a) == pe.PE_ERR_WORKSPACE
+    b = lib.pe_varlen_attn_bwd_qkv
+    okb = [P, P, P, P, P, 4, 100, 64, 2, 64, 0, 0.125, 3, P, P, 1 << 20, None]
+    for i in (0, 1, 2, 3, 4, 13):
+        a = list(okb); a[i] = NUL
+        assert b(*a) == pe.PE_ERR_NULL, i
+    a = list(okb); a[12] = -7
+    assert b(*a) == pe.PE_ERR_ARG
 
 
 def test_local_rejects():
