@@ -105,6 +105,30 @@ pe_status pe_pack(const int32_t* lengths, int32_t num_seqs, int32_t max_seq_len,
                   int32_t* cu_seqlens, int64_t* flat_index, void* packed, int64_t capacity,
                   int64_t* h_total_tokens, void* workspace, size_t workspace_bytes, void* stream);
 
+/* ------------------------------------------------------- pack without host read
+ * pe_pack_async: pe_pack with no host read, so that a stream capture can record
+ * it (the launch-bound short-batch case, where the packed-encoders README runs
+ * the whole forward as one graph replay over fixed (batch, length) buckets).
+ *
+ * Source: as pe_pack; packed-encoders README, "CUDA graphs" (bucketed runner
+ * over padded shapes, explicit batch and sequence bounds for packed graphs).
+ *
+ * Same layout as pe_pack. The token count stays on the device:
+ *   status   device int64 [2], written: status[0] = N = sum of the lengths,
+ *            status[1] = 0 (ok), 1 (a length outside [1, max_seq_len]) or
+ *            2 (N > capacity)
+ * On status[1] != 0 cu_seqlens is all zeros (a batch of empty sequences, which
+ * every kernel queued behind reads as "no rows") and flat_index and packed are
+ * untouched; nothing reads or writes out of bounds whatever the lengths.
+ * `capacity` (rows of flat_index / packed) may be any value >= 0; the copy
+ * kernels are sized for min(capacity, num_seqs * max_seq_len) rows and skip the
+ * tail past N on the device. Asynchronous; host arguments are checked first
+ * (PE_ERR_* and nothing enqueued). Workspace: pe_pack_workspace_size.
+ */
+pe_status pe_pack_async(const int32_t* lengths, int32_t num_seqs, int32_t max_seq_len, const void* grid,
+                        int64_t row_elems, pe_dtype dtype, int32_t* cu_seqlens, int64_t* flat_index, void* packed,
+                        int64_t capacity, int64_t* status, void* workspace, size_t workspace_bytes, void* stream);
+
 /* -------------------------------------------------------------------- unpack
  * pe_unpack: packed rows -> padded grid, the inverse of the gather.
  *
@@ -162,6 +186,10 @@ pe_status pe_worklist(const int32_t* cu_seqlens, int32_t num_seqs, int64_t total
  *   max_seq_len  upper bound on every length (host int, as the GiGL call takes)
  *   softmax_scale  finite and > 0; the GiGL call uses the SDPA default 1/sqrt(d)
  *   workspace    device, at least pe_attn_workspace_size(..., for_backward=0)
+ *   total_tokens N = cu[B], or a capacity above it (rows of q, k, v, out and of
+ *                lse's row stride); rows cu[B]..N-1 are then neither read nor
+ *                written. This holds for every forward call (local, fused QKV,
+ *                first-token), so a forward can follow pe_pack_async with no host read.
  */
 size_t pe_attn_workspace_size(int32_t num_seqs, int64_t total_tokens, int32_t num_heads,
                               int32_t head_dim, pe_dtype dtype, int for_backward);
@@ -304,6 +332,45 @@ pe_status pe_varlen_attn_bwd_qkv(const void* dout, const void* qkv, const void* 
                                  int32_t max_seq_len, int32_t num_heads, int32_t head_dim, pe_dtype dtype,
                                  float softmax_scale, int32_t window, void* dqkv, void* workspace,
                                  size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------- captured bucket forward
+ * pe_forward_graph_create / pe_graph_launch / pe_graph_destroy: the whole padded
+ * forward of one fixed bucket (num_seqs sequence slots, max_seq_len) recorded
+ * once as a HIP graph and replayed with one launch.
+ *
+ * Source: packed-encoders README, "CUDA graphs": short-sequence inference is
+ * bound by host launches; a bucketed runner collapses the forward to a single
+ * replay; packed graphs take explicit batch and sequence bounds; graphs serve
+ * only gradient-free calls.
+ *
+ * One replay runs, on the buffers given here:
+ *   pe_pack_async(lengths, qkv_grid -> cu_seqlens, qkv_packed; capacity C = num_seqs * max_seq_len)
+ *   pe_varlen_attn_fwd_qkv(qkv_packed, total_tokens = C, window -> out_packed, lse)
+ *   pe_unpack(out_packed -> out_grid)
+ * Buffers (device, caller-owned, fixed for the life of the graph)
+ *   lengths     int32 [num_seqs]; the caller writes the batch before each replay.
+ *               A batch of fewer sequences fills the unused slots with length 1:
+ *               sequences never interact, so those slots change no real output.
+ *   qkv_grid    [num_seqs, max_seq_len, 3, num_heads, head_dim] of dtype (fused Q, K, V)
+ *   cu_seqlens  int32 [num_seqs + 1];  qkv_packed [C, 3, H, d];  out_packed [C, H, d]
+ *   lse         fp32 [H, C], or NULL;  out_grid [num_seqs, max_seq_len, H, d]
+ *   status      int64 [2] as in pe_pack_async (on an error out_grid is all +0.0)
+ *   workspace   at least pe_forward_graph_workspace_size(...) bytes
+ * Rows of out_packed and lse past the replay's N are not written. *graph is
+ * NULL on any error. Creation captures on a stream of its own and enqueues
+ * nothing; pe_graph_launch enqueues one replay on `stream` (asynchronous);
+ * replays on one graph must not overlap (they share every buffer).
+ */
+typedef struct pe_graph_s* pe_graph;
+size_t pe_forward_graph_workspace_size(int32_t num_seqs, int32_t max_seq_len, int32_t num_heads, int32_t head_dim,
+                                       pe_dtype dtype);
+pe_status pe_forward_graph_create(const int32_t* lengths, int32_t num_seqs, int32_t max_seq_len, const void* qkv_grid,
+                                  int32_t num_heads, int32_t head_dim, pe_dtype dtype, float softmax_scale,
+                                  int32_t window, int32_t* cu_seqlens, void* qkv_packed, void* out_packed, float* lse,
+                                  void* out_grid, int64_t* status, void* workspace, size_t workspace_bytes,
+                                  pe_graph* graph);
+pe_status pe_graph_launch(pe_graph graph, void* stream);
+pe_status pe_graph_destroy(pe_graph graph);
 
 /* ---------------------------------------------------------- packing metadata
  * pe_position_ids / pe_document_ids: per packed token, its position inside its

@@ -2,6 +2,7 @@
 // layout, and the launch sequence of every call. See include/pe.h.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <climits>
 #include <cmath>
 #include <cstdint>
@@ -98,7 +99,7 @@ pe_status pe_pack(const int32_t* lengths, int32_t num_seqs, int32_t max_seq_len,
   hipStream_t st = as_stream(stream);
   int64_t* result = static_cast<int64_t*>(workspace);
   int32_t* items = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + kAlign);
-  hipError_t e = pe::launch_scan(lengths, num_seqs, max_seq_len, cu_seqlens, result, st);
+  hipError_t e = pe::launch_scan(lengths, num_seqs, max_seq_len, -1, cu_seqlens, result, st);
   if (e != hipSuccess) return PE_ERR_HIP;
   // The one host read of the library: the token count and the length-error flag.
   int64_t host[2] = {0, 0};
@@ -457,6 +458,118 @@ pe_status pe_scatter_rows(const void* src, const int64_t* flat_index, int64_t n,
   if (!valid_dtype(dtype)) return PE_ERR_UNSUPPORTED;
   return hip_status(pe::launch_scatter_rows(src, flat_index, n, row_elems * elem_bytes(dtype), dst, dst_rows,
                                             as_stream(stream)));
+}
+
+}  // extern "C"
+
+// ------------------------------------------------------- pack without host read
+
+extern "C" {
+
+pe_status pe_pack_async(const int32_t* lengths, int32_t num_seqs, int32_t max_seq_len, const void* grid,
+                        int64_t row_elems, pe_dtype dtype, int32_t* cu_seqlens, int64_t* flat_index, void* packed,
+                        int64_t capacity, int64_t* status, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!lengths || !cu_seqlens || !status) return PE_ERR_NULL;
+  if (grid && !packed) return PE_ERR_NULL;
+  if (!grid && packed) return PE_ERR_ARG;
+  if (num_seqs < 1 || max_seq_len < 1 || capacity < 0) return PE_ERR_ARG;
+  if (static_cast<int64_t>(num_seqs) * max_seq_len > INT32_MAX) return PE_ERR_ARG;
+  if (!valid_dtype(dtype)) return PE_ERR_UNSUPPORTED;
+  if (grid && row_elems < 1) return PE_ERR_ARG;
+  for (const void* p : {static_cast<const void*>(lengths), static_cast<const void*>(cu_seqlens),
+                        static_cast<const void*>(flat_index), grid, static_cast<const void*>(packed),
+                        static_cast<const void*>(status), static_cast<const void*>(workspace)})
+    if (p && !aligned16(p)) return PE_ERR_ARG;
+  if (!workspace || workspace_bytes < pe_pack_workspace_size(num_seqs, max_seq_len, row_elems, dtype))
+    return PE_ERR_WORKSPACE;
+  hipStream_t st = as_stream(stream);
+  // no valid batch holds more than num_seqs * max_seq_len rows
+  const int64_t cap = std::min(capacity, static_cast<int64_t>(num_seqs) * max_seq_len);
+  hipError_t e = pe::launch_scan(lengths, num_seqs, max_seq_len, cap, cu_seqlens, status, st);
+  if (e != hipSuccess) return PE_ERR_HIP;
+  if ((!flat_index && !packed) || cap == 0) return PE_OK;
+  int32_t* items = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + kAlign);
+  const int64_t rowbytes = (packed ? row_elems : 1) * elem_bytes(dtype);
+  const int32_t R = pe::pack_tile_rows(packed ? rowbytes : 64);
+  e = pe::launch_worklist(cu_seqlens, num_seqs, cap, R, items, st);
+  if (e != hipSuccess) return PE_ERR_HIP;
+  return hip_status(pe::launch_pack_rows(grid, packed, flat_index, cu_seqlens, items, num_seqs, max_seq_len,
+                                         rowbytes, cap, R, st));
+}
+
+// ----------------------------------------------------- captured bucket forward
+
+struct pe_graph_s {
+  hipGraphExec_t exec;
+};
+
+size_t pe_forward_graph_workspace_size(int32_t num_seqs, int32_t max_seq_len, int32_t num_heads, int32_t head_dim,
+                                       pe_dtype dtype) {
+  if (num_seqs < 1 || max_seq_len < 1 || num_heads < 1 || head_dim < 1) return 0;
+  const int64_t cap = static_cast<int64_t>(num_seqs) * max_seq_len;
+  return round_up(pe_pack_workspace_size(num_seqs, max_seq_len, 3 * dense_ld(num_heads, head_dim), dtype)) +
+         pe_attn_workspace_size(num_seqs, cap, num_heads, head_dim, dtype, 0);
+}
+
+pe_status pe_forward_graph_create(const int32_t* lengths, int32_t num_seqs, int32_t max_seq_len, const void* qkv_grid,
+                                  int32_t num_heads, int32_t head_dim, pe_dtype dtype, float softmax_scale,
+                                  int32_t window, int32_t* cu_seqlens, void* qkv_packed, void* out_packed, float* lse,
+                                  void* out_grid, int64_t* status, void* workspace, size_t workspace_bytes,
+                                  pe_graph* graph) {
+  if (!graph) return PE_ERR_NULL;
+  *graph = nullptr;
+  if (!lengths || !qkv_grid || !cu_seqlens || !qkv_packed || !out_packed || !out_grid || !status || !workspace)
+    return PE_ERR_NULL;
+  if (num_seqs < 1 || max_seq_len < 1 || window < -1) return PE_ERR_ARG;
+  for (const void* p : {static_cast<const void*>(lengths), qkv_grid, static_cast<const void*>(cu_seqlens),
+                        static_cast<const void*>(qkv_packed), static_cast<const void*>(out_packed),
+                        static_cast<const void*>(lse), static_cast<const void*>(out_grid),
+                        static_cast<const void*>(status), static_cast<const void*>(workspace)})
+    if (p && !aligned16(p)) return PE_ERR_ARG;
+  const int64_t cap = static_cast<int64_t>(num_seqs) * max_seq_len;
+  const pe_status chk = check_attn_args(num_seqs, cap, max_seq_len, num_heads, head_dim, dtype, softmax_scale);
+  if (chk != PE_OK) return chk;
+  if (workspace_bytes < pe_forward_graph_workspace_size(num_seqs, max_seq_len, num_heads, head_dim, dtype))
+    return PE_ERR_WORKSPACE;
+  const int64_t hd = dense_ld(num_heads, head_dim);
+  const size_t pack_ws = round_up(pe_pack_workspace_size(num_seqs, max_seq_len, 3 * hd, dtype));
+  void* attn_ws = static_cast<char*>(workspace) + pack_ws;
+  const size_t attn_wsb = workspace_bytes - pack_ws;
+
+  hipStream_t cs = nullptr;
+  if (hipStreamCreateWithFlags(&cs, hipStreamNonBlocking) != hipSuccess) return PE_ERR_HIP;
+  if (hipStreamBeginCapture(cs, hipStreamCaptureModeThreadLocal) != hipSuccess) {
+    (void)hipStreamDestroy(cs);
+    return PE_ERR_HIP;
+  }
+  pe_status s = pe_pack_async(lengths, num_seqs, max_seq_len, qkv_grid, 3 * hd, dtype, cu_seqlens, nullptr,
+                              qkv_packed, cap, status, workspace, pack_ws, cs);
+  if (s == PE_OK)
+    s = pe_varlen_attn_fwd_qkv(qkv_packed, cu_seqlens, num_seqs, cap, max_seq_len, num_heads, head_dim, dtype,
+                               softmax_scale, window, out_packed, lse, attn_ws, attn_wsb, cs);
+  if (s == PE_OK) s = pe_unpack(out_packed, cu_seqlens, num_seqs, max_seq_len, cap, hd, dtype, out_grid, cs);
+  hipGraph_t g = nullptr;
+  const hipError_t e = hipStreamEndCapture(cs, &g);
+  if (s == PE_OK && e != hipSuccess) s = PE_ERR_HIP;
+  hipGraphExec_t exec = nullptr;
+  if (s == PE_OK && hipGraphInstantiate(&exec, g, nullptr, nullptr, 0) != hipSuccess) s = PE_ERR_HIP;
+  if (g) (void)hipGraphDestroy(g);
+  (void)hipStreamDestroy(cs);
+  if (s != PE_OK) return s;
+  *graph = new pe_graph_s{exec};
+  return PE_OK;
+}
+
+pe_status pe_graph_launch(pe_graph graph, void* stream) {
+  if (!graph) return PE_ERR_NULL;
+  return hip_status(hipGraphLaunch(graph->exec, as_stream(stream)));
+}
+
+pe_status pe_graph_destroy(pe_graph graph) {
+  if (!graph) return PE_OK;
+  const hipError_t e = hipGraphExecDestroy(graph->exec);
+  delete graph;
+  return hip_status(e);
 }
 
 }  // extern "C"

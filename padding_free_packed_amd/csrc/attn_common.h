@@ -254,6 +254,9 @@ __device__ __forceinline__ TileSpan tile_span(const int32_t* __restrict__ cu, co
   __syncthreads();
   s.lo = cul[0];
   s.hi = cul[s.ncu - 1];
+  // rows past cu[B] (a row count given as a capacity) belong to no sequence;
+  // a tile after the last sequence (items[t] == B) ends up empty
+  s.rend = min(s.rend, s.hi);
   return s;
 }
 

@@ -69,12 +69,15 @@ __global__ __launch_bounds__(64, 2) void attn_fwd_f32_kernel(
   const int lane = threadIdx.x, ql = lane & 31, g = lane >> 5;
 
   // sequences of rows r0 .. rend-1
-  const int r0 = t * kRows, rend = min(r0 + kRows, N);
+  const int r0 = t * kRows, rcap = min(r0 + kRows, N);
   const int blo = items[t], nxt = items[t + 1];
-  const int bhi = nxt >= B ? B - 1 : (cu[nxt] == rend ? nxt - 1 : nxt);
+  const int bhi = nxt >= B ? B - 1 : (cu[nxt] == rcap ? nxt - 1 : nxt);
   const int ncu = min(bhi - blo + 2, kRows + 2);
   if (lane < ncu) cul[lane] = cu[blo + lane];
   __syncthreads();
+  // rows past cu[B] (a row count given as a capacity) belong to no sequence
+  const int rend = min(rcap, cul[ncu - 1]);
+  if (rend <= r0) return;
 
   const int qrow = r0 + ql;
   const bool qvalid = qrow < rend;
@@ -244,12 +247,15 @@ __global__ __launch_bounds__(64, 2) void bwd_dq_f32_kernel(
   const int h = lin / T, t = lin - h * T;
   const int lane = threadIdx.x, ql = lane & 31, g = lane >> 5;
 
-  const int r0 = t * kRows, rend = min(r0 + kRows, N);
+  const int r0 = t * kRows, rcap = min(r0 + kRows, N);
   const int blo = items[t], nxt = items[t + 1];
-  const int bhi = nxt >= B ? B - 1 : (cu[nxt] == rend ? nxt - 1 : nxt);
+  const int bhi = nxt >= B ? B - 1 : (cu[nxt] == rcap ? nxt - 1 : nxt);
   const int ncu = min(bhi - blo + 2, kRows + 2);
   if (lane < ncu) cul[lane] = cu[blo + lane];
   __syncthreads();
+  // rows past cu[B] (a row count given as a capacity) belong to no sequence
+  const int rend = min(rcap, cul[ncu - 1]);
+  if (rend <= r0) return;
 
   const int qrow = r0 + ql;
   const bool qvalid = qrow < rend;
@@ -371,12 +377,15 @@ __global__ __launch_bounds__(64, D > 32 ? 1 : 2) void bwd_dkdv_f32_kernel(
   const int h = lin / T, t = lin - h * T;
   const int lane = threadIdx.x, ql = lane & 31, g = lane >> 5;
 
-  const int r0 = t * kRows, rend = min(r0 + kRows, N);
+  const int r0 = t * kRows, rcap = min(r0 + kRows, N);
   const int blo = items[t], nxt = items[t + 1];
-  const int bhi = nxt >= B ? B - 1 : (cu[nxt] == rend ? nxt - 1 : nxt);
+  const int bhi = nxt >= B ? B - 1 : (cu[nxt] == rcap ? nxt - 1 : nxt);
   const int ncu = min(bhi - blo + 2, kRows + 2);
   if (lane < ncu) cul[lane] = cu[blo + lane];
   __syncthreads();
+  // rows past cu[B] (a row count given as a capacity) belong to no sequence
+  const int rend = min(rcap, cul[ncu - 1]);
+  if (rend <= r0) return;
 
   const int krow = r0 + ql;
   const bool kvalid = krow < rend;

@@ -43,6 +43,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
 
   // the sequences this tile touches; their keys are [sp.lo, sp.hi)
   const TileSpan sp = tile_span(cu, items, t, B, N, cul);
+  if (sp.rend <= sp.r0) return;  // block-uniform: no rows in this tile
 
   // this lane's query row and its own key range [qk0, qk1)
   const int qrow = sp.r0 + wv * 32 + ql;

@@ -46,6 +46,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, ql = lane & 31, g = lane >> 5;
 
   const TileSpan sp = tile_span(cu, items, t, B, N, cul);
+  if (sp.rend <= sp.r0) return;  // block-uniform: no rows in this tile
   const int qrow = sp.r0 + wv * 32 + ql;
   const bool qvalid = qrow < sp.rend;
   int qk0 = 0, qk1 = 0;

@@ -58,6 +58,7 @@ __global__ __launch_bounds__(kW64Threads) __attribute__((amdgpu_waves_per_eu(2))
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, ql = lane & 31, g = lane >> 5;
 
   const TileSpan sp = tile_span<kW64Threads>(cu, items, t, B, N, cul);
+  if (sp.rend <= sp.r0) return;  // block-uniform: no rows in this tile
   int qrow[2], qk0[2], qk1[2], bk0[2], bk1[2], mk0[2], mk1[2];
   bool qvalid[2];
 #pragma unroll

@@ -14,8 +14,11 @@ constexpr int kAttnTileRows = 128;
 // packed rows per work item of the one-wave fp32 kernels
 constexpr int kAttnWaveRows = 32;
 
-hipError_t launch_scan(const int32_t* lengths, int32_t B, int32_t S, int32_t* cu, int64_t* result,
+// cap < 0: no capacity check, cu keeps the running sum even on a length error;
+// cap >= 0: a length error or a total above cap zeroes cu (see scan_lengths_kernel)
+hipError_t launch_scan(const int32_t* lengths, int32_t B, int32_t S, int64_t cap, int32_t* cu, int64_t* result,
                        hipStream_t stream);
+// N may exceed cu[B] (a capacity): tiles from ceil(cu[B] / R) on get item B
 hipError_t launch_worklist(const int32_t* cu, int32_t B, int64_t N, int32_t R, int32_t* items,
                            hipStream_t stream);
 int32_t pack_tile_rows(int64_t rowbytes);

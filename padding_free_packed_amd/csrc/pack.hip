@@ -15,12 +15,15 @@ namespace pe {
 // ---------------------------------------------------------------- scan
 // One workgroup of 1024 threads; each pass scans 8192 lengths (8 per thread)
 // and carries the running total in int64. Writes cu[0..B], result[0] = total
-// token count (int64), result[1] = 1 if any length lies outside [1, S].
+// token count (int64), result[1] = 1 if any length lies outside [1, S], else 2
+// if cap >= 0 and the total exceeds cap, else 0. With cap >= 0 a nonzero
+// result[1] also rewrites cu[0..B] as zeros, so that kernels queued behind the
+// scan without a host check see no rows at all.
 constexpr int kScanThreads = 1024;
 constexpr int kScanPer = 8;
 
 __global__ __launch_bounds__(kScanThreads) void scan_lengths_kernel(
-    const int32_t* __restrict__ lengths, int32_t B, int32_t S, int32_t* __restrict__ cu,
+    const int32_t* __restrict__ lengths, int32_t B, int32_t S, int64_t cap, int32_t* __restrict__ cu,
     int64_t* __restrict__ result) {
   __shared__ int64_t wsum[kScanThreads / 64];
   __shared__ int bad_any;
@@ -69,25 +72,31 @@ __global__ __launch_bounds__(kScanThreads) void scan_lengths_kernel(
   }
   if (bad) atomicOr(&bad_any, 1);
   __syncthreads();
+  const int64_t code = bad_any ? 1 : (cap >= 0 && carry > cap ? 2 : 0);
   if (tid == 0) {
     result[0] = carry;
-    result[1] = bad_any;
+    result[1] = code;
   }
+  if (cap >= 0 && code != 0)
+    for (int64_t i = tid; i <= B; i += kScanThreads) cu[i] = 0;
 }
 
 // ---------------------------------------------------------------- work list
-// items[t] = b with cu[b] <= t*R < cu[b+1]; items[T] = B. One thread per
-// sequence writes the entries of the tiles that start inside it.
+// items[t] = b with cu[b] <= t*R < cu[b+1]; items[T] = B, T = ceil(N / R).
+// Thread b writes the entries of the tiles that start inside sequence b. N may
+// be a capacity above cu[B]: thread i then also marks tile i, if it starts at
+// or after cu[B], with B (a tile of no sequence).
 __global__ void worklist_kernel(const int32_t* __restrict__ cu, int32_t B, int64_t N, int32_t R,
                                 int32_t* __restrict__ items) {
   const int64_t T = (N + R - 1) / R;
-  const int64_t b = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (b == 0) items[T] = B;
-  if (b >= B) return;
-  const int64_t c0 = cu[b], c1 = cu[b + 1];
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i == 0) items[T] = B;
+  if (i < T && i >= (static_cast<int64_t>(cu[B]) + R - 1) / R) items[i] = B;
+  if (i >= B) return;
+  const int64_t c0 = cu[i], c1 = cu[i + 1];
   int64_t t = (c0 + R - 1) / R;
   const int64_t tend = min((c1 + R - 1) / R, T);
-  for (; t < tend; ++t) items[t] = static_cast<int32_t>(b);
+  for (; t < tend; ++t) items[t] = static_cast<int32_t>(i);
 }
 
 // ---------------------------------------------------------------- segment copy
@@ -166,10 +175,10 @@ __global__ __launch_bounds__(256) void unpack_rows_kernel(
 
 // ---------------------------------------------------------------- launchers
 
-hipError_t launch_scan(const int32_t* lengths, int32_t B, int32_t S, int32_t* cu, int64_t* result,
+hipError_t launch_scan(const int32_t* lengths, int32_t B, int32_t S, int64_t cap, int32_t* cu, int64_t* result,
                        hipStream_t stream) {
   hipEvent_t ev = timing_start(stream);
-  hipLaunchKernelGGL(scan_lengths_kernel, dim3(1), dim3(kScanThreads), 0, stream, lengths, B, S, cu, result);
+  hipLaunchKernelGGL(scan_lengths_kernel, dim3(1), dim3(kScanThreads), 0, stream, lengths, B, S, cap, cu, result);
   timing_stop("scan", ev, stream);
   return hipGetLastError();
 }
@@ -177,7 +186,9 @@ hipError_t launch_scan(const int32_t* lengths, int32_t B, int32_t S, int32_t* cu
 hipError_t launch_worklist(const int32_t* cu, int32_t B, int64_t N, int32_t R, int32_t* items,
                            hipStream_t stream) {
   const int threads = 256;
-  const int blocks = static_cast<int>((static_cast<int64_t>(B) + threads - 1) / threads);
+  const int64_t T = (N + R - 1) / R;
+  const int64_t n = T > B ? T : static_cast<int64_t>(B);
+  const int blocks = static_cast<int>((n + threads - 1) / threads);
   hipEvent_t ev = timing_start(stream);
   hipLaunchKernelGGL(worklist_kernel, dim3(blocks), dim3(threads), 0, stream, cu, B, N, R, items);
   timing_stop("worklist", ev, stream);

@@ -1,5 +1,6 @@
 // Optional per-kernel timing: while enabled, every kernel launch of the library
-// is bracketed by two HIP events recorded on the launch's stream. Events come
+// is bracketed by two HIP events recorded on the launch's stream (launches
+// recorded into a graph under stream capture are not timed). Events come
 // from a pool that grows on first use and is reused after each read.
 #include <hip/hip_runtime.h>
 
@@ -36,6 +37,8 @@ hipEvent_t take_event() {
 
 hipEvent_t timing_start(hipStream_t stream) {
   if (!g_on || g_recs.size() >= kMaxRecords) return nullptr;
+  hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(stream, &cap) != hipSuccess || cap != hipStreamCaptureStatusNone) return nullptr;
   hipEvent_t e = take_event();
   if (e != nullptr && hipEventRecord(e, stream) != hipSuccess) return nullptr;
   return e;

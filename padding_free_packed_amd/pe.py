@@ -28,8 +28,12 @@ EXPORTS = (
     "pe_varlen_attn_bwd", "pe_varlen_attn_fwd_local", "pe_varlen_attn_bwd_local", "pe_varlen_attn_fwd_first_row",
     "pe_varlen_attn_bwd_first_token", "pe_position_ids", "pe_flatten_workspace_size", "pe_flatten_packed_metadata",
     "pe_flatten_document_mask", "pe_gather_rows", "pe_scatter_rows", "pe_varlen_attn_fwd_qkv",
-    "pe_varlen_attn_bwd_qkv", "pe_timing_enable", "pe_timing_read",
+    "pe_varlen_attn_bwd_qkv", "pe_timing_enable", "pe_timing_read", "pe_pack_async",
+    "pe_forward_graph_workspace_size", "pe_forward_graph_create", "pe_graph_launch", "pe_graph_destroy",
 )
+
+# status[1] codes of pe_pack_async
+PACK_OK, PACK_BAD_LENGTH, PACK_OVER_CAPACITY = 0, 1, 2
 
 
 class PeError(RuntimeError):
@@ -77,6 +81,12 @@ def _load():
                                                    SZ, P]),
         "pe_varlen_attn_bwd_qkv": (ctypes.c_int, [P, P, P, P, P, I32, I64, I32, I32, I32, ctypes.c_int, F, I32, P,
                                                    P, SZ, P]),
+        "pe_pack_async": (ctypes.c_int, [P, I32, I32, P, I64, ctypes.c_int, P, P, P, I64, P, P, SZ, P]),
+        "pe_forward_graph_workspace_size": (SZ, [I32, I32, I32, I32, ctypes.c_int]),
+        "pe_forward_graph_create": (ctypes.c_int, [P, I32, I32, P, I32, I32, ctypes.c_int, F, I32, P, P, P, P, P,
+                                                    P, P, SZ, ctypes.POINTER(ctypes.c_void_p)]),
+        "pe_graph_launch": (ctypes.c_int, [P, P]),
+        "pe_graph_destroy": (ctypes.c_int, [P]),
         "pe_timing_enable": (ctypes.c_int, [ctypes.c_int]),
         "pe_timing_read": (ctypes.c_int, [P, P, ctypes.c_int]),
     }
@@ -145,6 +155,19 @@ def pe_pack(lengths, max_seq_len, grid, cu_seqlens, flat_index, packed, capacity
                       _ptr(workspace), 0 if workspace is None else workspace.numel(), _stream())
     _check("pe_pack", st, n.value)
     return n.value
+
+
+def pe_pack_async(lengths, max_seq_len, grid, cu_seqlens, flat_index, packed, capacity, status, workspace,
+                  dtype: int | None = None) -> None:
+    """pe_pack with no host read: the token count and an error code land in the
+    device int64 tensor ``status`` ([N, code], code one of PACK_*)."""
+    if dtype is None:
+        dtype = _dtype_code(grid) if grid is not None else PE_FP32
+    row_elems = 0 if grid is None else grid.numel() // (lengths.numel() * max_seq_len)
+    st = _lib.pe_pack_async(_ptr(lengths), lengths.numel(), max_seq_len, _ptr(grid), row_elems, dtype,
+                            _ptr(cu_seqlens), _ptr(flat_index), _ptr(packed), capacity, _ptr(status),
+                            _ptr(workspace), 0 if workspace is None else workspace.numel(), _stream())
+    _check("pe_pack_async", st)
 
 
 def pe_unpack(packed, cu_seqlens, num_seqs, max_seq_len, total_tokens, grid):
@@ -244,6 +267,35 @@ def pe_varlen_attn_bwd_qkv(dout, qkv, out, lse, cu_seqlens, num_seqs, total_toke
                                      total_tokens, max_seq_len, H, d, _dtype_code(qkv), softmax_scale, window,
                                      _ptr(dqkv), _ptr(workspace), workspace.numel(), _stream())
     _check("pe_varlen_attn_bwd_qkv", st)
+
+
+# ------------------------------------------------------------------ captured bucket forward
+
+def pe_forward_graph_workspace_size(num_seqs: int, max_seq_len: int, num_heads: int, head_dim: int,
+                                    dtype: int) -> int:
+    return int(_lib.pe_forward_graph_workspace_size(num_seqs, max_seq_len, num_heads, head_dim, dtype))
+
+
+def pe_forward_graph_create(lengths, qkv_grid, softmax_scale, window, cu_seqlens, qkv_packed, out_packed, lse,
+                            out_grid, status, workspace):
+    """qkv_grid [B, S, 3, H, d]; returns an opaque graph handle (int) for pe_graph_launch."""
+    B, S, three, H, d = qkv_grid.shape
+    assert three == 3 and qkv_grid.is_contiguous() and lengths.numel() == B
+    handle = ctypes.c_void_p(None)
+    st = _lib.pe_forward_graph_create(_ptr(lengths), B, S, _ptr(qkv_grid), H, d, _dtype_code(qkv_grid),
+                                      softmax_scale, window, _ptr(cu_seqlens), _ptr(qkv_packed), _ptr(out_packed),
+                                      _ptr(lse), _ptr(out_grid), _ptr(status), _ptr(workspace), workspace.numel(),
+                                      ctypes.byref(handle))
+    _check("pe_forward_graph_create", st)
+    return handle.value
+
+
+def pe_graph_launch(graph) -> None:
+    _check("pe_graph_launch", _lib.pe_graph_launch(ctypes.c_void_p(graph), _stream()))
+
+
+def pe_graph_destroy(graph) -> None:
+    _check("pe_graph_destroy", _lib.pe_graph_destroy(ctypes.c_void_p(graph)))
 
 
 # ------------------------------------------------------------------ packing metadata

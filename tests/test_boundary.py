@@ -27,7 +27,7 @@ def _header_functions():
 
 def test_header_symbols_exported():
     names = _header_functions()
-    assert len(names) == 24
+    assert len(names) == 29
     for n in names:
         assert hasattr(lib, n), n
     assert sorted(pe.EXPORTS) == names
@@ -230,3 +230,47 @@ def test_unpack_and_worklist_reject():
     assert w(NUL, 4, 100, 128, P, None) == pe.PE_ERR_NULL
     assert w(P, 4, 100, 0, P, None) == pe.PE_ERR_ARG
     assert w(P, 0, 100, 128, P, None) == pe.PE_ERR_ARG
+
+
+def test_pack_async_rejects():
+    f = lib.pe_pack_async
+    ok = [P, 4, 64, P, 16, 0, P, P, P, 100, P, P, 1 << 20, None]
+    a = list(ok); a[0] = NUL
+    assert f(*a) == pe.PE_ERR_NULL
+    a = list(ok); a[10] = NUL                    # no status buffer
+    assert f(*a) == pe.PE_ERR_NULL
+    a = list(ok); a[8] = NUL
+    assert f(*a) == pe.PE_ERR_NULL
+    a = list(ok); a[3] = NUL
+    assert f(*a) == pe.PE_ERR_ARG
+    a = list(ok); a[9] = -1
+    assert f(*a) == pe.PE_ERR_ARG
+    a = list(ok); a[1] = 1 << 20; a[2] = 1 << 12  # slots * length bound above INT32_MAX
+    assert f(*a) == pe.PE_ERR_ARG
+    a = list(ok); a[5] = 7
+    assert f(*a) == pe.PE_ERR_UNSUPPORTED
+    a = list(ok); a[12] = 10
+    assert f(*a) == pe.PE_ERR_WORKSPACE
+    a = list(ok); a[10] = MIS
+    assert f(*a) == pe.PE_ERR_ARG
+
+
+def test_forward_graph_rejects_before_any_capture():
+    f = lib.pe_forward_graph_create
+    g = ctypes.c_void_p(P)
+    ws = pe.pe_forward_graph_workspace_size(8, 64, 2, 64, pe.PE_BF16)
+    assert pe.pe_forward_graph_workspace_size(256, 512, 2, 64, pe.PE_BF16) > ws > 0
+    assert pe.pe_forward_graph_workspace_size(0, 64, 2, 64, pe.PE_BF16) == 0
+    ok = [P, 8, 64, P, 2, 64, pe.PE_BF16, 0.125, -1, P, P, P, NUL, P, P, P, ws, ctypes.byref(g)]
+    a = list(ok); a[17] = NUL
+    assert f(*a) == pe.PE_ERR_NULL
+    for i, bad, code in [(0, NUL, pe.PE_ERR_NULL), (3, NUL, pe.PE_ERR_NULL), (14, NUL, pe.PE_ERR_NULL),
+                         (8, -2, pe.PE_ERR_ARG), (1, 0, pe.PE_ERR_ARG), (6, 7, pe.PE_ERR_UNSUPPORTED),
+                         (5, 24, pe.PE_ERR_UNSUPPORTED), (7, 0.0, pe.PE_ERR_ARG), (16, ws - 1, pe.PE_ERR_WORKSPACE),
+                         (13, MIS, pe.PE_ERR_ARG)]:
+        a = list(ok); a[i] = bad
+        g.value = P
+        assert f(*a) == code, i
+        assert g.value is None, i                # no handle on an error
+    assert lib.pe_graph_launch(NUL, None) == pe.PE_ERR_NULL
+    assert lib.pe_graph_destroy(NUL) == pe.PE_OK
