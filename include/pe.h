@@ -59,7 +59,7 @@ typedef enum {
   PE_ERR_METADATA = 8     /* pe_flatten_*: packed metadata that is not consistent */
 } pe_status;
 
-typedef enum { PE_FP32 = 0, PE_BF16 = 1 } pe_dtype;
+typedef enum { PE_FP32 = 0, PE_BF16 = 1, PE_FP16 = 2 } pe_dtype;
 
 /* Human-readable name of a status code. Never NULL. */
 const char* pe_status_string(int status);

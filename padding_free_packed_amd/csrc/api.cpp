@@ -20,9 +20,9 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 bool supported_head_dim(int32_t d) { return d == 8 || d == 16 || d == 32 || d == 64 || d == 128; }
 
-bool valid_dtype(int dt) { return dt == PE_FP32 || dt == PE_BF16; }
+bool valid_dtype(int dt) { return dt == PE_FP32 || dt == PE_BF16 || dt == PE_FP16; }
 
-int64_t elem_bytes(pe_dtype dt) { return dt == PE_BF16 ? 2 : 4; }
+int64_t elem_bytes(pe_dtype dt) { return dt == PE_FP32 ? 4 : 2; }
 
 hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
 
@@ -188,7 +188,7 @@ pe_status fwd_impl(const void* q, const void* k, const void* v, const int32_t* c
   }
   hipError_t e = pe::launch_worklist(cu_seqlens, num_seqs, total_tokens, pe::kAttnTileRows, items, st);
   if (e != hipSuccess) return PE_ERR_HIP;
-  e = pe::launch_attn_fwd(dtype == PE_BF16, head_dim, q, k, v, cu_seqlens, items, num_seqs,
+  e = pe::launch_attn_fwd(dtype, head_dim, q, k, v, cu_seqlens, items, num_seqs,
                           static_cast<int32_t>(total_tokens), num_heads, max_seq_len, win, ld, softmax_scale, out,
                           lse, st);
   return hip_status(e);
@@ -237,7 +237,7 @@ pe_status first_impl(const void* q, int32_t gather, const void* k, const void* v
   for (const void* p : {q, k, v, static_cast<const void*>(cu_seqlens), static_cast<const void*>(out_first),
                         static_cast<const void*>(lse_first)})
     if (p && !aligned16(p)) return PE_ERR_ARG;
-  return hip_status(pe::launch_attn_fwd_first(dtype == PE_BF16, head_dim, q, k, v, cu_seqlens, num_seqs,
+  return hip_status(pe::launch_attn_fwd_first(dtype, head_dim, q, k, v, cu_seqlens, num_seqs,
                                               static_cast<int32_t>(total_tokens), num_heads, gather,
                                               static_cast<int64_t>(num_heads) * head_dim, softmax_scale, out_first,
                                               lse_first, as_stream(stream)));
@@ -278,7 +278,7 @@ pe_status pe_varlen_attn_bwd_first_token(const void* dout_first, const void* q_f
                         static_cast<const void*>(cu_seqlens), static_cast<const void*>(dq_first),
                         static_cast<const void*>(dk), static_cast<const void*>(dv)})
     if (!aligned16(p)) return PE_ERR_ARG;
-  return hip_status(pe::launch_attn_bwd_first(dtype == PE_BF16, head_dim, dout_first, q_first, k, v, out_first,
+  return hip_status(pe::launch_attn_bwd_first(dtype, head_dim, dout_first, q_first, k, v, out_first,
                                               lse_first, cu_seqlens, num_seqs, static_cast<int32_t>(total_tokens),
                                               num_heads, static_cast<int64_t>(num_heads) * head_dim, softmax_scale,
                                               dq_first, dk, dv, as_stream(stream)));
@@ -315,7 +315,7 @@ pe_status bwd_impl(const void* dout, const void* q, const void* k, const void* v
     e = pe::launch_worklist(cu_seqlens, num_seqs, total_tokens, pe::kAttnWaveRows, items32, st);
     if (e != hipSuccess) return PE_ERR_HIP;
   }
-  e = pe::launch_attn_bwd(dtype == PE_BF16, head_dim, dout, q, k, v, out, lse, cu_seqlens, items,
+  e = pe::launch_attn_bwd(dtype, head_dim, dout, q, k, v, out, lse, cu_seqlens, items,
                           dtype == PE_FP32 ? items32 : nullptr, num_seqs, static_cast<int32_t>(total_tokens),
                           num_heads, win, ld, softmax_scale, dq, dk, dv, delta, st);
   if (e == hipErrorNotSupported) return PE_ERR_UNSUPPORTED;

@@ -24,20 +24,20 @@ namespace pe {
 
 namespace {
 
-template <bool BF, int D>
+template <typename Et, int D>
 __global__ __launch_bounds__(256) void bwd_delta_kernel(const void* __restrict__ dout, const void* __restrict__ out,
                                                         int32_t N, int32_t H, float* __restrict__ delta) {
-  using G = Geo<BF, D>;
+  using G = Geo<Et, D>;
   const int64_t ch = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;  // 16-byte chunk
   const int64_t total = static_cast<int64_t>(N) * H * G::CH;
   float s = 0.f;
   if (ch < total) {
     const uint4 a = *reinterpret_cast<const uint4*>(static_cast<const char*>(dout) + ch * 16);
     const uint4 b = *reinterpret_cast<const uint4*>(static_cast<const char*>(out) + ch * 16);
-    if constexpr (BF) {
+    if constexpr (kIs16<Et>) {
       const u16x8 x = __builtin_bit_cast(u16x8, a), y = __builtin_bit_cast(u16x8, b);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) s = fmaf(bf16_to_f32(x[e]), bf16_to_f32(y[e]), s);
+      for (int e = 0; e < 8; ++e) s = fmaf(h16_to_f32<Et>(x[e]), h16_to_f32<Et>(y[e]), s);
     } else {
       const float4 x = __builtin_bit_cast(float4, a), y = __builtin_bit_cast(float4, b);
       s = fmaf(x.x, y.x, fmaf(x.y, y.y, fmaf(x.z, y.z, x.w * y.w)));
@@ -52,17 +52,17 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(const void* __restrict__
   }
 }
 
-template <bool BF, int D>
+template <typename Et, int D>
 __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(
     const void* __restrict__ dop, const void* __restrict__ qp, const void* __restrict__ kp,
     const void* __restrict__ vp, const float* __restrict__ lse, const float* __restrict__ delta,
     const int32_t* __restrict__ cu, const int32_t* __restrict__ items, int32_t B, int32_t N, int32_t H,
     int32_t T, int32_t win, int64_t ld, float c, float scale, void* __restrict__ dkp, void* __restrict__ dvp) {
-  using G = Geo<BF, D>;
+  using G = Geo<Et, D>;
   using E = typename G::E;
   // bf16 tiles with whole 16-byte chunks per lane half use the XOR-swizzled layout
   // (conflict-free for both the row reads and the transposing reads)
-  constexpr bool SWZ = BF && D % 32 == 0;
+  constexpr bool SWZ = kIs16<Et> && D % 32 == 0;
   constexpr int TS = SWZ ? kBlk * D : G::TSZ;
   __shared__ __align__(16) E qt[2][TS];
   __shared__ __align__(16) E dt[2][TS];
@@ -88,10 +88,10 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(
   const int mq0 = wave_max_i(kvalid ? jk0 : INT_MIN);
   const int mq1 = wave_min_i(kvalid ? jk1 : INT_MAX);
 
-  typename RegT<BF>::T kreg[G::QS], vreg[G::QS];
+  typename RegT<Et>::type kreg[G::QS], vreg[G::QS];
   const int64_t roff = static_cast<int64_t>(krow) * ld + h * D;  // rows of K, V, dK, dV are ld apart
-  load_row_regs<BF, D>(kp, roff + g * G::HALF, kvalid, kreg);
-  load_row_regs<BF, D>(vp, roff + g * G::HALF, kvalid, vreg);
+  load_row_regs<Et, D>(kp, roff + g * G::HALF, kvalid, kreg);
+  load_row_regs<Et, D>(vp, roff + g * G::HALF, kvalid, vreg);
 
   floatx16 dk[G::DB], dv[G::DB];
 #pragma unroll
@@ -108,8 +108,8 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(
   const float* lse_h = lse + static_cast<int64_t>(h) * N;
   const float* del_h = delta + static_cast<int64_t>(h) * N;
   auto gload = [&](int qb) {
-    tile_gload<BF, D>(qp, qb, qhi, ld, h, qr);
-    tile_gload<BF, D>(dop, qb, qhi, static_cast<int64_t>(H) * D, h, dr);
+    tile_gload<Et, D>(qp, qb, qhi, ld, h, qr);
+    tile_gload<Et, D>(dop, qb, qhi, static_cast<int64_t>(H) * D, h, dr);
     if (tid < kBlk) {
       const int row = qb + tid;
       lsr = row < qhi ? lse_h[row] * kLog2e : 0.f;
@@ -124,8 +124,8 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(
       tile_store_swz<D>(qt[buf], qr);
       tile_store_swz<D>(dt[buf], dr);
     } else {
-      tile_store<BF, D>(qt[buf], qr);
-      tile_store<BF, D>(dt[buf], dr);
+      tile_store<Et, D>(qt[buf], qr);
+      tile_store<Et, D>(dt[buf], dr);
     }
     if (tid < kBlk) {
       ls[buf][tid] = lsr;
@@ -139,11 +139,11 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(
       for (int qq = 0; qq < 2; ++qq) {
         floatx16 s = floatx16{}, dp = floatx16{};
         if constexpr (SWZ) {
-          mma_rows_swz<D>(qt[buf], 32 * qq, kreg, s, ql, g);   // S[q][key]
-          mma_rows_swz<D>(dt[buf], 32 * qq, vreg, dp, ql, g);  // dP[q][key]
+          mma_rows_swz<Et, D>(qt[buf], 32 * qq, kreg, s, ql, g);   // S[q][key]
+          mma_rows_swz<Et, D>(dt[buf], 32 * qq, vreg, dp, ql, g);  // dP[q][key]
         } else {
-          mma_rows_regs<BF, D>(qt[buf], 32 * qq, kreg, s, ql, g);
-          mma_rows_regs<BF, D>(dt[buf], 32 * qq, vreg, dp, ql, g);
+          mma_rows_regs<Et, D>(qt[buf], 32 * qq, kreg, s, ql, g);
+          mma_rows_regs<Et, D>(dt[buf], 32 * qq, vreg, dp, ql, g);
         }
         const int base = qb + 32 * qq + 4 * g;
         if (need_mask) mask_block(s, jk0 - base, jk1 - base);
@@ -162,34 +162,34 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(
           }
         }
         if constexpr (SWZ) {
-          bf16x8 pb[2], sb[2];
-          acc_to_bf16(s, pb);
-          acc_to_bf16(dp, sb);
-          mma_tr_swz<D>(dt[buf], 32 * qq, pb, dv, lane);  // dV^T += dO^T P
-          mma_tr_swz<D>(qt[buf], 32 * qq, sb, dk, lane);  // dK^T += Q^T dS
+          vec8<Et> pb[2], sb[2];
+          acc_to_h16<Et>(s, pb);
+          acc_to_h16<Et>(dp, sb);
+          mma_tr_swz<Et, D>(dt[buf], 32 * qq, pb, dv, lane);  // dV^T += dO^T P
+          mma_tr_swz<Et, D>(qt[buf], 32 * qq, sb, dk, lane);  // dK^T += Q^T dS
         } else {
-          mma_tr_regs<BF, D>(dt[buf], 32 * qq, s, dv, lane);
-          mma_tr_regs<BF, D>(qt[buf], 32 * qq, dp, dk, lane);
+          mma_tr_regs<Et, D>(dt[buf], 32 * qq, s, dv, lane);
+          mma_tr_regs<Et, D>(qt[buf], 32 * qq, dp, dk, lane);
         }
       }
     }
     buf ^= 1;
   }
   if (kvalid) {
-    store_acc_row<BF, D>(dkp, roff, dk, scale, g);
-    store_acc_row<BF, D>(dvp, roff, dv, 1.f, g);
+    store_acc_row<Et, D>(dkp, roff, dk, scale, g);
+    store_acc_row<Et, D>(dvp, roff, dv, 1.f, g);
   }
 }
 
-template <bool BF, int D>
+template <typename Et, int D>
 __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
     const void* __restrict__ dop, const void* __restrict__ qp, const void* __restrict__ kp,
     const void* __restrict__ vp, const float* __restrict__ lse, const float* __restrict__ delta,
     const int32_t* __restrict__ cu, const int32_t* __restrict__ items, int32_t B, int32_t N, int32_t H,
     int32_t T, int32_t win, int64_t ld, float c, float scale, void* __restrict__ dqp) {
-  using G = Geo<BF, D>;
+  using G = Geo<Et, D>;
   using E = typename G::E;
-  constexpr bool SWZ = BF && D % 32 == 0;
+  constexpr bool SWZ = kIs16<Et> && D % 32 == 0;
   constexpr int TS = SWZ ? kBlk * D : G::TSZ;
   __shared__ __align__(16) E kt[2][TS];
   __shared__ __align__(16) E vt[2][TS];
@@ -213,10 +213,10 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
   const int mk0 = wave_max_i(qvalid ? qk0 : INT_MIN);
   const int mk1 = wave_min_i(qvalid ? qk1 : INT_MAX);
 
-  typename RegT<BF>::T qreg[G::QS], dreg[G::QS];
+  typename RegT<Et>::type qreg[G::QS], dreg[G::QS];
   const int64_t roff = static_cast<int64_t>(qrow) * ld + h * D;  // rows of Q and dQ are ld apart
-  load_row_regs<BF, D>(qp, roff + g * G::HALF, qvalid, qreg);
-  load_row_regs<BF, D>(dop, (static_cast<int64_t>(qrow) * H + h) * D + g * G::HALF, qvalid, dreg);
+  load_row_regs<Et, D>(qp, roff + g * G::HALF, qvalid, qreg);
+  load_row_regs<Et, D>(dop, (static_cast<int64_t>(qrow) * H + h) * D + g * G::HALF, qvalid, dreg);
   const float lse2 = qvalid ? lse[static_cast<int64_t>(h) * N + qrow] * kLog2e : 0.f;
   const float dlq = qvalid ? delta[static_cast<int64_t>(h) * N + qrow] : 0.f;
 
@@ -229,21 +229,21 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
   const int khi = win >= 0 ? min(sp.hi, sp.rend + win) : sp.hi;
   int buf = 0;
   if (klo < khi) {
-    tile_gload<BF, D>(kp, klo, khi, ld, h, kr);
-    tile_gload<BF, D>(vp, klo, khi, ld, h, vr);
+    tile_gload<Et, D>(kp, klo, khi, ld, h, kr);
+    tile_gload<Et, D>(vp, klo, khi, ld, h, vr);
   }
   for (int kb = klo; kb < khi; kb += kBlk) {
     if constexpr (SWZ) {
       tile_store_swz<D>(kt[buf], kr);
       tile_store_swz<D>(vt[buf], vr);
     } else {
-      tile_store<BF, D>(kt[buf], kr);
-      tile_store<BF, D>(vt[buf], vr);
+      tile_store<Et, D>(kt[buf], kr);
+      tile_store<Et, D>(vt[buf], vr);
     }
     __syncthreads();
     if (kb + kBlk < khi) {
-      tile_gload<BF, D>(kp, kb + kBlk, khi, ld, h, kr);
-      tile_gload<BF, D>(vp, kb + kBlk, khi, ld, h, vr);
+      tile_gload<Et, D>(kp, kb + kBlk, khi, ld, h, kr);
+      tile_gload<Et, D>(vp, kb + kBlk, khi, ld, h, vr);
     }
     if (kb < wk1 && kb + kBlk > wk0) {
       const bool need_mask = !(kb >= mk0 && kb + kBlk <= mk1);
@@ -251,11 +251,11 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
       for (int kk = 0; kk < 2; ++kk) {
         floatx16 s = floatx16{}, dp = floatx16{};
         if constexpr (SWZ) {
-          mma_rows_swz<D>(kt[buf], 32 * kk, qreg, s, ql, g);   // S^T[key][q]
-          mma_rows_swz<D>(vt[buf], 32 * kk, dreg, dp, ql, g);  // dP^T[key][q]
+          mma_rows_swz<Et, D>(kt[buf], 32 * kk, qreg, s, ql, g);   // S^T[key][q]
+          mma_rows_swz<Et, D>(vt[buf], 32 * kk, dreg, dp, ql, g);  // dP^T[key][q]
         } else {
-          mma_rows_regs<BF, D>(kt[buf], 32 * kk, qreg, s, ql, g);
-          mma_rows_regs<BF, D>(vt[buf], 32 * kk, dreg, dp, ql, g);
+          mma_rows_regs<Et, D>(kt[buf], 32 * kk, qreg, s, ql, g);
+          mma_rows_regs<Et, D>(vt[buf], 32 * kk, dreg, dp, ql, g);
         }
         if (need_mask) {
           const int base = kb + 32 * kk + 4 * g;
@@ -267,34 +267,34 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
           dp[i] = p * (dp[i] - dlq);
         }
         if constexpr (SWZ) {
-          bf16x8 sb[2];
-          acc_to_bf16(dp, sb);
-          mma_tr_swz<D>(kt[buf], 32 * kk, sb, dq, lane);  // dQ^T += K^T dS^T
+          vec8<Et> sb[2];
+          acc_to_h16<Et>(dp, sb);
+          mma_tr_swz<Et, D>(kt[buf], 32 * kk, sb, dq, lane);  // dQ^T += K^T dS^T
         } else {
-          mma_tr_regs<BF, D>(kt[buf], 32 * kk, dp, dq, lane);
+          mma_tr_regs<Et, D>(kt[buf], 32 * kk, dp, dq, lane);
         }
       }
     }
     buf ^= 1;
   }
-  if (qvalid) store_acc_row<BF, D>(dqp, roff, dq, scale, g);
+  if (qvalid) store_acc_row<Et, D>(dqp, roff, dq, scale, g);
 }
 
-template <bool BF, int D>
+template <typename Et, int D>
 hipError_t bwd_dispatch(const void* dout, const void* q, const void* k, const void* v, const void* out,
                         const float* lse, const int32_t* cu, const int32_t* items, const int32_t* items32, int32_t B,
                         int32_t N, int32_t H, int32_t win, int64_t ld, float scale, void* dq, void* dk, void* dv,
                         float* delta, hipStream_t stream) {
-  using G = Geo<BF, D>;
+  using G = Geo<Et, D>;
   if (N == 0) return hipSuccess;
   const int64_t chunks = static_cast<int64_t>(N) * H * G::CH;
   hipEvent_t ev_bwd_delta = timing_start(stream);
-  hipLaunchKernelGGL((bwd_delta_kernel<BF, D>), dim3(static_cast<unsigned>((chunks + 255) / 256)), dim3(256), 0,
+  hipLaunchKernelGGL((bwd_delta_kernel<Et, D>), dim3(static_cast<unsigned>((chunks + 255) / 256)), dim3(256), 0,
                    stream, dout, out, N, H, delta);
   timing_stop("bwd_delta", ev_bwd_delta, stream);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (!BF && items32 != nullptr && (D == 32 || D == 64)) {
+  if (!kIs16<Et> && items32 != nullptr && (D == 32 || D == 64)) {
     e = launch_bwd_dkdv_f32_wave(D, dout, q, k, v, lse, delta, cu, items32, B, N, H, win, ld, scale, dk, dv,
                                  stream);
     if (e != hipSuccess) return e;
@@ -304,13 +304,13 @@ hipError_t bwd_dispatch(const void* dout, const void* q, const void* k, const vo
   const unsigned blocks = static_cast<unsigned>(static_cast<int64_t>(T) * H);
   const float c = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
   hipEvent_t ev_bwd_dkdv = timing_start(stream);
-  hipLaunchKernelGGL((bwd_dkdv_kernel<BF, D>), dim3(blocks), dim3(kThreads), 0, stream, dout, q, k, v, lse, delta,
+  hipLaunchKernelGGL((bwd_dkdv_kernel<Et, D>), dim3(blocks), dim3(kThreads), 0, stream, dout, q, k, v, lse, delta,
                    cu, items, B, N, H, T, win, ld, c, scale, dk, dv);
   timing_stop("bwd_dkdv", ev_bwd_dkdv, stream);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipEvent_t ev_bwd_dq = timing_start(stream);
-  hipLaunchKernelGGL((bwd_dq_kernel<BF, D>), dim3(blocks), dim3(kThreads), 0, stream, dout, q, k, v, lse, delta,
+  hipLaunchKernelGGL((bwd_dq_kernel<Et, D>), dim3(blocks), dim3(kThreads), 0, stream, dout, q, k, v, lse, delta,
                    cu, items, B, N, H, T, win, ld, c, scale, dq);
   timing_stop("bwd_dq", ev_bwd_dq, stream);
   return hipGetLastError();
@@ -318,16 +318,18 @@ hipError_t bwd_dispatch(const void* dout, const void* q, const void* k, const vo
 
 }  // namespace
 
-hipError_t launch_attn_bwd(bool bf16, int D, const void* dout, const void* q, const void* k, const void* v,
+hipError_t launch_attn_bwd(int dt, int D, const void* dout, const void* q, const void* k, const void* v,
                            const void* out, const float* lse, const int32_t* cu, const int32_t* items,
                            const int32_t* items32, int32_t B, int32_t N, int32_t H, int32_t win, int64_t ld,
                            float scale, void* dq, void* dk, void* dv, float* delta, hipStream_t stream) {
-#define PE_BWD_CASE(DD)                                                                                    \
-  case DD:                                                                                                \
-    return bf16 ? bwd_dispatch<true, DD>(dout, q, k, v, out, lse, cu, items, items32, B, N, H, win, ld, scale, dq,  \
-                                         dk, dv, delta, stream)                                           \
-                : bwd_dispatch<false, DD>(dout, q, k, v, out, lse, cu, items, items32, B, N, H, win, ld, scale, dq, \
-                                          dk, dv, delta, stream);
+#define PE_BWD_CASE(DD)                                                                                       \
+  case DD:                                                                                                   \
+    return dt == kDtF32  ? bwd_dispatch<float, DD>(dout, q, k, v, out, lse, cu, items, items32, B, N, H, win, ld, \
+                                                  scale, dq, dk, dv, delta, stream)                             \
+           : dt == kDtF16 ? bwd_dispatch<_Float16, DD>(dout, q, k, v, out, lse, cu, items, items32, B, N, H, win, \
+                                                     ld, scale, dq, dk, dv, delta, stream)                      \
+                         : bwd_dispatch<__bf16, DD>(dout, q, k, v, out, lse, cu, items, items32, B, N, H, win, ld, \
+                                                   scale, dq, dk, dv, delta, stream);
   switch (D) {
     PE_BWD_CASE(8)
     PE_BWD_CASE(16)

@@ -1,8 +1,8 @@
 // Building blocks shared by the attention kernels: tile geometry, staging of
 // 64-row tiles through LDS, and the two MFMA products every kernel is made of.
 //
-// All products work on 32x32 output blocks of v_mfma_f32_32x32x16_bf16 (bf16)
-// or v_mfma_f32_32x32x2_f32 (fp32). In the 32x32 accumulator layout lane l,
+// All products work on 32x32 output blocks of v_mfma_f32_32x32x16_bf16 / _f16
+// (16-bit elements) or v_mfma_f32_32x32x2_f32 (fp32). In the 32x32 accumulator layout lane l,
 // register i holds row 8*(i/4) + 4*(l/32) + (i%4), column l%32. Kernels place
 // the index they keep per lane (a query in the forward and dQ kernels, a key in
 // the dK/dV kernel) on the columns, so each lane owns one row of attention
@@ -35,30 +35,27 @@ constexpr int kThreads = 256;  // 4 waves per block
 typedef uint16_t u16x4 __attribute__((ext_vector_type(4)));
 typedef short shortx4 __attribute__((ext_vector_type(4)));
 
-template <bool BF, int D>
+template <typename Et, int D>
 struct Geo {
-  using E = typename std::conditional<BF, uint16_t, float>::type;
-  static constexpr int ES = BF ? 2 : 4;
+  using E = typename std::conditional<kIs16<Et>, uint16_t, float>::type;
+  static constexpr int ES = kIs16<Et> ? 2 : 4;
   static constexpr int ROWB = D * ES;              // bytes of one head row
   static constexpr int CH = ROWB / 16;             // 16-byte chunks per head row
   static constexpr int EPC = 16 / ES;              // elements per chunk
-  static constexpr int ST = BF ? D + 8 : D + 4;    // LDS row stride in elements
+  static constexpr int ST = kIs16<Et> ? D + 8 : D + 4;    // LDS row stride in elements
   static constexpr int TSZ = kBlk * ST;            // elements of one staged tile
   static constexpr int HALF = D / 2;               // head-dim elements per lane half
-  static constexpr int QS = BF ? (HALF + 7) / 8 : HALF;  // MFMA steps over head_dim
+  static constexpr int QS = kIs16<Et> ? (HALF + 7) / 8 : HALF;  // MFMA steps over head_dim
   static constexpr int DB = (D + 31) / 32;         // 32-row blocks over head_dim
   static constexpr int TOTCH = kBlk * CH;
   static constexpr int PER = (TOTCH + kThreads - 1) / kThreads;
 };
 
-template <bool BF>
-struct RegT;
+// per-lane operand type of the products: an 8-element vector, or one float
+template <typename Et>
+struct RegT { using type = vec8<Et>; };
 template <>
-struct RegT<true> { using T = bf16x8; };
-template <>
-struct RegT<false> { using T = float; };
-
-__device__ __forceinline__ bf16x8 as_bf16x8(u16x8 x) { return __builtin_bit_cast(bf16x8, x); }
+struct RegT<float> { using type = float; };
 
 __device__ __forceinline__ u16x4 ds_read_tr16(const uint16_t* p) {
   const shortx4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
@@ -77,11 +74,11 @@ __device__ __forceinline__ float xhalf_sum(float x) {
 }
 
 // The lane's own head row (elements g*HALF .. g*HALF+HALF-1) as MFMA operands.
-template <bool BF, int D>
+template <typename Et, int D>
 __device__ __forceinline__ void load_row_regs(const void* base, int64_t off, bool valid,
-                                              typename RegT<BF>::T (&r)[Geo<BF, D>::QS]) {
-  using G = Geo<BF, D>;
-  if constexpr (BF) {
+                                              typename RegT<Et>::type (&r)[Geo<Et, D>::QS]) {
+  using G = Geo<Et, D>;
+  if constexpr (kIs16<Et>) {
     const uint16_t* src = static_cast<const uint16_t*>(base) + off;
 #pragma unroll
     for (int s = 0; s < G::QS; ++s) {
@@ -94,7 +91,7 @@ __device__ __forceinline__ void load_row_regs(const void* base, int64_t off, boo
           for (int j = 0; j < G::HALF; ++j) x[j] = src[j];
         }
       }
-      r[s] = as_bf16x8(x);
+      r[s] = as_vec8<Et>(x);
     }
   } else {
     const float* src = static_cast<const float*>(base) + off;
@@ -105,10 +102,10 @@ __device__ __forceinline__ void load_row_regs(const void* base, int64_t off, boo
 
 // Global -> registers for one 64-row tile of head h of a tensor whose rows are
 // `ld` elements apart; rows >= row_lim are zero.
-template <bool BF, int D>
+template <typename Et, int D>
 __device__ __forceinline__ void tile_gload(const void* base, int row0, int row_lim, int64_t ld, int h,
-                                           uint4 (&r)[Geo<BF, D>::PER]) {
-  using G = Geo<BF, D>;
+                                           uint4 (&r)[Geo<Et, D>::PER]) {
+  using G = Geo<Et, D>;
   const char* b = static_cast<const char*>(base);
 #pragma unroll
   for (int p = 0; p < G::PER; ++p) {
@@ -125,9 +122,9 @@ __device__ __forceinline__ void tile_gload(const void* base, int row0, int row_l
 }
 
 // Registers -> LDS tile [kBlk][ST], row-major.
-template <bool BF, int D>
-__device__ __forceinline__ void tile_store(typename Geo<BF, D>::E* tile, const uint4 (&r)[Geo<BF, D>::PER]) {
-  using G = Geo<BF, D>;
+template <typename Et, int D>
+__device__ __forceinline__ void tile_store(typename Geo<Et, D>::E* tile, const uint4 (&r)[Geo<Et, D>::PER]) {
+  using G = Geo<Et, D>;
 #pragma unroll
   for (int p = 0; p < G::PER; ++p) {
     const int ch = threadIdx.x + p * kThreads;
@@ -140,15 +137,15 @@ __device__ __forceinline__ void tile_store(typename Geo<BF, D>::E* tile, const u
 
 // acc += X . Y^T over head_dim; X = rows row0..row0+31 of an LDS tile (row l%32
 // for lane l), Y = the lane's row in registers.
-template <bool BF, int D>
-__device__ __forceinline__ void mma_rows_regs(const typename Geo<BF, D>::E* tile, int row0,
-                                              const typename RegT<BF>::T (&y)[Geo<BF, D>::QS],
+template <typename Et, int D>
+__device__ __forceinline__ void mma_rows_regs(const typename Geo<Et, D>::E* tile, int row0,
+                                              const typename RegT<Et>::type (&y)[Geo<Et, D>::QS],
                                               floatx16& acc, int ql, int g) {
-  using G = Geo<BF, D>;
+  using G = Geo<Et, D>;
   const typename G::E* xr = tile + (row0 + ql) * G::ST + g * G::HALF;
 #pragma unroll
   for (int st = 0; st < G::QS; ++st) {
-    if constexpr (BF) {
+    if constexpr (kIs16<Et>) {
       u16x8 a;
       if constexpr (G::HALF >= 8) {
         a = *reinterpret_cast<const u16x8*>(xr + 8 * st);
@@ -157,7 +154,7 @@ __device__ __forceinline__ void mma_rows_regs(const typename Geo<BF, D>::E* tile
 #pragma unroll
         for (int j = 0; j < G::HALF; ++j) a[j] = xr[j];
       }
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), y[st], acc, 0, 0, 0);
+      acc = mfma16<Et>(as_vec8<Et>(a), y[st], acc);
     } else {
       acc = __builtin_amdgcn_mfma_f32_32x32x2f32(xr[st], y[st], acc, 0, 0, 0);
     }
@@ -166,18 +163,18 @@ __device__ __forceinline__ void mma_rows_regs(const typename Geo<BF, D>::E* tile
 
 // acc[db] += X^T . P; X = rows row0..row0+31 of an LDS tile (reduction index),
 // P = 32x32 accumulator block whose rows are those 32 tile rows.
-template <bool BF, int D>
-__device__ __forceinline__ void mma_tr_regs(const typename Geo<BF, D>::E* tile, int row0, const floatx16& p,
-                                            floatx16 (&acc)[Geo<BF, D>::DB], int lane) {
-  using G = Geo<BF, D>;
+template <typename Et, int D>
+__device__ __forceinline__ void mma_tr_regs(const typename Geo<Et, D>::E* tile, int row0, const floatx16& p,
+                                            floatx16 (&acc)[Geo<Et, D>::DB], int lane) {
+  using G = Geo<Et, D>;
   const int ql = lane & 31, g = lane >> 5;
-  if constexpr (BF) {
+  if constexpr (kIs16<Et>) {
     const int sub = lane & 15, grp = (lane >> 4) & 1;
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
-      bf16x8 pb;
+      vec8<Et> pb;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) pb[j] = static_cast<__bf16>(p[8 * s + j]);
+      for (int j = 0; j < 8; ++j) pb[j] = static_cast<Et>(p[8 * s + j]);
       const int rowa = row0 + 16 * s + 4 * g + (sub >> 2);
 #pragma unroll
       for (int db = 0; db < G::DB; ++db) {
@@ -189,7 +186,7 @@ __device__ __forceinline__ void mma_tr_regs(const typename Geo<BF, D>::E* tile, 
         if constexpr (D % 32 != 0) {
           if (db * 32 + ql >= D) a = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
         }
-        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), pb, acc[db], 0, 0, 0);
+        acc[db] = mfma16<Et>(as_vec8<Et>(a), pb, acc[db]);
       }
     }
   } else {
@@ -208,20 +205,20 @@ __device__ __forceinline__ void mma_tr_regs(const typename Geo<BF, D>::E* tile, 
 
 // Store a [d x 32] accumulator (lane = row of the output, registers = head dim)
 // to out[row][h][:], multiplied by `mul`.
-template <bool BF, int D>
-__device__ __forceinline__ void store_acc_row(void* outp, int64_t off, const floatx16 (&acc)[Geo<BF, D>::DB],
+template <typename Et, int D>
+__device__ __forceinline__ void store_acc_row(void* outp, int64_t off, const floatx16 (&acc)[Geo<Et, D>::DB],
                                               float mul, int g) {
-  using G = Geo<BF, D>;
+  using G = Geo<Et, D>;
 #pragma unroll
   for (int db = 0; db < G::DB; ++db)
 #pragma unroll
     for (int i4 = 0; i4 < 4; ++i4) {
       const int d0 = db * 32 + 8 * i4 + 4 * g;
       if (d0 < D) {
-        if constexpr (BF) {
+        if constexpr (kIs16<Et>) {
           uint16_t* O = static_cast<uint16_t*>(outp) + off + d0;
-          const uint32_t lo = f32_to_bf16(acc[db][4 * i4 + 0] * mul) | (uint32_t(f32_to_bf16(acc[db][4 * i4 + 1] * mul)) << 16);
-          const uint32_t hi = f32_to_bf16(acc[db][4 * i4 + 2] * mul) | (uint32_t(f32_to_bf16(acc[db][4 * i4 + 3] * mul)) << 16);
+          const uint32_t lo = f32_to_h16<Et>(acc[db][4 * i4 + 0] * mul) | (uint32_t(f32_to_h16<Et>(acc[db][4 * i4 + 1] * mul)) << 16);
+          const uint32_t hi = f32_to_h16<Et>(acc[db][4 * i4 + 2] * mul) | (uint32_t(f32_to_h16<Et>(acc[db][4 * i4 + 3] * mul)) << 16);
           *reinterpret_cast<uint2*>(O) = make_uint2(lo, hi);
         } else {
           float* O = static_cast<float*>(outp) + off + d0;
@@ -290,8 +287,8 @@ __device__ __forceinline__ void mask_block(floatx16& s, int lo, int hi) {
   }
 }
 
-// ---------------------------------------------------------------- bf16 tiles staged by LDS DMA
-// bf16 tiles of kBlk rows x D elements are copied global -> LDS by
+// ---------------------------------------------------------------- 16-bit tiles staged by LDS DMA
+// bf16 or fp16 tiles of kBlk rows x D elements are copied global -> LDS by
 // global_load_lds_dwordx4 (no registers, no VALU) into a ring of stages. Rows
 // are not padded; instead the 16-byte chunk c of row r sits at position
 // c ^ swz(r) of the row. With 64 LDS banks of 4 bytes this puts the 16 rows of
@@ -323,19 +320,19 @@ __device__ __forceinline__ void vmem_fence_for_compiler() { __builtin_amdgcn_s_w
 // (LDS-DMA completion) are issued explicitly before it.
 __device__ __forceinline__ void raw_barrier() { asm volatile("s_barrier" ::: "memory"); }
 
-// DMA instructions each thread issues per bf16 tile of head dim D
+// DMA instructions each thread issues per 16-bit tile of head dim D
 template <int D>
 constexpr int dma_per_tile() { return kBlk * (D / 8) / kThreads; }
 
 // Issue the LDS-DMA copy of rows row0..row0+kBlk-1 of head h of a [N, H, D]
-// bf16 tensor into an LDS tile. Rows >= row_lim repeat row row_lim-1 (valid
+// 16-bit tensor into an LDS tile. Rows >= row_lim repeat row row_lim-1 (valid
 // memory; kernels mask those keys). A wave's instruction fills 64 consecutive
 // 16-byte LDS slots (M0 = wave base, lane l -> slot l); the global address of
 // each lane is chosen so that the slot receives its swizzled chunk.
 // The copy is asynchronous: it is complete for this thread once vmcnt drops
 // below the number of later VMEM instructions.
 template <int D>
-__device__ __forceinline__ void dma_tile_bf16(const uint16_t* lds_tile, const void* gbase, int row0, int row_lim,
+__device__ __forceinline__ void dma_tile16(const uint16_t* lds_tile, const void* gbase, int row0, int row_lim,
                                               int H, int h) {
   constexpr int CH = D / 8;
   constexpr int NLD = dma_per_tile<D>();
@@ -365,18 +362,18 @@ __device__ __forceinline__ void dma16(uint32_t lds, const void* sbase, uint32_t 
                : "memory", "m0");
 }
 
-// A operand (8 bf16 along head_dim) of mma over a swizzled tile: row r,
-// logical chunk c.
-template <int CH>
-__device__ __forceinline__ bf16x8 swz_read_b128(const uint16_t* tile, int r, int c) {
-  return as_bf16x8(*reinterpret_cast<const u16x8*>(reinterpret_cast<const char*>(tile) + chunk_off<CH>(r, c)));
+// A operand (8 16-bit elements along head_dim) of mma over a swizzled tile:
+// row r, logical chunk c.
+template <typename Et, int CH>
+__device__ __forceinline__ vec8<Et> swz_read_b128(const uint16_t* tile, int r, int c) {
+  return as_vec8<Et>(*reinterpret_cast<const u16x8*>(reinterpret_cast<const char*>(tile) + chunk_off<CH>(r, c)));
 }
 
-// Registers (as loaded by tile_gload) -> unpadded bf16 tile of kBlk rows with
+// Registers (as loaded by tile_gload) -> unpadded 16-bit tile of kBlk rows with
 // XOR-swizzled 16-byte chunks.
 template <int D>
-__device__ __forceinline__ void tile_store_swz(uint16_t* tile, const uint4 (&r)[Geo<true, D>::PER]) {
-  using G = Geo<true, D>;
+__device__ __forceinline__ void tile_store_swz(uint16_t* tile, const uint4 (&r)[Geo<__bf16, D>::PER]) {
+  using G = Geo<__bf16, D>;
   constexpr int CH = D / 8;
 #pragma unroll
   for (int p = 0; p < G::PER; ++p) {
@@ -388,28 +385,28 @@ __device__ __forceinline__ void tile_store_swz(uint16_t* tile, const uint4 (&r)[
   }
 }
 
-// The mma_rows_regs product over a swizzled bf16 tile.
-template <int D>
-__device__ __forceinline__ void mma_rows_swz(const uint16_t* tile, int row0, const bf16x8 (&y)[D / 16],
+// The mma_rows_regs product over a swizzled 16-bit tile.
+template <typename Et, int D>
+__device__ __forceinline__ void mma_rows_swz(const uint16_t* tile, int row0, const vec8<Et> (&y)[D / 16],
                                              floatx16& acc, int ql, int g) {
   constexpr int CH = D / 8;
 #pragma unroll
   for (int st = 0; st < D / 16; ++st)
-    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(swz_read_b128<CH>(tile, row0 + ql, g * (CH / 2) + st), y[st], acc,
-                                                  0, 0, 0);
+    acc = mfma16<Et>(swz_read_b128<Et, CH>(tile, row0 + ql, g * (CH / 2) + st), y[st], acc);
 }
 
-// The 16 values of a 32x32 accumulator block as two bf16 MFMA B operands.
-__device__ __forceinline__ void acc_to_bf16(const floatx16& p, bf16x8 (&pb)[2]) {
+// The 16 values of a 32x32 accumulator block as two 16-bit MFMA B operands.
+template <typename Et>
+__device__ __forceinline__ void acc_to_h16(const floatx16& p, vec8<Et> (&pb)[2]) {
 #pragma unroll
   for (int s = 0; s < 2; ++s)
 #pragma unroll
-    for (int j = 0; j < 8; ++j) pb[s][j] = static_cast<__bf16>(p[8 * s + j]);
+    for (int j = 0; j < 8; ++j) pb[s][j] = static_cast<Et>(p[8 * s + j]);
 }
 
-// acc[db] += X^T . P over a swizzled bf16 tile (the mma_tr_regs product).
-template <int D>
-__device__ __forceinline__ void mma_tr_swz(const uint16_t* tile, int row0, const bf16x8 (&pb)[2],
+// acc[db] += X^T . P over a swizzled 16-bit tile (the mma_tr_regs product).
+template <typename Et, int D>
+__device__ __forceinline__ void mma_tr_swz(const uint16_t* tile, int row0, const vec8<Et> (&pb)[2],
                                            floatx16 (&acc)[D / 32], int lane) {
   constexpr int CH = D / 8;
   const int g = lane >> 5, sub = lane & 15, grp = (lane >> 4) & 1;
@@ -424,19 +421,21 @@ __device__ __forceinline__ void mma_tr_swz(const uint16_t* tile, int row0, const
       const u16x4 lo = ds_read_tr16(reinterpret_cast<const uint16_t*>(t + chunk_off<CH>(rowa, c) + within));
       const u16x4 hi = ds_read_tr16(reinterpret_cast<const uint16_t*>(t + chunk_off<CH>(rowa + 8, c) + within));
       const u16x8 a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-      acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), pb[s], acc[db], 0, 0, 0);
+      acc[db] = mfma16<Et>(as_vec8<Et>(a), pb[s], acc[db]);
     }
   }
 }
 
-// Round the 16 probabilities of a 32x32 accumulator block to bf16 (two MFMA
-// B operands) and add their fp32 sum to l. The log-sum-exp needs the sum of the
-// unrounded values: bf16 rounding would move it by up to 2^-9 relative.
-__device__ __forceinline__ void probs_to_bf16(const floatx16& p, bf16x8 (&pb)[2], float& l) {
+// Round the 16 probabilities of a 32x32 accumulator block to the 16-bit type
+// (two MFMA B operands) and add their fp32 sum to l. The log-sum-exp needs the
+// sum of the unrounded values: bf16 rounding would move it by up to 2^-9
+// relative (fp16 by 2^-12).
+template <typename Et>
+__device__ __forceinline__ void probs_to_h16(const floatx16& p, vec8<Et> (&pb)[2], float& l) {
 #pragma unroll
   for (int s = 0; s < 2; ++s)
 #pragma unroll
-    for (int j = 0; j < 8; ++j) pb[s][j] = static_cast<__bf16>(p[8 * s + j]);
+    for (int j = 0; j < 8; ++j) pb[s][j] = static_cast<Et>(p[8 * s + j]);
   float acc0 = p[0], acc1 = p[1];  // two chains
 #pragma unroll
   for (int i = 2; i < 16; i += 2) {

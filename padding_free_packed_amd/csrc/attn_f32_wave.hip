@@ -161,7 +161,7 @@ __global__ __launch_bounds__(64, 2) void attn_fwd_f32_kernel(
   const float lt = xhalf_sum(l);
   const float inv = lt > 0.f ? 1.f / lt : 0.f;
   if (qvalid) {
-    store_acc_row<false, D>(op, (static_cast<int64_t>(qrow) * H + h) * D, o, inv, g);
+    store_acc_row<float, D>(op, (static_cast<int64_t>(qrow) * H + h) * D, o, inv, g);
     if (lse != nullptr && g == 0) lse[static_cast<int64_t>(h) * N + qrow] = (m + log2f(lt)) * kLn2;
   }
 }
@@ -322,7 +322,7 @@ __global__ __launch_bounds__(64, 2) void bwd_dq_f32_kernel(
       if (more) load_tr<D>(kt, at(kp, kb + 32, LD), klast - kb - 32, LD, ql, g);
     }
   }
-  if (qvalid) store_acc_row<false, D>(dqp, static_cast<int64_t>(qrow) * ld + hoff, dq, scale, g);
+  if (qvalid) store_acc_row<float, D>(dqp, static_cast<int64_t>(qrow) * ld + hoff, dq, scale, g);
 }
 
 }  // namespace
@@ -463,8 +463,8 @@ __global__ __launch_bounds__(64, D > 32 ? 1 : 2) void bwd_dkdv_f32_kernel(
   }
   if (kvalid) {
     const int64_t off = static_cast<int64_t>(krow) * ld + hoff;
-    store_acc_row<false, D>(dkp, off, dk, scale, g);
-    store_acc_row<false, D>(dvp, off, dv, 1.0f, g);
+    store_acc_row<float, D>(dkp, off, dk, scale, g);
+    store_acc_row<float, D>(dvp, off, dv, 1.0f, g);
   }
 }
 

@@ -23,17 +23,17 @@ namespace {
 constexpr int kFbThreads = 512;
 constexpr int kFbBatch = 4;
 
-template <bool BF, int D>
+template <typename Et, int D>
 __global__ __launch_bounds__(kFbThreads) void attn_bwd_first_kernel(
     const void* __restrict__ dof, const void* __restrict__ qf, const void* __restrict__ kp,
     const void* __restrict__ vp, const void* __restrict__ of, const float* __restrict__ lse,
     const int32_t* __restrict__ cu, int32_t B, int32_t N, int32_t H, int32_t HPB, int64_t ld, float c, float scale,
     void* __restrict__ dqp, void* __restrict__ dkp, void* __restrict__ dvp) {
-  constexpr int ES = BF ? 2 : 4;
+  constexpr int ES = kIs16<Et> ? 2 : 4;
   constexpr int EPC = 16 / ES;  // elements per 16-byte chunk
   constexpr int GS = D / EPC;   // chunks (threads) per head row
   constexpr int U = kFbBatch;
-  using Chunk = typename std::conditional<BF, u16x8, float4>::type;
+  using Chunk = typename std::conditional<kIs16<Et>, u16x8, float4>::type;
   __shared__ float sq[kFbThreads * EPC];
 
   const int b = blockIdx.x;
@@ -47,18 +47,18 @@ __global__ __launch_bounds__(kFbThreads) void attn_bwd_first_kernel(
   const bool active = slot < KS && h < H;
 
   auto widen = [](const Chunk& x, float (&y)[EPC]) __attribute__((always_inline)) {
-    if constexpr (BF) {
+    if constexpr (kIs16<Et>) {
 #pragma unroll
-      for (int e = 0; e < EPC; ++e) y[e] = bf16_to_f32(x[e]);
+      for (int e = 0; e < EPC; ++e) y[e] = h16_to_f32<Et>(x[e]);
     } else {
       y[0] = x.x; y[1] = x.y; y[2] = x.z; y[3] = x.w;
     }
   };
   auto narrow = [](const float (&y)[EPC]) __attribute__((always_inline)) {
     Chunk x;
-    if constexpr (BF) {
+    if constexpr (kIs16<Et>) {
 #pragma unroll
-      for (int e = 0; e < EPC; ++e) x[e] = f32_to_bf16(y[e]);
+      for (int e = 0; e < EPC; ++e) x[e] = f32_to_h16<Et>(y[e]);
     } else {
       x = make_float4(y[0], y[1], y[2], y[3]);
     }
@@ -147,16 +147,16 @@ __global__ __launch_bounds__(kFbThreads) void attn_bwd_first_kernel(
   }
 }
 
-template <bool BF, int D>
+template <typename Et, int D>
 hipError_t bwd_first_dispatch(const void* dof, const void* qf, const void* k, const void* v, const void* of,
                               const float* lse, const int32_t* cu, int32_t B, int32_t N, int32_t H, int64_t ld,
                               float scale, void* dq, void* dk, void* dv, hipStream_t stream) {
-  constexpr int GS = D / (BF ? 8 : 4);
+  constexpr int GS = D / (kIs16<Et> ? 8 : 4);
   const int HPB = (H * GS <= kFbThreads) ? H : kFbThreads / GS;
   const int HG = (H + HPB - 1) / HPB;
   const float c = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
   hipEvent_t ev = timing_start(stream);
-  hipLaunchKernelGGL((attn_bwd_first_kernel<BF, D>), dim3(B, HG), dim3(kFbThreads), 0, stream, dof, qf, k, v, of,
+  hipLaunchKernelGGL((attn_bwd_first_kernel<Et, D>), dim3(B, HG), dim3(kFbThreads), 0, stream, dof, qf, k, v, of,
                      lse, cu, B, N, H, HPB, ld, c, scale, dq, dk, dv);
   timing_stop("attn_bwd_first", ev, stream);
   return hipGetLastError();
@@ -164,25 +164,27 @@ hipError_t bwd_first_dispatch(const void* dof, const void* qf, const void* k, co
 
 }  // namespace
 
-hipError_t launch_attn_bwd_first(bool bf16, int D, const void* dout_first, const void* q_first, const void* k,
+hipError_t launch_attn_bwd_first(int dt, int D, const void* dout_first, const void* q_first, const void* k,
                                  const void* v, const void* out_first, const float* lse_first, const int32_t* cu,
                                  int32_t B, int32_t N, int32_t H, int64_t ld, float scale, void* dq_first, void* dk,
                                  void* dv, hipStream_t stream) {
-#define PE_BF_CASE(DD)                                                                                         \
-  case DD:                                                                                                    \
-    return bf16 ? bwd_first_dispatch<true, DD>(dout_first, q_first, k, v, out_first, lse_first, cu, B, N, H, ld,  \
-                                               scale, dq_first, dk, dv, stream)                                   \
-                : bwd_first_dispatch<false, DD>(dout_first, q_first, k, v, out_first, lse_first, cu, B, N, H, ld, \
-                                                scale, dq_first, dk, dv, stream);
+#define PE_FB_CASE(DD)                                                                                        \
+  case DD:                                                                                                   \
+    return dt == kDtF32  ? bwd_first_dispatch<float, DD>(dout_first, q_first, k, v, out_first, lse_first, cu, B, N, \
+                                                        H, ld, scale, dq_first, dk, dv, stream)                   \
+           : dt == kDtF16 ? bwd_first_dispatch<_Float16, DD>(dout_first, q_first, k, v, out_first, lse_first, cu, B, \
+                                                           N, H, ld, scale, dq_first, dk, dv, stream)             \
+                         : bwd_first_dispatch<__bf16, DD>(dout_first, q_first, k, v, out_first, lse_first, cu, B, N, \
+                                                         H, ld, scale, dq_first, dk, dv, stream);
   switch (D) {
-    PE_BF_CASE(8)
-    PE_BF_CASE(16)
-    PE_BF_CASE(32)
-    PE_BF_CASE(64)
-    PE_BF_CASE(128)
+    PE_FB_CASE(8)
+    PE_FB_CASE(16)
+    PE_FB_CASE(32)
+    PE_FB_CASE(64)
+    PE_FB_CASE(128)
     default: return hipErrorInvalidValue;
   }
-#undef PE_BF_CASE
+#undef PE_FB_CASE
 }
 
 }  // namespace pe

@@ -22,16 +22,16 @@ namespace pe {
 
 namespace {
 
-template <bool BF, int D>
+template <typename Et, int D>
 __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
     const void* __restrict__ qp, const void* __restrict__ kp, const void* __restrict__ vp,
     const int32_t* __restrict__ cu, const int32_t* __restrict__ items, int32_t B, int32_t N,
     int32_t H, int32_t T, int32_t win, int64_t ld, float c, void* __restrict__ op, float* __restrict__ lse) {
-  using G = Geo<BF, D>;
+  using G = Geo<Et, D>;
   using E = typename G::E;
   // bf16 tiles with whole 16-byte chunks per lane half use the XOR-swizzled layout
   // (conflict-free for both the row reads and the transposing reads)
-  constexpr bool SWZ = BF && D % 32 == 0;
+  constexpr bool SWZ = kIs16<Et> && D % 32 == 0;
   constexpr int TS = SWZ ? kBlk * D : G::TSZ;
   __shared__ __align__(16) E kt[2][TS];
   __shared__ __align__(16) E vt[2][TS];
@@ -58,8 +58,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
   const int mk0 = wave_max_i(qvalid ? qk0 : INT_MIN);  // keys every row of the wave needs
   const int mk1 = wave_min_i(qvalid ? qk1 : INT_MAX);
 
-  typename RegT<BF>::T qr[G::QS];
-  load_row_regs<BF, D>(qp, static_cast<int64_t>(qrow) * ld + h * D + g * G::HALF, qvalid, qr);
+  typename RegT<Et>::type qr[G::QS];
+  load_row_regs<Et, D>(qp, static_cast<int64_t>(qrow) * ld + h * D + g * G::HALF, qvalid, qr);
 
   uint4 kr[G::PER], vr[G::PER];
   floatx16 o[G::DB];
@@ -72,29 +72,29 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
   const int khi = win >= 0 ? min(sp.hi, sp.rend + win) : sp.hi;
   int buf = 0;
   if (klo < khi) {
-    tile_gload<BF, D>(kp, klo, khi, ld, h, kr);
-    tile_gload<BF, D>(vp, klo, khi, ld, h, vr);
+    tile_gload<Et, D>(kp, klo, khi, ld, h, kr);
+    tile_gload<Et, D>(vp, klo, khi, ld, h, vr);
   }
   for (int kb = klo; kb < khi; kb += kBlk) {
     if constexpr (SWZ) {
       tile_store_swz<D>(kt[buf], kr);
       tile_store_swz<D>(vt[buf], vr);
     } else {
-      tile_store<BF, D>(kt[buf], kr);
-      tile_store<BF, D>(vt[buf], vr);
+      tile_store<Et, D>(kt[buf], kr);
+      tile_store<Et, D>(vt[buf], vr);
     }
     __syncthreads();
     if (kb + kBlk < khi) {
-      tile_gload<BF, D>(kp, kb + kBlk, khi, ld, h, kr);
-      tile_gload<BF, D>(vp, kb + kBlk, khi, ld, h, vr);
+      tile_gload<Et, D>(kp, kb + kBlk, khi, ld, h, kr);
+      tile_gload<Et, D>(vp, kb + kBlk, khi, ld, h, vr);
     }
     if (kb < wk1 && kb + kBlk > wk0) {
       floatx16 s[2];
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
         s[kk] = floatx16{};
-        if constexpr (SWZ) mma_rows_swz<D>(kt[buf], 32 * kk, qr, s[kk], ql, g);
-        else mma_rows_regs<BF, D>(kt[buf], 32 * kk, qr, s[kk], ql, g);
+        if constexpr (SWZ) mma_rows_swz<Et, D>(kt[buf], 32 * kk, qr, s[kk], ql, g);
+        else mma_rows_regs<Et, D>(kt[buf], 32 * kk, qr, s[kk], ql, g);
       }
       if (!(kb >= mk0 && kb + kBlk <= mk1)) {
 #pragma unroll
@@ -130,11 +130,11 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
         if constexpr (SWZ) {
-          bf16x8 pb[2];
-          acc_to_bf16(s[kk], pb);
-          mma_tr_swz<D>(vt[buf], 32 * kk, pb, o, lane);
+          vec8<Et> pb[2];
+          acc_to_h16<Et>(s[kk], pb);
+          mma_tr_swz<Et, D>(vt[buf], 32 * kk, pb, o, lane);
         } else {
-          mma_tr_regs<BF, D>(vt[buf], 32 * kk, s[kk], o, lane);
+          mma_tr_regs<Et, D>(vt[buf], 32 * kk, s[kk], o, lane);
         }
       }
     }
@@ -144,7 +144,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
   const float lt = xhalf_sum(l);
   const float inv = lt > 0.f ? 1.f / lt : 0.f;
   if (qvalid) {
-    store_acc_row<BF, D>(op, (static_cast<int64_t>(qrow) * H + h) * D, o, inv, g);
+    store_acc_row<Et, D>(op, (static_cast<int64_t>(qrow) * H + h) * D, o, inv, g);
     if (lse != nullptr && g == 0) lse[static_cast<int64_t>(h) * N + qrow] = (m + log2f(lt)) * kLn2;
   }
 }
@@ -160,16 +160,16 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
 constexpr int kFirstThreads = 512;
 constexpr int kFirstBatch = 4;
 
-template <bool BF, int D>
+template <typename Et, int D>
 __global__ __launch_bounds__(kFirstThreads) void attn_fwd_first_kernel(
     const void* __restrict__ qf, const void* __restrict__ kp, const void* __restrict__ vp,
     const int32_t* __restrict__ cu, int32_t B, int32_t N, int32_t H, int32_t HPB, int32_t gather, int64_t ld,
     float c, void* __restrict__ outp, float* __restrict__ lse) {
-  constexpr int ES = BF ? 2 : 4;
+  constexpr int ES = kIs16<Et> ? 2 : 4;
   constexpr int EPC = 16 / ES;       // elements per 16-byte chunk
   constexpr int GS = D / EPC;        // chunks (threads) per head row
   constexpr int U = kFirstBatch;
-  using Chunk = typename std::conditional<BF, u16x8, float4>::type;
+  using Chunk = typename std::conditional<kIs16<Et>, u16x8, float4>::type;
   __shared__ float sm[kFirstThreads], sl[kFirstThreads];
   __shared__ float so[kFirstThreads * EPC];
 
@@ -189,9 +189,9 @@ __global__ __launch_bounds__(kFirstThreads) void attn_fwd_first_kernel(
 #pragma unroll
   for (int e = 0; e < EPC; ++e) ov[e] = 0.f;
   auto widen = [](const Chunk& x, float (&y)[EPC]) __attribute__((always_inline)) {
-    if constexpr (BF) {
+    if constexpr (kIs16<Et>) {
 #pragma unroll
-      for (int e = 0; e < EPC; ++e) y[e] = bf16_to_f32(x[e]);
+      for (int e = 0; e < EPC; ++e) y[e] = h16_to_f32<Et>(x[e]);
     } else {
       y[0] = x.x; y[1] = x.y; y[2] = x.z; y[3] = x.w;
     }
@@ -263,10 +263,10 @@ __global__ __launch_bounds__(kFirstThreads) void attn_fwd_first_kernel(
     }
     const float inv = L > 0.f ? 1.f / L : 0.f;
     const int64_t off = (static_cast<int64_t>(b) * H + h) * D + sub * EPC;
-    if constexpr (BF) {
+    if constexpr (kIs16<Et>) {
       u16x8 y;
 #pragma unroll
-      for (int e = 0; e < EPC; ++e) y[e] = f32_to_bf16(acc[e] * inv);
+      for (int e = 0; e < EPC; ++e) y[e] = f32_to_h16<Et>(acc[e] * inv);
       *reinterpret_cast<u16x8*>(static_cast<uint16_t*>(outp) + off) = y;
     } else {
       *reinterpret_cast<float4*>(static_cast<float*>(outp) + off) =
@@ -276,7 +276,7 @@ __global__ __launch_bounds__(kFirstThreads) void attn_fwd_first_kernel(
   }
 }
 
-template <bool BF, int D>
+template <typename Et, int D>
 hipError_t fwd_dispatch(const void* q, const void* k, const void* v, const int32_t* cu,
                         const int32_t* items, int32_t B, int32_t N, int32_t H, int32_t win, int64_t ld,
                         float scale, void* out, float* lse, hipStream_t stream) {
@@ -285,22 +285,22 @@ hipError_t fwd_dispatch(const void* q, const void* k, const void* v, const int32
   if (blocks == 0) return hipSuccess;
   const float c = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
   hipEvent_t ev_attn_fwd = timing_start(stream);
-  hipLaunchKernelGGL((attn_fwd_kernel<BF, D>), dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0, stream,
+  hipLaunchKernelGGL((attn_fwd_kernel<Et, D>), dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0, stream,
                    q, k, v, cu, items, B, N, H, T, win, ld, c, out, lse);
   timing_stop("attn_fwd", ev_attn_fwd, stream);
   return hipGetLastError();
 }
 
-template <bool BF, int D>
+template <typename Et, int D>
 hipError_t first_dispatch(const void* q, const void* k, const void* v, const int32_t* cu, int32_t B,
                           int32_t N, int32_t H, int32_t gather, int64_t ld, float scale, void* out, float* lse,
                           hipStream_t stream) {
-  constexpr int GS = D / (BF ? 8 : 4);
+  constexpr int GS = D / (kIs16<Et> ? 8 : 4);
   const int HPB = (H * GS <= kFirstThreads) ? H : kFirstThreads / GS;
   const int HG = (H + HPB - 1) / HPB;
   const float c = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
   hipEvent_t ev_attn_fwd_first = timing_start(stream);
-  hipLaunchKernelGGL((attn_fwd_first_kernel<BF, D>), dim3(B, HG), dim3(kFirstThreads), 0, stream, q, k, v, cu, B,
+  hipLaunchKernelGGL((attn_fwd_first_kernel<Et, D>), dim3(B, HG), dim3(kFirstThreads), 0, stream, q, k, v, cu, B,
                    N, H, HPB, gather, ld, c, out, lse);
   timing_stop("attn_fwd_first", ev_attn_fwd_first, stream);
   return hipGetLastError();
@@ -308,19 +308,21 @@ hipError_t first_dispatch(const void* q, const void* k, const void* v, const int
 
 }  // namespace
 
-hipError_t launch_attn_fwd(bool bf16, int D, const void* q, const void* k, const void* v,
+hipError_t launch_attn_fwd(int dt, int D, const void* q, const void* k, const void* v,
                            const int32_t* cu, const int32_t* items, int32_t B, int32_t N, int32_t H,
                            int32_t max_seq_len, int32_t win, int64_t ld, float scale, void* out, float* lse,
                            hipStream_t stream) {
-  if (bf16 && attn_fwd_bf16_supported(D, max_seq_len)) {
+  const bool f16 = dt == kDtF16;
+  if (dt != kDtF32 && attn_fwd_bf16_supported(D, max_seq_len)) {
     if (attn_fwd_bf16_w64_supported(D))
-      return launch_attn_fwd_bf16_w64(D, q, k, v, cu, items, B, N, H, win, ld, scale, out, lse, stream);
-    return launch_attn_fwd_bf16(D, q, k, v, cu, items, B, N, H, win, ld, scale, out, lse, stream);
+      return launch_attn_fwd_bf16_w64(f16, D, q, k, v, cu, items, B, N, H, win, ld, scale, out, lse, stream);
+    return launch_attn_fwd_bf16(f16, D, q, k, v, cu, items, B, N, H, win, ld, scale, out, lse, stream);
   }
-#define PE_FWD_CASE(DD)                                                                      \
-  case DD:                                                                                  \
-    return bf16 ? fwd_dispatch<true, DD>(q, k, v, cu, items, B, N, H, win, ld, scale, out, lse, stream) \
-                : fwd_dispatch<false, DD>(q, k, v, cu, items, B, N, H, win, ld, scale, out, lse, stream);
+#define PE_FWD_CASE(DD)                                                                                      \
+  case DD:                                                                                                  \
+    return dt == kDtF32 ? fwd_dispatch<float, DD>(q, k, v, cu, items, B, N, H, win, ld, scale, out, lse, stream) \
+           : f16        ? fwd_dispatch<_Float16, DD>(q, k, v, cu, items, B, N, H, win, ld, scale, out, lse, stream) \
+                        : fwd_dispatch<__bf16, DD>(q, k, v, cu, items, B, N, H, win, ld, scale, out, lse, stream);
   switch (D) {
     PE_FWD_CASE(8)
     PE_FWD_CASE(16)
@@ -332,15 +334,17 @@ hipError_t launch_attn_fwd(bool bf16, int D, const void* q, const void* k, const
 #undef PE_FWD_CASE
 }
 
-hipError_t launch_attn_fwd_first(bool bf16, int D, const void* q_first, const void* k, const void* v,
+hipError_t launch_attn_fwd_first(int dt, int D, const void* q_first, const void* k, const void* v,
                                  const int32_t* cu, int32_t B, int32_t N, int32_t H, int32_t gather, int64_t ld,
                                  float scale, void* out_first, float* lse_first, hipStream_t stream) {
-#define PE_FIRST_CASE(DD)                                                                          \
-  case DD:                                                                                        \
-    return bf16 ? first_dispatch<true, DD>(q_first, k, v, cu, B, N, H, gather, ld, scale, out_first, lse_first, \
-                                           stream)                                                              \
-                : first_dispatch<false, DD>(q_first, k, v, cu, B, N, H, gather, ld, scale, out_first, lse_first, \
-                                            stream);
+#define PE_FIRST_CASE(DD)                                                                                     \
+  case DD:                                                                                                   \
+    return dt == kDtF32  ? first_dispatch<float, DD>(q_first, k, v, cu, B, N, H, gather, ld, scale, out_first,    \
+                                                    lse_first, stream)                                           \
+           : dt == kDtF16 ? first_dispatch<_Float16, DD>(q_first, k, v, cu, B, N, H, gather, ld, scale, out_first, \
+                                                       lse_first, stream)                                        \
+                         : first_dispatch<__bf16, DD>(q_first, k, v, cu, B, N, H, gather, ld, scale, out_first,    \
+                                                     lse_first, stream);
   switch (D) {
     PE_FIRST_CASE(8)
     PE_FIRST_CASE(16)

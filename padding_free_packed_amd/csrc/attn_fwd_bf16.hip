@@ -28,7 +28,7 @@ struct StageTag {
   static constexpr int value = ST;
 };
 
-template <int D>
+template <typename Et, int D>
 __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
     const void* __restrict__ qp, const void* __restrict__ kp, const void* __restrict__ vp,
     const int32_t* __restrict__ cu, const int32_t* __restrict__ items, int32_t B, int32_t N, int32_t H,
@@ -62,8 +62,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
   const int klo = __builtin_amdgcn_readfirstlane(win >= 0 ? max(sp.lo, sp.r0 - win) : sp.lo);
   const int khi = __builtin_amdgcn_readfirstlane(win >= 0 ? min(sp.hi, sp.rend + win) : sp.hi);
 
-  bf16x8 qr[QS];
-  load_row_regs<true, D>(qp, static_cast<int64_t>(qrow) * ld + h * D + g * (D / 2), qvalid, qr);
+  vec8<Et> qr[QS];
+  load_row_regs<Et, D>(qp, static_cast<int64_t>(qrow) * ld + h * D + g * (D / 2), qvalid, qr);
   // Retire the Q loads with a wait the compiler sees: otherwise it places a
   // vmcnt wait for them inside the loop, which would also drain the DMA ring.
   vmem_fence_for_compiler();
@@ -122,19 +122,19 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
         }
 
   auto qk = [&](const char* ktile, floatx16 (&s)[2]) __attribute__((always_inline)) {
-    bf16x8 ka[2][QS];
+    vec8<Et> ka[2][QS];
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
       for (int st = 0; st < QS; ++st)
-        ka[kk][st] = as_bf16x8(*reinterpret_cast<const u16x8*>(ktile + koff[kk][st]));
+        ka[kk][st] = as_vec8<Et>(*reinterpret_cast<const u16x8*>(ktile + koff[kk][st]));
     s[0] = floatx16{};
     s[1] = floatx16{};
 #pragma unroll
     for (int st = 0; st < QS; ++st)
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk)
-        s[kk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[kk][st], qr[st], s[kk], 0, 0, 0);
+        s[kk] = mfma16<Et>(ka[kk][st], qr[st], s[kk]);
   };
 
   floatx16 o[DB];
@@ -166,12 +166,12 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
         for (int i2 = 0; i2 < 16; ++i2) o[db][i2] *= alpha;
       m = mnew;
     }
-    bf16x8 pb[2][2];
+    vec8<Et> pb[2][2];
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
 #pragma unroll
       for (int i2 = 0; i2 < 16; ++i2) s[kk][i2] = __builtin_amdgcn_exp2f(fmaf(s[kk][i2], c, -m));
-      probs_to_bf16(s[kk], pb[kk], l);
+      probs_to_h16<Et>(s[kk], pb[kk], l);
     }
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk)
@@ -182,7 +182,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
           const u16x4 lo4 = ds_read_tr16(reinterpret_cast<const uint16_t*>(vtile + voff[kk][s2][0][db]));
           const u16x4 hi4 = ds_read_tr16(reinterpret_cast<const uint16_t*>(vtile + voff[kk][s2][1][db]));
           const u16x8 a = {lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
-          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), pb[kk][s2], o[db], 0, 0, 0);
+          o[db] = mfma16<Et>(as_vec8<Et>(a), pb[kk][s2], o[db]);
         }
   };
 
@@ -227,12 +227,12 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
   const float lt = xhalf_sum(l);
   const float inv = lt > 0.f ? 1.f / lt : 0.f;
   if (qvalid) {
-    store_acc_row<true, D>(op, (static_cast<int64_t>(qrow) * H + h) * D, o, inv, g);
+    store_acc_row<Et, D>(op, (static_cast<int64_t>(qrow) * H + h) * D, o, inv, g);
     if (lse != nullptr && g == 0) lse[static_cast<int64_t>(h) * N + qrow] = (m + log2f(lt)) * kLn2;
   }
 }
 
-template <int D>
+template <typename Et, int D>
 hipError_t dispatch(const void* q, const void* k, const void* v, const int32_t* cu, const int32_t* items,
                     int32_t B, int32_t N, int32_t H, int32_t win, int64_t ld, float scale, void* out, float* lse,
                     hipStream_t stream) {
@@ -241,7 +241,7 @@ hipError_t dispatch(const void* q, const void* k, const void* v, const int32_t* 
   if (blocks == 0) return hipSuccess;
   const float c = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
   hipEvent_t ev = timing_start(stream);
-  hipLaunchKernelGGL((attn_fwd_bf16_kernel<D>), dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0, stream, q,
+  hipLaunchKernelGGL((attn_fwd_bf16_kernel<Et, D>), dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0, stream, q,
                      k, v, cu, items, B, N, H, T, win, ld, c, out, lse);
   timing_stop("attn_fwd", ev, stream);
   return hipGetLastError();
@@ -256,15 +256,23 @@ bool attn_fwd_bf16_supported(int D, int max_seq_len) {
   return (D == 32 || D == 64 || D == 128) && max_seq_len > 2 * kBlk;
 }
 
-hipError_t launch_attn_fwd_bf16(int D, const void* q, const void* k, const void* v, const int32_t* cu,
-                                const int32_t* items, int32_t B, int32_t N, int32_t H, int32_t win, int64_t ld,
-                                float scale, void* out, float* lse, hipStream_t stream) {
+template <typename Et>
+hipError_t launch_typed(int D, const void* q, const void* k, const void* v, const int32_t* cu, const int32_t* items,
+                        int32_t B, int32_t N, int32_t H, int32_t win, int64_t ld, float scale, void* out, float* lse,
+                        hipStream_t stream) {
   switch (D) {
-    case 32: return dispatch<32>(q, k, v, cu, items, B, N, H, win, ld, scale, out, lse, stream);
-    case 64: return dispatch<64>(q, k, v, cu, items, B, N, H, win, ld, scale, out, lse, stream);
-    case 128: return dispatch<128>(q, k, v, cu, items, B, N, H, win, ld, scale, out, lse, stream);
+    case 32: return dispatch<Et, 32>(q, k, v, cu, items, B, N, H, win, ld, scale, out, lse, stream);
+    case 64: return dispatch<Et, 64>(q, k, v, cu, items, B, N, H, win, ld, scale, out, lse, stream);
+    case 128: return dispatch<Et, 128>(q, k, v, cu, items, B, N, H, win, ld, scale, out, lse, stream);
     default: return hipErrorInvalidValue;
   }
+}
+
+hipError_t launch_attn_fwd_bf16(bool f16, int D, const void* q, const void* k, const void* v, const int32_t* cu,
+                                const int32_t* items, int32_t B, int32_t N, int32_t H, int32_t win, int64_t ld,
+                                float scale, void* out, float* lse, hipStream_t stream) {
+  return f16 ? launch_typed<_Float16>(D, q, k, v, cu, items, B, N, H, win, ld, scale, out, lse, stream)
+             : launch_typed<__bf16>(D, q, k, v, cu, items, B, N, H, win, ld, scale, out, lse, stream);
 }
 
 }  // namespace pe

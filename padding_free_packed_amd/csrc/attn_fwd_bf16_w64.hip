@@ -39,7 +39,7 @@ struct W64Stage {
   static constexpr int value = ST;
 };
 
-template <int D>
+template <typename Et, int D>
 __global__ __launch_bounds__(kW64Threads) __attribute__((amdgpu_waves_per_eu(2))) void attn_fwd_bf16_w64_kernel(
     const void* __restrict__ qp, const void* __restrict__ kp, const void* __restrict__ vp,
     const int32_t* __restrict__ cu, const int32_t* __restrict__ items, int32_t B, int32_t N, int32_t H,
@@ -80,10 +80,10 @@ __global__ __launch_bounds__(kW64Threads) __attribute__((amdgpu_waves_per_eu(2))
   const int klo = __builtin_amdgcn_readfirstlane(win >= 0 ? max(sp.lo, sp.r0 - win) : sp.lo);
   const int khi = __builtin_amdgcn_readfirstlane(win >= 0 ? min(sp.hi, sp.rend + win) : sp.hi);
 
-  bf16x8 qr[2][QS];
+  vec8<Et> qr[2][QS];
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb)
-    load_row_regs<true, D>(qp, static_cast<int64_t>(qrow[qb]) * ld + h * D + g * (D / 2), qvalid[qb], qr[qb]);
+    load_row_regs<Et, D>(qp, static_cast<int64_t>(qrow[qb]) * ld + h * D + g * (D / 2), qvalid[qb], qr[qb]);
   // retire the Q loads with a wait the compiler sees, so none lands inside the DMA loop
   vmem_fence_for_compiler();
 
@@ -146,25 +146,25 @@ __global__ __launch_bounds__(kW64Threads) __attribute__((amdgpu_waves_per_eu(2))
   // ---- the pieces of one step
   // S^T of both query blocks for the key block in `ktile`
   auto qk_both = [&](const char* ktile, floatx16 (&s)[2]) __attribute__((always_inline)) {
-    bf16x8 ka[QS];
+    vec8<Et> ka[QS];
 #pragma unroll
-    for (int st = 0; st < QS; ++st) ka[st] = as_bf16x8(*reinterpret_cast<const u16x8*>(ktile + koff[st]));
-    s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[0], qr[0][0], floatx16{}, 0, 0, 0);
-    s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[0], qr[1][0], floatx16{}, 0, 0, 0);
+    for (int st = 0; st < QS; ++st) ka[st] = as_vec8<Et>(*reinterpret_cast<const u16x8*>(ktile + koff[st]));
+    s[0] = mfma16<Et>(ka[0], qr[0][0], floatx16{});
+    s[1] = mfma16<Et>(ka[0], qr[1][0], floatx16{});
 #pragma unroll
     for (int st = 1; st < QS; ++st) {
-      s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[st], qr[0][st], s[0], 0, 0, 0);
-      s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[st], qr[1][st], s[1], 0, 0, 0);
+      s[0] = mfma16<Et>(ka[st], qr[0][st], s[0]);
+      s[1] = mfma16<Et>(ka[st], qr[1][st], s[1]);
     }
   };
-  auto read_vt = [&](const char* vtile, bf16x8 (&vt)[2][DB]) __attribute__((always_inline)) {
+  auto read_vt = [&](const char* vtile, vec8<Et> (&vt)[2][DB]) __attribute__((always_inline)) {
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
         const u16x4 lo4 = ds_read_tr16(reinterpret_cast<const uint16_t*>(vtile + voff[s2][0][db]));
         const u16x4 hi4 = ds_read_tr16(reinterpret_cast<const uint16_t*>(vtile + voff[s2][1][db]));
-        vt[s2][db] = as_bf16x8(u16x8{lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]});
+        vt[s2][db] = as_vec8<Et>(u16x8{lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]});
       }
   };
   // mask, block max and (rarely) the move of the running max with the O rescale
@@ -188,17 +188,17 @@ __global__ __launch_bounds__(kW64Threads) __attribute__((amdgpu_waves_per_eu(2))
       m[qb] = mnew;
     }
   };
-  auto probs = [&](int qb, floatx16& s, bf16x8 (&pb)[2]) __attribute__((always_inline)) {
+  auto probs = [&](int qb, floatx16& s, vec8<Et> (&pb)[2]) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) s[i] = __builtin_amdgcn_exp2f(fmaf(s[i], c, -m[qb]));
-    probs_to_bf16(s, pb, l[qb]);
+    probs_to_h16<Et>(s, pb, l[qb]);
   };
-  auto pv = [&](int qb, const bf16x8 (&pb)[2], const bf16x8 (&vt)[2][DB]) __attribute__((always_inline)) {
+  auto pv = [&](int qb, const vec8<Et> (&pb)[2], const vec8<Et> (&vt)[2][DB]) __attribute__((always_inline)) {
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
       for (int db = 0; db < DB; ++db)
-        o[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vt[s2][db], pb[s2], o[qb][db], 0, 0, 0);
+        o[qb][db] = mfma16<Et>(vt[s2][db], pb[s2], o[qb][db]);
   };
 
   // Step j: S of both query blocks for key block j, then softmax and PV per query
@@ -218,7 +218,7 @@ __global__ __launch_bounds__(kW64Threads) __attribute__((amdgpu_waves_per_eu(2))
     if (!(need0 || need1)) return;
     floatx16 s[2];
     qk_both(ring[ST][0], s);
-    bf16x8 vt[2][DB], pb0[2], pb1[2];
+    vec8<Et> vt[2][DB], pb0[2], pb1[2];
     read_vt(ring[ST][1], vt);
     row_max(0, s[0], kb);
     probs(0, s[0], pb0);
@@ -243,13 +243,13 @@ __global__ __launch_bounds__(kW64Threads) __attribute__((amdgpu_waves_per_eu(2))
     const float lt = xhalf_sum(l[qb]);
     const float inv = lt > 0.f ? 1.f / lt : 0.f;
     if (qvalid[qb]) {
-      store_acc_row<true, D>(op, (static_cast<int64_t>(qrow[qb]) * H + h) * D, o[qb], inv, g);
+      store_acc_row<Et, D>(op, (static_cast<int64_t>(qrow[qb]) * H + h) * D, o[qb], inv, g);
       if (lse != nullptr && g == 0) lse[static_cast<int64_t>(h) * N + qrow[qb]] = (m[qb] + log2f(lt)) * kLn2;
     }
   }
 }
 
-template <int D>
+template <typename Et, int D>
 hipError_t dispatch_w64(const void* q, const void* k, const void* v, const int32_t* cu, const int32_t* items,
                         int32_t B, int32_t N, int32_t H, int32_t win, int64_t ld, float scale, void* out,
                         float* lse, hipStream_t stream) {
@@ -258,7 +258,7 @@ hipError_t dispatch_w64(const void* q, const void* k, const void* v, const int32
   if (blocks == 0) return hipSuccess;
   const float c = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
   hipEvent_t ev = timing_start(stream);
-  hipLaunchKernelGGL((attn_fwd_bf16_w64_kernel<D>), dim3(static_cast<unsigned>(blocks)), dim3(kW64Threads), 0,
+  hipLaunchKernelGGL((attn_fwd_bf16_w64_kernel<Et, D>), dim3(static_cast<unsigned>(blocks)), dim3(kW64Threads), 0,
                      stream, q, k, v, cu, items, B, N, H, T, win, ld, c, out, lse);
   timing_stop("attn_fwd", ev, stream);
   return hipGetLastError();
@@ -268,14 +268,19 @@ hipError_t dispatch_w64(const void* q, const void* k, const void* v, const int32
 
 bool attn_fwd_bf16_w64_supported(int D) { return D == 32 || D == 64; }
 
-hipError_t launch_attn_fwd_bf16_w64(int D, const void* q, const void* k, const void* v, const int32_t* cu,
+hipError_t launch_attn_fwd_bf16_w64(bool f16, int D, const void* q, const void* k, const void* v, const int32_t* cu,
                                     const int32_t* items, int32_t B, int32_t N, int32_t H, int32_t win, int64_t ld,
                                     float scale, void* out, float* lse, hipStream_t stream) {
+#define PE_W64_CASE(DD)                                                                                       \
+  case DD:                                                                                                    \
+    return f16 ? dispatch_w64<_Float16, DD>(q, k, v, cu, items, B, N, H, win, ld, scale, out, lse, stream) \
+               : dispatch_w64<__bf16, DD>(q, k, v, cu, items, B, N, H, win, ld, scale, out, lse, stream);
   switch (D) {
-    case 32: return dispatch_w64<32>(q, k, v, cu, items, B, N, H, win, ld, scale, out, lse, stream);
-    case 64: return dispatch_w64<64>(q, k, v, cu, items, B, N, H, win, ld, scale, out, lse, stream);
+    PE_W64_CASE(32)
+    PE_W64_CASE(64)
     default: return hipErrorInvalidValue;
   }
+#undef PE_W64_CASE
 }
 
 }  // namespace pe

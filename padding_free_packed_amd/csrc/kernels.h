@@ -9,6 +9,11 @@ namespace pe {
 hipEvent_t timing_start(hipStream_t stream);
 void timing_stop(const char* name, hipEvent_t start, hipStream_t stream);
 
+// element type codes of the attention launchers (the pe_dtype values)
+constexpr int kDtF32 = 0;
+constexpr int kDtBF16 = 1;
+constexpr int kDtF16 = 2;
+
 // packed query (or key) rows per attention work item
 constexpr int kAttnTileRows = 128;
 // packed rows per work item of the one-wave fp32 kernels
@@ -29,19 +34,20 @@ hipError_t launch_unpack_rows(const void* packed, void* grid, const int32_t* cu,
                               int64_t rowbytes, hipStream_t stream);
 
 // Forward over tiles of kAttnTileRows packed query rows; items from launch_worklist.
-hipError_t launch_attn_fwd(bool bf16, int D, const void* q, const void* k, const void* v,
+// dt: kDtF32, kDtBF16 or kDtF16 (every attention launcher takes it).
+hipError_t launch_attn_fwd(int dt, int D, const void* q, const void* k, const void* v,
                            const int32_t* cu, const int32_t* items, int32_t B, int32_t N, int32_t H,
                            int32_t max_seq_len, int32_t win, int64_t ld, float scale, void* out, float* lse,
                            hipStream_t stream);
 
-// bf16 forward with LDS-DMA staging (head dims 32, 64, 128).
+// 16-bit forward with LDS-DMA staging (head dims 32, 64, 128); f16 selects fp16 over bf16.
 bool attn_fwd_bf16_supported(int D, int max_seq_len);
 // the same items with two 64-row waves per block (head dims 32, 64)
 bool attn_fwd_bf16_w64_supported(int D);
-hipError_t launch_attn_fwd_bf16_w64(int D, const void* q, const void* k, const void* v, const int32_t* cu,
+hipError_t launch_attn_fwd_bf16_w64(bool f16, int D, const void* q, const void* k, const void* v, const int32_t* cu,
                                     const int32_t* items, int32_t B, int32_t N, int32_t H, int32_t win, int64_t ld,
                                     float scale, void* out, float* lse, hipStream_t stream);
-hipError_t launch_attn_fwd_bf16(int D, const void* q, const void* k, const void* v, const int32_t* cu,
+hipError_t launch_attn_fwd_bf16(bool f16, int D, const void* q, const void* k, const void* v, const int32_t* cu,
                                 const int32_t* items, int32_t B, int32_t N, int32_t H, int32_t win, int64_t ld,
                                 float scale, void* out, float* lse, hipStream_t stream);
 
@@ -63,11 +69,11 @@ hipError_t launch_bwd_dq_f32_wave(int D, const void* dout, const void* q, const 
                                   hipStream_t stream);
 
 // gather = 0: q_first is [B, H, D]; gather = 1: the query of sequence b is row cu[b] of a packed [N, H, D]
-hipError_t launch_attn_fwd_first(bool bf16, int D, const void* q_first, const void* k, const void* v,
+hipError_t launch_attn_fwd_first(int dt, int D, const void* q_first, const void* k, const void* v,
                                  const int32_t* cu, int32_t B, int32_t N, int32_t H, int32_t gather, int64_t ld,
                                  float scale, void* out_first, float* lse_first, hipStream_t stream);
 // backward of the first-token readout: dq_first [B, H, D], dk and dv [N, H, D] (every row written)
-hipError_t launch_attn_bwd_first(bool bf16, int D, const void* dout_first, const void* q_first, const void* k,
+hipError_t launch_attn_bwd_first(int dt, int D, const void* dout_first, const void* q_first, const void* k,
                                  const void* v, const void* out_first, const float* lse_first, const int32_t* cu,
                                  int32_t B, int32_t N, int32_t H, int64_t ld, float scale, void* dq_first, void* dk,
                                  void* dv, hipStream_t stream);
@@ -78,7 +84,7 @@ hipError_t launch_attn_bwd_first(bool bf16, int D, const void* dout_first, const
 // ld: elements between consecutive rows of Q, K, V (and of dQ, dK, dV): num_heads * D for
 // separate [N, H, D] tensors, 3 * num_heads * D for a fused [N, 3, H, D] buffer. O, dO,
 // LSE and D keep their own dense layouts. Every attention launcher takes both.
-hipError_t launch_attn_bwd(bool bf16, int D, const void* dout, const void* q, const void* k,
+hipError_t launch_attn_bwd(int dt, int D, const void* dout, const void* q, const void* k,
                            const void* v, const void* out, const float* lse, const int32_t* cu,
                            const int32_t* items, const int32_t* items32, int32_t B, int32_t N, int32_t H,
                            int32_t win, int64_t ld, float scale, void* dq, void* dk, void* dv, float* delta,

@@ -41,7 +41,7 @@ class ForwardBucket:
         self.lse = torch.empty(num_heads, cap, dtype=torch.float32, device=device) if with_lse else None
         self.out_grid = torch.empty(slots, max_seq_len, num_heads, head_dim, dtype=dtype, device=device)
         self.status = torch.zeros(2, dtype=torch.int64, device=device)
-        code = pe.PE_BF16 if dtype == torch.bfloat16 else pe.PE_FP32
+        code = {torch.bfloat16: pe.PE_BF16, torch.float16: pe.PE_FP16}.get(dtype, pe.PE_FP32)
         self.workspace = pe.workspace(
             pe.pe_forward_graph_workspace_size(slots, max_seq_len, num_heads, head_dim, code), device)
         torch.cuda.synchronize(device)  # the buffers exist before the capture records their addresses

@@ -20,7 +20,7 @@ LIB_PATH = os.path.join(_HERE, "libpe.so")
 
 PE_OK, PE_ERR_NULL, PE_ERR_ARG, PE_ERR_UNSUPPORTED, PE_ERR_LENGTHS, PE_ERR_CAPACITY, \
     PE_ERR_WORKSPACE, PE_ERR_HIP, PE_ERR_METADATA = range(9)
-PE_FP32, PE_BF16 = 0, 1
+PE_FP32, PE_BF16, PE_FP16 = 0, 1, 2
 
 EXPORTS = (
     "pe_status_string", "pe_attn_tile_rows", "pe_pack_workspace_size", "pe_pack", "pe_unpack",
@@ -117,6 +117,8 @@ def _dtype_code(t: torch.Tensor) -> int:
         return PE_FP32
     if t.dtype == torch.bfloat16:
         return PE_BF16
+    if t.dtype == torch.float16:
+        return PE_FP16
     raise TypeError(f"unsupported dtype {t.dtype}")
 
 

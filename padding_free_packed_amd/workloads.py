@@ -12,8 +12,9 @@ Every workload follows one recipe:
   dtype=float32)`` with shape ``[N, H, d]``;
 * "uniform int in [a, b]" is ``rng.integers(a, b + 1)``; "round" is
   ``numpy.rint`` (half to even), clipped after rounding;
-* bf16 values are the round-to-nearest-even images of those fp32 draws,
-  produced on the bit patterns below; arrays of bf16 are ``uint16`` bit arrays;
+* bf16 and fp16 values are the round-to-nearest-even images of those fp32
+  draws (bf16 produced on the bit patterns below, fp16 by numpy's IEEE
+  conversion); arrays of either are ``uint16`` bit arrays;
 * padding cells of a grid hold NaN, so a pack that reads padding is caught.
 
 The length distributions and shapes are those of the workloads described on the
@@ -30,8 +31,10 @@ import numpy as np
 
 FP32 = "fp32"
 BF16 = "bf16"
+FP16 = "fp16"
 
 BF16_NAN = np.uint16(0x7FC0)
+FP16_NAN = np.uint16(0x7E00)
 
 
 def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
@@ -49,10 +52,35 @@ def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
     return (np.ascontiguousarray(b, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
 
 
+def f32_to_f16_bits(x: np.ndarray) -> np.ndarray:
+    """Round fp32 values to IEEE fp16 (nearest, ties to even) and return the uint16 bits."""
+    return np.ascontiguousarray(x, dtype=np.float32).astype(np.float16).view(np.uint16)
+
+
+def f16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    """Exact widening of fp16 bit patterns to fp32."""
+    return np.ascontiguousarray(b, dtype=np.uint16).view(np.float16).astype(np.float32)
+
+
+def is16(dtype: str) -> bool:
+    return dtype in (BF16, FP16)
+
+
+def to_bits(x: np.ndarray, dtype: str) -> np.ndarray:
+    """fp32 values -> the workload encoding of dtype (fp32 values, or 16-bit bits)."""
+    if dtype == BF16:
+        return f32_to_bf16_bits(x)
+    if dtype == FP16:
+        return f32_to_f16_bits(x)
+    return np.ascontiguousarray(x, dtype=np.float32)
+
+
 def to_f64(x: np.ndarray, dtype: str) -> np.ndarray:
-    """Exact widening of a workload array (fp32 values or bf16 bits) to float64."""
+    """Exact widening of a workload array (fp32 values or 16-bit bits) to float64."""
     if dtype == BF16:
         return bf16_bits_to_f32(x).astype(np.float64)
+    if dtype == FP16:
+        return f16_bits_to_f32(x).astype(np.float64)
     return np.asarray(x, dtype=np.float32).astype(np.float64)
 
 
@@ -86,14 +114,14 @@ class Workload:
 
 
 def _cast(x: np.ndarray, dtype: str) -> np.ndarray:
-    return f32_to_bf16_bits(x) if dtype == BF16 else x
+    return to_bits(x, dtype) if is16(dtype) else x
 
 
 def _draw_grid(rng, lengths, S, D, dtype):
     g = rng.standard_normal((lengths.shape[0], S, D), dtype=np.float32)
     g = _cast(g, dtype)
     pad = np.arange(S)[None, :] >= lengths[:, None]
-    g[pad] = BF16_NAN if dtype == BF16 else np.float32("nan")
+    g[pad] = {BF16: BF16_NAN, FP16: FP16_NAN}.get(dtype, np.float32("nan"))
     return g
 
 
@@ -155,6 +183,14 @@ def mixed_training() -> Workload:
     docs = np.clip(np.rint(rng.lognormal(np.log(1024.0), 0.7, size=256)), 128, 8192).astype(np.int64)
     lengths = rng.permutation(np.concatenate([queries, docs]))
     return _finish("mixed_training", BF16, rng, lengths, 8192, 16, 64, False, ("q", "k", "v", "dout"))
+
+
+def short_batch(num_seqs: int = 64) -> Workload:
+    """The short-query recipe at a serving batch: num_seqs sequences, lengths uniform in
+    [8, 48], S = 48, 12 x 64, bf16 (the launch-bound case of a captured bucket forward)."""
+    rng = np.random.default_rng(5)
+    lengths = rng.integers(8, 49, size=num_seqs)
+    return _finish("short_batch", BF16, rng, lengths, 48, 12, 64, False, ("q", "k", "v"))
 
 
 def nemo_rows(base: Workload, width: int):

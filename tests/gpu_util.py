@@ -4,13 +4,15 @@ back, and the tolerance checks against the fp64 oracle.
 Tolerances (written here once, used by every parity test):
 * fp32: max |gpu - ref| <= 1e-5, and |gpu - ref| / |ref| <= 1e-4 wherever
   |ref| >= 0.1 (below that the absolute bound governs);
-* bf16 in / fp32 accumulate: max |gpu - ref| <= 2e-2, and the cosine between
+* bf16 or fp16 in / fp32 accumulate: max |gpu - ref| <= 2e-2, and the cosine between
   the GPU and oracle vectors of every token row (all heads and head dims of
   that row) >= 0.999 for rows whose oracle norm exceeds 2e-2 (a row below the
   per-element bound is rounding noise around zero, e.g. the exactly-zero dQ and
   dK of a length-1 sequence, and is held by the element-wise bound alone);
 * log-sum-exp (always fp32): |delta| <= 1e-5 * max(1, |lse|) for fp32 inputs,
-  |delta| <= 1e-3 for bf16 inputs;
+  |delta| <= 1e-3 for bf16 or fp16 inputs;
+  (fp16 is held to the bf16 bar: the same 16-bit storage with fp32
+  accumulation, and 8 times finer rounding;)
 * integer and byte outputs: bit-exact.
 """
 import sys
@@ -27,21 +29,31 @@ def say(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+TORCH_DTYPE = {W.FP32: torch.float32, W.BF16: torch.bfloat16, W.FP16: torch.float16}
+
+
+def pe_code(dtype: str) -> int:
+    from padding_free_packed_amd import pe
+    return {W.FP32: pe.PE_FP32, W.BF16: pe.PE_BF16, W.FP16: pe.PE_FP16}[dtype]
+
+
 def to_dev(x: np.ndarray, dtype: str) -> torch.Tensor:
-    if dtype == W.BF16:
-        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).to(DEV)
+    if W.is16(dtype):
+        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(TORCH_DTYPE[dtype]).to(DEV)
     return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(DEV)
 
 
 def from_dev(t: torch.Tensor) -> np.ndarray:
     t = t.detach().cpu()
-    if t.dtype == torch.bfloat16:
+    if t.dtype in (torch.bfloat16, torch.float16):
         return t.view(torch.int16).numpy().view(np.uint16)
     return t.numpy()
 
 
 def to_f64(t: torch.Tensor) -> np.ndarray:
     a = from_dev(t)
+    if t.dtype == torch.float16:
+        return W.f16_bits_to_f32(a).astype(np.float64)
     return W.bf16_bits_to_f32(a).astype(np.float64) if a.dtype == np.uint16 else a.astype(np.float64)
 
 
