@@ -114,7 +114,110 @@ def load_traffic(kernel, workload):
     return t.get("bytes_per_launch")
 
 
-def cpu_baseline(w, budget_s, window=None, nemo_mask=None):
+def graph_bench(args):
+    """The short_batch workload: one step is one replay of the captured bucket forward
+    (pe_pack_async of the fused Q/K/V grid, pe_varlen_attn_fwd_qkv over the bucket's
+    capacity, pe_unpack) for a batch of 64 short sequences in a (64, 48) bucket. The same
+    forward by the eager calls (pe_pack with its host read, then the same two calls) is
+    timed beside it; per-kernel times come from the eager pass (launches inside a graph
+    carry no events), and the graph replays the same kernels."""
+    import numpy as np
+    import torch
+
+    from padding_free_packed_amd import graphs, pe
+    from padding_free_packed_amd import workloads as W
+
+    w = W.short_batch(args.num_seqs)
+    dev = "cuda:0"
+    B, S, H, d = w.num_seqs, w.max_seq_len, w.num_heads, w.head_dim
+    D, N, e = H * d, w.total_tokens, 2
+    cu_h = np.concatenate([[0], np.cumsum(w.lengths.astype(np.int64))])
+    # the fused grid [B, S, 3, H, d] holding each sequence's q, k, v rows; padding NaN
+    fused = np.full((B, S, 3, H, d), W.f32_to_bf16_bits(np.array([np.nan], np.float32))[0], dtype=np.uint16)
+    for b in range(B):
+        for j, x in enumerate((w.q, w.k, w.v)):
+            fused[b, :w.lengths[b], j] = x[cu_h[b]:cu_h[b + 1]]
+    w.grid = fused.reshape(B, S, 3 * D)
+    bucket = graphs.ForwardBucket(B, S, H, d, torch.bfloat16, w.scale, -1, with_lse=False, device=dev)
+    bucket.lengths.copy_(torch.from_numpy(w.lengths.astype(np.int32)))
+    bucket.qkv_grid.copy_(torch.from_numpy(fused.view(np.int16)).view(torch.bfloat16))
+    cu = torch.empty(B + 1, dtype=torch.int32, device=dev)
+    packed = torch.empty(N, 3, H, d, dtype=torch.bfloat16, device=dev)
+    out = torch.empty(N, H, d, dtype=torch.bfloat16, device=dev)
+    grid_out = torch.empty_like(bucket.out_grid)
+    ws_pack = pe.workspace(pe.pe_pack_workspace_size(B, S, 3 * D, pe.PE_BF16), dev)
+    ws = pe.workspace(pe.pe_attn_workspace_size(B, N, H, d, pe.PE_BF16, False), dev)
+    grid_in = bucket.qkv_grid.view(B, S, 3 * D)
+
+    def eager():
+        n = pe.pe_pack(bucket.lengths, S, grid_in, cu, None, packed.view(N, 3 * D), N, ws_pack, pe.PE_BF16)
+        pe.pe_varlen_attn_fwd_qkv(packed, cu, B, n, S, w.scale, -1, out, None, ws)
+        pe.pe_unpack(out, cu, B, S, n, grid_out)
+
+    def timed(fn, steps):
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        wall0 = time.perf_counter()
+        t0.record()
+        for _ in range(steps):
+            fn()
+        t1.record()
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1) / steps, time.perf_counter() - wall0
+
+    for _ in range(args.warmup):
+        bucket.replay()
+        eager()
+    torch.cuda.synchronize()
+    assert bucket.status.tolist() == [N, pe.PACK_OK]
+    assert torch.equal(bucket.out_grid.view(torch.int16), grid_out.view(torch.int16))
+    ms_step, wall = timed(bucket.replay, args.steps)
+    ms_eager, _ = timed(eager, args.steps)
+    pe.pe_timing_enable(True)
+    pe.pe_timing_read()
+    eager()
+    torch.cuda.synchronize()
+    recs = pe.pe_timing_read()
+    pe.pe_timing_enable(False)
+    breakdown = {}
+    L2 = band_pairs(w.lengths, None)
+    for name, ms in recs:
+        ent = breakdown.setdefault(name, {"avg_ms": 0.0, "launches_per_step": 0})
+        ent["avg_ms"] += ms
+        ent["launches_per_step"] += 1
+    for name, ent in breakdown.items():
+        ent["avg_ms"] /= ent["launches_per_step"]
+        ent["ms_per_step"] = ent["avg_ms"] * ent["launches_per_step"]
+        aw = algo_work(name, w, N, L2, e, False, True)
+        if name == "pack_rows":
+            aw = {"byte": 2.0 * N * 3 * D * e}          # rows of the fused grid; no flat_index written
+        if aw is not None and ent["avg_ms"] > 0:
+            ent.update(rate(aw, ent["avg_ms"], "bf16"))
+    dom = max(breakdown, key=lambda k_: breakdown[k_]["ms_per_step"])
+    work = algo_work(dom, w, N, L2, e, False, True)
+    if dom == "pack_rows":
+        work = {"byte": 2.0 * N * 3 * D * e}
+    roof = rate(work, breakdown[dom]["avg_ms"], "bf16")
+    roof.update({"traffic": None, "kernel": dom,
+                 "algorithmic_per_launch": work["flop"] if roof["bound"] == "mfma" else work["byte"]})
+    result = {
+        "metric": METRIC, "value": N / (ms_step * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "short_batch", "num_seqs": B, "max_seq_len": S, "total_tokens": N, "num_heads": H,
+                   "head_dim": d, "grid": [B, S, 3, H, d], "window": None,
+                   "step": "graph replay: pack_async(fused qkv grid)+fwd_qkv(capacity rows)+unpack"},
+        "eager_ms_per_step": ms_eager,
+        "kernel_ms_sum": sum(v_["ms_per_step"] for v_ in breakdown.values()),
+        "roofline": roof, "breakdown": breakdown, "wall_s_timed_region": wall,
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(w, args.cpu_budget, first_token=False)
+    bucket.close()
+    print(json.dumps(result))
+
+
+def cpu_baseline(w, budget_s, window=None, nemo_mask=None, first_token=True):
     """The fp64 oracle on the first m sequences of the batch (a valid packed batch itself),
     with m sized for about `budget_s` seconds, BLAS limited to one thread."""
     import numpy as np
@@ -142,7 +245,7 @@ def cpu_baseline(w, budget_s, window=None, nemo_mask=None):
         if grid is not None:
             oracle.pack(grid, flat)
         o, _ = oracle.attention(q, k, v, cu, w.scale, window=window)
-        if nemo_mask is None:
+        if nemo_mask is None and first_token:
             oracle.attention_first_token(q[cu[:-1]], k, v, cu, w.scale)
         if do is not None:
             oracle.attention_backward(do, q, k, v, cu, w.scale, window=window)
@@ -159,7 +262,7 @@ def cpu_baseline(w, budget_s, window=None, nemo_mask=None):
     return {"value": n / t, "unit": "tokens/s", "cores": 1, "kind": "oracle",
             "sample": f"first {m} of {w.num_seqs} sequences ({n} tokens): "
                       + ("flatten of their rows, gather, layout, forward," if nemo_mask is not None else
-                         "layout, pack, forward, first-token,")
+                         "layout, pack, forward," + (" first-token," if first_token else ""))
                       + (" backward, first-token backward," if w.dout is not None else "")
                       + (" unpack" if w.grid is not None else "") + f" in float64, {t:.1f} s"}
 
@@ -171,7 +274,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="graph_transformer",
                     choices=["graph_transformer", "short_query", "long_document", "mixed_training", "tiny",
-                             "nemo_packed"])
+                             "nemo_packed", "short_batch"])
+    ap.add_argument("--num-seqs", type=int, default=64,
+                    help="short_batch only: sequences in the batch (and slots of its captured bucket)")
     ap.add_argument("--window", type=int, default=None,
                     help="local attention: each query sees the keys within this distance in its sequence "
                          "(pe_varlen_attn_fwd_local / _bwd_local); default global attention")
@@ -187,6 +292,9 @@ def main():
               "measures the single-GPU path; sharding across GPUs is described in DESIGN.md, not run.",
               file=sys.stderr)
         sys.exit(2)
+
+    if args.workload == "short_batch":
+        return graph_bench(args)
 
     import numpy as np
     import torch

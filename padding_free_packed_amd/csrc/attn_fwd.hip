@@ -1,11 +1,13 @@
 // Flash-style forward of non-causal attention over packed sequences, and the
 // first-token query variant.
 //
-// Work item = one head and one tile of 128 consecutive packed query rows. A
-// tile may span several short sequences or sit inside one long document; its
-// keys are those of every sequence it touches, and each query row masks keys
-// outside its own sequence. Short queries and long documents thus share one
-// launch without padding any sequence to a tile.
+// Work item = one tile of 128 consecutive packed query rows and a group of
+// heads (as many as keep the launch wide). A tile may span several short
+// sequences or sit inside one long document; its keys are those of every
+// sequence it touches, and each query row masks keys outside its own sequence.
+// Short queries and long documents thus share one launch without padding any
+// sequence to a tile. The offsets of the tile's sequences are read once per
+// block, and its K/V loads stream on from one head to the next.
 //
 // Each of the 4 waves owns 32 query rows. Per 64-key block staged in LDS:
 //   S^T (32 keys x 32 queries) = K Q^T     (mma_rows_regs: K from LDS, Q in registers)
@@ -13,6 +15,7 @@
 //   O^T (d x 32 queries) += V^T P^T        (mma_tr_regs: V from LDS, P straight from S^T)
 // Computing S transposed leaves every lane with one query and 16 of its keys,
 // the layout the PV product needs as its B operand, so P never goes through LDS.
+#include <algorithm>
 #include <climits>
 #include <type_traits>
 
@@ -22,30 +25,38 @@ namespace pe {
 
 namespace {
 
+// the generic forward groups heads per block while the launch keeps this many blocks
+constexpr int64_t kFwdMinBlocks = 2048;
+
 template <typename Et, int D>
 __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
     const void* __restrict__ qp, const void* __restrict__ kp, const void* __restrict__ vp,
     const int32_t* __restrict__ cu, const int32_t* __restrict__ items, int32_t B, int32_t N,
-    int32_t H, int32_t T, int32_t win, int64_t ld, float c, void* __restrict__ op, float* __restrict__ lse) {
+    int32_t H, int32_t T, int32_t HG, int32_t win, int64_t ld, float c, void* __restrict__ op,
+    float* __restrict__ lse) {
   using G = Geo<Et, D>;
   using E = typename G::E;
   // bf16 tiles with whole 16-byte chunks per lane half use the XOR-swizzled layout
   // (conflict-free for both the row reads and the transposing reads)
   constexpr bool SWZ = kIs16<Et> && D % 32 == 0;
   constexpr int TS = SWZ ? kBlk * D : G::TSZ;
+  // the next head's Q rows are fetched one step early where the registers allow it
+  constexpr bool PREFQ = D <= 32;
   __shared__ __align__(16) E kt[2][TS];
   __shared__ __align__(16) E vt[2][TS];
   __shared__ int32_t cul[kAttnTileRows + 2];
 
   const int lin = xcd_remap(blockIdx.x, gridDim.x);
-  const int h = lin / T, t = lin - h * T;
+  const int hgi = lin / T, t = lin - hgi * T;
+  const int h0 = hgi * HG, nh = min(HG, H - h0);
+  if (nh <= 0) return;  // block-uniform; the host's even grouping never leaves an empty group
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, ql = lane & 31, g = lane >> 5;
 
   // the sequences this tile touches; their keys are [sp.lo, sp.hi)
   const TileSpan sp = tile_span(cu, items, t, B, N, cul);
   if (sp.rend <= sp.r0) return;  // block-uniform: no rows in this tile
 
-  // this lane's query row and its own key range [qk0, qk1)
+  // this lane's query row and its own key range [qk0, qk1) (the same for every head)
   const int qrow = sp.r0 + wv * 32 + ql;
   const bool qvalid = qrow < sp.rend;
   int qk0 = 0, qk1 = 0;
@@ -57,9 +68,10 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
   const int wk1 = wave_max_i(qvalid ? qk1 : INT_MIN);
   const int mk0 = wave_max_i(qvalid ? qk0 : INT_MIN);  // keys every row of the wave needs
   const int mk1 = wave_min_i(qvalid ? qk1 : INT_MAX);
+  const int64_t qoff = static_cast<int64_t>(qrow) * ld + g * G::HALF;
 
   typename RegT<Et>::type qr[G::QS];
-  load_row_regs<Et, D>(qp, static_cast<int64_t>(qrow) * ld + h * D + g * G::HALF, qvalid, qr);
+  load_row_regs<Et, D>(qp, qoff + h0 * D, qvalid, qr);
 
   uint4 kr[G::PER], vr[G::PER];
   floatx16 o[G::DB];
@@ -67,15 +79,89 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
   for (int db = 0; db < G::DB; ++db) o[db] = floatx16{};
   float m = kNegBig, l = 0.f;
 
+  auto finish = [&](int h) __attribute__((always_inline)) {
+    const float lt = xhalf_sum(l);
+    const float inv = lt > 0.f ? 1.f / lt : 0.f;
+    if (qvalid) {
+      store_acc_row<Et, D>(op, (static_cast<int64_t>(qrow) * H + h) * D, o, inv, g);
+      if (lse != nullptr && g == 0) lse[static_cast<int64_t>(h) * N + qrow] = (m + log2f(lt)) * kLn2;
+    }
+#pragma unroll
+    for (int db = 0; db < G::DB; ++db) o[db] = floatx16{};
+    m = kNegBig;
+    l = 0.f;
+  };
+
+  // one 64-key block of LDS tile `buf` against the lane's query row
+  auto block = [&](int kb, int buf) __attribute__((always_inline)) {
+    if (!(kb < wk1 && kb + kBlk > wk0)) return;
+    floatx16 s[2];
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      s[kk] = floatx16{};
+      if constexpr (SWZ) mma_rows_swz<Et, D>(kt[buf], 32 * kk, qr, s[kk], ql, g);
+      else mma_rows_regs<Et, D>(kt[buf], 32 * kk, qr, s[kk], ql, g);
+    }
+    if (!(kb >= mk0 && kb + kBlk <= mk1)) {
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        const int base = kb + 32 * kk + 4 * g;
+        mask_block(s[kk], qk0 - base, qk1 - base);
+      }
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kk][i]);
+    mx = xhalf_max(mx);
+    const float mnew = fmaxf(m, mx * c);
+    if (__any(mnew > m)) {
+      const float alpha = __builtin_amdgcn_exp2f(m - mnew);
+      l *= alpha;
+#pragma unroll
+      for (int db = 0; db < G::DB; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
+      m = mnew;
+    }
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float p = __builtin_amdgcn_exp2f(fmaf(s[kk][i], c, -m));
+        s[kk][i] = p;
+        l += p;
+      }
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      if constexpr (SWZ) {
+        vec8<Et> pb[2];
+        acc_to_h16<Et>(s[kk], pb);
+        mma_tr_swz<Et, D>(vt[buf], 32 * kk, pb, o, lane);
+      } else {
+        mma_tr_regs<Et, D>(vt[buf], 32 * kk, s[kk], o, lane);
+      }
+    }
+  };
+
   // keys of the tile: those of its sequences, and within win of its rows for local attention
   const int klo = win >= 0 ? max(sp.lo, sp.r0 - win) : sp.lo;
   const int khi = win >= 0 ? min(sp.hi, sp.rend + win) : sp.hi;
-  int buf = 0;
-  if (klo < khi) {
-    tile_gload<Et, D>(kp, klo, khi, ld, h, kr);
-    tile_gload<Et, D>(vp, klo, khi, ld, h, vr);
+  const int nkb = klo < khi ? (khi - klo + kBlk - 1) / kBlk : 0;
+  if (nkb == 0) {  // no keys at all (not reached by valid offsets): zero outputs
+    for (int hh = 0; hh < nh; ++hh) finish(h0 + hh);
+    return;
   }
-  for (int kb = klo; kb < khi; kb += kBlk) {
+  // Steps run over (head, key block) pairs, heads outer. The key blocks are the
+  // same for every head, so the register-staged prefetch of the next step's
+  // K and V rows runs on across the head boundary.
+  tile_gload<Et, D>(kp, klo, khi, ld, h0, kr);
+  tile_gload<Et, D>(vp, klo, khi, ld, h0, vr);
+  int buf = 0, hh = 0, j = 0;
+  const int nsteps = nh * nkb;
+  for (int step = 0; step < nsteps; ++step) {
+    const int kb = klo + j * kBlk;
     if constexpr (SWZ) {
       tile_store_swz<D>(kt[buf], kr);
       tile_store_swz<D>(vt[buf], vr);
@@ -84,68 +170,33 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
       tile_store<Et, D>(vt[buf], vr);
     }
     __syncthreads();
-    if (kb + kBlk < khi) {
-      tile_gload<Et, D>(kp, kb + kBlk, khi, ld, h, kr);
-      tile_gload<Et, D>(vp, kb + kBlk, khi, ld, h, vr);
+    const bool last = j + 1 == nkb;  // last key block of head h0 + hh
+    if (step + 1 < nsteps) {
+      const int hn = h0 + (last ? hh + 1 : hh);
+      const int kn = last ? klo : kb + kBlk;
+      tile_gload<Et, D>(kp, kn, khi, ld, hn, kr);
+      tile_gload<Et, D>(vp, kn, khi, ld, hn, vr);
     }
-    if (kb < wk1 && kb + kBlk > wk0) {
-      floatx16 s[2];
+    typename RegT<Et>::type qn[G::QS];
+    const bool next_head = last && hh + 1 < nh;
+    if (PREFQ && next_head) load_row_regs<Et, D>(qp, qoff + (h0 + hh + 1) * D, qvalid, qn);
+    block(kb, buf);
+    if (last) {
+      finish(h0 + hh);
+      if (next_head) {
+        if constexpr (PREFQ) {
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        s[kk] = floatx16{};
-        if constexpr (SWZ) mma_rows_swz<Et, D>(kt[buf], 32 * kk, qr, s[kk], ql, g);
-        else mma_rows_regs<Et, D>(kt[buf], 32 * kk, qr, s[kk], ql, g);
-      }
-      if (!(kb >= mk0 && kb + kBlk <= mk1)) {
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-          const int base = kb + 32 * kk + 4 * g;
-          mask_block(s[kk], qk0 - base, qk1 - base);
-        }
-      }
-      float mx = -INFINITY;
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kk][i]);
-      mx = xhalf_max(mx);
-      const float mnew = fmaxf(m, mx * c);
-      if (__any(mnew > m)) {
-        const float alpha = __builtin_amdgcn_exp2f(m - mnew);
-        l *= alpha;
-#pragma unroll
-        for (int db = 0; db < G::DB; ++db)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
-        m = mnew;
-      }
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const float p = __builtin_amdgcn_exp2f(fmaf(s[kk][i], c, -m));
-          s[kk][i] = p;
-          l += p;
-        }
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        if constexpr (SWZ) {
-          vec8<Et> pb[2];
-          acc_to_h16<Et>(s[kk], pb);
-          mma_tr_swz<Et, D>(vt[buf], 32 * kk, pb, o, lane);
+          for (int st = 0; st < G::QS; ++st) qr[st] = qn[st];
         } else {
-          mma_tr_regs<Et, D>(vt[buf], 32 * kk, s[kk], o, lane);
+          load_row_regs<Et, D>(qp, qoff + (h0 + hh + 1) * D, qvalid, qr);
         }
       }
+      ++hh;
+      j = 0;
+    } else {
+      ++j;
     }
     buf ^= 1;
-  }
-
-  const float lt = xhalf_sum(l);
-  const float inv = lt > 0.f ? 1.f / lt : 0.f;
-  if (qvalid) {
-    store_acc_row<Et, D>(op, (static_cast<int64_t>(qrow) * H + h) * D, o, inv, g);
-    if (lse != nullptr && g == 0) lse[static_cast<int64_t>(h) * N + qrow] = (m + log2f(lt)) * kLn2;
   }
 }
 
@@ -281,12 +332,16 @@ hipError_t fwd_dispatch(const void* q, const void* k, const void* v, const int32
                         const int32_t* items, int32_t B, int32_t N, int32_t H, int32_t win, int64_t ld,
                         float scale, void* out, float* lse, hipStream_t stream) {
   const int T = (N + kAttnTileRows - 1) / kAttnTileRows;
-  const int64_t blocks = static_cast<int64_t>(T) * H;
-  if (blocks == 0) return hipSuccess;
+  if (T == 0) return hipSuccess;
+  // heads per block: as many as keep at least kFwdMinBlocks blocks in the launch
+  int HG = static_cast<int>(std::min<int64_t>(H, std::max<int64_t>(1, static_cast<int64_t>(T) * H / kFwdMinBlocks)));
+  const int HGN = (H + HG - 1) / HG;
+  HG = (H + HGN - 1) / HGN;  // even groups
+  const int64_t blocks = static_cast<int64_t>(T) * HGN;
   const float c = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
   hipEvent_t ev_attn_fwd = timing_start(stream);
   hipLaunchKernelGGL((attn_fwd_kernel<Et, D>), dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0, stream,
-                   q, k, v, cu, items, B, N, H, T, win, ld, c, out, lse);
+                   q, k, v, cu, items, B, N, H, T, HG, win, ld, c, out, lse);
   timing_stop("attn_fwd", ev_attn_fwd, stream);
   return hipGetLastError();
 }
