@@ -34,16 +34,18 @@ KERNEL_SOURCES = {
     "worklist": ["pack.hip", "common.h"],
 }
 
-# device kernel names (as the profiler prints them) behind each timing name
+# device kernel names behind each timing name, as the profiler prints them:
+# demangled ("attn_fwd_kernel<float, 64>") or, where its demangler does not know
+# the __bf16 mangling, mangled ("...15attn_fwd_kernelIDF16bLi64E...")
 KERNEL_PATTERNS = {
-    "attn_fwd": r"attn_fwd(_bf16|_bf16_w64|_f32)?_kernel<",
-    "attn_fwd_first": r"attn_fwd_first_kernel<",
-    "attn_bwd_first": r"attn_bwd_first_kernel<",
-    "bwd_delta": r"bwd_delta_kernel<",
-    "bwd_dkdv": r"bwd_dkdv(_f32)?_kernel<",
-    "bwd_dq": r"bwd_dq(_f32)?_kernel<",
-    "pack_rows": r"(?<!un)pack_rows_kernel<",
-    "unpack_rows": r"unpack_rows_kernel<",
+    "attn_fwd": r"attn_fwd(_bf16|_bf16_w64|_f32)?_kernel(<|I)",
+    "attn_fwd_first": r"attn_fwd_first_kernel(<|I)",
+    "attn_bwd_first": r"attn_bwd_first_kernel(<|I)",
+    "bwd_delta": r"bwd_delta_kernel(<|I)",
+    "bwd_dkdv": r"bwd_dkdv(_f32)?_kernel(<|I)",
+    "bwd_dq": r"bwd_dq(_f32)?_kernel(<|I)",
+    "pack_rows": r"(?<!un)pack_rows_kernel(<|I)",
+    "unpack_rows": r"unpack_rows_kernel(<|I)",
     "scan": r"scan_lengths_kernel",
     "worklist": r"worklist_kernel",
 }
