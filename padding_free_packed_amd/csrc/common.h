@@ -54,6 +54,21 @@ __device__ __forceinline__ uint16_t f32_to_h16(float f) {
   return __builtin_bit_cast(uint16_t, static_cast<T>(f));
 }
 
+// Store with the non-temporal hint (streaming writes of copies that no later
+// kernel step reads back from the caches); U is a 1-16 byte unit.
+template <typename U>
+__device__ __forceinline__ void st_nt(U* p, const U& v) {
+  if constexpr (sizeof(U) == 16) {
+    typedef unsigned int u4 __attribute__((ext_vector_type(4)));
+    __builtin_nontemporal_store(__builtin_bit_cast(u4, v), reinterpret_cast<u4*>(p));
+  } else if constexpr (sizeof(U) == 8) {
+    typedef unsigned int u2 __attribute__((ext_vector_type(2)));
+    __builtin_nontemporal_store(__builtin_bit_cast(u2, v), reinterpret_cast<u2*>(p));
+  } else {
+    __builtin_nontemporal_store(v, p);
+  }
+}
+
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 // Finite stand-in for minus infinity as the running maximum, so that

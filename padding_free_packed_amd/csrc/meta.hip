@@ -175,7 +175,7 @@ __global__ __launch_bounds__(256) void gather_rows_kernel(const U* __restrict__ 
        i += static_cast<int64_t>(gridDim.x) * 256) {
     const int64_t row = i / upr, u = i - row * upr;
     const int64_t s = flat[row];
-    dst[i] = (s >= 0 && s < src_rows) ? src[s * upr + u] : U{};
+    st_nt(dst + i, (s >= 0 && s < src_rows) ? src[s * upr + u] : U{});
   }
 }
 
@@ -183,7 +183,7 @@ template <typename U>
 __global__ __launch_bounds__(256) void fill_zero_kernel(U* __restrict__ dst, int64_t total) {
   for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < total;
        i += static_cast<int64_t>(gridDim.x) * 256)
-    dst[i] = U{};
+    st_nt(dst + i, U{});
 }
 
 template <typename U>
@@ -195,7 +195,7 @@ __global__ __launch_bounds__(256) void scatter_rows_kernel(const U* __restrict__
        i += static_cast<int64_t>(gridDim.x) * 256) {
     const int64_t row = i / upr, u = i - row * upr;
     const int64_t d = flat[row];
-    if (d >= 0 && d < dst_rows) dst[d * upr + u] = src[i];
+    if (d >= 0 && d < dst_rows) st_nt(dst + d * upr + u, src[i]);
   }
 }
 

@@ -106,19 +106,19 @@ __device__ __forceinline__ void copy_units(const U* __restrict__ src, U* __restr
   constexpr int BS = 256;
   for (; i + 3 * BS < n; i += 4 * BS) {
     const U a = src[i], b = src[i + BS], c = src[i + 2 * BS], d = src[i + 3 * BS];
-    dst[i] = a;
-    dst[i + BS] = b;
-    dst[i + 2 * BS] = c;
-    dst[i + 3 * BS] = d;
+    st_nt(dst + i, a);
+    st_nt(dst + i + BS, b);
+    st_nt(dst + i + 2 * BS, c);
+    st_nt(dst + i + 3 * BS, d);
   }
-  for (; i < n; i += BS) dst[i] = src[i];
+  for (; i < n; i += BS) st_nt(dst + i, src[i]);
 }
 
 template <typename U>
 __device__ __forceinline__ void zero_units(U* __restrict__ dst, int64_t n) {
   U z;
   __builtin_memset(&z, 0, sizeof(U));
-  for (int64_t i = threadIdx.x; i < n; i += 256) dst[i] = z;
+  for (int64_t i = threadIdx.x; i < n; i += 256) st_nt(dst + i, z);
 }
 
 // Block w packs rows [w*R, min((w+1)*R, N)) of the packed buffer. items[w] is
