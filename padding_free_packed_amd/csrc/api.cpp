@@ -238,7 +238,7 @@ pe_status first_impl(const void* q, int32_t gather, const void* k, const void* v
                         static_cast<const void*>(lse_first)})
     if (p && !aligned16(p)) return PE_ERR_ARG;
   return hip_status(pe::launch_attn_fwd_first(dtype, head_dim, q, k, v, cu_seqlens, num_seqs,
-                                              static_cast<int32_t>(total_tokens), num_heads, gather,
+                                              static_cast<int32_t>(total_tokens), num_heads, max_seq_len, gather,
                                               static_cast<int64_t>(num_heads) * head_dim, softmax_scale, out_first,
                                               lse_first, as_stream(stream)));
 }
@@ -280,7 +280,8 @@ pe_status pe_varlen_attn_bwd_first_token(const void* dout_first, const void* q_f
     if (!aligned16(p)) return PE_ERR_ARG;
   return hip_status(pe::launch_attn_bwd_first(dtype, head_dim, dout_first, q_first, k, v, out_first,
                                               lse_first, cu_seqlens, num_seqs, static_cast<int32_t>(total_tokens),
-                                              num_heads, static_cast<int64_t>(num_heads) * head_dim, softmax_scale,
+                                              num_heads, max_seq_len, static_cast<int64_t>(num_heads) * head_dim,
+                                              softmax_scale,
                                               dq_first, dk, dv, as_stream(stream)));
 }
 

@@ -12,6 +12,7 @@
 // keys slot, slot + KS, ... in batches of four rows whose loads are issued
 // before any is used; dq partials of the slots merge through LDS at the end.
 // No atomics: every output element has exactly one writer.
+#include <algorithm>
 #include <type_traits>
 
 #include "attn_common.h"
@@ -149,11 +150,14 @@ __global__ __launch_bounds__(kFbThreads) void attn_bwd_first_kernel(
 
 template <typename Et, int D>
 hipError_t bwd_first_dispatch(const void* dof, const void* qf, const void* k, const void* v, const void* of,
-                              const float* lse, const int32_t* cu, int32_t B, int32_t N, int32_t H, int64_t ld,
-                              float scale, void* dq, void* dk, void* dv, hipStream_t stream) {
+                              const float* lse, const int32_t* cu, int32_t B, int32_t N, int32_t H,
+                              int32_t max_seq_len, int64_t ld, float scale, void* dq, void* dk, void* dv,
+                              hipStream_t stream) {
   constexpr int GS = D / (kIs16<Et> ? 8 : 4);
-  const int HPB = (H * GS <= kFbThreads) ? H : kFbThreads / GS;
-  const int HG = (H + HPB - 1) / HPB;
+  // heads per block: as many as leave the key slots the first-token forward takes
+  const int HPB0 = std::max(1, std::min<int>(H, kFbThreads / (GS * first_token_slots(max_seq_len))));
+  const int HG = (H + HPB0 - 1) / HPB0;
+  const int HPB = (H + HG - 1) / HG;
   const float c = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
   hipEvent_t ev = timing_start(stream);
   hipLaunchKernelGGL((attn_bwd_first_kernel<Et, D>), dim3(B, HG), dim3(kFbThreads), 0, stream, dof, qf, k, v, of,
@@ -166,16 +170,16 @@ hipError_t bwd_first_dispatch(const void* dof, const void* qf, const void* k, co
 
 hipError_t launch_attn_bwd_first(int dt, int D, const void* dout_first, const void* q_first, const void* k,
                                  const void* v, const void* out_first, const float* lse_first, const int32_t* cu,
-                                 int32_t B, int32_t N, int32_t H, int64_t ld, float scale, void* dq_first, void* dk,
-                                 void* dv, hipStream_t stream) {
+                                 int32_t B, int32_t N, int32_t H, int32_t max_seq_len, int64_t ld, float scale,
+                                 void* dq_first, void* dk, void* dv, hipStream_t stream) {
 #define PE_FB_CASE(DD)                                                                                        \
   case DD:                                                                                                   \
     return dt == kDtF32  ? bwd_first_dispatch<float, DD>(dout_first, q_first, k, v, out_first, lse_first, cu, B, N, \
-                                                        H, ld, scale, dq_first, dk, dv, stream)                   \
+                                                        H, max_seq_len, ld, scale, dq_first, dk, dv, stream)                   \
            : dt == kDtF16 ? bwd_first_dispatch<_Float16, DD>(dout_first, q_first, k, v, out_first, lse_first, cu, B, \
-                                                           N, H, ld, scale, dq_first, dk, dv, stream)             \
+                                                           N, H, max_seq_len, ld, scale, dq_first, dk, dv, stream)             \
                          : bwd_first_dispatch<__bf16, DD>(dout_first, q_first, k, v, out_first, lse_first, cu, B, N, \
-                                                         H, ld, scale, dq_first, dk, dv, stream);
+                                                         H, max_seq_len, ld, scale, dq_first, dk, dv, stream);
   switch (D) {
     PE_FB_CASE(8)
     PE_FB_CASE(16)

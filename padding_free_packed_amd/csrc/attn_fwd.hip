@@ -209,6 +209,12 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
 // HBM round trips in flight per thread), keeps its own running max, sum and
 // output, and the slots merge through LDS at the end.
 constexpr int kFirstThreads = 512;
+
+// Key slots per block of the first-token kernels: few for short sequences (a
+// block then covers many heads of a row, read as one contiguous run), more as
+// the length bound grows (a long sequence is one block's work, and its loads
+// in flight scale with the slots): max_seq_len / 16, within [4, 32]. Defined
+// at the end of this file (first_token_slots, declared in kernels.h).
 constexpr int kFirstBatch = 4;
 
 template <typename Et, int D>
@@ -348,11 +354,13 @@ hipError_t fwd_dispatch(const void* q, const void* k, const void* v, const int32
 
 template <typename Et, int D>
 hipError_t first_dispatch(const void* q, const void* k, const void* v, const int32_t* cu, int32_t B,
-                          int32_t N, int32_t H, int32_t gather, int64_t ld, float scale, void* out, float* lse,
-                          hipStream_t stream) {
+                          int32_t N, int32_t H, int32_t max_seq_len, int32_t gather, int64_t ld, float scale,
+                          void* out, float* lse, hipStream_t stream) {
   constexpr int GS = D / (kIs16<Et> ? 8 : 4);
-  const int HPB = (H * GS <= kFirstThreads) ? H : kFirstThreads / GS;
-  const int HG = (H + HPB - 1) / HPB;
+  // heads per block: as many as leave the key slots wanted, then even groups
+  const int HPB0 = std::max(1, std::min<int>(H, kFirstThreads / (GS * first_token_slots(max_seq_len))));
+  const int HG = (H + HPB0 - 1) / HPB0;
+  const int HPB = (H + HG - 1) / HG;
   const float c = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
   hipEvent_t ev_attn_fwd_first = timing_start(stream);
   hipLaunchKernelGGL((attn_fwd_first_kernel<Et, D>), dim3(B, HG), dim3(kFirstThreads), 0, stream, q, k, v, cu, B,
@@ -390,15 +398,16 @@ hipError_t launch_attn_fwd(int dt, int D, const void* q, const void* k, const vo
 }
 
 hipError_t launch_attn_fwd_first(int dt, int D, const void* q_first, const void* k, const void* v,
-                                 const int32_t* cu, int32_t B, int32_t N, int32_t H, int32_t gather, int64_t ld,
-                                 float scale, void* out_first, float* lse_first, hipStream_t stream) {
+                                 const int32_t* cu, int32_t B, int32_t N, int32_t H, int32_t max_seq_len,
+                                 int32_t gather, int64_t ld, float scale, void* out_first, float* lse_first,
+                                 hipStream_t stream) {
 #define PE_FIRST_CASE(DD)                                                                                     \
   case DD:                                                                                                   \
-    return dt == kDtF32  ? first_dispatch<float, DD>(q_first, k, v, cu, B, N, H, gather, ld, scale, out_first,    \
+    return dt == kDtF32  ? first_dispatch<float, DD>(q_first, k, v, cu, B, N, H, max_seq_len, gather, ld, scale, out_first,    \
                                                     lse_first, stream)                                           \
-           : dt == kDtF16 ? first_dispatch<_Float16, DD>(q_first, k, v, cu, B, N, H, gather, ld, scale, out_first, \
+           : dt == kDtF16 ? first_dispatch<_Float16, DD>(q_first, k, v, cu, B, N, H, max_seq_len, gather, ld, scale, out_first, \
                                                        lse_first, stream)                                        \
-                         : first_dispatch<__bf16, DD>(q_first, k, v, cu, B, N, H, gather, ld, scale, out_first,    \
+                         : first_dispatch<__bf16, DD>(q_first, k, v, cu, B, N, H, max_seq_len, gather, ld, scale, out_first,    \
                                                      lse_first, stream);
   switch (D) {
     PE_FIRST_CASE(8)
@@ -410,5 +419,7 @@ hipError_t launch_attn_fwd_first(int dt, int D, const void* q_first, const void*
   }
 #undef PE_FIRST_CASE
 }
+
+int first_token_slots(int max_seq_len) { return std::max(4, std::min(32, max_seq_len / 16)); }
 
 }  // namespace pe

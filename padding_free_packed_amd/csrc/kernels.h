@@ -69,14 +69,17 @@ hipError_t launch_bwd_dq_f32_wave(int D, const void* dout, const void* q, const 
                                   hipStream_t stream);
 
 // gather = 0: q_first is [B, H, D]; gather = 1: the query of sequence b is row cu[b] of a packed [N, H, D]
+// max_seq_len (the host length bound) sets the key slots per block of both first-token kernels.
+int first_token_slots(int max_seq_len);
 hipError_t launch_attn_fwd_first(int dt, int D, const void* q_first, const void* k, const void* v,
-                                 const int32_t* cu, int32_t B, int32_t N, int32_t H, int32_t gather, int64_t ld,
-                                 float scale, void* out_first, float* lse_first, hipStream_t stream);
+                                 const int32_t* cu, int32_t B, int32_t N, int32_t H, int32_t max_seq_len,
+                                 int32_t gather, int64_t ld, float scale, void* out_first, float* lse_first,
+                                 hipStream_t stream);
 // backward of the first-token readout: dq_first [B, H, D], dk and dv [N, H, D] (every row written)
 hipError_t launch_attn_bwd_first(int dt, int D, const void* dout_first, const void* q_first, const void* k,
                                  const void* v, const void* out_first, const float* lse_first, const int32_t* cu,
-                                 int32_t B, int32_t N, int32_t H, int64_t ld, float scale, void* dq_first, void* dk,
-                                 void* dv, hipStream_t stream);
+                                 int32_t B, int32_t N, int32_t H, int32_t max_seq_len, int64_t ld, float scale,
+                                 void* dq_first, void* dk, void* dv, hipStream_t stream);
 
 // Backward: D = rowsum(dO * O) per (head, row), then dK/dV over key tiles, then dQ over query tiles.
 // items: work list with tile height kAttnTileRows; items32: with kAttnWaveRows (or NULL).
