@@ -8,7 +8,7 @@
 // otherwise the limit of the d=64 attention loop, ahead of the matrix core.
 //
 //   * K and V tiles of 32 keys travel global -> LDS by LDS DMA into a ring of
-//     four stages, three blocks ahead; tiles are unpadded with XOR-swizzled
+//     three stages, two blocks ahead; tiles are unpadded with XOR-swizzled
 //     16-byte chunks;
 //   * S^T = K Q^T per query block (K rows as A operand, Q^T from registers),
 //     then O^T += V^T P^T with P taken straight from the accumulators and V^T
@@ -31,7 +31,8 @@ namespace {
 constexpr int kW64Waves = 2;
 constexpr int kW64Threads = 64 * kW64Waves;
 constexpr int kW64Keys = 32;    // keys per ring stage
-constexpr int kW64Stages = 4;
+constexpr int kW64Stages = 3;  // 2..6
+static_assert(kW64Stages >= 2 && kW64Stages <= 6, "ring stages");
 constexpr float kRescaleHeadroom = 8.f;
 
 template <int ST>
@@ -204,14 +205,28 @@ __global__ __launch_bounds__(kW64Threads) __attribute__((amdgpu_waves_per_eu(2))
   // Step j: S of both query blocks for key block j, then softmax and PV per query
   // block. A query block that does not need block j sees it fully masked (P = 0,
   // no max change), so one straight-line path serves every needed block.
+  constexpr int AHEAD = kW64Stages - 1;  // blocks in flight ahead of the one computed
+  // Wait until block j has landed: `later` blocks issued after it may stay in
+  // flight (each 2*NL DMA instructions per thread; loads complete in order).
+  auto wait_block = [&](int later) __attribute__((always_inline)) {
+    if constexpr (AHEAD - 1 >= 4) {
+      if (later >= 4) { wait_vmcnt<8 * NL>(); return; }
+    }
+    if constexpr (AHEAD - 1 >= 3) {
+      if (later >= 3) { wait_vmcnt<6 * NL>(); return; }
+    }
+    if constexpr (AHEAD - 1 >= 2) {
+      if (later >= 2) { wait_vmcnt<4 * NL>(); return; }
+    }
+    if (later >= 1) { wait_vmcnt<2 * NL>(); return; }
+    wait_vmcnt<0>();
+  };
   auto step = [&](auto tag, int j) __attribute__((always_inline)) {
     constexpr int ST = decltype(tag)::value;
-    constexpr int STF = (ST + 3) % kW64Stages;  // stage receiving block j+3
-    if (j + 2 < nblk) wait_vmcnt<4 * NL>();
-    else if (j + 1 < nblk) wait_vmcnt<2 * NL>();
-    else wait_vmcnt<0>();
+    constexpr int STF = (ST + AHEAD) % kW64Stages;  // stage receiving block j+AHEAD
+    wait_block(min(AHEAD - 1, nblk - 1 - j));
     raw_barrier();  // block j visible to all; the stage of block j-1 is no longer read
-    if (j + 3 < nblk) issue(j + 3, STF);
+    if (j + AHEAD < nblk) issue(j + AHEAD, STF);
     const int kb = klo + j * kW64Keys;
     const bool need0 = kb < bk1[0] && kb + kW64Keys > bk0[0];
     const bool need1 = kb < bk1[1] && kb + kW64Keys > bk0[1];
@@ -228,14 +243,23 @@ __global__ __launch_bounds__(kW64Threads) __attribute__((amdgpu_waves_per_eu(2))
     pv(1, pb1, vt);
   };
 
-  if (nblk > 0) issue(0, 0);
-  if (nblk > 1) issue(1, 1);
-  if (nblk > 2) issue(2, 2);
+  for (int i = 0; i < AHEAD; ++i)
+    if (i < nblk) issue(i, i);
   for (int j = 0; j < nblk; j += kW64Stages) {
     step(W64Stage<0>{}, j);
     if (j + 1 < nblk) step(W64Stage<1>{}, j + 1);
-    if (j + 2 < nblk) step(W64Stage<2>{}, j + 2);
-    if (j + 3 < nblk) step(W64Stage<3>{}, j + 3);
+    if constexpr (kW64Stages > 2) {
+      if (j + 2 < nblk) step(W64Stage<2>{}, j + 2);
+    }
+    if constexpr (kW64Stages > 3) {
+      if (j + 3 < nblk) step(W64Stage<3>{}, j + 3);
+    }
+    if constexpr (kW64Stages > 4) {
+      if (j + 4 < nblk) step(W64Stage<4>{}, j + 4);
+    }
+    if constexpr (kW64Stages > 5) {
+      if (j + 5 < nblk) step(W64Stage<5>{}, j + 5);
+    }
   }
 
 #pragma unroll
