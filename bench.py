@@ -288,9 +288,9 @@ def main():
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE={world}): this build "
-              "measures the single-GPU path; sharding across GPUs is described in DESIGN.md, not run.",
-              file=sys.stderr)
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE={world}): it measures "
+              "one GPU's share of the batch. The path shards by sequence (no exchange inside attention), "
+              "which is not run here.", file=sys.stderr)
         sys.exit(2)
 
     if args.workload == "short_batch":
