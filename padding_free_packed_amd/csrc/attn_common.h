@@ -324,35 +324,6 @@ __device__ __forceinline__ void raw_barrier() { asm volatile("s_barrier" ::: "me
 template <int D>
 constexpr int dma_per_tile() { return kBlk * (D / 8) / kThreads; }
 
-// Issue the LDS-DMA copy of rows row0..row0+kBlk-1 of head h of a [N, H, D]
-// 16-bit tensor into an LDS tile. Rows >= row_lim repeat row row_lim-1 (valid
-// memory; kernels mask those keys). A wave's instruction fills 64 consecutive
-// 16-byte LDS slots (M0 = wave base, lane l -> slot l); the global address of
-// each lane is chosen so that the slot receives its swizzled chunk.
-// The copy is asynchronous: it is complete for this thread once vmcnt drops
-// below the number of later VMEM instructions.
-template <int D>
-__device__ __forceinline__ void dma_tile16(const uint16_t* lds_tile, const void* gbase, int row0, int row_lim,
-                                              int H, int h) {
-  constexpr int CH = D / 8;
-  constexpr int NLD = dma_per_tile<D>();
-  static_assert(NLD >= 1, "one DMA instruction per thread at least");
-  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
-  const char* gb = static_cast<const char*>(gbase);
-  const uint32_t tile = lds_addr(lds_tile);
-#pragma unroll
-  for (int j = 0; j < NLD; ++j) {
-    const int slot = j * kThreads + w * 64 + l;
-    const int r = slot / CH, pc = slot - r * CH;
-    const int c = pc ^ (swz(r) & (CH - 1));
-    const int gr = min(row0 + r, row_lim - 1);
-    const char* src = gb + (static_cast<int64_t>(gr) * H + h) * (D * 2) + c * 16;
-    const uint32_t dst = __builtin_amdgcn_readfirstlane(tile + (j * kThreads + w * 64) * 16);
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(dst), "v"(src)
-                 : "memory", "m0");
-  }
-}
-
 // One LDS-DMA instruction: 16 bytes per lane from sbase + voff (sbase wave-
 // uniform, voff per lane) to LDS bytes [lds, lds + 1024) of the wave, lane l
 // writing lds + 16*l.

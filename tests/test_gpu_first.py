@@ -7,7 +7,7 @@ import torch
 
 import oracle
 from padding_free_packed_amd import workloads as W
-from tests.gpu_util import DEV, from_dev, say, to_dev, to_f64
+from tests.gpu_util import DEV, check_out, from_dev, say, to_dev, to_f64
 from tests.test_gpu_bwd import check_grad
 
 pytestmark = pytest.mark.gpu
@@ -99,3 +99,30 @@ def test_graph_transformer_first_token_backward_sampled():
         check_grad(gdq[b:b + 1].astype(np.float64), ref[0], w.dtype, f"gt seq {b} dq_first")
         check_grad(gdk[c0:c1].astype(np.float64), ref[1], w.dtype, f"gt seq {b} dk")
         check_grad(gdv[c0:c1].astype(np.float64), ref[2], w.dtype, f"gt seq {b} dv")
+
+
+def test_mixed_training_first_token_backward_sampled():
+    """Full-size mixed batch (bf16, 16 heads, documents up to 8192 tokens): the length
+    bound gives each block 32 key slots, so a long document is spread over many slots.
+    The longest documents and a spread of others are checked against the oracle."""
+    w = W.mixed_training()
+    say(f"[first bwd] mixed-training full size: B={w.num_seqs} N={w.total_tokens}")
+    cu_ref, _, N = oracle.layout(w.lengths, w.max_seq_len)
+    dof_bits = w.dout[cu_ref[:-1]]
+    cu_ref, q, k, v, cu, qf, out_f, lse_f, dqf, dk, dv = first_fwd_bwd(w, dof_bits)
+    L = np.diff(cu_ref)
+    seqs = sorted(set(np.argsort(L)[-4:].tolist()) | set(range(0, w.num_seqs, 211)))
+    gdk, gdv, gdq = to_f64(dk), to_f64(dv), to_f64(dqf)
+    qd, kd, vd = (W.to_f64(x, w.dtype) for x in (w.q, w.k, w.v))
+    for b in seqs:
+        c0, c1 = int(cu_ref[b]), int(cu_ref[b + 1])
+        cu_b = np.array([0, c1 - c0], dtype=np.int32)
+        qb, kb, vb = qd[c0:c0 + 1], kd[c0:c1], vd[c0:c1]
+        dob = W.to_f64(dof_bits[b:b + 1], w.dtype)
+        o_ref, l_ref = oracle.attention_first_token(qb, kb, vb, cu_b, w.scale)
+        given = W.to_f64(W.to_bits(o_ref.astype(np.float32), w.dtype), w.dtype)
+        check_out(to_f64(out_f)[b:b + 1], o_ref, w.dtype, f"mt seq {b} out_first")
+        ref = oracle.attention_first_token_backward(dob, qb, kb, vb, cu_b, w.scale, out_first=given, lse_first=l_ref)
+        check_grad(gdq[b:b + 1], ref[0], w.dtype, f"mt seq {b} dq_first")
+        check_grad(gdk[c0:c1], ref[1], w.dtype, f"mt seq {b} dk")
+        check_grad(gdv[c0:c1], ref[2], w.dtype, f"mt seq {b} dv")
