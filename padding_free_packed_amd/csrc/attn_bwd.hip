@@ -110,10 +110,10 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(
   auto gload = [&](int qb) {
     tile_gload<Et, D>(qp, qb, qhi, ld, h, qr);
     tile_gload<Et, D>(dop, qb, qhi, static_cast<int64_t>(H) * D, h, dr);
-    if (tid < kBlk) {
-      const int row = qb + tid;
-      lsr = row < qhi ? lse_h[row] * kLog2e : 0.f;
-      dlr = row < qhi ? del_h[row] : 0.f;
+    if (tid < kBlk) {  // raw values: any arithmetic here would wait for the whole prefetch
+      const int row = min(qb + tid, qhi - 1);
+      lsr = lse_h[row];
+      dlr = del_h[row];
     }
   };
 
@@ -128,8 +128,9 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(
       tile_store<Et, D>(dt[buf], dr);
     }
     if (tid < kBlk) {
-      ls[buf][tid] = lsr;
-      dl[buf][tid] = dlr;
+      const bool in = qb + tid < qhi;
+      ls[buf][tid] = in ? lsr * kLog2e : 0.f;
+      dl[buf][tid] = in ? dlr : 0.f;
     }
     __syncthreads();
     if (qb + kBlk < qhi) gload(qb + kBlk);

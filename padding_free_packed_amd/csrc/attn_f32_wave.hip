@@ -150,10 +150,15 @@ __global__ __launch_bounds__(64, 2) void attn_fwd_f32_kernel(
     O a, b;
     load_ops<D>(a, kp, vp, wk0, klast, ld, h, ql, g);
     for (int kb = wk0; kb < wk1; kb += 64) {
-      if (kb + 32 < wk1) load_ops<D>(b, kp, vp, kb + 32, klast, ld, h, ql, g);
+      // Unconditional (rows clamp to klast, so a step past the end reloads the last rows): a
+      // load under a branch makes the wait counts at the join assume the worst path and wait
+      // for the younger loads too. The empty asm keeps each load group where it is written.
+      load_ops<D>(b, kp, vp, kb + 32, klast, ld, h, ql, g);
+      asm volatile("" ::: "memory");
       block(a, kb);
       if (kb + 32 >= wk1) break;
-      if (kb + 64 < wk1) load_ops<D>(a, kp, vp, kb + 64, klast, ld, h, ql, g);
+      load_ops<D>(a, kp, vp, kb + 64, klast, ld, h, ql, g);
+      asm volatile("" ::: "memory");
       block(b, kb + 32);
     }
   }
@@ -302,9 +307,11 @@ __global__ __launch_bounds__(64, 2) void bwd_dq_f32_kernel(
         s = __builtin_amdgcn_mfma_f32_32x32x2f32(kr[st], qf[st], s, 0, 0, 0);
         dp = __builtin_amdgcn_mfma_f32_32x32x2f32(vr[st], df[st], dp, 0, 0, 0);
       }
-      if (more) {
-        load_rows<D>(kr, at(kp, kb + 32, LD), min(ql, klast - kb - 32), LD, g);
-        load_rows<D>(vr, at(vp, kb + 32, LD), min(ql, klast - kb - 32), LD, g);
+      {
+        const int nb = more ? kb + 32 : kb;
+        load_rows<D>(kr, at(kp, nb, LD), min(ql, klast - nb), LD, g);
+        load_rows<D>(vr, at(vp, nb, LD), min(ql, klast - nb), LD, g);
+        asm volatile("" ::: "memory");
       }
       if (!(kb >= mk0 && kb + 32 <= mk1)) {
         const int base = kb + 4 * g;
@@ -319,7 +326,11 @@ __global__ __launch_bounds__(64, 2) void bwd_dq_f32_kernel(
       for (int st = 0; st < 16; ++st)
 #pragma unroll
         for (int db = 0; db < DB; ++db) dq[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(kt[st][db], dp[st], dq[db], 0, 0, 0);
-      if (more) load_tr<D>(kt, at(kp, kb + 32, LD), klast - kb - 32, LD, ql, g);
+      {
+        const int nb = more ? kb + 32 : kb;
+        load_tr<D>(kt, at(kp, nb, LD), klast - nb, LD, ql, g);
+        asm volatile("" ::: "memory");
+      }
     }
   }
   if (qvalid) store_acc_row<float, D>(dqp, static_cast<int64_t>(qrow) * ld + hoff, dq, scale, g);
@@ -414,15 +425,26 @@ __global__ __launch_bounds__(64, D > 32 ? 1 : 2) void bwd_dkdv_f32_kernel(
 
   const float* lse_h = lse + static_cast<int64_t>(h) * N;
   const float* del_h = delta + static_cast<int64_t>(h) * N;
+  // The rows of the next query block (and their statistics) load under this block's dV/dK
+  // products; the transposed operands of a block load under its own S/dP products.
   const int qlast = wq1 - 1;
-  for (int qb = wq0; qb < wq1; qb += 32) {
+  float qr[HALF], dr[HALF];
+  float lse_r = 0.f, del_r = 0.f;
+  auto load_rows_blk = [&](int qb) {
     const int qrow = min(qb + ql, qlast);
-    float qr[HALF], dr[HALF];
     load_rows<D>(qr, at(qp, qb, LD), qrow - qb, LD, g);
     load_rows<D>(dr, at(dop, qb, HD), qrow - qb, HD, g);
+    lse_r = lse_h[qrow];
+    del_r = del_h[qrow];
+  };
+  if (wq0 < wq1) load_rows_blk(wq0);
+  for (int qb = wq0; qb < wq1; qb += 32) {
+    float qt[16][DB], dt[16][DB];
+    load_tr<D>(qt, at(qp, qb, LD), qlast - qb, LD, ql, g);
+    load_tr<D>(dt, at(dop, qb, HD), qlast - qb, HD, ql, g);
     if (g == 0) {
-      stat[0][ql] = lse_h[qrow] * kLog2e;
-      stat[1][ql] = del_h[qrow];
+      stat[0][ql] = lse_r * kLog2e;
+      stat[1][ql] = del_r;
     }
     floatx16 s = floatx16{}, dp = floatx16{};
 #pragma unroll
@@ -430,9 +452,6 @@ __global__ __launch_bounds__(64, D > 32 ? 1 : 2) void bwd_dkdv_f32_kernel(
       s = __builtin_amdgcn_mfma_f32_32x32x2f32(qr[st], kr[st], s, 0, 0, 0);
       dp = __builtin_amdgcn_mfma_f32_32x32x2f32(dr[st], vr[st], dp, 0, 0, 0);
     }
-    float qt[16][DB], dt[16][DB];
-    load_tr<D>(qt, at(qp, qb, LD), qlast - qb, LD, ql, g);
-    load_tr<D>(dt, at(dop, qb, HD), qlast - qb, HD, ql, g);
     // rows of this block are queries qb + 8(i/4) + 4g + i%4; keep those inside the key's own sequence
     if (!(qb >= mq0 && qb + 32 <= mq1)) {
       const int base = qb + 4 * g;
@@ -453,6 +472,10 @@ __global__ __launch_bounds__(64, D > 32 ? 1 : 2) void bwd_dkdv_f32_kernel(
       }
     }
     __syncthreads();
+    // unconditional (the last block reloads itself), so no branch splits the wait counts; the
+    // empty asm keeps these loads here instead of letting them merge with the next iteration's use
+    load_rows_blk(qb + 32 < wq1 ? qb + 32 : qb);
+    asm volatile("" ::: "memory");
 #pragma unroll
     for (int st = 0; st < 16; ++st)
 #pragma unroll
