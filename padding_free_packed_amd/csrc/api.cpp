@@ -30,9 +30,10 @@ pe_status hip_status(hipError_t e) { return e == hipSuccess ? PE_OK : PE_ERR_HIP
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-// work list of the finest tiling any kernel uses (kAttnWaveRows rows per item)
-size_t items_bytes(int64_t total_tokens) {
-  return round_up(static_cast<size_t>(ceil_div(total_tokens, pe::kAttnWaveRows) + 1) * sizeof(int32_t));
+// A work list of any tiling the kernels use: the sequence-aligned one of kAttnWaveRows rows
+// (N / 32 + B + 1 entries) is the longest.
+size_t items_bytes(int32_t num_seqs, int64_t total_tokens) {
+  return round_up(static_cast<size_t>(total_tokens / pe::kAttnWaveRows + num_seqs + 1) * sizeof(int32_t));
 }
 
 // Checks shared by the attention calls.
@@ -150,12 +151,12 @@ pe_status pe_worklist(const int32_t* cu_seqlens, int32_t num_seqs, int64_t total
 
 size_t pe_attn_workspace_size(int32_t num_seqs, int64_t total_tokens, int32_t num_heads, int32_t head_dim,
                               pe_dtype dtype, int for_backward) {
-  (void)num_seqs;
   (void)head_dim;
   (void)dtype;
-  if (total_tokens < 0 || num_heads < 1) return 0;
-  size_t s = items_bytes(total_tokens);
-  if (for_backward) s += items_bytes(total_tokens) + round_up(static_cast<size_t>(total_tokens) * num_heads * sizeof(float));
+  if (num_seqs < 1 || total_tokens < 0 || num_heads < 1) return 0;
+  size_t s = items_bytes(num_seqs, total_tokens);
+  if (for_backward)
+    s += items_bytes(num_seqs, total_tokens) + round_up(static_cast<size_t>(total_tokens) * num_heads * sizeof(float));
   return s;
 }
 
@@ -180,7 +181,7 @@ pe_status fwd_impl(const void* q, const void* k, const void* v, const int32_t* c
   hipStream_t st = as_stream(stream);
   int32_t* items = static_cast<int32_t*>(workspace);
   if (dtype == PE_FP32 && pe::attn_fwd_f32_wave_supported(head_dim)) {
-    hipError_t e = pe::launch_worklist(cu_seqlens, num_seqs, total_tokens, pe::kAttnWaveRows, items, st);
+    hipError_t e = pe::launch_seq_worklist(cu_seqlens, num_seqs, total_tokens, pe::kAttnWaveRows, items, st);
     if (e != hipSuccess) return PE_ERR_HIP;
     return hip_status(pe::launch_attn_fwd_f32_wave(head_dim, q, k, v, cu_seqlens, items, num_seqs,
                                                    static_cast<int32_t>(total_tokens), num_heads, win, ld,
@@ -308,12 +309,13 @@ pe_status bwd_impl(const void* dout, const void* q, const void* k, const void* v
     return PE_ERR_WORKSPACE;
   hipStream_t st = as_stream(stream);
   int32_t* items = static_cast<int32_t*>(workspace);
-  int32_t* items32 = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + items_bytes(total_tokens));
-  float* delta = reinterpret_cast<float*>(static_cast<char*>(workspace) + 2 * items_bytes(total_tokens));
+  const size_t ib = items_bytes(num_seqs, total_tokens);
+  int32_t* items32 = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + ib);
+  float* delta = reinterpret_cast<float*>(static_cast<char*>(workspace) + 2 * ib);
   hipError_t e = pe::launch_worklist(cu_seqlens, num_seqs, total_tokens, pe::kAttnTileRows, items, st);
   if (e != hipSuccess) return PE_ERR_HIP;
   if (dtype == PE_FP32) {
-    e = pe::launch_worklist(cu_seqlens, num_seqs, total_tokens, pe::kAttnWaveRows, items32, st);
+    e = pe::launch_seq_worklist(cu_seqlens, num_seqs, total_tokens, pe::kAttnWaveRows, items32, st);
     if (e != hipSuccess) return PE_ERR_HIP;
   }
   e = pe::launch_attn_bwd(dtype, head_dim, dout, q, k, v, out, lse, cu_seqlens, items,

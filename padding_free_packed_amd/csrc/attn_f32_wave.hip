@@ -1,7 +1,11 @@
-// fp32 attention kernels with one independent wave per 32 packed rows: the forward,
-// and the dQ and dK/dV passes of the backward.
+// fp32 attention kernels with one independent wave per 32 rows of one sequence: the
+// forward, and the dQ and dK/dV passes of the backward. Tiles start at each
+// sequence's first row (the sequence-aligned work list), so a wave's rows share one
+// key range and the 32x32 products only overhang at a sequence's last tile; there
+// the forward and the dK/dV pass skip the products of whole 8-row groups past the
+// range (in the dQ pass that measured no faster).
 //
-// fp32 forward, one independent wave per (head, 32 packed query rows).
+// fp32 forward, one independent wave per (head, 32 query rows).
 //
 // On fp32 the MFMA operands of both products are one element per lane per
 // step, so no operand ever needs a transposed copy and the waves need not share
@@ -23,6 +27,24 @@ namespace pe {
 namespace {
 
 constexpr int kRows = 32;  // query rows per wave
+
+// Slot t of the sequence-aligned work list (tiles of kRows rows starting at each
+// sequence's first row, sequence b in slots cu[b]/kRows + b onwards): rows
+// [r0, rend) of sequence b = items[t], which spans rows [lo, hi). False for an
+// empty slot (past a sequence's last tile, or past cu[B]).
+struct SeqTile {
+  int r0, rend, lo, hi;
+};
+__device__ __forceinline__ bool seq_tile(const int32_t* __restrict__ cu, const int32_t* __restrict__ items, int t,
+                                         int B, SeqTile& sp) {
+  const int b = items[t];
+  if (b >= B) return false;
+  sp.lo = cu[b];
+  sp.hi = cu[b + 1];
+  sp.r0 = sp.lo + (t - (sp.lo / kRows + b)) * kRows;
+  sp.rend = min(sp.r0 + kRows, sp.hi);
+  return sp.r0 < sp.hi;
+}
 
 template <int D>
 struct F32Ops {
@@ -63,33 +85,25 @@ __global__ __launch_bounds__(64, 2) void attn_fwd_f32_kernel(
     const int32_t* __restrict__ cu, const int32_t* __restrict__ items, int32_t B, int32_t N, int32_t H, int32_t T,
     int32_t win, int64_t ld, float c, float* __restrict__ op, float* __restrict__ lse) {
   using O = F32Ops<D>;
-  __shared__ int32_t cul[kRows + 2];
   const int lin = xcd_remap(blockIdx.x, gridDim.x);
   const int h = lin / T, t = lin - h * T;
   const int lane = threadIdx.x, ql = lane & 31, g = lane >> 5;
 
-  // sequences of rows r0 .. rend-1
-  const int r0 = t * kRows, rcap = min(r0 + kRows, N);
-  const int blo = items[t], nxt = items[t + 1];
-  const int bhi = nxt >= B ? B - 1 : (cu[nxt] == rcap ? nxt - 1 : nxt);
-  const int ncu = min(bhi - blo + 2, kRows + 2);
-  if (lane < ncu) cul[lane] = cu[blo + lane];
-  __syncthreads();
-  // rows past cu[B] (a row count given as a capacity) belong to no sequence
-  const int rend = min(rcap, cul[ncu - 1]);
-  if (rend <= r0) return;
-
+  SeqTile sp;
+  if (!seq_tile(cu, items, t, B, sp)) return;
+  const int r0 = sp.r0;
   const int qrow = r0 + ql;
-  const bool qvalid = qrow < rend;
+  const bool qvalid = qrow < sp.rend;
   int qk0 = 0, qk1 = 0;
   if (qvalid) {
-    own_range(cul, ncu, qrow, qk0, qk1);
+    qk0 = sp.lo;
+    qk1 = sp.hi;
     band_limit(qrow, win, qk0, qk1);
   }
-  const int wk0 = wave_min_i(qvalid ? qk0 : INT_MAX);
-  const int wk1 = wave_max_i(qvalid ? qk1 : INT_MIN);
-  const int mk0 = wave_max_i(qvalid ? qk0 : INT_MIN);
-  const int mk1 = wave_min_i(qvalid ? qk1 : INT_MAX);
+  const int wk0 = __builtin_amdgcn_readfirstlane(wave_min_i(qvalid ? qk0 : INT_MAX));
+  const int wk1 = __builtin_amdgcn_readfirstlane(wave_max_i(qvalid ? qk1 : INT_MIN));
+  const int mk0 = __builtin_amdgcn_readfirstlane(wave_max_i(qvalid ? qk0 : INT_MIN));
+  const int mk1 = __builtin_amdgcn_readfirstlane(wave_min_i(qvalid ? qk1 : INT_MAX));
 
   float qf[O::HALF];
   {
@@ -138,10 +152,17 @@ __global__ __launch_bounds__(64, 2) void attn_fwd_f32_kernel(
       s[i] = p;
       l += p;
     }
+    // keys 8j .. 8j+7 of the block (steps 4j .. 4j+3) at or past wk1 have P = 0 for every
+    // query of the wave: their products would add nothing, so they are skipped
 #pragma unroll
-    for (int st = 0; st < 16; ++st)
+    for (int j = 0; j < 4; ++j) {
+      if (j > 0 && kb + 8 * j >= wk1) break;
 #pragma unroll
-      for (int db = 0; db < O::DB; ++db) o[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(ops.v[st][db], s[st], o[db], 0, 0, 0);
+      for (int e = 0; e < 4; ++e)
+#pragma unroll
+        for (int db = 0; db < O::DB; ++db)
+          o[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(ops.v[4 * j + e][db], s[4 * j + e], o[db], 0, 0, 0);
+    }
   };
 
   // keys [wk0, wk1) in steps of 32; operands of the next step load while this one computes
@@ -175,7 +196,7 @@ template <int D>
 hipError_t dispatch(const void* q, const void* k, const void* v, const int32_t* cu, const int32_t* items,
                     int32_t B, int32_t N, int32_t H, int32_t win, int64_t ld, float scale, void* out, float* lse,
                     hipStream_t stream) {
-  const int T = (N + kRows - 1) / kRows;
+  const int T = N / kRows + B;  // slots of the sequence-aligned work list
   const int64_t blocks = static_cast<int64_t>(T) * H;
   if (blocks == 0) return hipSuccess;
   const float c = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
@@ -247,32 +268,25 @@ __global__ __launch_bounds__(64, 2) void bwd_dq_f32_kernel(
     const int32_t* __restrict__ cu, const int32_t* __restrict__ items, int32_t B, int32_t N, int32_t H, int32_t T,
     int32_t win, int64_t ld, float c, float scale, float* __restrict__ dqp) {
   constexpr int HALF = D / 2, DB = D / 32;
-  __shared__ int32_t cul[kRows + 2];
   const int lin = xcd_remap(blockIdx.x, gridDim.x);
   const int h = lin / T, t = lin - h * T;
   const int lane = threadIdx.x, ql = lane & 31, g = lane >> 5;
 
-  const int r0 = t * kRows, rcap = min(r0 + kRows, N);
-  const int blo = items[t], nxt = items[t + 1];
-  const int bhi = nxt >= B ? B - 1 : (cu[nxt] == rcap ? nxt - 1 : nxt);
-  const int ncu = min(bhi - blo + 2, kRows + 2);
-  if (lane < ncu) cul[lane] = cu[blo + lane];
-  __syncthreads();
-  // rows past cu[B] (a row count given as a capacity) belong to no sequence
-  const int rend = min(rcap, cul[ncu - 1]);
-  if (rend <= r0) return;
-
+  SeqTile sp;
+  if (!seq_tile(cu, items, t, B, sp)) return;
+  const int r0 = sp.r0;
   const int qrow = r0 + ql;
-  const bool qvalid = qrow < rend;
+  const bool qvalid = qrow < sp.rend;
   int qk0 = 0, qk1 = 0;
   if (qvalid) {
-    own_range(cul, ncu, qrow, qk0, qk1);
+    qk0 = sp.lo;
+    qk1 = sp.hi;
     band_limit(qrow, win, qk0, qk1);
   }
-  const int wk0 = wave_min_i(qvalid ? qk0 : INT_MAX);
-  const int wk1 = wave_max_i(qvalid ? qk1 : INT_MIN);
-  const int mk0 = wave_max_i(qvalid ? qk0 : INT_MIN);
-  const int mk1 = wave_min_i(qvalid ? qk1 : INT_MAX);
+  const int wk0 = __builtin_amdgcn_readfirstlane(wave_min_i(qvalid ? qk0 : INT_MAX));
+  const int wk1 = __builtin_amdgcn_readfirstlane(wave_max_i(qvalid ? qk1 : INT_MIN));
+  const int mk0 = __builtin_amdgcn_readfirstlane(wave_max_i(qvalid ? qk0 : INT_MIN));
+  const int mk1 = __builtin_amdgcn_readfirstlane(wave_min_i(qvalid ? qk1 : INT_MAX));
 
   float qf[HALF], df[HALF];
   const int qsafe = qvalid ? qrow : r0;
@@ -342,7 +356,7 @@ hipError_t launch_bwd_dq_f32_wave(int D, const void* dout, const void* q, const 
                                   const float* lse, const float* delta, const int32_t* cu, const int32_t* items32,
                                   int32_t B, int32_t N, int32_t H, int32_t win, int64_t ld, float scale, void* dq,
                                   hipStream_t stream) {
-  const int T = (N + kRows - 1) / kRows;
+  const int T = N / kRows + B;  // slots of the sequence-aligned work list
   const int64_t blocks = static_cast<int64_t>(T) * H;
   if (blocks == 0) return hipSuccess;
   const float c = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
@@ -382,33 +396,26 @@ __global__ __launch_bounds__(64, D > 32 ? 1 : 2) void bwd_dkdv_f32_kernel(
     const int32_t* __restrict__ cu, const int32_t* __restrict__ items, int32_t B, int32_t N, int32_t H, int32_t T,
     int32_t win, int64_t ld, float c, float scale, float* __restrict__ dkp, float* __restrict__ dvp) {
   constexpr int HALF = D / 2, DB = D / 32;
-  __shared__ int32_t cul[kRows + 2];
   __shared__ __align__(16) float stat[2][kRows];
   const int lin = xcd_remap(blockIdx.x, gridDim.x);
   const int h = lin / T, t = lin - h * T;
   const int lane = threadIdx.x, ql = lane & 31, g = lane >> 5;
 
-  const int r0 = t * kRows, rcap = min(r0 + kRows, N);
-  const int blo = items[t], nxt = items[t + 1];
-  const int bhi = nxt >= B ? B - 1 : (cu[nxt] == rcap ? nxt - 1 : nxt);
-  const int ncu = min(bhi - blo + 2, kRows + 2);
-  if (lane < ncu) cul[lane] = cu[blo + lane];
-  __syncthreads();
-  // rows past cu[B] (a row count given as a capacity) belong to no sequence
-  const int rend = min(rcap, cul[ncu - 1]);
-  if (rend <= r0) return;
-
+  SeqTile sp;
+  if (!seq_tile(cu, items, t, B, sp)) return;
+  const int r0 = sp.r0;
   const int krow = r0 + ql;
-  const bool kvalid = krow < rend;
+  const bool kvalid = krow < sp.rend;
   int kq0 = 0, kq1 = 0;
   if (kvalid) {  // the queries that attend to this key
-    own_range(cul, ncu, krow, kq0, kq1);
+    kq0 = sp.lo;
+    kq1 = sp.hi;
     band_limit(krow, win, kq0, kq1);
   }
-  const int wq0 = wave_min_i(kvalid ? kq0 : INT_MAX);
-  const int wq1 = wave_max_i(kvalid ? kq1 : INT_MIN);
-  const int mq0 = wave_max_i(kvalid ? kq0 : INT_MIN);
-  const int mq1 = wave_min_i(kvalid ? kq1 : INT_MAX);
+  const int wq0 = __builtin_amdgcn_readfirstlane(wave_min_i(kvalid ? kq0 : INT_MAX));
+  const int wq1 = __builtin_amdgcn_readfirstlane(wave_max_i(kvalid ? kq1 : INT_MIN));
+  const int mq0 = __builtin_amdgcn_readfirstlane(wave_max_i(kvalid ? kq0 : INT_MIN));
+  const int mq1 = __builtin_amdgcn_readfirstlane(wave_min_i(kvalid ? kq1 : INT_MAX));
 
   float kr[HALF], vr[HALF];
   const int ksafe = kvalid ? krow : r0;
@@ -476,13 +483,18 @@ __global__ __launch_bounds__(64, D > 32 ? 1 : 2) void bwd_dkdv_f32_kernel(
     // empty asm keeps these loads here instead of letting them merge with the next iteration's use
     load_rows_blk(qb + 32 < wq1 ? qb + 32 : qb);
     asm volatile("" ::: "memory");
+    // queries at or past wq1 have P = dS = 0 for every key of the wave: skip their steps
 #pragma unroll
-    for (int st = 0; st < 16; ++st)
+    for (int j = 0; j < 4; ++j) {
+      if (j > 0 && qb + 8 * j >= wq1) break;
 #pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        dv[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(dt[st][db], s[st], dv[db], 0, 0, 0);
-        dk[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(qt[st][db], dp[st], dk[db], 0, 0, 0);
-      }
+      for (int e = 0; e < 4; ++e)
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          dv[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(dt[4 * j + e][db], s[4 * j + e], dv[db], 0, 0, 0);
+          dk[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(qt[4 * j + e][db], dp[4 * j + e], dk[db], 0, 0, 0);
+        }
+    }
   }
   if (kvalid) {
     const int64_t off = static_cast<int64_t>(krow) * ld + hoff;
@@ -497,7 +509,7 @@ hipError_t launch_bwd_dkdv_f32_wave(int D, const void* dout, const void* q, cons
                                     const float* lse, const float* delta, const int32_t* cu, const int32_t* items32,
                                     int32_t B, int32_t N, int32_t H, int32_t win, int64_t ld, float scale, void* dk,
                                     void* dv, hipStream_t stream) {
-  const int T = (N + kRows - 1) / kRows;
+  const int T = N / kRows + B;  // slots of the sequence-aligned work list
   const int64_t blocks = static_cast<int64_t>(T) * H;
   if (blocks == 0) return hipSuccess;
   const float c = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);

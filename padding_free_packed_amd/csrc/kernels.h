@@ -26,6 +26,10 @@ hipError_t launch_scan(const int32_t* lengths, int32_t B, int32_t S, int64_t cap
 // N may exceed cu[B] (a capacity): tiles from ceil(cu[B] / R) on get item B
 hipError_t launch_worklist(const int32_t* cu, int32_t B, int64_t N, int32_t R, int32_t* items,
                            hipStream_t stream);
+// Tiles of R rows aligned to each sequence's first row: N / R + B slots, items[N / R + B] = B
+// (see seq_worklist_kernel for the slot layout)
+hipError_t launch_seq_worklist(const int32_t* cu, int32_t B, int64_t N, int32_t R, int32_t* items,
+                               hipStream_t stream);
 int32_t pack_tile_rows(int64_t rowbytes);
 hipError_t launch_pack_rows(const void* grid, void* packed, int64_t* flat_index, const int32_t* cu,
                             const int32_t* items, int32_t B, int32_t S, int64_t rowbytes, int64_t N,
@@ -51,14 +55,15 @@ hipError_t launch_attn_fwd_bf16(bool f16, int D, const void* q, const void* k, c
                                 const int32_t* items, int32_t B, int32_t N, int32_t H, int32_t win, int64_t ld,
                                 float scale, void* out, float* lse, hipStream_t stream);
 
-// fp32 forward, one independent wave per 32 query rows (head dims 32, 64);
-// items32 is the work list with tile height kAttnWaveRows.
+// fp32 forward, one independent wave per 32 query rows of one sequence (head dims 32, 64);
+// items32 is the sequence-aligned work list (launch_seq_worklist) with tile height kAttnWaveRows.
 bool attn_fwd_f32_wave_supported(int D);
 hipError_t launch_attn_fwd_f32_wave(int D, const void* q, const void* k, const void* v, const int32_t* cu,
                                     const int32_t* items32, int32_t B, int32_t N, int32_t H, int32_t win, int64_t ld,
                                     float scale, void* out, float* lse, hipStream_t stream);
 
-// fp32 dK/dV and dQ, one independent wave per 32 key (query) rows (head dims 32, 64)
+// fp32 dK/dV and dQ, one independent wave per 32 key (query) rows of one sequence (head dims 32, 64;
+// items32 as for the fp32 forward)
 hipError_t launch_bwd_dkdv_f32_wave(int D, const void* dout, const void* q, const void* k, const void* v,
                                     const float* lse, const float* delta, const int32_t* cu, const int32_t* items32,
                                     int32_t B, int32_t N, int32_t H, int32_t win, int64_t ld, float scale, void* dk,
@@ -82,7 +87,8 @@ hipError_t launch_attn_bwd_first(int dt, int D, const void* dout_first, const vo
                                  void* dq_first, void* dk, void* dv, hipStream_t stream);
 
 // Backward: D = rowsum(dO * O) per (head, row), then dK/dV over key tiles, then dQ over query tiles.
-// items: work list with tile height kAttnTileRows; items32: with kAttnWaveRows (or NULL).
+// items: work list with tile height kAttnTileRows; items32: the sequence-aligned list with
+// kAttnWaveRows (or NULL).
 // win: local attention radius (keys with |i - j| <= win), or -1 for global attention;
 // ld: elements between consecutive rows of Q, K, V (and of dQ, dK, dV): num_heads * D for
 // separate [N, H, D] tensors, 3 * num_heads * D for a fused [N, 3, H, D] buffer. O, dO,

@@ -99,6 +99,26 @@ __global__ void worklist_kernel(const int32_t* __restrict__ cu, int32_t B, int64
   for (; t < tend; ++t) items[t] = static_cast<int32_t>(i);
 }
 
+// ---------------------------------------------------------------- sequence-aligned work list
+// Tiles of R rows that start at each sequence's first row, so no tile holds two
+// sequences. Sequence b owns the slots [s_b, s_{b+1}) with s_b = cu[b]/R + b:
+// its ceil(L_b/R) tiles fit there because floor(cu/R) + ceil(L/R) <= floor((cu + L)/R) + 1,
+// so the slots need no prefix sum over tile counts, at the price of at most one
+// empty slot per sequence. items[s] = b for every slot of sequence b (slot s holds
+// tile s - s_b, empty when that tile starts at or past cu[b+1]); slots before s_0
+// and from s_B to T = N/R + B are marked B; items[T] = B. One thread per slot or
+// sequence, whichever is more.
+__global__ void seq_worklist_kernel(const int32_t* __restrict__ cu, int32_t B, int64_t N, int32_t R,
+                                    int32_t* __restrict__ items) {
+  const int64_t T = N / R + B;
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i == 0) items[T] = B;
+  if (i < T && (i < cu[0] / R || i >= static_cast<int64_t>(cu[B]) / R + B)) items[i] = B;
+  if (i >= B) return;
+  const int64_t s0 = cu[i] / R + i, s1 = cu[i + 1] / R + i + 1;
+  for (int64_t s = s0; s < s1; ++s) items[s] = static_cast<int32_t>(i);
+}
+
 // ---------------------------------------------------------------- segment copy
 template <typename U>
 __device__ __forceinline__ void copy_units(const U* __restrict__ src, U* __restrict__ dst, int64_t n) {
@@ -191,6 +211,17 @@ hipError_t launch_worklist(const int32_t* cu, int32_t B, int64_t N, int32_t R, i
   const int blocks = static_cast<int>((n + threads - 1) / threads);
   hipEvent_t ev = timing_start(stream);
   hipLaunchKernelGGL(worklist_kernel, dim3(blocks), dim3(threads), 0, stream, cu, B, N, R, items);
+  timing_stop("worklist", ev, stream);
+  return hipGetLastError();
+}
+
+hipError_t launch_seq_worklist(const int32_t* cu, int32_t B, int64_t N, int32_t R, int32_t* items,
+                               hipStream_t stream) {
+  const int threads = 256;
+  const int64_t T = N / R + B;
+  const int blocks = static_cast<int>((T + threads - 1) / threads);  // T >= B
+  hipEvent_t ev = timing_start(stream);
+  hipLaunchKernelGGL(seq_worklist_kernel, dim3(blocks), dim3(threads), 0, stream, cu, B, N, R, items);
   timing_stop("worklist", ev, stream);
   return hipGetLastError();
 }
