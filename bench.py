@@ -116,11 +116,12 @@ def load_traffic(kernel, workload):
 
 def graph_bench(args):
     """The short_batch workload: one step is one replay of the captured bucket forward
-    (pe_pack_async of the fused Q/K/V grid, pe_varlen_attn_fwd_qkv over the bucket's
-    capacity, pe_unpack) for a batch of 64 short sequences in a (64, 48) bucket. The same
-    forward by the eager calls (pe_pack with its host read, then the same two calls) is
-    timed beside it; per-kernel times come from the eager pass (launches inside a graph
-    carry no events), and the graph replays the same kernels."""
+    (the work of pe_pack_async of the fused Q/K/V grid, pe_varlen_attn_fwd_qkv over the
+    bucket's capacity and pe_unpack, with the scan and work lists fused into one plan
+    kernel) for a batch of 64 short sequences in a (64, 48) bucket. The same forward by
+    the eager calls (pe_pack with its host read, then the same two calls) is timed beside
+    it; per-kernel times come from the eager pass (launches inside a graph carry no
+    events), and the graph replays the same copy and attention kernels."""
     import numpy as np
     import torch
 
@@ -206,7 +207,7 @@ def graph_bench(args):
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": "short_batch", "num_seqs": B, "max_seq_len": S, "total_tokens": N, "num_heads": H,
                    "head_dim": d, "grid": [B, S, 3, H, d], "window": None,
-                   "step": "graph replay: pack_async(fused qkv grid)+fwd_qkv(capacity rows)+unpack"},
+                   "step": "graph replay: plan(scan+work lists)+pack(fused qkv grid)+fwd_qkv(capacity rows)+unpack"},
         "eager_ms_per_step": ms_eager,
         "kernel_ms_sum": sum(v_["ms_per_step"] for v_ in breakdown.values()),
         "roofline": roof, "breakdown": breakdown, "wall_s_timed_region": wall,

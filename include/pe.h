@@ -343,10 +343,13 @@ pe_status pe_varlen_attn_bwd_qkv(const void* dout, const void* qkv, const void* 
  * replay; packed graphs take explicit batch and sequence bounds; graphs serve
  * only gradient-free calls.
  *
- * One replay runs, on the buffers given here:
+ * One replay computes, on the buffers given here, what these calls would:
  *   pe_pack_async(lengths, qkv_grid -> cu_seqlens, qkv_packed; capacity C = num_seqs * max_seq_len)
  *   pe_varlen_attn_fwd_qkv(qkv_packed, total_tokens = C, window -> out_packed, lse)
  *   pe_unpack(out_packed -> out_grid)
+ * bit for bit. For buckets of up to ~16k work-list entries (about C / pack rows per
+ * tile + C / 128) the scan and both work lists run as one single-workgroup kernel,
+ * so a replay is four dependent kernels instead of six.
  * Buffers (device, caller-owned, fixed for the life of the graph)
  *   lengths     int32 [num_seqs]; the caller writes the batch before each replay.
  *               A batch of fewer sequences fills the unused slots with length 1:

@@ -506,6 +506,22 @@ struct pe_graph_s {
   hipGraphExec_t exec;
 };
 
+namespace {
+
+// Work-list entries the single-workgroup plan kernel writes for a bucket; above
+// kPlanMaxEntries the separate multi-block kernels are faster than one workgroup
+// (measured per replay: 2-3 us gained up to ~8k entries, even at ~16k, 4.5 us lost at ~33k).
+constexpr int64_t kPlanMaxEntries = 1 << 14;
+int64_t plan_entries(int32_t num_seqs, int64_t cap, int64_t rowbytes, pe_dtype dtype, int32_t head_dim) {
+  const int64_t np = std::max(ceil_div(cap, pe::pack_tile_rows(rowbytes)), static_cast<int64_t>(num_seqs));
+  const bool wave = dtype == PE_FP32 && pe::attn_fwd_f32_wave_supported(head_dim);
+  const int64_t na = wave ? cap / pe::kAttnWaveRows + num_seqs
+                          : std::max(ceil_div(cap, pe::kAttnTileRows), static_cast<int64_t>(num_seqs));
+  return np + na;
+}
+
+}  // namespace
+
 size_t pe_forward_graph_workspace_size(int32_t num_seqs, int32_t max_seq_len, int32_t num_heads, int32_t head_dim,
                                        pe_dtype dtype) {
   if (num_seqs < 1 || max_seq_len < 1 || num_heads < 1 || head_dim < 1) return 0;
@@ -545,12 +561,42 @@ pe_status pe_forward_graph_create(const int32_t* lengths, int32_t num_seqs, int3
     (void)hipStreamDestroy(cs);
     return PE_ERR_HIP;
   }
-  pe_status s = pe_pack_async(lengths, num_seqs, max_seq_len, qkv_grid, 3 * hd, dtype, cu_seqlens, nullptr,
-                              qkv_packed, cap, status, workspace, pack_ws, cs);
-  if (s == PE_OK)
-    s = pe_varlen_attn_fwd_qkv(qkv_packed, cu_seqlens, num_seqs, cap, max_seq_len, num_heads, head_dim, dtype,
-                               softmax_scale, window, out_packed, lse, attn_ws, attn_wsb, cs);
-  if (s == PE_OK) s = pe_unpack(out_packed, cu_seqlens, num_seqs, max_seq_len, cap, hd, dtype, out_grid, cs);
+  pe_status s = PE_OK;
+  if (plan_entries(num_seqs, cap, 3 * hd * elem_bytes(dtype), dtype, head_dim) <= kPlanMaxEntries) {
+    // Four kernels: plan (scan + both work lists), pack, attention, unpack. The work lists sit
+    // where pe_pack_async and the attention calls put them in the same workspace.
+    const bool wave = dtype == PE_FP32 && pe::attn_fwd_f32_wave_supported(head_dim);
+    const int64_t rowbytes = 3 * hd * elem_bytes(dtype);
+    const int32_t rp = pe::pack_tile_rows(rowbytes);
+    int32_t* items_p = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + kAlign);
+    int32_t* items_a = static_cast<int32_t*>(attn_ws);
+    const char* base = static_cast<const char*>(qkv_packed);
+    const size_t step = static_cast<size_t>(hd) * elem_bytes(dtype);
+    const int32_t win = window < 0 ? -1 : effective_window(window, max_seq_len);
+    const int32_t n = static_cast<int32_t>(cap);
+    hipError_t e = pe::launch_plan(lengths, num_seqs, max_seq_len, cap, cu_seqlens, status, rp, items_p,
+                                   wave ? pe::kAttnWaveRows : pe::kAttnTileRows, wave, items_a, cs);
+    if (e == hipSuccess)
+      e = pe::launch_pack_rows(qkv_grid, qkv_packed, nullptr, cu_seqlens, items_p, num_seqs, max_seq_len, rowbytes,
+                               cap, rp, cs);
+    if (e == hipSuccess)
+      e = wave ? pe::launch_attn_fwd_f32_wave(head_dim, base, base + step, base + 2 * step, cu_seqlens, items_a,
+                                              num_seqs, n, num_heads, win, 3 * hd, softmax_scale, out_packed, lse,
+                                              cs)
+               : pe::launch_attn_fwd(dtype, head_dim, base, base + step, base + 2 * step, cu_seqlens, items_a,
+                                     num_seqs, n, num_heads, max_seq_len, win, 3 * hd, softmax_scale, out_packed,
+                                     lse, cs);
+    if (e == hipSuccess)
+      e = pe::launch_unpack_rows(out_packed, out_grid, cu_seqlens, num_seqs, max_seq_len, hd * elem_bytes(dtype), cs);
+    s = hip_status(e);
+  } else {
+    s = pe_pack_async(lengths, num_seqs, max_seq_len, qkv_grid, 3 * hd, dtype, cu_seqlens, nullptr, qkv_packed, cap,
+                      status, workspace, pack_ws, cs);
+    if (s == PE_OK)
+      s = pe_varlen_attn_fwd_qkv(qkv_packed, cu_seqlens, num_seqs, cap, max_seq_len, num_heads, head_dim, dtype,
+                                 softmax_scale, window, out_packed, lse, attn_ws, attn_wsb, cs);
+    if (s == PE_OK) s = pe_unpack(out_packed, cu_seqlens, num_seqs, max_seq_len, cap, hd, dtype, out_grid, cs);
+  }
   hipGraph_t g = nullptr;
   const hipError_t e = hipStreamEndCapture(cs, &g);
   if (s == PE_OK && e != hipSuccess) s = PE_ERR_HIP;

@@ -30,6 +30,10 @@ hipError_t launch_worklist(const int32_t* cu, int32_t B, int64_t N, int32_t R, i
 // (see seq_worklist_kernel for the slot layout)
 hipError_t launch_seq_worklist(const int32_t* cu, int32_t B, int64_t N, int32_t R, int32_t* items,
                                hipStream_t stream);
+// One workgroup: launch_scan (with cap = N) followed by launch_worklist(cu, B, N, Rp, items_p) and
+// the attention list of tile height Ra (launch_seq_worklist if aligned, else launch_worklist).
+hipError_t launch_plan(const int32_t* lengths, int32_t B, int32_t S, int64_t N, int32_t* cu, int64_t* result,
+                       int32_t Rp, int32_t* items_p, int32_t Ra, bool aligned, int32_t* items_a, hipStream_t stream);
 int32_t pack_tile_rows(int64_t rowbytes);
 hipError_t launch_pack_rows(const void* grid, void* packed, int64_t* flat_index, const int32_t* cu,
                             const int32_t* items, int32_t B, int32_t S, int64_t rowbytes, int64_t N,

@@ -22,9 +22,9 @@ namespace pe {
 constexpr int kScanThreads = 1024;
 constexpr int kScanPer = 8;
 
-__global__ __launch_bounds__(kScanThreads) void scan_lengths_kernel(
-    const int32_t* __restrict__ lengths, int32_t B, int32_t S, int64_t cap, int32_t* __restrict__ cu,
-    int64_t* __restrict__ result) {
+__device__ __forceinline__ void scan_lengths_block(const int32_t* __restrict__ lengths, int32_t B, int32_t S,
+                                                   int64_t cap, int32_t* __restrict__ cu,
+                                                   int64_t* __restrict__ result) {
   __shared__ int64_t wsum[kScanThreads / 64];
   __shared__ int bad_any;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
@@ -81,22 +81,33 @@ __global__ __launch_bounds__(kScanThreads) void scan_lengths_kernel(
     for (int64_t i = tid; i <= B; i += kScanThreads) cu[i] = 0;
 }
 
+__global__ __launch_bounds__(kScanThreads) void scan_lengths_kernel(
+    const int32_t* __restrict__ lengths, int32_t B, int32_t S, int64_t cap, int32_t* __restrict__ cu,
+    int64_t* __restrict__ result) {
+  scan_lengths_block(lengths, B, S, cap, cu, result);
+}
+
 // ---------------------------------------------------------------- work list
 // items[t] = b with cu[b] <= t*R < cu[b+1]; items[T] = B, T = ceil(N / R).
 // Thread b writes the entries of the tiles that start inside sequence b. N may
 // be a capacity above cu[B]: thread i then also marks tile i, if it starts at
 // or after cu[B], with B (a tile of no sequence).
-__global__ void worklist_kernel(const int32_t* __restrict__ cu, int32_t B, int64_t N, int32_t R,
-                                int32_t* __restrict__ items) {
+// cu_B = cu[B], read once by the caller.
+__device__ __forceinline__ void worklist_entry(const int32_t* __restrict__ cu, int64_t cu_B, int32_t B, int64_t N,
+                                               int32_t R, int32_t* __restrict__ items, int64_t i) {
   const int64_t T = (N + R - 1) / R;
-  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   if (i == 0) items[T] = B;
-  if (i < T && i >= (static_cast<int64_t>(cu[B]) + R - 1) / R) items[i] = B;
+  if (i < T && i >= (cu_B + R - 1) / R) items[i] = B;
   if (i >= B) return;
   const int64_t c0 = cu[i], c1 = cu[i + 1];
   int64_t t = (c0 + R - 1) / R;
   const int64_t tend = min((c1 + R - 1) / R, T);
   for (; t < tend; ++t) items[t] = static_cast<int32_t>(i);
+}
+
+__global__ void worklist_kernel(const int32_t* __restrict__ cu, int32_t B, int64_t N, int32_t R,
+                                int32_t* __restrict__ items) {
+  worklist_entry(cu, cu[B], B, N, R, items, static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x);
 }
 
 // ---------------------------------------------------------------- sequence-aligned work list
@@ -108,15 +119,47 @@ __global__ void worklist_kernel(const int32_t* __restrict__ cu, int32_t B, int64
 // tile s - s_b, empty when that tile starts at or past cu[b+1]); slots before s_0
 // and from s_B to T = N/R + B are marked B; items[T] = B. One thread per slot or
 // sequence, whichever is more.
-__global__ void seq_worklist_kernel(const int32_t* __restrict__ cu, int32_t B, int64_t N, int32_t R,
-                                    int32_t* __restrict__ items) {
+// cu_0 = cu[0] and cu_B = cu[B], read once by the caller.
+__device__ __forceinline__ void seq_worklist_entry(const int32_t* __restrict__ cu, int64_t cu_0, int64_t cu_B,
+                                                   int32_t B, int64_t N, int32_t R, int32_t* __restrict__ items,
+                                                   int64_t i) {
   const int64_t T = N / R + B;
-  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   if (i == 0) items[T] = B;
-  if (i < T && (i < cu[0] / R || i >= static_cast<int64_t>(cu[B]) / R + B)) items[i] = B;
+  if (i < T && (i < cu_0 / R || i >= cu_B / R + B)) items[i] = B;
   if (i >= B) return;
   const int64_t s0 = cu[i] / R + i, s1 = cu[i + 1] / R + i + 1;
   for (int64_t s = s0; s < s1; ++s) items[s] = static_cast<int32_t>(i);
+}
+
+__global__ void seq_worklist_kernel(const int32_t* __restrict__ cu, int32_t B, int64_t N, int32_t R,
+                                    int32_t* __restrict__ items) {
+  seq_worklist_entry(cu, cu[0], cu[B], B, N, R, items,
+                     static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x);
+}
+
+// ---------------------------------------------------------------- plan (scan + both work lists)
+// One workgroup: the scan above, then from the offsets it has just written the
+// work list of the packing copy (tile height Rp over N rows) and that of the
+// attention (tile height Ra; sequence-aligned when `aligned`). The three kernels
+// of the pack -> attention path in one launch, for short batches whose captured
+// replay is a chain of dependent launches.
+__global__ __launch_bounds__(kScanThreads) void plan_kernel(
+    const int32_t* __restrict__ lengths, int32_t B, int32_t S, int64_t N, int32_t* __restrict__ cu,
+    int64_t* __restrict__ result, int32_t Rp, int32_t* __restrict__ items_p, int32_t Ra, int aligned,
+    int32_t* __restrict__ items_a) {
+  scan_lengths_block(lengths, B, S, N, cu, result);
+  __syncthreads();  // the offsets this workgroup wrote are visible to all of it
+  const int64_t cu_0 = cu[0], cu_B = cu[B];
+  const int64_t np = max((N + Rp - 1) / Rp, static_cast<int64_t>(B));
+  for (int64_t i = threadIdx.x; i < np; i += kScanThreads) worklist_entry(cu, cu_B, B, N, Rp, items_p, i);
+  if (aligned) {
+    const int64_t na = N / Ra + B;
+    for (int64_t i = threadIdx.x; i < na; i += kScanThreads)
+      seq_worklist_entry(cu, cu_0, cu_B, B, N, Ra, items_a, i);
+  } else {
+    const int64_t na = max((N + Ra - 1) / Ra, static_cast<int64_t>(B));
+    for (int64_t i = threadIdx.x; i < na; i += kScanThreads) worklist_entry(cu, cu_B, B, N, Ra, items_a, i);
+  }
 }
 
 // ---------------------------------------------------------------- segment copy
@@ -212,6 +255,15 @@ hipError_t launch_worklist(const int32_t* cu, int32_t B, int64_t N, int32_t R, i
   hipEvent_t ev = timing_start(stream);
   hipLaunchKernelGGL(worklist_kernel, dim3(blocks), dim3(threads), 0, stream, cu, B, N, R, items);
   timing_stop("worklist", ev, stream);
+  return hipGetLastError();
+}
+
+hipError_t launch_plan(const int32_t* lengths, int32_t B, int32_t S, int64_t N, int32_t* cu, int64_t* result,
+                       int32_t Rp, int32_t* items_p, int32_t Ra, bool aligned, int32_t* items_a, hipStream_t stream) {
+  hipEvent_t ev = timing_start(stream);
+  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kScanThreads), 0, stream, lengths, B, S, N, cu, result, Rp, items_p,
+                     Ra, aligned ? 1 : 0, items_a);
+  timing_stop("plan", ev, stream);
   return hipGetLastError();
 }
 
