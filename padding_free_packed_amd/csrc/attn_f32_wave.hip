@@ -5,17 +5,17 @@
 // the forward and the dK/dV pass skip the products of whole 8-row groups past the
 // range (in the dQ pass that measured no faster).
 //
-// fp32 forward, one independent wave per (head, 32 query rows).
+// On fp32 the MFMA operands of every product are one element per lane per step, so
+// the transposed operands load straight from global memory (L2-resident: neighbouring
+// waves read the same sequences) and the waves share no LDS tile and no barrier: a
+// wave whose rows cover short sequences never waits for one covering long ones. All
+// block loads go through buffer resources bounded at the walk's end (rows past it
+// read 0), with wave-uniform row offsets, so no lane computes addresses per load.
+// The forward loads each step's operands one step ahead; the dQ and dK/dV passes load
+// at use and rely on their second wave per SIMD to cover the latency (measured faster
+// than prefetching with the registers that takes).
 //
-// On fp32 the MFMA operands of both products are one element per lane per
-// step, so no operand ever needs a transposed copy and the waves need not share
-// an LDS tile. Each wave therefore walks only the key span of its own 32 rows,
-// in 32-key steps starting exactly at the first key it needs, with K and V
-// operands loaded straight from global memory (L2-resident: neighbouring waves
-// read the same sequences) one step ahead of their use. There are no LDS tiles
-// and no barriers, so a wave whose rows cover short sequences never waits for
-// one covering long ones.
-//
+// fp32 forward, one wave per (head, 32 query rows), over its key span in 32-key steps:
 //   S^T (32 keys x 32 queries) += K Q^T   v_mfma_f32_32x32x2f32, 32 steps of 2 over d=64
 //   O^T (d x 32 queries)       += V^T P^T 16 steps per 32-row d block
 #include <climits>
@@ -46,6 +46,23 @@ __device__ __forceinline__ bool seq_tile(const int32_t* __restrict__ cu, const i
   return sp.r0 < sp.hi;
 }
 
+// Buffer resource over `rows` rows of `stride` floats from `base`: a load at a byte
+// offset at or past rows * stride * 4 returns 0 and touches no memory, so rows past a
+// block's end need neither clamping nor per-lane address arithmetic. rows <= 32 here,
+// so the byte count fits the 32-bit record count for any row stride below 2^24.
+constexpr int kBufferFlags = 0x00020000;  // dword 3 of a raw buffer resource on CDNA
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const float* base, int rows, uint32_t stride) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(base), 0,
+                                           static_cast<int>(static_cast<uint32_t>(rows) * stride * 4u), kBufferFlags);
+}
+__device__ __forceinline__ float buf_f32(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, static_cast<int>(voff), static_cast<int>(soff), 0));
+}
+__device__ __forceinline__ float4 buf_f32x4(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(r, static_cast<int>(voff),
+                                                                          static_cast<int>(soff), 0));
+}
+
 template <int D>
 struct F32Ops {
   static constexpr int HALF = D / 2;  // head-dim elements per lane half (MFMA steps of S)
@@ -54,29 +71,28 @@ struct F32Ops {
   float v[16][DB];                    // V[kb + 8(st/4) + 4g + st%4][db*32 + lane%32]
 };
 
+// The operands of one 32-key step, through buffer resources over rows
+// [kb, min(kb + 32, kend)) of head h: rows past kend read 0 (kb < kend).
 template <int D>
-__device__ __forceinline__ void load_ops(F32Ops<D>& ops, const float* __restrict__ kp, const float* __restrict__ vp,
-                                         int kb, int klast, int64_t ld, int h, int ql, int g) {
+__device__ __forceinline__ void load_ops_buf(F32Ops<D>& ops, const float* __restrict__ kp,
+                                             const float* __restrict__ vp, int kb, int kend, uint32_t LD,
+                                             int64_t hoff, int ql, int g) {
   using O = F32Ops<D>;
-  {
-    const int key = min(kb + ql, klast);
-    const float4* src = reinterpret_cast<const float4*>(kp + static_cast<int64_t>(key) * ld + h * D + g * O::HALF);
+  const int n = min(32, kend - kb);
+  const int64_t off = static_cast<int64_t>(kb) * LD + hoff;
+  const auto rk = rows_rsrc(kp + off, n, LD), rv = rows_rsrc(vp + off, n, LD);
+  const uint32_t vrow = (static_cast<uint32_t>(ql) * LD + g * O::HALF) * 4u;
 #pragma unroll
-    for (int j = 0; j < O::HALF / 4; ++j) {
-      const float4 x = src[j];
-      ops.k[4 * j + 0] = x.x;
-      ops.k[4 * j + 1] = x.y;
-      ops.k[4 * j + 2] = x.z;
-      ops.k[4 * j + 3] = x.w;
-    }
+  for (int j = 0; j < O::HALF / 4; ++j) {
+    const float4 x = buf_f32x4(rk, vrow + 16u * j, 0);
+    ops.k[4 * j] = x.x, ops.k[4 * j + 1] = x.y, ops.k[4 * j + 2] = x.z, ops.k[4 * j + 3] = x.w;
   }
+  const uint32_t vtr = (static_cast<uint32_t>(4 * g) * LD + ql) * 4u;
 #pragma unroll
-  for (int st = 0; st < 16; ++st) {
-    const int key = min(kb + 8 * (st >> 2) + 4 * g + (st & 3), klast);
-    const float* row = vp + static_cast<int64_t>(key) * ld + h * D;
+  for (int st = 0; st < 16; ++st)
 #pragma unroll
-    for (int db = 0; db < O::DB; ++db) ops.v[st][db] = row[db * 32 + ql];
-  }
+    for (int db = 0; db < O::DB; ++db)
+      ops.v[st][db] = buf_f32(rv, vtr + 128u * db, (8u * (st >> 2) + (st & 3)) * LD * 4u);
 }
 
 template <int D>
@@ -169,16 +185,19 @@ __global__ __launch_bounds__(64, 2) void attn_fwd_f32_kernel(
   if (wk0 < wk1) {
     const int klast = wk1 - 1;
     O a, b;
-    load_ops<D>(a, kp, vp, wk0, klast, ld, h, ql, g);
+    const uint32_t LDu = static_cast<uint32_t>(ld);
+    const int64_t hoff = static_cast<int64_t>(h) * D;
+    const int kl = wk0 + (klast - wk0) / 32 * 32;  // first row of the last block
+    load_ops_buf<D>(a, kp, vp, wk0, wk1, LDu, hoff, ql, g);
     for (int kb = wk0; kb < wk1; kb += 64) {
-      // Unconditional (rows clamp to klast, so a step past the end reloads the last rows): a
-      // load under a branch makes the wait counts at the join assume the worst path and wait
-      // for the younger loads too. The empty asm keeps each load group where it is written.
-      load_ops<D>(b, kp, vp, kb + 32, klast, ld, h, ql, g);
+      // Unconditional (a step past the end reloads the last block): a load under a branch
+      // makes the wait counts at the join assume the worst path and wait for the younger
+      // loads too. The empty asm keeps each load group where it is written.
+      load_ops_buf<D>(b, kp, vp, min(kb + 32, kl), wk1, LDu, hoff, ql, g);
       asm volatile("" ::: "memory");
       block(a, kb);
       if (kb + 32 >= wk1) break;
-      load_ops<D>(a, kp, vp, kb + 64, klast, ld, h, ql, g);
+      load_ops_buf<D>(a, kp, vp, min(kb + 64, kl), wk1, LDu, hoff, ql, g);
       asm volatile("" ::: "memory");
       block(b, kb + 32);
     }
@@ -248,19 +267,6 @@ __device__ __forceinline__ void load_rows(float (&r)[D / 2], const float* __rest
   }
 }
 
-// t[st][db] = X[row 8(st/4) + 4g + st%4 (clamped to `last`)][db*32 + lane%32], rows relative to `base`.
-template <int D>
-__device__ __forceinline__ void load_tr(float (&t)[16][D / 32], const float* __restrict__ base, int last, uint32_t HD,
-                                        int ql, int g) {
-#pragma unroll
-  for (int st = 0; st < 16; ++st) {
-    const uint32_t rel = static_cast<uint32_t>(min(8 * (st >> 2) + 4 * g + (st & 3), last));
-    const float* row = base + (rel * HD + static_cast<uint32_t>(ql));
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db) t[st][db] = row[db * 32];
-  }
-}
-
 template <int D>
 __global__ __launch_bounds__(64, 2) void bwd_dq_f32_kernel(
     const float* __restrict__ dop, const float* __restrict__ qp, const float* __restrict__ kp,
@@ -308,25 +314,36 @@ __global__ __launch_bounds__(64, 2) void bwd_dq_f32_kernel(
   for (int db = 0; db < DB; ++db) dq[db] = floatx16{};
 
   if (wk0 < wk1) {
-    const int klast = wk1 - 1;
+    // key blocks through buffer resources over their rows inside [wk0, wk1): rows past wk1 read 0
+    const uint32_t vrow = (static_cast<uint32_t>(ql) * LD + g * HALF) * 4u;
+    const uint32_t vtr = (static_cast<uint32_t>(4 * g) * LD + ql) * 4u;
     float kr[HALF], vr[HALF], kt[16][DB];
-    load_rows<D>(kr, at(kp, wk0, LD), min(ql, klast - wk0), LD, g);
-    load_rows<D>(vr, at(vp, wk0, LD), min(ql, klast - wk0), LD, g);
-    load_tr<D>(kt, at(kp, wk0, LD), klast - wk0, LD, ql, g);
+    auto load_kv = [&](int kb) {
+      const int n = min(32, wk1 - kb);
+      const auto rk = rows_rsrc(at(kp, kb, LD), n, LD), rv = rows_rsrc(at(vp, kb, LD), n, LD);
+#pragma unroll
+      for (int j = 0; j < HALF / 4; ++j) {
+        const float4 x = buf_f32x4(rk, vrow + 16u * j, 0), y = buf_f32x4(rv, vrow + 16u * j, 0);
+        kr[4 * j] = x.x, kr[4 * j + 1] = x.y, kr[4 * j + 2] = x.z, kr[4 * j + 3] = x.w;
+        vr[4 * j] = y.x, vr[4 * j + 1] = y.y, vr[4 * j + 2] = y.z, vr[4 * j + 3] = y.w;
+      }
+    };
+    auto load_kt = [&](int kb) {
+      const auto rk = rows_rsrc(at(kp, kb, LD), min(32, wk1 - kb), LD);
+#pragma unroll
+      for (int st = 0; st < 16; ++st)
+#pragma unroll
+        for (int db = 0; db < DB; ++db) kt[st][db] = buf_f32(rk, vtr + 128u * db, (8u * (st >> 2) + (st & 3)) * LD * 4u);
+    };
     for (int kb = wk0; kb < wk1; kb += 32) {
-      const bool more = kb + 32 < wk1;
+      load_kv(kb);
       floatx16 s = floatx16{}, dp = floatx16{};
 #pragma unroll
       for (int st = 0; st < HALF; ++st) {
         s = __builtin_amdgcn_mfma_f32_32x32x2f32(kr[st], qf[st], s, 0, 0, 0);
         dp = __builtin_amdgcn_mfma_f32_32x32x2f32(vr[st], df[st], dp, 0, 0, 0);
       }
-      {
-        const int nb = more ? kb + 32 : kb;
-        load_rows<D>(kr, at(kp, nb, LD), min(ql, klast - nb), LD, g);
-        load_rows<D>(vr, at(vp, nb, LD), min(ql, klast - nb), LD, g);
-        asm volatile("" ::: "memory");
-      }
+      load_kt(kb);
       if (!(kb >= mk0 && kb + 32 <= mk1)) {
         const int base = kb + 4 * g;
         mask_block(s, qk0 - base, qk1 - base);
@@ -340,11 +357,6 @@ __global__ __launch_bounds__(64, 2) void bwd_dq_f32_kernel(
       for (int st = 0; st < 16; ++st)
 #pragma unroll
         for (int db = 0; db < DB; ++db) dq[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(kt[st][db], dp[st], dq[db], 0, 0, 0);
-      {
-        const int nb = more ? kb + 32 : kb;
-        load_tr<D>(kt, at(kp, nb, LD), klast - nb, LD, ql, g);
-        asm volatile("" ::: "memory");
-      }
     }
   }
   if (qvalid) store_acc_row<float, D>(dqp, static_cast<int64_t>(qrow) * ld + hoff, dq, scale, g);
@@ -390,7 +402,7 @@ namespace pe {
 namespace {
 
 template <int D>
-__global__ __launch_bounds__(64, D > 32 ? 1 : 2) void bwd_dkdv_f32_kernel(
+__global__ __launch_bounds__(64, 2) void bwd_dkdv_f32_kernel(
     const float* __restrict__ dop, const float* __restrict__ qp, const float* __restrict__ kp,
     const float* __restrict__ vp, const float* __restrict__ lse, const float* __restrict__ delta,
     const int32_t* __restrict__ cu, const int32_t* __restrict__ items, int32_t B, int32_t N, int32_t H, int32_t T,
@@ -432,23 +444,30 @@ __global__ __launch_bounds__(64, D > 32 ? 1 : 2) void bwd_dkdv_f32_kernel(
 
   const float* lse_h = lse + static_cast<int64_t>(h) * N;
   const float* del_h = delta + static_cast<int64_t>(h) * N;
-  // The rows of the next query block (and their statistics) load under this block's dV/dK
-  // products; the transposed operands of a block load under its own S/dP products.
-  const int qlast = wq1 - 1;
+  // Query blocks load through buffer resources over their rows inside [wq0, wq1), so rows
+  // past wq1 read 0 and no lane computes an address per load. Two waves share a SIMD
+  // (256 registers each), one computing while the other waits for its loads; a
+  // one-wave kernel prefetching a block ahead (360 registers) ran 1.2x slower.
+  const uint32_t vrow_q = (static_cast<uint32_t>(ql) * LD + g * HALF) * 4u;
+  const uint32_t vrow_d = (static_cast<uint32_t>(ql) * HD + g * HALF) * 4u;
+  const uint32_t vtr_q = (static_cast<uint32_t>(4 * g) * LD + ql) * 4u;
+  const uint32_t vtr_d = (static_cast<uint32_t>(4 * g) * HD + ql) * 4u;
   float qr[HALF], dr[HALF];
   float lse_r = 0.f, del_r = 0.f;
   auto load_rows_blk = [&](int qb) {
-    const int qrow = min(qb + ql, qlast);
-    load_rows<D>(qr, at(qp, qb, LD), qrow - qb, LD, g);
-    load_rows<D>(dr, at(dop, qb, HD), qrow - qb, HD, g);
-    lse_r = lse_h[qrow];
-    del_r = del_h[qrow];
+    const int n = min(32, wq1 - qb);
+    const auto rq = rows_rsrc(at(qp, qb, LD), n, LD), rd = rows_rsrc(at(dop, qb, HD), n, HD);
+#pragma unroll
+    for (int j = 0; j < HALF / 4; ++j) {
+      const float4 x = buf_f32x4(rq, vrow_q + 16u * j, 0), y = buf_f32x4(rd, vrow_d + 16u * j, 0);
+      qr[4 * j] = x.x, qr[4 * j + 1] = x.y, qr[4 * j + 2] = x.z, qr[4 * j + 3] = x.w;
+      dr[4 * j] = y.x, dr[4 * j + 1] = y.y, dr[4 * j + 2] = y.z, dr[4 * j + 3] = y.w;
+    }
+    lse_r = buf_f32(rows_rsrc(lse_h + qb, n, 1), ql * 4u, 0);
+    del_r = buf_f32(rows_rsrc(del_h + qb, n, 1), ql * 4u, 0);
   };
-  if (wq0 < wq1) load_rows_blk(wq0);
   for (int qb = wq0; qb < wq1; qb += 32) {
-    float qt[16][DB], dt[16][DB];
-    load_tr<D>(qt, at(qp, qb, LD), qlast - qb, LD, ql, g);
-    load_tr<D>(dt, at(dop, qb, HD), qlast - qb, HD, ql, g);
+    load_rows_blk(qb);
     if (g == 0) {
       stat[0][ql] = lse_r * kLog2e;
       stat[1][ql] = del_r;
@@ -459,7 +478,20 @@ __global__ __launch_bounds__(64, D > 32 ? 1 : 2) void bwd_dkdv_f32_kernel(
       s = __builtin_amdgcn_mfma_f32_32x32x2f32(qr[st], kr[st], s, 0, 0, 0);
       dp = __builtin_amdgcn_mfma_f32_32x32x2f32(dr[st], vr[st], dp, 0, 0, 0);
     }
-    // rows of this block are queries qb + 8(i/4) + 4g + i%4; keep those inside the key's own sequence
+    float qt[16][DB], dt[16][DB];
+    {
+      const int n = min(32, wq1 - qb);
+      const auto rq = rows_rsrc(at(qp, qb, LD), n, LD), rd = rows_rsrc(at(dop, qb, HD), n, HD);
+#pragma unroll
+      for (int st = 0; st < 16; ++st) {
+        const uint32_t r = 8 * (st >> 2) + (st & 3);
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          qt[st][db] = buf_f32(rq, vtr_q + 128u * db, r * LD * 4u);
+          dt[st][db] = buf_f32(rd, vtr_d + 128u * db, r * HD * 4u);
+        }
+      }
+    }
     if (!(qb >= mq0 && qb + 32 <= mq1)) {
       const int base = qb + 4 * g;
       mask_block(s, kq0 - base, kq1 - base);
@@ -479,11 +511,6 @@ __global__ __launch_bounds__(64, D > 32 ? 1 : 2) void bwd_dkdv_f32_kernel(
       }
     }
     __syncthreads();
-    // unconditional (the last block reloads itself), so no branch splits the wait counts; the
-    // empty asm keeps these loads here instead of letting them merge with the next iteration's use
-    load_rows_blk(qb + 32 < wq1 ? qb + 32 : qb);
-    asm volatile("" ::: "memory");
-    // queries at or past wq1 have P = dS = 0 for every key of the wave: skip their steps
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       if (j > 0 && qb + 8 * j >= wq1) break;
