@@ -180,7 +180,7 @@ pe_status fwd_impl(const void* q, const void* k, const void* v, const int32_t* c
     return PE_ERR_WORKSPACE;
   hipStream_t st = as_stream(stream);
   int32_t* items = static_cast<int32_t*>(workspace);
-  if (dtype == PE_FP32 && pe::attn_fwd_f32_wave_supported(head_dim)) {
+  if (dtype == PE_FP32 && pe::attn_f32_wave_supported(head_dim, ld, num_heads)) {
     hipError_t e = pe::launch_seq_worklist(cu_seqlens, num_seqs, total_tokens, pe::kAttnWaveRows, items, st);
     if (e != hipSuccess) return PE_ERR_HIP;
     return hip_status(pe::launch_attn_fwd_f32_wave(head_dim, q, k, v, cu_seqlens, items, num_seqs,
@@ -512,9 +512,8 @@ namespace {
 // kPlanMaxEntries the separate multi-block kernels are faster than one workgroup
 // (measured per replay: 2-3 us gained up to ~8k entries, even at ~16k, 4.5 us lost at ~33k).
 constexpr int64_t kPlanMaxEntries = 1 << 14;
-int64_t plan_entries(int32_t num_seqs, int64_t cap, int64_t rowbytes, pe_dtype dtype, int32_t head_dim) {
+int64_t plan_entries(int32_t num_seqs, int64_t cap, int64_t rowbytes, bool wave) {
   const int64_t np = std::max(ceil_div(cap, pe::pack_tile_rows(rowbytes)), static_cast<int64_t>(num_seqs));
-  const bool wave = dtype == PE_FP32 && pe::attn_fwd_f32_wave_supported(head_dim);
   const int64_t na = wave ? cap / pe::kAttnWaveRows + num_seqs
                           : std::max(ceil_div(cap, pe::kAttnTileRows), static_cast<int64_t>(num_seqs));
   return np + na;
@@ -562,11 +561,11 @@ pe_status pe_forward_graph_create(const int32_t* lengths, int32_t num_seqs, int3
     return PE_ERR_HIP;
   }
   pe_status s = PE_OK;
-  if (plan_entries(num_seqs, cap, 3 * hd * elem_bytes(dtype), dtype, head_dim) <= kPlanMaxEntries) {
+  const bool wave = dtype == PE_FP32 && pe::attn_f32_wave_supported(head_dim, 3 * hd, num_heads);
+  const int64_t rowbytes = 3 * hd * elem_bytes(dtype);
+  if (plan_entries(num_seqs, cap, rowbytes, wave) <= kPlanMaxEntries) {
     // Four kernels: plan (scan + both work lists), pack, attention, unpack. The work lists sit
     // where pe_pack_async and the attention calls put them in the same workspace.
-    const bool wave = dtype == PE_FP32 && pe::attn_fwd_f32_wave_supported(head_dim);
-    const int64_t rowbytes = 3 * hd * elem_bytes(dtype);
     const int32_t rp = pe::pack_tile_rows(rowbytes);
     int32_t* items_p = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + kAlign);
     int32_t* items_a = static_cast<int32_t*>(attn_ws);

@@ -295,9 +295,7 @@ hipError_t bwd_dispatch(const void* dout, const void* q, const void* k, const vo
   timing_stop("bwd_delta", ev_bwd_delta, stream);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  // the fp32 wave kernels address rows through 32-bit buffer offsets: row strides below 2^24
-  if (!kIs16<Et> && items32 != nullptr && (D == 32 || D == 64) && ld < (int64_t{1} << 24) &&
-      static_cast<int64_t>(H) * D < (int64_t{1} << 24)) {
+  if (!kIs16<Et> && items32 != nullptr && attn_f32_wave_supported(D, ld, H)) {
     e = launch_bwd_dkdv_f32_wave(D, dout, q, k, v, lse, delta, cu, items32, B, N, H, win, ld, scale, dk, dv,
                                  stream);
     if (e != hipSuccess) return e;

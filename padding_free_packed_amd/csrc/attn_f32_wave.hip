@@ -229,7 +229,11 @@ hipError_t dispatch(const void* q, const void* k, const void* v, const int32_t* 
 
 }  // namespace
 
-bool attn_fwd_f32_wave_supported(int D) { return D == 32 || D == 64; }
+// Head dims 32 and 64; the buffer offsets are 32-bit, so row strides (ld, and H * D for
+// O and dO) stay below 2^24 elements.
+bool attn_f32_wave_supported(int D, int64_t ld, int32_t H) {
+  return (D == 32 || D == 64) && ld < (int64_t{1} << 24) && static_cast<int64_t>(H) * D < (int64_t{1} << 24);
+}
 
 hipError_t launch_attn_fwd_f32_wave(int D, const void* q, const void* k, const void* v, const int32_t* cu,
                                     const int32_t* items32, int32_t B, int32_t N, int32_t H, int32_t win, int64_t ld,

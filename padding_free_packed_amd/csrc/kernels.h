@@ -61,7 +61,7 @@ hipError_t launch_attn_fwd_bf16(bool f16, int D, const void* q, const void* k, c
 
 // fp32 forward, one independent wave per 32 query rows of one sequence (head dims 32, 64);
 // items32 is the sequence-aligned work list (launch_seq_worklist) with tile height kAttnWaveRows.
-bool attn_fwd_f32_wave_supported(int D);
+bool attn_f32_wave_supported(int D, int64_t ld, int32_t H);  // forward and backward alike
 hipError_t launch_attn_fwd_f32_wave(int D, const void* q, const void* k, const void* v, const int32_t* cu,
                                     const int32_t* items32, int32_t B, int32_t N, int32_t H, int32_t win, int64_t ld,
                                     float scale, void* out, float* lse, hipStream_t stream);
