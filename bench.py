@@ -56,6 +56,7 @@ def algo_work(kernel, w, N, L2, e, with_lse, with_grid=True):
     D = H * d
     T = (N + 127) // 128
     lse_b = 4.0 * N * H if with_lse else 0.0
+    wave_dq = e == 4 and d in (32, 64)
     return {
         # forward: 4 L2 H d flops (QK^T and PV); read Q, K, V, write O (+ LSE)
         "attn_fwd": {"flop": 4.0 * L2 * H * d, "byte": 4.0 * N * D * e + lse_b},
@@ -63,7 +64,8 @@ def algo_work(kernel, w, N, L2, e, with_lse, with_grid=True):
         # Q, K, V, dO, LSE, D in and dK, dV out; dQ is credited with dQ alone (2 L2 H d),
         # its recomputation of S and dP is not counted
         "bwd_dkdv": {"flop": 8.0 * L2 * H * d, "byte": 6.0 * N * D * e + 8.0 * N * H},
-        "bwd_dq": {"flop": 2.0 * L2 * H * d, "byte": 5.0 * N * D * e + 8.0 * N * H},
+        # (the fp32 one-wave dQ also reads O and writes D, the delta pass it replaces)
+        "bwd_dq": {"flop": 2.0 * L2 * H * d, "byte": (6.0 if wave_dq else 5.0) * N * D * e + 8.0 * N * H},
         # first token: read K and V once, the B queries, write B outputs (+ LSE)
         "attn_fwd_first": {"byte": 2.0 * N * D * e + 2.0 * B * D * e + (4.0 * B * H if with_lse else 0.0)},
         # first-token backward: read K, V and the B rows of q, dO, O (+ LSE), write dK, dV and dq_first

@@ -15,7 +15,9 @@
 //
 // The dQ pass recomputes S and dP once more than an atomic-accumulation scheme
 // would (14 instead of 10 matrix products of the size of S per head), the price
-// of determinism.
+// of determinism. On the fp32 one-wave path (attn_f32_wave.hip) the dQ pass runs
+// first and computes D of its own rows on the way (it holds dO already and reads
+// O once), so there are two launches and no delta pass.
 #include <climits>
 
 #include "attn_common.h"
@@ -288,6 +290,14 @@ hipError_t bwd_dispatch(const void* dout, const void* q, const void* k, const vo
                         float* delta, hipStream_t stream) {
   using G = Geo<Et, D>;
   if (N == 0) return hipSuccess;
+  if (!kIs16<Et> && items32 != nullptr && attn_f32_wave_supported(D, ld, H)) {
+    // the fp32 dQ pass computes D itself and stores it for the dK/dV pass
+    hipError_t e = launch_bwd_dq_f32_wave(D, dout, q, k, v, out, lse, delta, cu, items32, B, N, H, win, ld, scale,
+                                          dq, stream);
+    if (e != hipSuccess) return e;
+    return launch_bwd_dkdv_f32_wave(D, dout, q, k, v, lse, delta, cu, items32, B, N, H, win, ld, scale, dk, dv,
+                                    stream);
+  }
   const int64_t chunks = static_cast<int64_t>(N) * H * G::CH;
   hipEvent_t ev_bwd_delta = timing_start(stream);
   hipLaunchKernelGGL((bwd_delta_kernel<Et, D>), dim3(static_cast<unsigned>((chunks + 255) / 256)), dim3(256), 0,
@@ -295,12 +305,6 @@ hipError_t bwd_dispatch(const void* dout, const void* q, const void* k, const vo
   timing_stop("bwd_delta", ev_bwd_delta, stream);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (!kIs16<Et> && items32 != nullptr && attn_f32_wave_supported(D, ld, H)) {
-    e = launch_bwd_dkdv_f32_wave(D, dout, q, k, v, lse, delta, cu, items32, B, N, H, win, ld, scale, dk, dv,
-                                 stream);
-    if (e != hipSuccess) return e;
-    return launch_bwd_dq_f32_wave(D, dout, q, k, v, lse, delta, cu, items32, B, N, H, win, ld, scale, dq, stream);
-  }
   const int T = (N + kAttnTileRows - 1) / kAttnTileRows;
   const unsigned blocks = static_cast<unsigned>(static_cast<int64_t>(T) * H);
   const float c = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);

@@ -274,9 +274,9 @@ __device__ __forceinline__ void load_rows(float (&r)[D / 2], const float* __rest
 template <int D>
 __global__ __launch_bounds__(64, 2) void bwd_dq_f32_kernel(
     const float* __restrict__ dop, const float* __restrict__ qp, const float* __restrict__ kp,
-    const float* __restrict__ vp, const float* __restrict__ lse, const float* __restrict__ delta,
-    const int32_t* __restrict__ cu, const int32_t* __restrict__ items, int32_t B, int32_t N, int32_t H, int32_t T,
-    int32_t win, int64_t ld, float c, float scale, float* __restrict__ dqp) {
+    const float* __restrict__ vp, const float* __restrict__ op, const float* __restrict__ lse,
+    float* __restrict__ delta, const int32_t* __restrict__ cu, const int32_t* __restrict__ items, int32_t B,
+    int32_t N, int32_t H, int32_t T, int32_t win, int64_t ld, float c, float scale, float* __restrict__ dqp) {
   constexpr int HALF = D / 2, DB = D / 32;
   const int lin = xcd_remap(blockIdx.x, gridDim.x);
   const int h = lin / T, t = lin - h * T;
@@ -311,7 +311,18 @@ __global__ __launch_bounds__(64, 2) void bwd_dq_f32_kernel(
     for (int i = 0; i < HALF; ++i) qf[i] = df[i] = 0.f;
   }
   const float lse2 = qvalid ? lse[static_cast<int64_t>(h) * N + qrow] * kLog2e : 0.f;
-  const float dlq = qvalid ? delta[static_cast<int64_t>(h) * N + qrow] : 0.f;
+  // D = <dO, O> of the lane's row (each half of the wave holds half of the row), stored
+  // for the dK/dV pass that follows: every row of every sequence is one wave's, per head
+  float dlq;
+  {
+    float of[HALF];
+    load_rows<D>(of, at(op, r0, HD), qsafe - r0, HD, g);
+    float part = 0.f;
+#pragma unroll
+    for (int i = 0; i < HALF; ++i) part = fmaf(df[i], of[i], part);
+    dlq = qvalid ? xhalf_sum(part) : 0.f;
+    if (qvalid && g == 0) delta[static_cast<int64_t>(h) * N + qrow] = dlq;
+  }
 
   floatx16 dq[DB];
 #pragma unroll
@@ -369,7 +380,8 @@ __global__ __launch_bounds__(64, 2) void bwd_dq_f32_kernel(
 }  // namespace
 
 hipError_t launch_bwd_dq_f32_wave(int D, const void* dout, const void* q, const void* k, const void* v,
-                                  const float* lse, const float* delta, const int32_t* cu, const int32_t* items32,
+                                  const void* out, const float* lse, float* delta, const int32_t* cu,
+                                  const int32_t* items32,
                                   int32_t B, int32_t N, int32_t H, int32_t win, int64_t ld, float scale, void* dq,
                                   hipStream_t stream) {
   const int T = N / kRows + B;  // slots of the sequence-aligned work list
@@ -380,12 +392,14 @@ hipError_t launch_bwd_dq_f32_wave(int D, const void* dout, const void* q, const 
   hipEvent_t ev = timing_start(stream);
   if (D == 32)
     hipLaunchKernelGGL((bwd_dq_f32_kernel<32>), gd, bd, 0, stream, static_cast<const float*>(dout),
-                       static_cast<const float*>(q), static_cast<const float*>(k), static_cast<const float*>(v), lse,
-                       delta, cu, items32, B, N, H, T, win, ld, c, scale, static_cast<float*>(dq));
+                       static_cast<const float*>(q), static_cast<const float*>(k), static_cast<const float*>(v),
+                       static_cast<const float*>(out), lse, delta, cu, items32, B, N, H, T, win, ld, c, scale,
+                       static_cast<float*>(dq));
   else if (D == 64)
     hipLaunchKernelGGL((bwd_dq_f32_kernel<64>), gd, bd, 0, stream, static_cast<const float*>(dout),
-                       static_cast<const float*>(q), static_cast<const float*>(k), static_cast<const float*>(v), lse,
-                       delta, cu, items32, B, N, H, T, win, ld, c, scale, static_cast<float*>(dq));
+                       static_cast<const float*>(q), static_cast<const float*>(k), static_cast<const float*>(v),
+                       static_cast<const float*>(out), lse, delta, cu, items32, B, N, H, T, win, ld, c, scale,
+                       static_cast<float*>(dq));
   else
     return hipErrorInvalidValue;
   timing_stop("bwd_dq", ev, stream);

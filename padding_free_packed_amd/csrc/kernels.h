@@ -72,10 +72,12 @@ hipError_t launch_bwd_dkdv_f32_wave(int D, const void* dout, const void* q, cons
                                     const float* lse, const float* delta, const int32_t* cu, const int32_t* items32,
                                     int32_t B, int32_t N, int32_t H, int32_t win, int64_t ld, float scale, void* dk,
                                     void* dv, hipStream_t stream);
+// The dQ pass also computes D = rowsum(dO * O) (O dense [N, H, D]) and stores it to delta for
+// the dK/dV pass, which therefore runs after it.
 hipError_t launch_bwd_dq_f32_wave(int D, const void* dout, const void* q, const void* k, const void* v,
-                                  const float* lse, const float* delta, const int32_t* cu, const int32_t* items32,
-                                  int32_t B, int32_t N, int32_t H, int32_t win, int64_t ld, float scale, void* dq,
-                                  hipStream_t stream);
+                                  const void* out, const float* lse, float* delta, const int32_t* cu,
+                                  const int32_t* items32, int32_t B, int32_t N, int32_t H, int32_t win, int64_t ld,
+                                  float scale, void* dq, hipStream_t stream);
 
 // gather = 0: q_first is [B, H, D]; gather = 1: the query of sequence b is row cu[b] of a packed [N, H, D]
 // max_seq_len (the host length bound) sets the key slots per block of both first-token kernels.
