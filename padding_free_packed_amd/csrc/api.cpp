@@ -312,15 +312,14 @@ pe_status bwd_impl(const void* dout, const void* q, const void* k, const void* v
   const size_t ib = items_bytes(num_seqs, total_tokens);
   int32_t* items32 = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + ib);
   float* delta = reinterpret_cast<float*>(static_cast<char*>(workspace) + 2 * ib);
-  hipError_t e = pe::launch_worklist(cu_seqlens, num_seqs, total_tokens, pe::kAttnTileRows, items, st);
+  // the fp32 one-wave kernels take the sequence-aligned list, every other kernel the 128-row one
+  const bool wave = dtype == PE_FP32 && pe::attn_f32_wave_supported(head_dim, ld, num_heads);
+  hipError_t e = wave ? pe::launch_seq_worklist(cu_seqlens, num_seqs, total_tokens, pe::kAttnWaveRows, items32, st)
+                      : pe::launch_worklist(cu_seqlens, num_seqs, total_tokens, pe::kAttnTileRows, items, st);
   if (e != hipSuccess) return PE_ERR_HIP;
-  if (dtype == PE_FP32) {
-    e = pe::launch_seq_worklist(cu_seqlens, num_seqs, total_tokens, pe::kAttnWaveRows, items32, st);
-    if (e != hipSuccess) return PE_ERR_HIP;
-  }
-  e = pe::launch_attn_bwd(dtype, head_dim, dout, q, k, v, out, lse, cu_seqlens, items,
-                          dtype == PE_FP32 ? items32 : nullptr, num_seqs, static_cast<int32_t>(total_tokens),
-                          num_heads, win, ld, softmax_scale, dq, dk, dv, delta, st);
+  e = pe::launch_attn_bwd(dtype, head_dim, dout, q, k, v, out, lse, cu_seqlens, wave ? nullptr : items,
+                          wave ? items32 : nullptr, num_seqs, static_cast<int32_t>(total_tokens), num_heads, win, ld,
+                          softmax_scale, dq, dk, dv, delta, st);
   if (e == hipErrorNotSupported) return PE_ERR_UNSUPPORTED;
   return hip_status(e);
 }

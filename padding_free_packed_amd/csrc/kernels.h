@@ -93,8 +93,9 @@ hipError_t launch_attn_bwd_first(int dt, int D, const void* dout_first, const vo
                                  void* dq_first, void* dk, void* dv, hipStream_t stream);
 
 // Backward: D = rowsum(dO * O) per (head, row), then dK/dV over key tiles, then dQ over query tiles.
-// items: work list with tile height kAttnTileRows; items32: the sequence-aligned list with
-// kAttnWaveRows (or NULL).
+// items32: the sequence-aligned list with kAttnWaveRows, given exactly when fp32 and
+// attn_f32_wave_supported (the one-wave kernels run); otherwise NULL and items is the work
+// list with tile height kAttnTileRows.
 // win: local attention radius (keys with |i - j| <= win), or -1 for global attention;
 // ld: elements between consecutive rows of Q, K, V (and of dQ, dK, dV): num_heads * D for
 // separate [N, H, D] tensors, 3 * num_heads * D for a fused [N, 3, H, D] buffer. O, dO,

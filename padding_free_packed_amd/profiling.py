@@ -32,6 +32,7 @@ KERNEL_SOURCES = {
     "unpack_rows": ["pack.hip", "common.h"],
     "scan": ["pack.hip", "common.h"],
     "worklist": ["pack.hip", "common.h"],
+    "plan": ["pack.hip", "common.h"],
 }
 
 # device kernel names behind each timing name, as the profiler prints them:
@@ -48,6 +49,7 @@ KERNEL_PATTERNS = {
     "unpack_rows": r"unpack_rows_kernel(<|I)",
     "scan": r"scan_lengths_kernel",
     "worklist": r"worklist_kernel",
+    "plan": r"plan_kernel",
 }
 COPY_PATTERN = r"copy|elementwise"
 
