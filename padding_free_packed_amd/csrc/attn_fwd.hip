@@ -15,6 +15,10 @@
 //   O^T (d x 32 queries) += V^T P^T        (mma_tr_regs: V from LDS, P straight from S^T)
 // Computing S transposed leaves every lane with one query and 16 of its keys,
 // the layout the PV product needs as its B operand, so P never goes through LDS.
+// For 16-bit types (d <= 64) each head's Q rows arrive by LDS DMA into a tile of
+// the block's 128 rows, issued during the previous head's last key block, so a
+// head switch does not wait for its Q (and the rows load whole, 8 lanes per
+// 128-byte row, instead of one row per lane).
 #include <algorithm>
 #include <climits>
 #include <type_traits>
@@ -40,10 +44,16 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
   // (conflict-free for both the row reads and the transposing reads)
   constexpr bool SWZ = kIs16<Et> && D % 32 == 0;
   constexpr int TS = SWZ ? kBlk * D : G::TSZ;
-  // the next head's Q rows are fetched one step early where the registers allow it
-  constexpr bool PREFQ = D <= 32;
+  // 16-bit tiles: each head's Q rows come by LDS DMA into a tile of the block's 128 rows,
+  // issued during the previous head's last key block; otherwise the next head's Q rows are
+  // fetched one step early where the registers allow it
+  constexpr bool QDMA = SWZ && D <= 64;  // (the d = 128 tile would cost a block per CU)
+  constexpr bool PREFQ = !QDMA && D <= 32;
+  constexpr int QCH = D / 8;                                  // 16-byte chunks per Q row
+  constexpr int QNL = QDMA ? kAttnTileRows * QCH / kThreads : 1;  // DMA instructions per thread
   __shared__ __align__(16) E kt[2][TS];
   __shared__ __align__(16) E vt[2][TS];
+  __shared__ __align__(16) uint16_t qtile[QDMA ? kAttnTileRows * D : 8];
   __shared__ int32_t cul[kAttnTileRows + 2];
 
   const int lin = xcd_remap(blockIdx.x, gridDim.x);
@@ -71,7 +81,33 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
   const int64_t qoff = static_cast<int64_t>(qrow) * ld + g * G::HALF;
 
   typename RegT<Et>::type qr[G::QS];
-  load_row_regs<Et, D>(qp, qoff + h0 * D, qvalid, qr);
+  // Q DMA: thread slot j*256 + tid fills LDS chunk position j*256 + tid of the tile, i.e.
+  // row pos / QCH, physical chunk pos % QCH, which holds logical chunk (pos % QCH) ^ swz(row);
+  // rows past the tile's last one repeat it (their queries are not stored)
+  uint32_t qdoff[QNL];
+  if constexpr (QDMA) {
+#pragma unroll
+    for (int jn = 0; jn < QNL; ++jn) {
+      const int pos = jn * kThreads + tid, r = pos / QCH, pc = pos - r * QCH;
+      const int rr = min(r, sp.rend - 1 - sp.r0);
+      qdoff[jn] = static_cast<uint32_t>(rr) * static_cast<uint32_t>(ld) * 2u + ((pc ^ (swz(r) & (QCH - 1))) * 16u);
+    }
+  }
+  auto q_dma = [&](int h) __attribute__((always_inline)) {
+    if constexpr (QDMA) {
+      const char* base = static_cast<const char*>(qp) + (static_cast<int64_t>(sp.r0) * ld + static_cast<int64_t>(h) * D) * 2;
+#pragma unroll
+      for (int jn = 0; jn < QNL; ++jn)
+        dma16(lds_addr(qtile) + static_cast<uint32_t>((jn * kThreads + wv * 64) * 16), base, qdoff[jn]);
+    }
+  };
+  auto q_from_lds = [&]() __attribute__((always_inline)) {
+    if constexpr (QDMA) {
+#pragma unroll
+      for (int st = 0; st < G::QS; ++st) qr[st] = swz_read_b128<Et, QCH>(qtile, wv * 32 + ql, g * (QCH / 2) + st);
+    }
+  };
+  if constexpr (!QDMA) load_row_regs<Et, D>(qp, qoff + h0 * D, qvalid, qr);
 
   uint4 kr[G::PER], vr[G::PER];
   floatx16 o[G::DB];
@@ -156,6 +192,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
   // Steps run over (head, key block) pairs, heads outer. The key blocks are the
   // same for every head, so the register-staged prefetch of the next step's
   // K and V rows runs on across the head boundary.
+  q_dma(h0);  // waited for with the first K/V loads below
   tile_gload<Et, D>(kp, klo, khi, ld, h0, kr);
   tile_gload<Et, D>(vp, klo, khi, ld, h0, vr);
   int buf = 0, hh = 0, j = 0;
@@ -171,6 +208,15 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
     }
     __syncthreads();
     const bool last = j + 1 == nkb;  // last key block of head h0 + hh
+    if constexpr (QDMA) {
+      // the DMA of this head's Q completed with the K/V loads waited for above (it was
+      // issued before them); all waves read it here, then the tile is free again
+      if (j == 0) {
+        q_from_lds();
+        if (last) __syncthreads();  // one key block per head: reads before the next DMA
+      }
+      if (last && hh + 1 < nh) q_dma(h0 + hh + 1);
+    }
     if (step + 1 < nsteps) {
       const int hn = h0 + (last ? hh + 1 : hh);
       const int kn = last ? klo : kb + kBlk;
@@ -187,7 +233,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
         if constexpr (PREFQ) {
 #pragma unroll
           for (int st = 0; st < G::QS; ++st) qr[st] = qn[st];
-        } else {
+        } else if constexpr (!QDMA) {
           load_row_regs<Et, D>(qp, qoff + (h0 + hh + 1) * D, qvalid, qr);
         }
       }
