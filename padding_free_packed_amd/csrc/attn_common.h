@@ -209,6 +209,41 @@ template <typename Et, int D>
 __device__ __forceinline__ void store_acc_row(void* outp, int64_t off, const floatx16 (&acc)[Geo<Et, D>::DB],
                                               float mul, int g) {
   using G = Geo<Et, D>;
+  if constexpr (kIs16<Et> && D % 32 == 0) {
+    // Pair the two half-waves (same row, alternate groups of 4 columns) through one
+    // permlane32 swap per value, so each lane stores 8 consecutive columns (16 bytes)
+    // instead of two runs of 4.
+#pragma unroll
+    for (int db = 0; db < G::DB; ++db)
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        float mine[4], sent[4], got[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float a = acc[db][8 * k + e] * mul, b = acc[db][8 * k + 4 + e] * mul;  // columns 16k+4g+e, 16k+8+4g+e
+          mine[e] = g == 0 ? a : b;
+          sent[e] = g == 0 ? b : a;
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(sent[e]), __float_as_uint(sent[e]), false, false);
+          got[e] = __uint_as_float(g == 0 ? r[1] : r[0]);
+        }
+        // lane g = 0: columns 16k .. 16k+7 = own 0..3, partner's 4..7; g = 1: 16k+8 .. 16k+15
+        float v[8];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          v[e] = g == 0 ? mine[e] : got[e];
+          v[4 + e] = g == 0 ? got[e] : mine[e];
+        }
+        uint32_t w[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w[e] = f32_to_h16<Et>(v[2 * e]) | (uint32_t(f32_to_h16<Et>(v[2 * e + 1])) << 16);
+        uint16_t* O = static_cast<uint16_t*>(outp) + off + db * 32 + 16 * k + 8 * g;
+        *reinterpret_cast<uint4*>(O) = make_uint4(w[0], w[1], w[2], w[3]);
+      }
+    return;
+  }
 #pragma unroll
   for (int db = 0; db < G::DB; ++db)
 #pragma unroll
