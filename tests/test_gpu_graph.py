@@ -195,3 +195,31 @@ def test_bucket_graph_replays(dtype, H, d, window):
         assert torch.equal(_bits(bucket.out_grid), _bits(ref_grid))
     finally:
         bucket.close()
+
+
+@pytest.mark.parametrize("dtype,H,d", [(torch.bfloat16, 12, 64), (torch.float32, 8, 64)])
+def test_large_bucket_replays_the_six_kernel_capture(dtype, H, d):
+    """A bucket whose work lists exceed what the single-workgroup plan kernel takes
+    (here one pack tile per 12 x 64 bf16 row: 300 x 64 = 19,200 entries) is captured
+    as scan, two work lists, pack, attention, unpack; its replays match the eager calls
+    bit for bit, like the small buckets' four-kernel replays."""
+    slots, S = 300, 64
+    scale = 1.0 / np.sqrt(d)
+    say(f"[graph large] {dtype} H={H} d={d}: bucket ({slots}, {S})")
+    bucket = graphs.ForwardBucket(slots, S, H, d, dtype, scale, -1, with_lse=True, device=DEV)
+    rng = np.random.default_rng(77 + H)
+    wdt = W.BF16 if dtype == torch.bfloat16 else W.FP32
+    try:
+        for rep, B in enumerate([slots, 123]):
+            L = rng.integers(1, S + 1, size=B).astype(np.int32)
+            x = rng.standard_normal((B, S, 3, H, d), dtype=np.float32)
+            bucket.run(torch.from_numpy(L).to(DEV), to_dev(W.f32_to_bf16_bits(x) if wdt == W.BF16 else x, wdt))
+            torch.cuda.synchronize()
+            ref_grid, ref_lse, n, cu = _eager(bucket, scale, -1)
+            say(f"  replay {rep}: B={B} N={n}")
+            assert bucket.status.tolist() == [n, pe.PACK_OK]
+            assert torch.equal(_bits(bucket.out_grid), _bits(ref_grid))
+            assert torch.equal(bucket.lse[:, :n], ref_lse)
+            assert torch.equal(bucket.cu_seqlens, cu)
+    finally:
+        bucket.close()
