@@ -29,7 +29,13 @@
  *   runtime call or launch failed.
  * - The attention calls do not validate device contents: cu_seqlens must be
  *   non-decreasing from 0 to N with every length in [1, max_seq_len], as
- *   pe_pack produces it. Anything else is undefined behaviour.
+ *   pe_pack produces it. Anything else is undefined behaviour. With the
+ *   environment variable PE_CHECK=1 (a debugging aid) every attention call
+ *   first checks cu_seqlens on the device (cu[0] = 0, every length in
+ *   [1, max_seq_len], cu[B] <= total_tokens) and waits for the answer: on a
+ *   violation it returns PE_ERR_LENGTHS with nothing else launched. That mode
+ *   synchronizes the stream (no graph capture) and shares one device flag
+ *   between calls, so calls must not overlap.
  * - dtype PE_FP32 computes in fp32 throughout (the GiGL page runs its kernel in
  *   fp32 because inference needs it). PE_BF16 reads and writes bf16 and
  *   accumulates in fp32; the probabilities are rounded to bf16 before they
@@ -52,7 +58,7 @@ typedef enum {
   PE_ERR_NULL = 1,        /* a required pointer is NULL */
   PE_ERR_ARG = 2,         /* a size, count, alignment or the scale is invalid */
   PE_ERR_UNSUPPORTED = 3, /* head_dim or dtype outside what the kernels support */
-  PE_ERR_LENGTHS = 4,     /* pe_pack found a length outside [1, max_seq_len] */
+  PE_ERR_LENGTHS = 4,     /* pe_pack (or the PE_CHECK=1 mode) found a length outside [1, max_seq_len] */
   PE_ERR_CAPACITY = 5,    /* pe_pack: the token count exceeds `capacity` */
   PE_ERR_WORKSPACE = 6,   /* workspace NULL or smaller than required */
   PE_ERR_HIP = 7,         /* a HIP runtime call or kernel launch failed */

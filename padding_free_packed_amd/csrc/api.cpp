@@ -6,11 +6,35 @@
 #include <climits>
 #include <cmath>
 #include <cstdint>
+#include <cstdlib>
 
 #include "kernels.h"
 #include "pe.h"
 
 namespace {
+
+// Checked mode: with PE_CHECK=1 in the environment, every attention call first
+// checks cu_seqlens on the device and waits for the answer; on a violation it
+// returns PE_ERR_LENGTHS with nothing else launched. A debugging aid: it
+// synchronizes the stream (so it cannot be captured in a graph), and calls that
+// overlap on one device share the flag.
+__device__ int32_t g_check_flag;
+
+bool check_mode() {
+  const char* e = std::getenv("PE_CHECK");
+  return e != nullptr && e[0] == '1' && e[1] == '\0';
+}
+
+pe_status check_cu(const int32_t* cu, int32_t B, int64_t N, int32_t S, hipStream_t st) {
+  if (!check_mode()) return PE_OK;
+  int32_t* flag = nullptr;
+  if (hipGetSymbolAddress(reinterpret_cast<void**>(&flag), HIP_SYMBOL(g_check_flag)) != hipSuccess) return PE_ERR_HIP;
+  if (pe::launch_check_cu(cu, B, N, S, flag, st) != hipSuccess) return PE_ERR_HIP;
+  int32_t h = 0;
+  if (hipMemcpyAsync(&h, flag, sizeof h, hipMemcpyDeviceToHost, st) != hipSuccess) return PE_ERR_HIP;
+  if (hipStreamSynchronize(st) != hipSuccess) return PE_ERR_HIP;
+  return h ? PE_ERR_LENGTHS : PE_OK;
+}
 
 constexpr size_t kAlign = 256;
 
@@ -179,6 +203,7 @@ pe_status fwd_impl(const void* q, const void* k, const void* v, const int32_t* c
   if (!workspace || workspace_bytes < pe_attn_workspace_size(num_seqs, total_tokens, num_heads, head_dim, dtype, 0))
     return PE_ERR_WORKSPACE;
   hipStream_t st = as_stream(stream);
+  if (const pe_status c = check_cu(cu_seqlens, num_seqs, total_tokens, max_seq_len, st); c != PE_OK) return c;
   int32_t* items = static_cast<int32_t*>(workspace);
   if (dtype == PE_FP32 && pe::attn_f32_wave_supported(head_dim, ld, num_heads)) {
     hipError_t e = pe::launch_seq_worklist(cu_seqlens, num_seqs, total_tokens, pe::kAttnWaveRows, items, st);
@@ -238,6 +263,8 @@ pe_status first_impl(const void* q, int32_t gather, const void* k, const void* v
   for (const void* p : {q, k, v, static_cast<const void*>(cu_seqlens), static_cast<const void*>(out_first),
                         static_cast<const void*>(lse_first)})
     if (p && !aligned16(p)) return PE_ERR_ARG;
+  if (const pe_status c = check_cu(cu_seqlens, num_seqs, total_tokens, max_seq_len, as_stream(stream)); c != PE_OK)
+    return c;
   return hip_status(pe::launch_attn_fwd_first(dtype, head_dim, q, k, v, cu_seqlens, num_seqs,
                                               static_cast<int32_t>(total_tokens), num_heads, max_seq_len, gather,
                                               static_cast<int64_t>(num_heads) * head_dim, softmax_scale, out_first,
@@ -279,6 +306,8 @@ pe_status pe_varlen_attn_bwd_first_token(const void* dout_first, const void* q_f
                         static_cast<const void*>(cu_seqlens), static_cast<const void*>(dq_first),
                         static_cast<const void*>(dk), static_cast<const void*>(dv)})
     if (!aligned16(p)) return PE_ERR_ARG;
+  if (const pe_status c = check_cu(cu_seqlens, num_seqs, total_tokens, max_seq_len, as_stream(stream)); c != PE_OK)
+    return c;
   return hip_status(pe::launch_attn_bwd_first(dtype, head_dim, dout_first, q_first, k, v, out_first,
                                               lse_first, cu_seqlens, num_seqs, static_cast<int32_t>(total_tokens),
                                               num_heads, max_seq_len, static_cast<int64_t>(num_heads) * head_dim,
@@ -308,6 +337,7 @@ pe_status bwd_impl(const void* dout, const void* q, const void* k, const void* v
   if (!workspace || workspace_bytes < pe_attn_workspace_size(num_seqs, total_tokens, num_heads, head_dim, dtype, 1))
     return PE_ERR_WORKSPACE;
   hipStream_t st = as_stream(stream);
+  if (const pe_status c = check_cu(cu_seqlens, num_seqs, total_tokens, max_seq_len, st); c != PE_OK) return c;
   int32_t* items = static_cast<int32_t*>(workspace);
   const size_t ib = items_bytes(num_seqs, total_tokens);
   int32_t* items32 = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + ib);

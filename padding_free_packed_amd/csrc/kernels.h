@@ -106,6 +106,9 @@ hipError_t launch_attn_bwd(int dt, int D, const void* dout, const void* q, const
                            int32_t win, int64_t ld, float scale, void* dq, void* dk, void* dv, float* delta,
                            hipStream_t stream);
 
+// checked mode (meta.hip): flag[0] = 1 if cu[0] != 0, a length is outside [1, S] or cu[B] > N
+hipError_t launch_check_cu(const int32_t* cu, int32_t B, int64_t N, int32_t S, int32_t* flag, hipStream_t stream);
+
 // packing metadata (meta.hip)
 hipError_t launch_ids(const int32_t* cu, int32_t B, int64_t N, int64_t* pos, int32_t* doc, hipStream_t stream);
 size_t flatten_workspace_bytes(int32_t rows);

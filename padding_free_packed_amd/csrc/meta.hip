@@ -10,6 +10,31 @@
 
 namespace pe {
 
+// ---------------------------------------------------------------- checked mode
+// One workgroup: flag[0] = 1 unless cu[0] == 0, every length cu[b+1] - cu[b] lies
+// in [1, S] and cu[B] <= N (the contract the attention kernels assume), else 0.
+// Reads cu[0..B] only; the flag is one vector store by thread 0.
+__global__ __launch_bounds__(1024) void check_cu_kernel(const int32_t* __restrict__ cu, int32_t B, int64_t N,
+                                                        int32_t S, int32_t* __restrict__ flag) {
+  __shared__ int bad;
+  if (threadIdx.x == 0) bad = (cu[0] != 0 || static_cast<int64_t>(cu[B]) > N) ? 1 : 0;
+  __syncthreads();
+  int mine = 0;
+  for (int64_t i = threadIdx.x; i < B; i += blockDim.x) {
+    const int32_t L = cu[i + 1] - cu[i];
+    mine |= (L < 1) | (L > S);
+  }
+  if (mine) bad = 1;  // every writer stores the same value
+  __syncthreads();
+  if (threadIdx.x == 0) flag[0] = bad;
+}
+
+hipError_t launch_check_cu(const int32_t* cu, int32_t B, int64_t N, int32_t S, int32_t* flag, hipStream_t stream) {
+  hipLaunchKernelGGL(check_cu_kernel, dim3(1), dim3(1024), 0, stream, cu, B, N, S, flag);
+  return hipGetLastError();
+}
+
+
 namespace {
 
 // ---------------------------------------------------------------- position / document ids
