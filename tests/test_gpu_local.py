@@ -115,3 +115,10 @@ def test_local_backward_edge_lengths(dtype, d, window):
 def test_local_backward_generic_head_dims():
     check_local_bwd(W.custom(71, EDGE[:12], 300, 2, 16, W.FP32, with_grad=True), 7, "fp32 d=16")
     check_local_bwd(W.custom(72, EDGE[:12], 300, 2, 128, W.BF16, with_grad=True), 7, "bf16 d=128")
+
+
+@pytest.mark.parametrize("dtype", [W.FP32, W.BF16])
+def test_local_backward_long_sequences(dtype):
+    # an 8192-token document among shorter ones: the banded tiles run across many key blocks
+    L = [2188, 17, 8192, 368, 1, 16, 1000, 129]
+    check_local_bwd(W.custom(73, L, 8192, 2, 64, dtype, with_grad=True), 32, "long sequences d=64")
