@@ -67,6 +67,7 @@ def check_bwd(w: W.Workload, label: str, seqs=None):
     ref = oracle.attention_backward(do, q, k, v, cu_ref, w.scale, seqs, out=out_given)
     for name, gtens, r in zip(("dq", "dk", "dv"), (dq, dk, dv), ref):
         check_grad(to_f64(gtens)[rows], r[rows], w.dtype, f"{label} {name}")
+    return cu_ref, dq, dk, dv
 
 
 def test_tiny():
@@ -139,3 +140,31 @@ def test_graph_transformer_full_size():
     seqs = sorted({int(order[0]), int(order[-1]), int(order[len(L) // 2]), 0, 1, len(L) - 1} |
                   set(int(x) for x in np.random.default_rng(5).integers(0, len(L), size=24)))
     check_bwd(w, "graph-transformer full size", seqs=seqs)
+
+
+@pytest.mark.parametrize("dtype", [W.FP32, W.BF16])
+def test_very_long_sequence(dtype):
+    """A 40000-token document (313 query tiles and 1250 key blocks of its own)
+    among shorter sequences. The forward is checked at sampled rows, the
+    backward in full on the other sequences and, on the long document, through
+    two sums that hold at any length: each row of P sums to 1, so the dV rows
+    sum to the dO rows; each row of dS sums to 0 (D is <dO, O> with O = P V), so
+    the dK rows sum to 0."""
+    from tests.test_gpu_fwd import check_sampled
+
+    w = W.custom(95, [40000, 3, 1, 6000, 777], 40000, 2, 64, dtype, with_grad=True)
+    label = f"40000-token document {dtype}"
+    check_sampled(w, label)
+    cu_ref, dq, dk, dv = check_bwd(w, label, seqs=[1, 2, 3, 4])
+    c0, c1 = int(cu_ref[0]), int(cu_ref[1])
+    do = W.to_f64(w.dout, w.dtype)[c0:c1]
+    gdv, gdk = to_f64(dv)[c0:c1], to_f64(dk)[c0:c1]
+    assert np.isfinite(gdv).all() and np.isfinite(gdk).all() and np.isfinite(to_f64(dq)[c0:c1]).all()
+    # bf16: P enters the dV product rounded to bf16 (2^-9 of each weight) and dV is stored in bf16
+    rel = 2.0 ** -8 if dtype == W.BF16 else 1e-5
+    err_v = np.abs(gdv.sum(axis=0) - do.sum(axis=0))
+    assert (err_v <= rel * (np.abs(gdv).sum(axis=0) + np.abs(do).sum(axis=0))).all(), \
+        f"sum of dV rows vs sum of dO rows: max |delta| {err_v.max():.3e}"
+    if dtype == W.FP32:
+        err_k = np.abs(gdk.sum(axis=0))
+        assert (err_k <= 1e-4 * np.abs(gdk).sum(axis=0)).all(), f"sum of dK rows: max {err_k.max():.3e}"
