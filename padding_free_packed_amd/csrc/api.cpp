@@ -189,6 +189,14 @@ size_t pe_attn_workspace_size(int32_t num_seqs, int64_t total_tokens, int32_t nu
 namespace {
 
 // The forward for every entry point: win is the local-attention radius, or -1.
+// The 16-bit forward that runs with two 64-row waves per block takes the
+// sequence-aligned work list of kAttnTileRows-row tiles; every other non-fp32
+// forward takes the plain 128-row list.
+bool fwd_w64(pe_dtype dtype, int32_t head_dim, int32_t max_seq_len) {
+  return dtype != PE_FP32 && pe::attn_fwd_bf16_supported(head_dim, max_seq_len) &&
+         pe::attn_fwd_bf16_w64_supported(head_dim);
+}
+
 pe_status fwd_impl(const void* q, const void* k, const void* v, const int32_t* cu_seqlens, int32_t num_seqs,
                    int64_t total_tokens, int32_t max_seq_len, int32_t num_heads, int32_t head_dim, pe_dtype dtype,
                    float softmax_scale, int32_t win, int64_t ld, void* out, float* lse, void* workspace,
@@ -212,7 +220,10 @@ pe_status fwd_impl(const void* q, const void* k, const void* v, const int32_t* c
                                                    static_cast<int32_t>(total_tokens), num_heads, win, ld,
                                                    softmax_scale, out, lse, st));
   }
-  hipError_t e = pe::launch_worklist(cu_seqlens, num_seqs, total_tokens, pe::kAttnTileRows, items, st);
+  hipError_t e =
+      fwd_w64(dtype, head_dim, max_seq_len)
+          ? pe::launch_seq_worklist(cu_seqlens, num_seqs, total_tokens, pe::kAttnTileRows, items, st)
+          : pe::launch_worklist(cu_seqlens, num_seqs, total_tokens, pe::kAttnTileRows, items, st);
   if (e != hipSuccess) return PE_ERR_HIP;
   e = pe::launch_attn_fwd(dtype, head_dim, q, k, v, cu_seqlens, items, num_seqs,
                           static_cast<int32_t>(total_tokens), num_heads, max_seq_len, win, ld, softmax_scale, out,
@@ -541,10 +552,11 @@ namespace {
 // kPlanMaxEntries the separate multi-block kernels are faster than one workgroup
 // (measured per replay: 2-3 us gained up to ~8k entries, even at ~16k, 4.5 us lost at ~33k).
 constexpr int64_t kPlanMaxEntries = 1 << 14;
-int64_t plan_entries(int32_t num_seqs, int64_t cap, int64_t rowbytes, bool wave) {
+int64_t plan_entries(int32_t num_seqs, int64_t cap, int64_t rowbytes, bool wave, bool w64) {
   const int64_t np = std::max(ceil_div(cap, pe::pack_tile_rows(rowbytes)), static_cast<int64_t>(num_seqs));
-  const int64_t na = wave ? cap / pe::kAttnWaveRows + num_seqs
-                          : std::max(ceil_div(cap, pe::kAttnTileRows), static_cast<int64_t>(num_seqs));
+  const int64_t na = wave  ? cap / pe::kAttnWaveRows + num_seqs
+                     : w64 ? cap / pe::kAttnTileRows + num_seqs
+                           : std::max(ceil_div(cap, pe::kAttnTileRows), static_cast<int64_t>(num_seqs));
   return np + na;
 }
 
@@ -591,8 +603,9 @@ pe_status pe_forward_graph_create(const int32_t* lengths, int32_t num_seqs, int3
   }
   pe_status s = PE_OK;
   const bool wave = dtype == PE_FP32 && pe::attn_f32_wave_supported(head_dim, 3 * hd, num_heads);
+  const bool w64 = !wave && fwd_w64(dtype, head_dim, max_seq_len);
   const int64_t rowbytes = 3 * hd * elem_bytes(dtype);
-  if (plan_entries(num_seqs, cap, rowbytes, wave) <= kPlanMaxEntries) {
+  if (plan_entries(num_seqs, cap, rowbytes, wave, w64) <= kPlanMaxEntries) {
     // Four kernels: plan (scan + both work lists), pack, attention, unpack. The work lists sit
     // where pe_pack_async and the attention calls put them in the same workspace.
     const int32_t rp = pe::pack_tile_rows(rowbytes);
@@ -603,7 +616,7 @@ pe_status pe_forward_graph_create(const int32_t* lengths, int32_t num_seqs, int3
     const int32_t win = window < 0 ? -1 : effective_window(window, max_seq_len);
     const int32_t n = static_cast<int32_t>(cap);
     hipError_t e = pe::launch_plan(lengths, num_seqs, max_seq_len, cap, cu_seqlens, status, rp, items_p,
-                                   wave ? pe::kAttnWaveRows : pe::kAttnTileRows, wave, items_a, cs);
+                                   wave ? pe::kAttnWaveRows : pe::kAttnTileRows, wave || w64, items_a, cs);
     if (e == hipSuccess)
       e = pe::launch_pack_rows(qkv_grid, qkv_packed, nullptr, cu_seqlens, items_p, num_seqs, max_seq_len, rowbytes,
                                cap, rp, cs);

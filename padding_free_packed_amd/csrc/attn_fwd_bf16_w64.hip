@@ -1,8 +1,13 @@
 // bf16 forward for head dims 32 and 64 with 64 query rows per wave.
 //
-// Work items are the usual ones (a head and 128 consecutive packed query rows
-// per block, blocks mapped XCD-aware), but a block has two waves and each wave
-// owns two 32-row query blocks. Every K or V operand a wave reads from LDS
+// A block takes a head and up to 128 query rows of ONE sequence: slot t of the
+// sequence-aligned work list (launch_seq_worklist with tile height 128) belongs
+// to the sequence b = items[t] and covers its rows from
+// cu[b] + 128 * (t - cu[b] / 128 - b); slots past a sequence's end exit at
+// once. Every row of a block then has the same key range, no key block of a
+// neighbouring sequence is staged, and only a sequence's last key block needs a
+// mask. Blocks are mapped XCD-aware. A block has two waves and each wave owns
+// two 32-row query blocks. Every K or V operand a wave reads from LDS
 // therefore feeds two MFMAs instead of one: on gfx950 the LDS instruction rate
 // (about one wave-wide ds_read per 7 cycles per CU, whatever its width) is
 // otherwise the limit of the d=64 attention loop, ahead of the matrix core.
@@ -52,23 +57,28 @@ __global__ __launch_bounds__(kW64Threads) __attribute__((amdgpu_waves_per_eu(2))
   constexpr int NL = kW64Keys * CH / kW64Threads;  // DMA instructions per thread per tile
   static_assert(NL >= 1 && (kW64Keys * CH) % kW64Threads == 0, "whole DMA instructions per tile");
   __shared__ __align__(16) char ring[kW64Stages][2][TB];  // [stage][K, V][tile]
-  __shared__ int32_t cul[kAttnTileRows + 2];
 
   const int lin = xcd_remap(blockIdx.x, gridDim.x);
   const int h = lin / T, t = lin - h * T;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, ql = lane & 31, g = lane >> 5;
 
-  const TileSpan sp = tile_span<kW64Threads>(cu, items, t, B, N, cul);
-  if (sp.rend <= sp.r0) return;  // block-uniform: no rows in this tile
+  // sequence-aligned tile: slot t of sequence b covers rows r0 .. r0 + 127 of it
+  const int b = items[t];
+  if (b >= B) return;  // block-uniform: a slot past the last sequence
+  const int lo = cu[b], hi = cu[b + 1];
+  const int r0 = lo + (t - (lo / kAttnTileRows + b)) * kAttnTileRows;
+  if (r0 >= hi) return;  // block-uniform: an empty slot at the end of the sequence
+  const int rend = min(r0 + kAttnTileRows, hi);
   int qrow[2], qk0[2], qk1[2], bk0[2], bk1[2], mk0[2], mk1[2];
   bool qvalid[2];
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
-    qrow[qb] = sp.r0 + wv * 64 + 32 * qb + ql;
-    qvalid[qb] = qrow[qb] < sp.rend;
+    qrow[qb] = r0 + wv * 64 + 32 * qb + ql;
+    qvalid[qb] = qrow[qb] < rend;
     qk0[qb] = qk1[qb] = 0;
     if (qvalid[qb]) {
-      own_range(cul, sp.ncu, qrow[qb], qk0[qb], qk1[qb]);
+      qk0[qb] = lo;
+      qk1[qb] = hi;
       band_limit(qrow[qb], win, qk0[qb], qk1[qb]);
     }
     // wave-uniform bounds (scalar registers, so the per-block tests are scalar branches)
@@ -78,8 +88,8 @@ __global__ __launch_bounds__(kW64Threads) __attribute__((amdgpu_waves_per_eu(2))
     mk1[qb] = __builtin_amdgcn_readfirstlane(wave_min_i(qvalid[qb] ? qk1[qb] : INT_MAX));
   }
   // keys of the tile: those of its sequences, and within win of its rows for local attention
-  const int klo = __builtin_amdgcn_readfirstlane(win >= 0 ? max(sp.lo, sp.r0 - win) : sp.lo);
-  const int khi = __builtin_amdgcn_readfirstlane(win >= 0 ? min(sp.hi, sp.rend + win) : sp.hi);
+  const int klo = __builtin_amdgcn_readfirstlane(win >= 0 ? max(lo, r0 - win) : lo);
+  const int khi = __builtin_amdgcn_readfirstlane(win >= 0 ? min(hi, rend + win) : hi);
 
   vec8<Et> qr[2][QS];
 #pragma unroll
@@ -277,7 +287,7 @@ template <typename Et, int D>
 hipError_t dispatch_w64(const void* q, const void* k, const void* v, const int32_t* cu, const int32_t* items,
                         int32_t B, int32_t N, int32_t H, int32_t win, int64_t ld, float scale, void* out,
                         float* lse, hipStream_t stream) {
-  const int T = (N + kAttnTileRows - 1) / kAttnTileRows;
+  const int T = N / kAttnTileRows + B;  // sequence-aligned slots
   const int64_t blocks = static_cast<int64_t>(T) * H;
   if (blocks == 0) return hipSuccess;
   const float c = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);

@@ -41,7 +41,9 @@ hipError_t launch_pack_rows(const void* grid, void* packed, int64_t* flat_index,
 hipError_t launch_unpack_rows(const void* packed, void* grid, const int32_t* cu, int32_t B, int32_t S,
                               int64_t rowbytes, hipStream_t stream);
 
-// Forward over tiles of kAttnTileRows packed query rows; items from launch_worklist.
+// Forward over tiles of kAttnTileRows packed query rows; items from launch_worklist,
+// except where attn_fwd_bf16_w64_supported selects the 64-row-wave kernel: then
+// items is the sequence-aligned list (launch_seq_worklist) with tile height kAttnTileRows.
 // dt: kDtF32, kDtBF16 or kDtF16 (every attention launcher takes it).
 hipError_t launch_attn_fwd(int dt, int D, const void* q, const void* k, const void* v,
                            const int32_t* cu, const int32_t* items, int32_t B, int32_t N, int32_t H,
@@ -50,7 +52,7 @@ hipError_t launch_attn_fwd(int dt, int D, const void* q, const void* k, const vo
 
 // 16-bit forward with LDS-DMA staging (head dims 32, 64, 128); f16 selects fp16 over bf16.
 bool attn_fwd_bf16_supported(int D, int max_seq_len);
-// the same items with two 64-row waves per block (head dims 32, 64)
+// two 64-row waves per block over sequence-aligned 128-row tiles (head dims 32, 64)
 bool attn_fwd_bf16_w64_supported(int D);
 hipError_t launch_attn_fwd_bf16_w64(bool f16, int D, const void* q, const void* k, const void* v, const int32_t* cu,
                                     const int32_t* items, int32_t B, int32_t N, int32_t H, int32_t win, int64_t ld,
