@@ -143,46 +143,84 @@ def _finish(name, dtype, rng, lengths, S, H, d, grid, names):
 
 
 # The five standing workloads. Numbers in the names are those of the list of
-# configurations this library is measured on.
+# configurations this library is measured on. Each draws its lengths first from
+# its own seed (so `standing_lengths` gives the same lengths without drawing any
+# tensor), then its grid and tensors.
+
+def _lengths_tiny(rng):
+    return rng.integers(1, 65, size=8)
+
+
+def _lengths_graph_transformer(rng):
+    return np.clip(np.rint(rng.normal(90.0, 40.0, size=4096)), 1, 256).astype(np.int64)
+
+
+def _lengths_short_query(rng):
+    return rng.integers(8, 49, size=32768)
+
+
+def _lengths_long_document(rng):
+    return np.clip(np.rint(rng.lognormal(np.log(512.0), 0.8, size=1024)), 64, 8192).astype(np.int64)
+
+
+def _lengths_mixed_training(rng):
+    queries = rng.integers(16, 49, size=2048)
+    docs = np.clip(np.rint(rng.lognormal(np.log(1024.0), 0.7, size=256)), 128, 8192).astype(np.int64)
+    return rng.permutation(np.concatenate([queries, docs]))
+
+
+# name: (seed, lengths, S, H, d, dtype, has a padded grid, carries dO)
+SPECS = {
+    "tiny": (0, _lengths_tiny, 64, 2, 8, FP32, True, True),
+    "graph_transformer": (1, _lengths_graph_transformer, 256, 8, 64, FP32, True, True),
+    "short_query": (2, _lengths_short_query, 48, 12, 64, BF16, True, False),
+    "long_document": (3, _lengths_long_document, 8192, 12, 64, BF16, False, False),
+    "mixed_training": (4, _lengths_mixed_training, 8192, 16, 64, BF16, False, True),
+}
+
+
+def _standing(name, grid=None, with_grad=None):
+    seed, draw, S, H, d, dtype, g, grad = SPECS[name]
+    rng = np.random.default_rng(seed)
+    lengths = draw(rng)
+    g = g if grid is None else grid
+    grad = grad if with_grad is None else with_grad
+    names = ("q", "k", "v", "dout") if grad else ("q", "k", "v")
+    return _finish(name, dtype, rng, lengths, S, H, d, g, names)
+
+
+def standing_lengths(name) -> Workload:
+    """The standing workload `name` with its lengths, shape and scale but no tensors
+    (the same lengths as the full workload: they are drawn first from its seed)."""
+    seed, draw, S, H, d, dtype, _, _ = SPECS[name]
+    lengths = np.asarray(draw(np.random.default_rng(seed)), dtype=np.int32)
+    return Workload(name, dtype, lengths, S, H, d, float(np.float32(1.0 / np.sqrt(d))))
+
 
 def tiny(with_grad: bool = True) -> Workload:
     """8 sequences, lengths uniform in [1, 64], S = 64, 2 heads x 8, fp32, grid [8, 64, 16]."""
-    rng = np.random.default_rng(0)
-    lengths = rng.integers(1, 65, size=8)
-    names = ("q", "k", "v", "dout") if with_grad else ("q", "k", "v")
-    return _finish("tiny", FP32, rng, lengths, 64, 2, 8, True, names)
+    return _standing("tiny", with_grad=with_grad)
 
 
 def graph_transformer(grid: bool = True, with_grad: bool = True) -> Workload:
     """4096 sequences, lengths round(N(90, 40)) clipped to [1, 256], S = 256, 8 x 64, fp32."""
-    rng = np.random.default_rng(1)
-    lengths = np.clip(np.rint(rng.normal(90.0, 40.0, size=4096)), 1, 256).astype(np.int64)
-    names = ("q", "k", "v", "dout") if with_grad else ("q", "k", "v")
-    return _finish("graph_transformer", FP32, rng, lengths, 256, 8, 64, grid, names)
+    return _standing("graph_transformer", grid=grid, with_grad=with_grad)
 
 
 def short_query(grid: bool = True) -> Workload:
     """32768 sequences, lengths uniform in [8, 48], S = 48, 12 x 64, bf16."""
-    rng = np.random.default_rng(2)
-    lengths = rng.integers(8, 49, size=32768)
-    return _finish("short_query", BF16, rng, lengths, 48, 12, 64, grid, ("q", "k", "v"))
+    return _standing("short_query", grid=grid)
 
 
 def long_document() -> Workload:
     """1024 sequences, lengths round(lognormal(ln 512, 0.8)) clipped to [64, 8192], S = 8192, 12 x 64, bf16."""
-    rng = np.random.default_rng(3)
-    lengths = np.clip(np.rint(rng.lognormal(np.log(512.0), 0.8, size=1024)), 64, 8192).astype(np.int64)
-    return _finish("long_document", BF16, rng, lengths, 8192, 12, 64, False, ("q", "k", "v"))
+    return _standing("long_document")
 
 
 def mixed_training() -> Workload:
     """2048 queries U[16, 48] + 256 documents round(lognormal(ln 1024, 0.7)) clipped to [128, 8192],
     shuffled together, S = 8192, 16 x 64, bf16, with dO for the backward."""
-    rng = np.random.default_rng(4)
-    queries = rng.integers(16, 49, size=2048)
-    docs = np.clip(np.rint(rng.lognormal(np.log(1024.0), 0.7, size=256)), 128, 8192).astype(np.int64)
-    lengths = rng.permutation(np.concatenate([queries, docs]))
-    return _finish("mixed_training", BF16, rng, lengths, 8192, 16, 64, False, ("q", "k", "v", "dout"))
+    return _standing("mixed_training")
 
 
 def short_batch(num_seqs: int = 64) -> Workload:
@@ -233,6 +271,33 @@ STANDING = {
     "long_document": long_document,
     "mixed_training": mixed_training,
 }
+
+
+def device_inputs(w: Workload, device, seed: int, grid: bool = False, with_grad: bool = False) -> dict:
+    """Q, K, V (and dO, and the padded grid [B, S, D] with NaN padding) of the
+    shape and dtype of `w`, drawn on the device by torch's seeded generator:
+    N(0, 1) fp32 values rounded to nearest-even in the workload's dtype. Same
+    shapes and distributions as the host recipe above, not the same values; for
+    timing runs, where drawing the host arrays would take minutes."""
+    import torch
+
+    dt = {FP32: torch.float32, BF16: torch.bfloat16, FP16: torch.float16}[w.dtype]
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed)
+    N, H, d, B, S = w.total_tokens, w.num_heads, w.head_dim, w.num_seqs, w.max_seq_len
+
+    def draw(shape):
+        return torch.randn(shape, generator=gen, device=device, dtype=torch.float32).to(dt)
+
+    out = {}
+    if grid:
+        g = draw((B, S, H * d))
+        pad = torch.arange(S, device=device)[None, :] >= torch.from_numpy(w.lengths).to(device)[:, None]
+        g[pad] = float("nan")
+        out["grid"] = g
+    for nm in (("q", "k", "v", "dout") if with_grad else ("q", "k", "v")):
+        out[nm] = draw((N, H, d))
+    return out
 
 
 def custom(seed: int, lengths, max_seq_len: int, num_heads: int, head_dim: int, dtype: str,
