@@ -40,8 +40,9 @@
  *   fp32 because inference needs it). PE_BF16 reads and writes bf16 and
  *   accumulates in fp32; the probabilities are rounded to bf16 before they
  *   multiply V. Log-sum-exp values are always fp32.
- * - Supported head_dim: 8, 16, 32, 64, 128 (the GiGL page requires a multiple
- *   of 8 for its aligned kernels).
+ * - Supported head_dim: every multiple of 8 from 8 to 128 (the GiGL page's
+ *   "Constraints" require a multiple of 8). Any other head_dim returns
+ *   PE_ERR_UNSUPPORTED before anything is launched.
  */
 #ifndef PE_H
 #define PE_H

@@ -42,7 +42,7 @@ size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-bool supported_head_dim(int32_t d) { return d == 8 || d == 16 || d == 32 || d == 64 || d == 128; }
+bool supported_head_dim(int32_t d) { return pe::head_dim_supported(d); }
 
 bool valid_dtype(int dt) { return dt == PE_FP32 || dt == PE_BF16 || dt == PE_FP16; }
 
@@ -188,14 +188,16 @@ size_t pe_attn_workspace_size(int32_t num_seqs, int64_t total_tokens, int32_t nu
 
 namespace {
 
-// The forward for every entry point: win is the local-attention radius, or -1.
-// The 16-bit forward that runs with two 64-row waves per block takes the
-// sequence-aligned work list of kAttnTileRows-row tiles; every other non-fp32
-// forward takes the plain 128-row list.
-bool fwd_w64(pe_dtype dtype, int32_t head_dim, int32_t max_seq_len) {
-  return dtype != PE_FP32 && pe::attn_fwd_bf16_supported(head_dim, max_seq_len) &&
-         pe::attn_fwd_bf16_w64_supported(head_dim);
+// The work list of a forward (the one pe::attn_fwd_list names), built on `st`.
+hipError_t build_fwd_list(pe::FwdList kind, const int32_t* cu, int32_t B, int64_t N, int32_t* items, hipStream_t st) {
+  switch (kind) {
+    case pe::kFwdListSeq32: return pe::launch_seq_worklist(cu, B, N, pe::kAttnWaveRows, items, st);
+    case pe::kFwdListSeq128: return pe::launch_seq_worklist(cu, B, N, pe::kAttnTileRows, items, st);
+    default: return pe::launch_worklist(cu, B, N, pe::kAttnTileRows, items, st);
+  }
 }
+
+// The forward for every entry point: win is the local-attention radius, or -1.
 
 pe_status fwd_impl(const void* q, const void* k, const void* v, const int32_t* cu_seqlens, int32_t num_seqs,
                    int64_t total_tokens, int32_t max_seq_len, int32_t num_heads, int32_t head_dim, pe_dtype dtype,
@@ -213,17 +215,8 @@ pe_status fwd_impl(const void* q, const void* k, const void* v, const int32_t* c
   hipStream_t st = as_stream(stream);
   if (const pe_status c = check_cu(cu_seqlens, num_seqs, total_tokens, max_seq_len, st); c != PE_OK) return c;
   int32_t* items = static_cast<int32_t*>(workspace);
-  if (dtype == PE_FP32 && pe::attn_f32_wave_supported(head_dim, ld, num_heads)) {
-    hipError_t e = pe::launch_seq_worklist(cu_seqlens, num_seqs, total_tokens, pe::kAttnWaveRows, items, st);
-    if (e != hipSuccess) return PE_ERR_HIP;
-    return hip_status(pe::launch_attn_fwd_f32_wave(head_dim, q, k, v, cu_seqlens, items, num_seqs,
-                                                   static_cast<int32_t>(total_tokens), num_heads, win, ld,
-                                                   softmax_scale, out, lse, st));
-  }
-  hipError_t e =
-      fwd_w64(dtype, head_dim, max_seq_len)
-          ? pe::launch_seq_worklist(cu_seqlens, num_seqs, total_tokens, pe::kAttnTileRows, items, st)
-          : pe::launch_worklist(cu_seqlens, num_seqs, total_tokens, pe::kAttnTileRows, items, st);
+  hipError_t e = build_fwd_list(pe::attn_fwd_list(dtype, head_dim, max_seq_len, ld, num_heads), cu_seqlens,
+                                num_seqs, total_tokens, items, st);
   if (e != hipSuccess) return PE_ERR_HIP;
   e = pe::launch_attn_fwd(dtype, head_dim, q, k, v, cu_seqlens, items, num_seqs,
                           static_cast<int32_t>(total_tokens), num_heads, max_seq_len, win, ld, softmax_scale, out,
@@ -602,8 +595,9 @@ pe_status pe_forward_graph_create(const int32_t* lengths, int32_t num_seqs, int3
     return PE_ERR_HIP;
   }
   pe_status s = PE_OK;
-  const bool wave = dtype == PE_FP32 && pe::attn_f32_wave_supported(head_dim, 3 * hd, num_heads);
-  const bool w64 = !wave && fwd_w64(dtype, head_dim, max_seq_len);
+  const pe::FwdList list = pe::attn_fwd_list(dtype, head_dim, max_seq_len, 3 * hd, num_heads);
+  const bool wave = list == pe::kFwdListSeq32;
+  const bool w64 = list == pe::kFwdListSeq128;
   const int64_t rowbytes = 3 * hd * elem_bytes(dtype);
   if (plan_entries(num_seqs, cap, rowbytes, wave, w64) <= kPlanMaxEntries) {
     // Four kernels: plan (scan + both work lists), pack, attention, unpack. The work lists sit
@@ -621,12 +615,8 @@ pe_status pe_forward_graph_create(const int32_t* lengths, int32_t num_seqs, int3
       e = pe::launch_pack_rows(qkv_grid, qkv_packed, nullptr, cu_seqlens, items_p, num_seqs, max_seq_len, rowbytes,
                                cap, rp, cs);
     if (e == hipSuccess)
-      e = wave ? pe::launch_attn_fwd_f32_wave(head_dim, base, base + step, base + 2 * step, cu_seqlens, items_a,
-                                              num_seqs, n, num_heads, win, 3 * hd, softmax_scale, out_packed, lse,
-                                              cs)
-               : pe::launch_attn_fwd(dtype, head_dim, base, base + step, base + 2 * step, cu_seqlens, items_a,
-                                     num_seqs, n, num_heads, max_seq_len, win, 3 * hd, softmax_scale, out_packed,
-                                     lse, cs);
+      e = pe::launch_attn_fwd(dtype, head_dim, base, base + step, base + 2 * step, cu_seqlens, items_a, num_seqs, n,
+                              num_heads, max_seq_len, win, 3 * hd, softmax_scale, out_packed, lse, cs);
     if (e == hipSuccess)
       e = pe::launch_unpack_rows(out_packed, out_grid, cu_seqlens, num_seqs, max_seq_len, hd * elem_bytes(dtype), cs);
     s = hip_status(e);

@@ -26,14 +26,21 @@ namespace pe {
 
 namespace {
 
+// One group of CHP lanes (CH rounded up to a power of two) per (row, head): lane
+// `sub` of the group reads 16-byte chunk `sub` of both head rows (lanes past CH
+// read nothing and add 0), and the group sums by butterfly.
 template <typename Et, int D>
 __global__ __launch_bounds__(256) void bwd_delta_kernel(const void* __restrict__ dout, const void* __restrict__ out,
                                                         int32_t N, int32_t H, float* __restrict__ delta) {
   using G = Geo<Et, D>;
-  const int64_t ch = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;  // 16-byte chunk
-  const int64_t total = static_cast<int64_t>(N) * H * G::CH;
+  constexpr int CHP = pow2_ceil(G::CH);
+  const int64_t idx = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  const int64_t hr = idx / CHP;  // (row, head) pair, row-major over [N, H]
+  const int sub = static_cast<int>(idx - hr * CHP);
+  const int64_t total = static_cast<int64_t>(N) * H;
   float s = 0.f;
-  if (ch < total) {
+  if (hr < total && sub < G::CH) {
+    const int64_t ch = hr * G::CH + sub;
     const uint4 a = *reinterpret_cast<const uint4*>(static_cast<const char*>(dout) + ch * 16);
     const uint4 b = *reinterpret_cast<const uint4*>(static_cast<const char*>(out) + ch * 16);
     if constexpr (kIs16<Et>) {
@@ -46,9 +53,8 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(const void* __restrict__
     }
   }
 #pragma unroll
-  for (int o = 1; o < G::CH; o <<= 1) s += __shfl_xor(s, o);
-  if (ch < total && (ch % G::CH) == 0) {
-    const int64_t hr = ch / G::CH;
+  for (int o = 1; o < CHP; o <<= 1) s += __shfl_xor(s, o);
+  if (hr < total && sub == 0) {
     const int64_t i = hr / H, hh = hr - i * H;
     delta[hh * N + i] = s;
   }
@@ -92,8 +98,8 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(
 
   typename RegT<Et>::type kreg[G::QS], vreg[G::QS];
   const int64_t roff = static_cast<int64_t>(krow) * ld + h * D;  // rows of K, V, dK, dV are ld apart
-  load_row_regs<Et, D>(kp, roff + g * G::HALF, kvalid, kreg);
-  load_row_regs<Et, D>(vp, roff + g * G::HALF, kvalid, vreg);
+  load_row_regs<Et, D>(kp, roff, g, kvalid, kreg);
+  load_row_regs<Et, D>(vp, roff, g, kvalid, vreg);
 
   floatx16 dk[G::DB], dv[G::DB];
 #pragma unroll
@@ -218,8 +224,8 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
 
   typename RegT<Et>::type qreg[G::QS], dreg[G::QS];
   const int64_t roff = static_cast<int64_t>(qrow) * ld + h * D;  // rows of Q and dQ are ld apart
-  load_row_regs<Et, D>(qp, roff + g * G::HALF, qvalid, qreg);
-  load_row_regs<Et, D>(dop, (static_cast<int64_t>(qrow) * H + h) * D + g * G::HALF, qvalid, dreg);
+  load_row_regs<Et, D>(qp, roff, g, qvalid, qreg);
+  load_row_regs<Et, D>(dop, (static_cast<int64_t>(qrow) * H + h) * D, g, qvalid, dreg);
   const float lse2 = qvalid ? lse[static_cast<int64_t>(h) * N + qrow] * kLog2e : 0.f;
   const float dlq = qvalid ? delta[static_cast<int64_t>(h) * N + qrow] : 0.f;
 
@@ -298,9 +304,9 @@ hipError_t bwd_dispatch(const void* dout, const void* q, const void* k, const vo
     return launch_bwd_dkdv_f32_wave(D, dout, q, k, v, lse, delta, cu, items32, B, N, H, win, ld, scale, dk, dv,
                                     stream);
   }
-  const int64_t chunks = static_cast<int64_t>(N) * H * G::CH;
+  const int64_t lanes = static_cast<int64_t>(N) * H * pow2_ceil(G::CH);
   hipEvent_t ev_bwd_delta = timing_start(stream);
-  hipLaunchKernelGGL((bwd_delta_kernel<Et, D>), dim3(static_cast<unsigned>((chunks + 255) / 256)), dim3(256), 0,
+  hipLaunchKernelGGL((bwd_delta_kernel<Et, D>), dim3(static_cast<unsigned>((lanes + 255) / 256)), dim3(256), 0,
                    stream, dout, out, N, H, delta);
   timing_stop("bwd_delta", ev_bwd_delta, stream);
   hipError_t e = hipGetLastError();
@@ -336,11 +342,7 @@ hipError_t launch_attn_bwd(int dt, int D, const void* dout, const void* q, const
                          : bwd_dispatch<__bf16, DD>(dout, q, k, v, out, lse, cu, items, items32, B, N, H, win, ld, \
                                                    scale, dq, dk, dv, delta, stream);
   switch (D) {
-    PE_BWD_CASE(8)
-    PE_BWD_CASE(16)
-    PE_BWD_CASE(32)
-    PE_BWD_CASE(64)
-    PE_BWD_CASE(128)
+    PE_HEAD_DIMS(PE_BWD_CASE)
     default: return hipErrorInvalidValue;
   }
 #undef PE_BWD_CASE

@@ -45,7 +45,17 @@ struct Geo {
   static constexpr int ST = kIs16<Et> ? D + 8 : D + 4;    // LDS row stride in elements
   static constexpr int TSZ = kBlk * ST;            // elements of one staged tile
   static constexpr int HALF = D / 2;               // head-dim elements per lane half
-  static constexpr int QS = kIs16<Et> ? (HALF + 7) / 8 : HALF;  // MFMA steps over head_dim
+  // How the two lane halves split head_dim in an MFMA over it. Normally half g
+  // holds elements g*HALF + 8s .. (16-bit) or g*HALF + s (fp32) at step s. For
+  // 16-bit head dims whose half is not a whole number of 8-element chunks
+  // (24, 40, ..., 120) the split is by chunks instead: half g holds chunk 2s + g
+  // (elements 16s + 8g .. 16s + 8g + 7) at step s, so every operand is one aligned
+  // 16-byte chunk, and the chunk of half 1 past the row at the last step is zero.
+  // A and B operands always use the same split, so the product is unchanged.
+  static constexpr bool CHUNKED = kIs16<Et> && HALF > 8 && HALF % 8 != 0;
+  static constexpr int QS = kIs16<Et> ? (CHUNKED ? (D + 15) / 16 : (HALF + 7) / 8) : HALF;  // MFMA steps
+  static constexpr int GOFF = CHUNKED ? 8 : HALF;  // lane half g starts at element g * GOFF
+  static constexpr int SSTEP = CHUNKED ? 16 : 8;   // elements between the 16-bit steps
   static constexpr int DB = (D + 31) / 32;         // 32-row blocks over head_dim
   static constexpr int TOTCH = kBlk * CH;
   static constexpr int PER = (TOTCH + kThreads - 1) / kThreads;
@@ -73,17 +83,22 @@ __device__ __forceinline__ float xhalf_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// The lane's own head row (elements g*HALF .. g*HALF+HALF-1) as MFMA operands.
+// The lane's share of its own head row as MFMA operands (the split of head_dim
+// between the lane halves described at Geo); row_off is the element offset of
+// the row's first element, g the lane half.
 template <typename Et, int D>
-__device__ __forceinline__ void load_row_regs(const void* base, int64_t off, bool valid,
+__device__ __forceinline__ void load_row_regs(const void* base, int64_t row_off, int g, bool valid,
                                               typename RegT<Et>::type (&r)[Geo<Et, D>::QS]) {
   using G = Geo<Et, D>;
+  const int64_t off = row_off + g * G::GOFF;
   if constexpr (kIs16<Et>) {
     const uint16_t* src = static_cast<const uint16_t*>(base) + off;
 #pragma unroll
     for (int s = 0; s < G::QS; ++s) {
       u16x8 x = {0, 0, 0, 0, 0, 0, 0, 0};
-      if (valid) {
+      if constexpr (G::CHUNKED) {
+        if (valid && (s + 1 < G::QS || g == 0)) x = *reinterpret_cast<const u16x8*>(src + G::SSTEP * s);
+      } else if (valid) {
         if constexpr (G::HALF >= 8) {
           x = *reinterpret_cast<const u16x8*>(src + 8 * s);
         } else {
@@ -142,12 +157,15 @@ __device__ __forceinline__ void mma_rows_regs(const typename Geo<Et, D>::E* tile
                                               const typename RegT<Et>::type (&y)[Geo<Et, D>::QS],
                                               floatx16& acc, int ql, int g) {
   using G = Geo<Et, D>;
-  const typename G::E* xr = tile + (row0 + ql) * G::ST + g * G::HALF;
+  const typename G::E* xr = tile + (row0 + ql) * G::ST + g * G::GOFF;
 #pragma unroll
   for (int st = 0; st < G::QS; ++st) {
     if constexpr (kIs16<Et>) {
       u16x8 a;
-      if constexpr (G::HALF >= 8) {
+      if constexpr (G::CHUNKED) {
+        a = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
+        if (st + 1 < G::QS || g == 0) a = *reinterpret_cast<const u16x8*>(xr + G::SSTEP * st);
+      } else if constexpr (G::HALF >= 8) {
         a = *reinterpret_cast<const u16x8*>(xr + 8 * st);
       } else {
         a = u16x8{0, 0, 0, 0, 0, 0, 0, 0};

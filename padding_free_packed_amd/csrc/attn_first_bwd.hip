@@ -11,6 +11,8 @@
 // once and each dK/dV row written once, fully coalesced. Each slot walks the
 // keys slot, slot + KS, ... in batches of four rows whose loads are issued
 // before any is used; dq partials of the slots merge through LDS at the end.
+// A head row of GS chunks takes GSP lanes (GS rounded up to a power of two, for
+// the butterfly sums); lanes past GS load nothing, add zero and store nothing.
 // No atomics: every output element has exactly one writer.
 #include <algorithm>
 #include <type_traits>
@@ -32,7 +34,8 @@ __global__ __launch_bounds__(kFbThreads) void attn_bwd_first_kernel(
     void* __restrict__ dqp, void* __restrict__ dkp, void* __restrict__ dvp) {
   constexpr int ES = kIs16<Et> ? 2 : 4;
   constexpr int EPC = 16 / ES;  // elements per 16-byte chunk
-  constexpr int GS = D / EPC;   // chunks (threads) per head row
+  constexpr int GS = D / EPC;         // chunks per head row
+  constexpr int GSP = pow2_ceil(GS);  // lanes per head row
   constexpr int U = kFbBatch;
   using Chunk = typename std::conditional<kIs16<Et>, u16x8, float4>::type;
   __shared__ float sq[kFbThreads * EPC];
@@ -40,12 +43,13 @@ __global__ __launch_bounds__(kFbThreads) void attn_bwd_first_kernel(
   const int b = blockIdx.x;
   const int hg = blockIdx.y;
   const int tid = threadIdx.x;
-  const int CPR = HPB * GS;
+  const int CPR = HPB * GSP;
   const int KS = kFbThreads / CPR;
   const int slot = tid / CPR, cidx = tid - slot * CPR;
-  const int hl = cidx / GS, sub = cidx - hl * GS;
+  const int hl = cidx / GSP, sub = cidx - hl * GSP;
   const int h = hg * HPB + hl;
   const bool active = slot < KS && h < H;
+  const bool live = GS == GSP || sub < GS;  // the lane holds a chunk of the row
 
   auto widen = [](const Chunk& x, float (&y)[EPC]) __attribute__((always_inline)) {
     if constexpr (kIs16<Et>) {
@@ -74,14 +78,19 @@ __global__ __launch_bounds__(kFbThreads) void attn_bwd_first_kernel(
     const int64_t hoff = static_cast<int64_t>(h) * D + sub * EPC;
     const int64_t boff = (static_cast<int64_t>(b) * H * D + hoff) * ES;
     float qv[EPC], dov[EPC], ov[EPC];
-    widen(*reinterpret_cast<const Chunk*>(static_cast<const char*>(qf) + boff), qv);
-    widen(*reinterpret_cast<const Chunk*>(static_cast<const char*>(dof) + boff), dov);
-    widen(*reinterpret_cast<const Chunk*>(static_cast<const char*>(of) + boff), ov);
+    if (live) {
+      widen(*reinterpret_cast<const Chunk*>(static_cast<const char*>(qf) + boff), qv);
+      widen(*reinterpret_cast<const Chunk*>(static_cast<const char*>(dof) + boff), dov);
+      widen(*reinterpret_cast<const Chunk*>(static_cast<const char*>(of) + boff), ov);
+    } else {
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) qv[e] = dov[e] = ov[e] = 0.f;
+    }
     float dd = 0.f;
 #pragma unroll
     for (int e = 0; e < EPC; ++e) dd = fmaf(dov[e], ov[e], dd);
 #pragma unroll
-    for (int o = 1; o < GS; o <<= 1) dd += __shfl_xor(dd, o);
+    for (int o = 1; o < GSP; o <<= 1) dd += __shfl_xor(dd, o);
     const float lse2 = lse[static_cast<int64_t>(h) * B + b] * kLog2e;
     const char* kb = static_cast<const char*>(kp) + hoff * ES;
     const char* vb = static_cast<const char*>(vp) + hoff * ES;
@@ -93,8 +102,13 @@ __global__ __launch_bounds__(kFbThreads) void attn_bwd_first_kernel(
 #pragma unroll
       for (int u = 0; u < U; ++u) {  // rows past the sequence re-read its last row and are not stored
         const int j = min(j0 + u * KS, c1 - 1);
-        xk[u] = *reinterpret_cast<const Chunk*>(kb + j * rs);
-        xv[u] = *reinterpret_cast<const Chunk*>(vb + j * rs);
+        if (live) {
+          xk[u] = *reinterpret_cast<const Chunk*>(kb + j * rs);
+          xv[u] = *reinterpret_cast<const Chunk*>(vb + j * rs);
+        } else {
+          __builtin_memset(&xk[u], 0, sizeof(Chunk));
+          __builtin_memset(&xv[u], 0, sizeof(Chunk));
+        }
       }
 #pragma unroll
       for (int u = 0; u < U; ++u) {
@@ -109,11 +123,11 @@ __global__ __launch_bounds__(kFbThreads) void attn_bwd_first_kernel(
           dp = fmaf(dov[e], vv[e], dp);
         }
 #pragma unroll
-        for (int o = 1; o < GS; o <<= 1) {
+        for (int o = 1; o < GSP; o <<= 1) {
           s += __shfl_xor(s, o);
           dp += __shfl_xor(dp, o);
         }
-        if (j < c1) {
+        if (j < c1 && live) {
           const float p = __builtin_amdgcn_exp2f(fmaf(s, c, -lse2));
           const float ds = p * (dp - dd);
           float dk[EPC], dv[EPC];
@@ -132,7 +146,7 @@ __global__ __launch_bounds__(kFbThreads) void attn_bwd_first_kernel(
 #pragma unroll
   for (int e = 0; e < EPC; ++e) sq[tid * EPC + e] = dq[e];
   __syncthreads();
-  if (slot == 0 && h < H) {
+  if (slot == 0 && h < H && live) {
     float acc[EPC];
 #pragma unroll
     for (int e = 0; e < EPC; ++e) acc[e] = 0.f;
@@ -153,7 +167,7 @@ hipError_t bwd_first_dispatch(const void* dof, const void* qf, const void* k, co
                               const float* lse, const int32_t* cu, int32_t B, int32_t N, int32_t H,
                               int32_t max_seq_len, int64_t ld, float scale, void* dq, void* dk, void* dv,
                               hipStream_t stream) {
-  constexpr int GS = D / (kIs16<Et> ? 8 : 4);
+  constexpr int GS = pow2_ceil(D / (kIs16<Et> ? 8 : 4));  // lanes per head row
   // heads per block: as many as leave the key slots the first-token forward takes
   const int HPB0 = std::max(1, std::min<int>(H, kFbThreads / (GS * first_token_slots(max_seq_len))));
   const int HG = (H + HPB0 - 1) / HPB0;
@@ -181,11 +195,7 @@ hipError_t launch_attn_bwd_first(int dt, int D, const void* dout_first, const vo
                          : bwd_first_dispatch<__bf16, DD>(dout_first, q_first, k, v, out_first, lse_first, cu, B, N, \
                                                          H, max_seq_len, ld, scale, dq_first, dk, dv, stream);
   switch (D) {
-    PE_FB_CASE(8)
-    PE_FB_CASE(16)
-    PE_FB_CASE(32)
-    PE_FB_CASE(64)
-    PE_FB_CASE(128)
+    PE_HEAD_DIMS(PE_FB_CASE)
     default: return hipErrorInvalidValue;
   }
 #undef PE_FB_CASE

@@ -79,7 +79,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
   const int wk1 = wave_max_i(qvalid ? qk1 : INT_MIN);
   const int mk0 = wave_max_i(qvalid ? qk0 : INT_MIN);  // keys every row of the wave needs
   const int mk1 = wave_min_i(qvalid ? qk1 : INT_MAX);
-  const int64_t qoff = static_cast<int64_t>(qrow) * ld + g * G::HALF;
+  const int64_t qoff = static_cast<int64_t>(qrow) * ld;
 
   typename RegT<Et>::type qr[G::QS];
   // Q DMA: thread slot j*256 + tid fills LDS chunk position j*256 + tid of the tile, i.e.
@@ -108,7 +108,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
       for (int st = 0; st < G::QS; ++st) qr[st] = swz_read_b128<Et, QCH>(qtile, wv * 32 + ql, g * (QCH / 2) + st);
     }
   };
-  if constexpr (!QDMA) load_row_regs<Et, D>(qp, qoff + h0 * D, qvalid, qr);
+  if constexpr (!QDMA) load_row_regs<Et, D>(qp, qoff + h0 * D, g, qvalid, qr);
 
   uint4 kr[G::PER], vr[G::PER];
   floatx16 o[G::DB];
@@ -226,7 +226,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
     }
     typename RegT<Et>::type qn[G::QS];
     const bool next_head = last && hh + 1 < nh;
-    if (PREFQ && next_head) load_row_regs<Et, D>(qp, qoff + (h0 + hh + 1) * D, qvalid, qn);
+    if (PREFQ && next_head) load_row_regs<Et, D>(qp, qoff + (h0 + hh + 1) * D, g, qvalid, qn);
     block(kb, buf);
     if (last) {
       finish(h0 + hh);
@@ -235,7 +235,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
 #pragma unroll
           for (int st = 0; st < G::QS; ++st) qr[st] = qn[st];
         } else if constexpr (!QDMA) {
-          load_row_regs<Et, D>(qp, qoff + (h0 + hh + 1) * D, qvalid, qr);
+          load_row_regs<Et, D>(qp, qoff + (h0 + hh + 1) * D, g, qvalid, qr);
         }
       }
       ++hh;
@@ -254,7 +254,9 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
 // fully coalesced. Each key slot walks the keys slot, slot + KS, ... in batches
 // of kFirstBatch rows whose loads are all issued before any is used (several
 // HBM round trips in flight per thread), keeps its own running max, sum and
-// output, and the slots merge through LDS at the end.
+// output, and the slots merge through LDS at the end. A head row of GS chunks
+// takes GSP lanes (GS rounded up to a power of two, for the butterfly sums);
+// lanes past GS load nothing, add zero and store nothing.
 constexpr int kFirstThreads = 512;
 
 // Key slots per block of the first-token kernels: few for short sequences (a
@@ -271,7 +273,8 @@ __global__ __launch_bounds__(kFirstThreads) void attn_fwd_first_kernel(
     float c, void* __restrict__ outp, float* __restrict__ lse) {
   constexpr int ES = kIs16<Et> ? 2 : 4;
   constexpr int EPC = 16 / ES;       // elements per 16-byte chunk
-  constexpr int GS = D / EPC;        // chunks (threads) per head row
+  constexpr int GS = D / EPC;        // chunks per head row
+  constexpr int GSP = pow2_ceil(GS);  // lanes per head row
   constexpr int U = kFirstBatch;
   using Chunk = typename std::conditional<kIs16<Et>, u16x8, float4>::type;
   __shared__ float sm[kFirstThreads], sl[kFirstThreads];
@@ -280,12 +283,13 @@ __global__ __launch_bounds__(kFirstThreads) void attn_fwd_first_kernel(
   const int b = blockIdx.x;
   const int hg = blockIdx.y;
   const int tid = threadIdx.x;
-  const int CPR = HPB * GS;
+  const int CPR = HPB * GSP;
   const int KS = kFirstThreads / CPR;
   const int slot = tid / CPR, cidx = tid - slot * CPR;
-  const int hl = cidx / GS, sub = cidx - hl * GS;
+  const int hl = cidx / GSP, sub = cidx - hl * GSP;
   const int h = hg * HPB + hl;
   const bool active = slot < KS && h < H;
+  const bool live = GS == GSP || sub < GS;  // the lane holds a chunk of the row
 
   const int c0 = cu[b], c1 = cu[b + 1];
   float qv[EPC], ov[EPC];
@@ -304,7 +308,12 @@ __global__ __launch_bounds__(kFirstThreads) void attn_fwd_first_kernel(
     const int64_t hoff = static_cast<int64_t>(h) * D + sub * EPC;
     // the query is row b of q_first [B, H, D], or (gather) row cu[b] of the packed Q (rows ld apart)
     const int64_t qoff = gather ? static_cast<int64_t>(c0) * ld : static_cast<int64_t>(b) * H * D;
-    widen(*reinterpret_cast<const Chunk*>(static_cast<const char*>(qf) + (qoff + hoff) * ES), qv);
+    if (live) {
+      widen(*reinterpret_cast<const Chunk*>(static_cast<const char*>(qf) + (qoff + hoff) * ES), qv);
+    } else {
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) qv[e] = 0.f;
+    }
     const char* kb = static_cast<const char*>(kp) + hoff * ES;
     const char* vb = static_cast<const char*>(vp) + hoff * ES;
     const int64_t rs = ld * ES;  // bytes between packed K/V rows
@@ -313,8 +322,13 @@ __global__ __launch_bounds__(kFirstThreads) void attn_fwd_first_kernel(
 #pragma unroll
       for (int u = 0; u < U; ++u) {  // rows past the sequence re-read its last row; their weight is 0
         const int j = min(j0 + u * KS, c1 - 1);
-        xk[u] = *reinterpret_cast<const Chunk*>(kb + j * rs);
-        xv[u] = *reinterpret_cast<const Chunk*>(vb + j * rs);
+        if (live) {
+          xk[u] = *reinterpret_cast<const Chunk*>(kb + j * rs);
+          xv[u] = *reinterpret_cast<const Chunk*>(vb + j * rs);
+        } else {
+          __builtin_memset(&xk[u], 0, sizeof(Chunk));
+          __builtin_memset(&xv[u], 0, sizeof(Chunk));
+        }
       }
       float x[U];
       float bmax = -INFINITY;
@@ -326,7 +340,7 @@ __global__ __launch_bounds__(kFirstThreads) void attn_fwd_first_kernel(
 #pragma unroll
         for (int e = 0; e < EPC; ++e) s = fmaf(qv[e], kv[e], s);
 #pragma unroll
-        for (int o = 1; o < GS; o <<= 1) s += __shfl_xor(s, o);
+        for (int o = 1; o < GSP; o <<= 1) s += __shfl_xor(s, o);
         x[u] = j0 + u * KS < c1 ? s * c : -INFINITY;
         bmax = fmaxf(bmax, x[u]);
       }
@@ -352,7 +366,7 @@ __global__ __launch_bounds__(kFirstThreads) void attn_fwd_first_kernel(
 #pragma unroll
   for (int e = 0; e < EPC; ++e) so[tid * EPC + e] = ov[e];
   __syncthreads();
-  if (slot == 0 && h < H) {
+  if (slot == 0 && h < H && live) {
     float M = kNegBig;
     for (int s2 = 0; s2 < KS; ++s2) M = fmaxf(M, sm[s2 * CPR + cidx]);
     float L = 0.f, acc[EPC];
@@ -403,7 +417,7 @@ template <typename Et, int D>
 hipError_t first_dispatch(const void* q, const void* k, const void* v, const int32_t* cu, int32_t B,
                           int32_t N, int32_t H, int32_t max_seq_len, int32_t gather, int64_t ld, float scale,
                           void* out, float* lse, hipStream_t stream) {
-  constexpr int GS = D / (kIs16<Et> ? 8 : 4);
+  constexpr int GS = pow2_ceil(D / (kIs16<Et> ? 8 : 4));  // lanes per head row
   // heads per block: as many as leave the key slots wanted, then even groups
   const int HPB0 = std::max(1, std::min<int>(H, kFirstThreads / (GS * first_token_slots(max_seq_len))));
   const int HG = (H + HPB0 - 1) / HPB0;
@@ -418,27 +432,34 @@ hipError_t first_dispatch(const void* q, const void* k, const void* v, const int
 
 }  // namespace
 
+FwdList attn_fwd_list(int dt, int D, int max_seq_len, int64_t ld, int32_t H) {
+  if (dt == kDtF32) return attn_f32_wave_supported(D, ld, H) ? kFwdListSeq32 : kFwdListPacked128;
+  return attn_fwd_bf16_supported(D, max_seq_len) && attn_fwd_bf16_w64_supported(D) ? kFwdListSeq128
+                                                                                   : kFwdListPacked128;
+}
+
 hipError_t launch_attn_fwd(int dt, int D, const void* q, const void* k, const void* v,
                            const int32_t* cu, const int32_t* items, int32_t B, int32_t N, int32_t H,
                            int32_t max_seq_len, int32_t win, int64_t ld, float scale, void* out, float* lse,
                            hipStream_t stream) {
   const bool f16 = dt == kDtF16;
-  if (dt != kDtF32 && attn_fwd_bf16_supported(D, max_seq_len)) {
-    if (attn_fwd_bf16_w64_supported(D))
+  switch (attn_fwd_list(dt, D, max_seq_len, ld, H)) {
+    case kFwdListSeq32:
+      return launch_attn_fwd_f32_wave(D, q, k, v, cu, items, B, N, H, win, ld, scale, out, lse, stream);
+    case kFwdListSeq128:
       return launch_attn_fwd_bf16_w64(f16, D, q, k, v, cu, items, B, N, H, win, ld, scale, out, lse, stream);
-    return launch_attn_fwd_bf16(f16, D, q, k, v, cu, items, B, N, H, win, ld, scale, out, lse, stream);
+    case kFwdListPacked128:
+      break;
   }
+  if (dt != kDtF32 && attn_fwd_bf16_supported(D, max_seq_len))
+    return launch_attn_fwd_bf16(f16, D, q, k, v, cu, items, B, N, H, win, ld, scale, out, lse, stream);
 #define PE_FWD_CASE(DD)                                                                                      \
   case DD:                                                                                                  \
     return dt == kDtF32 ? fwd_dispatch<float, DD>(q, k, v, cu, items, B, N, H, win, ld, scale, out, lse, stream) \
            : f16        ? fwd_dispatch<_Float16, DD>(q, k, v, cu, items, B, N, H, win, ld, scale, out, lse, stream) \
                         : fwd_dispatch<__bf16, DD>(q, k, v, cu, items, B, N, H, win, ld, scale, out, lse, stream);
   switch (D) {
-    PE_FWD_CASE(8)
-    PE_FWD_CASE(16)
-    PE_FWD_CASE(32)
-    PE_FWD_CASE(64)
-    PE_FWD_CASE(128)
+    PE_HEAD_DIMS(PE_FWD_CASE)
     default: return hipErrorInvalidValue;
   }
 #undef PE_FWD_CASE
@@ -457,11 +478,7 @@ hipError_t launch_attn_fwd_first(int dt, int D, const void* q_first, const void*
                          : first_dispatch<__bf16, DD>(q_first, k, v, cu, B, N, H, max_seq_len, gather, ld, scale, out_first,    \
                                                      lse_first, stream);
   switch (D) {
-    PE_FIRST_CASE(8)
-    PE_FIRST_CASE(16)
-    PE_FIRST_CASE(32)
-    PE_FIRST_CASE(64)
-    PE_FIRST_CASE(128)
+    PE_HEAD_DIMS(PE_FIRST_CASE)
     default: return hipErrorInvalidValue;
   }
 #undef PE_FIRST_CASE

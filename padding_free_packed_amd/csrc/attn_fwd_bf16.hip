@@ -63,7 +63,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
   const int khi = __builtin_amdgcn_readfirstlane(win >= 0 ? min(sp.hi, sp.rend + win) : sp.hi);
 
   vec8<Et> qr[QS];
-  load_row_regs<Et, D>(qp, static_cast<int64_t>(qrow) * ld + h * D + g * (D / 2), qvalid, qr);
+  load_row_regs<Et, D>(qp, static_cast<int64_t>(qrow) * ld + h * D, g, qvalid, qr);
   // Retire the Q loads with a wait the compiler sees: otherwise it places a
   // vmcnt wait for them inside the loop, which would also drain the DMA ring.
   vmem_fence_for_compiler();

@@ -94,7 +94,7 @@ __global__ __launch_bounds__(kW64Threads) __attribute__((amdgpu_waves_per_eu(2))
   vec8<Et> qr[2][QS];
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb)
-    load_row_regs<Et, D>(qp, static_cast<int64_t>(qrow[qb]) * ld + h * D + g * (D / 2), qvalid[qb], qr[qb]);
+    load_row_regs<Et, D>(qp, static_cast<int64_t>(qrow[qb]) * ld + h * D, g, qvalid[qb], qr[qb]);
   // retire the Q loads with a wait the compiler sees, so none lands inside the DMA loop
   vmem_fence_for_compiler();
 

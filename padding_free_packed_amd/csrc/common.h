@@ -69,6 +69,9 @@ __device__ __forceinline__ void st_nt(U* p, const U& v) {
   }
 }
 
+// smallest power of two >= x (x >= 1)
+constexpr int pow2_ceil(int x) { return x <= 1 ? 1 : 2 * pow2_ceil((x + 1) / 2); }
+
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 // Finite stand-in for minus infinity as the running maximum, so that

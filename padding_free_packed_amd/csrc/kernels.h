@@ -14,6 +14,11 @@ constexpr int kDtF32 = 0;
 constexpr int kDtBF16 = 1;
 constexpr int kDtF16 = 2;
 
+// Every head dim the attention kernels are built for: the multiples of 8 up to 128.
+#define PE_HEAD_DIMS(X) \
+  X(8) X(16) X(24) X(32) X(40) X(48) X(56) X(64) X(72) X(80) X(88) X(96) X(104) X(112) X(120) X(128)
+constexpr bool head_dim_supported(int d) { return d >= 8 && d <= 128 && d % 8 == 0; }
+
 // packed query (or key) rows per attention work item
 constexpr int kAttnTileRows = 128;
 // packed rows per work item of the one-wave fp32 kernels
@@ -41,10 +46,17 @@ hipError_t launch_pack_rows(const void* grid, void* packed, int64_t* flat_index,
 hipError_t launch_unpack_rows(const void* packed, void* grid, const int32_t* cu, int32_t B, int32_t S,
                               int64_t rowbytes, hipStream_t stream);
 
-// Forward over tiles of kAttnTileRows packed query rows; items from launch_worklist,
-// except where attn_fwd_bf16_w64_supported selects the 64-row-wave kernel: then
-// items is the sequence-aligned list (launch_seq_worklist) with tile height kAttnTileRows.
-// dt: kDtF32, kDtBF16 or kDtF16 (every attention launcher takes it).
+// The work list a forward reads, decided from host-visible arguments only. The
+// entry points build the list this names, and launch_attn_fwd picks its kernel
+// from the same answer, so list and kernel cannot disagree:
+//   kFwdListPacked128: tiles of kAttnTileRows consecutive packed rows (launch_worklist);
+//   kFwdListSeq128:    sequence-aligned tiles of kAttnTileRows rows (launch_seq_worklist),
+//                      the 16-bit 64-row-wave kernel;
+//   kFwdListSeq32:     sequence-aligned tiles of kAttnWaveRows rows, the fp32 one-wave kernel.
+enum FwdList { kFwdListPacked128 = 0, kFwdListSeq128 = 1, kFwdListSeq32 = 2 };
+FwdList attn_fwd_list(int dt, int D, int max_seq_len, int64_t ld, int32_t H);
+// The forward of every entry point; items is the list attn_fwd_list names for the same
+// arguments. dt: kDtF32, kDtBF16 or kDtF16 (every attention launcher takes it).
 hipError_t launch_attn_fwd(int dt, int D, const void* q, const void* k, const void* v,
                            const int32_t* cu, const int32_t* items, int32_t B, int32_t N, int32_t H,
                            int32_t max_seq_len, int32_t win, int64_t ld, float scale, void* out, float* lse,

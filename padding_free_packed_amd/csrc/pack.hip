@@ -127,7 +127,9 @@ __device__ __forceinline__ void seq_worklist_entry(const int32_t* __restrict__ c
   if (i == 0) items[T] = B;
   if (i < T && (i < cu_0 / R || i >= cu_B / R + B)) items[i] = B;
   if (i >= B) return;
-  const int64_t s0 = cu[i] / R + i, s1 = cu[i + 1] / R + i + 1;
+  // clamped to [0, T): offsets outside [0, N] (a broken precondition) never write past the list
+  const int64_t s0 = max(static_cast<int64_t>(cu[i]) / R + i, static_cast<int64_t>(0));
+  const int64_t s1 = min(static_cast<int64_t>(cu[i + 1]) / R + i + 1, T);
   for (int64_t s = s0; s < s1; ++s) items[s] = static_cast<int32_t>(i);
 }
 

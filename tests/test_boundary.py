@@ -87,7 +87,8 @@ def test_fwd_rejects(kw, code):
 def test_first_token_rejects():
     f = lib.pe_varlen_attn_fwd_first_token
     assert f(NUL, P, P, P, 4, 100, 64, 2, 64, 0, 0.125, P, NUL, None) == pe.PE_ERR_NULL
-    assert f(P, P, P, P, 4, 100, 64, 2, 24, 0, 0.125, P, NUL, None) == pe.PE_ERR_UNSUPPORTED
+    assert f(P, P, P, P, 4, 100, 64, 2, 20, 0, 0.125, P, NUL, None) == pe.PE_ERR_UNSUPPORTED
+    assert f(P, P, P, P, 4, 100, 64, 2, 136, 0, 0.125, P, NUL, None) == pe.PE_ERR_UNSUPPORTED
     assert f(P, P, P, P, 4, 100, 64, 2, 64, 0, -1.0, P, NUL, None) == pe.PE_ERR_ARG
     assert f(P, P, P, P, 4, 100, 64, 2, 64, 0, 0.125, P, MIS, None) == pe.PE_ERR_ARG
 
@@ -102,7 +103,7 @@ def test_first_row_and_first_token_backward_reject():
     for i in (0, 1, 2, 3, 4, 5, 6, 14, 15, 16):  # lse_first is required too
         a = list(ok); a[i] = NUL
         assert b(*a) == pe.PE_ERR_NULL, i
-    a = list(ok); a[11] = 40
+    a = list(ok); a[11] = 44
     assert b(*a) == pe.PE_ERR_UNSUPPORTED
     a = list(ok); a[16] = MIS
     assert b(*a) == pe.PE_ERR_ARG
@@ -188,7 +189,7 @@ def test_bwd_rejects():
     a[18] = 100
     assert f(*a) == pe.PE_ERR_WORKSPACE
     a = list(ok)
-    a[11] = 40
+    a[11] = 36          # not a multiple of 8
     assert f(*a) == pe.PE_ERR_UNSUPPORTED
 
 
@@ -266,7 +267,7 @@ def test_forward_graph_rejects_before_any_capture():
     assert f(*a) == pe.PE_ERR_NULL
     for i, bad, code in [(0, NUL, pe.PE_ERR_NULL), (3, NUL, pe.PE_ERR_NULL), (14, NUL, pe.PE_ERR_NULL),
                          (8, -2, pe.PE_ERR_ARG), (1, 0, pe.PE_ERR_ARG), (6, 7, pe.PE_ERR_UNSUPPORTED),
-                         (5, 24, pe.PE_ERR_UNSUPPORTED), (7, 0.0, pe.PE_ERR_ARG), (16, ws - 1, pe.PE_ERR_WORKSPACE),
+                         (5, 28, pe.PE_ERR_UNSUPPORTED), (7, 0.0, pe.PE_ERR_ARG), (16, ws - 1, pe.PE_ERR_WORKSPACE),
                          (13, MIS, pe.PE_ERR_ARG)]:
         a = list(ok); a[i] = bad
         g.value = P

@@ -46,7 +46,7 @@ def _fwd(w, window=None):
 
 
 @pytest.mark.parametrize("d,S", [(8, 64), (16, 64), (32, 64), (64, 64), (128, 64), (32, 300), (64, 300),
-                                 (128, 300), (16, 300)])
+                                 (128, 300), (16, 300), (24, 300), (40, 64), (96, 300), (120, 300)])
 def test_forward(d, S):
     w = W.custom(300 + d + S, np.minimum(EDGE, S), S, 2, d, F16)
     say(f"[f16 fwd] d={d} S={S} N={w.total_tokens}")
@@ -90,7 +90,7 @@ def test_local_forward_and_backward(d, S, window):
         check_grad(to_f64(g), r, F16, f"f16 local {name}")
 
 
-@pytest.mark.parametrize("d,S", [(16, 64), (64, 64), (64, 300), (128, 300), (8, 40)])
+@pytest.mark.parametrize("d,S", [(16, 64), (64, 64), (64, 300), (128, 300), (8, 40), (24, 300), (72, 64), (120, 300)])
 def test_backward(d, S):
     w = W.custom(320 + d + S, np.minimum(EDGE, S), S, 2, d, F16, with_grad=True)
     say(f"[f16 bwd] d={d} S={S}")

@@ -20,11 +20,15 @@ graphs = pytest.importorskip("padding_free_packed_amd.graphs")
 
 
 def _bits(t):
-    return t.view(torch.int16) if t.dtype == torch.bfloat16 else t.view(torch.int32)
+    return t.view(torch.int16) if t.dtype in (torch.bfloat16, torch.float16) else t.view(torch.int32)
 
 
 def _code(dtype):
-    return pe.PE_BF16 if dtype == torch.bfloat16 else pe.PE_FP32
+    return {torch.bfloat16: pe.PE_BF16, torch.float16: pe.PE_FP16}.get(dtype, pe.PE_FP32)
+
+
+def _wdt(dtype):
+    return {torch.bfloat16: W.BF16, torch.float16: W.FP16}.get(dtype, W.FP32)
 
 
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
@@ -142,25 +146,34 @@ def _eager(bucket, scale, window):
     return grid, lse, n, cu
 
 
-GRAPH_CASES = [(torch.bfloat16, 12, 64, -1), (torch.float32, 8, 64, -1), (torch.bfloat16, 12, 64, 16),
-               (torch.bfloat16, 4, 128, -1)]
+GRAPH_CASES = [  # dtype, H, d, window, slots, length bound
+    (torch.bfloat16, 12, 64, -1, 64, 48), (torch.float32, 8, 64, -1, 64, 48), (torch.bfloat16, 12, 64, 16, 64, 48),
+    (torch.bfloat16, 4, 128, -1, 64, 48),
+    # bounds above 128: the 16-bit forward is the 64-row-wave kernel on sequence-aligned tiles
+    # of the bucket's capacity rows (lengths crossing 128 and 256, fewer sequences than slots)
+    (torch.bfloat16, 4, 64, -1, 16, 300), (torch.bfloat16, 4, 64, 20, 16, 300),
+    (torch.float16, 4, 32, -1, 16, 300), (torch.float16, 4, 32, 20, 16, 300),
+]
 
 
-@pytest.mark.parametrize("dtype,H,d,window", GRAPH_CASES)
-def test_bucket_graph_replays(dtype, H, d, window):
-    slots, S = 64, 48
+def _to_wdt(x, wdt):
+    return W.to_bits(x, wdt) if W.is16(wdt) else x
+
+
+@pytest.mark.parametrize("dtype,H,d,window,slots,S", GRAPH_CASES)
+def test_bucket_graph_replays(dtype, H, d, window, slots, S):
     scale = 1.0 / np.sqrt(d)
     say(f"[graph] {dtype} H={H} d={d} window={window}: bucket ({slots}, {S})")
     bucket = graphs.ForwardBucket(slots, S, H, d, dtype, scale, window, with_lse=True, device=DEV)
-    rng = np.random.default_rng(21 + d + H)
-    wdt = W.BF16 if dtype == torch.bfloat16 else W.FP32
+    rng = np.random.default_rng(21 + d + H + S)
+    wdt = _wdt(dtype)
     try:
-        for rep, B in enumerate([64, 37, 64, 5, 1]):
+        for rep, B in enumerate([slots, slots * 37 // 64, slots, 5, 1]):
             L = rng.integers(8, S + 1, size=B).astype(np.int32)
             L[0] = 1 if rep == 4 else L[0]
             Sb = int(L.max())
             x = rng.standard_normal((B, Sb, 3, H, d), dtype=np.float32)
-            xq = W.f32_to_bf16_bits(x) if wdt == W.BF16 else x
+            xq = _to_wdt(x, wdt)
             got = bucket.run(torch.from_numpy(L).to(DEV), to_dev(xq, wdt))
             torch.cuda.synchronize()
             ref_grid, ref_lse, n, cu = _eager(bucket, scale, window)
@@ -188,7 +201,7 @@ def test_bucket_graph_replays(dtype, H, d, window):
         # and the next good batch replays correctly
         L = rng.integers(8, S + 1, size=slots).astype(np.int32)
         x = rng.standard_normal((slots, S, 3, H, d), dtype=np.float32)
-        bucket.run(torch.from_numpy(L).to(DEV), to_dev(W.f32_to_bf16_bits(x) if wdt == W.BF16 else x, wdt))
+        bucket.run(torch.from_numpy(L).to(DEV), to_dev(_to_wdt(x, wdt), wdt))
         torch.cuda.synchronize()
         ref_grid, _, n, _ = _eager(bucket, scale, window)
         assert bucket.status.tolist() == [n, pe.PACK_OK]
