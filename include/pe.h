@@ -317,6 +317,33 @@ pe_status pe_varlen_attn_bwd_local(const void* dout, const void* q, const void* 
                                    int32_t window, void* dq, void* dk, void* dv, void* workspace,
                                    size_t workspace_bytes, void* stream);
 
+/* ---------------------------------------------- forward without allocation
+ * pe_varlen_attn_fwd_noalloc: pe_varlen_attn_fwd with no workspace argument, for
+ * callers that cannot allocate device memory or pass a workspace (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).
+ * Its work list lives in a fixed scratch array the library holds in device
+ * memory (pe_noalloc_scratch_size() bytes, 1 MiB, one copy on each GPU it is
+ * called on, kept until the process ends); the call itself allocates nothing.
+ *
+ * Arguments, layouts, results and errors as pe_varlen_attn_fwd, except:
+ *   - a batch whose work list would not fit the scratch array, i.e.
+ *     pe_attn_workspace_size(num_seqs, total_tokens, num_heads, head_dim,
+ *     dtype, 0) > pe_noalloc_scratch_size() (about total_tokens / 32 + num_seqs
+ *     + 1 int32 entries, so up to ~8 million tokens), returns PE_ERR_WORKSPACE
+ *     before anything is launched;
+ *   - every call on one GPU shares that GPU's array: calls that overlap on one
+ *     GPU (concurrent streams, or host threads) race and are not allowed. Each
+ *     call rewrites the whole list before its kernel reads it, so nothing in it
+ *     needs to start at zero.
+ * The first call on a device looks the array's address up on that device (the
+ * device current at the call).
+ */
+size_t pe_noalloc_scratch_size(void);
+pe_status pe_varlen_attn_fwd_noalloc(const void* q, const void* k, const void* v, const int32_t* cu_seqlens,
+                                     int32_t num_seqs, int64_t total_tokens, int32_t max_seq_len,
+                                     int32_t num_heads, int32_t head_dim, pe_dtype dtype, float softmax_scale,
+                                     void* out, float* lse, void* stream);
+
 /* ---------------------------------------------------------------- fused QKV
  * pe_varlen_attn_fwd_qkv / pe_varlen_attn_bwd_qkv: the attention calls on a
  * fused projection buffer qkv [total_tokens, 3, num_heads, head_dim] (Q, K and V

@@ -7,6 +7,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstdlib>
+#include <mutex>
 
 #include "kernels.h"
 #include "pe.h"
@@ -241,6 +242,58 @@ pe_status pe_varlen_attn_fwd(const void* q, const void* k, const void* v, const 
                              void* workspace, size_t workspace_bytes, void* stream) {
   return fwd_impl(q, k, v, cu_seqlens, num_seqs, total_tokens, max_seq_len, num_heads, head_dim, dtype,
                   softmax_scale, -1, dense_ld(num_heads, head_dim), out, lse, workspace, workspace_bytes, stream);
+}
+
+}  // extern "C"
+
+// ------------------------------------------------------ forward without allocation
+
+namespace {
+
+// The work list of pe_varlen_attn_fwd_noalloc, in device memory the library holds
+// for the process's lifetime (one copy per GPU it runs on). kNoAllocScratchBytes
+// bounds the batch: the list takes pe_attn_workspace_size(..., 0) bytes.
+constexpr size_t kNoAllocScratchBytes = size_t{1} << 20;
+static __device__ __align__(256) char scratch[kNoAllocScratchBytes];
+
+// Device address of `scratch` on each GPU, looked up once per device with that
+// device current (the host-side name is not a device address).
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+pe_status scratch_on_current_device(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return PE_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) return PE_ERR_HIP;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return PE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t pe_noalloc_scratch_size(void) { return kNoAllocScratchBytes; }
+
+pe_status pe_varlen_attn_fwd_noalloc(const void* q, const void* k, const void* v, const int32_t* cu_seqlens,
+                                     int32_t num_seqs, int64_t total_tokens, int32_t max_seq_len, int32_t num_heads,
+                                     int32_t head_dim, pe_dtype dtype, float softmax_scale, void* out, float* lse,
+                                     void* stream) {
+  // sizes first: a batch whose work list exceeds the built-in scratch is rejected before
+  // the device is touched
+  if (num_seqs >= 1 && total_tokens >= 0 && num_heads >= 1 &&
+      pe_attn_workspace_size(num_seqs, total_tokens, num_heads, head_dim, dtype, 0) > kNoAllocScratchBytes)
+    return PE_ERR_WORKSPACE;
+  void* ws = nullptr;
+  if (const pe_status s = scratch_on_current_device(&ws); s != PE_OK) return s;
+  return fwd_impl(q, k, v, cu_seqlens, num_seqs, total_tokens, max_seq_len, num_heads, head_dim, dtype,
+                  softmax_scale, -1, dense_ld(num_heads, head_dim), out, lse, ws, kNoAllocScratchBytes, stream);
 }
 
 pe_status pe_varlen_attn_fwd_local(const void* q, const void* k, const void* v, const int32_t* cu_seqlens,

@@ -30,6 +30,7 @@ EXPORTS = (
     "pe_flatten_document_mask", "pe_gather_rows", "pe_scatter_rows", "pe_varlen_attn_fwd_qkv",
     "pe_varlen_attn_bwd_qkv", "pe_timing_enable", "pe_timing_read", "pe_pack_async",
     "pe_forward_graph_workspace_size", "pe_forward_graph_create", "pe_graph_launch", "pe_graph_destroy",
+    "pe_noalloc_scratch_size", "pe_varlen_attn_fwd_noalloc",
 )
 
 # status[1] codes of pe_pack_async
@@ -87,6 +88,9 @@ def _load():
                                                     P, P, SZ, ctypes.POINTER(ctypes.c_void_p)]),
         "pe_graph_launch": (ctypes.c_int, [P, P]),
         "pe_graph_destroy": (ctypes.c_int, [P]),
+        "pe_noalloc_scratch_size": (SZ, []),
+        "pe_varlen_attn_fwd_noalloc": (ctypes.c_int, [P, P, P, P, I32, I64, I32, I32, I32, ctypes.c_int, F, P, P,
+                                                       P]),
         "pe_timing_enable": (ctypes.c_int, [ctypes.c_int]),
         "pe_timing_read": (ctypes.c_int, [P, P, ctypes.c_int]),
     }
@@ -191,6 +195,18 @@ def pe_varlen_attn_fwd(q, k, v, cu_seqlens, num_seqs, total_tokens, max_seq_len,
                                  max_seq_len, H, d, _dtype_code(q), softmax_scale, _ptr(out), _ptr(lse),
                                  _ptr(workspace), workspace.numel(), _stream())
     _check("pe_varlen_attn_fwd", st)
+
+
+def pe_noalloc_scratch_size() -> int:
+    return int(_lib.pe_noalloc_scratch_size())
+
+
+def pe_varlen_attn_fwd_noalloc(q, k, v, cu_seqlens, num_seqs, total_tokens, max_seq_len, softmax_scale, out, lse):
+    N, H, d = q.shape
+    st = _lib.pe_varlen_attn_fwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens), num_seqs, total_tokens,
+                                         max_seq_len, H, d, _dtype_code(q), softmax_scale, _ptr(out), _ptr(lse),
+                                         _stream())
+    _check("pe_varlen_attn_fwd_noalloc", st)
 
 
 def pe_varlen_attn_fwd_first_token(q_first, k, v, cu_seqlens, num_seqs, total_tokens, max_seq_len,

@@ -27,7 +27,7 @@ def _header_functions():
 
 def test_header_symbols_exported():
     names = _header_functions()
-    assert len(names) == 29
+    assert len(names) == 31
     for n in names:
         assert hasattr(lib, n), n
     assert sorted(pe.EXPORTS) == names
@@ -275,3 +275,11 @@ def test_forward_graph_rejects_before_any_capture():
         assert g.value is None, i                # no handle on an error
     assert lib.pe_graph_launch(NUL, None) == pe.PE_ERR_NULL
     assert lib.pe_graph_destroy(NUL) == pe.PE_OK
+
+
+def test_noalloc_forward_rejects_batches_beyond_its_scratch_before_touching_the_device():
+    assert lib.pe_noalloc_scratch_size() == 1 << 20
+    f = lib.pe_varlen_attn_fwd_noalloc
+    # a work list of 2^28 / 32 + 5 int32 entries (32 MiB) cannot fit: refused on sizes alone
+    assert f(P, P, P, P, 4, 2**28, 2**26, 2, 64, 0, 0.125, P, NUL, None) == pe.PE_ERR_WORKSPACE
+    assert f(P, P, P, P, 2**20, 2**24, 64, 2, 64, 1, 0.125, P, NUL, None) == pe.PE_ERR_WORKSPACE
