@@ -73,6 +73,16 @@ __device__ __forceinline__ u16x4 ds_read_tr16(const uint16_t* p) {
   return __builtin_bit_cast(u16x4, r);
 }
 
+// The same reads at an LDS byte address (a 32-bit LDS pointer value)
+__device__ __forceinline__ u16x8 ds_read_b128_at(uint32_t addr) {
+  return *reinterpret_cast<const __attribute__((address_space(3))) u16x8*>(static_cast<size_t>(addr));
+}
+__device__ __forceinline__ u16x4 ds_read_tr16_at(uint32_t addr) {
+  const shortx4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      reinterpret_cast<__attribute__((address_space(3))) shortx4*>(static_cast<size_t>(addr)));
+  return __builtin_bit_cast(u16x4, r);
+}
+
 // max / sum of a value with the same lane of the other half wave
 __device__ __forceinline__ float xhalf_max(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);

@@ -447,6 +447,8 @@ hipError_t launch_attn_fwd(int dt, int D, const void* q, const void* k, const vo
     case kFwdListSeq32:
       return launch_attn_fwd_f32_wave(D, q, k, v, cu, items, B, N, H, win, ld, scale, out, lse, stream);
     case kFwdListSeq128:
+      if (win < 0)  // global attention: every row of a tile has the same key range
+        return launch_attn_fwd_w64b(f16, D, q, k, v, cu, items, B, N, H, ld, scale, out, lse, stream);
       return launch_attn_fwd_bf16_w64(f16, D, q, k, v, cu, items, B, N, H, win, ld, scale, out, lse, stream);
     case kFwdListPacked128:
       break;

@@ -69,6 +69,11 @@ bool attn_fwd_bf16_w64_supported(int D);
 hipError_t launch_attn_fwd_bf16_w64(bool f16, int D, const void* q, const void* k, const void* v, const int32_t* cu,
                                     const int32_t* items, int32_t B, int32_t N, int32_t H, int32_t win, int64_t ld,
                                     float scale, void* out, float* lse, hipStream_t stream);
+// two 64-row waves per workgroup over sequence-aligned 128-row tiles, global attention
+// (head dims 32, 64; items as for the 64-row-wave kernel)
+hipError_t launch_attn_fwd_w64b(bool f16, int D, const void* q, const void* k, const void* v, const int32_t* cu,
+                                const int32_t* items, int32_t B, int32_t N, int32_t H, int64_t ld, float scale,
+                                void* out, float* lse, hipStream_t stream);
 hipError_t launch_attn_fwd_bf16(bool f16, int D, const void* q, const void* k, const void* v, const int32_t* cu,
                                 const int32_t* items, int32_t B, int32_t N, int32_t H, int32_t win, int64_t ld,
                                 float scale, void* out, float* lse, hipStream_t stream);
