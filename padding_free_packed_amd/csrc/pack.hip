@@ -13,14 +13,15 @@
 namespace pe {
 
 // ---------------------------------------------------------------- scan
-// One workgroup of 1024 threads; each pass scans 8192 lengths (8 per thread)
-// and carries the running total in int64. Writes cu[0..B], result[0] = total
-// token count (int64), result[1] = 1 if any length lies outside [1, S], else 2
-// if cap >= 0 and the total exceeds cap, else 0. With cap >= 0 a nonzero
-// result[1] also rewrites cu[0..B] as zeros, so that kernels queued behind the
-// scan without a host check see no rows at all.
+// One workgroup of 1024 threads; each pass scans 32768 lengths, thread i taking
+// the 32 consecutive lengths from 32 i (eight 16-byte loads, eight 16-byte stores
+// of their exclusive prefixes), and carries the running total in int64. Writes
+// cu[0..B], result[0] = total token count (int64), result[1] = 1 if any length
+// lies outside [1, S], else 2 if cap >= 0 and the total exceeds cap, else 0. With
+// cap >= 0 a nonzero result[1] also rewrites cu[0..B] as zeros, so that kernels
+// queued behind the scan without a host check see no rows at all.
 constexpr int kScanThreads = 1024;
-constexpr int kScanPer = 8;
+constexpr int kScanPer = 32;
 
 __device__ __forceinline__ void scan_lengths_block(const int32_t* __restrict__ lengths, int32_t B, int32_t S,
                                                    int64_t cap, int32_t* __restrict__ cu,
@@ -28,22 +29,28 @@ __device__ __forceinline__ void scan_lengths_block(const int32_t* __restrict__ l
   __shared__ int64_t wsum[kScanThreads / 64];
   __shared__ int bad_any;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  if (tid == 0) { cu[0] = 0; bad_any = 0; }
+  if (tid == 0) bad_any = 0;
   int bad = 0;
   int64_t carry = 0;
   for (int64_t base = 0; base < B; base += kScanThreads * kScanPer) {
-    int64_t v[kScanPer];
+    const int64_t i0 = base + static_cast<int64_t>(tid) * kScanPer;
+    const bool whole = i0 + kScanPer <= B;  // the thread's lengths all exist
+    int32_t L[kScanPer];
+    if (whole) {
+#pragma unroll
+      for (int v = 0; v < kScanPer / 4; ++v) {
+        const int4 x = *reinterpret_cast<const int4*>(lengths + i0 + 4 * v);
+        L[4 * v] = x.x; L[4 * v + 1] = x.y; L[4 * v + 2] = x.z; L[4 * v + 3] = x.w;
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < kScanPer; ++j) L[j] = i0 + j < B ? lengths[i0 + j] : 0;
+    }
     int64_t local = 0;
 #pragma unroll
     for (int j = 0; j < kScanPer; ++j) {
-      const int64_t idx = base + static_cast<int64_t>(tid) * kScanPer + j;
-      int64_t L = 0;
-      if (idx < B) {
-        L = lengths[idx];
-        bad |= (L < 1) | (L > S);
-      }
-      local += L;
-      v[j] = local;  // inclusive within the thread
+      if (i0 + j < B) bad |= (L[j] < 1) | (L[j] > S);
+      local += L[j];
     }
     // inclusive scan of `local` across the wave
     int64_t incl = local;
@@ -61,11 +68,21 @@ __device__ __forceinline__ void scan_lengths_block(const int32_t* __restrict__ l
       if (w < wv) wprefix += s;
       total += s;
     }
-    const int64_t excl = carry + wprefix + incl - local;
+    int64_t run = carry + wprefix + incl - local;  // rows before the thread's first sequence
+    int32_t E[kScanPer];                            // exclusive prefixes = cu[i0 + j]
 #pragma unroll
     for (int j = 0; j < kScanPer; ++j) {
-      const int64_t idx = base + static_cast<int64_t>(tid) * kScanPer + j;
-      if (idx < B) cu[idx + 1] = static_cast<int32_t>(excl + v[j]);
+      E[j] = static_cast<int32_t>(run);
+      run += L[j];
+    }
+    if (whole) {
+#pragma unroll
+      for (int v = 0; v < kScanPer / 4; ++v)
+        *reinterpret_cast<int4*>(cu + i0 + 4 * v) = make_int4(E[4 * v], E[4 * v + 1], E[4 * v + 2], E[4 * v + 3]);
+    } else {
+#pragma unroll
+      for (int j = 0; j < kScanPer; ++j)
+        if (i0 + j < B) cu[i0 + j] = E[j];
     }
     carry += total;
     __syncthreads();  // wsum is rewritten by the next pass
@@ -73,11 +90,13 @@ __device__ __forceinline__ void scan_lengths_block(const int32_t* __restrict__ l
   if (bad) atomicOr(&bad_any, 1);
   __syncthreads();
   const int64_t code = bad_any ? 1 : (cap >= 0 && carry > cap ? 2 : 0);
+  const bool clear = cap >= 0 && code != 0;
   if (tid == 0) {
     result[0] = carry;
     result[1] = code;
+    if (!clear) cu[B] = static_cast<int32_t>(carry);
   }
-  if (cap >= 0 && code != 0)
+  if (clear)
     for (int64_t i = tid; i <= B; i += kScanThreads) cu[i] = 0;
 }
 
