@@ -1,21 +1,21 @@
-// 16-bit forward of global attention for head dims 32 and 64: two waves per
-// workgroup, 64 query rows per wave, over sequence-aligned 128-row tiles.
+// 16-bit forward of global attention for head dims 32 and 64 over sequence-aligned
+// 128-row tiles: four waves of 32 query rows per workgroup at d = 64, two waves of
+// 64 rows at d = 32.
 //
 // A workgroup takes slot t of the sequence-aligned work list of 128-row tiles
 // (launch_seq_worklist with tile height 128): rows cu[b] + 128 * (t - cu[b] /
 // 128 - b) .. of sequence b = items[t]. Every row of it has the key range
 // [cu[b], cu[b+1]), so the loop needs no per-row range tests and only the
-// sequence's last key block needs a mask. Wave w owns rows 64w .. 64w + 63 as
-// two 32-row query blocks; a wave whose rows all lie past the sequence's end
-// still stages its share of every key block but computes nothing.
+// sequence's last key block needs a mask. Wave w owns 32 or 64 rows (one or two
+// 32-row query blocks); a wave whose rows all lie past the sequence's end still
+// stages its share of every key block but computes nothing.
 //
-//   * K and V tiles of 32 keys travel global -> LDS by LDS DMA into a ring the
-//     two waves fill together (each a half), tiles unpadded with XOR-swizzled
-//     16-byte chunks; one barrier per key block;
+//   * K and V tiles of 32 keys travel global -> LDS by LDS DMA into a ring of two
+//     stages (one block in flight) the waves fill together, tiles unpadded with
+//     XOR-swizzled 16-byte chunks; one barrier per key block;
 //   * S^T = K Q^T per query block (K rows from LDS as the A operand, Q^T in
 //     registers), O^T += V^T P^T with P straight from the accumulators and V^T
-//     read by ds_read_b64_tr_b16, so every K or V^T operand read from LDS feeds
-//     both query blocks' MFMAs;
+//     read by ds_read_b64_tr_b16;
 //   * the first key block sets each row's reference m to its exact maximum;
 //     after it, p = exp2(c s - m) and their sums are taken against the current m
 //     and only a block whose sum exceeds 2^16 (or is infinite) takes its exact
@@ -36,8 +36,18 @@ namespace pe {
 
 namespace {
 
-constexpr int kB64Waves = 2;
-constexpr int kB64Threads = 64 * kB64Waves;
+// 32-row query blocks per wave, waves per 128-row tile, threads per workgroup and the
+// waves per SIMD the register budget is sized for. At d = 64 one query block per wave
+// (124 registers, four waves per SIMD) measured 10-12% faster side by side than two
+// (213 registers, two waves per SIMD): the loop is latency-bound, and the extra waves
+// outweigh reading each K and V^T operand from LDS for one MFMA instead of two. At
+// d = 32 a 32-key tile is too small to split between four waves' DMA.
+template <int D>
+constexpr int b64_nq() { return D == 64 ? 1 : 2; }
+template <int D>
+constexpr int b64_threads() { return 64 * (4 / b64_nq<D>()); }
+template <int D>
+constexpr int b64_waves_per_simd() { return D == 64 ? 4 : 2; }
 constexpr int kB64Keys = 32;      // keys per ring stage
 // ring stages: one block in flight ahead of the one computed (2, 3 and 4 stages measured
 // side by side on the long-document and mixed-batch forwards; 2 was fastest)
@@ -53,6 +63,7 @@ __device__ __forceinline__ void b64_run(const void* __restrict__ qp, const void*
   constexpr int CH = D / 8;                     // 16-byte chunks per row
   constexpr int QS = D / 16;                    // MFMA steps over head_dim
   constexpr int DB = D / 32;                    // 32-row blocks of O^T
+  constexpr int kB64Threads = b64_threads<D>();
   constexpr int NL = kB64Keys * CH / kB64Threads;  // DMA instructions per lane per tile
   static_assert(NL >= 1 && (kB64Keys * CH) % kB64Threads == 0, "whole DMA instructions per tile");
   constexpr int QB = NQ > 0 ? NQ : 1;           // array extents
@@ -276,7 +287,7 @@ __device__ __forceinline__ void b64_run(const void* __restrict__ qp, const void*
 }
 
 template <typename Et, int D>
-__global__ __launch_bounds__(kB64Threads) __attribute__((amdgpu_waves_per_eu(2))) void attn_fwd_w64b_kernel(
+__global__ __launch_bounds__(b64_threads<D>(), b64_waves_per_simd<D>()) void attn_fwd_w64b_kernel(
     const void* __restrict__ qp, const void* __restrict__ kp, const void* __restrict__ vp,
     const int32_t* __restrict__ cu, const int32_t* __restrict__ items, int32_t B, int32_t N, int32_t H,
     int32_t T, int64_t ld, float c, void* __restrict__ op, float* __restrict__ lse) {
@@ -290,10 +301,16 @@ __global__ __launch_bounds__(kB64Threads) __attribute__((amdgpu_waves_per_eu(2))
   const int r0 = lo + (t - (lo / kAttnTileRows + b)) * kAttnTileRows;
   if (r0 >= hi) return;  // block-uniform: an empty slot at the end of the sequence
   const int rend = min(r0 + kAttnTileRows, hi);
-  const int rw = r0 + 64 * static_cast<int>(threadIdx.x >> 6);  // this wave's first row
-  const int nq = rw >= rend ? 0 : (rend - rw > 32 ? 2 : 1);    // wave-uniform
-  if (nq == 2) b64_run<Et, D, 2>(qp, kp, vp, h, rw, rend, lo, hi, N, H, ld, c, op, lse, ring);
-  else if (nq == 1) b64_run<Et, D, 1>(qp, kp, vp, h, rw, rend, lo, hi, N, H, ld, c, op, lse, ring);
+  constexpr int NQ = b64_nq<D>();
+  const int rw = r0 + 32 * NQ * static_cast<int>(threadIdx.x >> 6);  // this wave's first row
+  const int nq = rw >= rend ? 0 : min(NQ, (rend - rw + 31) / 32);   // wave-uniform
+  if constexpr (NQ == 2) {
+    if (nq == 2) {
+      b64_run<Et, D, 2>(qp, kp, vp, h, rw, rend, lo, hi, N, H, ld, c, op, lse, ring);
+      return;
+    }
+  }
+  if (nq == 1) b64_run<Et, D, 1>(qp, kp, vp, h, rw, rend, lo, hi, N, H, ld, c, op, lse, ring);
   else b64_run<Et, D, 0>(qp, kp, vp, h, rw, rend, lo, hi, N, H, ld, c, op, lse, ring);
 }
 
@@ -306,7 +323,7 @@ hipError_t dispatch_w64b(const void* q, const void* k, const void* v, const int3
   if (blocks == 0) return hipSuccess;
   const float c = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
   hipEvent_t ev = timing_start(stream);
-  hipLaunchKernelGGL((attn_fwd_w64b_kernel<Et, D>), dim3(static_cast<unsigned>(blocks)), dim3(kB64Threads), 0,
+  hipLaunchKernelGGL((attn_fwd_w64b_kernel<Et, D>), dim3(static_cast<unsigned>(blocks)), dim3(b64_threads<D>()), 0,
                      stream, q, k, v, cu, items, B, N, H, T, ld, c, out, lse);
   timing_stop("attn_fwd", ev, stream);
   return hipGetLastError();
