@@ -104,7 +104,9 @@ def algo_work(kernel, w, N, L2, e, with_lse, with_grid=True):
         "attn_fwd_first": {"byte": 2.0 * N * D * e + 2.0 * B * D * e + (4.0 * B * H if with_lse else 0.0)},
         # first-token backward: read K, V and the B rows of q, dO, O (+ LSE), write dK, dV and dq_first
         "attn_bwd_first": {"byte": 4.0 * N * D * e + 4.0 * B * D * e + 4.0 * B * H},
-        "bwd_delta": {"byte": 2.0 * N * D * e + 4.0 * N * H},
+        # D = rowsum(dO * O): read dO and O, write D; the 16-bit pass at head dims 32 and 64 also
+        # reads the LSE and writes its scaled copy
+        "bwd_delta": {"byte": 2.0 * N * D * e + (12.0 if e == 2 and d in (32, 64) else 4.0) * N * H},
         # pack: read and write the real rows, write flat_index (only flat_index without a grid)
         "pack_rows": {"byte": (2.0 * N * D * e if with_grid else 0.0) + 8.0 * N},
         # unpack: read the real rows, write the whole grid

@@ -180,8 +180,9 @@ size_t pe_attn_workspace_size(int32_t num_seqs, int64_t total_tokens, int32_t nu
   (void)dtype;
   if (num_seqs < 1 || total_tokens < 0 || num_heads < 1) return 0;
   size_t s = items_bytes(num_seqs, total_tokens);
-  if (for_backward)
-    s += items_bytes(num_seqs, total_tokens) + round_up(static_cast<size_t>(total_tokens) * num_heads * sizeof(float));
+  if (for_backward)  // a second list and two [H, N] float arrays
+    s += items_bytes(num_seqs, total_tokens) +
+         2 * round_up(static_cast<size_t>(total_tokens) * num_heads * sizeof(float));
   return s;
 }
 
@@ -399,6 +400,15 @@ pe_status bwd_impl(const void* dout, const void* q, const void* k, const void* v
   const size_t ib = items_bytes(num_seqs, total_tokens);
   int32_t* items32 = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + ib);
   float* delta = reinterpret_cast<float*>(static_cast<char*>(workspace) + 2 * ib);
+  if (pe::attn_bwd_seq_supported(dtype, head_dim, win, total_tokens, num_heads, ld)) {
+    float* nd = reinterpret_cast<float*>(reinterpret_cast<char*>(delta) +
+                                         round_up(static_cast<size_t>(total_tokens) * num_heads * sizeof(float)));
+    hipError_t e = pe::launch_seq_worklist(cu_seqlens, num_seqs, total_tokens, pe::kAttnTileRows, items, st);
+    if (e != hipSuccess) return PE_ERR_HIP;
+    return hip_status(pe::launch_attn_bwd_seq(dtype, head_dim, dout, q, k, v, out, lse, cu_seqlens, items, num_seqs,
+                                              static_cast<int32_t>(total_tokens), num_heads, ld, softmax_scale, dq,
+                                              dk, dv, delta, nd, st));
+  }
   // the fp32 one-wave kernels take the sequence-aligned list, every other kernel the 128-row one
   const bool wave = dtype == PE_FP32 && pe::attn_f32_wave_supported(head_dim, ld, num_heads);
   hipError_t e = wave ? pe::launch_seq_worklist(cu_seqlens, num_seqs, total_tokens, pe::kAttnWaveRows, items32, st)

@@ -396,6 +396,13 @@ __device__ __forceinline__ void dma16(uint32_t lds, const void* sbase, uint32_t 
                : "memory", "m0");
 }
 
+// The same with 4 bytes per lane: lane l writes lds + 4*l.
+__device__ __forceinline__ void dma4(uint32_t lds, const void* sbase, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, %2" ::"s"(__builtin_amdgcn_readfirstlane(lds)),
+               "v"(voff), "s"(sbase)
+               : "memory", "m0");
+}
+
 // A operand (8 16-bit elements along head_dim) of mma over a swizzled tile:
 // row r, logical chunk c.
 template <typename Et, int CH>

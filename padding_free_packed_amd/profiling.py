@@ -25,9 +25,9 @@ KERNEL_SOURCES = {
                  "attn_common.h", "common.h"],
     "attn_fwd_first": ["attn_fwd.hip", "common.h"],
     "attn_bwd_first": ["attn_first_bwd.hip", "attn_common.h", "common.h"],
-    "bwd_delta": ["attn_bwd.hip", "attn_common.h", "common.h"],
-    "bwd_dkdv": ["attn_bwd.hip", "attn_f32_wave.hip", "attn_common.h", "common.h"],
-    "bwd_dq": ["attn_bwd.hip", "attn_f32_wave.hip", "attn_common.h", "common.h"],
+    "bwd_delta": ["attn_bwd.hip", "attn_bwd_seq.hip", "attn_common.h", "common.h"],
+    "bwd_dkdv": ["attn_bwd.hip", "attn_bwd_seq.hip", "attn_f32_wave.hip", "attn_common.h", "common.h"],
+    "bwd_dq": ["attn_bwd.hip", "attn_bwd_seq.hip", "attn_f32_wave.hip", "attn_common.h", "common.h"],
     "pack_rows": ["pack.hip", "common.h"],
     "unpack_rows": ["pack.hip", "common.h"],
     "scan": ["pack.hip", "common.h"],
@@ -42,9 +42,9 @@ KERNEL_PATTERNS = {
     "attn_fwd": r"attn_fwd(_bf16|_bf16_w64|_w64b|_f32)?_kernel(<|I)",
     "attn_fwd_first": r"attn_fwd_first_kernel(<|I)",
     "attn_bwd_first": r"attn_bwd_first_kernel(<|I)",
-    "bwd_delta": r"bwd_delta_kernel(<|I)",
-    "bwd_dkdv": r"bwd_dkdv(_f32)?_kernel(<|I)",
-    "bwd_dq": r"bwd_dq(_f32)?_kernel(<|I)",
+    "bwd_delta": r"bwd_(delta|seq_prep)_kernel(<|I)",
+    "bwd_dkdv": r"bwd_(dkdv(_f32)?|kv_seq)_kernel(<|I)",
+    "bwd_dq": r"bwd_(dq(_f32)?|q_seq)_kernel(<|I)",
     "pack_rows": r"(?<!un)pack_rows_kernel(<|I)",
     "unpack_rows": r"unpack_rows_kernel(<|I)",
     "scan": r"scan_lengths_kernel",

@@ -44,9 +44,9 @@ def test_tile_rows():
 
 
 def test_workspace_sizes():
-    # work list: ceil(N/32)+1 int32, rounded to 256 bytes; backward adds a second list and an fp32 [H, N] array
+    # work list: ceil(N/32)+1 int32, rounded to 256 bytes; backward adds a second list and two fp32 [H, N] arrays
     assert pe.pe_attn_workspace_size(4, 1000, 8, 64, pe.PE_FP32, False) == 256
-    assert pe.pe_attn_workspace_size(4, 1000, 8, 64, pe.PE_FP32, True) == 256 + 256 + 32000
+    assert pe.pe_attn_workspace_size(4, 1000, 8, 64, pe.PE_FP32, True) == 256 + 256 + 2 * 32000
     big = pe.pe_attn_workspace_size(4096, 368449, 8, 64, pe.PE_FP32, False)
     assert big >= (368449 // 128 + 2) * 4 and big % 256 == 0
     assert pe.pe_pack_workspace_size(8, 64, 16, pe.PE_FP32) >= 256 + 8
