@@ -40,26 +40,32 @@ namespace {
 // 64-row stages (two 32-row sub-blocks per barrier) were 1-6% slower in both passes; the
 // dK/dV pass at three waves per SIMD (168 registers) beat two (213) by 7%; the dQ pass at
 // four waves (128 registers, spilling inside the loop) was 35% slower than at three; raising
-// the wave priority around each run of MFMAs (s_setprio) was 3% slower.
+// the wave priority around each run of MFMAs (s_setprio) was 3% slower; software-pipelining
+// the dQ pass (the S^T, dP^T MFMAs of key block j+1 issued beside the softmax of block j,
+// a three-stage ring, 222 registers so two waves per SIMD) was 15% slower.
 constexpr int kKvRows = 32;
 constexpr int kQRows = 32;
 constexpr int kKvWaves = 3;
 constexpr int kQWaves = 3;
 
-// One group of CH lanes per (row, head), as the delta pass of attn_bwd.hip (same
-// summation order, so D is the same value).
+// One group of CH lanes per (head, row), rows fastest: lane `sub` of the group reads
+// 16-byte chunk `sub` of the head row of dO and of O, and the group sums by butterfly
+// (the summation order of the delta pass of attn_bwd.hip, so D is the same value).
+// Consecutive groups take consecutive rows of one head, so the LSE reads and the
+// nl, nd writes of a wave are contiguous.
 template <typename Et, int D>
 __global__ __launch_bounds__(256) void bwd_seq_prep_kernel(const void* __restrict__ dout, const void* __restrict__ out,
                                                            const float* __restrict__ lse, int32_t N, int32_t H,
                                                            float* __restrict__ nl, float* __restrict__ nd) {
   constexpr int CH = D / 8;  // 16-byte chunks per head row (4 or 8)
   const int64_t idx = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-  const int64_t hr = idx / CH;  // (row, head) pair, row-major over [N, H]
-  const int sub = static_cast<int>(idx - hr * CH);
+  const int64_t hi = idx / CH;  // (head, row) pair, head-major over [H, N]
+  const int sub = static_cast<int>(idx - hi * CH);
   const int64_t total = static_cast<int64_t>(N) * H;
   float s = 0.f;
-  if (hr < total) {
-    const int64_t ch = hr * CH + sub;
+  if (hi < total) {
+    const int64_t hh = hi / N, i = hi - hh * N;
+    const int64_t ch = (i * H + hh) * CH + sub;
     const uint4 a = *reinterpret_cast<const uint4*>(static_cast<const char*>(dout) + ch * 16);
     const uint4 b = *reinterpret_cast<const uint4*>(static_cast<const char*>(out) + ch * 16);
     const u16x8 x = __builtin_bit_cast(u16x8, a), y = __builtin_bit_cast(u16x8, b);
@@ -68,10 +74,9 @@ __global__ __launch_bounds__(256) void bwd_seq_prep_kernel(const void* __restric
   }
 #pragma unroll
   for (int o = 1; o < CH; o <<= 1) s += __shfl_xor(s, o);
-  if (hr < total && sub == 0) {
-    const int64_t i = hr / H, hh = hr - i * H;
-    nd[hh * N + i] = -s;
-    nl[hh * N + i] = -(lse[hh * N + i] * kLog2e);
+  if (hi < total && sub == 0) {
+    nd[hi] = -s;
+    nl[hi] = -(lse[hi] * kLog2e);
   }
 }
 
