@@ -171,8 +171,30 @@ struct PairDma {
   }
 };
 
-// Blocks 0 .. nblk-1 through the two-stage ring, two per iteration so that each
-// step's stage is a constant; the last block is the one that masks.
+// A ring stage given as a constant (std::integral_constant) or at run time (int), and
+// the other stage of the two.
+template <typename S>
+__device__ __forceinline__ int stage_of(S st) {
+  if constexpr (std::is_integral<S>::value) return st;
+  else return S::value;
+}
+template <typename S>
+__device__ __forceinline__ auto other_stage(S st) {
+  if constexpr (std::is_integral<S>::value) return 1 - st;
+  else return std::integral_constant<int, 1 - S::value>{};
+}
+
+// Blocks 0 .. nblk-1 through the two-stage ring, the stage of each block at run time;
+// the last block is the one that masks.
+template <typename Issue, typename Step>
+__device__ __forceinline__ void run_blocks_dyn(int nblk, Issue& issue, Step& step) {
+  issue(0, 0);
+  for (int j = 0; j + 1 < nblk; ++j) step(j, j & 1, std::false_type{});
+  step(nblk - 1, (nblk - 1) & 1, std::true_type{});
+}
+
+// The same, two blocks per iteration so that each step's stage is a constant (every LDS
+// address is then a lane offset plus an immediate).
 template <typename Issue, typename Step>
 __device__ __forceinline__ void run_blocks(int nblk, Issue& issue, Step& step) {
   using S0 = std::integral_constant<int, 0>;
@@ -228,9 +250,9 @@ __global__ __launch_bounds__(kThreads, kKvWaves) void bwd_kv_seq_kernel(
   const float* nlh = nl + static_cast<int64_t>(h) * N;
   const uint32_t ring0 = lds_addr(ring[0]);
   const int nblk = (hi - lo + RS - 1) / RS;
-  // block blk into ring stage blk % 2 (ST)
+  // block blk into ring stage ST = blk % 2
   auto issue = [&](int blk, auto st_tag) __attribute__((always_inline)) {
-    constexpr int ST = decltype(st_tag)::value;
+    const int ST = stage_of(st_tag);
     const int row0 = lo + blk * RS;
     const int nrows = hi - row0;
     const uint32_t st = ring0 + static_cast<uint32_t>(ST * SB);
@@ -293,17 +315,16 @@ __global__ __launch_bounds__(kThreads, kKvWaves) void bwd_kv_seq_kernel(
       for (int db = 0; db < DB; ++db) dk[db] = mfma16<Et>(tr_operand<Et, D>(qt, so, s2, db), sb16[s2], dk[db]);
   };
 
-  // block j from ring stage ST = j % 2 (a constant, so every LDS address is a lane offset
-  // plus an immediate)
+  // block j from ring stage ST = j % 2
   auto step = [&](int j, auto st_tag, auto last_tag) __attribute__((always_inline)) {
-    constexpr int ST = decltype(st_tag)::value;
+    const int ST = stage_of(st_tag);
     constexpr bool LAST = decltype(last_tag)::value;
     wait_vmcnt<0>();
     // this wave's reads of block j-1's stage have completed before the barrier, after
     // which the DMA below overwrites that stage
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     raw_barrier();  // block j visible to every wave; all have read block j-1's stage
-    if (j + 1 < nblk) issue(j + 1, std::integral_constant<int, 1 - ST>{});
+    if (j + 1 < nblk) issue(j + 1, other_stage(st_tag));
     if (!active) return;
     const uint32_t st = ring0 + static_cast<uint32_t>(ST * SB);
 #pragma unroll
@@ -318,7 +339,7 @@ __global__ __launch_bounds__(kThreads, kKvWaves) void bwd_kv_seq_kernel(
     }
   };
 
-  run_blocks(nblk, issue, step);
+  run_blocks_dyn(nblk, issue, step);
 
   if (kvalid) {
     store_acc_row<Et, D>(dkp, roff, dk, scale, g);
@@ -362,9 +383,9 @@ __global__ __launch_bounds__(kThreads, kQWaves) void bwd_q_seq_kernel(
   const char* vbase = static_cast<const char*>(vp);
   const uint32_t ring0 = lds_addr(ring[0]);
   const int nblk = (hi - lo + RS - 1) / RS;
-  // block blk into ring stage blk % 2 (ST)
+  // block blk into ring stage ST = blk % 2
   auto issue = [&](int blk, auto st_tag) __attribute__((always_inline)) {
-    constexpr int ST = decltype(st_tag)::value;
+    const int ST = stage_of(st_tag);
     const int row0 = lo + blk * RS;
     dma.issue(ring0 + static_cast<uint32_t>(ST * SB), kbase, vbase, row0, hi - row0);
   };
@@ -398,12 +419,12 @@ __global__ __launch_bounds__(kThreads, kQWaves) void bwd_q_seq_kernel(
   };
 
   auto step = [&](int j, auto st_tag, auto last_tag) __attribute__((always_inline)) {
-    constexpr int ST = decltype(st_tag)::value;
+    const int ST = stage_of(st_tag);
     constexpr bool LAST = decltype(last_tag)::value;
     wait_vmcnt<0>();
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     raw_barrier();
-    if (j + 1 < nblk) issue(j + 1, std::integral_constant<int, 1 - ST>{});
+    if (j + 1 < nblk) issue(j + 1, other_stage(st_tag));
     if (!active) return;
     const uint32_t st = ring0 + static_cast<uint32_t>(ST * SB);
 #pragma unroll
