@@ -171,19 +171,6 @@ struct PairDma {
   }
 };
 
-// A ring stage given as a constant (std::integral_constant) or at run time (int), and
-// the other stage of the two.
-template <typename S>
-__device__ __forceinline__ int stage_of(S st) {
-  if constexpr (std::is_integral<S>::value) return st;
-  else return S::value;
-}
-template <typename S>
-__device__ __forceinline__ auto other_stage(S st) {
-  if constexpr (std::is_integral<S>::value) return 1 - st;
-  else return std::integral_constant<int, 1 - S::value>{};
-}
-
 // Blocks 0 .. nblk-1 through the two-stage ring, the stage of each block at run time;
 // the last block is the one that masks.
 template <typename Issue, typename Step>

@@ -403,6 +403,20 @@ __device__ __forceinline__ void dma4(uint32_t lds, const void* sbase, uint32_t v
                : "memory", "m0");
 }
 
+// A ring stage given as a constant (std::integral_constant) or at run time (int), and
+// the other stage of a two-stage ring. A constant stage turns every LDS address of the
+// stage into a lane offset plus an immediate.
+template <typename S>
+__device__ __forceinline__ int stage_of(S st) {
+  if constexpr (std::is_integral<S>::value) return st;
+  else return S::value;
+}
+template <typename S>
+__device__ __forceinline__ auto other_stage(S st) {
+  if constexpr (std::is_integral<S>::value) return 1 - st;
+  else return std::integral_constant<int, 1 - S::value>{};
+}
+
 // A operand (8 16-bit elements along head_dim) of mma over a swizzled tile:
 // row r, logical chunk c.
 template <typename Et, int CH>

@@ -50,7 +50,8 @@ template <int D>
 constexpr int b64_waves_per_simd() { return D == 64 ? 4 : 2; }
 constexpr int kB64Keys = 32;      // keys per ring stage
 // ring stages: one block in flight ahead of the one computed (2, 3 and 4 stages measured
-// side by side on the long-document and mixed-batch forwards; 2 was fastest)
+// side by side on the long-document and mixed-batch forwards: 3 was 8% slower, 4 even
+// with 2); the key loop below is written for two
 constexpr int kB64Stages = 2;
 constexpr float kB64Overflow = 65536.f;  // largest block sum of p kept without a new reference
 
@@ -67,7 +68,8 @@ __device__ __forceinline__ void b64_run(const void* __restrict__ qp, const void*
   constexpr int NL = kB64Keys * CH / kB64Threads;  // DMA instructions per lane per tile
   static_assert(NL >= 1 && (kB64Keys * CH) % kB64Threads == 0, "whole DMA instructions per tile");
   constexpr int QB = NQ > 0 ? NQ : 1;           // array extents
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, ql = lane & 31, g = lane >> 5;
+  const int tid = threadIdx.x, lane = tid & 63, ql = lane & 31, g = lane >> 5;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: DMA addresses stay scalar
 
   int qrow[QB];
   bool qvalid[QB];
@@ -96,9 +98,10 @@ __device__ __forceinline__ void b64_run(const void* __restrict__ qp, const void*
   constexpr int TB = kB64Keys * D * 2;   // bytes per tile
   constexpr int STB = 2 * TB;            // bytes per ring stage (K and V tiles)
   const uint32_t ring0 = lds_addr(ring[0][0]);
-  auto issue = [&](int blk) __attribute__((always_inline)) {
+  // block blk into ring stage blk % 2 (a constant, or an int at run time)
+  auto issue = [&](int blk, auto st_tag) __attribute__((always_inline)) {
     const int row0 = lo + blk * kB64Keys;
-    const uint32_t st = static_cast<uint32_t>((blk % kB64Stages) * STB);
+    const uint32_t st = static_cast<uint32_t>(stage_of(st_tag) * STB);
     const char* kb = kbase + static_cast<int64_t>(row0) * rowstride;
     const char* vb = vbase + static_cast<int64_t>(row0) * rowstride;
     if (row0 + kB64Keys <= hi) {
@@ -177,20 +180,6 @@ __device__ __forceinline__ void b64_run(const void* __restrict__ qp, const void*
     m[qb] = mnew;
   };
 
-  constexpr int AHEAD = kB64Stages - 1;  // blocks in flight ahead of the one computed
-  // Wait until block j has landed: `later` blocks issued after it may stay in flight
-  // (each 2*NL DMA instructions; loads complete in order).
-  auto wait_block = [&](int later) __attribute__((always_inline)) {
-    if constexpr (AHEAD - 1 >= 3) {
-      if (later >= 3) { wait_vmcnt<6 * NL>(); return; }
-    }
-    if constexpr (AHEAD - 1 >= 2) {
-      if (later >= 2) { wait_vmcnt<4 * NL>(); return; }
-    }
-    if (later >= 1) { wait_vmcnt<2 * NL>(); return; }
-    wait_vmcnt<0>();
-  };
-
   vec8<Et> pb[QB][2], vt[2][DB];  // block j's probabilities and V^T operands
   auto pv = [&]() __attribute__((always_inline)) {
 #pragma unroll
@@ -203,17 +192,19 @@ __device__ __forceinline__ void b64_run(const void* __restrict__ qp, const void*
 
   // Step j. FIRST: block 0 (each query block's exact maximum becomes its reference).
   // LAST: the sequence's last key block (keys past its end masked).
-  auto step = [&](int j, auto first_tag, auto last_tag) __attribute__((always_inline)) {
+  // st_tag: block j's ring stage, j % 2 (a constant in the loop, so its LDS addresses are a
+  // lane offset plus an immediate)
+  auto step = [&](int j, auto st_tag, auto first_tag, auto last_tag) __attribute__((always_inline)) {
     constexpr bool FIRST = decltype(first_tag)::value;
     constexpr bool LAST = decltype(last_tag)::value;
-    wait_block(min(AHEAD - 1, nblk - 1 - j));
+    wait_vmcnt<0>();  // block j landed (the only block in flight)
     // this wave's reads of block j-1's stage have completed before the barrier, after which
     // the DMA below overwrites that stage
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     raw_barrier();  // block j visible to both waves; both have read block j-1's stage
-    if (j + AHEAD < nblk) issue(j + AHEAD);
+    if (j + 1 < nblk) issue(j + 1, other_stage(st_tag));
     if constexpr (NQ == 0) return;
-    const uint32_t kt = ring0 + static_cast<uint32_t>((j % kB64Stages) * STB);
+    const uint32_t kt = ring0 + static_cast<uint32_t>(stage_of(st_tag) * STB);
     const uint32_t vtl = kt + static_cast<uint32_t>(TB);
     vec8<Et> ka[QS];
 #pragma unroll
@@ -265,14 +256,23 @@ __device__ __forceinline__ void b64_run(const void* __restrict__ qp, const void*
     pv();
   };
 
-  for (int i = 0; i < AHEAD; ++i)
-    if (i < nblk) issue(i);
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+  using T_ = std::true_type;
+  using F_ = std::false_type;
+  issue(0, S0{});
   if (nblk == 1) {
-    step(0, std::true_type{}, std::true_type{});
-  } else {
-    step(0, std::true_type{}, std::false_type{});
-    for (int j = 1; j + 1 < nblk; ++j) step(j, std::false_type{}, std::false_type{});
-    step(nblk - 1, std::false_type{}, std::true_type{});
+    step(0, S0{}, T_{}, T_{});
+  } else {  // blocks 1 .. nblk-1 two per iteration (stages 1, 0), the last one masked
+    step(0, S0{}, T_{}, F_{});
+    int j = 1;
+    for (; j + 2 < nblk; j += 2) {
+      step(j, S1{}, F_{}, F_{});
+      step(j + 1, S0{}, F_{}, F_{});
+    }
+    if (j + 1 < nblk) step(j++, S1{}, F_{}, F_{});
+    step(j, j & 1, F_{}, T_{});  // (the stage at run time: as constants, the two copies of
+                                 // this step spilled registers to scratch)
   }
 
 #pragma unroll
