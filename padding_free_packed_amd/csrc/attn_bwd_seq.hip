@@ -95,32 +95,33 @@ __device__ __forceinline__ bool seq_tile(const int32_t* __restrict__ cu, const i
 // Per-lane LDS offsets of the operands read from a 32-row swizzled stage tile:
 // rows (row ql, logical chunk g*(CH/2) + q: an A operand over head_dim) and the
 // transposed reads (two ds_read_b64_tr_b16 per A operand over the 32 rows, in the
-// row order of the accumulator layout, as mma_tr_swz).
+// row order of the accumulator layout, as mma_tr_swz). The rows 16 s + r of step s = 1
+// have the swizzle of row r (it depends on bits 1-3 of the row), so their offsets are
+// those of step 0 plus 16 rows: only step 0's are kept.
 template <int D>
 struct StageOffsets {
   static constexpr int CH = D / 8, QS = D / 16, DB = D / 32;
+  static constexpr int STEP1 = 16 * CH * 16;  // bytes of 16 rows
   int row[QS];
-  int tr[2][2][DB];
+  int tr[2][DB];  // step 0, rows 4g + sub/4 (+8 for [1])
   __device__ __forceinline__ StageOffsets(int lane) {
     const int ql = lane & 31, g = lane >> 5, sub = lane & 15, grp = (lane >> 4) & 1;
 #pragma unroll
     for (int q = 0; q < QS; ++q) row[q] = chunk_off<CH>(ql, g * (CH / 2) + q);
 #pragma unroll
-    for (int s = 0; s < 2; ++s)
+    for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
-      for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-        for (int db = 0; db < DB; ++db)
-          tr[s][hh][db] = chunk_off<CH>(16 * s + 4 * g + (sub >> 2) + 8 * hh, 4 * db + 2 * grp + ((sub >> 1) & 1)) +
-                          8 * (sub & 1);
+      for (int db = 0; db < DB; ++db)
+        tr[hh][db] = chunk_off<CH>(4 * g + (sub >> 2) + 8 * hh, 4 * db + 2 * grp + ((sub >> 1) & 1)) + 8 * (sub & 1);
   }
 };
 
 // The transposed A operand of step s, head-dim block db, from the tile at LDS byte tile.
 template <typename Et, int D>
 __device__ __forceinline__ vec8<Et> tr_operand(uint32_t tile, const StageOffsets<D>& so, int s, int db) {
-  const u16x4 lo4 = ds_read_tr16_at(tile + so.tr[s][0][db]);
-  const u16x4 hi4 = ds_read_tr16_at(tile + so.tr[s][1][db]);
+  const uint32_t t = tile + static_cast<uint32_t>(s * StageOffsets<D>::STEP1);
+  const u16x4 lo4 = ds_read_tr16_at(t + so.tr[0][db]);
+  const u16x4 hi4 = ds_read_tr16_at(t + so.tr[1][db]);
   return as_vec8<Et>(u16x8{lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]});
 }
 
@@ -192,12 +193,8 @@ __device__ __forceinline__ void run_blocks(int nblk, Issue& issue, Step& step) {
     step(j, S0{}, std::false_type{});
     step(j + 1, S1{}, std::false_type{});
   }
-  if (j + 1 < nblk) {
-    step(j, S0{}, std::false_type{});
-    step(j + 1, S1{}, std::true_type{});
-  } else {
-    step(j, S0{}, std::true_type{});
-  }
+  if (j + 1 < nblk) step(j++, S0{}, std::false_type{});
+  step(j, j & 1, std::true_type{});  // one copy of the masked step, its stage at run time
 }
 
 template <typename Et, int D>
@@ -326,7 +323,7 @@ __global__ __launch_bounds__(kThreads, kKvWaves) void bwd_kv_seq_kernel(
     }
   };
 
-  run_blocks_dyn(nblk, issue, step);
+  run_blocks(nblk, issue, step);
 
   if (kvalid) {
     store_acc_row<Et, D>(dkp, roff, dk, scale, g);

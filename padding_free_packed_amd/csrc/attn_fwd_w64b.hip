@@ -153,10 +153,14 @@ __device__ __forceinline__ void b64_run(const void* __restrict__ qp, const void*
   }
 
   // p = exp2(c s - m) of one query block in place, returning the block's sum
+  // (two chains of sums, each started at its first p: p >= 0, so 0 + p would be the same
+  // value, but the compiler cannot drop that add)
   auto probs = [&](int qb, floatx16& s) __attribute__((always_inline)) {
-    float a0 = 0.f, a1 = 0.f;
+    s[0] = __builtin_amdgcn_exp2f(fmaf(s[0], c, -m[qb]));
+    s[1] = __builtin_amdgcn_exp2f(fmaf(s[1], c, -m[qb]));
+    float a0 = s[0], a1 = s[1];
 #pragma unroll
-    for (int i = 0; i < 16; i += 2) {
+    for (int i = 2; i < 16; i += 2) {
       s[i] = __builtin_amdgcn_exp2f(fmaf(s[i], c, -m[qb]));
       s[i + 1] = __builtin_amdgcn_exp2f(fmaf(s[i + 1], c, -m[qb]));
       a0 += s[i];
