@@ -172,17 +172,6 @@ struct PairDma {
   }
 };
 
-// Blocks 0 .. nblk-1 through the two-stage ring, the stage of each block at run time;
-// the last block is the one that masks.
-template <typename Issue, typename Step>
-__device__ __forceinline__ void run_blocks_dyn(int nblk, Issue& issue, Step& step) {
-  issue(0, 0);
-  for (int j = 0; j + 1 < nblk; ++j) step(j, j & 1, std::false_type{});
-  step(nblk - 1, (nblk - 1) & 1, std::true_type{});
-}
-
-// The same, two blocks per iteration so that each step's stage is a constant (every LDS
-// address is then a lane offset plus an immediate).
 template <typename Issue, typename Step>
 __device__ __forceinline__ void run_blocks(int nblk, Issue& issue, Step& step) {
   using S0 = std::integral_constant<int, 0>;
