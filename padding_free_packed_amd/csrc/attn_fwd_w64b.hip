@@ -130,17 +130,19 @@ __device__ __forceinline__ void b64_run(const void* __restrict__ qp, const void*
 #pragma unroll
   for (int q = 0; q < QS; ++q) koff[q] = chunk_off<CH>(ql, g * (CH / 2) + q);
   const int sub = lane & 15, grp = (lane >> 4) & 1;
-  int voff[2][2][DB];  // V^T operand: [s][hi][db], row 16s+4g+sub/4 (+8 for hi)
+  // V^T operand of step s: rows 16s + 4g + sub/4 (+8 for hi). Rows 16 + r carry the
+  // swizzle of row r (it depends on bits 1-3 of the row), so step 1's offsets are step 0's
+  // plus 16 rows, a constant: only step 0's are kept, voff[hi][db].
+  int voff[2][DB];
+  constexpr int VSTEP1 = 16 * CH * 16;
 #pragma unroll
-  for (int s = 0; s < 2; ++s)
+  for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
-    for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        const int rowa = 16 * s + 4 * g + (sub >> 2) + 8 * hh;
-        const int cc = 4 * db + 2 * grp + ((sub >> 1) & 1);
-        voff[s][hh][db] = chunk_off<CH>(rowa, cc) + 8 * (sub & 1);
-      }
+    for (int db = 0; db < DB; ++db) {
+      const int rowa = 4 * g + (sub >> 2) + 8 * hh;
+      const int cc = 4 * db + 2 * grp + ((sub >> 1) & 1);
+      voff[hh][db] = chunk_off<CH>(rowa, cc) + 8 * (sub & 1);
+    }
 
   floatx16 o[QB][DB];
   float m[QB], l[QB];
@@ -224,8 +226,8 @@ __device__ __forceinline__ void b64_run(const void* __restrict__ qp, const void*
     for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
-        const u16x4 lo4 = ds_read_tr16_at(vtl + voff[s2][0][db]);
-        const u16x4 hi4 = ds_read_tr16_at(vtl + voff[s2][1][db]);
+        const u16x4 lo4 = ds_read_tr16_at(vtl + s2 * VSTEP1 + voff[0][db]);
+        const u16x4 hi4 = ds_read_tr16_at(vtl + s2 * VSTEP1 + voff[1][db]);
         vt[s2][db] = as_vec8<Et>(u16x8{lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]});
       }
     if constexpr (LAST) {  // keys past the sequence's end get no weight
