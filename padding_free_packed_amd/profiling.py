@@ -51,7 +51,10 @@ KERNEL_PATTERNS = {
     "worklist": r"worklist_kernel",
     "plan": r"plan_kernel",
 }
-COPY_PATTERN = r"copy|elementwise"
+# the copy probe: bench.py's 1 GiB device-to-device tensor copy, which the runtime runs as
+# its blit kernel (torch's own elementwise kernels, e.g. the bf16 conversion of the input
+# draws, also read and write gigabytes and must not be taken for it)
+COPY_PATTERN = r"__amd_rocclr_copyBuffer"
 
 
 def source_hash(kernel: str) -> str:
