@@ -152,10 +152,9 @@ struct PairDma {
     const int rs = min(r, nrows - 1);
     return static_cast<uint32_t>(rs * (tl ? s1 : s0) + hoff + (pc ^ (swz(r) & (CH - 1))) * 16);
   }
-  // block of rows row0 .. row0 + RS - 1 (nrows of them inside the sequence) into the stage at LDS byte st
-  __device__ __forceinline__ void issue(uint32_t st, const char* b0, const char* b1, int row0, int nrows) const {
-    const char* p0 = b0 + static_cast<int64_t>(row0) * s0;
-    const char* p1 = b1 + static_cast<int64_t>(row0) * s1;
+  // the block whose first rows are at p0 and p1 (nrows of its RS rows inside the sequence)
+  // into the stage at LDS byte st
+  __device__ __forceinline__ void issue(uint32_t st, const char* p0, const char* p1, int nrows) const {
     if (nrows >= RS) {
 #pragma unroll
       for (int j = 0; j < NI; ++j) dma16(dst(st, j), (j * kThreads + wv * 64) / TC ? p1 : p0, off[j]);
@@ -176,7 +175,7 @@ template <typename Issue, typename Step>
 __device__ __forceinline__ void run_blocks(int nblk, Issue& issue, Step& step) {
   using S0 = std::integral_constant<int, 0>;
   using S1 = std::integral_constant<int, 1>;
-  issue(0, S0{});
+  issue(S0{});
   int j = 0;
   for (; j + 2 < nblk; j += 2) {
     step(j, S0{}, std::false_type{});
@@ -223,13 +222,20 @@ __global__ __launch_bounds__(kThreads, kKvWaves) void bwd_kv_seq_kernel(
   const float* nlh = nl + static_cast<int64_t>(h) * N;
   const uint32_t ring0 = lds_addr(ring[0]);
   const int nblk = (hi - lo + RS - 1) / RS;
-  // block blk into ring stage ST = blk % 2
-  auto issue = [&](int blk, auto st_tag) __attribute__((always_inline)) {
+  // The next block in order into ring stage st_tag (its index % 2); the source rows
+  // advance by a constant per block.
+  const char* qnext = qbase + static_cast<int64_t>(lo) * dma.s0;
+  const char* dnext = dbase + static_cast<int64_t>(lo) * dma.s1;
+  int rnext = lo;
+  auto issue = [&](auto st_tag) __attribute__((always_inline)) {
     const int ST = stage_of(st_tag);
-    const int row0 = lo + blk * RS;
+    const int row0 = rnext;
     const int nrows = hi - row0;
     const uint32_t st = ring0 + static_cast<uint32_t>(ST * SB);
-    dma.issue(st, qbase, dbase, row0, nrows);
+    dma.issue(st, qnext, dnext, nrows);
+    rnext += RS;
+    qnext += RS * dma.s0;
+    dnext += RS * dma.s1;
     if (wv < 2 * RS / 64) {  // dwords u = 64 wv + lane: nl (u < RS) then nd of the RS rows
       const int u = 64 * wv + lane;
       const int arr = u >= RS, r = u - arr * RS;
@@ -297,7 +303,7 @@ __global__ __launch_bounds__(kThreads, kKvWaves) void bwd_kv_seq_kernel(
     // which the DMA below overwrites that stage
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     raw_barrier();  // block j visible to every wave; all have read block j-1's stage
-    if (j + 1 < nblk) issue(j + 1, other_stage(st_tag));
+    if (j + 1 < nblk) issue(other_stage(st_tag));
     if (!active) return;
     const uint32_t st = ring0 + static_cast<uint32_t>(ST * SB);
 #pragma unroll
@@ -356,11 +362,17 @@ __global__ __launch_bounds__(kThreads, kQWaves) void bwd_q_seq_kernel(
   const char* vbase = static_cast<const char*>(vp);
   const uint32_t ring0 = lds_addr(ring[0]);
   const int nblk = (hi - lo + RS - 1) / RS;
-  // block blk into ring stage ST = blk % 2
-  auto issue = [&](int blk, auto st_tag) __attribute__((always_inline)) {
+  // The next block in order into ring stage st_tag (its index % 2); the source rows
+  // advance by a constant per block.
+  const char* knext = kbase + static_cast<int64_t>(lo) * dma.s0;
+  const char* vnext = vbase + static_cast<int64_t>(lo) * dma.s1;
+  int rnext = lo;
+  auto issue = [&](auto st_tag) __attribute__((always_inline)) {
     const int ST = stage_of(st_tag);
-    const int row0 = lo + blk * RS;
-    dma.issue(ring0 + static_cast<uint32_t>(ST * SB), kbase, vbase, row0, hi - row0);
+    dma.issue(ring0 + static_cast<uint32_t>(ST * SB), knext, vnext, hi - rnext);
+    rnext += RS;
+    knext += RS * dma.s0;
+    vnext += RS * dma.s1;
   };
 
   const StageOffsets<D> so(lane);
@@ -397,7 +409,7 @@ __global__ __launch_bounds__(kThreads, kQWaves) void bwd_q_seq_kernel(
     wait_vmcnt<0>();
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     raw_barrier();
-    if (j + 1 < nblk) issue(j + 1, other_stage(st_tag));
+    if (j + 1 < nblk) issue(other_stage(st_tag));
     if (!active) return;
     const uint32_t st = ring0 + static_cast<uint32_t>(ST * SB);
 #pragma unroll

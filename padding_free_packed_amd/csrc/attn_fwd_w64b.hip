@@ -98,12 +98,20 @@ __device__ __forceinline__ void b64_run(const void* __restrict__ qp, const void*
   constexpr int TB = kB64Keys * D * 2;   // bytes per tile
   constexpr int STB = 2 * TB;            // bytes per ring stage (K and V tiles)
   const uint32_t ring0 = lds_addr(ring[0][0]);
-  // block blk into ring stage blk % 2 (a constant, or an int at run time)
-  auto issue = [&](int blk, auto st_tag) __attribute__((always_inline)) {
-    const int row0 = lo + blk * kB64Keys;
+  // The next block in order into ring stage st_tag (its index % 2, a constant or an int at
+  // run time); its source rows advance by a constant per block (no per-block multiply).
+  const int64_t blkbytes = static_cast<int64_t>(kB64Keys) * rowstride;
+  const char* knext = kbase + static_cast<int64_t>(lo) * rowstride;
+  const char* vnext = vbase + static_cast<int64_t>(lo) * rowstride;
+  int rnext = lo;
+  auto issue = [&](auto st_tag) __attribute__((always_inline)) {
+    const int row0 = rnext;
     const uint32_t st = static_cast<uint32_t>(stage_of(st_tag) * STB);
-    const char* kb = kbase + static_cast<int64_t>(row0) * rowstride;
-    const char* vb = vbase + static_cast<int64_t>(row0) * rowstride;
+    const char* kb = knext;
+    const char* vb = vnext;
+    rnext += kB64Keys;
+    knext += blkbytes;
+    vnext += blkbytes;
     if (row0 + kB64Keys <= hi) {
 #pragma unroll
       for (int j = 0; j < NL; ++j) {
@@ -208,7 +216,7 @@ __device__ __forceinline__ void b64_run(const void* __restrict__ qp, const void*
     // the DMA below overwrites that stage
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     raw_barrier();  // block j visible to both waves; both have read block j-1's stage
-    if (j + 1 < nblk) issue(j + 1, other_stage(st_tag));
+    if (j + 1 < nblk) issue(other_stage(st_tag));
     if constexpr (NQ == 0) return;
     const uint32_t kt = ring0 + static_cast<uint32_t>(stage_of(st_tag) * STB);
     const uint32_t vtl = kt + static_cast<uint32_t>(TB);
@@ -266,7 +274,7 @@ __device__ __forceinline__ void b64_run(const void* __restrict__ qp, const void*
   using S1 = std::integral_constant<int, 1>;
   using T_ = std::true_type;
   using F_ = std::false_type;
-  issue(0, S0{});
+  issue(S0{});
   if (nblk == 1) {
     step(0, S0{}, T_{}, T_{});
   } else {  // blocks 1 .. nblk-1 two per iteration (stages 1, 0), the last one masked
