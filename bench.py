@@ -380,7 +380,9 @@ class Case:
             self.dq_first = torch.empty_like(self.q_first)
             self.dk_first, self.dv_first = torch.empty_like(self.k), torch.empty_like(self.v)
         self.ws_pack = pe.workspace(pe.pe_pack_workspace_size(B, S, D, self.code), dev)
-        self.ws = pe.workspace(pe.pe_attn_workspace_size(B, N, H, d, self.code, with_bwd), dev)
+        # a backward case takes the workspace of the fastest backward path
+        self.ws = pe.workspace(pe.pe_attn_bwd_workspace_size(B, N, S, H, d, self.code) if with_bwd
+                               else pe.pe_attn_workspace_size(B, N, H, d, self.code, False), dev)
         self.pe = pe
         self.call("pack")  # cu_seqlens for every later call
 

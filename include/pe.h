@@ -279,9 +279,21 @@ pe_status pe_varlen_attn_bwd_first_token(const void* dout_first, const void* q_f
  *   dout, q, k, v, out   device [total_tokens, num_heads, head_dim] of `dtype`
  *   lse                  device fp32 [num_heads, total_tokens] from the forward
  *   dq, dk, dv           device [total_tokens, num_heads, head_dim] of `dtype`, written
- *   workspace            at least pe_attn_workspace_size(..., for_backward=1)
+ *   workspace            at least pe_attn_workspace_size(..., for_backward=1); with
+ *                        pe_attn_bwd_workspace_size(...) bytes (more for fp32 at head dims
+ *                        32 and 64) the fp32 global-attention path passes the blocks of dS
+ *                        from its dK/dV pass to its dQ pass through the workspace instead of
+ *                        recomputing S and dP for dQ. Both sizes give gradients within the
+ *                        same tolerances; each is deterministic.
  * Deterministic: no floating-point atomics; the same inputs give the same bits.
  */
+/* The workspace size of the fastest backward path: pe_attn_workspace_size(..., 1), plus for
+ * fp32 at head dims 32 and 64 one 32x32 fp32 block per (32-row query tile, 32-row key
+ * block) of a sequence of max_seq_len rows, per head:
+ * num_heads * (total_tokens / 32 + num_seqs) * ceil(max_seq_len / 32) * 4096 bytes.
+ * Returns 0 for invalid sizes. */
+size_t pe_attn_bwd_workspace_size(int32_t num_seqs, int64_t total_tokens, int32_t max_seq_len,
+                                  int32_t num_heads, int32_t head_dim, pe_dtype dtype);
 pe_status pe_varlen_attn_bwd(const void* dout, const void* q, const void* k, const void* v,
                              const void* out, const float* lse, const int32_t* cu_seqlens,
                              int32_t num_seqs, int64_t total_tokens, int32_t max_seq_len,

@@ -61,6 +61,19 @@ size_t items_bytes(int32_t num_seqs, int64_t total_tokens) {
   return round_up(static_cast<size_t>(total_tokens / pe::kAttnWaveRows + num_seqs + 1) * sizeof(int32_t));
 }
 
+// Elements between rows of separate [N, H, d] tensors.
+int64_t dense_ld(int32_t num_heads, int32_t head_dim) { return static_cast<int64_t>(num_heads) * head_dim; }
+
+// The fp32 backward's dS hand-off: one 32x32 fp32 block per (query tile, key block) of every
+// sequence and head, [H][N/32 + B][nb_max][1024] floats (nb_max: 32-row blocks of a sequence of
+// max_seq_len rows).
+int32_t nb_max(int32_t max_seq_len) { return (max_seq_len + pe::kAttnWaveRows - 1) / pe::kAttnWaveRows; }
+size_t ds_bytes(int32_t num_seqs, int64_t total_tokens, int32_t max_seq_len, int32_t num_heads) {
+  return round_up(static_cast<size_t>(num_heads) *
+                  static_cast<size_t>(total_tokens / pe::kAttnWaveRows + num_seqs) *
+                  static_cast<size_t>(nb_max(max_seq_len)) * 1024 * sizeof(float));
+}
+
 // Checks shared by the attention calls.
 pe_status check_attn_args(int32_t num_seqs, int64_t total_tokens, int32_t max_seq_len, int32_t num_heads,
                           int32_t head_dim, int dtype, float scale) {
@@ -186,6 +199,15 @@ size_t pe_attn_workspace_size(int32_t num_seqs, int64_t total_tokens, int32_t nu
   return s;
 }
 
+size_t pe_attn_bwd_workspace_size(int32_t num_seqs, int64_t total_tokens, int32_t max_seq_len, int32_t num_heads,
+                                  int32_t head_dim, pe_dtype dtype) {
+  if (num_seqs < 1 || total_tokens < 0 || num_heads < 1 || max_seq_len < 1) return 0;
+  size_t s = pe_attn_workspace_size(num_seqs, total_tokens, num_heads, head_dim, dtype, 1);
+  if (dtype == PE_FP32 && pe::attn_f32_wave_supported(head_dim, dense_ld(num_heads, head_dim), num_heads))
+    s += ds_bytes(num_seqs, total_tokens, max_seq_len, num_heads);
+  return s;
+}
+
 }  // extern "C"
 
 namespace {
@@ -226,9 +248,6 @@ pe_status fwd_impl(const void* q, const void* k, const void* v, const int32_t* c
   return hip_status(e);
 }
 
-
-// Elements between rows of separate [N, H, d] tensors.
-int64_t dense_ld(int32_t num_heads, int32_t head_dim) { return static_cast<int64_t>(num_heads) * head_dim; }
 
 // A window at least max_seq_len - 1 keeps every key of every sequence: global attention.
 int32_t effective_window(int32_t window, int32_t max_seq_len) { return window >= max_seq_len - 1 ? -1 : window; }
@@ -411,12 +430,20 @@ pe_status bwd_impl(const void* dout, const void* q, const void* k, const void* v
   }
   // the fp32 one-wave kernels take the sequence-aligned list, every other kernel the 128-row one
   const bool wave = dtype == PE_FP32 && pe::attn_f32_wave_supported(head_dim, ld, num_heads);
+  // fp32 global attention with a workspace of pe_attn_bwd_workspace_size: the dK/dV pass hands
+  // its dS blocks to the dQ pass through the rest of the workspace
+  float* ds = nullptr;
+  if (wave && win < 0) {
+    const size_t base = pe_attn_workspace_size(num_seqs, total_tokens, num_heads, head_dim, dtype, 1);
+    if (workspace_bytes >= base + ds_bytes(num_seqs, total_tokens, max_seq_len, num_heads))
+      ds = reinterpret_cast<float*>(static_cast<char*>(workspace) + base);
+  }
   hipError_t e = wave ? pe::launch_seq_worklist(cu_seqlens, num_seqs, total_tokens, pe::kAttnWaveRows, items32, st)
                       : pe::launch_worklist(cu_seqlens, num_seqs, total_tokens, pe::kAttnTileRows, items, st);
   if (e != hipSuccess) return PE_ERR_HIP;
   e = pe::launch_attn_bwd(dtype, head_dim, dout, q, k, v, out, lse, cu_seqlens, wave ? nullptr : items,
                           wave ? items32 : nullptr, num_seqs, static_cast<int32_t>(total_tokens), num_heads, win, ld,
-                          softmax_scale, dq, dk, dv, delta, st);
+                          softmax_scale, dq, dk, dv, delta, ds, nb_max(max_seq_len), st);
   if (e == hipErrorNotSupported) return PE_ERR_UNSUPPORTED;
   return hip_status(e);
 }

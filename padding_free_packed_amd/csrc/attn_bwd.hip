@@ -293,23 +293,35 @@ template <typename Et, int D>
 hipError_t bwd_dispatch(const void* dout, const void* q, const void* k, const void* v, const void* out,
                         const float* lse, const int32_t* cu, const int32_t* items, const int32_t* items32, int32_t B,
                         int32_t N, int32_t H, int32_t win, int64_t ld, float scale, void* dq, void* dk, void* dv,
-                        float* delta, hipStream_t stream) {
+                        float* delta, float* ds, int32_t nb_max, hipStream_t stream) {
   using G = Geo<Et, D>;
   if (N == 0) return hipSuccess;
+  const int64_t lanes = static_cast<int64_t>(N) * H * pow2_ceil(G::CH);
+  auto delta_pass = [&]() {
+    hipEvent_t ev_bwd_delta = timing_start(stream);
+    hipLaunchKernelGGL((bwd_delta_kernel<Et, D>), dim3(static_cast<unsigned>((lanes + 255) / 256)), dim3(256), 0,
+                       stream, dout, out, N, H, delta);
+    timing_stop("bwd_delta", ev_bwd_delta, stream);
+    return hipGetLastError();
+  };
+  if (!kIs16<Et> && items32 != nullptr && attn_f32_wave_supported(D, ld, H) && ds != nullptr && win < 0) {
+    // dS handed from the dK/dV pass to the dQ pass: 10 products of the size of S instead of 14
+    hipError_t e = delta_pass();
+    if (e != hipSuccess) return e;
+    e = launch_bwd_dkdv_f32_wave(D, dout, q, k, v, lse, delta, cu, items32, B, N, H, win, ld, scale, dk, dv, ds,
+                                 nb_max, stream);
+    if (e != hipSuccess) return e;
+    return launch_bwd_dq_ds_f32_wave(D, k, ds, nb_max, cu, items32, B, N, H, ld, scale, dq, stream);
+  }
   if (!kIs16<Et> && items32 != nullptr && attn_f32_wave_supported(D, ld, H)) {
     // the fp32 dQ pass computes D itself and stores it for the dK/dV pass
     hipError_t e = launch_bwd_dq_f32_wave(D, dout, q, k, v, out, lse, delta, cu, items32, B, N, H, win, ld, scale,
                                           dq, stream);
     if (e != hipSuccess) return e;
     return launch_bwd_dkdv_f32_wave(D, dout, q, k, v, lse, delta, cu, items32, B, N, H, win, ld, scale, dk, dv,
-                                    stream);
+                                    nullptr, 0, stream);
   }
-  const int64_t lanes = static_cast<int64_t>(N) * H * pow2_ceil(G::CH);
-  hipEvent_t ev_bwd_delta = timing_start(stream);
-  hipLaunchKernelGGL((bwd_delta_kernel<Et, D>), dim3(static_cast<unsigned>((lanes + 255) / 256)), dim3(256), 0,
-                   stream, dout, out, N, H, delta);
-  timing_stop("bwd_delta", ev_bwd_delta, stream);
-  hipError_t e = hipGetLastError();
+  hipError_t e = delta_pass();
   if (e != hipSuccess) return e;
   const int T = (N + kAttnTileRows - 1) / kAttnTileRows;
   const unsigned blocks = static_cast<unsigned>(static_cast<int64_t>(T) * H);
@@ -332,15 +344,16 @@ hipError_t bwd_dispatch(const void* dout, const void* q, const void* k, const vo
 hipError_t launch_attn_bwd(int dt, int D, const void* dout, const void* q, const void* k, const void* v,
                            const void* out, const float* lse, const int32_t* cu, const int32_t* items,
                            const int32_t* items32, int32_t B, int32_t N, int32_t H, int32_t win, int64_t ld,
-                           float scale, void* dq, void* dk, void* dv, float* delta, hipStream_t stream) {
+                           float scale, void* dq, void* dk, void* dv, float* delta, float* ds, int32_t nb_max,
+                           hipStream_t stream) {
 #define PE_BWD_CASE(DD)                                                                                       \
   case DD:                                                                                                   \
     return dt == kDtF32  ? bwd_dispatch<float, DD>(dout, q, k, v, out, lse, cu, items, items32, B, N, H, win, ld, \
-                                                  scale, dq, dk, dv, delta, stream)                             \
+                                                  scale, dq, dk, dv, delta, ds, nb_max, stream)                             \
            : dt == kDtF16 ? bwd_dispatch<_Float16, DD>(dout, q, k, v, out, lse, cu, items, items32, B, N, H, win, \
-                                                     ld, scale, dq, dk, dv, delta, stream)                      \
+                                                     ld, scale, dq, dk, dv, delta, ds, nb_max, stream)                      \
                          : bwd_dispatch<__bf16, DD>(dout, q, k, v, out, lse, cu, items, items32, B, N, H, win, ld, \
-                                                   scale, dq, dk, dv, delta, stream);
+                                                   scale, dq, dk, dv, delta, ds, nb_max, stream);
   switch (D) {
     PE_HEAD_DIMS(PE_BWD_CASE)
     default: return hipErrorInvalidValue;

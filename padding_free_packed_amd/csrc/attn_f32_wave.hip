@@ -46,6 +46,14 @@ __device__ __forceinline__ bool seq_tile(const int32_t* __restrict__ cu, const i
   return sp.r0 < sp.hi;
 }
 
+// The lane's index in the wave, computed where it is used: an opaque instruction, so the
+// compiler neither hoists it out of a loop nor keeps it live in a register across one.
+__device__ __forceinline__ int lane_now() {
+  int l;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+  return l;
+}
+
 // Buffer resource over `rows` rows of `stride` floats from `base`: a load at a byte
 // offset at or past rows * stride * 4 returns 0 and touches no memory, so rows past a
 // block's end need neither clamping nor per-lane address arithmetic. rows <= 32 here,
@@ -377,6 +385,87 @@ __global__ __launch_bounds__(64, 2) void bwd_dq_f32_kernel(
   if (qvalid) store_acc_row<float, D>(dqp, static_cast<int64_t>(qrow) * ld + hoff, dq, scale, g);
 }
 
+// dQ from the dS blocks the dK/dV pass stored (global attention): per 32-key block of the
+// wave's sequence, dQ^T += K^T dS^T with the K scalars as A operands, 32 MFMAs per block at
+// d = 64 instead of the 96 that recompute S and dP. A block arrives in the dK/dV
+// accumulator layout (lane = key, chunk-major); the B operands want lane = query, so each block passes
+// through 4 KB of LDS: written as the wave's 16-byte chunks, read back as single floats.
+// Rows are placed so that both sides are free of bank conflicts: row L of the block
+// (the 16 floats of stored lane L) sits at row prow(L) = L ^ bit2(L) ^ 2 bit5(L), its
+// chunk c at chunk c ^ ((L >> 2) & 3).
+template <int D>
+__global__ __launch_bounds__(64, 4) void bwd_dq_ds_f32_kernel(const float* __restrict__ kp, const float* __restrict__ dsp,
+                                                            const int32_t* __restrict__ cu,
+                                                            const int32_t* __restrict__ items, int32_t B, int32_t H,
+                                                            int32_t T, int32_t NB, int64_t ld, float scale,
+                                                            float* __restrict__ dqp) {
+  constexpr int DB = D / 32;
+  __shared__ __align__(16) float tile[1024];
+  const int lin = xcd_remap(blockIdx.x, gridDim.x);
+  const int h = lin / T, t = lin - h * T;
+  const int lane = threadIdx.x, ql = lane & 31, g = lane >> 5;
+
+  SeqTile sp;
+  if (!seq_tile(cu, items, t, B, sp)) return;
+  const int qrow = sp.r0 + ql;
+  const bool qvalid = qrow < sp.rend;
+  const uint32_t LD = static_cast<uint32_t>(ld);
+  const int64_t hoff = static_cast<int64_t>(h) * D;
+  const int sb = sp.lo / kRows + items[t];  // slot of the sequence's first tile
+  const float* row = dsp + (static_cast<int64_t>(h) * T + sb + (sp.r0 - sp.lo) / kRows) * NB * 1024 + lane * 4;
+  const uint32_t vtr = (static_cast<uint32_t>(4 * g) * LD + ql) * 4u;
+
+  // write side: float index of this lane's chunk c4
+  int wr[4];
+#pragma unroll
+  for (int c4 = 0; c4 < 4; ++c4)
+    wr[c4] = 16 * (lane ^ ((lane >> 2) & 1) ^ (((lane >> 5) & 1) << 1)) + 4 * (c4 ^ ((lane >> 2) & 3));
+  // read side: at step st = 8 u + 4 a + b the lane takes dS[ql][key], key = 8 (st/4) + 4 g + b,
+  // element 4 (ql/8) + ql%4 of stored lane key + 32 gq (gq = bit 2 of ql); its float index
+  // is rd[a][b] + 256 u
+  const int gq = (ql >> 2) & 1;
+  int rd[2][4];
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const int prow = 8 * a + (b ^ (g | (gq << 1))) + 4 * g + 32 * gq;
+      rd[a][b] = 16 * prow + 4 * ((ql >> 3) ^ ((2 * a + g) & 3)) + (ql & 3);
+    }
+
+  floatx16 dq[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) dq[db] = floatx16{};
+  const int nb = min(NB, (sp.hi - sp.lo + kRows - 1) / kRows);  // blocks the dK/dV pass stored
+  for (int j = 0; j < nb; ++j) {
+    const int kb = sp.lo + j * kRows;
+    const floatx4* src = reinterpret_cast<const floatx4*>(row + static_cast<int64_t>(j) * 1024);
+    const floatx4 x0 = __builtin_nontemporal_load(src), x1 = __builtin_nontemporal_load(src + 64),
+                  x2 = __builtin_nontemporal_load(src + 128), x3 = __builtin_nontemporal_load(src + 192);
+    // K[key(st)][d] for the key order of the dS operands; rows past the sequence read 0
+    const auto rk = rows_rsrc(kp + (static_cast<int64_t>(kb) * LD + hoff), min(kRows, sp.hi - kb), LD);
+    float kt[16][DB];
+#pragma unroll
+    for (int st = 0; st < 16; ++st)
+#pragma unroll
+      for (int db = 0; db < DB; ++db) kt[st][db] = buf_f32(rk, vtr + 128u * db, (8u * (st >> 2) + (st & 3)) * LD * 4u);
+    __syncthreads();  // the previous block's reads are done
+    *reinterpret_cast<floatx4*>(&tile[wr[0]]) = x0;
+    *reinterpret_cast<floatx4*>(&tile[wr[1]]) = x1;
+    *reinterpret_cast<floatx4*>(&tile[wr[2]]) = x2;
+    *reinterpret_cast<floatx4*>(&tile[wr[3]]) = x3;
+    __syncthreads();
+    float ds[16];
+#pragma unroll
+    for (int st = 0; st < 16; ++st) ds[st] = tile[rd[(st >> 2) & 1][st & 3] + 256 * (st >> 3)];
+#pragma unroll
+    for (int st = 0; st < 16; ++st)
+#pragma unroll
+      for (int db = 0; db < DB; ++db) dq[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(kt[st][db], ds[st], dq[db], 0, 0, 0);
+  }
+  if (qvalid) store_acc_row<float, D>(dqp, static_cast<int64_t>(qrow) * ld + hoff, dq, scale, g);
+}
+
 }  // namespace
 
 hipError_t launch_bwd_dq_f32_wave(int D, const void* dout, const void* q, const void* k, const void* v,
@@ -424,7 +513,8 @@ __global__ __launch_bounds__(64, 2) void bwd_dkdv_f32_kernel(
     const float* __restrict__ dop, const float* __restrict__ qp, const float* __restrict__ kp,
     const float* __restrict__ vp, const float* __restrict__ lse, const float* __restrict__ delta,
     const int32_t* __restrict__ cu, const int32_t* __restrict__ items, int32_t B, int32_t N, int32_t H, int32_t T,
-    int32_t win, int64_t ld, float c, float scale, float* __restrict__ dkp, float* __restrict__ dvp) {
+    int32_t win, int64_t ld, float c, float scale, float* __restrict__ dkp, float* __restrict__ dvp,
+    float* __restrict__ dsp, int32_t NB) {
   constexpr int HALF = D / 2, DB = D / 32;
   __shared__ __align__(16) float stat[2][kRows];
   const int lin = xcd_remap(blockIdx.x, gridDim.x);
@@ -529,6 +619,23 @@ __global__ __launch_bounds__(64, 2) void bwd_dkdv_f32_kernel(
       }
     }
     __syncthreads();
+    // hand dS to the dQ pass (global attention: query blocks start at lo); a key block at
+    // or past NB (a length above the stated maximum) writes nothing
+    if (dsp != nullptr && r0 - sp.lo < NB * kRows) {
+      // block (query block (qb - lo)/32, key block (r0 - lo)/32) of the sequence in the
+      // accumulator layout, chunk-major: the lane's c-th four values (queries
+      // 8 c + 4 g + 0..3 of key ql) go to float4 c * 64 + lane, so each of the four stores
+      // writes 1 KB contiguous. Keys past the sequence store finite values that meet
+      // zero K rows in the dQ pass. The lane offset is recomputed here (not kept across
+      // the loop, where it would take a register the loop cannot spare).
+      const int sb = sp.lo / kRows + items[t];  // slot of the sequence's first tile
+      const int64_t blk = (static_cast<int64_t>(h) * T + sb + (qb - sp.lo) / kRows) * NB + (r0 - sp.lo) / kRows;
+      floatx4* dst = reinterpret_cast<floatx4*>(dsp + blk * 1024) + lane_now();
+#pragma unroll
+      for (int c4 = 0; c4 < 4; ++c4)  // streamed: read once by the dQ pass
+        __builtin_nontemporal_store(floatx4{dp[4 * c4], dp[4 * c4 + 1], dp[4 * c4 + 2], dp[4 * c4 + 3]},
+                                    dst + 64 * c4);
+    }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       if (j > 0 && qb + 8 * j >= wq1) break;
@@ -553,7 +660,7 @@ __global__ __launch_bounds__(64, 2) void bwd_dkdv_f32_kernel(
 hipError_t launch_bwd_dkdv_f32_wave(int D, const void* dout, const void* q, const void* k, const void* v,
                                     const float* lse, const float* delta, const int32_t* cu, const int32_t* items32,
                                     int32_t B, int32_t N, int32_t H, int32_t win, int64_t ld, float scale, void* dk,
-                                    void* dv, hipStream_t stream) {
+                                    void* dv, float* ds, int32_t nb_max, hipStream_t stream) {
   const int T = N / kRows + B;  // slots of the sequence-aligned work list
   const int64_t blocks = static_cast<int64_t>(T) * H;
   if (blocks == 0) return hipSuccess;
@@ -564,15 +671,35 @@ hipError_t launch_bwd_dkdv_f32_wave(int D, const void* dout, const void* q, cons
     hipLaunchKernelGGL((bwd_dkdv_f32_kernel<32>), gd, bd, 0, stream, static_cast<const float*>(dout),
                        static_cast<const float*>(q), static_cast<const float*>(k), static_cast<const float*>(v), lse,
                        delta, cu, items32, B, N, H, T, win, ld, c, scale, static_cast<float*>(dk),
-                       static_cast<float*>(dv));
+                       static_cast<float*>(dv), ds, nb_max);
   else if (D == 64)
     hipLaunchKernelGGL((bwd_dkdv_f32_kernel<64>), gd, bd, 0, stream, static_cast<const float*>(dout),
                        static_cast<const float*>(q), static_cast<const float*>(k), static_cast<const float*>(v), lse,
                        delta, cu, items32, B, N, H, T, win, ld, c, scale, static_cast<float*>(dk),
-                       static_cast<float*>(dv));
+                       static_cast<float*>(dv), ds, nb_max);
   else
     return hipErrorInvalidValue;
   timing_stop("bwd_dkdv", ev, stream);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_dq_ds_f32_wave(int D, const void* k, const float* ds, int32_t nb_max, const int32_t* cu,
+                                     const int32_t* items32, int32_t B, int32_t N, int32_t H, int64_t ld, float scale,
+                                     void* dq, hipStream_t stream) {
+  const int T = N / kRows + B;  // slots of the sequence-aligned work list
+  const int64_t blocks = static_cast<int64_t>(T) * H;
+  if (blocks == 0) return hipSuccess;
+  const dim3 gd(static_cast<unsigned>(blocks)), bd(64);
+  hipEvent_t ev = timing_start(stream);
+  if (D == 32)
+    hipLaunchKernelGGL((bwd_dq_ds_f32_kernel<32>), gd, bd, 0, stream, static_cast<const float*>(k), ds, cu, items32, B,
+                       H, T, nb_max, ld, scale, static_cast<float*>(dq));
+  else if (D == 64)
+    hipLaunchKernelGGL((bwd_dq_ds_f32_kernel<64>), gd, bd, 0, stream, static_cast<const float*>(k), ds, cu, items32, B,
+                       H, T, nb_max, ld, scale, static_cast<float*>(dq));
+  else
+    return hipErrorInvalidValue;
+  timing_stop("bwd_dq", ev, stream);
   return hipGetLastError();
 }
 

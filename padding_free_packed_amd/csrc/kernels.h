@@ -69,8 +69,8 @@ bool attn_fwd_bf16_w64_supported(int D);
 hipError_t launch_attn_fwd_bf16_w64(bool f16, int D, const void* q, const void* k, const void* v, const int32_t* cu,
                                     const int32_t* items, int32_t B, int32_t N, int32_t H, int32_t win, int64_t ld,
                                     float scale, void* out, float* lse, hipStream_t stream);
-// two 64-row waves per workgroup over sequence-aligned 128-row tiles, global attention
-// (head dims 32, 64; items as for the 64-row-wave kernel)
+// global attention over sequence-aligned 128-row tiles: four waves of 32 query rows at d = 64,
+// two of 64 rows at d = 32 (items as for the 64-row-wave kernel)
 hipError_t launch_attn_fwd_w64b(bool f16, int D, const void* q, const void* k, const void* v, const int32_t* cu,
                                 const int32_t* items, int32_t B, int32_t N, int32_t H, int64_t ld, float scale,
                                 void* out, float* lse, hipStream_t stream);
@@ -86,11 +86,17 @@ hipError_t launch_attn_fwd_f32_wave(int D, const void* q, const void* k, const v
                                     float scale, void* out, float* lse, hipStream_t stream);
 
 // fp32 dK/dV and dQ, one independent wave per 32 key (query) rows of one sequence (head dims 32, 64;
-// items32 as for the fp32 forward)
+// items32 as for the fp32 forward). With ds non-NULL (global attention only) the dK/dV pass also
+// stores every 32x32 block of dS to ds, [H][T][nb_max][1024] floats (T = N/32 + B slots,
+// nb_max >= the 32-row blocks of the longest sequence), for launch_bwd_dq_ds_f32_wave.
 hipError_t launch_bwd_dkdv_f32_wave(int D, const void* dout, const void* q, const void* k, const void* v,
                                     const float* lse, const float* delta, const int32_t* cu, const int32_t* items32,
                                     int32_t B, int32_t N, int32_t H, int32_t win, int64_t ld, float scale, void* dk,
-                                    void* dv, hipStream_t stream);
+                                    void* dv, float* ds, int32_t nb_max, hipStream_t stream);
+// dQ from the dS blocks of launch_bwd_dkdv_f32_wave (no recomputation of S and dP)
+hipError_t launch_bwd_dq_ds_f32_wave(int D, const void* k, const float* ds, int32_t nb_max, const int32_t* cu,
+                                     const int32_t* items32, int32_t B, int32_t N, int32_t H, int64_t ld, float scale,
+                                     void* dq, hipStream_t stream);
 // The dQ pass also computes D = rowsum(dO * O) (O dense [N, H, D]) and stores it to delta for
 // the dK/dV pass, which therefore runs after it.
 hipError_t launch_bwd_dq_f32_wave(int D, const void* dout, const void* q, const void* k, const void* v,
@@ -119,10 +125,13 @@ hipError_t launch_attn_bwd_first(int dt, int D, const void* dout_first, const vo
 // ld: elements between consecutive rows of Q, K, V (and of dQ, dK, dV): num_heads * D for
 // separate [N, H, D] tensors, 3 * num_heads * D for a fused [N, 3, H, D] buffer. O, dO,
 // LSE and D keep their own dense layouts. Every attention launcher takes both.
+// ds, nb_max: the dS hand-off buffer of the fp32 one-wave path (launch_bwd_dkdv_f32_wave), or
+// NULL; used for global attention only (then: delta pass, dK/dV storing dS, dQ from dS).
 hipError_t launch_attn_bwd(int dt, int D, const void* dout, const void* q, const void* k,
                            const void* v, const void* out, const float* lse, const int32_t* cu,
                            const int32_t* items, const int32_t* items32, int32_t B, int32_t N, int32_t H,
                            int32_t win, int64_t ld, float scale, void* dq, void* dk, void* dv, float* delta,
+                           float* ds, int32_t nb_max,
                            hipStream_t stream);
 
 // The 16-bit backward of global attention over sequence-aligned tiles (attn_bwd_seq.hip):

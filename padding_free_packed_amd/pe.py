@@ -30,7 +30,7 @@ EXPORTS = (
     "pe_flatten_document_mask", "pe_gather_rows", "pe_scatter_rows", "pe_varlen_attn_fwd_qkv",
     "pe_varlen_attn_bwd_qkv", "pe_timing_enable", "pe_timing_read", "pe_pack_async",
     "pe_forward_graph_workspace_size", "pe_forward_graph_create", "pe_graph_launch", "pe_graph_destroy",
-    "pe_noalloc_scratch_size", "pe_varlen_attn_fwd_noalloc",
+    "pe_noalloc_scratch_size", "pe_varlen_attn_fwd_noalloc", "pe_attn_bwd_workspace_size",
 )
 
 # status[1] codes of pe_pack_async
@@ -58,6 +58,7 @@ def _load():
         "pe_unpack": (ctypes.c_int, [P, P, I32, I32, I64, I64, ctypes.c_int, P, P]),
         "pe_worklist": (ctypes.c_int, [P, I32, I64, I32, P, P]),
         "pe_attn_workspace_size": (SZ, [I32, I64, I32, I32, ctypes.c_int, ctypes.c_int]),
+        "pe_attn_bwd_workspace_size": (SZ, [I32, I64, I32, I32, I32, ctypes.c_int]),
         "pe_varlen_attn_fwd": (ctypes.c_int, [P, P, P, P, I32, I64, I32, I32, I32, ctypes.c_int, F, P, P, P,
                                                SZ, P]),
         "pe_varlen_attn_fwd_first_token": (ctypes.c_int, [P, P, P, P, I32, I64, I32, I32, I32, ctypes.c_int,
@@ -145,6 +146,11 @@ def pe_attn_workspace_size(num_seqs: int, total_tokens: int, num_heads: int, hea
                            for_backward: bool) -> int:
     return int(_lib.pe_attn_workspace_size(num_seqs, total_tokens, num_heads, head_dim, dtype,
                                            int(for_backward)))
+
+
+def pe_attn_bwd_workspace_size(num_seqs: int, total_tokens: int, max_seq_len: int, num_heads: int, head_dim: int,
+                               dtype: int) -> int:
+    return int(_lib.pe_attn_bwd_workspace_size(num_seqs, total_tokens, max_seq_len, num_heads, head_dim, dtype))
 
 
 # ------------------------------------------------------------------ calls

@@ -44,7 +44,7 @@ KERNEL_PATTERNS = {
     "attn_bwd_first": r"attn_bwd_first_kernel(<|I)",
     "bwd_delta": r"bwd_(delta|seq_prep)_kernel(<|I)",
     "bwd_dkdv": r"bwd_(dkdv(_f32)?|kv_seq)_kernel(<|I)",
-    "bwd_dq": r"bwd_(dq(_f32)?|q_seq)_kernel(<|I)",
+    "bwd_dq": r"bwd_(dq(_ds)?(_f32)?|q_seq)_kernel(<|I)",
     "pack_rows": r"(?<!un)pack_rows_kernel(<|I)",
     "unpack_rows": r"unpack_rows_kernel(<|I)",
     "scan": r"scan_lengths_kernel",

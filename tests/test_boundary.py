@@ -27,7 +27,7 @@ def _header_functions():
 
 def test_header_symbols_exported():
     names = _header_functions()
-    assert len(names) == 31
+    assert len(names) == 32
     for n in names:
         assert hasattr(lib, n), n
     assert sorted(pe.EXPORTS) == names
@@ -47,6 +47,12 @@ def test_workspace_sizes():
     # work list: ceil(N/32)+1 int32, rounded to 256 bytes; backward adds a second list and two fp32 [H, N] arrays
     assert pe.pe_attn_workspace_size(4, 1000, 8, 64, pe.PE_FP32, False) == 256
     assert pe.pe_attn_workspace_size(4, 1000, 8, 64, pe.PE_FP32, True) == 256 + 256 + 2 * 32000
+    # the fastest backward: fp32 at d 32/64 adds one 4 KiB block per (query tile, key block) slot
+    base = pe.pe_attn_workspace_size(4, 1000, 8, 64, pe.PE_FP32, True)
+    assert pe.pe_attn_bwd_workspace_size(4, 1000, 64, 8, 64, pe.PE_FP32) == base + 8 * (1000 // 32 + 4) * 2 * 4096
+    assert pe.pe_attn_bwd_workspace_size(4, 1000, 64, 8, 64, pe.PE_BF16) == base
+    assert pe.pe_attn_bwd_workspace_size(4, 1000, 64, 8, 48, pe.PE_FP32) == base
+    assert pe.pe_attn_bwd_workspace_size(0, 1000, 64, 8, 64, pe.PE_FP32) == 0
     big = pe.pe_attn_workspace_size(4096, 368449, 8, 64, pe.PE_FP32, False)
     assert big >= (368449 // 128 + 2) * 4 and big % 256 == 0
     assert pe.pe_pack_workspace_size(8, 64, 16, pe.PE_FP32) >= 256 + 8

@@ -32,12 +32,17 @@ def check_grad(gpu: np.ndarray, ref: np.ndarray, dtype: str, what: str):
     return float(err.max())
 
 
-def gpu_fwd_bwd(w: W.Workload):
+def gpu_fwd_bwd(w: W.Workload, full_workspace: bool = True):
+    """Forward then backward on the GPU. full_workspace: the workspace of pe_attn_bwd_workspace_size
+    (fp32 at d 32/64: dS handed from the dK/dV pass to the dQ pass), else the smaller one of
+    pe_attn_workspace_size (dQ recomputes S and dP)."""
     cu_ref, _, N = oracle.layout(w.lengths, w.max_seq_len)
     cu = torch.from_numpy(cu_ref).to(DEV)
     q, k, v, do = (to_dev(x, w.dtype) for x in (w.q, w.k, w.v, w.dout))
     code = pe.PE_BF16 if w.dtype == W.BF16 else pe.PE_FP32
-    ws = pe.workspace(pe.pe_attn_workspace_size(w.num_seqs, N, w.num_heads, w.head_dim, code, True), DEV)
+    size = (pe.pe_attn_bwd_workspace_size(w.num_seqs, N, w.max_seq_len, w.num_heads, w.head_dim, code)
+            if full_workspace else pe.pe_attn_workspace_size(w.num_seqs, N, w.num_heads, w.head_dim, code, True))
+    ws = pe.workspace(size, DEV)
     out = torch.empty_like(q)
     lse = torch.empty(w.num_heads, N, device=DEV)
     pe.pe_varlen_attn_fwd(q, k, v, cu, w.num_seqs, N, w.max_seq_len, w.scale, out, lse, ws)
@@ -47,13 +52,13 @@ def gpu_fwd_bwd(w: W.Workload):
     return cu_ref, dq, dk, dv
 
 
-def check_bwd(w: W.Workload, label: str, seqs=None):
+def check_bwd(w: W.Workload, label: str, seqs=None, full_workspace: bool = True):
     """The backward op takes the forward's output as an input (its D term is
     <dO, out>). For bf16 the reference is therefore evaluated at the output the
     forward contract delivers: the oracle's own output rounded to bf16 (nearest
     even). fp32 compares against the exact gradient."""
     say(f"[bwd] {label}: B={w.num_seqs} N={w.total_tokens} H={w.num_heads} d={w.head_dim} {w.dtype}")
-    cu_ref, dq, dk, dv = gpu_fwd_bwd(w)
+    cu_ref, dq, dk, dv = gpu_fwd_bwd(w, full_workspace)
     q, k, v, do = (W.to_f64(x, w.dtype) for x in (w.q, w.k, w.v, w.dout))
     if seqs is None:
         rows = np.arange(int(cu_ref[-1]))
@@ -85,6 +90,19 @@ EDGE = [1, 127, 128, 129, 5, 256, 257, 3, 300, 64, 65, 1, 1, 2, 31, 32, 33, 16, 
 @pytest.mark.parametrize("d", list(range(8, 129, 8)))
 def test_edge_lengths(dtype, d):
     check_bwd(W.custom(60 + d, EDGE, 300, 3, d, dtype, with_grad=True), f"edge lengths d={d}")
+
+
+@pytest.mark.parametrize("d", [32, 64])
+def test_fp32_recompute_path(d):
+    """fp32 with the smaller workspace: dQ recomputes S and dP instead of reading the dS blocks
+    of the dK/dV pass; the same oracle bar, and the two paths agree to fp32 rounding."""
+    w = W.custom(80 + d, EDGE, 300, 3, d, W.FP32, with_grad=True)
+    check_bwd(w, f"edge lengths d={d}, recompute path", full_workspace=False)
+    a = gpu_fwd_bwd(w, True)[1:]
+    b = gpu_fwd_bwd(w, False)[1:]
+    for x, y in zip(a, b):
+        err = (x - y).abs().max().item()
+        assert err <= 1e-5 * max(1.0, y.abs().max().item()), f"paths differ by {err:.3e}"
 
 
 @pytest.mark.parametrize("dtype", [W.FP32, W.BF16])

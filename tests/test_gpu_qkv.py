@@ -42,7 +42,7 @@ def test_fused_qkv_forward_and_backward(dtype, d, S, window):
     q, k, v, do = (to_dev(x, dtype) for x in (w.q, w.k, w.v, w.dout))
     qkv = torch.stack([q, k, v], dim=1).contiguous()     # [N, 3, H, d]
     code = pe.PE_BF16 if dtype == W.BF16 else pe.PE_FP32
-    ws = pe.workspace(pe.pe_attn_workspace_size(w.num_seqs, N, 2, d, code, True), DEV)
+    ws = pe.workspace(pe.pe_attn_bwd_workspace_size(w.num_seqs, N, S, 2, d, code), DEV)
     out = torch.full_like(q, float("nan"))
     lse = torch.full((2, N), float("nan"), device=DEV)
     pe.pe_varlen_attn_fwd_qkv(qkv, cu, w.num_seqs, N, S, w.scale, window, out, lse, ws)
