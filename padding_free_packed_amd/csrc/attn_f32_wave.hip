@@ -59,6 +59,7 @@ __device__ __forceinline__ int lane_now() {
 // block's end need neither clamping nor per-lane address arithmetic. rows <= 32 here,
 // so the byte count fits the 32-bit record count for any row stride below 2^24.
 constexpr int kBufferFlags = 0x00020000;  // dword 3 of a raw buffer resource on CDNA
+constexpr int kNonTemporal = 2;           // cache policy operand of a buffer access: streamed
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const float* base, int rows, uint32_t stride) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(base), 0,
                                            static_cast<int>(static_cast<uint32_t>(rows) * stride * 4u), kBufferFlags);
@@ -394,7 +395,7 @@ __global__ __launch_bounds__(64, 2) void bwd_dq_f32_kernel(
 // (the 16 floats of stored lane L) sits at row prow(L) = L ^ bit2(L) ^ 2 bit5(L), its
 // chunk c at chunk c ^ ((L >> 2) & 3).
 template <int D>
-__global__ __launch_bounds__(64, 4) void bwd_dq_ds_f32_kernel(const float* __restrict__ kp, const float* __restrict__ dsp,
+__global__ __launch_bounds__(64, 2) void bwd_dq_ds_f32_kernel(const float* __restrict__ kp, const float* __restrict__ dsp,
                                                             const int32_t* __restrict__ cu,
                                                             const int32_t* __restrict__ items, int32_t B, int32_t H,
                                                             int32_t T, int32_t NB, int64_t ld, float scale,
@@ -412,7 +413,7 @@ __global__ __launch_bounds__(64, 4) void bwd_dq_ds_f32_kernel(const float* __res
   const uint32_t LD = static_cast<uint32_t>(ld);
   const int64_t hoff = static_cast<int64_t>(h) * D;
   const int sb = sp.lo / kRows + items[t];  // slot of the sequence's first tile
-  const float* row = dsp + (static_cast<int64_t>(h) * T + sb + (sp.r0 - sp.lo) / kRows) * NB * 1024 + lane * 4;
+  const float* row = dsp + (static_cast<int64_t>(h) * T + sb + (sp.r0 - sp.lo) / kRows) * NB * 1024;
   const uint32_t vtr = (static_cast<uint32_t>(4 * g) * LD + ql) * 4u;
 
   // write side: float index of this lane's chunk c4
@@ -437,23 +438,33 @@ __global__ __launch_bounds__(64, 4) void bwd_dq_ds_f32_kernel(const float* __res
 #pragma unroll
   for (int db = 0; db < DB; ++db) dq[db] = floatx16{};
   const int nb = min(NB, (sp.hi - sp.lo + kRows - 1) / kRows);  // blocks the dK/dV pass stored
-  for (int j = 0; j < nb; ++j) {
-    const int kb = sp.lo + j * kRows;
-    const floatx4* src = reinterpret_cast<const floatx4*>(row + static_cast<int64_t>(j) * 1024);
-    const floatx4 x0 = __builtin_nontemporal_load(src), x1 = __builtin_nontemporal_load(src + 64),
-                  x2 = __builtin_nontemporal_load(src + 128), x3 = __builtin_nontemporal_load(src + 192);
+  // Two register sets: block j + 1 is fetched into one while block j's MFMAs read the
+  // other (buffer loads for dS: plain loads here are merged into a single load at the
+  // loop's head, which waits for it at once)
+  struct Blk {
+    floatx4 x[4];
+    float k[16][DB];
+  };
+  Blk b0, b1;
+  const auto rds = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(row), 0, nb * 4096, kBufferFlags);
+  const int vl = lane * 16;  // byte offset of the lane's float4 in each 1 KB chunk
+  auto fetch = [&](int j, Blk& bk) {
+    const int o = j * 4096;
+#pragma unroll
+    for (int c4 = 0; c4 < 4; ++c4)
+      bk.x[c4] = __builtin_bit_cast(floatx4, __builtin_amdgcn_raw_buffer_load_b128(rds, vl + 1024 * c4, o, kNonTemporal));
     // K[key(st)][d] for the key order of the dS operands; rows past the sequence read 0
+    const int kb = sp.lo + j * kRows;
     const auto rk = rows_rsrc(kp + (static_cast<int64_t>(kb) * LD + hoff), min(kRows, sp.hi - kb), LD);
-    float kt[16][DB];
 #pragma unroll
     for (int st = 0; st < 16; ++st)
 #pragma unroll
-      for (int db = 0; db < DB; ++db) kt[st][db] = buf_f32(rk, vtr + 128u * db, (8u * (st >> 2) + (st & 3)) * LD * 4u);
+      for (int db = 0; db < DB; ++db) bk.k[st][db] = buf_f32(rk, vtr + 128u * db, (8u * (st >> 2) + (st & 3)) * LD * 4u);
+  };
+  auto consume = [&](const Blk& bk) {
     __syncthreads();  // the previous block's reads are done
-    *reinterpret_cast<floatx4*>(&tile[wr[0]]) = x0;
-    *reinterpret_cast<floatx4*>(&tile[wr[1]]) = x1;
-    *reinterpret_cast<floatx4*>(&tile[wr[2]]) = x2;
-    *reinterpret_cast<floatx4*>(&tile[wr[3]]) = x3;
+#pragma unroll
+    for (int c4 = 0; c4 < 4; ++c4) *reinterpret_cast<floatx4*>(&tile[wr[c4]]) = bk.x[c4];
     __syncthreads();
     float ds[16];
 #pragma unroll
@@ -461,7 +472,15 @@ __global__ __launch_bounds__(64, 4) void bwd_dq_ds_f32_kernel(const float* __res
 #pragma unroll
     for (int st = 0; st < 16; ++st)
 #pragma unroll
-      for (int db = 0; db < DB; ++db) dq[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(kt[st][db], ds[st], dq[db], 0, 0, 0);
+      for (int db = 0; db < DB; ++db) dq[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(bk.k[st][db], ds[st], dq[db], 0, 0, 0);
+  };
+  if (nb > 0) fetch(0, b0);
+  for (int j = 0; j < nb; j += 2) {
+    if (j + 1 < nb) fetch(j + 1, b1);
+    consume(b0);
+    if (j + 1 >= nb) break;
+    if (j + 2 < nb) fetch(j + 2, b0);
+    consume(b1);
   }
   if (qvalid) store_acc_row<float, D>(dqp, static_cast<int64_t>(qrow) * ld + hoff, dq, scale, g);
 }
