@@ -527,7 +527,7 @@ hipError_t launch_bwd_dq_f32_wave(int D, const void* dout, const void* q, const 
 namespace pe {
 namespace {
 
-template <int D>
+template <int D, bool kDs>
 __global__ __launch_bounds__(64, 2) void bwd_dkdv_f32_kernel(
     const float* __restrict__ dop, const float* __restrict__ qp, const float* __restrict__ kp,
     const float* __restrict__ vp, const float* __restrict__ lse, const float* __restrict__ delta,
@@ -593,6 +593,16 @@ __global__ __launch_bounds__(64, 2) void bwd_dkdv_f32_kernel(
     lse_r = buf_f32(rows_rsrc(lse_h + qb, n, 1), ql * 4u, 0);
     del_r = buf_f32(rows_rsrc(del_h + qb, n, 1), ql * 4u, 0);
   };
+  // dS hand-off (global attention: the walk covers the sequence's query blocks from lo):
+  // block (query block (qb - lo)/32, key block (r0 - lo)/32) of the sequence, one block of
+  // NB * 1024 floats further per query block; a key block at or past NB (a length above
+  // the stated maximum) writes nothing
+  float* dsw = nullptr;
+  if constexpr (kDs) {
+    const int sb = sp.lo / kRows + items[t];  // slot of the sequence's first tile
+    if (r0 - sp.lo < NB * kRows)
+      dsw = dsp + ((static_cast<int64_t>(h) * T + sb + (wq0 - sp.lo) / kRows) * NB + (r0 - sp.lo) / kRows) * 1024;
+  }
   for (int qb = wq0; qb < wq1; qb += 32) {
     load_rows_blk(qb);
     if (g == 0) {
@@ -638,22 +648,20 @@ __global__ __launch_bounds__(64, 2) void bwd_dkdv_f32_kernel(
       }
     }
     __syncthreads();
-    // hand dS to the dQ pass (global attention: query blocks start at lo); a key block at
-    // or past NB (a length above the stated maximum) writes nothing
-    if (dsp != nullptr && r0 - sp.lo < NB * kRows) {
-      // block (query block (qb - lo)/32, key block (r0 - lo)/32) of the sequence in the
-      // accumulator layout, chunk-major: the lane's c-th four values (queries
-      // 8 c + 4 g + 0..3 of key ql) go to float4 c * 64 + lane, so each of the four stores
-      // writes 1 KB contiguous. Keys past the sequence store finite values that meet
-      // zero K rows in the dQ pass. The lane offset is recomputed here (not kept across
+    if constexpr (kDs) {
+      // stored in the accumulator layout, chunk-major: the lane's c-th four values
+      // (queries 8 c + 4 g + 0..3 of key ql) go to float4 c * 64 + lane, so each of the
+      // four stores writes 1 KB contiguous. Keys past the sequence store finite values that
+      // meet zero K rows in the dQ pass. The lane offset is recomputed here (not kept across
       // the loop, where it would take a register the loop cannot spare).
-      const int sb = sp.lo / kRows + items[t];  // slot of the sequence's first tile
-      const int64_t blk = (static_cast<int64_t>(h) * T + sb + (qb - sp.lo) / kRows) * NB + (r0 - sp.lo) / kRows;
-      floatx4* dst = reinterpret_cast<floatx4*>(dsp + blk * 1024) + lane_now();
+      if (dsw != nullptr) {
+        floatx4* dst = reinterpret_cast<floatx4*>(dsw) + lane_now();
 #pragma unroll
-      for (int c4 = 0; c4 < 4; ++c4)  // streamed: read once by the dQ pass
-        __builtin_nontemporal_store(floatx4{dp[4 * c4], dp[4 * c4 + 1], dp[4 * c4 + 2], dp[4 * c4 + 3]},
-                                    dst + 64 * c4);
+        for (int c4 = 0; c4 < 4; ++c4)  // streamed: read once by the dQ pass
+          __builtin_nontemporal_store(floatx4{dp[4 * c4], dp[4 * c4 + 1], dp[4 * c4 + 2], dp[4 * c4 + 3]},
+                                      dst + 64 * c4);
+        dsw += static_cast<int64_t>(NB) * 1024;
+      }
     }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -687,15 +695,15 @@ hipError_t launch_bwd_dkdv_f32_wave(int D, const void* dout, const void* q, cons
   const dim3 gd(static_cast<unsigned>(blocks)), bd(64);
   hipEvent_t ev = timing_start(stream);
   if (D == 32)
-    hipLaunchKernelGGL((bwd_dkdv_f32_kernel<32>), gd, bd, 0, stream, static_cast<const float*>(dout),
-                       static_cast<const float*>(q), static_cast<const float*>(k), static_cast<const float*>(v), lse,
-                       delta, cu, items32, B, N, H, T, win, ld, c, scale, static_cast<float*>(dk),
-                       static_cast<float*>(dv), ds, nb_max);
+    hipLaunchKernelGGL((ds != nullptr ? bwd_dkdv_f32_kernel<32, true> : bwd_dkdv_f32_kernel<32, false>), gd, bd, 0,
+                       stream, static_cast<const float*>(dout), static_cast<const float*>(q),
+                       static_cast<const float*>(k), static_cast<const float*>(v), lse, delta, cu, items32, B, N, H, T,
+                       win, ld, c, scale, static_cast<float*>(dk), static_cast<float*>(dv), ds, nb_max);
   else if (D == 64)
-    hipLaunchKernelGGL((bwd_dkdv_f32_kernel<64>), gd, bd, 0, stream, static_cast<const float*>(dout),
-                       static_cast<const float*>(q), static_cast<const float*>(k), static_cast<const float*>(v), lse,
-                       delta, cu, items32, B, N, H, T, win, ld, c, scale, static_cast<float*>(dk),
-                       static_cast<float*>(dv), ds, nb_max);
+    hipLaunchKernelGGL((ds != nullptr ? bwd_dkdv_f32_kernel<64, true> : bwd_dkdv_f32_kernel<64, false>), gd, bd, 0,
+                       stream, static_cast<const float*>(dout), static_cast<const float*>(q),
+                       static_cast<const float*>(k), static_cast<const float*>(v), lse, delta, cu, items32, B, N, H, T,
+                       win, ld, c, scale, static_cast<float*>(dk), static_cast<float*>(dv), ds, nb_max);
   else
     return hipErrorInvalidValue;
   timing_stop("bwd_dkdv", ev, stream);
