@@ -217,6 +217,7 @@ hipError_t build_fwd_list(pe::FwdList kind, const int32_t* cu, int32_t B, int64_
   switch (kind) {
     case pe::kFwdListSeq32: return pe::launch_seq_worklist(cu, B, N, pe::kAttnWaveRows, items, st);
     case pe::kFwdListSeq128: return pe::launch_seq_worklist(cu, B, N, pe::kAttnTileRows, items, st);
+    case pe::kFwdListNone: return hipSuccess;
     default: return pe::launch_worklist(cu, B, N, pe::kAttnTileRows, items, st);
   }
 }

@@ -52,8 +52,9 @@ hipError_t launch_unpack_rows(const void* packed, void* grid, const int32_t* cu,
 //   kFwdListPacked128: tiles of kAttnTileRows consecutive packed rows (launch_worklist);
 //   kFwdListSeq128:    sequence-aligned tiles of kAttnTileRows rows (launch_seq_worklist),
 //                      the 16-bit 64-row-wave kernel;
-//   kFwdListSeq32:     sequence-aligned tiles of kAttnWaveRows rows, the fp32 one-wave kernel.
-enum FwdList { kFwdListPacked128 = 0, kFwdListSeq128 = 1, kFwdListSeq32 = 2 };
+//   kFwdListSeq32:     sequence-aligned tiles of kAttnWaveRows rows, the fp32 one-wave kernel;
+//   kFwdListNone:      no list, the 16-bit short-sequence kernel (one wave per sequence and head).
+enum FwdList { kFwdListPacked128 = 0, kFwdListSeq128 = 1, kFwdListSeq32 = 2, kFwdListNone = 3 };
 FwdList attn_fwd_list(int dt, int D, int max_seq_len, int64_t ld, int32_t H);
 // The forward of every entry point; items is the list attn_fwd_list names for the same
 // arguments. dt: kDtF32, kDtBF16 or kDtF16 (every attention launcher takes it).
@@ -62,6 +63,12 @@ hipError_t launch_attn_fwd(int dt, int D, const void* q, const void* k, const vo
                            int32_t max_seq_len, int32_t win, int64_t ld, float scale, void* out, float* lse,
                            hipStream_t stream);
 
+// 16-bit forward for lengths up to 64 at head dims 32 and 64: one wave per (sequence,
+// head), K and Q rows loaded as operands, V by LDS DMA; global or windowed attention.
+bool attn_fwd_short_supported(int dt, int D, int max_seq_len);
+hipError_t launch_attn_fwd_short(bool f16, int D, const void* q, const void* k, const void* v, const int32_t* cu,
+                                 int32_t B, int32_t N, int32_t H, int32_t win, int64_t ld, float scale, void* out,
+                                 float* lse, hipStream_t stream);
 // 16-bit forward with LDS-DMA staging (head dims 32, 64, 128); f16 selects fp16 over bf16.
 bool attn_fwd_bf16_supported(int D, int max_seq_len);
 // two 64-row waves per block over sequence-aligned 128-row tiles (head dims 32, 64)

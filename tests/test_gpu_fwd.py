@@ -106,8 +106,9 @@ SHORT_EDGE = [64, 1, 63, 33, 32, 31, 1, 1, 64, 64, 2, 17, 48, 49, 5, 64, 1]
 @pytest.mark.parametrize("d", [8, 32, 64, 128])
 @pytest.mark.parametrize("S", [64, 48, 16])
 def test_short_length_bounds(d, S):
-    # length bounds <= 64 take the windowed short-sequence path for bf16 d 32/64:
-    # lengths at the bound, of one token, and straddling 32-key blocks and 64-row tiles
+    # length bounds <= 64 take the one-wave-per-sequence kernel for bf16 d 32/64 (the
+    # packed-tile kernel for other d): lengths at the bound, of one token, and straddling
+    # 32-key blocks
     rng = np.random.default_rng(48 + S + d)
     L = np.concatenate([np.minimum(SHORT_EDGE, S), rng.integers(1, S + 1, size=300)])
     L = rng.permutation(L).astype(np.int32)

@@ -58,9 +58,11 @@ def test_local_forward_edge_lengths(dtype, d, window):
 
 @pytest.mark.parametrize("dtype", [W.FP32, W.BF16])
 @pytest.mark.parametrize("window", [3, 31, 64])
-def test_local_forward_short_bound(dtype, window):
+@pytest.mark.parametrize("d", [32, 64])
+def test_local_forward_short_bound(dtype, window, d):
+    # length bound 48: 16-bit d 32/64 take the one-wave-per-sequence kernel (band mask per score)
     L = W.random_lengths(61, 300, 1, 48)
-    check_local(W.custom(62, L, 48, 3, 64, dtype), window, "short bound")
+    check_local(W.custom(62 + d, L, 48, 3, d, dtype), window, f"short bound d={d}")
 
 
 def test_local_wide_window_equals_global_bitwise():
