@@ -79,15 +79,19 @@ def band_pairs(lengths, window):
     return float((L + 2.0 * (m * L - m * (m + 1) / 2.0)).sum())
 
 
-def algo_work(kernel, w, N, L2, e, with_lse, with_grid=True):
+def algo_work(kernel, w, N, L2, e, with_lse, with_grid=True, window=None):
     """Algorithmic work of one launch: {'flop': count, 'byte': count} (attention kernels
     carry both). L2 is the number of attended (query, key) pairs: sum L^2, or the
-    band's for local attention."""
+    band's for local attention (window not None)."""
     B, S, H, d = w.num_seqs, w.max_seq_len, w.num_heads, w.head_dim
     D = H * d
     T = (N + 127) // 128
     lse_b = 4.0 * N * H if with_lse else 0.0
-    wave_dq = e == 4 and d in (32, 64)
+    # fp32 at d 32/64: with a window the one-wave dQ recomputes S and dP and forms D itself;
+    # for global attention it takes the dS blocks the dK/dV pass stored and reads only K
+    # (dS is an intermediate of the method, not one of its inputs: not credited)
+    wave_dq = e == 4 and d in (32, 64) and window is not None
+    ds_dq = e == 4 and d in (32, 64) and window is None
     return {
         # forward: 4 L2 H d flops (QK^T and PV); read Q, K, V, write O (+ LSE)
         "attn_fwd": {"flop": 4.0 * L2 * H * d, "byte": 4.0 * N * D * e + lse_b},
@@ -95,8 +99,10 @@ def algo_work(kernel, w, N, L2, e, with_lse, with_grid=True):
         # Q, K, V, dO, LSE, D in and dK, dV out; dQ is credited with dQ alone (2 L2 H d),
         # its recomputation of S and dP is not counted
         "bwd_dkdv": {"flop": 8.0 * L2 * H * d, "byte": 6.0 * N * D * e + 8.0 * N * H},
-        # (the fp32 one-wave dQ also reads O and writes D, the delta pass it replaces)
-        "bwd_dq": {"flop": 2.0 * L2 * H * d, "byte": (6.0 if wave_dq else 5.0) * N * D * e + 8.0 * N * H},
+        # (the fp32 one-wave dQ also reads O and writes D, the delta pass it replaces; the fp32
+        # dQ from stored dS reads K and writes dQ)
+        "bwd_dq": {"flop": 2.0 * L2 * H * d,
+                   "byte": 2.0 * N * D * e if ds_dq else (6.0 if wave_dq else 5.0) * N * D * e + 8.0 * N * H},
         # the whole backward in one pass (short sequences): 10 L2 H d; reads Q, K, V, O, dO, LSE,
         # writes dQ, dK, dV
         "bwd_fused": {"flop": 10.0 * L2 * H * d, "byte": 8.0 * N * D * e + 4.0 * N * H},
@@ -418,7 +424,7 @@ class Case:
             raise ValueError(op)
 
     def kernel_rate(self, kernel, ms):
-        aw = algo_work(kernel, self.w, self.N, self.L2, self.e, self.with_lse, self.grid is not None)
+        aw = algo_work(kernel, self.w, self.N, self.L2, self.e, self.with_lse, self.grid is not None, self.window)
         if aw is None or ms <= 0:
             return {}
         return rate(aw, ms, self.dt)
@@ -750,7 +756,7 @@ def main():
         ent.update(case.kernel_rate(name, ent["mean_ms"]))
         breakdown[name] = ent
     dom = "attn_fwd" if "attn_fwd" in breakdown else max(breakdown, key=lambda k_: breakdown[k_]["ms_per_step"])
-    work = algo_work(dom, w, N, case.L2, case.e, case.with_lse, case.grid is not None)
+    work = algo_work(dom, w, N, case.L2, case.e, case.with_lse, case.grid is not None, case.window)
     roof = rate(work, breakdown[dom]["mean_ms"], case.dt)
     roof["traffic"] = load_traffic(dom, args.workload if args.window is None else f"{args.workload}_w{args.window}")
     roof["kernel"] = dom
