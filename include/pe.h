@@ -281,16 +281,19 @@ pe_status pe_varlen_attn_bwd_first_token(const void* dout_first, const void* q_f
  *   dq, dk, dv           device [total_tokens, num_heads, head_dim] of `dtype`, written
  *   workspace            at least pe_attn_workspace_size(..., for_backward=1); with
  *                        pe_attn_bwd_workspace_size(...) bytes (more for fp32 at head dims
- *                        32 and 64) the fp32 global-attention path passes the blocks of dS
+ *                        32 and 64 with max_seq_len <= 256) the fp32 global-attention path
+ *                        passes the blocks of dS
  *                        from its dK/dV pass to its dQ pass through the workspace instead of
  *                        recomputing S and dP for dQ. Both sizes give gradients within the
  *                        same tolerances; each is deterministic.
  * Deterministic: no floating-point atomics; the same inputs give the same bits.
  */
 /* The workspace size of the fastest backward path: pe_attn_workspace_size(..., 1), plus for
- * fp32 at head dims 32 and 64 one 32x32 fp32 block per (32-row query tile, 32-row key
- * block) of a sequence of max_seq_len rows, per head:
- * num_heads * (total_tokens / 32 + num_seqs) * ceil(max_seq_len / 32) * 4096 bytes.
+ * fp32 at head dims 32 and 64 with max_seq_len <= 256 one 32x32 fp32 block per (32-row query
+ * tile, 32-row key block) of a sequence of max_seq_len rows, per head:
+ * num_heads * (total_tokens / 32 + num_seqs) * ceil(max_seq_len / 32) * 4096 bytes (about
+ * 4.1 GB for 368,449 tokens in 4096 sequences of up to 256 rows and 8 heads; a caller that
+ * passes only the smaller workspace gets the path that recomputes S and dP instead).
  * Returns 0 for invalid sizes. */
 size_t pe_attn_bwd_workspace_size(int32_t num_seqs, int64_t total_tokens, int32_t max_seq_len,
                                   int32_t num_heads, int32_t head_dim, pe_dtype dtype);

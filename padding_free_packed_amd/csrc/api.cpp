@@ -66,8 +66,15 @@ int64_t dense_ld(int32_t num_heads, int32_t head_dim) { return static_cast<int64
 
 // The fp32 backward's dS hand-off: one 32x32 fp32 block per (query tile, key block) of every
 // sequence and head, [H][N/32 + B][nb_max][1024] floats (nb_max: 32-row blocks of a sequence of
-// max_seq_len rows).
+// max_seq_len rows). The region reserves nb_max blocks for every query tile, so it is offered
+// only for length bounds up to kDsMaxSeqLen (8 blocks per tile; the blocks used are the
+// sum over sequences of ceil(L/32)^2 per head).
+constexpr int32_t kDsMaxSeqLen = 256;
 int32_t nb_max(int32_t max_seq_len) { return (max_seq_len + pe::kAttnWaveRows - 1) / pe::kAttnWaveRows; }
+bool ds_handoff(pe_dtype dtype, int32_t head_dim, int32_t num_heads, int32_t max_seq_len) {
+  return dtype == PE_FP32 && max_seq_len <= kDsMaxSeqLen &&
+         pe::attn_f32_wave_supported(head_dim, dense_ld(num_heads, head_dim), num_heads);
+}
 size_t ds_bytes(int32_t num_seqs, int64_t total_tokens, int32_t max_seq_len, int32_t num_heads) {
   return round_up(static_cast<size_t>(num_heads) *
                   static_cast<size_t>(total_tokens / pe::kAttnWaveRows + num_seqs) *
@@ -203,8 +210,7 @@ size_t pe_attn_bwd_workspace_size(int32_t num_seqs, int64_t total_tokens, int32_
                                   int32_t head_dim, pe_dtype dtype) {
   if (num_seqs < 1 || total_tokens < 0 || num_heads < 1 || max_seq_len < 1) return 0;
   size_t s = pe_attn_workspace_size(num_seqs, total_tokens, num_heads, head_dim, dtype, 1);
-  if (dtype == PE_FP32 && pe::attn_f32_wave_supported(head_dim, dense_ld(num_heads, head_dim), num_heads))
-    s += ds_bytes(num_seqs, total_tokens, max_seq_len, num_heads);
+  if (ds_handoff(dtype, head_dim, num_heads, max_seq_len)) s += ds_bytes(num_seqs, total_tokens, max_seq_len, num_heads);
   return s;
 }
 
@@ -434,7 +440,7 @@ pe_status bwd_impl(const void* dout, const void* q, const void* k, const void* v
   // fp32 global attention with a workspace of pe_attn_bwd_workspace_size: the dK/dV pass hands
   // its dS blocks to the dQ pass through the rest of the workspace
   float* ds = nullptr;
-  if (wave && win < 0) {
+  if (wave && win < 0 && max_seq_len <= kDsMaxSeqLen) {
     const size_t base = pe_attn_workspace_size(num_seqs, total_tokens, num_heads, head_dim, dtype, 1);
     if (workspace_bytes >= base + ds_bytes(num_seqs, total_tokens, max_seq_len, num_heads))
       ds = reinterpret_cast<float*>(static_cast<char*>(workspace) + base);

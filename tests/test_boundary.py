@@ -53,6 +53,9 @@ def test_workspace_sizes():
     assert pe.pe_attn_bwd_workspace_size(4, 1000, 64, 8, 64, pe.PE_BF16) == base
     assert pe.pe_attn_bwd_workspace_size(4, 1000, 64, 8, 48, pe.PE_FP32) == base
     assert pe.pe_attn_bwd_workspace_size(0, 1000, 64, 8, 64, pe.PE_FP32) == 0
+    # the dS region is offered up to a length bound of 256 (8 blocks per query tile)
+    assert pe.pe_attn_bwd_workspace_size(4, 1000, 256, 8, 64, pe.PE_FP32) == base + 8 * (1000 // 32 + 4) * 8 * 4096
+    assert pe.pe_attn_bwd_workspace_size(4, 1000, 257, 8, 64, pe.PE_FP32) == base
     big = pe.pe_attn_workspace_size(4096, 368449, 8, 64, pe.PE_FP32, False)
     assert big >= (368449 // 128 + 2) * 4 and big % 256 == 0
     assert pe.pe_pack_workspace_size(8, 64, 16, pe.PE_FP32) >= 256 + 8

@@ -92,11 +92,20 @@ def test_edge_lengths(dtype, d):
     check_bwd(W.custom(60 + d, EDGE, 300, 3, d, dtype, with_grad=True), f"edge lengths d={d}")
 
 
+@pytest.mark.parametrize("d,S", [(32, 256), (64, 256), (64, 64), (32, 40)])
+def test_fp32_ds_handoff_edge_lengths(d, S):
+    """fp32 global attention with the workspace of pe_attn_bwd_workspace_size (length bounds up
+    to 256): the dK/dV pass stores every 32x32 dS block and the dQ pass reads them back; lengths
+    at the bound, of one token and around 32-row blocks."""
+    L = np.minimum(np.array(EDGE + [S, S - 1, 33, 97], dtype=np.int32), S)
+    check_bwd(W.custom(90 + d + S, L, S, 3, d, W.FP32, with_grad=True), f"dS hand-off d={d} S={S}")
+
+
 @pytest.mark.parametrize("d", [32, 64])
 def test_fp32_recompute_path(d):
     """fp32 with the smaller workspace: dQ recomputes S and dP instead of reading the dS blocks
     of the dK/dV pass; the same oracle bar, and the two paths agree to fp32 rounding."""
-    w = W.custom(80 + d, EDGE, 300, 3, d, W.FP32, with_grad=True)
+    w = W.custom(80 + d, np.minimum(EDGE, 256), 256, 3, d, W.FP32, with_grad=True)
     check_bwd(w, f"edge lengths d={d}, recompute path", full_workspace=False)
     a = gpu_fwd_bwd(w, True)[1:]
     b = gpu_fwd_bwd(w, False)[1:]
