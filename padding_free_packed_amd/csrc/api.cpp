@@ -117,12 +117,32 @@ int32_t pe_attn_tile_rows(void) { return pe::kAttnTileRows; }
 
 // ------------------------------------------------------------------------ pack
 
+}  // extern "C"
+
+namespace {
+// Bytes of the copy work list a pack call may build: tiles of pack_tile_rows(row bytes)
+// rows when it copies rows, of pack_tile_rows(64) rows when it writes flat_index only
+// (the list for the smaller tiles is the longer one).
+size_t pack_items_bytes(int32_t num_seqs, int32_t max_seq_len, int64_t row_elems, pe_dtype dtype) {
+  const int64_t rowbytes = (row_elems > 0 ? row_elems : 1) * elem_bytes(dtype);
+  const int64_t R = std::min(pe::pack_tile_rows(rowbytes), pe::pack_tile_rows(64));
+  const int64_t max_rows = static_cast<int64_t>(num_seqs) * max_seq_len;
+  return round_up(static_cast<size_t>(ceil_div(max_rows, R) + 1) * sizeof(int32_t));
+}
+// The scan's scratch in a pack workspace: after the result words and the copy work list.
+int64_t* scan_part(void* workspace, int32_t num_seqs, int32_t max_seq_len, int64_t row_elems, pe_dtype dtype) {
+  if (pe::scan_scratch_bytes(num_seqs) == 0) return nullptr;
+  return reinterpret_cast<int64_t*>(static_cast<char*>(workspace) + kAlign +
+                                    pack_items_bytes(num_seqs, max_seq_len, row_elems, dtype));
+}
+}  // namespace
+
+extern "C" {
+
 size_t pe_pack_workspace_size(int32_t num_seqs, int32_t max_seq_len, int64_t row_elems, pe_dtype dtype) {
   if (num_seqs < 1 || max_seq_len < 1) return 0;
-  const int64_t rowbytes = (row_elems > 0 ? row_elems : 1) * elem_bytes(dtype);
-  const int64_t R = pe::pack_tile_rows(rowbytes);
-  const int64_t max_rows = static_cast<int64_t>(num_seqs) * max_seq_len;
-  return kAlign + round_up(static_cast<size_t>(ceil_div(max_rows, R) + 1) * sizeof(int32_t));
+  return kAlign + pack_items_bytes(num_seqs, max_seq_len, row_elems, dtype) +
+         round_up(static_cast<size_t>(pe::scan_scratch_bytes(num_seqs)));
 }
 
 pe_status pe_pack(const int32_t* lengths, int32_t num_seqs, int32_t max_seq_len, const void* grid,
@@ -145,7 +165,8 @@ pe_status pe_pack(const int32_t* lengths, int32_t num_seqs, int32_t max_seq_len,
   hipStream_t st = as_stream(stream);
   int64_t* result = static_cast<int64_t*>(workspace);
   int32_t* items = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + kAlign);
-  hipError_t e = pe::launch_scan(lengths, num_seqs, max_seq_len, -1, cu_seqlens, result, st);
+  hipError_t e = pe::launch_scan(lengths, num_seqs, max_seq_len, -1, cu_seqlens, result,
+                                 scan_part(workspace, num_seqs, max_seq_len, row_elems, dtype), st);
   if (e != hipSuccess) return PE_ERR_HIP;
   // The one host read of the library: the token count and the length-error flag.
   int64_t host[2] = {0, 0};
@@ -618,7 +639,8 @@ pe_status pe_pack_async(const int32_t* lengths, int32_t num_seqs, int32_t max_se
   hipStream_t st = as_stream(stream);
   // no valid batch holds more than num_seqs * max_seq_len rows
   const int64_t cap = std::min(capacity, static_cast<int64_t>(num_seqs) * max_seq_len);
-  hipError_t e = pe::launch_scan(lengths, num_seqs, max_seq_len, cap, cu_seqlens, status, st);
+  hipError_t e = pe::launch_scan(lengths, num_seqs, max_seq_len, cap, cu_seqlens, status,
+                                 scan_part(workspace, num_seqs, max_seq_len, row_elems, dtype), st);
   if (e != hipSuccess) return PE_ERR_HIP;
   if ((!flat_index && !packed) || cap == 0) return PE_OK;
   int32_t* items = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + kAlign);

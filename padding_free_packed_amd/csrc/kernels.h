@@ -25,9 +25,12 @@ constexpr int kAttnTileRows = 128;
 constexpr int kAttnWaveRows = 32;
 
 // cap < 0: no capacity check, cu keeps the running sum even on a length error;
-// cap >= 0: a length error or a total above cap zeroes cu (see scan_lengths_kernel)
+// cap >= 0: a length error or a total above cap zeroes cu (see scan_lengths_kernel).
+// part: scan_scratch_bytes(B) bytes of device scratch (16-byte aligned) for the
+// multi-workgroup scan of large batches; nullptr (or a small batch) takes one workgroup.
+int64_t scan_scratch_bytes(int32_t B);
 hipError_t launch_scan(const int32_t* lengths, int32_t B, int32_t S, int64_t cap, int32_t* cu, int64_t* result,
-                       hipStream_t stream);
+                       int64_t* part, hipStream_t stream);
 // N may exceed cu[B] (a capacity): tiles from ceil(cu[B] / R) on get item B
 hipError_t launch_worklist(const int32_t* cu, int32_t B, int64_t N, int32_t R, int32_t* items,
                            hipStream_t stream);

@@ -106,6 +106,130 @@ __global__ __launch_bounds__(kScanThreads) void scan_lengths_kernel(
   scan_lengths_block(lengths, B, S, cap, cu, result);
 }
 
+// The same scan over many workgroups, for batches of at least kScanMbMin sequences, in two
+// launches (no workgroup waits for another): the first writes each workgroup's length sum
+// and length-error flag (part[2 g], part[2 g + 1]); the second has every workgroup add up
+// the partials before its own (its offset), all of them (the total and the flags, so each
+// knows whether the batch is rejected) and rescan its 4096 lengths into cu.
+constexpr int kScanMbThreads = 256;
+constexpr int kScanMbPer = 16;  // lengths per thread
+constexpr int kScanMbRows = kScanMbThreads * kScanMbPer;
+constexpr int32_t kScanMbMin = 8192;
+
+// the lengths of one thread: [i0, i0 + kScanMbPer), zeros past B
+__device__ __forceinline__ void scan_mb_load(const int32_t* __restrict__ lengths, int64_t i0, int32_t B,
+                                             int32_t (&L)[kScanMbPer]) {
+  if (i0 + kScanMbPer <= B) {
+#pragma unroll
+    for (int v = 0; v < kScanMbPer / 4; ++v) {
+      const int4 x = *reinterpret_cast<const int4*>(lengths + i0 + 4 * v);
+      L[4 * v] = x.x; L[4 * v + 1] = x.y; L[4 * v + 2] = x.z; L[4 * v + 3] = x.w;
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < kScanMbPer; ++j) L[j] = i0 + j < B ? lengths[i0 + j] : 0;
+  }
+}
+
+// sum over the workgroup (every thread gets it)
+__device__ __forceinline__ int64_t scan_mb_sum(int64_t x, int64_t* red) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o);
+  const int wv = threadIdx.x >> 6;
+  __syncthreads();  // red may hold an earlier sum
+  if ((threadIdx.x & 63) == 0) red[wv] = x;
+  __syncthreads();
+  int64_t t = 0;
+#pragma unroll
+  for (int w = 0; w < kScanMbThreads / 64; ++w) t += red[w];
+  return t;
+}
+
+__global__ __launch_bounds__(kScanMbThreads) void scan_part_kernel(const int32_t* __restrict__ lengths, int32_t B,
+                                                                   int32_t S, int64_t* __restrict__ part) {
+  __shared__ int64_t red[kScanMbThreads / 64];
+  const int64_t i0 = static_cast<int64_t>(blockIdx.x) * kScanMbRows + threadIdx.x * kScanMbPer;
+  int32_t L[kScanMbPer];
+  scan_mb_load(lengths, i0, B, L);
+  int64_t local = 0;
+  int bad = 0;
+#pragma unroll
+  for (int j = 0; j < kScanMbPer; ++j) {
+    if (i0 + j < B) bad |= (L[j] < 1) | (L[j] > S);
+    local += L[j];
+  }
+  const int64_t sum = scan_mb_sum(local, red);
+  const int64_t nbad = scan_mb_sum(bad, red);
+  if (threadIdx.x == 0) {
+    part[2 * blockIdx.x] = sum;
+    part[2 * blockIdx.x + 1] = nbad != 0;
+  }
+}
+
+__global__ __launch_bounds__(kScanMbThreads) void scan_fin_kernel(const int32_t* __restrict__ lengths, int32_t B,
+                                                                  int64_t cap, const int64_t* __restrict__ part,
+                                                                  int32_t G, int32_t* __restrict__ cu,
+                                                                  int64_t* __restrict__ result) {
+  __shared__ int64_t red[kScanMbThreads / 64];
+  __shared__ int64_t wsum[kScanMbThreads / 64];
+  const int g = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  int64_t pre = 0, tot = 0, bad = 0;
+  for (int i = tid; i < G; i += kScanMbThreads) {
+    const int64_t x = part[2 * i];
+    if (i < g) pre += x;
+    tot += x;
+    bad |= part[2 * i + 1];
+  }
+  pre = scan_mb_sum(pre, red);
+  tot = scan_mb_sum(tot, red);
+  bad = scan_mb_sum(bad, red);
+  const int64_t code = bad ? 1 : (cap >= 0 && tot > cap ? 2 : 0);
+  const bool clear = cap >= 0 && code != 0;
+  const int64_t i0 = static_cast<int64_t>(g) * kScanMbRows + tid * kScanMbPer;
+  if (clear) {  // a rejected batch: every offset 0 (no rows for the kernels queued behind)
+    for (int j = 0; j < kScanMbPer; ++j)
+      if (i0 + j < B) cu[i0 + j] = 0;
+  } else {
+    int32_t L[kScanMbPer];
+    scan_mb_load(lengths, i0, B, L);
+    int64_t local = 0;
+#pragma unroll
+    for (int j = 0; j < kScanMbPer; ++j) local += L[j];
+    int64_t incl = local;  // inclusive scan of `local` across the wave
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int64_t up = __shfl_up(incl, o);
+      if (lane >= o) incl += up;
+    }
+    if (lane == 63) wsum[wv] = incl;
+    __syncthreads();
+    int64_t run = pre + incl - local;
+#pragma unroll
+    for (int w = 0; w < kScanMbThreads / 64; ++w)
+      if (w < wv) run += wsum[w];
+    int32_t E[kScanMbPer];
+#pragma unroll
+    for (int j = 0; j < kScanMbPer; ++j) {
+      E[j] = static_cast<int32_t>(run);
+      run += L[j];
+    }
+    if (i0 + kScanMbPer <= B) {
+#pragma unroll
+      for (int v = 0; v < kScanMbPer / 4; ++v)
+        *reinterpret_cast<int4*>(cu + i0 + 4 * v) = make_int4(E[4 * v], E[4 * v + 1], E[4 * v + 2], E[4 * v + 3]);
+    } else {
+#pragma unroll
+      for (int j = 0; j < kScanMbPer; ++j)
+        if (i0 + j < B) cu[i0 + j] = E[j];
+    }
+  }
+  if (tid == 0 && g == G - 1) cu[B] = clear ? 0 : static_cast<int32_t>(tot);
+  if (tid == 0 && g == 0) {
+    result[0] = tot;
+    result[1] = code;
+  }
+}
+
 // ---------------------------------------------------------------- work list
 // items[t] = b with cu[b] <= t*R < cu[b+1]; items[T] = B, T = ceil(N / R).
 // Thread b writes the entries of the tiles that start inside sequence b. N may
@@ -259,10 +383,21 @@ __global__ __launch_bounds__(256) void unpack_rows_kernel(
 
 // ---------------------------------------------------------------- launchers
 
+int64_t scan_scratch_bytes(int32_t B) {
+  return B >= kScanMbMin ? 16 * ((static_cast<int64_t>(B) + kScanMbRows - 1) / kScanMbRows) : 0;
+}
+
 hipError_t launch_scan(const int32_t* lengths, int32_t B, int32_t S, int64_t cap, int32_t* cu, int64_t* result,
-                       hipStream_t stream) {
+                       int64_t* part, hipStream_t stream) {
   hipEvent_t ev = timing_start(stream);
-  hipLaunchKernelGGL(scan_lengths_kernel, dim3(1), dim3(kScanThreads), 0, stream, lengths, B, S, cap, cu, result);
+  if (B >= kScanMbMin && part != nullptr) {
+    const int32_t G = static_cast<int32_t>((static_cast<int64_t>(B) + kScanMbRows - 1) / kScanMbRows);
+    hipLaunchKernelGGL(scan_part_kernel, dim3(G), dim3(kScanMbThreads), 0, stream, lengths, B, S, part);
+    hipLaunchKernelGGL(scan_fin_kernel, dim3(G), dim3(kScanMbThreads), 0, stream, lengths, B, cap, part, G, cu,
+                       result);
+  } else {
+    hipLaunchKernelGGL(scan_lengths_kernel, dim3(1), dim3(kScanThreads), 0, stream, lengths, B, S, cap, cu, result);
+  }
   timing_stop("scan", ev, stream);
   return hipGetLastError();
 }

@@ -106,3 +106,36 @@ def test_worklist(R):
     pe.pe_worklist(cu, len(L), N, R, items)
     torch.cuda.synchronize()
     assert np.array_equal(from_dev(items), oracle.worklist(cu_ref, R))
+
+
+@pytest.mark.parametrize("B", [8191, 8192, 12345, 100000])
+def test_pack_layout_many_sequences(B):
+    # from 8192 sequences on the scan runs over many workgroups (4096 lengths each, two
+    # launches): offsets, a length error in a late workgroup, and (pe_pack_async) the
+    # rejected batch that must leave every offset 0
+    S = 90
+    L = W.random_lengths(14 + B, B, 1, S)
+    cu_ref, _, N = oracle.layout(L, S)
+    say(f"[pack] layout of {B} sequences")
+    ws = pe.workspace(pe.pe_pack_workspace_size(B, S, 1, pe.PE_FP32), DEV)
+    cu = torch.full((B + 1,), -3, dtype=torch.int32, device=DEV)
+    n = pe.pe_pack(torch.from_numpy(L).to(DEV), S, None, cu, None, None, 0, ws)
+    assert n == N and from_dev(cu).tolist() == cu_ref.tolist()
+    bad = L.copy()
+    bad[B - 5] = 0
+    with pytest.raises(pe.PeError) as e:
+        pe.pe_pack(torch.from_numpy(bad).to(DEV), S, None, cu, None, None, 0, ws)
+    assert e.value.status == pe.PE_ERR_LENGTHS
+    # the running sum of the given values, as the call documents
+    assert from_dev(cu).tolist() == np.concatenate([[0], np.cumsum(bad.astype(np.int64))]).tolist()
+    for lengths, cap, code in ((L, N, pe.PACK_OK), (bad, B * S, pe.PACK_BAD_LENGTH), (L, N - 1, pe.PACK_OVER_CAPACITY)):
+        cu = torch.full((B + 1,), -3, dtype=torch.int32, device=DEV)
+        flat = torch.full((max(cap, 1),), -3, dtype=torch.int64, device=DEV)
+        status = torch.full((2,), -3, dtype=torch.int64, device=DEV)
+        pe.pe_pack_async(torch.from_numpy(lengths).to(DEV), S, None, cu, flat, None, cap, status, ws)
+        torch.cuda.synchronize()
+        assert status.tolist() == [int(lengths.astype(np.int64).sum()), code]
+        if code == pe.PACK_OK:
+            assert from_dev(cu).tolist() == cu_ref.tolist()
+        else:
+            assert (cu == 0).all() and (flat == -3).all()
