@@ -34,8 +34,9 @@
  *   first checks cu_seqlens on the device (cu[0] = 0, every length in
  *   [1, max_seq_len], cu[B] <= total_tokens) and waits for the answer: on a
  *   violation it returns PE_ERR_LENGTHS with nothing else launched. That mode
- *   synchronizes the stream (no graph capture) and shares one device flag
- *   between calls, so calls must not overlap.
+ *   synchronizes the stream (no graph capture); each call writes its answer to
+ *   its own word of a ring of 256, so calls that overlap from other threads or
+ *   streams do not interfere.
  * - dtype PE_FP32 computes in fp32 throughout (the GiGL page runs its kernel in
  *   fp32 because inference needs it). PE_BF16 reads and writes bf16 and
  *   accumulates in fp32; the probabilities are rounded to bf16 before they

@@ -3,6 +3,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <climits>
 #include <cmath>
 #include <cstdint>
@@ -17,9 +18,12 @@ namespace {
 // Checked mode: with PE_CHECK=1 in the environment, every attention call first
 // checks cu_seqlens on the device and waits for the answer; on a violation it
 // returns PE_ERR_LENGTHS with nothing else launched. A debugging aid: it
-// synchronizes the stream (so it cannot be captured in a graph), and calls that
-// overlap on one device share the flag.
-__device__ int32_t g_check_flag;
+// synchronizes the stream (so it cannot be captured in a graph). Each call takes
+// the next of kCheckSlots answer words in turn, so calls that overlap (from other
+// threads, on other streams) write different words.
+constexpr uint32_t kCheckSlots = 256;
+__device__ int32_t g_check_flags[kCheckSlots];
+std::atomic<uint32_t> g_check_next{0};
 
 bool check_mode() {
   const char* e = std::getenv("PE_CHECK");
@@ -28,8 +32,10 @@ bool check_mode() {
 
 pe_status check_cu(const int32_t* cu, int32_t B, int64_t N, int32_t S, hipStream_t st) {
   if (!check_mode()) return PE_OK;
-  int32_t* flag = nullptr;
-  if (hipGetSymbolAddress(reinterpret_cast<void**>(&flag), HIP_SYMBOL(g_check_flag)) != hipSuccess) return PE_ERR_HIP;
+  int32_t* flags = nullptr;
+  if (hipGetSymbolAddress(reinterpret_cast<void**>(&flags), HIP_SYMBOL(g_check_flags)) != hipSuccess)
+    return PE_ERR_HIP;
+  int32_t* flag = flags + g_check_next.fetch_add(1, std::memory_order_relaxed) % kCheckSlots;
   if (pe::launch_check_cu(cu, B, N, S, flag, st) != hipSuccess) return PE_ERR_HIP;
   int32_t h = 0;
   if (hipMemcpyAsync(&h, flag, sizeof h, hipMemcpyDeviceToHost, st) != hipSuccess) return PE_ERR_HIP;

@@ -83,3 +83,41 @@ def test_bad_offsets_are_refused_before_any_launch(case, monkeypatch):
     assert e.value.status == pe.PE_ERR_LENGTHS
     torch.cuda.synchronize()
     assert torch.isnan(out).all() and torch.isnan(lse).all() and torch.isnan(dq).all() and torch.isnan(of).all()
+
+
+def test_overlapping_checked_calls(monkeypatch):
+    # two threads on their own streams, one with valid offsets and one with a zero length,
+    # checking at the same time: each call reads its own answer
+    import threading
+    monkeypatch.setenv("PE_CHECK", "1")
+    S = 8
+    cases = {"good": [0, 5, 12, 15], "bad": [0, 5, 5, 8]}
+    results = {}
+
+    def worker(name):
+        cu_l = cases[name]
+        B, N = len(cu_l) - 1, cu_l[-1]
+        stream = torch.cuda.Stream()
+        with torch.cuda.stream(stream):
+            cu = torch.tensor(cu_l, dtype=torch.int32, device=DEV)
+            q, k, v, _ = _tensors(N, torch.float32, seed=2)
+            out = torch.empty_like(q)
+            lse = torch.empty(H, N, device=DEV)
+            ws = pe.workspace(pe.pe_attn_workspace_size(B, N, H, D, pe.PE_FP32, False), DEV)
+            got = []
+            for _ in range(40):
+                try:
+                    pe.pe_varlen_attn_fwd(q, k, v, cu, B, N, S, 0.125, out, lse, ws)
+                    got.append(pe.PE_OK)
+                except pe.PeError as e:
+                    got.append(e.status)
+            stream.synchronize()
+        results[name] = got
+
+    threads = [threading.Thread(target=worker, args=(n,)) for n in cases]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    assert results["good"] == [pe.PE_OK] * 40
+    assert results["bad"] == [pe.PE_ERR_LENGTHS] * 40
