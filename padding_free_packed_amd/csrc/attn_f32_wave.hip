@@ -15,6 +15,11 @@
 // at use and rely on their second wave per SIMD to cover the latency (measured faster
 // than prefetching with the registers that takes).
 //
+// Backward of global attention given the larger workspace: the dK/dV pass also stores
+// every 32x32 dS block of a sequence, and a dQ pass computes dQ = dS K from those blocks
+// (transposed through LDS) instead of recomputing S and dP; with a window or the smaller
+// workspace the dQ pass recomputes them (and forms D = <dO, O> of its rows itself).
+//
 // fp32 forward, one wave per (head, 32 query rows), over its key span in 32-key steps:
 //   S^T (32 keys x 32 queries) += K Q^T   v_mfma_f32_32x32x2f32, 32 steps of 2 over d=64
 //   O^T (d x 32 queries)       += V^T P^T 16 steps per 32-row d block
