@@ -18,9 +18,10 @@
 //     read by ds_read_b64_tr_b16;
 //   * the first key block sets each row's reference m to its exact maximum;
 //     after it, p = exp2(c s - m) and their sums are taken against the current m
-//     and only a block whose sum exceeds 2^16 (or is infinite) takes its exact
-//     maximum, rescales O and l and recomputes p. p stays below 2^16, which the
-//     fp32 sums and 16-bit products hold without loss of relative precision, and
+//     and only a block whose sum exceeds 2^15 (or is infinite) takes its exact
+//     maximum, rescales O and l and recomputes p. p stays at most 2^15, which the
+//     fp32 sums and the 16-bit products hold without loss of relative precision
+//     (fp16's largest finite value is 65504: at 2^16 a p could round to infinity), and
 //     O, l and the log-sum-exp share the one m, so the result is that of the
 //     exact running maximum; the per-score maximum of the usual online softmax
 //     is not computed. A middle key block is then one basic block (no branch
@@ -53,7 +54,7 @@ constexpr int kB64Keys = 32;      // keys per ring stage
 // side by side on the long-document and mixed-batch forwards: 3 was 8% slower, 4 even
 // with 2); the key loop below is written for two
 constexpr int kB64Stages = 2;
-constexpr float kB64Overflow = 65536.f;  // largest block sum of p kept without a new reference
+constexpr float kB64Overflow = 32768.f;  // largest block sum of p kept without a new reference
 
 // NQ: query blocks of this wave holding rows (0, 1 or 2; 0 only stages keys)
 template <typename Et, int D, int NQ>

@@ -70,6 +70,33 @@ def test_forward_long_sequences_and_large_scores():
     check_lse(to_f64(lse), l_ref, F16, "f16 long lse")
 
 
+@pytest.mark.parametrize("d", [32, 64])
+def test_forward_probability_near_fp16_max(d):
+    """A key block after the first whose one large score sits just under 16
+    (log2 units) above the first block's maximum, the rest of its scores far
+    below: its unnormalised probability, about 65529, is finite in fp32 but
+    rounds to infinity in fp16 (largest finite value 65504), so the forward
+    must take a new reference before that block's probabilities enter the
+    fp16 product. Query rows are e0; keys 0..31 are zero (scores 0), key 32
+    is e0 (score 1), every later key is -8 e0; scale * log2(e) = 15.99985."""
+    L, H = 200, 2
+    w = W.custom(330 + d, np.array([L], dtype=np.int32), L, H, d, F16, scale=11.090250968933105)
+    c = float(np.float32(w.scale * 1.4426950408889634))
+    assert 65520.0 < 2.0 ** c < 65536.0  # rounds to fp16 infinity (halfway above 65504 is 65520)
+    q = np.zeros((L, H, d), np.float32)
+    q[:, :, 0] = 1.0
+    k = np.zeros((L, H, d), np.float32)
+    k[32, :, 0] = 1.0
+    k[33:, :, 0] = -8.0
+    w.q, w.k = (x.astype(np.float16).view(np.uint16) for x in (q, k))
+    say(f"[f16 fwd] p near the fp16 maximum: d={d} L={L}")
+    cu_ref, _, _, out, lse, _ = _fwd(w)
+    torch.cuda.synchronize()
+    o_ref, l_ref = oracle.attention(*(W.to_f64(x, F16) for x in (w.q, w.k, w.v)), cu_ref, w.scale)
+    check_out(to_f64(out), o_ref, F16, "f16 out, p near 65504")
+    check_lse(to_f64(lse), l_ref, F16, "f16 lse, p near 65504")
+
+
 @pytest.mark.parametrize("d,S,window", [(64, 300, 20), (128, 300, 0), (16, 64, 5), (32, 48, 7), (64, 64, 0)])
 def test_local_forward_and_backward(d, S, window):
     w = W.custom(310 + d, np.minimum(EDGE, S), S, 2, d, F16, with_grad=True)
