@@ -435,7 +435,7 @@ hipError_t first_dispatch(const void* q, const void* k, const void* v, const int
 FwdList attn_fwd_list(int dt, int D, int max_seq_len, int64_t ld, int32_t H) {
   if (dt == kDtF32) return attn_f32_wave_supported(D, ld, H) ? kFwdListSeq32 : kFwdListPacked128;
   if (attn_fwd_short_supported(dt, D, max_seq_len)) return kFwdListNone;
-  return attn_fwd_bf16_supported(D, max_seq_len) && attn_fwd_bf16_w64_supported(D) ? kFwdListSeq128
+  return attn_fwd_bf16_supported(D, max_seq_len) && attn_fwd_w64b_supported(D) ? kFwdListSeq128
                                                                                    : kFwdListPacked128;
 }
 
@@ -448,9 +448,7 @@ hipError_t launch_attn_fwd(int dt, int D, const void* q, const void* k, const vo
     case kFwdListSeq32:
       return launch_attn_fwd_f32_wave(D, q, k, v, cu, items, B, N, H, win, ld, scale, out, lse, stream);
     case kFwdListSeq128:
-      if (win < 0)  // global attention: every row of a tile has the same key range
-        return launch_attn_fwd_w64b(f16, D, q, k, v, cu, items, B, N, H, ld, scale, out, lse, stream);
-      return launch_attn_fwd_bf16_w64(f16, D, q, k, v, cu, items, B, N, H, win, ld, scale, out, lse, stream);
+      return launch_attn_fwd_w64b(f16, D, q, k, v, cu, items, B, N, H, win, ld, scale, out, lse, stream);
     case kFwdListNone:
       return launch_attn_fwd_short(f16, D, q, k, v, cu, B, N, H, win, ld, scale, out, lse, stream);
     case kFwdListPacked128:

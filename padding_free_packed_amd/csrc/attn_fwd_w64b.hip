@@ -1,6 +1,6 @@
-// 16-bit forward of global attention for head dims 32 and 64 over sequence-aligned
-// 128-row tiles: four waves of 32 query rows per workgroup at d = 64, two waves of
-// 64 rows at d = 32.
+// 16-bit forward of global or local (windowed) attention for head dims 32 and 64
+// over sequence-aligned 128-row tiles: four waves of 32 query rows per workgroup at
+// d = 64, two waves of 64 rows at d = 32.
 //
 // A workgroup takes slot t of the sequence-aligned work list of 128-row tiles
 // (launch_seq_worklist with tile height 128): rows cu[b] + 128 * (t - cu[b] /
@@ -27,7 +27,13 @@
 //     is not computed. A middle key block is then one basic block (no branch
 //     between its reads, MFMAs and softmax), which the other wave on the SIMD
 //     overlaps.
-// Local (windowed) attention takes the two-wave kernel of attn_fwd_bf16_w64.hip.
+// Local attention (LOCAL, window win: key j is seen by row i when |i - j| <= win)
+// stages only the keys within win of the tile's rows; a wave computes only the
+// key blocks that hold a key within win of one of its rows, and masks the keys
+// farther than win from a row in the blocks that are not wholly within win of
+// all of them. A wave whose first computed block is not the tile's first still
+// has the initial reference: its first block's sums are infinite and take the
+// exact-maximum path above, as does a row whose first keys come in a later block.
 #include <climits>
 #include <type_traits>
 
@@ -57,10 +63,11 @@ constexpr int kB64Stages = 2;
 constexpr float kB64Overflow = 32768.f;  // largest block sum of p kept without a new reference
 
 // NQ: query blocks of this wave holding rows (0, 1 or 2; 0 only stages keys)
-template <typename Et, int D, int NQ>
+// [lo, hi): the keys of the tile (its sequence's; with LOCAL, those within win of its rows)
+template <typename Et, int D, int NQ, bool LOCAL>
 __device__ __forceinline__ void b64_run(const void* __restrict__ qp, const void* __restrict__ kp,
                                         const void* __restrict__ vp, int h, int rw, int rend, int lo, int hi,
-                                        int32_t N, int32_t H, int64_t ld, float c, void* __restrict__ op,
+                                        int win, int32_t N, int32_t H, int64_t ld, float c, void* __restrict__ op,
                                         float* __restrict__ lse, char (*ring)[2][kB64Keys * D * 2]) {
   constexpr int CH = D / 8;                     // 16-byte chunks per row
   constexpr int QS = D / 16;                    // MFMA steps over head_dim
@@ -81,6 +88,10 @@ __device__ __forceinline__ void b64_run(const void* __restrict__ qp, const void*
     qvalid[qb] = qrow[qb] < rend;
     load_row_regs<Et, D>(qp, static_cast<int64_t>(qrow[qb]) * ld + h * D, g, qvalid[qb], qr[qb]);
   }
+  // LOCAL: key blocks starting in [bnd0, bnd1] hold a key within win of some row of this
+  // wave, and those starting in [in0, in1] only keys within win of all of them
+  const int bnd0 = rw - win - (kB64Keys - 1), bnd1 = rw + 32 * NQ - 1 + win;
+  const int in0 = rw + 32 * NQ - 1 - win, in1 = rw + win - (kB64Keys - 1);
   // retire the Q loads with a wait the compiler sees, so none lands inside the DMA loop
   vmem_fence_for_compiler();
 
@@ -219,6 +230,10 @@ __device__ __forceinline__ void b64_run(const void* __restrict__ qp, const void*
     raw_barrier();  // block j visible to both waves; both have read block j-1's stage
     if (j + 1 < nblk) issue(other_stage(st_tag));
     if constexpr (NQ == 0) return;
+    const int kb = lo + j * kB64Keys;
+    if constexpr (LOCAL) {
+      if (kb < bnd0 || kb > bnd1) return;  // wave-uniform: no key of the block is within win of a row
+    }
     const uint32_t kt = ring0 + static_cast<uint32_t>(stage_of(st_tag) * STB);
     const uint32_t vtl = kt + static_cast<uint32_t>(TB);
     vec8<Et> ka[QS];
@@ -240,9 +255,14 @@ __device__ __forceinline__ void b64_run(const void* __restrict__ qp, const void*
         vt[s2][db] = as_vec8<Et>(u16x8{lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]});
       }
     if constexpr (LAST) {  // keys past the sequence's end get no weight
-      const int kb = lo + j * kB64Keys;
 #pragma unroll
       for (int qb = 0; qb < NQ; ++qb) mask_block(s[qb], -INT_MAX, hi - (kb + 4 * g));
+    }
+    if constexpr (LOCAL) {  // keys farther than win from the row get no weight
+      if (kb < in0 || kb > in1) {
+#pragma unroll
+        for (int qb = 0; qb < NQ; ++qb) mask_block(s[qb], qrow[qb] - win - (kb + 4 * g), qrow[qb] + win + 1 - (kb + 4 * g));
+      }
     }
     float ps[QB];
     bool ovf = false;
@@ -301,11 +321,11 @@ __device__ __forceinline__ void b64_run(const void* __restrict__ qp, const void*
   }
 }
 
-template <typename Et, int D>
+template <typename Et, int D, bool LOCAL>
 __global__ __launch_bounds__(b64_threads<D>(), b64_waves_per_simd<D>()) void attn_fwd_w64b_kernel(
     const void* __restrict__ qp, const void* __restrict__ kp, const void* __restrict__ vp,
     const int32_t* __restrict__ cu, const int32_t* __restrict__ items, int32_t B, int32_t N, int32_t H,
-    int32_t T, int64_t ld, float c, void* __restrict__ op, float* __restrict__ lse) {
+    int32_t T, int32_t win, int64_t ld, float c, void* __restrict__ op, float* __restrict__ lse) {
   __shared__ __align__(16) char ring[kB64Stages][2][kB64Keys * D * 2];  // [stage][K, V][tile]
   const int lin = xcd_remap(blockIdx.x, gridDim.x);
   const int h = lin / T, t = lin - h * T;
@@ -316,46 +336,55 @@ __global__ __launch_bounds__(b64_threads<D>(), b64_waves_per_simd<D>()) void att
   const int r0 = lo + (t - (lo / kAttnTileRows + b)) * kAttnTileRows;
   if (r0 >= hi) return;  // block-uniform: an empty slot at the end of the sequence
   const int rend = min(r0 + kAttnTileRows, hi);
+  // the tile's keys: its sequence's, with LOCAL only those within win of one of its rows
+  const int klo = LOCAL ? max(lo, r0 - win) : lo;
+  const int khi = LOCAL ? min(hi, rend + win) : hi;
   constexpr int NQ = b64_nq<D>();
   const int rw = r0 + 32 * NQ * static_cast<int>(threadIdx.x >> 6);  // this wave's first row
   const int nq = rw >= rend ? 0 : min(NQ, (rend - rw + 31) / 32);   // wave-uniform
   if constexpr (NQ == 2) {
     if (nq == 2) {
-      b64_run<Et, D, 2>(qp, kp, vp, h, rw, rend, lo, hi, N, H, ld, c, op, lse, ring);
+      b64_run<Et, D, 2, LOCAL>(qp, kp, vp, h, rw, rend, klo, khi, win, N, H, ld, c, op, lse, ring);
       return;
     }
   }
-  if (nq == 1) b64_run<Et, D, 1>(qp, kp, vp, h, rw, rend, lo, hi, N, H, ld, c, op, lse, ring);
-  else b64_run<Et, D, 0>(qp, kp, vp, h, rw, rend, lo, hi, N, H, ld, c, op, lse, ring);
+  if (nq == 1) b64_run<Et, D, 1, LOCAL>(qp, kp, vp, h, rw, rend, klo, khi, win, N, H, ld, c, op, lse, ring);
+  else b64_run<Et, D, 0, LOCAL>(qp, kp, vp, h, rw, rend, klo, khi, win, N, H, ld, c, op, lse, ring);
 }
 
 template <typename Et, int D>
 hipError_t dispatch_w64b(const void* q, const void* k, const void* v, const int32_t* cu, const int32_t* items,
-                         int32_t B, int32_t N, int32_t H, int64_t ld, float scale, void* out, float* lse,
+                         int32_t B, int32_t N, int32_t H, int32_t win, int64_t ld, float scale, void* out, float* lse,
                          hipStream_t stream) {
   const int T = N / kAttnTileRows + B;  // sequence-aligned slots
   const int64_t blocks = static_cast<int64_t>(T) * H;
   if (blocks == 0) return hipSuccess;
   const float c = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
   hipEvent_t ev = timing_start(stream);
-  hipLaunchKernelGGL((attn_fwd_w64b_kernel<Et, D>), dim3(static_cast<unsigned>(blocks)), dim3(b64_threads<D>()), 0,
-                     stream, q, k, v, cu, items, B, N, H, T, ld, c, out, lse);
+  if (win >= 0)
+    hipLaunchKernelGGL((attn_fwd_w64b_kernel<Et, D, true>), dim3(static_cast<unsigned>(blocks)),
+                       dim3(b64_threads<D>()), 0, stream, q, k, v, cu, items, B, N, H, T, win, ld, c, out, lse);
+  else
+    hipLaunchKernelGGL((attn_fwd_w64b_kernel<Et, D, false>), dim3(static_cast<unsigned>(blocks)),
+                       dim3(b64_threads<D>()), 0, stream, q, k, v, cu, items, B, N, H, T, win, ld, c, out, lse);
   timing_stop("attn_fwd", ev, stream);
   return hipGetLastError();
 }
 
 }  // namespace
 
+bool attn_fwd_w64b_supported(int D) { return D == 32 || D == 64; }
+
 hipError_t launch_attn_fwd_w64b(bool f16, int D, const void* q, const void* k, const void* v, const int32_t* cu,
-                                const int32_t* items, int32_t B, int32_t N, int32_t H, int64_t ld, float scale,
-                                void* out, float* lse, hipStream_t stream) {
+                                const int32_t* items, int32_t B, int32_t N, int32_t H, int32_t win, int64_t ld,
+                                float scale, void* out, float* lse, hipStream_t stream) {
   switch (D) {
     case 32:
-      return f16 ? dispatch_w64b<_Float16, 32>(q, k, v, cu, items, B, N, H, ld, scale, out, lse, stream)
-                 : dispatch_w64b<__bf16, 32>(q, k, v, cu, items, B, N, H, ld, scale, out, lse, stream);
+      return f16 ? dispatch_w64b<_Float16, 32>(q, k, v, cu, items, B, N, H, win, ld, scale, out, lse, stream)
+                 : dispatch_w64b<__bf16, 32>(q, k, v, cu, items, B, N, H, win, ld, scale, out, lse, stream);
     case 64:
-      return f16 ? dispatch_w64b<_Float16, 64>(q, k, v, cu, items, B, N, H, ld, scale, out, lse, stream)
-                 : dispatch_w64b<__bf16, 64>(q, k, v, cu, items, B, N, H, ld, scale, out, lse, stream);
+      return f16 ? dispatch_w64b<_Float16, 64>(q, k, v, cu, items, B, N, H, win, ld, scale, out, lse, stream)
+                 : dispatch_w64b<__bf16, 64>(q, k, v, cu, items, B, N, H, win, ld, scale, out, lse, stream);
     default: return hipErrorInvalidValue;
   }
 }

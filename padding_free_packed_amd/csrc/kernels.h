@@ -54,7 +54,7 @@ hipError_t launch_unpack_rows(const void* packed, void* grid, const int32_t* cu,
 // from the same answer, so list and kernel cannot disagree:
 //   kFwdListPacked128: tiles of kAttnTileRows consecutive packed rows (launch_worklist);
 //   kFwdListSeq128:    sequence-aligned tiles of kAttnTileRows rows (launch_seq_worklist),
-//                      the 16-bit 64-row-wave kernel;
+//                      the 16-bit kernel of attn_fwd_w64b.hip;
 //   kFwdListSeq32:     sequence-aligned tiles of kAttnWaveRows rows, the fp32 one-wave kernel;
 //   kFwdListNone:      no list, the 16-bit short-sequence kernel (one wave per sequence and head).
 enum FwdList { kFwdListPacked128 = 0, kFwdListSeq128 = 1, kFwdListSeq32 = 2, kFwdListNone = 3 };
@@ -74,16 +74,12 @@ hipError_t launch_attn_fwd_short(bool f16, int D, const void* q, const void* k, 
                                  float* lse, hipStream_t stream);
 // 16-bit forward with LDS-DMA staging (head dims 32, 64, 128); f16 selects fp16 over bf16.
 bool attn_fwd_bf16_supported(int D, int max_seq_len);
-// two 64-row waves per block over sequence-aligned 128-row tiles (head dims 32, 64)
-bool attn_fwd_bf16_w64_supported(int D);
-hipError_t launch_attn_fwd_bf16_w64(bool f16, int D, const void* q, const void* k, const void* v, const int32_t* cu,
-                                    const int32_t* items, int32_t B, int32_t N, int32_t H, int32_t win, int64_t ld,
-                                    float scale, void* out, float* lse, hipStream_t stream);
-// global attention over sequence-aligned 128-row tiles: four waves of 32 query rows at d = 64,
-// two of 64 rows at d = 32 (items as for the 64-row-wave kernel)
+// global or windowed attention over sequence-aligned 128-row tiles (head dims 32, 64): four
+// waves of 32 query rows at d = 64, two of 64 rows at d = 32
+bool attn_fwd_w64b_supported(int D);
 hipError_t launch_attn_fwd_w64b(bool f16, int D, const void* q, const void* k, const void* v, const int32_t* cu,
-                                const int32_t* items, int32_t B, int32_t N, int32_t H, int64_t ld, float scale,
-                                void* out, float* lse, hipStream_t stream);
+                                const int32_t* items, int32_t B, int32_t N, int32_t H, int32_t win, int64_t ld,
+                                float scale, void* out, float* lse, hipStream_t stream);
 hipError_t launch_attn_fwd_bf16(bool f16, int D, const void* q, const void* k, const void* v, const int32_t* cu,
                                 const int32_t* items, int32_t B, int32_t N, int32_t H, int32_t win, int64_t ld,
                                 float scale, void* out, float* lse, hipStream_t stream);

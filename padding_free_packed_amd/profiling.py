@@ -21,7 +21,7 @@ import re
 CSRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "csrc")
 
 KERNEL_SOURCES = {
-    "attn_fwd": ["attn_fwd.hip", "attn_fwd_bf16.hip", "attn_fwd_bf16_w64.hip", "attn_fwd_w64b.hip", "attn_fwd_short.hip",
+    "attn_fwd": ["attn_fwd.hip", "attn_fwd_bf16.hip", "attn_fwd_w64b.hip", "attn_fwd_short.hip",
                  "attn_f32_wave.hip", "attn_common.h", "common.h"],
     "attn_fwd_first": ["attn_fwd.hip", "common.h"],
     "attn_bwd_first": ["attn_first_bwd.hip", "attn_common.h", "common.h"],
@@ -39,7 +39,7 @@ KERNEL_SOURCES = {
 # demangled ("attn_fwd_kernel<float, 64>") or, where its demangler does not know
 # the __bf16 mangling, mangled ("...15attn_fwd_kernelIDF16bLi64E...")
 KERNEL_PATTERNS = {
-    "attn_fwd": r"attn_fwd(_bf16|_bf16_w64|_w64b|_short|_f32)?_kernel(<|I)",
+    "attn_fwd": r"attn_fwd(_bf16|_w64b|_short|_f32)?_kernel(<|I)",
     "attn_fwd_first": r"attn_fwd_first_kernel(<|I)",
     "attn_bwd_first": r"attn_bwd_first_kernel(<|I)",
     "bwd_delta": r"bwd_(delta|seq_prep)_kernel(<|I)",

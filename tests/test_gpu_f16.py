@@ -1,6 +1,6 @@
 """GPU parity of the fp16 element type against the fp64 oracle, over every
 kernel family: the generic forward (short length bounds, every head dim), the
-64-row-wave and LDS-DMA forwards (long bounds), local attention, the
+LDS-DMA forwards on sequence-aligned tiles (long bounds), local attention, the
 first-token forward (given rows and gathered rows), the backward (swizzled and
 plain tiles), the first-token backward, the fused-QKV calls (bit-exact against
 separate tensors), pack/unpack (bit-exact) and the captured bucket forward.
@@ -58,7 +58,7 @@ def test_forward(d, S):
 
 
 def test_forward_long_sequences_and_large_scores():
-    """Long sequences through the 64-row-wave kernel, with scores far above the
+    """Long sequences through the sequence-aligned tile kernel, with scores far above the
     rescale headroom (scale 1): the running maximum moves many times."""
     L = np.array([3000, 1, 2047, 640], dtype=np.int32)
     w = W.custom(41, L, 4096, 4, 64, F16, scale=1.0)

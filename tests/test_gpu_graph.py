@@ -88,7 +88,7 @@ EDGE = [1, 127, 128, 129, 5, 256, 257, 3, 300, 64, 65, 1, 1, 2, 31, 32, 33, 16, 
 CAP_CASES = [  # dtype, d, max_seq_len: every forward kernel family
     (W.FP32, 64, 300),    # fp32 one-wave kernel
     (W.FP32, 16, 300),    # generic fp32
-    (W.BF16, 64, 300),    # bf16 64-row-wave kernel
+    (W.BF16, 64, 300),    # bf16 sequence-aligned 128-row-tile kernel
     (W.BF16, 128, 300),   # bf16 LDS-DMA kernel
     (W.BF16, 64, 64),     # generic bf16 (short bound)
 ]
@@ -149,7 +149,7 @@ def _eager(bucket, scale, window):
 GRAPH_CASES = [  # dtype, H, d, window, slots, length bound
     (torch.bfloat16, 12, 64, -1, 64, 48), (torch.float32, 8, 64, -1, 64, 48), (torch.bfloat16, 12, 64, 16, 64, 48),
     (torch.bfloat16, 4, 128, -1, 64, 48),
-    # bounds above 128: the 16-bit forward is the 64-row-wave kernel on sequence-aligned tiles
+    # bounds above 128: the 16-bit forward is the LDS-DMA kernel on sequence-aligned tiles
     # of the bucket's capacity rows (lengths crossing 128 and 256, fewer sequences than slots)
     (torch.bfloat16, 4, 64, -1, 16, 300), (torch.bfloat16, 4, 64, 20, 16, 300),
     (torch.float16, 4, 32, -1, 16, 300), (torch.float16, 4, 32, 20, 16, 300),

@@ -2,7 +2,7 @@
 fixed scratch array) against pe_varlen_attn_fwd with a caller workspace: the same
 kernels on the same list, so out and lse must agree bit for bit; two calls in a
 row, the second on a smaller batch (the array keeps the first call's list), for
-each work-list kind (fp32 32-row tiles, bf16 64-row-wave tiles, packed 128-row
+each work-list kind (fp32 32-row tiles, bf16 sequence-aligned 128-row tiles, packed 128-row
 tiles). The first batch of each kind is also checked against the fp64 oracle."""
 import numpy as np
 import pytest
@@ -23,7 +23,7 @@ def _bits(t):
 
 CASES = [  # dtype, head dim, length bound: the three work-list kinds
     (W.FP32, 64, 300),   # sequence-aligned 32-row tiles
-    (W.BF16, 64, 300),   # sequence-aligned 128-row tiles (64-row waves)
+    (W.BF16, 64, 300),   # sequence-aligned 128-row tiles
     (W.BF16, 64, 64),    # packed 128-row tiles
     (W.FP16, 40, 300),   # packed 128-row tiles, generic kernel
 ]
