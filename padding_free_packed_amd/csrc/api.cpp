@@ -459,8 +459,8 @@ pe_status bwd_impl(const void* dout, const void* q, const void* k, const void* v
     hipError_t e = pe::launch_seq_worklist(cu_seqlens, num_seqs, total_tokens, pe::kAttnTileRows, items, st);
     if (e != hipSuccess) return PE_ERR_HIP;
     return hip_status(pe::launch_attn_bwd_seq(dtype, head_dim, dout, q, k, v, out, lse, cu_seqlens, items, num_seqs,
-                                              static_cast<int32_t>(total_tokens), num_heads, ld, softmax_scale, dq,
-                                              dk, dv, delta, nd, st));
+                                              static_cast<int32_t>(total_tokens), num_heads, win, ld, softmax_scale,
+                                              dq, dk, dv, delta, nd, st));
   }
   // the fp32 one-wave kernels take the sequence-aligned list, every other kernel the 128-row one
   const bool wave = dtype == PE_FP32 && pe::attn_f32_wave_supported(head_dim, ld, num_heads);

@@ -1,5 +1,6 @@
-// 16-bit backward of global attention for head dims 32 and 64 over sequence-aligned
-// 128-row tiles. Three launches, no atomics, so the result is bitwise reproducible:
+// 16-bit backward of global or local (windowed) attention for head dims 32 and 64 over
+// sequence-aligned 128-row tiles. Three launches, no atomics, so the result is bitwise
+// reproducible:
 //
 //   prep:   per (head, row): nl = -lse * log2(e) and nd = -<dO, O> (minus the row's D)
 //   dK/dV:  wave w of the workgroup on slot t of the sequence-aligned list of 128-row
@@ -26,6 +27,11 @@
 // Against the 128-row packed tiles of attn_bwd.hip (a tile spans the sequences its
 // rows fall in; query blocks start at the tile's first sequence), no product runs on
 // rows of another sequence, and subtracting D and scaling by log2(e) leave the loop.
+//
+// Local attention (LOCAL, window win: row i and key j interact when |i - j| <= win):
+// a tile streams only the rows within win of its own rows, a wave computes only the
+// streamed blocks that reach its 32 rows, and in blocks not wholly within win of all
+// of them the pairs farther apart get probability 0.
 #include <climits>
 #include <type_traits>
 
@@ -185,12 +191,12 @@ __device__ __forceinline__ void run_blocks(int nblk, Issue& issue, Step& step) {
   step(j, j & 1, std::true_type{});  // one copy of the masked step, its stage at run time
 }
 
-template <typename Et, int D>
+template <typename Et, int D, bool LOCAL>
 __global__ __launch_bounds__(kThreads, kKvWaves) void bwd_kv_seq_kernel(
     const void* __restrict__ dop, const void* __restrict__ qp, const void* __restrict__ kp,
     const void* __restrict__ vp, const float* __restrict__ nl, uint32_t nd_off, const int32_t* __restrict__ cu,
-    const int32_t* __restrict__ items, int32_t B, int32_t N, int32_t H, int32_t T, int64_t ld, float c, float scale,
-    void* __restrict__ dkp, void* __restrict__ dvp) {
+    const int32_t* __restrict__ items, int32_t B, int32_t N, int32_t H, int32_t T, int32_t win, int64_t ld, float c,
+    float scale, void* __restrict__ dkp, void* __restrict__ dvp) {
   constexpr int RS = kKvRows, QS = D / 16, DB = D / 32;
   using Dma = PairDma<D, RS>;
   constexpr int TB = Dma::TB;
@@ -201,10 +207,17 @@ __global__ __launch_bounds__(kThreads, kKvWaves) void bwd_kv_seq_kernel(
 
   const int lin = xcd_remap(blockIdx.x, gridDim.x);
   const int h = lin / T, t = lin - h * T;
-  int lo, hi, r0, rend;
-  if (!seq_tile(cu, items, t, B, lo, hi, r0, rend)) return;  // block-uniform
+  int slo, shi, r0, rend;
+  if (!seq_tile(cu, items, t, B, slo, shi, r0, rend)) return;  // block-uniform
+  // [lo, hi): the query rows streamed, the sequence's (LOCAL: those within win of a key of the tile)
+  const int lo = LOCAL ? max(slo, r0 - win) : slo;
+  const int hi = LOCAL ? min(shi, rend + win) : shi;
   const int tid = threadIdx.x, lane = tid & 63, ql = lane & 31, g = lane >> 5;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // LOCAL: query blocks starting in [bnd0, bnd1] hold a row within win of a key of this wave,
+  // those starting in [in0, in1] only rows within win of all of them
+  const int kw = r0 + 32 * wv;
+  const int bnd0 = kw - win - 31, bnd1 = kw + 31 + win, in0 = kw + 31 - win, in1 = kw + win - 31;
   const int krow = r0 + 32 * wv + ql;
   const bool kvalid = krow < rend;
   const bool active = r0 + 32 * wv < rend;  // wave-uniform
@@ -270,6 +283,9 @@ __global__ __launch_bounds__(kThreads, kKvWaves) void bwd_kv_seq_kernel(
 #pragma unroll
     for (int q = 0; q < QS; ++q) dp = mfma16<Et>(as_vec8<Et>(ds_read_b128_at(dt + so.row[q])), vreg[q], dp);
     if constexpr (LAST) mask_block(s, -INT_MAX, hi - (qr0 + 4 * g));  // query rows past the end
+    if constexpr (LOCAL) {  // rows farther than win from this lane's key
+      if (qr0 < in0 || qr0 > in1) mask_block(s, krow - win - (qr0 + 4 * g), krow + win + 1 - (qr0 + 4 * g));
+    }
 #pragma unroll
     for (int i4 = 0; i4 < 4; ++i4) {
       const floatx4 l4 = __builtin_bit_cast(floatx4, ds_read_b128_at(lt + 32 * i4));
@@ -309,6 +325,9 @@ __global__ __launch_bounds__(kThreads, kKvWaves) void bwd_kv_seq_kernel(
 #pragma unroll
     for (int sb = 0; sb < RS / 32; ++sb) {
       const int qr0 = lo + j * RS + 32 * sb;
+      if constexpr (LOCAL) {
+        if (qr0 < bnd0 || qr0 > bnd1) continue;  // wave-uniform: no row within win of this wave's keys
+      }
       if constexpr (LAST) {
         if (qr0 >= hi) break;  // wave-uniform: past the sequence's end
         sub(st, sb, qr0, std::true_type{});
@@ -326,12 +345,12 @@ __global__ __launch_bounds__(kThreads, kKvWaves) void bwd_kv_seq_kernel(
   }
 }
 
-template <typename Et, int D>
+template <typename Et, int D, bool LOCAL>
 __global__ __launch_bounds__(kThreads, kQWaves) void bwd_q_seq_kernel(
     const void* __restrict__ dop, const void* __restrict__ qp, const void* __restrict__ kp,
     const void* __restrict__ vp, const float* __restrict__ nl, const float* __restrict__ nd,
     const int32_t* __restrict__ cu, const int32_t* __restrict__ items, int32_t B, int32_t N, int32_t H, int32_t T,
-    int64_t ld, float c, float scale, void* __restrict__ dqp) {
+    int32_t win, int64_t ld, float c, float scale, void* __restrict__ dqp) {
   constexpr int RS = kQRows, QS = D / 16, DB = D / 32;
   using Dma = PairDma<D, RS>;
   constexpr int TB = Dma::TB;
@@ -341,10 +360,17 @@ __global__ __launch_bounds__(kThreads, kQWaves) void bwd_q_seq_kernel(
 
   const int lin = xcd_remap(blockIdx.x, gridDim.x);
   const int h = lin / T, t = lin - h * T;
-  int lo, hi, r0, rend;
-  if (!seq_tile(cu, items, t, B, lo, hi, r0, rend)) return;  // block-uniform
+  int slo, shi, r0, rend;
+  if (!seq_tile(cu, items, t, B, slo, shi, r0, rend)) return;  // block-uniform
+  // [lo, hi): the keys streamed, the sequence's (LOCAL: those within win of a row of the tile)
+  const int lo = LOCAL ? max(slo, r0 - win) : slo;
+  const int hi = LOCAL ? min(shi, rend + win) : shi;
   const int tid = threadIdx.x, lane = tid & 63, ql = lane & 31, g = lane >> 5;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // LOCAL: key blocks starting in [bnd0, bnd1] hold a key within win of a row of this wave,
+  // those starting in [in0, in1] only keys within win of all of them
+  const int qw = r0 + 32 * wv;
+  const int bnd0 = qw - win - 31, bnd1 = qw + 31 + win, in0 = qw + 31 - win, in1 = qw + win - 31;
   const int qrow = r0 + 32 * wv + ql;
   const bool qvalid = qrow < rend;
   const bool active = r0 + 32 * wv < rend;  // wave-uniform
@@ -393,6 +419,9 @@ __global__ __launch_bounds__(kThreads, kQWaves) void bwd_q_seq_kernel(
 #pragma unroll
     for (int q = 0; q < QS; ++q) dp = mfma16<Et>(as_vec8<Et>(ds_read_b128_at(vt + so.row[q])), dreg[q], dp);
     if constexpr (LAST) mask_block(s, -INT_MAX, hi - (kr0 + 4 * g));  // keys past the end
+    if constexpr (LOCAL) {  // keys farther than win from this lane's row
+      if (kr0 < in0 || kr0 > in1) mask_block(s, qrow - win - (kr0 + 4 * g), qrow + win + 1 - (kr0 + 4 * g));
+    }
 #pragma unroll
     for (int i = 0; i < 16; ++i) dp[i] *= __builtin_amdgcn_exp2f(fmaf(s[i], c, nlq));
     vec8<Et> sb16[2];
@@ -415,6 +444,9 @@ __global__ __launch_bounds__(kThreads, kQWaves) void bwd_q_seq_kernel(
 #pragma unroll
     for (int sb = 0; sb < RS / 32; ++sb) {
       const int kr0 = lo + j * RS + 32 * sb;
+      if constexpr (LOCAL) {
+        if (kr0 < bnd0 || kr0 > bnd1) continue;  // wave-uniform: no key within win of this wave's rows
+      }
       if constexpr (LAST) {
         if (kr0 >= hi) break;  // wave-uniform: past the sequence's end
         sub(st, sb, kr0, std::true_type{});
@@ -432,8 +464,8 @@ __global__ __launch_bounds__(kThreads, kQWaves) void bwd_q_seq_kernel(
 template <typename Et, int D>
 hipError_t bwd_seq_dispatch(const void* dout, const void* q, const void* k, const void* v, const void* out,
                             const float* lse, const int32_t* cu, const int32_t* items, int32_t B, int32_t N,
-                            int32_t H, int64_t ld, float scale, void* dq, void* dk, void* dv, float* nl, float* nd,
-                            hipStream_t stream) {
+                            int32_t H, int32_t win, int64_t ld, float scale, void* dq, void* dk, void* dv, float* nl,
+                            float* nd, hipStream_t stream) {
   if (N == 0) return hipSuccess;
   const int64_t lanes = static_cast<int64_t>(N) * H * (D / 8);
   hipEvent_t ev_prep = timing_start(stream);
@@ -447,14 +479,22 @@ hipError_t bwd_seq_dispatch(const void* dout, const void* q, const void* k, cons
   const float c = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
   const uint32_t nd_off = static_cast<uint32_t>((nd - nl) * static_cast<int64_t>(sizeof(float)));
   hipEvent_t ev_kv = timing_start(stream);
-  hipLaunchKernelGGL((bwd_kv_seq_kernel<Et, D>), dim3(blocks), dim3(kThreads), 0, stream, dout, q, k, v, nl, nd_off,
-                     cu, items, B, N, H, T, ld, c, scale, dk, dv);
+  if (win >= 0)
+    hipLaunchKernelGGL((bwd_kv_seq_kernel<Et, D, true>), dim3(blocks), dim3(kThreads), 0, stream, dout, q, k, v, nl,
+                       nd_off, cu, items, B, N, H, T, win, ld, c, scale, dk, dv);
+  else
+    hipLaunchKernelGGL((bwd_kv_seq_kernel<Et, D, false>), dim3(blocks), dim3(kThreads), 0, stream, dout, q, k, v, nl,
+                       nd_off, cu, items, B, N, H, T, win, ld, c, scale, dk, dv);
   timing_stop("bwd_dkdv", ev_kv, stream);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipEvent_t ev_q = timing_start(stream);
-  hipLaunchKernelGGL((bwd_q_seq_kernel<Et, D>), dim3(blocks), dim3(kThreads), 0, stream, dout, q, k, v, nl, nd, cu,
-                     items, B, N, H, T, ld, c, scale, dq);
+  if (win >= 0)
+    hipLaunchKernelGGL((bwd_q_seq_kernel<Et, D, true>), dim3(blocks), dim3(kThreads), 0, stream, dout, q, k, v, nl, nd,
+                       cu, items, B, N, H, T, win, ld, c, scale, dq);
+  else
+    hipLaunchKernelGGL((bwd_q_seq_kernel<Et, D, false>), dim3(blocks), dim3(kThreads), 0, stream, dout, q, k, v, nl,
+                       nd, cu, items, B, N, H, T, win, ld, c, scale, dq);
   timing_stop("bwd_dq", ev_q, stream);
   return hipGetLastError();
 }
@@ -463,7 +503,7 @@ hipError_t bwd_seq_dispatch(const void* dout, const void* q, const void* k, cons
 
 bool attn_bwd_seq_supported(int dt, int D, int32_t win, int64_t N, int32_t H, int64_t ld) {
   if (dt != kDtBF16 && dt != kDtF16) return false;
-  if (win >= 0 || (D != 32 && D != 64)) return false;
+  if (D != 32 && D != 64) return false;
   // 32-bit DMA offsets: 32 rows of the widest stride, and nl/nd ([H, N] floats each,
   // nd after nl) within 4 GiB of nl
   if (ld * 2 * max(kKvRows, kQRows) >= (int64_t{1} << 31)) return false;
@@ -472,19 +512,19 @@ bool attn_bwd_seq_supported(int dt, int D, int32_t win, int64_t N, int32_t H, in
 
 hipError_t launch_attn_bwd_seq(int dt, int D, const void* dout, const void* q, const void* k, const void* v,
                                const void* out, const float* lse, const int32_t* cu, const int32_t* items, int32_t B,
-                               int32_t N, int32_t H, int64_t ld, float scale, void* dq, void* dk, void* dv, float* nl,
-                               float* nd, hipStream_t stream) {
+                               int32_t N, int32_t H, int32_t win, int64_t ld, float scale, void* dq, void* dk, void* dv,
+                               float* nl, float* nd, hipStream_t stream) {
   const bool f16 = dt == kDtF16;
   switch (D) {
     case 32:
-      return f16 ? bwd_seq_dispatch<_Float16, 32>(dout, q, k, v, out, lse, cu, items, B, N, H, ld, scale, dq, dk, dv,
+      return f16 ? bwd_seq_dispatch<_Float16, 32>(dout, q, k, v, out, lse, cu, items, B, N, H, win, ld, scale, dq, dk, dv,
                                                  nl, nd, stream)
-                 : bwd_seq_dispatch<__bf16, 32>(dout, q, k, v, out, lse, cu, items, B, N, H, ld, scale, dq, dk, dv,
+                 : bwd_seq_dispatch<__bf16, 32>(dout, q, k, v, out, lse, cu, items, B, N, H, win, ld, scale, dq, dk, dv,
                                                nl, nd, stream);
     case 64:
-      return f16 ? bwd_seq_dispatch<_Float16, 64>(dout, q, k, v, out, lse, cu, items, B, N, H, ld, scale, dq, dk, dv,
+      return f16 ? bwd_seq_dispatch<_Float16, 64>(dout, q, k, v, out, lse, cu, items, B, N, H, win, ld, scale, dq, dk, dv,
                                                  nl, nd, stream)
-                 : bwd_seq_dispatch<__bf16, 64>(dout, q, k, v, out, lse, cu, items, B, N, H, ld, scale, dq, dk, dv,
+                 : bwd_seq_dispatch<__bf16, 64>(dout, q, k, v, out, lse, cu, items, B, N, H, win, ld, scale, dq, dk, dv,
                                                nl, nd, stream);
     default: return hipErrorInvalidValue;
   }

@@ -140,15 +140,15 @@ hipError_t launch_attn_bwd(int dt, int D, const void* dout, const void* q, const
                            float* ds, int32_t nb_max,
                            hipStream_t stream);
 
-// The 16-bit backward of global attention over sequence-aligned tiles (attn_bwd_seq.hip):
-// bf16 or fp16, head dims 32 and 64. items: the sequence-aligned list of kAttnTileRows
+// The 16-bit backward of global or local attention over sequence-aligned tiles
+// (attn_bwd_seq.hip): bf16 or fp16, head dims 32 and 64. items: the sequence-aligned list of kAttnTileRows
 // rows (launch_seq_worklist); nl, nd: [H, N] floats each, nd after nl within 4 GiB of it
 // (scratch of the call). Same layouts and ld as launch_attn_bwd.
 bool attn_bwd_seq_supported(int dt, int D, int32_t win, int64_t N, int32_t H, int64_t ld);
 hipError_t launch_attn_bwd_seq(int dt, int D, const void* dout, const void* q, const void* k, const void* v,
                                const void* out, const float* lse, const int32_t* cu, const int32_t* items, int32_t B,
-                               int32_t N, int32_t H, int64_t ld, float scale, void* dq, void* dk, void* dv, float* nl,
-                               float* nd, hipStream_t stream);
+                               int32_t N, int32_t H, int32_t win, int64_t ld, float scale, void* dq, void* dk, void* dv,
+                               float* nl, float* nd, hipStream_t stream);
 
 // checked mode (meta.hip): flag[0] = 1 if cu[0] != 0, a length is outside [1, S] or cu[B] > N
 hipError_t launch_check_cu(const int32_t* cu, int32_t B, int64_t N, int32_t S, int32_t* flag, hipStream_t stream);
