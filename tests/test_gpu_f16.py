@@ -97,7 +97,8 @@ def test_forward_probability_near_fp16_max(d):
     check_lse(to_f64(lse), l_ref, F16, "f16 lse, p near 65504")
 
 
-@pytest.mark.parametrize("d,S,window", [(64, 300, 20), (128, 300, 0), (16, 64, 5), (32, 48, 7), (64, 64, 0)])
+@pytest.mark.parametrize("d,S,window", [(64, 300, 20), (32, 300, 40), (128, 300, 0), (16, 64, 5), (32, 48, 7),
+                                         (64, 64, 0)])
 def test_local_forward_and_backward(d, S, window):
     w = W.custom(310 + d, np.minimum(EDGE, S), S, 2, d, F16, with_grad=True)
     say(f"[f16 local] d={d} S={S} window={window}")

@@ -80,6 +80,22 @@ def test_local_wide_window_equals_global_bitwise():
     assert torch.equal(lse, lse_l)
 
 
+def test_local_wide_window_backward_equals_global_bitwise():
+    """A window wider than every sequence: the local backward streams and computes exactly what
+    the global one does, so the gradients agree bit for bit."""
+    w = W.custom(65, EDGE, 300, 2, 64, W.BF16, with_grad=True)
+    cu_ref, out, lse, grads_l = gpu_local(w, 299, with_bwd=True)
+    cu = torch.from_numpy(cu_ref).to(DEV)
+    q, k, v, do = (to_dev(x, w.dtype) for x in (w.q, w.k, w.v, w.dout))
+    N = int(cu_ref[-1])
+    ws = pe.workspace(pe.pe_attn_workspace_size(w.num_seqs, N, 2, 64, pe.PE_BF16, True), DEV)
+    grads = tuple(torch.full_like(q, float("nan")) for _ in range(3))
+    pe.pe_varlen_attn_bwd(do, q, k, v, out, lse, cu, w.num_seqs, N, w.max_seq_len, w.scale, *grads, ws)
+    torch.cuda.synchronize()
+    for name, a, b in zip(("dq", "dk", "dv"), grads, grads_l):
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16)), name
+
+
 def test_local_long_document_sampled():
     # the long-document lengths (first 200 sequences), window 32, sampled rows
     full = W.long_document()
