@@ -453,6 +453,10 @@ pe_status bwd_impl(const void* dout, const void* q, const void* k, const void* v
   const size_t ib = items_bytes(num_seqs, total_tokens);
   int32_t* items32 = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + ib);
   float* delta = reinterpret_cast<float*>(static_cast<char*>(workspace) + 2 * ib);
+  if (pe::attn_bwd_short_supported(dtype, head_dim, max_seq_len, ld, num_heads))
+    return hip_status(pe::launch_attn_bwd_short(dtype, head_dim, dout, q, k, v, out, lse, cu_seqlens, num_seqs,
+                                                static_cast<int32_t>(total_tokens), num_heads, max_seq_len, win, ld,
+                                                softmax_scale, dq, dk, dv, st));
   if (pe::attn_bwd_seq_supported(dtype, head_dim, win, total_tokens, num_heads, ld)) {
     float* nd = reinterpret_cast<float*>(reinterpret_cast<char*>(delta) +
                                          round_up(static_cast<size_t>(total_tokens) * num_heads * sizeof(float)));

@@ -32,6 +32,7 @@
 // a tile streams only the rows within win of its own rows, a wave computes only the
 // streamed blocks that reach its 32 rows, and in blocks not wholly within win of all
 // of them the pairs farther apart get probability 0.
+#include <algorithm>
 #include <climits>
 #include <type_traits>
 
@@ -461,6 +462,247 @@ __global__ __launch_bounds__(kThreads, kQWaves) void bwd_q_seq_kernel(
   if (qvalid) store_acc_row<Et, D>(dqp, roff, dq, scale, g);
 }
 
+// ---------------------------------------------------------------- short sequences
+// Every length at most 64 (one or two 32-row blocks): one workgroup of two waves per
+// (sequence, head) computes dQ, dK and dV in a single pass, with no prep pass and no
+// work list. The sequence's Q, K, V and dO rows travel by LDS DMA into XOR-swizzled
+// tiles the two waves share (read back as row operands and, by ds_read_b64_tr_b16, as
+// transposed ones), and D = <dO, O> and -lse log2(e) of its rows are formed in place. Wave 0 takes, per key block, S = Q K^T and dP - D =
+// dO V^T + nd over every query block and accumulates dV^T += dO^T P, dK^T += Q^T dS;
+// wave 1 takes, per query block, S^T and dP^T - D over every key block and accumulates
+// dQ^T += K^T dS^T. S and dP are formed in both orientations (seven products where five
+// would do), so every P and dS enters its product straight from the accumulators: a
+// short sequence moves many bytes per flop, and the extra products cost less than a
+// transpose through LDS.
+constexpr int kShortBwdMaxLen = 64;
+
+// NB: 32-row blocks of this sequence (1 or 2, block-uniform); NBT: blocks per tile array
+template <typename Et, int D, int NB, int NBT>
+__device__ __forceinline__ void short_bwd(const void* __restrict__ dop, const void* __restrict__ qp,
+                                          const void* __restrict__ kp, const void* __restrict__ vp,
+                                          const void* __restrict__ op, const float* __restrict__ lse, int w, int h,
+                                          int lo, int hi, int32_t N, int32_t H, int32_t win, int64_t ld, float c,
+                                          float scale, void* __restrict__ dqp, void* __restrict__ dkp,
+                                          void* __restrict__ dvp, char (*tiles)[NBT][32 * D * 2], float* nlnd) {
+  // tiles: [Q, K, dO, V][block]
+  constexpr int CH = D / 8, QS = D / 16, DB = D / 32;
+  constexpr int TB = 32 * D * 2;     // bytes of one 32-row tile
+  constexpr int NL = 32 * CH / 64;   // DMA instructions per tile and wave
+  const int lane = threadIdx.x & 63, ql = lane & 31, g = lane >> 5;
+  const int64_t hd = static_cast<int64_t>(H) * D;  // elements between dO (and O) rows
+  const uint32_t tq = lds_addr(tiles[0][0]), tk = lds_addr(tiles[1][0]), td = lds_addr(tiles[2][0]);
+  const uint32_t tv = lds_addr(tiles[3][0]);
+
+  // Q, K (wave 0), dO and V (wave 1) rows -> the tiles (rows past the sequence repeat its last
+  // row: valid memory, and every product they enter is masked or never stored)
+  const char* qb0 = static_cast<const char*>(qp) + static_cast<int64_t>(lo) * ld * 2;
+  const char* kb0 = static_cast<const char*>(kp) + static_cast<int64_t>(lo) * ld * 2;
+  const char* db0 = static_cast<const char*>(dop) + static_cast<int64_t>(lo) * hd * 2;
+  const char* vb0 = static_cast<const char*>(vp) + static_cast<int64_t>(lo) * ld * 2;
+#pragma unroll
+  for (int b = 0; b < NB; ++b)
+#pragma unroll
+    for (int j = 0; j < NL; ++j) {
+      const int slot = j * 64 + lane;
+      const int r = slot / CH, pc = slot - r * CH;
+      const int rr = min(32 * b + r, hi - lo - 1);
+      const uint32_t cofs = static_cast<uint32_t>(h * D * 2 + (pc ^ (swz(r) & (CH - 1))) * 16);
+      const uint32_t dst = static_cast<uint32_t>(b * TB + j * 1024);
+      if (w == 0) {
+        dma16(tq + dst, qb0, static_cast<uint32_t>(rr * ld * 2) + cofs);
+        dma16(tk + dst, kb0, static_cast<uint32_t>(rr * ld * 2) + cofs);
+      } else {
+        dma16(td + dst, db0, static_cast<uint32_t>(rr * hd * 2) + cofs);
+        dma16(tv + dst, vb0, static_cast<uint32_t>(rr * ld * 2) + cofs);
+      }
+    }
+  // the lane's rows of O and the LSE (rows past the sequence: zero)
+  vec8<Et> orw[NB][QS];
+  float lq[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    const int row = lo + 32 * b + ql;
+    load_row_regs<Et, D>(op, static_cast<int64_t>(row) * hd + h * D, g, row < hi, orw[b]);
+    lq[b] = row < hi ? lse[static_cast<int64_t>(h) * N + row] : 0.f;
+  }
+  wait_vmcnt<0>();  // this wave's tile rows have landed
+  raw_barrier();    // and the other wave's
+
+  const StageOffsets<D> so(lane);
+  // nl = -lse log2(e) and nd = -<dO, O> of every row: the lane's own in registers, and (wave 0)
+  // all of them in LDS (nl[0..63], nd[64..127]) for the products whose rows span 16 lanes' rows
+  float nlq[NB], ndq[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    float dsum = 0.f;
+#pragma unroll
+    for (int q = 0; q < QS; ++q) {
+      const vec8<Et> dv8 = as_vec8<Et>(ds_read_b128_at(td + static_cast<uint32_t>(b * TB + so.row[q])));
+#pragma unroll
+      for (int e = 0; e < 8; ++e) dsum = fmaf(static_cast<float>(dv8[e]), static_cast<float>(orw[b][q][e]), dsum);
+    }
+    ndq[b] = -xhalf_sum(dsum);
+    nlq[b] = -(lq[b] * kLog2e);
+    if (w == 0 && g == 0) {
+      nlnd[32 * b + ql] = nlq[b];
+      nlnd[64 + 32 * b + ql] = ndq[b];
+    }
+  }
+
+  if (w == 0) {  // ---- dK and dV, one key block at a time (lane = key)
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // nl, nd written before they are read
+    const uint32_t nl0 = lds_addr(nlnd);
+#pragma unroll
+    for (int kb = 0; kb < NB; ++kb) {
+      asm volatile("" ::: "memory");  // no LDS read of this block is hoisted above the previous one's work
+      const int krow = lo + 32 * kb + ql;
+      vec8<Et> kreg[QS], vreg[QS];
+#pragma unroll
+      for (int q = 0; q < QS; ++q) {
+        kreg[q] = as_vec8<Et>(ds_read_b128_at(tk + static_cast<uint32_t>(kb * TB + so.row[q])));
+        vreg[q] = as_vec8<Et>(ds_read_b128_at(tv + static_cast<uint32_t>(kb * TB + so.row[q])));
+      }
+      floatx16 dk[DB], dv[DB];
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        dk[db] = floatx16{};
+        dv[db] = floatx16{};
+      }
+#pragma unroll
+      for (int qb = 0; qb < NB; ++qb) {
+        asm volatile("" ::: "memory");
+        const uint32_t qt = tq + static_cast<uint32_t>(qb * TB), dt = td + static_cast<uint32_t>(qb * TB);
+        const int qr0 = lo + 32 * qb;
+        const uint32_t lt = nl0 + static_cast<uint32_t>(4 * (32 * qb + 4 * g));  // nl of rows 4g.. (+32 bytes per 8 rows)
+        floatx16 s = floatx16{}, dp;
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4) {  // dP starts at -D of its rows
+          const floatx4 n4 = __builtin_bit_cast(floatx4, ds_read_b128_at(lt + 256 + 32 * i4));
+#pragma unroll
+          for (int e = 0; e < 4; ++e) dp[4 * i4 + e] = n4[e];
+        }
+#pragma unroll
+        for (int q = 0; q < QS; ++q) s = mfma16<Et>(as_vec8<Et>(ds_read_b128_at(qt + so.row[q])), kreg[q], s);
+#pragma unroll
+        for (int q = 0; q < QS; ++q) dp = mfma16<Et>(as_vec8<Et>(ds_read_b128_at(dt + so.row[q])), vreg[q], dp);
+        mask_block(s, -INT_MAX, hi - (qr0 + 4 * g));  // query rows past the end
+        if (win >= 0) mask_block(s, krow - win - (qr0 + 4 * g), krow + win + 1 - (qr0 + 4 * g));
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4) {
+          const floatx4 l4 = __builtin_bit_cast(floatx4, ds_read_b128_at(lt + 32 * i4));
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int i = 4 * i4 + e;
+            const float p = __builtin_amdgcn_exp2f(fmaf(s[i], c, l4[e]));
+            s[i] = p;
+            dp[i] *= p;
+          }
+        }
+        vec8<Et> pb[2], sb16[2];
+        acc_to_h16<Et>(s, pb);
+        acc_to_h16<Et>(dp, sb16);
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+          for (int db = 0; db < DB; ++db) {
+            dv[db] = mfma16<Et>(tr_operand<Et, D>(dt, so, s2, db), pb[s2], dv[db]);
+            dk[db] = mfma16<Et>(tr_operand<Et, D>(qt, so, s2, db), sb16[s2], dk[db]);
+          }
+      }
+      if (krow < hi) {  // the same for both lane halves, which store together
+        const int64_t roff = static_cast<int64_t>(krow) * ld + h * D;
+        store_acc_row<Et, D>(dkp, roff, dk, scale, g);
+        store_acc_row<Et, D>(dvp, roff, dv, 1.f, g);
+      }
+    }
+  } else {  // ---- dQ, one query block at a time (lane = query)
+#pragma unroll
+    for (int qb = 0; qb < NB; ++qb) {
+      asm volatile("" ::: "memory");
+      const int qrow = lo + 32 * qb + ql;
+      vec8<Et> qreg[QS], dreg[QS];
+#pragma unroll
+      for (int q = 0; q < QS; ++q) {
+        qreg[q] = as_vec8<Et>(ds_read_b128_at(tq + static_cast<uint32_t>(qb * TB + so.row[q])));
+        dreg[q] = as_vec8<Et>(ds_read_b128_at(td + static_cast<uint32_t>(qb * TB + so.row[q])));
+      }
+      floatx16 dq[DB];
+#pragma unroll
+      for (int db = 0; db < DB; ++db) dq[db] = floatx16{};
+#pragma unroll
+      for (int kb = 0; kb < NB; ++kb) {
+        asm volatile("" ::: "memory");
+        const uint32_t kt = tk + static_cast<uint32_t>(kb * TB);
+        const int kr0 = lo + 32 * kb;
+        floatx16 s = floatx16{}, dp;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) dp[i] = ndq[qb];  // dP^T starts at -D of this lane's query
+#pragma unroll
+        for (int q = 0; q < QS; ++q) s = mfma16<Et>(as_vec8<Et>(ds_read_b128_at(kt + so.row[q])), qreg[q], s);
+#pragma unroll
+        for (int q = 0; q < QS; ++q)
+          dp = mfma16<Et>(as_vec8<Et>(ds_read_b128_at(tv + static_cast<uint32_t>(kb * TB + so.row[q]))), dreg[q], dp);
+        mask_block(s, -INT_MAX, hi - (kr0 + 4 * g));  // keys past the end
+        if (win >= 0) mask_block(s, qrow - win - (kr0 + 4 * g), qrow + win + 1 - (kr0 + 4 * g));
+#pragma unroll
+        for (int i = 0; i < 16; ++i) dp[i] *= __builtin_amdgcn_exp2f(fmaf(s[i], c, nlq[qb]));
+        vec8<Et> sb16[2];
+        acc_to_h16<Et>(dp, sb16);
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+          for (int db = 0; db < DB; ++db) dq[db] = mfma16<Et>(tr_operand<Et, D>(kt, so, s2, db), sb16[s2], dq[db]);
+      }
+      if (qrow < hi) store_acc_row<Et, D>(dqp, static_cast<int64_t>(qrow) * ld + h * D, dq, scale, g);
+    }
+  }
+}
+
+template <typename Et, int D, int NBT>
+__global__ __launch_bounds__(128) void bwd_short_kernel(
+    const void* __restrict__ dop, const void* __restrict__ qp, const void* __restrict__ kp,
+    const void* __restrict__ vp, const void* __restrict__ op, const float* __restrict__ lse,
+    const int32_t* __restrict__ cu, int32_t B, int32_t N, int32_t H, int32_t win, int64_t ld, float c, float scale,
+    void* __restrict__ dqp, void* __restrict__ dkp, void* __restrict__ dvp) {
+  __shared__ __align__(16) char tiles[4][NBT][32 * D * 2];  // [Q, K, dO, V][block][tile]
+  __shared__ __align__(16) float nlnd[128];
+  const int w = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+  const int64_t item = blockIdx.x;  // (sequence, head), heads fastest
+  const int b = static_cast<int>(item / H), h = static_cast<int>(item - static_cast<int64_t>(b) * H);
+  if (b >= B) return;  // block-uniform
+  const int lo = cu[b];
+  // a length above the bound is cut to its first 32 NBT rows (rows past them are left as
+  // they were), so no access leaves the sequence or the tiles
+  const int hi = min(cu[b + 1], lo + 32 * NBT);
+  if (hi <= lo) return;  // block-uniform
+  if (NBT == 1 || hi - lo <= 32)
+    short_bwd<Et, D, 1, NBT>(dop, qp, kp, vp, op, lse, w, h, lo, hi, N, H, win, ld, c, scale, dqp, dkp, dvp, tiles,
+                             nlnd);
+  else
+    short_bwd<Et, D, (NBT > 1 ? 2 : 1), NBT>(dop, qp, kp, vp, op, lse, w, h, lo, hi, N, H, win, ld, c, scale, dqp,
+                                             dkp, dvp, tiles, nlnd);
+}
+
+template <typename Et, int D>
+hipError_t bwd_short_dispatch(const void* dout, const void* q, const void* k, const void* v, const void* out,
+                              const float* lse, const int32_t* cu, int32_t B, int32_t N, int32_t H,
+                              int32_t max_seq_len, int32_t win, int64_t ld, float scale, void* dq, void* dk, void* dv,
+                              hipStream_t stream) {
+  const int64_t items = static_cast<int64_t>(B) * H;
+  if (items == 0) return hipSuccess;
+  const unsigned blocks = static_cast<unsigned>(items);
+  const float c = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
+  hipEvent_t ev = timing_start(stream);
+  if (max_seq_len <= 32)
+    hipLaunchKernelGGL((bwd_short_kernel<Et, D, 1>), dim3(blocks), dim3(128), 0, stream, dout, q, k,
+                       v, out, lse, cu, B, N, H, win, ld, c, scale, dq, dk, dv);
+  else
+    hipLaunchKernelGGL((bwd_short_kernel<Et, D, 2>), dim3(blocks), dim3(128), 0, stream, dout, q, k,
+                       v, out, lse, cu, B, N, H, win, ld, c, scale, dq, dk, dv);
+  timing_stop("bwd_short", ev, stream);
+  return hipGetLastError();
+}
+
 template <typename Et, int D>
 hipError_t bwd_seq_dispatch(const void* dout, const void* q, const void* k, const void* v, const void* out,
                             const float* lse, const int32_t* cu, const int32_t* items, int32_t B, int32_t N,
@@ -508,6 +750,33 @@ bool attn_bwd_seq_supported(int dt, int D, int32_t win, int64_t N, int32_t H, in
   // nd after nl) within 4 GiB of nl
   if (ld * 2 * max(kKvRows, kQRows) >= (int64_t{1} << 31)) return false;
   return N * H * 2 * static_cast<int64_t>(sizeof(float)) + 256 < (int64_t{1} << 32);
+}
+
+bool attn_bwd_short_supported(int dt, int D, int32_t max_seq_len, int64_t ld, int32_t H) {
+  if (dt != kDtBF16 && dt != kDtF16) return false;
+  if ((D != 32 && D != 64) || max_seq_len > kShortBwdMaxLen) return false;
+  // 32-bit DMA offsets: 64 rows of the widest stride
+  return std::max(ld, static_cast<int64_t>(H) * D) * 2 * kShortBwdMaxLen < (int64_t{1} << 31);
+}
+
+hipError_t launch_attn_bwd_short(int dt, int D, const void* dout, const void* q, const void* k, const void* v,
+                                 const void* out, const float* lse, const int32_t* cu, int32_t B, int32_t N,
+                                 int32_t H, int32_t max_seq_len, int32_t win, int64_t ld, float scale, void* dq,
+                                 void* dk, void* dv, hipStream_t stream) {
+  const bool f16 = dt == kDtF16;
+  switch (D) {
+    case 32:
+      return f16 ? bwd_short_dispatch<_Float16, 32>(dout, q, k, v, out, lse, cu, B, N, H, max_seq_len, win, ld, scale,
+                                                   dq, dk, dv, stream)
+                 : bwd_short_dispatch<__bf16, 32>(dout, q, k, v, out, lse, cu, B, N, H, max_seq_len, win, ld, scale,
+                                                 dq, dk, dv, stream);
+    case 64:
+      return f16 ? bwd_short_dispatch<_Float16, 64>(dout, q, k, v, out, lse, cu, B, N, H, max_seq_len, win, ld, scale,
+                                                   dq, dk, dv, stream)
+                 : bwd_short_dispatch<__bf16, 64>(dout, q, k, v, out, lse, cu, B, N, H, max_seq_len, win, ld, scale,
+                                                 dq, dk, dv, stream);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 hipError_t launch_attn_bwd_seq(int dt, int D, const void* dout, const void* q, const void* k, const void* v,

@@ -150,6 +150,15 @@ hipError_t launch_attn_bwd_seq(int dt, int D, const void* dout, const void* q, c
                                int32_t N, int32_t H, int32_t win, int64_t ld, float scale, void* dq, void* dk, void* dv,
                                float* nl, float* nd, hipStream_t stream);
 
+// The 16-bit backward for lengths up to 64 (attn_bwd_seq.hip): bf16 or fp16, head dims 32
+// and 64, global or local; one wave per (sequence, head), dQ, dK and dV in one pass, no work
+// list and no scratch. Same layouts and ld as launch_attn_bwd.
+bool attn_bwd_short_supported(int dt, int D, int32_t max_seq_len, int64_t ld, int32_t H);
+hipError_t launch_attn_bwd_short(int dt, int D, const void* dout, const void* q, const void* k, const void* v,
+                                 const void* out, const float* lse, const int32_t* cu, int32_t B, int32_t N,
+                                 int32_t H, int32_t max_seq_len, int32_t win, int64_t ld, float scale, void* dq,
+                                 void* dk, void* dv, hipStream_t stream);
+
 // checked mode (meta.hip): flag[0] = 1 if cu[0] != 0, a length is outside [1, S] or cu[B] > N
 hipError_t launch_check_cu(const int32_t* cu, int32_t B, int64_t N, int32_t S, int32_t* flag, hipStream_t stream);
 

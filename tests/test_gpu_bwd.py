@@ -114,6 +114,16 @@ def test_fp32_recompute_path(d):
         assert err <= 1e-5 * max(1.0, y.abs().max().item()), f"paths differ by {err:.3e}"
 
 
+@pytest.mark.parametrize("S", [32, 64])
+@pytest.mark.parametrize("d", [32, 64])
+def test_short_single_pass(S, d):
+    """A length bound of at most 64: one wave per (sequence, head) forms dQ, dK and dV in one pass.
+    Lengths at the block edges (1, 31, 32, 33, 63, 64) and random ones, three heads."""
+    L = np.concatenate([[1, 2, 31, 32, 33, 63, 64, 17], W.random_lengths(81 + d, 200, 1, 64)])
+    L = np.minimum(L, S).astype(np.int32)
+    check_bwd(W.custom(80 + d + S, L, S, 3, d, W.BF16, with_grad=True), f"short single pass S={S} d={d}")
+
+
 @pytest.mark.parametrize("dtype", [W.FP32, W.BF16])
 def test_ragged_mixed(dtype):
     rng = np.random.default_rng(71)

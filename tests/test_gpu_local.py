@@ -130,6 +130,14 @@ def test_local_backward_edge_lengths(dtype, d, window):
     check_local_bwd(W.custom(70 + d, EDGE, 300, 2, d, dtype, with_grad=True), window, f"edge d={d}")
 
 
+@pytest.mark.parametrize("window", [0, 3, 31])
+@pytest.mark.parametrize("d", [32, 64])
+def test_local_backward_short_bound(window, d):
+    # length bound 48: the 16-bit single-pass kernel (one wave per sequence and head, band mask per score)
+    L = W.random_lengths(66, 200, 1, 48)
+    check_local_bwd(W.custom(67 + d, L, 48, 3, d, W.BF16, with_grad=True), window, f"short bound d={d}")
+
+
 def test_local_backward_generic_head_dims():
     check_local_bwd(W.custom(71, EDGE[:12], 300, 2, 16, W.FP32, with_grad=True), 7, "fp32 d=16")
     check_local_bwd(W.custom(72, EDGE[:12], 300, 2, 128, W.BF16, with_grad=True), 7, "bf16 d=128")
