@@ -105,7 +105,7 @@ def algo_work(kernel, w, N, L2, e, with_lse, with_grid=True, window=None):
                    "byte": 2.0 * N * D * e if ds_dq else (6.0 if wave_dq else 5.0) * N * D * e + 8.0 * N * H},
         # the whole backward in one pass (short sequences): 10 L2 H d; reads Q, K, V, O, dO, LSE,
         # writes dQ, dK, dV
-        "bwd_fused": {"flop": 10.0 * L2 * H * d, "byte": 8.0 * N * D * e + 4.0 * N * H},
+        "bwd_short": {"flop": 10.0 * L2 * H * d, "byte": 8.0 * N * D * e + 4.0 * N * H},
         # first token: read K and V once, the B queries, write B outputs (+ LSE)
         "attn_fwd_first": {"byte": 2.0 * N * D * e + 2.0 * B * D * e + (4.0 * B * H if with_lse else 0.0)},
         # first-token backward: read K, V and the B rows of q, dO, O (+ LSE), write dK, dV and dq_first

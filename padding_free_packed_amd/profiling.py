@@ -28,6 +28,7 @@ KERNEL_SOURCES = {
     "bwd_delta": ["attn_bwd.hip", "attn_bwd_seq.hip", "attn_common.h", "common.h"],
     "bwd_dkdv": ["attn_bwd.hip", "attn_bwd_seq.hip", "attn_f32_wave.hip", "attn_common.h", "common.h"],
     "bwd_dq": ["attn_bwd.hip", "attn_bwd_seq.hip", "attn_f32_wave.hip", "attn_common.h", "common.h"],
+    "bwd_short": ["attn_bwd_seq.hip", "attn_common.h", "common.h"],
     "pack_rows": ["pack.hip", "common.h"],
     "unpack_rows": ["pack.hip", "common.h"],
     "scan": ["pack.hip", "common.h"],
@@ -45,6 +46,7 @@ KERNEL_PATTERNS = {
     "bwd_delta": r"bwd_(delta|seq_prep)_kernel(<|I)",
     "bwd_dkdv": r"bwd_(dkdv(_f32)?|kv_seq)_kernel(<|I)",
     "bwd_dq": r"bwd_(dq(_ds)?(_f32)?|q_seq)_kernel(<|I)",
+    "bwd_short": r"bwd_short_kernel(<|I)",
     "pack_rows": r"(?<!un)pack_rows_kernel(<|I)",
     "unpack_rows": r"unpack_rows_kernel(<|I)",
     "scan": r"scan_lengths_kernel",
