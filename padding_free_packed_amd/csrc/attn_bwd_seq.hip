@@ -1,5 +1,6 @@
-// 16-bit backward of global or local (windowed) attention for head dims 32 and 64 over
-// sequence-aligned 128-row tiles. Three launches, no atomics, so the result is bitwise
+// 16-bit backward of global or local (windowed) attention for head dims 32 and 64. For a
+// length bound of at most 64 one single-pass kernel (see "short sequences" below); else
+// three launches over sequence-aligned 128-row tiles. No atomics, so the result is bitwise
 // reproducible:
 //
 //   prep:   per (head, row): nl = -lse * log2(e) and nd = -<dO, O> (minus the row's D)

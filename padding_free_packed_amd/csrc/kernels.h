@@ -151,7 +151,7 @@ hipError_t launch_attn_bwd_seq(int dt, int D, const void* dout, const void* q, c
                                float* nl, float* nd, hipStream_t stream);
 
 // The 16-bit backward for lengths up to 64 (attn_bwd_seq.hip): bf16 or fp16, head dims 32
-// and 64, global or local; one wave per (sequence, head), dQ, dK and dV in one pass, no work
+// and 64, global or local; one workgroup of two waves per (sequence, head), dQ, dK and dV in one pass, no work
 // list and no scratch. Same layouts and ld as launch_attn_bwd.
 bool attn_bwd_short_supported(int dt, int D, int32_t max_seq_len, int64_t ld, int32_t H);
 hipError_t launch_attn_bwd_short(int dt, int D, const void* dout, const void* q, const void* k, const void* v,
