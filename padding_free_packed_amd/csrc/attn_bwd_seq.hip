@@ -56,35 +56,60 @@ constexpr int kQRows = 32;
 constexpr int kKvWaves = 3;
 constexpr int kQWaves = 3;
 
-// One group of CH lanes per (head, row), rows fastest: lane `sub` of the group reads
-// 16-byte chunk `sub` of the head row of dO and of O, and the group sums by butterfly
-// (the summation order of the delta pass of attn_bwd.hip, so D is the same value).
-// Consecutive groups take consecutive rows of one head, so the LSE reads and the
-// nl, nd writes of a wave are contiguous.
+// A workgroup takes R consecutive rows with all their heads (R = kPrepCells / H, at most
+// kPrepRows): its lanes read the rows' dO and O as one contiguous run, one group of CH lanes
+// per (row, head) with the 16-byte chunks fastest, and each group sums by butterfly (the
+// summation order of the delta pass of attn_bwd.hip, so D is the same value). The sums go
+// through LDS so that nl and nd of each head leave as one run of R values of [H, N].
+constexpr int kPrepRows = 32;
+constexpr int kPrepCells = 2048;  // (row, head) sums per workgroup at most
 template <typename Et, int D>
 __global__ __launch_bounds__(256) void bwd_seq_prep_kernel(const void* __restrict__ dout, const void* __restrict__ out,
                                                            const float* __restrict__ lse, int32_t N, int32_t H,
-                                                           float* __restrict__ nl, float* __restrict__ nd) {
+                                                           int32_t R, float* __restrict__ nl, float* __restrict__ nd) {
   constexpr int CH = D / 8;  // 16-byte chunks per head row (4 or 8)
-  const int64_t idx = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-  const int64_t hi = idx / CH;  // (head, row) pair, head-major over [H, N]
-  const int sub = static_cast<int>(idx - hi * CH);
-  const int64_t total = static_cast<int64_t>(N) * H;
-  float s = 0.f;
-  if (hi < total) {
-    const int64_t hh = hi / N, i = hi - hh * N;
-    const int64_t ch = (i * H + hh) * CH + sub;
-    const uint4 a = *reinterpret_cast<const uint4*>(static_cast<const char*>(dout) + ch * 16);
-    const uint4 b = *reinterpret_cast<const uint4*>(static_cast<const char*>(out) + ch * 16);
-    const u16x8 x = __builtin_bit_cast(u16x8, a), y = __builtin_bit_cast(u16x8, b);
+  __shared__ float res[kPrepCells];  // [head][row] sums of the workgroup's rows
+  const int64_t r0 = static_cast<int64_t>(blockIdx.x) * R;
+  const int rows = static_cast<int>(min(static_cast<int64_t>(R), static_cast<int64_t>(N) - r0));
+  const int cells = rows * H;
+  const int chunks = cells * CH;
+  const char* a = static_cast<const char*>(dout) + r0 * H * D * 2;
+  const char* b = static_cast<const char*>(out) + r0 * H * D * 2;
+  constexpr int U = 4;  // chunks per lane whose loads are in flight together
+  for (int u0 = 0; u0 < chunks; u0 += U * 256) {  // block-uniform trip count: every lane takes part in the sums
+    uint4 xa[U], xb[U];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) s = fmaf(h16_to_f32<Et>(x[e]), h16_to_f32<Et>(y[e]), s);
+    for (int k = 0; k < U; ++k) {
+      const int u = u0 + k * 256 + static_cast<int>(threadIdx.x);
+      if (u < chunks) {
+        xa[k] = *reinterpret_cast<const uint4*>(a + static_cast<int64_t>(u) * 16);
+        xb[k] = *reinterpret_cast<const uint4*>(b + static_cast<int64_t>(u) * 16);
+      } else {
+        xa[k] = uint4{0, 0, 0, 0};
+        xb[k] = uint4{0, 0, 0, 0};
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < U; ++k) {
+      const int u = u0 + k * 256 + static_cast<int>(threadIdx.x);
+      const u16x8 x = __builtin_bit_cast(u16x8, xa[k]), y = __builtin_bit_cast(u16x8, xb[k]);
+      float s = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) s = fmaf(h16_to_f32<Et>(x[e]), h16_to_f32<Et>(y[e]), s);
+#pragma unroll
+      for (int o = 1; o < CH; o <<= 1) s += __shfl_xor(s, o);
+      if (u < chunks && (u & (CH - 1)) == 0) {
+        const int cell = u / CH, row = cell / H, hh = cell - row * H;
+        res[hh * R + row] = s;
+      }
+    }
   }
-#pragma unroll
-  for (int o = 1; o < CH; o <<= 1) s += __shfl_xor(s, o);
-  if (hi < total && sub == 0) {
-    nd[hi] = -s;
-    nl[hi] = -(lse[hi] * kLog2e);
+  __syncthreads();
+  for (int v = threadIdx.x; v < cells; v += 256) {  // rows fastest: each head's run is contiguous
+    const int hh = v / rows, row = v - hh * rows;
+    const int64_t o = static_cast<int64_t>(hh) * N + r0 + row;
+    nd[o] = -res[hh * R + row];
+    nl[o] = -(lse[o] * kLog2e);
   }
 }
 
@@ -710,10 +735,10 @@ hipError_t bwd_seq_dispatch(const void* dout, const void* q, const void* k, cons
                             int32_t H, int32_t win, int64_t ld, float scale, void* dq, void* dk, void* dv, float* nl,
                             float* nd, hipStream_t stream) {
   if (N == 0) return hipSuccess;
-  const int64_t lanes = static_cast<int64_t>(N) * H * (D / 8);
+  const int R = std::max(1, std::min(kPrepRows, kPrepCells / H));  // rows per prep workgroup
   hipEvent_t ev_prep = timing_start(stream);
-  hipLaunchKernelGGL((bwd_seq_prep_kernel<Et, D>), dim3(static_cast<unsigned>((lanes + 255) / 256)), dim3(256), 0,
-                     stream, dout, out, lse, N, H, nl, nd);
+  hipLaunchKernelGGL((bwd_seq_prep_kernel<Et, D>), dim3(static_cast<unsigned>((N + R - 1) / R)), dim3(256), 0, stream,
+                     dout, out, lse, N, H, R, nl, nd);
   timing_stop("bwd_delta", ev_prep, stream);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -747,6 +772,7 @@ hipError_t bwd_seq_dispatch(const void* dout, const void* q, const void* k, cons
 bool attn_bwd_seq_supported(int dt, int D, int32_t win, int64_t N, int32_t H, int64_t ld) {
   if (dt != kDtBF16 && dt != kDtF16) return false;
   if (D != 32 && D != 64) return false;
+  if (H > kPrepCells) return false;  // the prep pass holds a row's sums of every head in LDS
   // 32-bit DMA offsets: 32 rows of the widest stride, and nl/nd ([H, N] floats each,
   // nd after nl) within 4 GiB of nl
   if (ld * 2 * max(kKvRows, kQRows) >= (int64_t{1} << 31)) return false;
