@@ -171,9 +171,9 @@ pe_status pe_unpack(const void* packed, const int32_t* cu_seqlens, int32_t num_s
  *   items   device int32 [ceil(total_tokens / tile_rows) + 1], written
  * Asynchronous. The attention calls run this themselves in their workspace;
  * it is exported so it can be checked and reused. The fp32 one-wave kernels
- * (head dims 32, 64) and the 16-bit forward with 64-row waves (head dims 32,
- * 64) build a sequence-aligned variant instead: tiles start at every
- * sequence's first row, so a tile never spans two sequences.
+ * (head dims 32, 64) and the 16-bit kernels at head dims 32 and 64 (length
+ * bounds above 64) build a sequence-aligned variant instead: tiles start at
+ * every sequence's first row, so a tile never spans two sequences.
  */
 pe_status pe_worklist(const int32_t* cu_seqlens, int32_t num_seqs, int64_t total_tokens,
                       int32_t tile_rows, int32_t* items, void* stream);
