@@ -25,9 +25,9 @@ def _bits(t):
 CASES = [  # dtype, d, max_seq_len: every kernel family
     (W.FP32, 64, 300),    # fp32 one-wave kernels
     (W.FP32, 16, 300),    # generic fp32
-    (W.BF16, 64, 300),    # bf16 sequence-aligned 128-row-tile forward, generic backward
-    (W.BF16, 128, 300),   # bf16 LDS-DMA forward, head dim 128
-    (W.BF16, 64, 64),     # generic bf16 (short bound)
+    (W.BF16, 64, 300),    # bf16 sequence-aligned 128-row tiles, forward and three-pass backward
+    (W.BF16, 128, 300),   # bf16 LDS-DMA forward, head dim 128, generic backward
+    (W.BF16, 64, 64),     # bf16 short bound: one-wave forward, single-pass backward
 ]
 
 
