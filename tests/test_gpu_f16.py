@@ -70,8 +70,9 @@ def test_forward_long_sequences_and_large_scores():
     check_lse(to_f64(lse), l_ref, F16, "f16 long lse")
 
 
+@pytest.mark.parametrize("window", [None, 100])
 @pytest.mark.parametrize("d", [32, 64])
-def test_forward_probability_near_fp16_max(d):
+def test_forward_probability_near_fp16_max(d, window):
     """A key block after the first whose one large score sits just under 16
     (log2 units) above the first block's maximum, the rest of its scores far
     below: its unnormalised probability, about 65529, is finite in fp32 but
@@ -89,10 +90,10 @@ def test_forward_probability_near_fp16_max(d):
     k[32, :, 0] = 1.0
     k[33:, :, 0] = -8.0
     w.q, w.k = (x.astype(np.float16).view(np.uint16) for x in (q, k))
-    say(f"[f16 fwd] p near the fp16 maximum: d={d} L={L}")
-    cu_ref, _, _, out, lse, _ = _fwd(w)
+    say(f"[f16 fwd] p near the fp16 maximum: d={d} L={L} window={window}")
+    cu_ref, _, _, out, lse, _ = _fwd(w, window)
     torch.cuda.synchronize()
-    o_ref, l_ref = oracle.attention(*(W.to_f64(x, F16) for x in (w.q, w.k, w.v)), cu_ref, w.scale)
+    o_ref, l_ref = oracle.attention(*(W.to_f64(x, F16) for x in (w.q, w.k, w.v)), cu_ref, w.scale, window=window)
     check_out(to_f64(out), o_ref, F16, "f16 out, p near 65504")
     check_lse(to_f64(lse), l_ref, F16, "f16 lse, p near 65504")
 
